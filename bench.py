@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""Benchmark: block-verify forward through a 40-layer NVFP4 MoE stack at K=2.
+
+Workload: 40 independent MoE layers (hidden 2048, 256 routed experts, top-8
+softmax-renormalised, intermediate 512, one shared expert of intermediate
+512, NVFP4 expert weights, bf16 routers), K = 2 verify rows, each layer's
+output RMS-normalised into the next layer's input.  All weights (18.2 GB)
+and a pool of 8 input blocks are resident in HBM before timing; each step
+is one captured-graph launch of the whole stack on the next input of the
+pool, so the experts each step streams differ.
+
+value = algorithmic bytes per step / measured time per step, where the
+bytes are the router, each *unique* routed expert once, the shared expert
+and the activations, summed over the 40 layers with the unique-expert
+counts the dedup pass reports for that input.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "MoE verify step: weight GB/s and % HBM peak at K=2; µs per 40-layer stack"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def nvfp4_bytes(rows, cols):
+    return rows * cols // 2 + rows * cols // 16 + 4
+
+
+def gateup_bytes(shape, n_unique, K):
+    """Algorithmic HBM bytes of one gate/up launch: gate + up of every unique
+    expert and the shared expert, x read once, h written once."""
+    H, I, Is, k = shape.hidden, shape.inter, shape.shared_inter, shape.top_k
+    b = n_unique * 2 * nvfp4_bytes(I, H)
+    if Is:
+        b += 2 * nvfp4_bytes(Is, H)
+    return b + K * H * 2 + (K * k * I + K * Is) * 4
+
+
+def cpu_baseline(layers, x, shape, K, budget_s):
+    """The oracle (single-threaded C, fp64) chained over the first layers of
+    the same stack and input until budget_s seconds of CPU work; GB/s over
+    the same algorithmic byte definition as the GPU figure."""
+    import oracle as orc
+    import numpy as np
+    from speculative_block_verify_amd import api
+    cfg = api.make_cfg(shape, K)
+    xo = x.cpu().numpy().view(np.uint16)
+    t_total, n_bytes, n_layers = 0.0, 0, 0
+    for w in layers:
+        wh = {k: (None if v is None else ({kk: vv.cpu() for kk, vv in v.items()} if isinstance(v, dict) else v.cpu()))
+              for k, v in w.items()}
+        t0 = time.perf_counter()
+        rec = orc.moe_layer(wh, xo, shape.top_k)
+        xo = orc.rmsnorm_bf16(rec["y"])
+        t_total += time.perf_counter() - t0
+        U = orc.dedup(rec["ids"], shape.n_experts)["n_unique"]
+        n_bytes += api.moe_verify_weight_bytes(cfg, U, K)
+        n_layers += 1
+        if t_total >= budget_s:
+            break
+    return {"value": n_bytes / t_total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "first %d of the 40 layers, K=2, input 0 of the pool; %.1f s single-threaded" % (n_layers, t_total)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--timing-steps", type=int, default=16, help="steps of the per-kernel timing pass")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this path runs on a single MI355X and has no multi-GPU mode "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from speculative_block_verify_amd import api, inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    shape, L, K, POOL, SEED = inputs.LAGUNA, 40, 2, 8, 2024
+    t0 = time.time()
+    layers = inputs.gen_stack(shape, L, SEED, device=dev)
+    xs = [inputs.gen_x(K, shape.hidden, SEED + 1 + i, device=dev) for i in range(POOL)]
+    torch.cuda.synchronize()
+    log("bench: generated %d layers (%.2f GB) in %.1f s" % (
+        L, sum(sum(t.numel() for t in (w[m].values() if isinstance(w[m], dict) else [w[m]]))
+               for w in layers for m in w if w[m] is not None) / 1e9, time.time() - t0))
+
+    cfg = api.make_cfg(shape, K)
+    ws = api.alloc_workspace(cfg, dev)
+    wts = [api.make_weights(w) for w in layers]
+    y = torch.empty(K, shape.hidden, dtype=torch.int16, device=dev)
+    y32 = torch.empty(K, shape.hidden, dtype=torch.float32, device=dev)
+
+    # unique-expert counts per (input, layer) from the dedup pass
+    nu = torch.empty(L, dtype=torch.int32, device=dev)
+    step_bytes, gu_bytes, uniques = [], [], []
+    for i in range(POOL):
+        api.moe_verify_stack(cfg, wts, xs[i], y, ws, y32=y32, debug=api.make_debug(n_unique=nu))
+        torch.cuda.synchronize()
+        U = nu.cpu().tolist()
+        uniques.append(U)
+        step_bytes.append(sum(api.moe_verify_weight_bytes(cfg, u, K) for u in U))
+        gu_bytes.append([gateup_bytes(shape, u, K) for u in U])
+    log("bench: unique experts per layer (mean) %.2f; bytes per step %.4f GB" % (
+        sum(map(sum, uniques)) / (POOL * L), sum(step_bytes) / POOL / 1e9))
+
+    graphs = [api.StackGraph(cfg, wts, xs[i], y, ws, y32=y32) for i in range(POOL)]
+    for s in range(args.warmup):
+        graphs[s % POOL].launch()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    evs[0].record(stream)
+    for s in range(args.steps):
+        graphs[s % POOL].launch()
+        evs[s + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    per_step_ms = [evs[s].elapsed_time(evs[s + 1]) for s in range(args.steps)]
+    total_ms = evs[0].elapsed_time(evs[-1])
+    total_bytes = sum(step_bytes[s % POOL] for s in range(args.steps))
+    gbs = total_bytes / (total_ms / 1e3) / 1e9
+    log("bench: %d steps in %.3f ms (wall %.3f ms): %.1f GB/s, %.1f us/stack" % (
+        args.steps, total_ms, wall * 1e3, gbs, total_ms / args.steps * 1e3))
+
+    # per-kernel timing pass: same inputs, kernels stamped by their own dispatch
+    kt = {"route": [], "gateup": [], "down": []}
+    gu_rates = []
+    for s in range(args.timing_steps):
+        ms = api.moe_verify_stack_timed(cfg, wts, xs[s % POOL], y, ws, y32=y32)
+        for l, (a, b, c) in enumerate(ms):
+            kt["route"].append(a); kt["gateup"].append(b); kt["down"].append(c)
+            gu_rates.append(gu_bytes[s % POOL][l])
+    avg = {k: sum(v) / len(v) for k, v in kt.items()}
+    gu_avg_bytes = sum(gu_rates) / len(gu_rates)
+    achieved = gu_avg_bytes / (avg["gateup"] / 1e3) / 1e9
+    log("bench: kernel averages (us): route %.2f gateup %.2f down %.2f; gateup %.1f GB/s" % (
+        avg["route"] * 1e3, avg["gateup"] * 1e3, avg["down"] * 1e3, achieved))
+
+    for g in graphs:
+        g.close()
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "40-layer NVFP4 MoE verify stack, K=2 rows", "hidden": shape.hidden,
+                   "experts": shape.n_experts, "top_k": shape.top_k, "inter": shape.inter,
+                   "shared_inter": shape.shared_inter, "layers": L, "rows": K, "input_pool": POOL,
+                   "weights": "NVFP4 (E2M1 + E4M3/16 + fp32 tensor scale), bf16 router/activations"},
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "us_per_stack": {"mean": round(total_ms / args.steps * 1e3, 2),
+                         "median": round(statistics.median(per_step_ms) * 1e3, 2),
+                         "min": round(min(per_step_ms) * 1e3, 2), "max": round(max(per_step_ms) * 1e3, 2)},
+        "bytes_per_step": round(sum(step_bytes) / POOL),
+        "unique_experts_per_layer": round(sum(map(sum, uniques)) / (POOL * L), 3),
+        "kernel_us": {k: round(v * 1e3, 3) for k, v in avg.items()},
+        "roofline": {"bound": "hbm", "kernel": "k_gateup", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": round(gu_avg_bytes)},
+        "wall_s": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle on the host (%.0f s budget)" % args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(layers, xs[0], shape, K, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

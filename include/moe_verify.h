@@ -1,0 +1,201 @@
+/*
+ * moe_verify.h -- C ABI of the MI355X (gfx950) block-verify MoE layer.
+ *
+ * What it computes.  One mixture-of-experts FFN layer of a target model that
+ * verifies K draft rows in one pass (speculative block verify).  Per layer:
+ *   1. router GEMV:  logits[r][e] = sum_h x[r][h] * Wr[e][h]   (bf16 in,
+ *      fp32 accumulate; routers stay bf16 -- mlxfast README, "Why this
+ *      challenge exists");
+ *   2. selection: top-k experts per row by key, ties to the lower expert
+ *      index; key = logit (softmax scoring) or fp32 sigmoid(logit) + bias
+ *      (the router tail of PR #844 section 4, item 3); mixture weights are
+ *      the softmax renormalised over the selected set, or the sigmoids
+ *      (renormalised when norm_topk) -- the bias only selects;
+ *   3. cross-row dedup: the distinct experts of all K*k slots, ascending,
+ *      with a CSR of their slots (PR #844 section 8 notes the stock gather
+ *      reads a repeated expert once per slot; here each is streamed once);
+ *   4. NVFP4 dequantisation inside the GEMM loops: W = e2m1(q) * e4m3(s) * ts
+ *      (README: expert projections are NVFP4 4-bit group-16);
+ *   5. gate/up GEMM + SwiGLU: h = silu(x Wg^T) * (x Wu^T), fp32;
+ *   6. down GEMM: o = h Wd^T, fp32;
+ *   7. shared expert: the same FFN on every row with weight 1 (ungated);
+ *   8. combine, in the order of PR #844 section 4 item 4 / section 5:
+ *        y[r] = routed_scale * sum_j w[r][j] * o[r][j]  + shared[r]
+ *               (+ residual[r])
+ *      summed over j in rank order (deterministic; no atomics).
+ *   9. stack glue: layer l+1 consumes bf16(RMSNorm(y_l)), eps = rms_eps,
+ *      gamma = 1, no residual; the stack returns the last layer's y.
+ *
+ * Conventions for every entry point.
+ *  - All array pointers are DEVICE pointers owned by the caller; the structs
+ *    themselves (moe_cfg, moe_layer_weights, moe_route_out, moe_debug) live
+ *    in host memory.  Arrays must be 16-byte aligned.
+ *  - bf16 values are passed as uint16_t bit patterns.
+ *  - NVFP4 matrix of `rows x cols` per expert (moe_nvfp4):
+ *      q  uint8 [E][rows][cols/2]  two E2M1 codes per byte; the even column
+ *                                  in the low nibble, the odd column in the
+ *                                  high nibble (sign = bit 3 of a nibble);
+ *      s  uint8 [E][rows][cols/16] OCP E4M3FN scale per 16 consecutive
+ *                                  columns of a row;
+ *      ts fp32  [E]                one tensor scale per expert matrix.
+ *    gate/up: rows = inter, cols = hidden;  down: rows = hidden, cols = inter.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and the call returns without synchronising.  Nothing is allocated on the
+ *    device: scratch lives in the caller's workspace.
+ *  - Return codes: MOE_OK, or a negative MOE_ERR_*; the thread-local text of
+ *    the last error is available from moe_verify_last_error().  There is no
+ *    silent fallback: an unsupported configuration is an error.
+ */
+#ifndef MOE_VERIFY_H
+#define MOE_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+#define MOE_OK 0
+#define MOE_ERR_INVALID (-1)      /* null/misaligned pointer, K out of range, bad enum */
+#define MOE_ERR_UNSUPPORTED (-2)  /* a shape this build does not implement */
+#define MOE_ERR_HIP (-3)          /* a HIP runtime call failed (text has hipGetErrorString) */
+#define MOE_ERR_WORKSPACE (-4)    /* workspace smaller than moe_verify_workspace_bytes() */
+
+#define MOE_SCORE_SOFTMAX 0       /* select on logits; weights = softmax over the selection */
+#define MOE_SCORE_SIGMOID_BIAS 1  /* select on fp32 sigmoid(logit) + bias; weights = sigmoid */
+
+typedef struct moe_nvfp4 {
+    const uint8_t* q;
+    const uint8_t* s;
+    const float* ts;
+} moe_nvfp4;
+
+typedef struct moe_cfg {
+    int32_t hidden;        /* H */
+    int32_t n_experts;     /* E routed experts */
+    int32_t top_k;         /* k */
+    int32_t inter;         /* I, routed expert intermediate */
+    int32_t shared_inter;  /* I_s of the one shared expert; 0 = none */
+    int32_t score_fn;      /* MOE_SCORE_* */
+    int32_t norm_topk;     /* 1 = divide the selected weights by their sum
+                              (required with MOE_SCORE_SOFTMAX) */
+    float routed_scale;    /* multiplies the weighted routed sum (2.5 on the
+                              pages' checkpoint, 1.0 for plain softmax MoE) */
+    float rms_eps;         /* RMSNorm epsilon between stacked layers */
+    int32_t max_rows;      /* largest K a workspace of this cfg serves */
+} moe_cfg;
+
+typedef struct moe_layer_weights {
+    const uint16_t* router_w;  /* bf16 [E][H] */
+    const float* router_bias;  /* fp32 [E]; required iff score_fn == SIGMOID_BIAS,
+                                  must be NULL otherwise */
+    moe_nvfp4 gate, up, down;  /* E experts */
+    moe_nvfp4 sh_gate, sh_up, sh_down;  /* one expert; all NULL iff shared_inter == 0 */
+} moe_layer_weights;
+
+/* Outputs of the selection step (device arrays, K = rows of the call):
+ *   ids [K][k] int32 selected experts in rank order; w [K][k] fp32 mixture
+ *   weights (routed_scale not folded in); n_unique [1]; uniq [K*k] distinct
+ *   experts ascending (first n_unique valid); off [K*k+1] CSR offsets
+ *   (first n_unique+1 valid); asg [K*k] flat slots r*k+j grouped by expert,
+ *   ascending within an expert; inv [K*k] position of each slot in asg. */
+typedef struct moe_route_out {
+    int32_t* ids;
+    float* w;
+    int32_t* n_unique;
+    int32_t* uniq;
+    int32_t* off;
+    int32_t* asg;
+    int32_t* inv;
+} moe_route_out;
+
+/* Optional per-layer copies of intermediates (device arrays, any may be
+ * NULL).  For a stack of L layers each array holds L consecutive per-layer
+ * blocks of the sizes in moe_route_out (logits: [K][E] fp32), plus
+ * x_in [K][H] bf16 (the layer's input) and y32 [K][H] fp32 (its output). */
+typedef struct moe_debug {
+    float* logits;
+    int32_t* ids;
+    float* w;
+    int32_t* n_unique;
+    int32_t* uniq;
+    int32_t* off;
+    int32_t* asg;
+    int32_t* inv;
+    uint16_t* x_in;
+    float* y32;
+} moe_debug;
+
+/* Bytes of device workspace that layer/stack/route calls with this cfg need
+ * (K <= cfg->max_rows).  0 if cfg is invalid (see moe_verify_last_error). */
+MOE_API size_t moe_verify_workspace_bytes(const moe_cfg* cfg);
+
+/* One layer (steps 1-8) on bf16 rows x [K][H].  residual (bf16 [K][H]) may be
+ * NULL.  Writes y bf16 [K][H] (round to nearest even of y32) and, if y32 is
+ * not NULL, the fp32 result.  dbg may be NULL. */
+MOE_API int moe_verify_layer(const moe_cfg* cfg, const moe_layer_weights* w, const uint16_t* x, int32_t K,
+                     const uint16_t* residual, uint16_t* y, float* y32, void* workspace,
+                     size_t workspace_bytes, void* stream, const moe_debug* dbg);
+
+/* n_layers layers (steps 1-9).  layers is a HOST array of n_layers weight
+ * structs.  Writes the last layer's output to y (bf16) and y32 (fp32, may be
+ * NULL).  dbg may be NULL. */
+MOE_API int moe_verify_stack(const moe_cfg* cfg, const moe_layer_weights* layers, int32_t n_layers,
+                     const uint16_t* x, int32_t K, uint16_t* y, float* y32, void* workspace,
+                     size_t workspace_bytes, void* stream, const moe_debug* dbg);
+
+/* Profiling aid: the work of moe_verify_stack (no debug copies), with each
+ * kernel launched so that a start/stop event pair carries that kernel's own
+ * dispatch timestamps.  Synchronises `stream`, then writes the durations in
+ * milliseconds to the HOST array kernel_ms[n_layers][3] (router + selection,
+ * gate/up + SwiGLU, down + combine). */
+MOE_API int moe_verify_stack_timed(const moe_cfg* cfg, const moe_layer_weights* layers, int32_t n_layers,
+                                   const uint16_t* x, int32_t K, uint16_t* y, float* y32, void* workspace,
+                                   size_t workspace_bytes, void* stream, float* kernel_ms);
+
+/* Selection only (steps 2-3) from given fp32 logits [K][E] (device), with
+ * the same device code the layer uses.  bias as in moe_layer_weights. */
+MOE_API int moe_verify_route(const moe_cfg* cfg, const float* logits, const float* bias, int32_t K,
+                     const moe_route_out* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Step 4 alone: dequantise n_experts expert matrices of rows x cols into
+ * fp32 out [E][rows][cols] with the decode the GEMM kernels use
+ * (e2m1 * e4m3 exactly, then one fp32 multiply by ts). */
+MOE_API int moe_verify_dequant_nvfp4(const moe_nvfp4* m, int32_t n_experts, int32_t rows, int32_t cols,
+                             float* out, void* stream);
+
+/* A captured stack launch (hipGraph).  It bakes in cfg, the weight pointers,
+ * K, x, y, y32 and the workspace; re-create it when any of them changes.
+ * A handle must not be launched from two threads at once. */
+typedef struct moe_stack_graph moe_stack_graph;
+MOE_API int moe_stack_graph_create(const moe_cfg* cfg, const moe_layer_weights* layers, int32_t n_layers,
+                           const uint16_t* x, int32_t K, uint16_t* y, float* y32, void* workspace,
+                           size_t workspace_bytes, void* stream, moe_stack_graph** out);
+MOE_API int moe_stack_graph_launch(moe_stack_graph* g, void* stream);
+MOE_API void moe_stack_graph_destroy(moe_stack_graph* g);
+
+/* Algorithmic HBM bytes of one layer step: the router (if with_router), each
+ * of n_unique routed experts once, the shared expert (if with_shared and
+ * cfg->shared_inter > 0), x in and y out (bf16, K rows).  NVFP4 matrices
+ * count codes + scales + the fp32 tensor scale. */
+MOE_API size_t moe_verify_weight_bytes(const moe_cfg* cfg, int32_t n_unique, int32_t K, int32_t with_shared,
+                               int32_t with_router);
+
+/* Text of the last error on this thread ("" if none). */
+MOE_API const char* moe_verify_last_error(void);
+
+/* ABI version (major * 100 + minor). */
+MOE_API int moe_verify_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_VERIFY_H */

@@ -1,0 +1,475 @@
+// C ABI of the NVFP4 MoE block-verify layer (include/moe_verify.h):
+// argument validation, workspace layout, kernel sequencing, graph capture.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/moe_verify.h"
+#include "moe_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------------------------
+// configuration checks
+// ---------------------------------------------------------------------------
+
+int check_inter(int I, int H, const char* name) {
+    if (I % 32 || !pow2(I / 32) || I / 32 > 64)
+        return fail(MOE_ERR_UNSUPPORTED, "%s=%d: need a power of two in [32, 2048]", name, I);
+    const int slab = moe::gateup_slab_rows(H);
+    if (I % slab) return fail(MOE_ERR_UNSUPPORTED, "%s=%d must be a multiple of %d at hidden=%d", name, I, slab, H);
+    return MOE_OK;
+}
+
+int check_cfg(const moe_cfg* c) {
+    if (!c) return fail(MOE_ERR_INVALID, "cfg is NULL");
+    if (c->hidden != 256 && c->hidden != 512 && c->hidden != 1024 && c->hidden != 2048)
+        return fail(MOE_ERR_UNSUPPORTED, "hidden=%d: supported 256, 512, 1024, 2048", c->hidden);
+    if (c->n_experts < 1 || c->n_experts > moe::kMaxExperts)
+        return fail(MOE_ERR_UNSUPPORTED, "n_experts=%d: supported 1..%d", c->n_experts, moe::kMaxExperts);
+    if (c->top_k < 1 || c->top_k > c->n_experts)
+        return fail(MOE_ERR_INVALID, "top_k=%d must be in [1, n_experts=%d]", c->top_k, c->n_experts);
+    if (c->top_k > moe::kMaxTopK) return fail(MOE_ERR_UNSUPPORTED, "top_k=%d > %d", c->top_k, moe::kMaxTopK);
+    int rc = check_inter(c->inter, c->hidden, "inter");
+    if (rc) return rc;
+    if (c->shared_inter < 0) return fail(MOE_ERR_INVALID, "shared_inter=%d < 0", c->shared_inter);
+    if (c->shared_inter > 0 && (rc = check_inter(c->shared_inter, c->hidden, "shared_inter"))) return rc;
+    if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID_BIAS)
+        return fail(MOE_ERR_INVALID, "score_fn=%d unknown", c->score_fn);
+    if (c->norm_topk != 0 && c->norm_topk != 1) return fail(MOE_ERR_INVALID, "norm_topk=%d not 0/1", c->norm_topk);
+    if (c->score_fn == MOE_SCORE_SOFTMAX && !c->norm_topk)
+        return fail(MOE_ERR_INVALID, "softmax scoring requires norm_topk=1");
+    if (!std::isfinite(c->routed_scale)) return fail(MOE_ERR_INVALID, "routed_scale not finite");
+    if (!(c->rms_eps >= 0.0f) || !std::isfinite(c->rms_eps)) return fail(MOE_ERR_INVALID, "rms_eps invalid");
+    if (c->max_rows < 1) return fail(MOE_ERR_INVALID, "max_rows=%d < 1", c->max_rows);
+    if (c->max_rows > moe::kMaxRows)
+        return fail(MOE_ERR_UNSUPPORTED, "max_rows=%d > %d (verify-width path)", c->max_rows, moe::kMaxRows);
+    return MOE_OK;
+}
+
+int check_mat(const moe_nvfp4& m, const char* name, int layer = 0) {
+    if (!m.q || !m.s || !m.ts) return fail(MOE_ERR_INVALID, "layer %d: %s has a NULL q/s/ts", layer, name);
+    if (!aligned16(m.q) || !aligned16(m.s) || !aligned16(m.ts))
+        return fail(MOE_ERR_INVALID, "layer %d: %s arrays must be 16-byte aligned", layer, name);
+    return MOE_OK;
+}
+
+int check_weights(const moe_cfg* c, const moe_layer_weights* w, int layer) {
+    if (!w) return fail(MOE_ERR_INVALID, "weights of layer %d are NULL", layer);
+    if (!w->router_w || !aligned16(w->router_w))
+        return fail(MOE_ERR_INVALID, "layer %d: router_w NULL or not 16-byte aligned", layer);
+    if (c->score_fn == MOE_SCORE_SIGMOID_BIAS && !w->router_bias)
+        return fail(MOE_ERR_INVALID, "layer %d: sigmoid scoring needs router_bias", layer);
+    if (c->score_fn == MOE_SCORE_SOFTMAX && w->router_bias)
+        return fail(MOE_ERR_INVALID, "layer %d: router_bias given with softmax scoring", layer);
+    int rc;
+    if ((rc = check_mat(w->gate, "gate", layer)) || (rc = check_mat(w->up, "up", layer)) ||
+        (rc = check_mat(w->down, "down", layer)))
+        return rc;
+    const bool any_sh = w->sh_gate.q || w->sh_up.q || w->sh_down.q;
+    if (c->shared_inter > 0) {
+        if ((rc = check_mat(w->sh_gate, "sh_gate", layer)) || (rc = check_mat(w->sh_up, "sh_up", layer)) ||
+            (rc = check_mat(w->sh_down, "sh_down", layer)))
+            return rc;
+    } else if (any_sh) {
+        return fail(MOE_ERR_INVALID, "layer %d: shared expert weights given with shared_inter=0", layer);
+    }
+    return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// workspace layout
+// ---------------------------------------------------------------------------
+
+struct Layout {
+    int32_t* meta;
+    float* logits;
+    int32_t* ids;
+    float* w;
+    int32_t* uniq;
+    int32_t* off;
+    int32_t* asg;
+    int32_t* inv;
+    float* h;
+    float* h_sh;
+    uint16_t* xbuf;
+    float* ybuf;
+    size_t bytes;
+};
+
+Layout layout(const moe_cfg* c, void* base) {
+    const size_t R = c->max_rows, E = c->n_experts, k = c->top_k, H = c->hidden;
+    const size_t I = c->inter, Is = c->shared_inter;
+    char* p = static_cast<char*>(base);
+    size_t o = 0;
+    Layout L{};
+    auto take = [&](size_t bytes) { char* r = p ? p + o : nullptr; o += align256(bytes); return r; };
+    L.meta = reinterpret_cast<int32_t*>(take(moe::kMetaWords * 4));
+    L.logits = reinterpret_cast<float*>(take(R * E * 4));
+    L.ids = reinterpret_cast<int32_t*>(take(R * k * 4));
+    L.w = reinterpret_cast<float*>(take(R * k * 4));
+    L.uniq = reinterpret_cast<int32_t*>(take(R * k * 4));
+    L.off = reinterpret_cast<int32_t*>(take((R * k + 1) * 4));
+    L.asg = reinterpret_cast<int32_t*>(take(R * k * 4));
+    L.inv = reinterpret_cast<int32_t*>(take(R * k * 4));
+    L.h = reinterpret_cast<float*>(take(R * k * I * 4));
+    L.h_sh = reinterpret_cast<float*>(take(R * (Is ? Is : 1) * 4));
+    L.xbuf = reinterpret_cast<uint16_t*>(take(R * H * 2));
+    L.ybuf = reinterpret_cast<float*>(take(R * H * 4));
+    L.bytes = o;
+    return L;
+}
+
+moe::Fp4Mat mat(const moe_nvfp4& m) { return moe::Fp4Mat{m.q, m.s, m.ts}; }
+
+// ---------------------------------------------------------------------------
+// one layer on the stream
+// ---------------------------------------------------------------------------
+
+struct LayerIO {
+    const uint16_t* x_in;    // bf16 input (first layer / single layer), or nullptr
+    const float* y_prev;     // fp32 output of the previous layer to normalise, or nullptr
+    const uint16_t* residual;
+    float* y32;              // fp32 output (required)
+    uint16_t* y;             // bf16 output or nullptr
+};
+
+int enqueue_layer(const moe_cfg* c, const moe_layer_weights* w, const LayerIO& io, int K, const Layout& L,
+                  hipStream_t st, const moe::Timing* tm = nullptr) {
+    hipError_t e;
+    moe::RouteArgs ra{};
+    ra.x_in = io.x_in;
+    ra.y_prev = io.y_prev;
+    ra.x_out = L.xbuf;
+    ra.eps = c->rms_eps;
+    ra.wr = w->router_w;
+    ra.bias = w->router_bias;
+    ra.logits = L.logits;
+    ra.ids = L.ids;
+    ra.w = L.w;
+    ra.meta = L.meta;
+    ra.n_unique = L.meta + moe::kMetaUnique;
+    ra.uniq = L.uniq;
+    ra.off = L.off;
+    ra.asg = L.asg;
+    ra.inv = L.inv;
+    ra.K = K; ra.H = c->hidden; ra.E = c->n_experts; ra.k = c->top_k;
+    ra.score_fn = c->score_fn; ra.norm_topk = c->norm_topk;
+    if ((e = moe::launch_route(ra, st, tm ? &tm[0] : nullptr)) != hipSuccess) return hip_fail(e, "route launch");
+
+    moe::GateUpArgs ga{};
+    ga.x = io.y_prev ? L.xbuf : io.x_in;
+    ga.gate = mat(w->gate); ga.up = mat(w->up);
+    ga.sgate = mat(w->sh_gate); ga.sup = mat(w->sh_up);
+    if (c->shared_inter == 0) { ga.sgate = moe::Fp4Mat{nullptr, nullptr, nullptr}; ga.sup = ga.sgate; }
+    ga.meta = L.meta;
+    ga.uniq = L.uniq; ga.off = L.off; ga.asg = L.asg;
+    ga.h = L.h; ga.h_sh = L.h_sh;
+    ga.K = K; ga.H = c->hidden; ga.I = c->inter; ga.Is = c->shared_inter; ga.k = c->top_k;
+    ga.slab = moe::gateup_slab_rows(c->hidden);
+    const int max_unique = std::min(c->n_experts, K * c->top_k);
+    if ((e = moe::launch_gateup(ga, max_unique, st, tm ? &tm[1] : nullptr)) != hipSuccess) return hip_fail(e, "gate/up launch");
+
+    moe::DownArgs da{};
+    da.down = mat(w->down);
+    da.sdown = c->shared_inter ? mat(w->sh_down) : moe::Fp4Mat{nullptr, nullptr, nullptr};
+    da.meta = L.meta;
+    da.uniq = L.uniq; da.off = L.off; da.inv = L.inv;
+    da.w = L.w; da.h = L.h; da.h_sh = L.h_sh;
+    da.residual = io.residual;
+    da.y32 = io.y32; da.y = io.y;
+    da.K = K; da.H = c->hidden; da.I = c->inter; da.Is = c->shared_inter; da.k = c->top_k;
+    da.rs = c->routed_scale;
+    if ((e = moe::launch_down(da, st, tm ? &tm[2] : nullptr)) != hipSuccess) return hip_fail(e, "down launch");
+    return MOE_OK;
+}
+
+int copy_debug(const moe_cfg* c, const moe_debug* d, int layer, int K, const Layout& L, const uint16_t* x_in,
+               const float* y32, hipStream_t st) {
+    if (!d) return MOE_OK;
+    const size_t E = c->n_experts, k = c->top_k, H = c->hidden, n = (size_t)K * k;
+    struct Item { void* dst; const void* src; size_t bytes; };
+    const Item items[] = {
+        {d->logits ? d->logits + layer * K * E : nullptr, L.logits, K * E * 4},
+        {d->ids ? d->ids + layer * n : nullptr, L.ids, n * 4},
+        {d->w ? d->w + layer * n : nullptr, L.w, n * 4},
+        {d->n_unique ? d->n_unique + layer : nullptr, L.meta + moe::kMetaUnique, 4},
+        {d->uniq ? d->uniq + layer * n : nullptr, L.uniq, n * 4},
+        {d->off ? d->off + layer * (n + 1) : nullptr, L.off, (n + 1) * 4},
+        {d->asg ? d->asg + layer * n : nullptr, L.asg, n * 4},
+        {d->inv ? d->inv + layer * n : nullptr, L.inv, n * 4},
+        {d->x_in ? d->x_in + layer * K * H : nullptr, x_in, K * H * 2},
+        {d->y32 ? d->y32 + layer * K * H : nullptr, y32, K * H * 4},
+    };
+    for (const Item& it : items) {
+        if (!it.dst) continue;
+        hipError_t e = hipMemcpyAsync(it.dst, it.src, it.bytes, hipMemcpyDeviceToDevice, st);
+        if (e != hipSuccess) return hip_fail(e, "debug copy");
+    }
+    return MOE_OK;
+}
+
+int check_common(const moe_cfg* c, int K, void* ws, size_t ws_bytes) {
+    int rc = check_cfg(c);
+    if (rc) return rc;
+    if (K < 1 || K > c->max_rows) return fail(MOE_ERR_INVALID, "K=%d outside [1, max_rows=%d]", K, c->max_rows);
+    const size_t need = layout(c, nullptr).bytes;
+    if (!ws) return fail(MOE_ERR_INVALID, "workspace is NULL");
+    if (!aligned16(ws)) return fail(MOE_ERR_INVALID, "workspace not 16-byte aligned");
+    if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    return MOE_OK;
+}
+
+int check_io(const void* x, const void* y, const void* y32, const void* residual) {
+    if (!x || !aligned16(x)) return fail(MOE_ERR_INVALID, "x NULL or not 16-byte aligned");
+    if (!y || !aligned16(y)) return fail(MOE_ERR_INVALID, "y NULL or not 16-byte aligned");
+    if (y32 && !aligned16(y32)) return fail(MOE_ERR_INVALID, "y32 not 16-byte aligned");
+    if (residual && !aligned16(residual)) return fail(MOE_ERR_INVALID, "residual not 16-byte aligned");
+    return MOE_OK;
+}
+
+int enqueue_stack(const moe_cfg* c, const moe_layer_weights* layers, int n_layers, const uint16_t* x, int K,
+                  uint16_t* y, float* y32, void* ws, hipStream_t st, const moe_debug* dbg,
+                  const moe::Timing* tm = nullptr) {
+    const Layout L = layout(c, ws);
+    hipError_t e = moe::init_kernels();
+    if (e != hipSuccess) return hip_fail(e, "kernel attributes");
+    if ((e = moe::launch_init(L.meta, st)) != hipSuccess) return hip_fail(e, "init launch");
+    for (int l = 0; l < n_layers; ++l) {
+        const bool last = (l == n_layers - 1);
+        LayerIO io{};
+        io.x_in = (l == 0) ? x : nullptr;
+        io.y_prev = (l == 0) ? nullptr : L.ybuf;
+        io.residual = nullptr;
+        io.y32 = last ? (y32 ? y32 : L.ybuf) : L.ybuf;
+        io.y = last ? y : nullptr;
+        int rc = enqueue_layer(c, &layers[l], io, K, L, st, tm ? tm + 3 * l : nullptr);
+        if (rc) return rc;
+        rc = copy_debug(c, dbg, l, K, L, l == 0 ? x : L.xbuf, io.y32, st);
+        if (rc) return rc;
+    }
+    return MOE_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// exported entry points
+// ---------------------------------------------------------------------------
+
+extern "C" {
+
+int moe_verify_version(void) { return 100; }
+
+const char* moe_verify_last_error(void) { return g_err.c_str(); }
+
+size_t moe_verify_workspace_bytes(const moe_cfg* cfg) {
+    if (check_cfg(cfg)) return 0;
+    return layout(cfg, nullptr).bytes;
+}
+
+size_t moe_verify_weight_bytes(const moe_cfg* c, int32_t n_unique, int32_t K, int32_t with_shared,
+                               int32_t with_router) {
+    if (check_cfg(c)) return 0;
+    auto matb = [](size_t rows, size_t cols) { return rows * cols / 2 + rows * cols / 16 + 4; };
+    const size_t H = c->hidden, I = c->inter, Is = c->shared_inter;
+    size_t b = (size_t)n_unique * (2 * matb(I, H) + matb(H, I));
+    if (with_shared && Is) b += 2 * matb(Is, H) + matb(H, Is);
+    if (with_router) b += 2 * (size_t)c->n_experts * H;
+    return b + 2 * 2 * (size_t)K * H;
+}
+
+int moe_verify_layer(const moe_cfg* cfg, const moe_layer_weights* w, const uint16_t* x, int32_t K,
+                     const uint16_t* residual, uint16_t* y, float* y32, void* workspace, size_t workspace_bytes,
+                     void* stream, const moe_debug* dbg) {
+    int rc;
+    if ((rc = check_common(cfg, K, workspace, workspace_bytes))) return rc;
+    if ((rc = check_weights(cfg, w, 0))) return rc;
+    if ((rc = check_io(x, y, y32, residual))) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Layout L = layout(cfg, workspace);
+    hipError_t e = moe::init_kernels();
+    if (e != hipSuccess) return hip_fail(e, "kernel attributes");
+    if ((e = moe::launch_init(L.meta, st)) != hipSuccess) return hip_fail(e, "init launch");
+    LayerIO io{};
+    io.x_in = x;
+    io.y_prev = nullptr;
+    io.residual = residual;
+    io.y32 = y32 ? y32 : L.ybuf;
+    io.y = y;
+    if ((rc = enqueue_layer(cfg, w, io, K, L, st))) return rc;
+    return copy_debug(cfg, dbg, 0, K, L, x, io.y32, st);
+}
+
+int moe_verify_stack(const moe_cfg* cfg, const moe_layer_weights* layers, int32_t n_layers, const uint16_t* x,
+                     int32_t K, uint16_t* y, float* y32, void* workspace, size_t workspace_bytes, void* stream,
+                     const moe_debug* dbg) {
+    int rc;
+    if ((rc = check_common(cfg, K, workspace, workspace_bytes))) return rc;
+    if (!layers || n_layers < 1) return fail(MOE_ERR_INVALID, "need n_layers >= 1 and a layer array");
+    for (int l = 0; l < n_layers; ++l)
+        if ((rc = check_weights(cfg, &layers[l], l))) return rc;
+    if ((rc = check_io(x, y, y32, nullptr))) return rc;
+    return enqueue_stack(cfg, layers, n_layers, x, K, y, y32, workspace, static_cast<hipStream_t>(stream), dbg);
+}
+
+int moe_verify_route(const moe_cfg* cfg, const float* logits, const float* bias, int32_t K,
+                     const moe_route_out* out, void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    int rc;
+    if ((rc = check_cfg(cfg))) return rc;
+    if (K < 1 || K > cfg->max_rows) return fail(MOE_ERR_INVALID, "K=%d outside [1, max_rows=%d]", K, cfg->max_rows);
+    if (!logits || !aligned16(logits)) return fail(MOE_ERR_INVALID, "logits NULL or not 16-byte aligned");
+    if (cfg->score_fn == MOE_SCORE_SIGMOID_BIAS && !bias) return fail(MOE_ERR_INVALID, "sigmoid scoring needs bias");
+    if (cfg->score_fn == MOE_SCORE_SOFTMAX && bias) return fail(MOE_ERR_INVALID, "bias given with softmax scoring");
+    if (!out || !out->ids || !out->w || !out->n_unique || !out->uniq || !out->off || !out->asg || !out->inv)
+        return fail(MOE_ERR_INVALID, "route outputs must all be non-NULL");
+    moe::RouteArgs ra{};
+    ra.bias = bias;
+    ra.logits = const_cast<float*>(logits);
+    ra.ids = out->ids; ra.w = out->w; ra.n_unique = out->n_unique;
+    ra.uniq = out->uniq; ra.off = out->off; ra.asg = out->asg; ra.inv = out->inv;
+    ra.K = K; ra.H = cfg->hidden; ra.E = cfg->n_experts; ra.k = cfg->top_k;
+    ra.score_fn = cfg->score_fn; ra.norm_topk = cfg->norm_topk;
+    hipError_t e = moe::launch_select(ra, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "select launch");
+    return MOE_OK;
+}
+
+int moe_verify_dequant_nvfp4(const moe_nvfp4* m, int32_t n_experts, int32_t rows, int32_t cols, float* out,
+                             void* stream) {
+    if (!m) return fail(MOE_ERR_INVALID, "matrix is NULL");
+    int rc = check_mat(*m, "matrix");
+    if (rc) return rc;
+    if (!out || !aligned16(out)) return fail(MOE_ERR_INVALID, "out NULL or not 16-byte aligned");
+    if (n_experts < 1 || rows < 1 || cols < 32 || cols % 32)
+        return fail(MOE_ERR_INVALID, "need n_experts, rows >= 1 and cols a positive multiple of 32");
+    hipError_t e = moe::launch_dequant(mat(*m), n_experts, rows, cols, out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "dequant launch");
+    return MOE_OK;
+}
+
+int moe_verify_stack_timed(const moe_cfg* cfg, const moe_layer_weights* layers, int32_t n_layers,
+                           const uint16_t* x, int32_t K, uint16_t* y, float* y32, void* workspace,
+                           size_t workspace_bytes, void* stream, float* kernel_ms) {
+    int rc;
+    if ((rc = check_common(cfg, K, workspace, workspace_bytes))) return rc;
+    if (!layers || n_layers < 1) return fail(MOE_ERR_INVALID, "need n_layers >= 1 and a layer array");
+    if (!kernel_ms) return fail(MOE_ERR_INVALID, "kernel_ms is NULL");
+    for (int l = 0; l < n_layers; ++l)
+        if ((rc = check_weights(cfg, &layers[l], l))) return rc;
+    if ((rc = check_io(x, y, y32, nullptr))) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int n_ev = 3 * n_layers;
+    moe::Timing* tm = new moe::Timing[n_ev]();
+    hipError_t e = hipSuccess;
+    int made = 0;
+    for (; made < n_ev; ++made) {
+        if ((e = hipEventCreate(&tm[made].start)) != hipSuccess) break;
+        if ((e = hipEventCreate(&tm[made].stop)) != hipSuccess) {
+            (void)hipEventDestroy(tm[made].start);
+            break;
+        }
+    }
+    if (e == hipSuccess) {
+        rc = enqueue_stack(cfg, layers, n_layers, x, K, y, y32, workspace, st, nullptr, tm);
+        if (!rc && (e = hipStreamSynchronize(st)) != hipSuccess) rc = hip_fail(e, "synchronize");
+        for (int i = 0; !rc && i < n_ev; ++i) {
+            float ms = 0.0f;
+            if ((e = hipEventElapsedTime(&ms, tm[i].start, tm[i].stop)) != hipSuccess) rc = hip_fail(e, "elapsed time");
+            kernel_ms[i] = ms;
+        }
+    } else {
+        rc = hip_fail(e, "event create");
+    }
+    for (int i = 0; i < made; ++i) {
+        (void)hipEventDestroy(tm[i].start);
+        (void)hipEventDestroy(tm[i].stop);
+    }
+    delete[] tm;
+    return rc;
+}
+
+struct moe_stack_graph {
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+};
+
+int moe_stack_graph_create(const moe_cfg* cfg, const moe_layer_weights* layers, int32_t n_layers,
+                           const uint16_t* x, int32_t K, uint16_t* y, float* y32, void* workspace,
+                           size_t workspace_bytes, void* stream, moe_stack_graph** out) {
+    int rc;
+    if (!out) return fail(MOE_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    if ((rc = check_common(cfg, K, workspace, workspace_bytes))) return rc;
+    if (!layers || n_layers < 1) return fail(MOE_ERR_INVALID, "need n_layers >= 1 and a layer array");
+    for (int l = 0; l < n_layers; ++l)
+        if ((rc = check_weights(cfg, &layers[l], l))) return rc;
+    if ((rc = check_io(x, y, y32, nullptr))) return rc;
+    hipError_t e = moe::init_kernels();
+    if (e != hipSuccess) return hip_fail(e, "kernel attributes");
+    hipStream_t cap;
+    if ((e = hipStreamCreateWithFlags(&cap, hipStreamNonBlocking)) != hipSuccess) return hip_fail(e, "stream create");
+    (void)stream;
+    if ((e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal)) != hipSuccess) {
+        (void)hipStreamDestroy(cap);
+        return hip_fail(e, "begin capture");
+    }
+    rc = enqueue_stack(cfg, layers, n_layers, x, K, y, y32, workspace, cap, nullptr);
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(cap, &graph);
+    (void)hipStreamDestroy(cap);
+    if (rc) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return rc;
+    }
+    if (e != hipSuccess) return hip_fail(e, "end capture");
+    hipGraphExec_t exec;
+    if ((e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0)) != hipSuccess) {
+        (void)hipGraphDestroy(graph);
+        return hip_fail(e, "graph instantiate");
+    }
+    moe_stack_graph* g = new moe_stack_graph{graph, exec};
+    *out = g;
+    return MOE_OK;
+}
+
+int moe_stack_graph_launch(moe_stack_graph* g, void* stream) {
+    if (!g) return fail(MOE_ERR_INVALID, "graph is NULL");
+    hipError_t e = hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "graph launch");
+    return MOE_OK;
+}
+
+void moe_stack_graph_destroy(moe_stack_graph* g) {
+    if (!g) return;
+    (void)hipGraphExecDestroy(g->exec);
+    (void)hipGraphDestroy(g->graph);
+    delete g;
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Internal interface between the C ABI (moe_abi.hip) and the gfx950 kernels
+// (moe_kernels.hip).  Not installed; the public surface is include/moe_verify.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Compile-time limits of the skinny (verify-width) path.
+constexpr int kMaxRows = 16;       // K
+constexpr int kMaxTopK = 32;       // k
+constexpr int kMaxExperts = 1024;  // E
+constexpr int kBlock = 256;        // threads per workgroup (4 wave64)
+constexpr int kWaves = kBlock / 64;
+constexpr int kRowsPerWave = 4;    // weight rows each wave keeps in flight in gate/up
+constexpr int kDownRowsPerBlock = 8;
+
+struct Fp4Mat {
+    const uint8_t* q;
+    const uint8_t* s;
+    const float* ts;
+};
+
+// Route metadata words kept in the workspace.
+enum MetaWord { kMetaUnique = 0, kMetaCounter = 1, kMetaWords = 16 };
+
+struct RouteArgs {
+    const uint16_t* x_in;   // bf16 [K][H], read when y_prev == nullptr
+    const float* y_prev;    // fp32 [K][H] to RMS-normalise into x, or nullptr
+    uint16_t* x_out;        // bf16 [K][H] normalised x (written when y_prev != nullptr)
+    float eps;
+    const uint16_t* wr;     // bf16 [E][H]
+    const float* bias;      // [E] or nullptr
+    float* logits;          // [K][E]
+    int32_t* ids;           // [K][k]
+    float* w;               // [K][k]
+    int32_t* meta;          // MetaWord (route counter)
+    int32_t* n_unique;      // [1] number of distinct experts
+    int32_t* uniq;          // [K*k]
+    int32_t* off;           // [K*k+1]
+    int32_t* asg;           // [K*k]
+    int32_t* inv;           // [K*k]
+    int K, H, E, k, score_fn, norm_topk;
+};
+
+struct GateUpArgs {
+    const uint16_t* x;      // bf16 [K][H]
+    Fp4Mat gate, up;        // [E][I][H/2]
+    Fp4Mat sgate, sup;      // [1][Is][H/2] (q == nullptr: no shared expert)
+    const int32_t* meta;
+    const int32_t* uniq;
+    const int32_t* off;
+    const int32_t* asg;
+    float* h;               // [K*k][I], indexed by position in asg
+    float* h_sh;            // [K][Is]
+    int K, H, I, Is, k;
+    int slab;               // weight rows (of gate and of up) per workgroup
+};
+
+struct DownArgs {
+    Fp4Mat down;            // [E][H][I/2]
+    Fp4Mat sdown;           // [1][H][Is/2]
+    const int32_t* meta;
+    const int32_t* uniq;
+    const int32_t* off;
+    const int32_t* inv;
+    const float* w;         // [K][k]
+    const float* h;
+    const float* h_sh;
+    const uint16_t* residual;  // bf16 [K][H] or nullptr
+    float* y32;             // [K][H]
+    uint16_t* y;            // bf16 [K][H] or nullptr
+    int K, H, I, Is, k;
+    float rs;
+};
+
+// Optional kernel timing: start/stop events stamped from the kernel's own
+// dispatch (hipExtLaunchKernelGGL); nullptr = plain launch.
+struct Timing {
+    hipEvent_t start;
+    hipEvent_t stop;
+};
+
+// Launchers (moe_kernels.hip).  Each returns the hipError_t of the launch.
+hipError_t launch_init(int32_t* meta, hipStream_t st);
+hipError_t launch_route(const RouteArgs& a, hipStream_t st, const Timing* t = nullptr);
+hipError_t launch_select(const RouteArgs& a, hipStream_t st);  // logits given
+hipError_t launch_gateup(const GateUpArgs& a, int max_unique, hipStream_t st, const Timing* t = nullptr);
+hipError_t launch_down(const DownArgs& a, hipStream_t st, const Timing* t = nullptr);
+hipError_t launch_dequant(Fp4Mat m, int n_experts, int rows, int cols, float* out, hipStream_t st);
+
+// One-time kernel attributes (dynamic LDS above 64 KiB for the router).
+hipError_t init_kernels();
+
+// Workgroups / slab size the gate/up launch uses for hidden H.
+int gateup_slab_rows(int H);
+
+}  // namespace moe

@@ -1,0 +1,711 @@
+// gfx950 (CDNA4) kernels of the NVFP4 MoE block-verify layer.
+//
+// Per layer three launches:
+//   k_route   router GEMV (one wave per expert row, bf16 x staged in LDS,
+//             v_dot2_f32_bf16), then the last workgroup to finish selects
+//             top-k per row with a DPP wave argmax and builds the dedup CSR
+//             (PR #844 section 4 item 3 router tail; section 8: the stock
+//             gather reads a repeated expert once per slot -- here each
+//             unique expert is streamed once);
+//   k_gateup  one workgroup per (unique expert, slab of intermediate rows):
+//             128-bit loads of packed E2M1 codes, in-register decode with
+//             v_cvt_scalef32_pk_bf16_fp4, dot2 against x held in registers,
+//             E4M3 block scale per 16 columns, tensor scale after the lane
+//             reduction, SwiGLU epilogue (silu(gate) * up, PR #844 section 4
+//             item 1) writing fp32 h;
+//   k_down    one workgroup per 8 output rows: every unique expert's down
+//             rows for that slab (fp32 decode, fp32 h), per-slot partials
+//             in LDS, then the deterministic combine
+//             y = rs * sum_j w_j o_j + shared (+ residual) in rank order
+//             (PR #844 section 4 item 4 and section 5 expression order).
+// The routed work list is data dependent (the number of unique experts is
+// known only on the device), so the gate/up grid is sized for the largest
+// possible count and surplus workgroups exit at once.
+#include <hip/hip_ext.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// scalar helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Order-preserving map of a float key onto uint32 (larger float -> larger
+// integer; -0 and +0 map together).  Real keys never map to 0, which marks
+// an empty or already-taken entry.
+__device__ __forceinline__ uint32_t key_bits(float f) {
+    uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// E4M3FN byte -> fp32 (gfx950 converts OCP FP8 natively).
+template <int SEL>
+__device__ __forceinline__ float e4m3_to_f32(uint32_t packed) {
+    return __builtin_amdgcn_cvt_f32_fp8((int)packed, SEL);
+}
+
+// Eight E2M1 codes (one dword, column 2t in the low nibble of byte t) ->
+// four bf16 pairs (exact: every E2M1 value is a bf16).
+__device__ __forceinline__ void fp4x8_to_bf16(uint32_t v, bf16x2_t* out) {
+    out[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 0);
+    out[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 1);
+    out[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 2);
+    out[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 3);
+}
+
+__device__ __forceinline__ void fp4x8_to_f32(uint32_t v, float* out) {
+    f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 0);
+    f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 1);
+    f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 2);
+    f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 3);
+    out[0] = p0.x; out[1] = p0.y; out[2] = p1.x; out[3] = p1.y;
+    out[4] = p2.x; out[5] = p2.y; out[6] = p3.x; out[7] = p3.y;
+}
+
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
+
+__device__ __forceinline__ float dot2(bf16x2_t a, bf16x2_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+
+// ---------------------------------------------------------------------------
+// cross-lane helpers (wave64).  DPP row shifts accumulate inside 16-lane
+// rows; readlane combines the four rows.  Summation order is fixed, so every
+// result is deterministic.
+// ---------------------------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+    return __int_as_float(dpp<CTRL>(__float_as_int(v)));
+}
+__device__ __forceinline__ float readlanef(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// inclusive prefix sum inside each 16-lane row
+__device__ __forceinline__ float row_scan(float v) {
+    v += dppf<0x111>(v);
+    v += dppf<0x112>(v);
+    v += dppf<0x114>(v);
+    v += dppf<0x118>(v);
+    return v;
+}
+__device__ __forceinline__ int row_scan_i(int v) {
+    v += dpp<0x111>(v);
+    v += dpp<0x112>(v);
+    v += dpp<0x114>(v);
+    v += dpp<0x118>(v);
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row_scan(v);
+    return (readlanef(v, 15) + readlanef(v, 31)) + (readlanef(v, 47) + readlanef(v, 63));
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int lane = threadIdx.x & 63;
+    v = row_scan_i(v);
+    const int t0 = __builtin_amdgcn_readlane(v, 15);
+    const int t1 = __builtin_amdgcn_readlane(v, 31);
+    const int t2 = __builtin_amdgcn_readlane(v, 47);
+    if (lane >= 16) v += t0;
+    if (lane >= 32) v += t1;
+    if (lane >= 48) v += t2;
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)dpp<0x111>((int)v));
+    v = max(v, (uint32_t)dpp<0x112>((int)v));
+    v = max(v, (uint32_t)dpp<0x114>((int)v));
+    v = max(v, (uint32_t)dpp<0x118>((int)v));
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+    return max(max(a, b), max(c, d));
+}
+
+// Sum over aligned groups of G lanes; valid in the last lane of each group.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (G == 64) {
+        return wave_sum(v);
+    } else if constexpr (G == 32) {
+        v = row_scan(v);
+        const float lo = readlanef(v, 15) + readlanef(v, 31);
+        const float hi = readlanef(v, 47) + readlanef(v, 63);
+        return (threadIdx.x & 32) ? hi : lo;
+    } else if constexpr (G == 16) {
+        return row_scan(v);
+    } else {
+#pragma unroll
+        for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+        return v;
+    }
+}
+
+__device__ __forceinline__ float group_sum_rt(float v, int G) {
+    switch (G) {
+        case 64: return group_sum<64>(v);
+        case 32: return group_sum<32>(v);
+        case 16: return group_sum<16>(v);
+        case 8: return group_sum<8>(v);
+        case 4: return group_sum<4>(v);
+        default: return group_sum<2>(v);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// selection + dedup (one workgroup)
+// ---------------------------------------------------------------------------
+
+struct SelectSmem {
+    int32_t sel[kMaxRows * kMaxTopK];
+    float w[kMaxRows * kMaxTopK];
+    int32_t cnt[kMaxExperts];
+    int32_t start[kMaxExperts];
+};
+
+// Top-k of row r by (key desc, index asc) with one wave.  Lane l owns experts
+// l*P .. l*P+P-1 (contiguous), so among equal keys the lowest lane holding
+// the maximum also holds the lowest index.
+__device__ void wave_select_row(const RouteArgs& a, const float* logits, int r, SelectSmem& sm) {
+    const int lane = threadIdx.x & 63;
+    const int E = a.E, k = a.k;
+    const int P = (E + 63) >> 6;
+    const float* lr = logits + (size_t)r * E;
+    uint32_t kv[kMaxExperts / 64];
+#pragma unroll
+    for (int p = 0; p < kMaxExperts / 64; ++p) {
+        const int e = lane * P + p;
+        uint32_t v = 0;
+        if (p < P && e < E) {
+            const float l = lr[e];
+            float key = l;
+            if (a.score_fn == 1) {
+                const float sig = (float)(1.0 / (1.0 + exp(-(double)l)));
+                key = sig + a.bias[e];
+            }
+            v = key_bits(key);
+        }
+        kv[p] = v;
+    }
+    uint32_t best = 0;
+    int bi = 0;
+#pragma unroll
+    for (int p = 0; p < kMaxExperts / 64; ++p)
+        if (kv[p] > best) { best = kv[p]; bi = p; }
+
+    int mine = 0;
+    for (int j = 0; j < k; ++j) {
+        const uint32_t m = wave_max_u32(best);
+        const unsigned long long mask = __ballot(best == m);
+        const int L = __builtin_ctzll(mask);
+        const int e = L * P + __builtin_amdgcn_readlane(bi, L);
+        if (lane == j) mine = e;
+        if (lane == L) {
+#pragma unroll
+            for (int p = 0; p < kMaxExperts / 64; ++p)
+                if (p == bi) kv[p] = 0;
+            best = 0; bi = 0;
+#pragma unroll
+            for (int p = 0; p < kMaxExperts / 64; ++p)
+                if (kv[p] > best) { best = kv[p]; bi = p; }
+        }
+    }
+    // mixture weights over the selection (routed scale not folded in)
+    const float l = (lane < k) ? lr[mine] : 0.0f;
+    float wv;
+    if (a.score_fn == 0) {
+        const float lmax = readlanef(l, 0);  // rank 0 holds the largest logit
+        const float ex = (lane < k) ? expf(l - lmax) : 0.0f;
+        const float s = wave_sum(ex);
+        wv = ex / s;
+    } else {
+        const float sg = (lane < k) ? (float)(1.0 / (1.0 + exp(-(double)l))) : 0.0f;
+        if (a.norm_topk) {
+            const float s = wave_sum(sg);
+            wv = sg / s;
+        } else {
+            wv = sg;
+        }
+    }
+    if (lane < k) {
+        sm.sel[r * k + lane] = mine;
+        sm.w[r * k + lane] = wv;
+    }
+}
+
+// All rows' top-k, then the canonical dedup CSR.  Called by a whole
+// workgroup; logits may be global memory.
+__device__ void select_and_dedup(const RouteArgs& a, const float* logits, int32_t* n_unique_out,
+                                 SelectSmem& sm) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int K = a.K, k = a.k, E = a.E, n = K * k;
+    for (int r = wave; r < K; r += kWaves) wave_select_row(a, logits, r, sm);
+    for (int e = tid; e < E; e += kBlock) sm.cnt[e] = 0;
+    __syncthreads();
+    for (int s = tid; s < n; s += kBlock) atomicAdd(&sm.cnt[sm.sel[s]], 1);
+    __syncthreads();
+    if (wave == 0) {
+        const int Q = (E + 63) >> 6;
+        int c = 0, f = 0;
+        for (int q = 0; q < Q; ++q) {
+            const int e = lane * Q + q;
+            if (e < E) { c += sm.cnt[e]; f += (sm.cnt[e] > 0); }
+        }
+        const int ci = wave_incl_scan(c), fi = wave_incl_scan(f);
+        int cs = ci - c, fs = fi - f;
+        for (int q = 0; q < Q; ++q) {
+            const int e = lane * Q + q;
+            if (e < E) {
+                const int cn = sm.cnt[e];
+                sm.start[e] = cs;
+                if (cn) { a.uniq[fs] = e; a.off[fs] = cs; }
+                cs += cn;
+                fs += (cn > 0);
+            }
+        }
+        const int U = __builtin_amdgcn_readlane(fi, 63);
+        if (lane == 0) { *n_unique_out = U; a.off[U] = n; }
+    }
+    __syncthreads();
+    for (int s = tid; s < n; s += kBlock) {
+        const int e = sm.sel[s];
+        int rank = 0;
+        for (int t = 0; t < s; ++t) rank += (sm.sel[t] == e);
+        const int pos = sm.start[e] + rank;
+        a.asg[pos] = s;
+        a.inv[s] = pos;
+        a.ids[s] = e;
+        a.w[s] = sm.w[s];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_init: clear the route counter at the start of every call
+// ---------------------------------------------------------------------------
+
+__global__ void k_init(int32_t* meta) {
+    if (threadIdx.x < kMetaWords) meta[threadIdx.x] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// k_route
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kBlock) void k_route(RouteArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+    __shared__ float s_inv[kMaxRows];
+    __shared__ int s_last;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int K = a.K, H = a.H, E = a.E;
+    const int KH = K * H;
+
+    // 1. bf16 x into LDS (RMS-normalised from the previous layer's fp32
+    //    output when chaining layers)
+    if (a.y_prev) {
+        for (int r = wave; r < K; r += kWaves) {
+            const float* yr = a.y_prev + (size_t)r * H;
+            float ss = 0.0f;
+            for (int h = lane; h < H; h += 64) ss = fmaf(yr[h], yr[h], ss);
+            ss = wave_sum(ss);
+            if (lane == 0) s_inv[r] = 1.0f / sqrtf(ss / (float)H + a.eps);
+        }
+        __syncthreads();
+        for (int i = tid; i < KH; i += kBlock) xs[i] = f32_to_bf16_rne(a.y_prev[i] * s_inv[i / H]);
+        __syncthreads();
+        // each workgroup publishes its share of the normalised x
+        const int per = (KH / 8 + gridDim.x - 1) / gridDim.x * 8;
+        const int i0 = blockIdx.x * per;
+        for (int i = i0 + tid * 8; i < min(KH, i0 + per); i += kBlock * 8)
+            *reinterpret_cast<uint4*>(a.x_out + i) = *reinterpret_cast<const uint4*>(xs + i);
+    } else {
+        for (int i = tid * 8; i < KH; i += kBlock * 8)
+            *reinterpret_cast<uint4*>(xs + i) = *reinterpret_cast<const uint4*>(a.x_in + i);
+        __syncthreads();
+    }
+
+    // 2. one wave per expert row: logits[r][e] = x_r . Wr[e]
+    const int e = blockIdx.x * kWaves + wave;
+    if (e < E) {
+        float acc[kMaxRows];
+#pragma unroll
+        for (int r = 0; r < kMaxRows; ++r) acc[r] = 0.0f;
+        const uint16_t* wrow = a.wr + (size_t)e * H;
+        for (int p = lane * 8; p < H; p += 512) {
+            const uint4 wv = *reinterpret_cast<const uint4*>(wrow + p);
+#pragma unroll
+            for (int r = 0; r < kMaxRows; ++r) {
+                if (r < K) {
+                    const uint4 xv = *reinterpret_cast<const uint4*>(xs + r * H + p);
+                    float s = acc[r];
+                    s = dot2(as_bf16x2(wv.x), as_bf16x2(xv.x), s);
+                    s = dot2(as_bf16x2(wv.y), as_bf16x2(xv.y), s);
+                    s = dot2(as_bf16x2(wv.z), as_bf16x2(xv.z), s);
+                    s = dot2(as_bf16x2(wv.w), as_bf16x2(xv.w), s);
+                    acc[r] = s;
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kMaxRows; ++r) {
+            if (r < K) {
+                const float t = wave_sum(acc[r]);
+                if (lane == 0) a.logits[(size_t)r * E + e] = t;
+            }
+        }
+    }
+
+    // 3. the last workgroup to finish selects and deduplicates
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = (atomicAdd(&a.meta[kMetaCounter], 1) == (int)gridDim.x - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    SelectSmem& sm = *reinterpret_cast<SelectSmem*>(smem);
+    select_and_dedup(a, a.logits, a.n_unique, sm);
+    if (tid == 0) a.meta[kMetaCounter] = 0;
+}
+
+// Selection from caller-provided logits (one workgroup).
+__global__ __launch_bounds__(kBlock) void k_select(RouteArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    SelectSmem& sm = *reinterpret_cast<SelectSmem*>(smem);
+    select_and_dedup(a, a.logits, a.n_unique, sm);
+}
+
+// ---------------------------------------------------------------------------
+// k_gateup
+// ---------------------------------------------------------------------------
+
+template <int MAXM>
+__global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int H = a.H;
+    const int U = a.meta[kMetaUnique];
+    const int nsr = a.I / a.slab;
+    int b = blockIdx.x;
+
+    const uint8_t *gq, *gs, *uq, *us;
+    float gts, uts;
+    float* hbase;
+    int hstride, m_cnt, n0, rows_total;
+    int rowsel[MAXM];
+    if (b < U * nsr) {
+        const int u = b / nsr;
+        const int e = a.uniq[u];
+        const int o0 = a.off[u];
+        m_cnt = a.off[u + 1] - o0;
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) rowsel[m] = (m < m_cnt) ? a.asg[o0 + m] / a.k : 0;
+        rows_total = a.I;
+        gq = a.gate.q + (size_t)e * rows_total * (H / 2);
+        gs = a.gate.s + (size_t)e * rows_total * (H / 16);
+        uq = a.up.q + (size_t)e * rows_total * (H / 2);
+        us = a.up.s + (size_t)e * rows_total * (H / 16);
+        gts = a.gate.ts[e];
+        uts = a.up.ts[e];
+        hbase = a.h + (size_t)o0 * a.I;
+        hstride = a.I;
+        n0 = (b % nsr) * a.slab;
+    } else {
+        b -= U * nsr;
+        if (a.sgate.q == nullptr || b >= a.Is / a.slab) return;
+        m_cnt = a.K;
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) rowsel[m] = (m < m_cnt) ? m : 0;
+        rows_total = a.Is;
+        gq = a.sgate.q; gs = a.sgate.s; uq = a.sup.q; us = a.sup.s;
+        gts = a.sgate.ts[0];
+        uts = a.sup.ts[0];
+        hbase = a.h_sh;
+        hstride = a.Is;
+        n0 = b * a.slab;
+    }
+
+    // lane -> (row inside a wave load, 32-column chunk)
+    const int CPR = H >> 5;          // chunks (16 code bytes) per weight row
+    const int RPW = 64 / CPR;        // weight rows per wave load
+    const int q = lane / CPR, chunk = lane % CPR;
+
+    // weight codes first: every load this wave issues is in flight at once
+    uint4 gc[kRowsPerWave], uc[kRowsPerWave];
+    uint32_t gsc[kRowsPerWave], usc[kRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+        const int n = n0 + (wave * kRowsPerWave + i) * RPW + q;
+        gc[i] = *reinterpret_cast<const uint4*>(gq + (size_t)n * (H / 2) + chunk * 16);
+        uc[i] = *reinterpret_cast<const uint4*>(uq + (size_t)n * (H / 2) + chunk * 16);
+        gsc[i] = *reinterpret_cast<const uint16_t*>(gs + (size_t)n * (H / 16) + chunk * 2);
+        usc[i] = *reinterpret_cast<const uint16_t*>(us + (size_t)n * (H / 16) + chunk * 2);
+    }
+    // this lane's 32 columns of every assigned row of x, as bf16 pairs
+    uint32_t xr[MAXM][16];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+        if (m < m_cnt) {
+            const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)rowsel[m] * H + chunk * 32);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint4 v = src[t];
+                xr[m][4 * t + 0] = v.x; xr[m][4 * t + 1] = v.y;
+                xr[m][4 * t + 2] = v.z; xr[m][4 * t + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 16; ++t) xr[m][t] = 0u;
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+        const int n = n0 + (wave * kRowsPerWave + i) * RPW + q;
+        bf16x2_t wg[16], wu[16];
+        fp4x8_to_bf16(gc[i].x, wg + 0); fp4x8_to_bf16(gc[i].y, wg + 4);
+        fp4x8_to_bf16(gc[i].z, wg + 8); fp4x8_to_bf16(gc[i].w, wg + 12);
+        fp4x8_to_bf16(uc[i].x, wu + 0); fp4x8_to_bf16(uc[i].y, wu + 4);
+        fp4x8_to_bf16(uc[i].z, wu + 8); fp4x8_to_bf16(uc[i].w, wu + 12);
+        const float sg0 = e4m3_to_f32<0>(gsc[i]), sg1 = e4m3_to_f32<1>(gsc[i]);
+        const float su0 = e4m3_to_f32<0>(usc[i]), su1 = e4m3_to_f32<1>(usc[i]);
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            if (m < m_cnt) {
+                float g0 = 0.f, g1 = 0.f, v0 = 0.f, v1 = 0.f;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    g0 = dot2(wg[t], as_bf16x2(xr[m][t]), g0);
+                    v0 = dot2(wu[t], as_bf16x2(xr[m][t]), v0);
+                    g1 = dot2(wg[t + 8], as_bf16x2(xr[m][t + 8]), g1);
+                    v1 = dot2(wu[t + 8], as_bf16x2(xr[m][t + 8]), v1);
+                }
+                float pg = fmaf(g1, sg1, g0 * sg0);
+                float pu = fmaf(v1, su1, v0 * su0);
+                pg = group_sum_rt(pg, CPR);
+                pu = group_sum_rt(pu, CPR);
+                if (chunk == CPR - 1) {
+                    const float g = pg * gts, v = pu * uts;
+                    hbase[(size_t)m * hstride + n] = g / (1.0f + expf(-g)) * v;
+                }
+            }
+        }
+    }
+    (void)rows_total;
+}
+
+// ---------------------------------------------------------------------------
+// k_down (+ combine)
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kBlock) void k_down(DownArgs a) {
+    constexpr int NH = kDownRowsPerBlock;
+    __shared__ float so[(kMaxRows * kMaxTopK + kMaxRows) * NH];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int H = a.H, K = a.K, k = a.k;
+    const int U = a.meta[kMetaUnique];
+    const int n_base = blockIdx.x * NH;
+    const bool has_sh = a.sdown.q != nullptr;
+
+    const int cprI = a.I >> 5;
+    const int gI = max(1, NH / (64 / cprI));
+    const int cprS = has_sh ? (a.Is >> 5) : 1;
+    const int gS = has_sh ? max(1, NH / (64 / cprS)) : 0;
+    const int total = U * gI + gS;
+
+    for (int t = wave; t < total; t += kWaves) {
+        int cols, CPR, grp, m_cnt, e;
+        const float* hsrc;
+        float* obase;
+        const Fp4Mat* mat;
+        if (t < U * gI) {
+            const int u = t / gI;
+            grp = t % gI;
+            e = a.uniq[u];
+            const int p0 = a.off[u];
+            m_cnt = a.off[u + 1] - p0;
+            cols = a.I; CPR = cprI; mat = &a.down;
+            hsrc = a.h + (size_t)p0 * a.I;
+            obase = so + p0 * NH;
+        } else {
+            grp = t - U * gI;
+            e = 0;
+            m_cnt = K;
+            cols = a.Is; CPR = cprS; mat = &a.sdown;
+            hsrc = a.h_sh;
+            obase = so + (K * k) * NH;
+        }
+        const int RPG = 64 / CPR;
+        const int q = lane / CPR, chunk = lane % CPR;
+        const int nl = grp * RPG + q;
+        const bool valid = nl < NH;
+        const int n = n_base + nl;
+        uint4 c = make_uint4(0, 0, 0, 0);
+        uint32_t sc = 0;
+        if (valid) {
+            c = *reinterpret_cast<const uint4*>(mat->q + ((size_t)e * H + n) * (cols / 2) + chunk * 16);
+            sc = *reinterpret_cast<const uint16_t*>(mat->s + ((size_t)e * H + n) * (cols / 16) + chunk * 2);
+        }
+        const float ts = mat->ts[e];
+        float wf[32];
+        fp4x8_to_f32(c.x, wf + 0); fp4x8_to_f32(c.y, wf + 8);
+        fp4x8_to_f32(c.z, wf + 16); fp4x8_to_f32(c.w, wf + 24);
+        const float s0 = e4m3_to_f32<0>(sc), s1 = e4m3_to_f32<1>(sc);
+        for (int m = 0; m < m_cnt; ++m) {
+            const float4* hp = reinterpret_cast<const float4*>(hsrc + (size_t)m * cols + chunk * 32);
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4) {
+                const float4 hv = hp[t4];
+                a0 = fmaf(wf[4 * t4 + 0], hv.x, a0);
+                a0 = fmaf(wf[4 * t4 + 1], hv.y, a0);
+                a0 = fmaf(wf[4 * t4 + 2], hv.z, a0);
+                a0 = fmaf(wf[4 * t4 + 3], hv.w, a0);
+            }
+#pragma unroll
+            for (int t4 = 4; t4 < 8; ++t4) {
+                const float4 hv = hp[t4];
+                a1 = fmaf(wf[4 * t4 + 0], hv.x, a1);
+                a1 = fmaf(wf[4 * t4 + 1], hv.y, a1);
+                a1 = fmaf(wf[4 * t4 + 2], hv.z, a1);
+                a1 = fmaf(wf[4 * t4 + 3], hv.w, a1);
+            }
+            float p = fmaf(a1, s1, a0 * s0);
+            p = group_sum_rt(p, CPR);
+            if (valid && chunk == CPR - 1) obase[m * NH + nl] = p * ts;
+        }
+    }
+    __syncthreads();
+
+    // combine: y = rs * sum_j w_j o_j (rank order) + shared (+ residual)
+    for (int i = tid; i < K * NH; i += kBlock) {
+        const int r = i / NH, nl = i % NH, n = n_base + nl;
+        float acc = 0.0f;
+        for (int j = 0; j < k; ++j) acc = fmaf(a.w[r * k + j], so[a.inv[r * k + j] * NH + nl], acc);
+        float y = a.rs * acc;
+        if (has_sh) y += so[(K * k + r) * NH + nl];
+        if (a.residual) y += bf16_to_f32(a.residual[(size_t)r * H + n]);
+        a.y32[(size_t)r * H + n] = y;
+        if (a.y) a.y[(size_t)r * H + n] = f32_to_bf16_rne(y);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_dequant: the decode of the GEMM kernels, written out (bf16 and fp32
+// decode paths are both evaluated; a disagreement is reported as NaN)
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kBlock) void k_dequant(Fp4Mat m, int n_experts, int rows, int cols, float* out) {
+    const size_t chunks_per_row = (size_t)cols / 32;
+    const size_t total = (size_t)n_experts * rows * chunks_per_row;
+    for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < total; i += (size_t)gridDim.x * kBlock) {
+        const size_t row = i / chunks_per_row;  // e * rows + n
+        const int chunk = (int)(i % chunks_per_row);
+        const int e = (int)(row / rows);
+        const uint4 c = *reinterpret_cast<const uint4*>(m.q + row * (cols / 2) + chunk * 16);
+        const uint32_t sc = *reinterpret_cast<const uint16_t*>(m.s + row * (cols / 16) + chunk * 2);
+        float wf[32];
+        bf16x2_t wb[16];
+        fp4x8_to_f32(c.x, wf + 0); fp4x8_to_f32(c.y, wf + 8);
+        fp4x8_to_f32(c.z, wf + 16); fp4x8_to_f32(c.w, wf + 24);
+        fp4x8_to_bf16(c.x, wb + 0); fp4x8_to_bf16(c.y, wb + 4);
+        fp4x8_to_bf16(c.z, wb + 8); fp4x8_to_bf16(c.w, wb + 12);
+        const float s0 = e4m3_to_f32<0>(sc), s1 = e4m3_to_f32<1>(sc);
+        const float ts = m.ts[e];
+        float* o = out + row * cols + chunk * 32;
+#pragma unroll
+        for (int t = 0; t < 32; ++t) {
+            const float fb = (float)((t & 1) ? wb[t >> 1].y : wb[t >> 1].x);
+            const float v = (fb == wf[t]) ? wf[t] : __builtin_nanf("");
+            o[t] = (v * (t < 16 ? s0 : s1)) * ts;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+int gateup_slab_rows(int H) { return kWaves * kRowsPerWave * (64 / (H >> 5)); }
+
+hipError_t launch_init(int32_t* meta, hipStream_t st) {
+    hipLaunchKernelGGL(k_init, dim3(1), dim3(64), 0, st, meta);
+    return hipGetLastError();
+}
+
+constexpr size_t kRouteMaxDynLds = 96 * 1024;
+
+hipError_t init_kernels() {
+    static hipError_t once = hipFuncSetAttribute(reinterpret_cast<const void*>(k_route),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)kRouteMaxDynLds);
+    return once;
+}
+
+// Plain launch, or one whose start/stop events carry the kernel's own
+// dispatch timestamps.
+template <typename Kern, typename Args>
+hipError_t launch(Kern k, dim3 grid, dim3 block, size_t smem, hipStream_t st, const Timing* t, const Args& a) {
+    if (t)
+        hipExtLaunchKernelGGL(k, grid, block, smem, st, t->start, t->stop, 0, a);
+    else
+        hipLaunchKernelGGL(k, grid, block, smem, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t st, const Timing* t) {
+    const size_t xbytes = (size_t)a.K * a.H * 2;
+    const size_t smem = xbytes > sizeof(SelectSmem) ? xbytes : sizeof(SelectSmem);
+    const int grid = (a.E + kWaves - 1) / kWaves;
+    return launch(k_route, dim3(grid), dim3(kBlock), smem, st, t, a);
+}
+
+hipError_t launch_select(const RouteArgs& a, hipStream_t st) {
+    return launch(k_select, dim3(1), dim3(kBlock), sizeof(SelectSmem), st, nullptr, a);
+}
+
+hipError_t launch_gateup(const GateUpArgs& a, int max_unique, hipStream_t st, const Timing* t) {
+    const int grid = max_unique * (a.I / a.slab) + (a.sgate.q ? a.Is / a.slab : 0);
+    const dim3 g(grid > 0 ? grid : 1), b(kBlock);
+    const int M = a.K;
+    if (M <= 1) return launch(k_gateup<1>, g, b, 0, st, t, a);
+    if (M <= 2) return launch(k_gateup<2>, g, b, 0, st, t, a);
+    if (M <= 4) return launch(k_gateup<4>, g, b, 0, st, t, a);
+    if (M <= 8) return launch(k_gateup<8>, g, b, 0, st, t, a);
+    return launch(k_gateup<16>, g, b, 0, st, t, a);
+}
+
+hipError_t launch_down(const DownArgs& a, hipStream_t st, const Timing* t) {
+    return launch(k_down, dim3(a.H / kDownRowsPerBlock), dim3(kBlock), 0, st, t, a);
+}
+
+hipError_t launch_dequant(Fp4Mat m, int n_experts, int rows, int cols, float* out, hipStream_t st) {
+    const size_t total = (size_t)n_experts * rows * (cols / 32);
+    size_t grid = (total + kBlock - 1) / kBlock;
+    if (grid > 65536) grid = 65536;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_dequant, dim3((unsigned)grid), dim3(kBlock), 0, st, m, n_experts, rows, cols, out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

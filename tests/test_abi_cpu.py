@@ -1,0 +1,140 @@
+"""The C ABI library loads, exports every entry point the header declares,
+and rejects bad arguments on the host before any GPU work (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from speculative_block_verify_amd import api, inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_verify.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:MOE_API\s+)?(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*(moe_[a-z0-9_]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return api.lib()
+
+
+def test_header_declares_the_expected_surface():
+    names = _declared_functions()
+    assert set(names) == set(api.EXPORTS), names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    assert api.moe_verify_version() >= 100
+
+
+def test_struct_layouts_match_header_sizes():
+    # pointer-only structs: 3 / 2 + 6*3 / 7 / 10 pointers; cfg: 10 x 4 bytes
+    P = ctypes.sizeof(ctypes.c_void_p)
+    assert ctypes.sizeof(api.moe_nvfp4) == 3 * P
+    assert ctypes.sizeof(api.moe_layer_weights) == 20 * P
+    assert ctypes.sizeof(api.moe_route_out) == 7 * P
+    assert ctypes.sizeof(api.moe_debug) == 10 * P
+    assert ctypes.sizeof(api.moe_cfg) == 40
+
+
+def _cfg(**kw):
+    c = api.make_cfg(inputs.LAGUNA, 2)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_workspace_bytes_valid_and_invalid():
+    n = api.moe_verify_workspace_bytes(_cfg())
+    assert n > 0 and n % 256 == 0
+    assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(hidden=300))) == 0
+    assert "hidden" in api.moe_verify_last_error()
+    assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(max_rows=17))) == 0
+    assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(top_k=300))) == 0
+    assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(inter=500))) == 0
+    assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(score_fn=7))) == 0
+    assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(norm_topk=0))) == 0
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def _weights(shared=True, bias=False):
+    m = api.moe_nvfp4(FAKE, FAKE, FAKE)
+    z = api.moe_nvfp4(None, None, None)
+    return api.moe_layer_weights(FAKE, FAKE if bias else None, m, m, m,
+                                 m if shared else z, m if shared else z, m if shared else z)
+
+
+def _layer(cfg, w, K=2, x=FAKE, y=FAKE, ws=FAKE, ws_bytes=None, residual=None):
+    if ws_bytes is None:
+        ws_bytes = api.lib().moe_verify_workspace_bytes(ctypes.byref(cfg)) or 1 << 30
+    return api.lib().moe_verify_layer(ctypes.byref(cfg), ctypes.byref(w), x, K, residual, y, None, ws,
+                                      ws_bytes, None, None)
+
+
+@pytest.mark.parametrize("case,code", [
+    ("K0", api.MOE_ERR_INVALID), ("K_over", api.MOE_ERR_INVALID), ("x_null", api.MOE_ERR_INVALID),
+    ("y_misaligned", api.MOE_ERR_INVALID), ("ws_small", api.MOE_ERR_WORKSPACE),
+    ("ws_null", api.MOE_ERR_INVALID), ("bias_with_softmax", api.MOE_ERR_INVALID),
+    ("sigmoid_without_bias", api.MOE_ERR_INVALID), ("shared_missing", api.MOE_ERR_INVALID),
+    ("shared_unexpected", api.MOE_ERR_INVALID), ("hidden_unsupported", api.MOE_ERR_UNSUPPORTED),
+    ("gate_null", api.MOE_ERR_INVALID), ("router_misaligned", api.MOE_ERR_INVALID),
+])
+def test_layer_argument_errors(case, code):
+    cfg, w, kw = _cfg(), _weights(), {}
+    if case == "K0": kw["K"] = 0
+    elif case == "K_over": kw["K"] = 3
+    elif case == "x_null": kw["x"] = None
+    elif case == "y_misaligned": kw["y"] = FAKE + 2
+    elif case == "ws_small": kw["ws_bytes"] = 1024
+    elif case == "ws_null": kw["ws"] = None
+    elif case == "bias_with_softmax": w = _weights(bias=True)
+    elif case == "sigmoid_without_bias": cfg = _cfg(score_fn=1)
+    elif case == "shared_missing": w = _weights(shared=False)
+    elif case == "shared_unexpected": cfg = _cfg(shared_inter=0)
+    elif case == "hidden_unsupported": cfg = _cfg(hidden=4096)
+    elif case == "gate_null": w.gate = api.moe_nvfp4(None, FAKE, FAKE)
+    elif case == "router_misaligned": w.router_w = FAKE + 4
+    assert _layer(cfg, w, **kw) == code
+    assert api.moe_verify_last_error()
+
+
+def test_stack_and_route_argument_errors():
+    cfg = _cfg()
+    L = api.lib()
+    arr = (api.moe_layer_weights * 2)(_weights(), _weights(shared=False))
+    n = L.moe_verify_workspace_bytes(ctypes.byref(cfg))
+    rc = L.moe_verify_stack(ctypes.byref(cfg), arr, 2, FAKE, 2, FAKE, None, FAKE, n, None, None)
+    assert rc == api.MOE_ERR_INVALID and "layer 1" in api.moe_verify_last_error()
+    rc = L.moe_verify_stack(ctypes.byref(cfg), arr, 0, FAKE, 2, FAKE, None, FAKE, n, None, None)
+    assert rc == api.MOE_ERR_INVALID
+    out = api.moe_route_out(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    rc = L.moe_verify_route(ctypes.byref(cfg), FAKE, None, 2, ctypes.byref(out), None, 0, None)
+    assert rc == api.MOE_ERR_INVALID
+    out.inv = FAKE
+    rc = L.moe_verify_route(ctypes.byref(_cfg(score_fn=1)), FAKE, None, 2, ctypes.byref(out), None, 0, None)
+    assert rc == api.MOE_ERR_INVALID and "bias" in api.moe_verify_last_error()
+    m = api.moe_nvfp4(FAKE, FAKE, FAKE)
+    assert L.moe_verify_dequant_nvfp4(ctypes.byref(m), 1, 4, 48, FAKE, None) == api.MOE_ERR_INVALID
+    h = ctypes.c_void_p()
+    rc = L.moe_stack_graph_create(ctypes.byref(cfg), arr, 2, FAKE, 2, FAKE, None, FAKE, n, None, ctypes.byref(h))
+    assert rc == api.MOE_ERR_INVALID and not h.value
+    assert L.moe_stack_graph_launch(None, None) == api.MOE_ERR_INVALID
+    L.moe_stack_graph_destroy(None)
+
+
+def test_weight_bytes_counts_unique_experts_once():
+    cfg = _cfg()
+    one = api.moe_verify_weight_bytes(cfg, 1, 2, with_shared=False, with_router=False) - 4 * 2 * 2048
+    assert one == 3 * (512 * 2048 // 2 + 512 * 2048 // 16 + 4)
+    full = api.moe_verify_weight_bytes(cfg, 16, 2)
+    assert full == 17 * one + 2 * 256 * 2048 + 4 * 2 * 2048

@@ -1,0 +1,83 @@
+"""GPU parity of chained layers (a9: RMSNorm glue + graph launch).
+
+The oracle runs its own free-running chain (it never takes the GPU's
+intermediate activations).  Each GPU layer output is compared with the
+oracle's for every row that has not legitimately diverged at an earlier
+near-tie in expert selection.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from speculative_block_verify_amd import api, inputs
+from tests import gpu_helpers as gh
+from tests.conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _host_layers(layers_dev):
+    for w in layers_dev:
+        yield {k: (None if v is None else ({kk: vv.cpu() for kk, vv in v.items()} if isinstance(v, dict) else v.cpu()))
+               for k, v in w.items()}
+
+
+def _stack_case(shape, n_layers, K, seed, label, min_alive_layers):
+    say("case: stack %s L=%d K=%d seed=%d" % (label, n_layers, K, seed))
+    layers = inputs.gen_stack(shape, n_layers, seed, device=DEV)
+    x = inputs.gen_x(K, shape.hidden, seed, device=DEV)
+    cfg = api.make_cfg(shape, K)
+    gpu = gh.run_stack_debug(cfg, layers, x, n_layers)
+    np.testing.assert_array_equal(gpu["y32_out"], gpu["y32"][-1])
+    np.testing.assert_array_equal(gpu["y"], gh.bf16_of(gpu["y32_out"]))
+    reps, alive = gh.compare_stack(gpu, _host_layers(layers), x.cpu().numpy(), shape.top_k, shape.n_experts,
+                                   label=label)
+    worst = max(r["max_abs_over_max_ref"] for r in reps)
+    say("  layers compared %d, rows alive at end %s, worst max-abs/max-ref %.3g, bf16 input diffs %s"
+        % (len(reps), alive.tolist(), worst, [r["x_in_bf16_diffs"] for r in reps][:8]))
+    assert len(reps) >= min_alive_layers
+    return layers, x, cfg, gpu
+
+
+def test_stack_tiny_40_layers():
+    _stack_case(inputs.TINY, 40, 1, 3, "tiny", 40)
+
+
+def test_stack_tiny_shared_40_layers_k4():
+    shape = inputs.MoEShape(256, 16, 2, 128, 128)
+    _stack_case(shape, 40, 4, 5, "tiny-shared", 10)
+
+
+def test_stack_full_size_4_layers_k2():
+    _stack_case(inputs.LAGUNA, 4, 2, 9, "full-4", 4)
+
+
+def test_stack_full_size_40_layers_graph_matches_direct_and_oracle():
+    """The benchmark's configuration: 40 full-size layers, K = 2, launched as
+    a captured graph.  The graph's output must equal the direct call bit for
+    bit on every replay (with eager work in between), and the direct call's
+    per-layer outputs must match the oracle's chain."""
+    layers, x, cfg, gpu = _stack_case(inputs.LAGUNA, 40, 2, 1, "full-40", 10)
+    K, H = x.shape
+    y = torch.empty(K, H, dtype=torch.int16, device=DEV)
+    y32 = torch.empty(K, H, dtype=torch.float32, device=DEV)
+    ws = api.alloc_workspace(cfg, DEV)
+    g = api.StackGraph(cfg, [api.make_weights(w) for w in layers], x, y, ws, y32=y32)
+    for rep in range(4):
+        y32.fill_(float("nan"))
+        g.launch()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y32.cpu().numpy(), gpu["y32_out"])
+        # unrelated eager work between replays
+        junk = torch.randn(1 << 20, device=DEV).sum()
+        api.moe_verify_stack(cfg, [api.make_weights(w) for w in layers[:3]], x, y, ws, y32=y32)
+        torch.cuda.synchronize()
+        del junk
+    g.close()
