@@ -113,8 +113,10 @@ struct Layout {
     int32_t* off;
     int32_t* asg;
     int32_t* inv;
+    int32_t* rowtab;
     float* h;
     float* h_sh;
+    float* ssq;
     uint16_t* xbuf;
     float* ybuf;
     size_t bytes;
@@ -135,8 +137,10 @@ Layout layout(const moe_cfg* c, void* base) {
     L.off = reinterpret_cast<int32_t*>(take((R * k + 1) * 4));
     L.asg = reinterpret_cast<int32_t*>(take(R * k * 4));
     L.inv = reinterpret_cast<int32_t*>(take(R * k * 4));
+    L.rowtab = reinterpret_cast<int32_t*>(take(R * k * moe::kMaxRows * 4));
     L.h = reinterpret_cast<float*>(take(R * k * I * 4));
     L.h_sh = reinterpret_cast<float*>(take(R * (Is ? Is : 1) * 4));
+    L.ssq = reinterpret_cast<float*>(take(R * (H / moe::kDownRowsPerBlock) * 4));
     L.xbuf = reinterpret_cast<uint16_t*>(take(R * H * 2));
     L.ybuf = reinterpret_cast<float*>(take(R * H * 4));
     L.bytes = o;
@@ -176,6 +180,8 @@ int enqueue_layer(const moe_cfg* c, const moe_layer_weights* w, const LayerIO& i
     ra.off = L.off;
     ra.asg = L.asg;
     ra.inv = L.inv;
+    ra.rowtab = L.rowtab;
+    ra.ssq = L.ssq;
     ra.K = K; ra.H = c->hidden; ra.E = c->n_experts; ra.k = c->top_k;
     ra.score_fn = c->score_fn; ra.norm_topk = c->norm_topk;
     if ((e = moe::launch_route(ra, st, tm ? &tm[0] : nullptr)) != hipSuccess) return hip_fail(e, "route launch");
@@ -185,19 +191,20 @@ int enqueue_layer(const moe_cfg* c, const moe_layer_weights* w, const LayerIO& i
     ga.gate = mat(w->gate); ga.up = mat(w->up);
     ga.sgate = mat(w->sh_gate); ga.sup = mat(w->sh_up);
     if (c->shared_inter == 0) { ga.sgate = moe::Fp4Mat{nullptr, nullptr, nullptr}; ga.sup = ga.sgate; }
-    ga.meta = L.meta;
-    ga.uniq = L.uniq; ga.off = L.off; ga.asg = L.asg;
+    ga.n_unique = L.meta + moe::kMetaUnique;
+    ga.uniq = L.uniq; ga.off = L.off; ga.rowtab = L.rowtab;
     ga.h = L.h; ga.h_sh = L.h_sh;
     ga.K = K; ga.H = c->hidden; ga.I = c->inter; ga.Is = c->shared_inter; ga.k = c->top_k;
     ga.slab = moe::gateup_slab_rows(c->hidden);
-    const int max_unique = std::min(c->n_experts, K * c->top_k);
-    if ((e = moe::launch_gateup(ga, max_unique, st, tm ? &tm[1] : nullptr)) != hipSuccess) return hip_fail(e, "gate/up launch");
+    ga.max_unique = std::min(c->n_experts, K * c->top_k);
+    if ((e = moe::launch_gateup(ga, st, tm ? &tm[1] : nullptr)) != hipSuccess) return hip_fail(e, "gate/up launch");
 
     moe::DownArgs da{};
     da.down = mat(w->down);
     da.sdown = c->shared_inter ? mat(w->sh_down) : moe::Fp4Mat{nullptr, nullptr, nullptr};
-    da.meta = L.meta;
+    da.n_unique = L.meta + moe::kMetaUnique;
     da.uniq = L.uniq; da.off = L.off; da.inv = L.inv;
+    da.ssq = L.ssq;
     da.w = L.w; da.h = L.h; da.h_sh = L.h_sh;
     da.residual = io.residual;
     da.y32 = io.y32; da.y = io.y;

@@ -15,6 +15,9 @@ constexpr int kBlock = 256;        // threads per workgroup (4 wave64)
 constexpr int kWaves = kBlock / 64;
 constexpr int kRowsPerWave = 4;    // weight rows each wave keeps in flight in gate/up
 constexpr int kDownRowsPerBlock = 8;
+constexpr int kDownThreads = 512;  // 8 wave64 per down workgroup
+constexpr int kDownHLdsBytes = 64 * 1024;  // h rows staged in LDS per chunk
+constexpr int kMaxSlots = kMaxRows * kMaxTopK;
 
 struct Fp4Mat {
     const uint8_t* q;
@@ -41,6 +44,8 @@ struct RouteArgs {
     int32_t* off;           // [K*k+1]
     int32_t* asg;           // [K*k]
     int32_t* inv;           // [K*k]
+    int32_t* rowtab;        // [K*k][kMaxRows] rows of x assigned to each unique expert
+    const float* ssq;       // [K][H / kDownRowsPerBlock] partial sums of squares of y_prev
     int K, H, E, k, score_fn, norm_topk;
 };
 
@@ -48,20 +53,21 @@ struct GateUpArgs {
     const uint16_t* x;      // bf16 [K][H]
     Fp4Mat gate, up;        // [E][I][H/2]
     Fp4Mat sgate, sup;      // [1][Is][H/2] (q == nullptr: no shared expert)
-    const int32_t* meta;
+    const int32_t* n_unique;
     const int32_t* uniq;
     const int32_t* off;
-    const int32_t* asg;
+    const int32_t* rowtab;  // [K*k][kMaxRows]
     float* h;               // [K*k][I], indexed by position in asg
     float* h_sh;            // [K][Is]
     int K, H, I, Is, k;
     int slab;               // weight rows (of gate and of up) per workgroup
+    int max_unique;         // min(E, K*k): routed workgroups = max_unique * (I / slab)
 };
 
 struct DownArgs {
     Fp4Mat down;            // [E][H][I/2]
     Fp4Mat sdown;           // [1][H][Is/2]
-    const int32_t* meta;
+    const int32_t* n_unique;
     const int32_t* uniq;
     const int32_t* off;
     const int32_t* inv;
@@ -71,6 +77,7 @@ struct DownArgs {
     const uint16_t* residual;  // bf16 [K][H] or nullptr
     float* y32;             // [K][H]
     uint16_t* y;            // bf16 [K][H] or nullptr
+    float* ssq;             // [K][H / kDownRowsPerBlock] per-workgroup sums of y^2
     int K, H, I, Is, k;
     float rs;
 };
@@ -86,11 +93,11 @@ struct Timing {
 hipError_t launch_init(int32_t* meta, hipStream_t st);
 hipError_t launch_route(const RouteArgs& a, hipStream_t st, const Timing* t = nullptr);
 hipError_t launch_select(const RouteArgs& a, hipStream_t st);  // logits given
-hipError_t launch_gateup(const GateUpArgs& a, int max_unique, hipStream_t st, const Timing* t = nullptr);
+hipError_t launch_gateup(const GateUpArgs& a, hipStream_t st, const Timing* t = nullptr);
 hipError_t launch_down(const DownArgs& a, hipStream_t st, const Timing* t = nullptr);
 hipError_t launch_dequant(Fp4Mat m, int n_experts, int rows, int cols, float* out, hipStream_t st);
 
-// One-time kernel attributes (dynamic LDS above 64 KiB for the router).
+// One-time kernel attributes (dynamic LDS sizes).
 hipError_t init_kernels();
 
 // Workgroups / slab size the gate/up launch uses for hidden H.

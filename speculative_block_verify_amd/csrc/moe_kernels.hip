@@ -179,20 +179,44 @@ __device__ __forceinline__ float group_sum_rt(float v, int G) {
 // ---------------------------------------------------------------------------
 
 struct SelectSmem {
-    int32_t sel[kMaxRows * kMaxTopK];
-    float w[kMaxRows * kMaxTopK];
+    int32_t sel[kMaxSlots];
+    float w[kMaxSlots];
+    int32_t asg[kMaxSlots];
+    int32_t off[kMaxSlots + 1];
     int32_t cnt[kMaxExperts];
     int32_t start[kMaxExperts];
+    float lg[1];  // K * E logits follow (dynamic tail)
 };
+
+__host__ __device__ constexpr size_t select_smem_bytes(int K, int E) {
+    return sizeof(SelectSmem) + (size_t)K * E * sizeof(float);
+}
+
+// Copy n floats global -> LDS with every load of a pass in flight at once.
+__device__ __forceinline__ void stage_floats(float* dst, const float* src, int n, int tid, int nthr) {
+    constexpr int U = 8;
+    for (int base = 0; base < n; base += U * nthr) {
+        float v[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const int i = base + j * nthr + tid;
+            v[j] = (i < n) ? src[i] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const int i = base + j * nthr + tid;
+            if (i < n) dst[i] = v[j];
+        }
+    }
+}
 
 // Top-k of row r by (key desc, index asc) with one wave.  Lane l owns experts
 // l*P .. l*P+P-1 (contiguous), so among equal keys the lowest lane holding
-// the maximum also holds the lowest index.
-__device__ void wave_select_row(const RouteArgs& a, const float* logits, int r, SelectSmem& sm) {
+// the maximum also holds the lowest index.  lr: the row's logits in LDS.
+__device__ void wave_select_row(const RouteArgs& a, const float* lr, int r, SelectSmem& sm) {
     const int lane = threadIdx.x & 63;
     const int E = a.E, k = a.k;
     const int P = (E + 63) >> 6;
-    const float* lr = logits + (size_t)r * E;
     uint32_t kv[kMaxExperts / 64];
 #pragma unroll
     for (int p = 0; p < kMaxExperts / 64; ++p) {
@@ -255,14 +279,16 @@ __device__ void wave_select_row(const RouteArgs& a, const float* logits, int r, 
     }
 }
 
-// All rows' top-k, then the canonical dedup CSR.  Called by a whole
-// workgroup; logits may be global memory.
-__device__ void select_and_dedup(const RouteArgs& a, const float* logits, int32_t* n_unique_out,
-                                 SelectSmem& sm) {
+// All rows' top-k, then the canonical dedup CSR and the per-expert row
+// table.  Called by a whole workgroup of kBlock threads; logits may be
+// global memory.
+__device__ void select_and_dedup(const RouteArgs& a, const float* logits, SelectSmem& sm) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int K = a.K, k = a.k, E = a.E, n = K * k;
-    for (int r = wave; r < K; r += kWaves) wave_select_row(a, logits, r, sm);
+    stage_floats(sm.lg, logits, K * E, tid, kBlock);
     for (int e = tid; e < E; e += kBlock) sm.cnt[e] = 0;
+    __syncthreads();
+    for (int r = wave; r < K; r += kWaves) wave_select_row(a, sm.lg + r * E, r, sm);
     __syncthreads();
     for (int s = tid; s < n; s += kBlock) atomicAdd(&sm.cnt[sm.sel[s]], 1);
     __syncthreads();
@@ -280,24 +306,34 @@ __device__ void select_and_dedup(const RouteArgs& a, const float* logits, int32_
             if (e < E) {
                 const int cn = sm.cnt[e];
                 sm.start[e] = cs;
-                if (cn) { a.uniq[fs] = e; a.off[fs] = cs; }
+                if (cn) { a.uniq[fs] = e; a.off[fs] = cs; sm.off[fs] = cs; }
                 cs += cn;
                 fs += (cn > 0);
             }
         }
         const int U = __builtin_amdgcn_readlane(fi, 63);
-        if (lane == 0) { *n_unique_out = U; a.off[U] = n; }
+        if (lane == 0) { *a.n_unique = U; a.off[U] = n; sm.off[U] = n; sm.cnt[0] = U; }
     }
     __syncthreads();
+    const int U = sm.cnt[0];
     for (int s = tid; s < n; s += kBlock) {
         const int e = sm.sel[s];
         int rank = 0;
         for (int t = 0; t < s; ++t) rank += (sm.sel[t] == e);
         const int pos = sm.start[e] + rank;
+        sm.asg[pos] = s;
         a.asg[pos] = s;
         a.inv[s] = pos;
         a.ids[s] = e;
         a.w[s] = sm.w[s];
+    }
+    __syncthreads();
+    if (a.rowtab) {
+        for (int i = tid; i < U * K; i += kBlock) {
+            const int u = i / K, m = i % K;
+            const int o0 = sm.off[u], cnt = sm.off[u + 1] - o0;
+            a.rowtab[u * kMaxRows + m] = (m < cnt) ? sm.asg[o0 + m] / k : 0;
+        }
     }
 }
 
@@ -313,6 +349,8 @@ __global__ void k_init(int32_t* meta) {
 // k_route
 // ---------------------------------------------------------------------------
 
+constexpr int kRouterPieces = 4;  // 16-byte router pieces per lane (hidden <= 2048)
+
 __global__ __launch_bounds__(kBlock) void k_route(RouteArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
@@ -322,18 +360,60 @@ __global__ __launch_bounds__(kBlock) void k_route(RouteArgs a) {
     const int K = a.K, H = a.H, E = a.E;
     const int KH = K * H;
 
-    // 1. bf16 x into LDS (RMS-normalised from the previous layer's fp32
-    //    output when chaining layers)
+    // 0. this wave's router row, requested before anything else
+    const int e = blockIdx.x * kWaves + wave;
+    uint4 wv[kRouterPieces];
+#pragma unroll
+    for (int t = 0; t < kRouterPieces; ++t) {
+        const int p = lane * 8 + t * 512;
+        wv[t] = (e < E && p < H) ? *reinterpret_cast<const uint4*>(a.wr + (size_t)e * H + p) : make_uint4(0, 0, 0, 0);
+    }
+
+    // 1. bf16 x into LDS; when chaining layers it is the RMS-normalised
+    //    previous output, with the sums of squares taken from the per-workgroup
+    //    partials the down kernel left behind
     if (a.y_prev) {
+        constexpr int CH = 2;  // float4 pairs (16 elements) per thread per pass
+        float4 v[2 * CH];
+        auto load_pass = [&](int base) {
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const int i = base + (j * kBlock + tid) * 8;
+                const bool ok = i < KH;
+                v[2 * j] = ok ? *reinterpret_cast<const float4*>(a.y_prev + i) : make_float4(0, 0, 0, 0);
+                v[2 * j + 1] = ok ? *reinterpret_cast<const float4*>(a.y_prev + i + 4) : make_float4(0, 0, 0, 0);
+            }
+        };
+        load_pass(0);
+        const int nparts = H / kDownRowsPerBlock;  // <= 256 for hidden <= 2048
         for (int r = wave; r < K; r += kWaves) {
-            const float* yr = a.y_prev + (size_t)r * H;
-            float ss = 0.0f;
-            for (int h = lane; h < H; h += 64) ss = fmaf(yr[h], yr[h], ss);
-            ss = wave_sum(ss);
+            float pv[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int j = lane + 64 * t;
+                pv[t] = (j < nparts) ? a.ssq[r * nparts + j] : 0.0f;
+            }
+            const float ss = wave_sum((pv[0] + pv[1]) + (pv[2] + pv[3]));
             if (lane == 0) s_inv[r] = 1.0f / sqrtf(ss / (float)H + a.eps);
         }
         __syncthreads();
-        for (int i = tid; i < KH; i += kBlock) xs[i] = f32_to_bf16_rne(a.y_prev[i] * s_inv[i / H]);
+        for (int base = 0; base < KH; base += kBlock * 8 * CH) {
+            if (base > 0) load_pass(base);
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const int i = base + (j * kBlock + tid) * 8;
+                if (i < KH) {
+                    const float sc = s_inv[i / H];
+                    const float4 p = v[2 * j], q = v[2 * j + 1];
+                    uint4 o;
+                    o.x = (uint32_t)f32_to_bf16_rne(p.x * sc) | ((uint32_t)f32_to_bf16_rne(p.y * sc) << 16);
+                    o.y = (uint32_t)f32_to_bf16_rne(p.z * sc) | ((uint32_t)f32_to_bf16_rne(p.w * sc) << 16);
+                    o.z = (uint32_t)f32_to_bf16_rne(q.x * sc) | ((uint32_t)f32_to_bf16_rne(q.y * sc) << 16);
+                    o.w = (uint32_t)f32_to_bf16_rne(q.z * sc) | ((uint32_t)f32_to_bf16_rne(q.w * sc) << 16);
+                    *reinterpret_cast<uint4*>(xs + i) = o;
+                }
+            }
+        }
         __syncthreads();
         // each workgroup publishes its share of the normalised x
         const int per = (KH / 8 + gridDim.x - 1) / gridDim.x * 8;
@@ -341,30 +421,43 @@ __global__ __launch_bounds__(kBlock) void k_route(RouteArgs a) {
         for (int i = i0 + tid * 8; i < min(KH, i0 + per); i += kBlock * 8)
             *reinterpret_cast<uint4*>(a.x_out + i) = *reinterpret_cast<const uint4*>(xs + i);
     } else {
-        for (int i = tid * 8; i < KH; i += kBlock * 8)
-            *reinterpret_cast<uint4*>(xs + i) = *reinterpret_cast<const uint4*>(a.x_in + i);
+        constexpr int CH = 4;
+        for (int base = 0; base < KH; base += kBlock * 8 * CH) {
+            uint4 v[CH];
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const int i = base + (j * kBlock + tid) * 8;
+                v[j] = (i < KH) ? *reinterpret_cast<const uint4*>(a.x_in + i) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const int i = base + (j * kBlock + tid) * 8;
+                if (i < KH) *reinterpret_cast<uint4*>(xs + i) = v[j];
+            }
+        }
         __syncthreads();
     }
 
     // 2. one wave per expert row: logits[r][e] = x_r . Wr[e]
-    const int e = blockIdx.x * kWaves + wave;
     if (e < E) {
         float acc[kMaxRows];
 #pragma unroll
         for (int r = 0; r < kMaxRows; ++r) acc[r] = 0.0f;
-        const uint16_t* wrow = a.wr + (size_t)e * H;
-        for (int p = lane * 8; p < H; p += 512) {
-            const uint4 wv = *reinterpret_cast<const uint4*>(wrow + p);
 #pragma unroll
-            for (int r = 0; r < kMaxRows; ++r) {
-                if (r < K) {
-                    const uint4 xv = *reinterpret_cast<const uint4*>(xs + r * H + p);
-                    float s = acc[r];
-                    s = dot2(as_bf16x2(wv.x), as_bf16x2(xv.x), s);
-                    s = dot2(as_bf16x2(wv.y), as_bf16x2(xv.y), s);
-                    s = dot2(as_bf16x2(wv.z), as_bf16x2(xv.z), s);
-                    s = dot2(as_bf16x2(wv.w), as_bf16x2(xv.w), s);
-                    acc[r] = s;
+        for (int t = 0; t < kRouterPieces; ++t) {
+            const int p = lane * 8 + t * 512;
+            if (p < H) {
+#pragma unroll
+                for (int r = 0; r < kMaxRows; ++r) {
+                    if (r < K) {
+                        const uint4 xv = *reinterpret_cast<const uint4*>(xs + r * H + p);
+                        float s = acc[r];
+                        s = dot2(as_bf16x2(wv[t].x), as_bf16x2(xv.x), s);
+                        s = dot2(as_bf16x2(wv[t].y), as_bf16x2(xv.y), s);
+                        s = dot2(as_bf16x2(wv[t].z), as_bf16x2(xv.z), s);
+                        s = dot2(as_bf16x2(wv[t].w), as_bf16x2(xv.w), s);
+                        acc[r] = s;
+                    }
                 }
             }
         }
@@ -385,7 +478,7 @@ __global__ __launch_bounds__(kBlock) void k_route(RouteArgs a) {
     if (!s_last) return;
     __threadfence();
     SelectSmem& sm = *reinterpret_cast<SelectSmem*>(smem);
-    select_and_dedup(a, a.logits, a.n_unique, sm);
+    select_and_dedup(a, a.logits, sm);
     if (tid == 0) a.meta[kMetaCounter] = 0;
 }
 
@@ -393,7 +486,7 @@ __global__ __launch_bounds__(kBlock) void k_route(RouteArgs a) {
 __global__ __launch_bounds__(kBlock) void k_select(RouteArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     SelectSmem& sm = *reinterpret_cast<SelectSmem*>(smem);
-    select_and_dedup(a, a.logits, a.n_unique, sm);
+    select_and_dedup(a, a.logits, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -404,39 +497,42 @@ template <int MAXM>
 __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int H = a.H;
-    const int U = a.meta[kMetaUnique];
     const int nsr = a.I / a.slab;
+    const int n_routed_blocks = a.max_unique * nsr;
     int b = blockIdx.x;
 
     const uint8_t *gq, *gs, *uq, *us;
     float gts, uts;
     float* hbase;
-    int hstride, m_cnt, n0, rows_total;
+    int hstride, m_cnt, n0;
     int rowsel[MAXM];
-    if (b < U * nsr) {
+    if (b < n_routed_blocks) {
+        // one round trip for everything this workgroup needs to know: all of
+        // these addresses are independent of each other
         const int u = b / nsr;
+        const int U = *a.n_unique;
         const int e = a.uniq[u];
         const int o0 = a.off[u];
-        m_cnt = a.off[u + 1] - o0;
+        const int o1 = a.off[u + 1];
 #pragma unroll
-        for (int m = 0; m < MAXM; ++m) rowsel[m] = (m < m_cnt) ? a.asg[o0 + m] / a.k : 0;
-        rows_total = a.I;
-        gq = a.gate.q + (size_t)e * rows_total * (H / 2);
-        gs = a.gate.s + (size_t)e * rows_total * (H / 16);
-        uq = a.up.q + (size_t)e * rows_total * (H / 2);
-        us = a.up.s + (size_t)e * rows_total * (H / 16);
+        for (int m = 0; m < MAXM; ++m) rowsel[m] = a.rowtab[u * kMaxRows + m];
+        if (u >= U) return;
+        m_cnt = o1 - o0;
+        gq = a.gate.q + (size_t)e * a.I * (H / 2);
+        gs = a.gate.s + (size_t)e * a.I * (H / 16);
+        uq = a.up.q + (size_t)e * a.I * (H / 2);
+        us = a.up.s + (size_t)e * a.I * (H / 16);
         gts = a.gate.ts[e];
         uts = a.up.ts[e];
         hbase = a.h + (size_t)o0 * a.I;
         hstride = a.I;
         n0 = (b % nsr) * a.slab;
     } else {
-        b -= U * nsr;
+        b -= n_routed_blocks;
         if (a.sgate.q == nullptr || b >= a.Is / a.slab) return;
         m_cnt = a.K;
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) rowsel[m] = (m < m_cnt) ? m : 0;
-        rows_total = a.Is;
         gq = a.sgate.q; gs = a.sgate.s; uq = a.sup.q; us = a.sup.s;
         gts = a.sgate.ts[0];
         uts = a.sup.ts[0];
@@ -511,102 +607,187 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
             }
         }
     }
-    (void)rows_total;
 }
 
 // ---------------------------------------------------------------------------
 // k_down (+ combine)
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(kBlock) void k_down(DownArgs a) {
+constexpr int kDownWaves = kDownThreads / 64;
+constexpr int kDownBatch = 6;  // tasks per wave whose codes are in flight together
+
+// The h rows are processed in chunks that fit kDownHLdsBytes: positions
+// 0..n-1 are the routed slots in dedup order (row length I), n..n+K-1 the
+// shared expert's rows (row length Is).
+__global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
     constexpr int NH = kDownRowsPerBlock;
-    __shared__ float so[(kMaxRows * kMaxTopK + kMaxRows) * NH];
+    __shared__ float so[(kMaxSlots + kMaxRows) * NH];
+    __shared__ int s_uniq[kMaxSlots];
+    __shared__ int s_off[kMaxSlots + 1];
+    __shared__ int s_inv[kMaxSlots];
+    __shared__ float s_w[kMaxSlots];
+    __shared__ float s_y[kMaxRows * NH];
+    __shared__ int s_U;
+    extern __shared__ __align__(16) float hs[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int H = a.H, K = a.K, k = a.k;
-    const int U = a.meta[kMetaUnique];
+    const int H = a.H, K = a.K, k = a.k, n = K * k;
     const int n_base = blockIdx.x * NH;
     const bool has_sh = a.sdown.q != nullptr;
 
+    // routing metadata: independent loads, one round trip
+    for (int i = tid; i <= n; i += kDownThreads) {
+        if (i < n) {
+            s_uniq[i] = a.uniq[i];
+            s_inv[i] = a.inv[i];
+            s_w[i] = a.w[i];
+        }
+        s_off[i] = a.off[i];
+    }
+    if (tid == 0) s_U = *a.n_unique;
+    __syncthreads();
+    const int U = s_U;
+
+    const int RL = max(a.I, has_sh ? a.Is : 0);   // LDS row stride of staged h
+    const int CAP = (kDownHLdsBytes / 4) / RL;      // rows per chunk
+    const int total_rows = n + (has_sh ? K : 0);
     const int cprI = a.I >> 5;
     const int gI = max(1, NH / (64 / cprI));
     const int cprS = has_sh ? (a.Is >> 5) : 1;
     const int gS = has_sh ? max(1, NH / (64 / cprS)) : 0;
-    const int total = U * gI + gS;
 
-    for (int t = wave; t < total; t += kWaves) {
-        int cols, CPR, grp, m_cnt, e;
-        const float* hsrc;
-        float* obase;
-        const Fp4Mat* mat;
-        if (t < U * gI) {
-            const int u = t / gI;
-            grp = t % gI;
-            e = a.uniq[u];
-            const int p0 = a.off[u];
-            m_cnt = a.off[u + 1] - p0;
-            cols = a.I; CPR = cprI; mat = &a.down;
-            hsrc = a.h + (size_t)p0 * a.I;
-            obase = so + p0 * NH;
-        } else {
-            grp = t - U * gI;
-            e = 0;
-            m_cnt = K;
-            cols = a.Is; CPR = cprS; mat = &a.sdown;
-            hsrc = a.h_sh;
-            obase = so + (K * k) * NH;
+    for (int c0 = 0; c0 < total_rows; c0 += CAP) {
+        const int c1 = min(total_rows, c0 + CAP);
+        // routed experts with slots in [c0, c1): a contiguous range of u
+        int u_lo = 0, u_hi = 0;
+        if (c0 < n) {
+            while (u_lo < U && s_off[u_lo + 1] <= c0) ++u_lo;
+            u_hi = u_lo;
+            while (u_hi < U && s_off[u_hi] < min(c1, n)) ++u_hi;
         }
-        const int RPG = 64 / CPR;
-        const int q = lane / CPR, chunk = lane % CPR;
-        const int nl = grp * RPG + q;
-        const bool valid = nl < NH;
-        const int n = n_base + nl;
-        uint4 c = make_uint4(0, 0, 0, 0);
-        uint32_t sc = 0;
-        if (valid) {
-            c = *reinterpret_cast<const uint4*>(mat->q + ((size_t)e * H + n) * (cols / 2) + chunk * 16);
-            sc = *reinterpret_cast<const uint16_t*>(mat->s + ((size_t)e * H + n) * (cols / 16) + chunk * 2);
-        }
-        const float ts = mat->ts[e];
-        float wf[32];
-        fp4x8_to_f32(c.x, wf + 0); fp4x8_to_f32(c.y, wf + 8);
-        fp4x8_to_f32(c.z, wf + 16); fp4x8_to_f32(c.w, wf + 24);
-        const float s0 = e4m3_to_f32<0>(sc), s1 = e4m3_to_f32<1>(sc);
-        for (int m = 0; m < m_cnt; ++m) {
-            const float4* hp = reinterpret_cast<const float4*>(hsrc + (size_t)m * cols + chunk * 32);
-            float a0 = 0.f, a1 = 0.f;
+        const bool sh_here = has_sh && c1 > n;
+        const int nT = (u_hi - u_lo) * gI + (sh_here ? gS : 0);
+
+        // stage h rows [c0, c1) into LDS (row stride RL floats), every load of
+        // a pass in flight together
+        {
+            const int q4 = RL / 4;                  // float4 per staged row
+            const int nf4 = (c1 - c0) * q4;
+            constexpr int SU = 8;
+            for (int base = 0; base < nf4; base += SU * kDownThreads) {
+                float4 v[SU];
 #pragma unroll
-            for (int t4 = 0; t4 < 4; ++t4) {
-                const float4 hv = hp[t4];
-                a0 = fmaf(wf[4 * t4 + 0], hv.x, a0);
-                a0 = fmaf(wf[4 * t4 + 1], hv.y, a0);
-                a0 = fmaf(wf[4 * t4 + 2], hv.z, a0);
-                a0 = fmaf(wf[4 * t4 + 3], hv.w, a0);
-            }
+                for (int j = 0; j < SU; ++j) {
+                    const int f = base + j * kDownThreads + tid;
+                    v[j] = make_float4(0, 0, 0, 0);
+                    if (f < nf4) {
+                        const int rr = c0 + f / q4, c4 = f % q4;
+                        const bool shared_row = rr >= n;
+                        const int len4 = (shared_row ? a.Is : a.I) / 4;
+                        if (c4 < len4)
+                            v[j] = shared_row ? reinterpret_cast<const float4*>(a.h_sh + (size_t)(rr - n) * a.Is)[c4]
+                                              : reinterpret_cast<const float4*>(a.h + (size_t)rr * a.I)[c4];
+                    }
+                }
 #pragma unroll
-            for (int t4 = 4; t4 < 8; ++t4) {
-                const float4 hv = hp[t4];
-                a1 = fmaf(wf[4 * t4 + 0], hv.x, a1);
-                a1 = fmaf(wf[4 * t4 + 1], hv.y, a1);
-                a1 = fmaf(wf[4 * t4 + 2], hv.z, a1);
-                a1 = fmaf(wf[4 * t4 + 3], hv.w, a1);
+                for (int j = 0; j < SU; ++j) {
+                    const int f = base + j * kDownThreads + tid;
+                    if (f < nf4) reinterpret_cast<float4*>(hs)[f] = v[j];
+                }
             }
-            float p = fmaf(a1, s1, a0 * s0);
-            p = group_sum_rt(p, CPR);
-            if (valid && chunk == CPR - 1) obase[m * NH + nl] = p * ts;
         }
+
+        for (int tb = 0; tb * kDownWaves * kDownBatch < nT; ++tb) {
+            // codes and scales of this wave's batch of tasks
+            uint4 code[kDownBatch];
+            uint32_t scl[kDownBatch];
+#pragma unroll
+            for (int i = 0; i < kDownBatch; ++i) {
+                const int t = (tb * kDownBatch + i) * kDownWaves + wave;
+                code[i] = make_uint4(0, 0, 0, 0);
+                scl[i] = 0;
+                if (t < nT) {
+                    const bool routed = t < (u_hi - u_lo) * gI;
+                    const int CPR = routed ? cprI : cprS;
+                    const int grp = routed ? t % gI : t - (u_hi - u_lo) * gI;
+                    const int e = routed ? s_uniq[u_lo + t / gI] : 0;
+                    const Fp4Mat& mat = routed ? a.down : a.sdown;
+                    const int cols = routed ? a.I : a.Is;
+                    const int q = lane / CPR, chunk = lane % CPR;
+                    const int nl = grp * (64 / CPR) + q;
+                    if (nl < NH) {
+                        const size_t row = (size_t)e * H + n_base + nl;
+                        code[i] = *reinterpret_cast<const uint4*>(mat.q + row * (cols / 2) + chunk * 16);
+                        scl[i] = *reinterpret_cast<const uint16_t*>(mat.s + row * (cols / 16) + chunk * 2);
+                    }
+                }
+            }
+            if (tb == 0) __syncthreads();  // staged h visible to every wave
+#pragma unroll
+            for (int i = 0; i < kDownBatch; ++i) {
+                const int t = (tb * kDownBatch + i) * kDownWaves + wave;
+                if (t >= nT) break;
+                const bool routed = t < (u_hi - u_lo) * gI;
+                const int CPR = routed ? cprI : cprS;
+                const int grp = routed ? t % gI : t - (u_hi - u_lo) * gI;
+                const int u = u_lo + (routed ? t / gI : 0);
+                const int e = routed ? s_uniq[u] : 0;
+                const float ts = routed ? a.down.ts[e] : a.sdown.ts[0];
+                int p_lo, p_hi;
+                if (routed) { p_lo = max(s_off[u], c0); p_hi = min(s_off[u + 1], c1); }
+                else { p_lo = max(n, c0); p_hi = c1; }
+                const int q = lane / CPR, chunk = lane % CPR;
+                const int nl = grp * (64 / CPR) + q;
+                float wf[32];
+                fp4x8_to_f32(code[i].x, wf + 0); fp4x8_to_f32(code[i].y, wf + 8);
+                fp4x8_to_f32(code[i].z, wf + 16); fp4x8_to_f32(code[i].w, wf + 24);
+                const float s0 = e4m3_to_f32<0>(scl[i]), s1 = e4m3_to_f32<1>(scl[i]);
+                for (int pp = p_lo; pp < p_hi; ++pp) {
+                    const float4* hp = reinterpret_cast<const float4*>(hs + (size_t)(pp - c0) * RL + chunk * 32);
+                    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+                    for (int t4 = 0; t4 < 4; ++t4) {
+                        const float4 hv = hp[t4];
+                        a0 = fmaf(wf[4 * t4 + 0], hv.x, a0);
+                        a0 = fmaf(wf[4 * t4 + 1], hv.y, a0);
+                        a0 = fmaf(wf[4 * t4 + 2], hv.z, a0);
+                        a0 = fmaf(wf[4 * t4 + 3], hv.w, a0);
+                    }
+#pragma unroll
+                    for (int t4 = 4; t4 < 8; ++t4) {
+                        const float4 hv = hp[t4];
+                        a1 = fmaf(wf[4 * t4 + 0], hv.x, a1);
+                        a1 = fmaf(wf[4 * t4 + 1], hv.y, a1);
+                        a1 = fmaf(wf[4 * t4 + 2], hv.z, a1);
+                        a1 = fmaf(wf[4 * t4 + 3], hv.w, a1);
+                    }
+                    float p = fmaf(a1, s1, a0 * s0);
+                    p = group_sum_rt(p, CPR);
+                    if (nl < NH && chunk == CPR - 1) so[pp * NH + nl] = p * ts;
+                }
+            }
+        }
+        if (nT == 0) __syncthreads();  // (the batch loop did not run: publish the staging)
+        __syncthreads();  // chunk done before its LDS rows are replaced
     }
-    __syncthreads();
 
     // combine: y = rs * sum_j w_j o_j (rank order) + shared (+ residual)
-    for (int i = tid; i < K * NH; i += kBlock) {
-        const int r = i / NH, nl = i % NH, n = n_base + nl;
+    for (int i = tid; i < K * NH; i += kDownThreads) {
+        const int r = i / NH, nl = i % NH, nn = n_base + nl;
         float acc = 0.0f;
-        for (int j = 0; j < k; ++j) acc = fmaf(a.w[r * k + j], so[a.inv[r * k + j] * NH + nl], acc);
+        for (int j = 0; j < k; ++j) acc = fmaf(s_w[r * k + j], so[s_inv[r * k + j] * NH + nl], acc);
         float y = a.rs * acc;
-        if (has_sh) y += so[(K * k + r) * NH + nl];
-        if (a.residual) y += bf16_to_f32(a.residual[(size_t)r * H + n]);
-        a.y32[(size_t)r * H + n] = y;
-        if (a.y) a.y[(size_t)r * H + n] = f32_to_bf16_rne(y);
+        if (has_sh) y += so[(n + r) * NH + nl];
+        if (a.residual) y += bf16_to_f32(a.residual[(size_t)r * H + nn]);
+        a.y32[(size_t)r * H + nn] = y;
+        if (a.y) a.y[(size_t)r * H + nn] = f32_to_bf16_rne(y);
+        s_y[i] = y;
+    }
+    __syncthreads();
+    // per-row partial sum of squares of this workgroup's columns (fixed order)
+    if (a.ssq && tid < K) {
+        float ss = 0.0f;
+        for (int nl = 0; nl < NH; ++nl) ss = fmaf(s_y[tid * NH + nl], s_y[tid * NH + nl], ss);
+        a.ssq[tid * gridDim.x + blockIdx.x] = ss;
     }
 }
 
@@ -656,9 +837,16 @@ hipError_t launch_init(int32_t* meta, hipStream_t st) {
 constexpr size_t kRouteMaxDynLds = 96 * 1024;
 
 hipError_t init_kernels() {
-    static hipError_t once = hipFuncSetAttribute(reinterpret_cast<const void*>(k_route),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)kRouteMaxDynLds);
+    static hipError_t once = [] {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_route),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRouteMaxDynLds);
+        if (e != hipSuccess) return e;
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_select),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRouteMaxDynLds);
+        if (e != hipSuccess) return e;
+        return hipFuncSetAttribute(reinterpret_cast<const void*>(k_down),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDownHLdsBytes);
+    }();
     return once;
 }
 
@@ -675,17 +863,18 @@ hipError_t launch(Kern k, dim3 grid, dim3 block, size_t smem, hipStream_t st, co
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t st, const Timing* t) {
     const size_t xbytes = (size_t)a.K * a.H * 2;
-    const size_t smem = xbytes > sizeof(SelectSmem) ? xbytes : sizeof(SelectSmem);
+    const size_t sel = select_smem_bytes(a.K, a.E);
+    const size_t smem = xbytes > sel ? xbytes : sel;
     const int grid = (a.E + kWaves - 1) / kWaves;
     return launch(k_route, dim3(grid), dim3(kBlock), smem, st, t, a);
 }
 
 hipError_t launch_select(const RouteArgs& a, hipStream_t st) {
-    return launch(k_select, dim3(1), dim3(kBlock), sizeof(SelectSmem), st, nullptr, a);
+    return launch(k_select, dim3(1), dim3(kBlock), select_smem_bytes(a.K, a.E), st, nullptr, a);
 }
 
-hipError_t launch_gateup(const GateUpArgs& a, int max_unique, hipStream_t st, const Timing* t) {
-    const int grid = max_unique * (a.I / a.slab) + (a.sgate.q ? a.Is / a.slab : 0);
+hipError_t launch_gateup(const GateUpArgs& a, hipStream_t st, const Timing* t) {
+    const int grid = a.max_unique * (a.I / a.slab) + (a.sgate.q ? a.Is / a.slab : 0);
     const dim3 g(grid > 0 ? grid : 1), b(kBlock);
     const int M = a.K;
     if (M <= 1) return launch(k_gateup<1>, g, b, 0, st, t, a);
@@ -696,7 +885,7 @@ hipError_t launch_gateup(const GateUpArgs& a, int max_unique, hipStream_t st, co
 }
 
 hipError_t launch_down(const DownArgs& a, hipStream_t st, const Timing* t) {
-    return launch(k_down, dim3(a.H / kDownRowsPerBlock), dim3(kBlock), 0, st, t, a);
+    return launch(k_down, dim3(a.H / kDownRowsPerBlock), dim3(kDownThreads), kDownHLdsBytes, st, t, a);
 }
 
 hipError_t launch_dequant(Fp4Mat m, int n_experts, int rows, int cols, float* out, hipStream_t st) {

@@ -12,6 +12,10 @@ Comparison rules (written out here and in the tests):
   * weights: |dw| <= 1e-6 |w| + 2 * (logit tolerance) * w;
   * output: max|y32 - y_oracle| <= 2e-3 * max|y_oracle| over the compared
     rows; y (bf16) is the round-to-nearest-even of y32.
+  * chained layers: a row whose bf16 input already differs from the
+    oracle's (a rounding-boundary flip of an earlier layer's output) is held
+    to 1e-2 * max|y_oracle| instead, since the two sides no longer evaluate
+    the same input.
 """
 from __future__ import annotations
 
@@ -23,6 +27,7 @@ from speculative_block_verify_amd import api
 from tests import refdecode as ref
 
 Y_TOL = 2e-3
+CHAIN_Y_TOL = 1e-2
 LOGIT_RTOL = 1e-5
 
 
@@ -110,7 +115,7 @@ def bf16_of(y32: np.ndarray) -> np.ndarray:
 
 
 def compare_layer(gpu, orec, k: int, n_experts: int, score_fn: int = 0, bias=None,
-                  logit_tol=None, label="", rows=None):
+                  logit_tol=None, label="", rows=None, y_tol=None):
     """Assert the rules above; return a small report dict.  rows (bool mask)
     restricts the comparison to some rows (the dedup lists, which mix all
     rows, are then not compared)."""
@@ -120,7 +125,9 @@ def compare_layer(gpu, orec, k: int, n_experts: int, score_fn: int = 0, bias=Non
         orec = {kk: orec[kk][sel] for kk in ("logits", "ids", "w", "y")}
         if logit_tol is not None:
             logit_tol = np.asarray(logit_tol)[sel]
-        rep = compare_layer(gpu, orec, k, n_experts, score_fn, bias, logit_tol, label, None)
+        if y_tol is not None:
+            y_tol = np.asarray(y_tol)[sel]
+        rep = compare_layer(gpu, orec, k, n_experts, score_fn, bias, logit_tol, label, None, y_tol)
         rep["partial_rows"] = True
         return rep
     K = orec["logits"].shape[0]
@@ -152,9 +159,13 @@ def compare_layer(gpu, orec, k: int, n_experts: int, score_fn: int = 0, bias=Non
     assert np.all(np.abs(gpu["w"][ok] - orec["w"][ok]) <= wt), label + " weights"
     yo = orec["y"]
     scale = np.abs(yo).max()
-    err = np.abs(gpu["y32"].astype(np.float64) - yo)[ok]
+    rowtol = np.full(K, Y_TOL) if y_tol is None else np.asarray(y_tol, np.float64)
+    errs = np.abs(gpu["y32"].astype(np.float64) - yo)
+    roww = errs.max(axis=1)
+    bad = ok & (roww > rowtol * scale)
+    assert not bad.any(), "%s y32 max err %s > %s" % (label, roww[bad], rowtol[bad] * scale)
+    err = errs[ok]
     maxerr = float(err.max()) if err.size else 0.0
-    assert maxerr <= Y_TOL * scale, "%s y32 max err %.3g > %.3g" % (label, maxerr, Y_TOL * scale)
     rel_l2 = float(np.linalg.norm(err) / max(np.linalg.norm(yo[ok]), 1e-30)) if err.size else 0.0
     return {"max_abs_over_max_ref": maxerr / scale, "rel_l2": rel_l2, "near_ties": int(tie.sum())}
 
@@ -179,7 +190,8 @@ def compare_stack(gpu, layers_host, x0: np.ndarray, k: int, n_experts: int, eps:
         xr = ref.bf16_to_f64(xo)
         wr_max = np.abs(ref.bf16_to_f64(np.asarray(w["router_w"]).view(np.uint16))).max(axis=0)
         ltol = (np.abs(xg - xr) * wr_max[None, :]).sum(axis=1) * 1.01
-        rep = compare_layer(g, orec, k, n_experts, score_fn, None, ltol, "%s layer %d" % (label, l), alive)
+        ytol = np.where((g["x_in"].view(np.uint16) != xo).any(axis=1), CHAIN_Y_TOL, Y_TOL)
+        rep = compare_layer(g, orec, k, n_experts, score_fn, None, ltol, "%s layer %d" % (label, l), alive, ytol)
         rep["x_in_bf16_diffs"] = int((g["x_in"].view(np.uint16) != xo).sum())
         reps.append(rep)
         diverged = np.any(g["ids"] != orec["ids"], axis=1)

@@ -81,7 +81,7 @@ def _route_case(K, E, k, logits, score_fn=0, bias=None, norm=1):
     np.testing.assert_array_equal(got["inv"], d["inv"])
 
 
-@pytest.mark.parametrize("K,E,k", [(1, 16, 2), (2, 256, 8), (16, 256, 8), (4, 1024, 32), (3, 64, 64), (5, 7, 3)])
+@pytest.mark.parametrize("K,E,k", [(1, 16, 2), (2, 256, 8), (16, 256, 8), (4, 1024, 32), (3, 32, 32), (5, 7, 3)])
 def test_route_random_logits(K, E, k):
     say("case: route K=%d E=%d k=%d" % (K, E, k))
     rng = np.random.default_rng(K * 1000 + E + k)
