@@ -113,7 +113,6 @@ struct Layout {
     int32_t* off;
     int32_t* asg;
     int32_t* inv;
-    int32_t* rowtab;
     float* h;
     float* h_sh;
     float* ssq;
@@ -129,7 +128,7 @@ Layout layout(const moe_cfg* c, void* base) {
     size_t o = 0;
     Layout L{};
     auto take = [&](size_t bytes) { char* r = p ? p + o : nullptr; o += align256(bytes); return r; };
-    L.meta = reinterpret_cast<int32_t*>(take(moe::kMetaWords * 4));
+    L.meta = reinterpret_cast<int32_t*>(take(16 * 4));
     L.logits = reinterpret_cast<float*>(take(R * E * 4));
     L.ids = reinterpret_cast<int32_t*>(take(R * k * 4));
     L.w = reinterpret_cast<float*>(take(R * k * 4));
@@ -137,7 +136,6 @@ Layout layout(const moe_cfg* c, void* base) {
     L.off = reinterpret_cast<int32_t*>(take((R * k + 1) * 4));
     L.asg = reinterpret_cast<int32_t*>(take(R * k * 4));
     L.inv = reinterpret_cast<int32_t*>(take(R * k * 4));
-    L.rowtab = reinterpret_cast<int32_t*>(take(R * k * moe::kMaxRows * 4));
     L.h = reinterpret_cast<float*>(take(R * k * I * 4));
     L.h_sh = reinterpret_cast<float*>(take(R * (Is ? Is : 1) * 4));
     L.ssq = reinterpret_cast<float*>(take(R * (H / moe::kDownRowsPerBlock) * 4));
@@ -164,50 +162,50 @@ struct LayerIO {
 int enqueue_layer(const moe_cfg* c, const moe_layer_weights* w, const LayerIO& io, int K, const Layout& L,
                   hipStream_t st, const moe::Timing* tm = nullptr) {
     hipError_t e;
-    moe::RouteArgs ra{};
+    const bool has_sh = c->shared_inter > 0;
+    const moe::Fp4Mat none{nullptr, nullptr, nullptr};
+
+    moe::RouterArgs ra{};
     ra.x_in = io.x_in;
     ra.y_prev = io.y_prev;
+    ra.ssq = L.ssq;
     ra.x_out = L.xbuf;
     ra.eps = c->rms_eps;
     ra.wr = w->router_w;
-    ra.bias = w->router_bias;
     ra.logits = L.logits;
-    ra.ids = L.ids;
-    ra.w = L.w;
-    ra.meta = L.meta;
-    ra.n_unique = L.meta + moe::kMetaUnique;
-    ra.uniq = L.uniq;
-    ra.off = L.off;
-    ra.asg = L.asg;
-    ra.inv = L.inv;
-    ra.rowtab = L.rowtab;
-    ra.ssq = L.ssq;
-    ra.K = K; ra.H = c->hidden; ra.E = c->n_experts; ra.k = c->top_k;
-    ra.score_fn = c->score_fn; ra.norm_topk = c->norm_topk;
-    if ((e = moe::launch_route(ra, st, tm ? &tm[0] : nullptr)) != hipSuccess) return hip_fail(e, "route launch");
+    ra.sgate = has_sh ? mat(w->sh_gate) : none;
+    ra.sup = has_sh ? mat(w->sh_up) : none;
+    ra.h_sh = L.h_sh;
+    ra.K = K; ra.H = c->hidden; ra.E = c->n_experts; ra.Is = c->shared_inter;
+    ra.slab = moe::gateup_slab_rows(c->hidden);
+    if ((e = moe::launch_router(ra, st, tm ? &tm[0] : nullptr)) != hipSuccess) return hip_fail(e, "router launch");
 
     moe::GateUpArgs ga{};
+    ga.sel.logits = L.logits;
+    ga.sel.bias = w->router_bias;
+    ga.sel.ids = L.ids; ga.sel.w = L.w;
+    ga.sel.n_unique = L.meta + moe::kMetaUnique;
+    ga.sel.uniq = L.uniq; ga.sel.off = L.off; ga.sel.asg = L.asg; ga.sel.inv = L.inv;
+    ga.sel.K = K; ga.sel.E = c->n_experts; ga.sel.k = c->top_k;
+    ga.sel.score_fn = c->score_fn; ga.sel.norm_topk = c->norm_topk;
     ga.x = io.y_prev ? L.xbuf : io.x_in;
     ga.gate = mat(w->gate); ga.up = mat(w->up);
-    ga.sgate = mat(w->sh_gate); ga.sup = mat(w->sh_up);
-    if (c->shared_inter == 0) { ga.sgate = moe::Fp4Mat{nullptr, nullptr, nullptr}; ga.sup = ga.sgate; }
-    ga.n_unique = L.meta + moe::kMetaUnique;
-    ga.uniq = L.uniq; ga.off = L.off; ga.rowtab = L.rowtab;
-    ga.h = L.h; ga.h_sh = L.h_sh;
-    ga.K = K; ga.H = c->hidden; ga.I = c->inter; ga.Is = c->shared_inter; ga.k = c->top_k;
+    ga.h = L.h;
+    ga.K = K; ga.H = c->hidden; ga.I = c->inter;
     ga.slab = moe::gateup_slab_rows(c->hidden);
-    ga.max_unique = std::min(c->n_experts, K * c->top_k);
-    if ((e = moe::launch_gateup(ga, st, tm ? &tm[1] : nullptr)) != hipSuccess) return hip_fail(e, "gate/up launch");
+    const int max_unique = std::min(c->n_experts, K * c->top_k);
+    if ((e = moe::launch_gateup(ga, max_unique, st, tm ? &tm[1] : nullptr)) != hipSuccess)
+        return hip_fail(e, "gate/up launch");
 
     moe::DownArgs da{};
     da.down = mat(w->down);
-    da.sdown = c->shared_inter ? mat(w->sh_down) : moe::Fp4Mat{nullptr, nullptr, nullptr};
+    da.sdown = has_sh ? mat(w->sh_down) : none;
     da.n_unique = L.meta + moe::kMetaUnique;
     da.uniq = L.uniq; da.off = L.off; da.inv = L.inv;
-    da.ssq = L.ssq;
     da.w = L.w; da.h = L.h; da.h_sh = L.h_sh;
     da.residual = io.residual;
     da.y32 = io.y32; da.y = io.y;
+    da.ssq = L.ssq;
     da.K = K; da.H = c->hidden; da.I = c->inter; da.Is = c->shared_inter; da.k = c->top_k;
     da.rs = c->routed_scale;
     if ((e = moe::launch_down(da, st, tm ? &tm[2] : nullptr)) != hipSuccess) return hip_fail(e, "down launch");
@@ -264,7 +262,6 @@ int enqueue_stack(const moe_cfg* c, const moe_layer_weights* layers, int n_layer
     const Layout L = layout(c, ws);
     hipError_t e = moe::init_kernels();
     if (e != hipSuccess) return hip_fail(e, "kernel attributes");
-    if ((e = moe::launch_init(L.meta, st)) != hipSuccess) return hip_fail(e, "init launch");
     for (int l = 0; l < n_layers; ++l) {
         const bool last = (l == n_layers - 1);
         LayerIO io{};
@@ -320,7 +317,6 @@ int moe_verify_layer(const moe_cfg* cfg, const moe_layer_weights* w, const uint1
     const Layout L = layout(cfg, workspace);
     hipError_t e = moe::init_kernels();
     if (e != hipSuccess) return hip_fail(e, "kernel attributes");
-    if ((e = moe::launch_init(L.meta, st)) != hipSuccess) return hip_fail(e, "init launch");
     LayerIO io{};
     io.x_in = x;
     io.y_prev = nullptr;
@@ -355,14 +351,16 @@ int moe_verify_route(const moe_cfg* cfg, const float* logits, const float* bias,
     if (cfg->score_fn == MOE_SCORE_SOFTMAX && bias) return fail(MOE_ERR_INVALID, "bias given with softmax scoring");
     if (!out || !out->ids || !out->w || !out->n_unique || !out->uniq || !out->off || !out->asg || !out->inv)
         return fail(MOE_ERR_INVALID, "route outputs must all be non-NULL");
-    moe::RouteArgs ra{};
+    hipError_t e = moe::init_kernels();
+    if (e != hipSuccess) return hip_fail(e, "kernel attributes");
+    moe::SelectArgs ra{};
+    ra.logits = logits;
     ra.bias = bias;
-    ra.logits = const_cast<float*>(logits);
     ra.ids = out->ids; ra.w = out->w; ra.n_unique = out->n_unique;
     ra.uniq = out->uniq; ra.off = out->off; ra.asg = out->asg; ra.inv = out->inv;
-    ra.K = K; ra.H = cfg->hidden; ra.E = cfg->n_experts; ra.k = cfg->top_k;
+    ra.K = K; ra.E = cfg->n_experts; ra.k = cfg->top_k;
     ra.score_fn = cfg->score_fn; ra.norm_topk = cfg->norm_topk;
-    hipError_t e = moe::launch_select(ra, static_cast<hipStream_t>(stream));
+    e = moe::launch_select(ra, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "select launch");
     return MOE_OK;
 }

@@ -11,13 +11,15 @@ namespace moe {
 constexpr int kMaxRows = 16;       // K
 constexpr int kMaxTopK = 32;       // k
 constexpr int kMaxExperts = 1024;  // E
+constexpr int kMaxSlots = kMaxRows * kMaxTopK;
 constexpr int kBlock = 256;        // threads per workgroup (4 wave64)
 constexpr int kWaves = kBlock / 64;
 constexpr int kRowsPerWave = 4;    // weight rows each wave keeps in flight in gate/up
 constexpr int kDownRowsPerBlock = 8;
 constexpr int kDownThreads = 512;  // 8 wave64 per down workgroup
 constexpr int kDownHLdsBytes = 64 * 1024;  // h rows staged in LDS per chunk
-constexpr int kMaxSlots = kMaxRows * kMaxTopK;
+constexpr int kGateUpMaxGrid = 1024;       // routed gate/up workgroups loop over work items
+constexpr int kMetaUnique = 0;             // workspace word holding the unique-expert count
 
 struct Fp4Mat {
     const uint8_t* q;
@@ -25,43 +27,43 @@ struct Fp4Mat {
     const float* ts;
 };
 
-// Route metadata words kept in the workspace.
-enum MetaWord { kMetaUnique = 0, kMetaCounter = 1, kMetaWords = 16 };
-
-struct RouteArgs {
-    const uint16_t* x_in;   // bf16 [K][H], read when y_prev == nullptr
-    const float* y_prev;    // fp32 [K][H] to RMS-normalise into x, or nullptr
-    uint16_t* x_out;        // bf16 [K][H] normalised x (written when y_prev != nullptr)
-    float eps;
-    const uint16_t* wr;     // bf16 [E][H]
+// Inputs and outputs of the selection step (top-k + dedup).
+struct SelectArgs {
+    const float* logits;    // [K][E]
     const float* bias;      // [E] or nullptr
-    float* logits;          // [K][E]
     int32_t* ids;           // [K][k]
     float* w;               // [K][k]
-    int32_t* meta;          // MetaWord (route counter)
-    int32_t* n_unique;      // [1] number of distinct experts
+    int32_t* n_unique;      // [1]
     int32_t* uniq;          // [K*k]
     int32_t* off;           // [K*k+1]
     int32_t* asg;           // [K*k]
     int32_t* inv;           // [K*k]
-    int32_t* rowtab;        // [K*k][kMaxRows] rows of x assigned to each unique expert
-    const float* ssq;       // [K][H / kDownRowsPerBlock] partial sums of squares of y_prev
-    int K, H, E, k, score_fn, norm_topk;
+    int K, E, k, score_fn, norm_topk;
 };
 
+// Router GEMV (+ the shared expert's gate/up, which needs only x).
+struct RouterArgs {
+    const uint16_t* x_in;   // bf16 [K][H], read when y_prev == nullptr
+    const float* y_prev;    // fp32 [K][H] to RMS-normalise into x, or nullptr
+    const float* ssq;       // [K][H / kDownRowsPerBlock] partial sums of squares of y_prev
+    uint16_t* x_out;        // bf16 [K][H] normalised x (written when y_prev != nullptr)
+    float eps;
+    const uint16_t* wr;     // bf16 [E][H]
+    float* logits;          // [K][E]
+    Fp4Mat sgate, sup;      // [1][Is][H/2] (q == nullptr: no shared expert)
+    float* h_sh;            // [K][Is]
+    int K, H, E, Is;
+    int slab;               // shared gate/up rows per workgroup
+};
+
+// Routed gate/up + SwiGLU; every workgroup recomputes the selection.
 struct GateUpArgs {
+    SelectArgs sel;         // its outputs are written by workgroup 0 only
     const uint16_t* x;      // bf16 [K][H]
     Fp4Mat gate, up;        // [E][I][H/2]
-    Fp4Mat sgate, sup;      // [1][Is][H/2] (q == nullptr: no shared expert)
-    const int32_t* n_unique;
-    const int32_t* uniq;
-    const int32_t* off;
-    const int32_t* rowtab;  // [K*k][kMaxRows]
     float* h;               // [K*k][I], indexed by position in asg
-    float* h_sh;            // [K][Is]
-    int K, H, I, Is, k;
-    int slab;               // weight rows (of gate and of up) per workgroup
-    int max_unique;         // min(E, K*k): routed workgroups = max_unique * (I / slab)
+    int K, H, I;
+    int slab;               // weight rows (of gate and of up) per work item
 };
 
 struct DownArgs {
@@ -90,17 +92,16 @@ struct Timing {
 };
 
 // Launchers (moe_kernels.hip).  Each returns the hipError_t of the launch.
-hipError_t launch_init(int32_t* meta, hipStream_t st);
-hipError_t launch_route(const RouteArgs& a, hipStream_t st, const Timing* t = nullptr);
-hipError_t launch_select(const RouteArgs& a, hipStream_t st);  // logits given
-hipError_t launch_gateup(const GateUpArgs& a, hipStream_t st, const Timing* t = nullptr);
+hipError_t launch_router(const RouterArgs& a, hipStream_t st, const Timing* t = nullptr);
+hipError_t launch_select(const SelectArgs& a, hipStream_t st);  // logits given
+hipError_t launch_gateup(const GateUpArgs& a, int max_unique, hipStream_t st, const Timing* t = nullptr);
 hipError_t launch_down(const DownArgs& a, hipStream_t st, const Timing* t = nullptr);
 hipError_t launch_dequant(Fp4Mat m, int n_experts, int rows, int cols, float* out, hipStream_t st);
 
 // One-time kernel attributes (dynamic LDS sizes).
 hipError_t init_kernels();
 
-// Workgroups / slab size the gate/up launch uses for hidden H.
+// Rows of gate (and of up) one gate/up work item covers at hidden H.
 int gateup_slab_rows(int H);
 
 }  // namespace moe

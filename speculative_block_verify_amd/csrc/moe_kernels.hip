@@ -1,14 +1,16 @@
 // gfx950 (CDNA4) kernels of the NVFP4 MoE block-verify layer.
 //
 // Per layer three launches:
-//   k_route   router GEMV (one wave per expert row, bf16 x staged in LDS,
-//             v_dot2_f32_bf16), then the last workgroup to finish selects
-//             top-k per row with a DPP wave argmax and builds the dedup CSR
-//             (PR #844 section 4 item 3 router tail; section 8: the stock
-//             gather reads a repeated expert once per slot -- here each
-//             unique expert is streamed once);
-//   k_gateup  one workgroup per (unique expert, slab of intermediate rows):
-//             128-bit loads of packed E2M1 codes, in-register decode with
+//   k_router  router GEMV (one wave per expert row, bf16 x staged in LDS,
+//             v_dot2_f32_bf16) and, in further workgroups, the shared
+//             expert's gate/up, which also needs only x;
+//   k_gateup  every workgroup first repeats the selection from the logits:
+//             top-k per row with a DPP wave argmax (PR #844 section 4 item 3
+//             router tail: argPartition + takeAlong) and the dedup CSR
+//             (section 8: the stock gather reads a repeated expert once per
+//             slot -- here each unique expert is streamed once); then work
+//             items (unique expert, slab of intermediate rows): 128-bit loads
+//             of packed E2M1 codes, in-register decode with
 //             v_cvt_scalef32_pk_bf16_fp4, dot2 against x held in registers,
 //             E4M3 block scale per 16 columns, tensor scale after the lane
 //             reduction, SwiGLU epilogue (silu(gate) * up, PR #844 section 4
@@ -20,7 +22,10 @@
 //             (PR #844 section 4 item 4 and section 5 expression order).
 // The routed work list is data dependent (the number of unique experts is
 // known only on the device), so the gate/up grid is sized for the largest
-// possible count and surplus workgroups exit at once.
+// possible count (capped; workgroups loop) and surplus workgroups finish
+// after the selection.  No kernel uses a device-wide fence: on this part an
+// agent-scope release writes back the L2 and costs far more than a launch
+// boundary inside a graph.
 #include <hip/hip_ext.h>
 
 #include "moe_internal.h"
@@ -175,16 +180,18 @@ __device__ __forceinline__ float group_sum_rt(float v, int G) {
 }
 
 // ---------------------------------------------------------------------------
-// selection + dedup (one workgroup)
+// selection + dedup (one workgroup of kBlock threads)
 // ---------------------------------------------------------------------------
 
 struct SelectSmem {
     int32_t sel[kMaxSlots];
     float w[kMaxSlots];
     int32_t asg[kMaxSlots];
+    int32_t uniq[kMaxSlots];
     int32_t off[kMaxSlots + 1];
     int32_t cnt[kMaxExperts];
     int32_t start[kMaxExperts];
+    int32_t n_unique;
     float lg[1];  // K * E logits follow (dynamic tail)
 };
 
@@ -213,7 +220,7 @@ __device__ __forceinline__ void stage_floats(float* dst, const float* src, int n
 // Top-k of row r by (key desc, index asc) with one wave.  Lane l owns experts
 // l*P .. l*P+P-1 (contiguous), so among equal keys the lowest lane holding
 // the maximum also holds the lowest index.  lr: the row's logits in LDS.
-__device__ void wave_select_row(const RouteArgs& a, const float* lr, int r, SelectSmem& sm) {
+__device__ void wave_select_row(const SelectArgs& a, const float* lr, int r, SelectSmem& sm) {
     const int lane = threadIdx.x & 63;
     const int E = a.E, k = a.k;
     const int P = (E + 63) >> 6;
@@ -279,13 +286,13 @@ __device__ void wave_select_row(const RouteArgs& a, const float* lr, int r, Sele
     }
 }
 
-// All rows' top-k, then the canonical dedup CSR and the per-expert row
-// table.  Called by a whole workgroup of kBlock threads; logits may be
-// global memory.
-__device__ void select_and_dedup(const RouteArgs& a, const float* logits, SelectSmem& sm) {
+// All rows' top-k, then the canonical dedup CSR, left in LDS (sm.uniq,
+// sm.off, sm.asg, sm.n_unique) and, if write_global, also in the SelectArgs
+// outputs.  Returns the number of unique experts.
+__device__ int select_and_dedup(const SelectArgs& a, SelectSmem& sm, bool write_global) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int K = a.K, k = a.k, E = a.E, n = K * k;
-    stage_floats(sm.lg, logits, K * E, tid, kBlock);
+    stage_floats(sm.lg, a.logits, K * E, tid, kBlock);
     for (int e = tid; e < E; e += kBlock) sm.cnt[e] = 0;
     __syncthreads();
     for (int r = wave; r < K; r += kWaves) wave_select_row(a, sm.lg + r * E, r, sm);
@@ -306,72 +313,154 @@ __device__ void select_and_dedup(const RouteArgs& a, const float* logits, Select
             if (e < E) {
                 const int cn = sm.cnt[e];
                 sm.start[e] = cs;
-                if (cn) { a.uniq[fs] = e; a.off[fs] = cs; sm.off[fs] = cs; }
+                if (cn) { sm.uniq[fs] = e; sm.off[fs] = cs; }
                 cs += cn;
                 fs += (cn > 0);
             }
         }
         const int U = __builtin_amdgcn_readlane(fi, 63);
-        if (lane == 0) { *a.n_unique = U; a.off[U] = n; sm.off[U] = n; sm.cnt[0] = U; }
+        if (lane == 0) { sm.n_unique = U; sm.off[U] = n; }
     }
     __syncthreads();
-    const int U = sm.cnt[0];
+    const int U = sm.n_unique;
     for (int s = tid; s < n; s += kBlock) {
         const int e = sm.sel[s];
         int rank = 0;
         for (int t = 0; t < s; ++t) rank += (sm.sel[t] == e);
         const int pos = sm.start[e] + rank;
         sm.asg[pos] = s;
-        a.asg[pos] = s;
-        a.inv[s] = pos;
-        a.ids[s] = e;
-        a.w[s] = sm.w[s];
+        if (write_global) {
+            a.asg[pos] = s;
+            a.inv[s] = pos;
+            a.ids[s] = e;
+            a.w[s] = sm.w[s];
+        }
+    }
+    if (write_global) {
+        for (int u = tid; u <= U; u += kBlock) {
+            if (u < U) a.uniq[u] = sm.uniq[u];
+            a.off[u] = sm.off[u];
+        }
+        if (tid == 0) *a.n_unique = U;
     }
     __syncthreads();
-    if (a.rowtab) {
-        for (int i = tid; i < U * K; i += kBlock) {
-            const int u = i / K, m = i % K;
-            const int o0 = sm.off[u], cnt = sm.off[u + 1] - o0;
-            a.rowtab[u * kMaxRows + m] = (m < cnt) ? sm.asg[o0 + m] / k : 0;
+    return U;
+}
+
+// Selection from caller-provided logits (one workgroup).
+__global__ __launch_bounds__(kBlock) void k_select(SelectArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    SelectSmem& sm = *reinterpret_cast<SelectSmem*>(smem);
+    select_and_dedup(a, sm, true);
+}
+
+// ---------------------------------------------------------------------------
+// gate/up tile: kWaves*kRowsPerWave*RPW rows of gate and of up for up to
+// MAXM rows of x; h = silu(x.Wg) * (x.Wu) in fp32
+// ---------------------------------------------------------------------------
+
+struct GateUpCodes {
+    uint4 gc[kRowsPerWave], uc[kRowsPerWave];
+    uint32_t gsc[kRowsPerWave], usc[kRowsPerWave];
+};
+
+// lane -> (weight row inside a wave load, 32-column chunk)
+__device__ __forceinline__ void gu_lane(int H, int lane, int& CPR, int& RPW, int& q, int& chunk) {
+    CPR = H >> 5;   // chunks (16 code bytes) per weight row
+    RPW = 64 / CPR; // weight rows per wave load
+    q = lane / CPR;
+    chunk = lane % CPR;
+}
+
+__device__ __forceinline__ GateUpCodes gateup_load(const uint8_t* gq, const uint8_t* gs, const uint8_t* uq,
+                                                  const uint8_t* us, int H, int n0) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int CPR, RPW, q, chunk;
+    gu_lane(H, lane, CPR, RPW, q, chunk);
+    GateUpCodes c;
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+        const int n = n0 + (wave * kRowsPerWave + i) * RPW + q;
+        c.gc[i] = *reinterpret_cast<const uint4*>(gq + (size_t)n * (H / 2) + chunk * 16);
+        c.uc[i] = *reinterpret_cast<const uint4*>(uq + (size_t)n * (H / 2) + chunk * 16);
+        c.gsc[i] = *reinterpret_cast<const uint16_t*>(gs + (size_t)n * (H / 16) + chunk * 2);
+        c.usc[i] = *reinterpret_cast<const uint16_t*>(us + (size_t)n * (H / 16) + chunk * 2);
+    }
+    return c;
+}
+
+// x: generic pointer to bf16 [.][H] (global or LDS); rowsel[m] its rows.
+template <int MAXM>
+__device__ __forceinline__ void gateup_compute(const GateUpCodes& c, float gts, float uts, int H, int n0,
+                                               const uint16_t* x, const int* rowsel, int m_cnt, float* hbase,
+                                               int hstride) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int CPR, RPW, q, chunk;
+    gu_lane(H, lane, CPR, RPW, q, chunk);
+    // this lane's 32 columns of every assigned row of x, as bf16 pairs
+    uint32_t xr[MAXM][16];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+        if (m < m_cnt) {
+            const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)rowsel[m] * H + chunk * 32);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint4 v = src[t];
+                xr[m][4 * t + 0] = v.x; xr[m][4 * t + 1] = v.y;
+                xr[m][4 * t + 2] = v.z; xr[m][4 * t + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 16; ++t) xr[m][t] = 0u;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+        const int n = n0 + (wave * kRowsPerWave + i) * RPW + q;
+        bf16x2_t wg[16], wu[16];
+        fp4x8_to_bf16(c.gc[i].x, wg + 0); fp4x8_to_bf16(c.gc[i].y, wg + 4);
+        fp4x8_to_bf16(c.gc[i].z, wg + 8); fp4x8_to_bf16(c.gc[i].w, wg + 12);
+        fp4x8_to_bf16(c.uc[i].x, wu + 0); fp4x8_to_bf16(c.uc[i].y, wu + 4);
+        fp4x8_to_bf16(c.uc[i].z, wu + 8); fp4x8_to_bf16(c.uc[i].w, wu + 12);
+        const float sg0 = e4m3_to_f32<0>(c.gsc[i]), sg1 = e4m3_to_f32<1>(c.gsc[i]);
+        const float su0 = e4m3_to_f32<0>(c.usc[i]), su1 = e4m3_to_f32<1>(c.usc[i]);
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            if (m < m_cnt) {
+                float g0 = 0.f, g1 = 0.f, v0 = 0.f, v1 = 0.f;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    g0 = dot2(wg[t], as_bf16x2(xr[m][t]), g0);
+                    v0 = dot2(wu[t], as_bf16x2(xr[m][t]), v0);
+                    g1 = dot2(wg[t + 8], as_bf16x2(xr[m][t + 8]), g1);
+                    v1 = dot2(wu[t + 8], as_bf16x2(xr[m][t + 8]), v1);
+                }
+                float pg = fmaf(g1, sg1, g0 * sg0);
+                float pu = fmaf(v1, su1, v0 * su0);
+                pg = group_sum_rt(pg, CPR);
+                pu = group_sum_rt(pu, CPR);
+                if (chunk == CPR - 1) {
+                    const float g = pg * gts, v = pu * uts;
+                    hbase[(size_t)m * hstride + n] = g / (1.0f + expf(-g)) * v;
+                }
+            }
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// k_init: clear the route counter at the start of every call
-// ---------------------------------------------------------------------------
-
-__global__ void k_init(int32_t* meta) {
-    if (threadIdx.x < kMetaWords) meta[threadIdx.x] = 0;
-}
-
-// ---------------------------------------------------------------------------
-// k_route
+// k_router: router GEMV (one wave per expert row) in the first ceil(E/4)
+// workgroups, the shared expert's gate/up in the rest.  Both stage bf16 x in
+// LDS; when chaining layers x is the RMS-normalised previous output, with
+// the sums of squares taken from the down kernel's per-workgroup partials.
 // ---------------------------------------------------------------------------
 
 constexpr int kRouterPieces = 4;  // 16-byte router pieces per lane (hidden <= 2048)
 
-__global__ __launch_bounds__(kBlock) void k_route(RouteArgs a) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-    __shared__ float s_inv[kMaxRows];
-    __shared__ int s_last;
+__device__ void stage_x(const RouterArgs& a, uint16_t* xs, float* s_inv, bool publish, int publish_idx,
+                        int publish_n) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int K = a.K, H = a.H, E = a.E;
-    const int KH = K * H;
-
-    // 0. this wave's router row, requested before anything else
-    const int e = blockIdx.x * kWaves + wave;
-    uint4 wv[kRouterPieces];
-#pragma unroll
-    for (int t = 0; t < kRouterPieces; ++t) {
-        const int p = lane * 8 + t * 512;
-        wv[t] = (e < E && p < H) ? *reinterpret_cast<const uint4*>(a.wr + (size_t)e * H + p) : make_uint4(0, 0, 0, 0);
-    }
-
-    // 1. bf16 x into LDS; when chaining layers it is the RMS-normalised
-    //    previous output, with the sums of squares taken from the per-workgroup
-    //    partials the down kernel left behind
+    const int K = a.K, H = a.H, KH = K * H;
     if (a.y_prev) {
         constexpr int CH = 2;  // float4 pairs (16 elements) per thread per pass
         float4 v[2 * CH];
@@ -415,11 +504,12 @@ __global__ __launch_bounds__(kBlock) void k_route(RouteArgs a) {
             }
         }
         __syncthreads();
-        // each workgroup publishes its share of the normalised x
-        const int per = (KH / 8 + gridDim.x - 1) / gridDim.x * 8;
-        const int i0 = blockIdx.x * per;
-        for (int i = i0 + tid * 8; i < min(KH, i0 + per); i += kBlock * 8)
-            *reinterpret_cast<uint4*>(a.x_out + i) = *reinterpret_cast<const uint4*>(xs + i);
+        if (publish) {  // this workgroup's share of the normalised x
+            const int per = (KH / 8 + publish_n - 1) / publish_n * 8;
+            const int i0 = publish_idx * per;
+            for (int i = i0 + tid * 8; i < min(KH, i0 + per); i += kBlock * 8)
+                *reinterpret_cast<uint4*>(a.x_out + i) = *reinterpret_cast<const uint4*>(xs + i);
+        }
     } else {
         constexpr int CH = 4;
         for (int base = 0; base < KH; base += kBlock * 8 * CH) {
@@ -437,175 +527,97 @@ __global__ __launch_bounds__(kBlock) void k_route(RouteArgs a) {
         }
         __syncthreads();
     }
+}
 
-    // 2. one wave per expert row: logits[r][e] = x_r . Wr[e]
-    if (e < E) {
-        float acc[kMaxRows];
-#pragma unroll
-        for (int r = 0; r < kMaxRows; ++r) acc[r] = 0.0f;
+template <int MAXM>
+__global__ __launch_bounds__(kBlock) void k_router(RouterArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+    __shared__ float s_inv[kMaxRows];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int K = a.K, H = a.H, E = a.E;
+    const int n_router_blocks = (E + kWaves - 1) / kWaves;
+
+    if ((int)blockIdx.x < n_router_blocks) {
+        // this wave's router row, requested before anything else
+        const int e = blockIdx.x * kWaves + wave;
+        uint4 wv[kRouterPieces];
 #pragma unroll
         for (int t = 0; t < kRouterPieces; ++t) {
             const int p = lane * 8 + t * 512;
-            if (p < H) {
+            wv[t] = (e < E && p < H) ? *reinterpret_cast<const uint4*>(a.wr + (size_t)e * H + p)
+                                     : make_uint4(0, 0, 0, 0);
+        }
+        stage_x(a, xs, s_inv, true, blockIdx.x, n_router_blocks);
+        if (e < E) {
+            float acc[kMaxRows];
 #pragma unroll
-                for (int r = 0; r < kMaxRows; ++r) {
-                    if (r < K) {
-                        const uint4 xv = *reinterpret_cast<const uint4*>(xs + r * H + p);
-                        float s = acc[r];
-                        s = dot2(as_bf16x2(wv[t].x), as_bf16x2(xv.x), s);
-                        s = dot2(as_bf16x2(wv[t].y), as_bf16x2(xv.y), s);
-                        s = dot2(as_bf16x2(wv[t].z), as_bf16x2(xv.z), s);
-                        s = dot2(as_bf16x2(wv[t].w), as_bf16x2(xv.w), s);
-                        acc[r] = s;
+            for (int r = 0; r < kMaxRows; ++r) acc[r] = 0.0f;
+#pragma unroll
+            for (int t = 0; t < kRouterPieces; ++t) {
+                const int p = lane * 8 + t * 512;
+                if (p < H) {
+#pragma unroll
+                    for (int r = 0; r < kMaxRows; ++r) {
+                        if (r < K) {
+                            const uint4 xv = *reinterpret_cast<const uint4*>(xs + r * H + p);
+                            float s = acc[r];
+                            s = dot2(as_bf16x2(wv[t].x), as_bf16x2(xv.x), s);
+                            s = dot2(as_bf16x2(wv[t].y), as_bf16x2(xv.y), s);
+                            s = dot2(as_bf16x2(wv[t].z), as_bf16x2(xv.z), s);
+                            s = dot2(as_bf16x2(wv[t].w), as_bf16x2(xv.w), s);
+                            acc[r] = s;
+                        }
                     }
                 }
             }
-        }
 #pragma unroll
-        for (int r = 0; r < kMaxRows; ++r) {
-            if (r < K) {
-                const float t = wave_sum(acc[r]);
-                if (lane == 0) a.logits[(size_t)r * E + e] = t;
+            for (int r = 0; r < kMaxRows; ++r) {
+                if (r < K) {
+                    const float t = wave_sum(acc[r]);
+                    if (lane == 0) a.logits[(size_t)r * E + e] = t;
+                }
             }
         }
+    } else {
+        // shared expert gate/up: weights requested before x is ready
+        const int n0 = (blockIdx.x - n_router_blocks) * a.slab;
+        const GateUpCodes c = gateup_load(a.sgate.q, a.sgate.s, a.sup.q, a.sup.s, H, n0);
+        stage_x(a, xs, s_inv, false, 0, 1);
+        int rowsel[MAXM];
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) rowsel[m] = (m < K) ? m : 0;
+        gateup_compute<MAXM>(c, a.sgate.ts[0], a.sup.ts[0], H, n0, xs, rowsel, K, a.h_sh, a.Is);
     }
-
-    // 3. the last workgroup to finish selects and deduplicates
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(&a.meta[kMetaCounter], 1) == (int)gridDim.x - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    SelectSmem& sm = *reinterpret_cast<SelectSmem*>(smem);
-    select_and_dedup(a, a.logits, sm);
-    if (tid == 0) a.meta[kMetaCounter] = 0;
-}
-
-// Selection from caller-provided logits (one workgroup).
-__global__ __launch_bounds__(kBlock) void k_select(RouteArgs a) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    SelectSmem& sm = *reinterpret_cast<SelectSmem*>(smem);
-    select_and_dedup(a, a.logits, sm);
 }
 
 // ---------------------------------------------------------------------------
-// k_gateup
+// k_gateup: every workgroup repeats the selection from the 2 KB of logits
+// (cheaper than a separate launch or a grid-wide fence), then loops over the
+// routed work items (unique expert, slab of intermediate rows)
 // ---------------------------------------------------------------------------
 
 template <int MAXM>
 __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int H = a.H;
+    extern __shared__ __align__(16) unsigned char smem[];
+    SelectSmem& sm = *reinterpret_cast<SelectSmem*>(smem);
+    const int U = select_and_dedup(a.sel, sm, blockIdx.x == 0);
+    const int H = a.H, k = a.sel.k;
     const int nsr = a.I / a.slab;
-    const int n_routed_blocks = a.max_unique * nsr;
-    int b = blockIdx.x;
-
-    const uint8_t *gq, *gs, *uq, *us;
-    float gts, uts;
-    float* hbase;
-    int hstride, m_cnt, n0;
-    int rowsel[MAXM];
-    if (b < n_routed_blocks) {
-        // one round trip for everything this workgroup needs to know: all of
-        // these addresses are independent of each other
-        const int u = b / nsr;
-        const int U = *a.n_unique;
-        const int e = a.uniq[u];
-        const int o0 = a.off[u];
-        const int o1 = a.off[u + 1];
+    const int items = U * nsr;
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const int u = it / nsr;
+        const int e = sm.uniq[u];
+        const int o0 = sm.off[u];
+        const int m_cnt = sm.off[u + 1] - o0;
+        const int n0 = (it % nsr) * a.slab;
+        const size_t eq = (size_t)e * a.I * (H / 2), es = (size_t)e * a.I * (H / 16);
+        const GateUpCodes c = gateup_load(a.gate.q + eq, a.gate.s + es, a.up.q + eq, a.up.s + es, H, n0);
+        int rowsel[MAXM];
 #pragma unroll
-        for (int m = 0; m < MAXM; ++m) rowsel[m] = a.rowtab[u * kMaxRows + m];
-        if (u >= U) return;
-        m_cnt = o1 - o0;
-        gq = a.gate.q + (size_t)e * a.I * (H / 2);
-        gs = a.gate.s + (size_t)e * a.I * (H / 16);
-        uq = a.up.q + (size_t)e * a.I * (H / 2);
-        us = a.up.s + (size_t)e * a.I * (H / 16);
-        gts = a.gate.ts[e];
-        uts = a.up.ts[e];
-        hbase = a.h + (size_t)o0 * a.I;
-        hstride = a.I;
-        n0 = (b % nsr) * a.slab;
-    } else {
-        b -= n_routed_blocks;
-        if (a.sgate.q == nullptr || b >= a.Is / a.slab) return;
-        m_cnt = a.K;
-#pragma unroll
-        for (int m = 0; m < MAXM; ++m) rowsel[m] = (m < m_cnt) ? m : 0;
-        gq = a.sgate.q; gs = a.sgate.s; uq = a.sup.q; us = a.sup.s;
-        gts = a.sgate.ts[0];
-        uts = a.sup.ts[0];
-        hbase = a.h_sh;
-        hstride = a.Is;
-        n0 = b * a.slab;
-    }
-
-    // lane -> (row inside a wave load, 32-column chunk)
-    const int CPR = H >> 5;          // chunks (16 code bytes) per weight row
-    const int RPW = 64 / CPR;        // weight rows per wave load
-    const int q = lane / CPR, chunk = lane % CPR;
-
-    // weight codes first: every load this wave issues is in flight at once
-    uint4 gc[kRowsPerWave], uc[kRowsPerWave];
-    uint32_t gsc[kRowsPerWave], usc[kRowsPerWave];
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-        const int n = n0 + (wave * kRowsPerWave + i) * RPW + q;
-        gc[i] = *reinterpret_cast<const uint4*>(gq + (size_t)n * (H / 2) + chunk * 16);
-        uc[i] = *reinterpret_cast<const uint4*>(uq + (size_t)n * (H / 2) + chunk * 16);
-        gsc[i] = *reinterpret_cast<const uint16_t*>(gs + (size_t)n * (H / 16) + chunk * 2);
-        usc[i] = *reinterpret_cast<const uint16_t*>(us + (size_t)n * (H / 16) + chunk * 2);
-    }
-    // this lane's 32 columns of every assigned row of x, as bf16 pairs
-    uint32_t xr[MAXM][16];
-#pragma unroll
-    for (int m = 0; m < MAXM; ++m) {
-        if (m < m_cnt) {
-            const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)rowsel[m] * H + chunk * 32);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const uint4 v = src[t];
-                xr[m][4 * t + 0] = v.x; xr[m][4 * t + 1] = v.y;
-                xr[m][4 * t + 2] = v.z; xr[m][4 * t + 3] = v.w;
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < 16; ++t) xr[m][t] = 0u;
-        }
-    }
-
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-        const int n = n0 + (wave * kRowsPerWave + i) * RPW + q;
-        bf16x2_t wg[16], wu[16];
-        fp4x8_to_bf16(gc[i].x, wg + 0); fp4x8_to_bf16(gc[i].y, wg + 4);
-        fp4x8_to_bf16(gc[i].z, wg + 8); fp4x8_to_bf16(gc[i].w, wg + 12);
-        fp4x8_to_bf16(uc[i].x, wu + 0); fp4x8_to_bf16(uc[i].y, wu + 4);
-        fp4x8_to_bf16(uc[i].z, wu + 8); fp4x8_to_bf16(uc[i].w, wu + 12);
-        const float sg0 = e4m3_to_f32<0>(gsc[i]), sg1 = e4m3_to_f32<1>(gsc[i]);
-        const float su0 = e4m3_to_f32<0>(usc[i]), su1 = e4m3_to_f32<1>(usc[i]);
-#pragma unroll
-        for (int m = 0; m < MAXM; ++m) {
-            if (m < m_cnt) {
-                float g0 = 0.f, g1 = 0.f, v0 = 0.f, v1 = 0.f;
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    g0 = dot2(wg[t], as_bf16x2(xr[m][t]), g0);
-                    v0 = dot2(wu[t], as_bf16x2(xr[m][t]), v0);
-                    g1 = dot2(wg[t + 8], as_bf16x2(xr[m][t + 8]), g1);
-                    v1 = dot2(wu[t + 8], as_bf16x2(xr[m][t + 8]), v1);
-                }
-                float pg = fmaf(g1, sg1, g0 * sg0);
-                float pu = fmaf(v1, su1, v0 * su0);
-                pg = group_sum_rt(pg, CPR);
-                pu = group_sum_rt(pu, CPR);
-                if (chunk == CPR - 1) {
-                    const float g = pg * gts, v = pu * uts;
-                    hbase[(size_t)m * hstride + n] = g / (1.0f + expf(-g)) * v;
-                }
-            }
-        }
+        for (int m = 0; m < MAXM; ++m) rowsel[m] = (m < m_cnt) ? sm.asg[o0 + m] / k : 0;
+        gateup_compute<MAXM>(c, a.gate.ts[e], a.up.ts[e], H, n0, a.x, rowsel, m_cnt, a.h + (size_t)o0 * a.I,
+                             a.I);
     }
 }
 
@@ -700,11 +712,13 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
             // codes and scales of this wave's batch of tasks
             uint4 code[kDownBatch];
             uint32_t scl[kDownBatch];
+            float tsv[kDownBatch];
 #pragma unroll
             for (int i = 0; i < kDownBatch; ++i) {
                 const int t = (tb * kDownBatch + i) * kDownWaves + wave;
                 code[i] = make_uint4(0, 0, 0, 0);
                 scl[i] = 0;
+                tsv[i] = 0.0f;
                 if (t < nT) {
                     const bool routed = t < (u_hi - u_lo) * gI;
                     const int CPR = routed ? cprI : cprS;
@@ -714,6 +728,7 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
                     const int cols = routed ? a.I : a.Is;
                     const int q = lane / CPR, chunk = lane % CPR;
                     const int nl = grp * (64 / CPR) + q;
+                    tsv[i] = mat.ts[e];
                     if (nl < NH) {
                         const size_t row = (size_t)e * H + n_base + nl;
                         code[i] = *reinterpret_cast<const uint4*>(mat.q + row * (cols / 2) + chunk * 16);
@@ -730,8 +745,7 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
                 const int CPR = routed ? cprI : cprS;
                 const int grp = routed ? t % gI : t - (u_hi - u_lo) * gI;
                 const int u = u_lo + (routed ? t / gI : 0);
-                const int e = routed ? s_uniq[u] : 0;
-                const float ts = routed ? a.down.ts[e] : a.sdown.ts[0];
+                const float ts = tsv[i];
                 int p_lo, p_hi;
                 if (routed) { p_lo = max(s_off[u], c0); p_hi = min(s_off[u + 1], c1); }
                 else { p_lo = max(n, c0); p_hi = c1; }
@@ -829,27 +843,6 @@ __global__ __launch_bounds__(kBlock) void k_dequant(Fp4Mat m, int n_experts, int
 
 int gateup_slab_rows(int H) { return kWaves * kRowsPerWave * (64 / (H >> 5)); }
 
-hipError_t launch_init(int32_t* meta, hipStream_t st) {
-    hipLaunchKernelGGL(k_init, dim3(1), dim3(64), 0, st, meta);
-    return hipGetLastError();
-}
-
-constexpr size_t kRouteMaxDynLds = 96 * 1024;
-
-hipError_t init_kernels() {
-    static hipError_t once = [] {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_route),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRouteMaxDynLds);
-        if (e != hipSuccess) return e;
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_select),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRouteMaxDynLds);
-        if (e != hipSuccess) return e;
-        return hipFuncSetAttribute(reinterpret_cast<const void*>(k_down),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDownHLdsBytes);
-    }();
-    return once;
-}
-
 // Plain launch, or one whose start/stop events carry the kernel's own
 // dispatch timestamps.
 template <typename Kern, typename Args>
@@ -861,27 +854,55 @@ hipError_t launch(Kern k, dim3 grid, dim3 block, size_t smem, hipStream_t st, co
     return hipGetLastError();
 }
 
-hipError_t launch_route(const RouteArgs& a, hipStream_t st, const Timing* t) {
-    const size_t xbytes = (size_t)a.K * a.H * 2;
-    const size_t sel = select_smem_bytes(a.K, a.E);
-    const size_t smem = xbytes > sel ? xbytes : sel;
-    const int grid = (a.E + kWaves - 1) / kWaves;
-    return launch(k_route, dim3(grid), dim3(kBlock), smem, st, t, a);
+// Dynamic LDS above the default per-launch limit: the selection stages
+// K*E logits (up to 64 KiB) next to its fixed tables; the down kernel stages
+// 64 KiB of h next to its static tables.
+constexpr int kSelectMaxDynLds = 96 * 1024;
+
+template <typename Kern>
+hipError_t set_lds(Kern k, int bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-hipError_t launch_select(const RouteArgs& a, hipStream_t st) {
+hipError_t init_kernels() {
+    static hipError_t once = [] {
+        hipError_t e;
+        if ((e = set_lds(k_select, kSelectMaxDynLds)) != hipSuccess) return e;
+        if ((e = set_lds(k_gateup<1>, kSelectMaxDynLds)) != hipSuccess) return e;
+        if ((e = set_lds(k_gateup<2>, kSelectMaxDynLds)) != hipSuccess) return e;
+        if ((e = set_lds(k_gateup<4>, kSelectMaxDynLds)) != hipSuccess) return e;
+        if ((e = set_lds(k_gateup<8>, kSelectMaxDynLds)) != hipSuccess) return e;
+        if ((e = set_lds(k_gateup<16>, kSelectMaxDynLds)) != hipSuccess) return e;
+        return set_lds(k_down, kDownHLdsBytes);
+    }();
+    return once;
+}
+
+hipError_t launch_router(const RouterArgs& a, hipStream_t st, const Timing* t) {
+    const int grid = (a.E + kWaves - 1) / kWaves + (a.sgate.q ? a.Is / a.slab : 0);
+    const size_t smem = (size_t)a.K * a.H * 2;
+    const dim3 g(grid), b(kBlock);
+    if (a.K <= 1) return launch(k_router<1>, g, b, smem, st, t, a);
+    if (a.K <= 2) return launch(k_router<2>, g, b, smem, st, t, a);
+    if (a.K <= 4) return launch(k_router<4>, g, b, smem, st, t, a);
+    if (a.K <= 8) return launch(k_router<8>, g, b, smem, st, t, a);
+    return launch(k_router<16>, g, b, smem, st, t, a);
+}
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
     return launch(k_select, dim3(1), dim3(kBlock), select_smem_bytes(a.K, a.E), st, nullptr, a);
 }
 
-hipError_t launch_gateup(const GateUpArgs& a, hipStream_t st, const Timing* t) {
-    const int grid = a.max_unique * (a.I / a.slab) + (a.sgate.q ? a.Is / a.slab : 0);
-    const dim3 g(grid > 0 ? grid : 1), b(kBlock);
-    const int M = a.K;
-    if (M <= 1) return launch(k_gateup<1>, g, b, 0, st, t, a);
-    if (M <= 2) return launch(k_gateup<2>, g, b, 0, st, t, a);
-    if (M <= 4) return launch(k_gateup<4>, g, b, 0, st, t, a);
-    if (M <= 8) return launch(k_gateup<8>, g, b, 0, st, t, a);
-    return launch(k_gateup<16>, g, b, 0, st, t, a);
+hipError_t launch_gateup(const GateUpArgs& a, int max_unique, hipStream_t st, const Timing* t) {
+    int grid = max_unique * (a.I / a.slab);
+    if (grid > kGateUpMaxGrid) grid = kGateUpMaxGrid;
+    const dim3 g(grid), b(kBlock);
+    const size_t smem = select_smem_bytes(a.K, a.sel.E);
+    if (a.K <= 1) return launch(k_gateup<1>, g, b, smem, st, t, a);
+    if (a.K <= 2) return launch(k_gateup<2>, g, b, smem, st, t, a);
+    if (a.K <= 4) return launch(k_gateup<4>, g, b, smem, st, t, a);
+    if (a.K <= 8) return launch(k_gateup<8>, g, b, smem, st, t, a);
+    return launch(k_gateup<16>, g, b, smem, st, t, a);
 }
 
 hipError_t launch_down(const DownArgs& a, hipStream_t st, const Timing* t) {
