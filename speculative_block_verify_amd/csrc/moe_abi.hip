@@ -67,6 +67,9 @@ int check_cfg(const moe_cfg* c) {
     if (c->max_rows < 1) return fail(MOE_ERR_INVALID, "max_rows=%d < 1", c->max_rows);
     if (c->max_rows > moe::kMaxRows)
         return fail(MOE_ERR_UNSUPPORTED, "max_rows=%d > %d (verify-width path)", c->max_rows, moe::kMaxRows);
+    if (!moe::lds_fits(c->max_rows, c->n_experts, c->hidden))
+        return fail(MOE_ERR_UNSUPPORTED, "max_rows=%d x n_experts=%d x hidden=%d exceeds the LDS budget",
+                    c->max_rows, c->n_experts, c->hidden);
     return MOE_OK;
 }
 

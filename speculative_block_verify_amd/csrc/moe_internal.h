@@ -104,4 +104,7 @@ hipError_t init_kernels();
 // Rows of gate (and of up) one gate/up work item covers at hidden H.
 int gateup_slab_rows(int H);
 
+// Whether the per-workgroup LDS the kernels need at (K, E, H) fits gfx950.
+bool lds_fits(int K, int E, int H);
+
 }  // namespace moe

@@ -187,17 +187,11 @@ struct SelectSmem {
     int32_t sel[kMaxSlots];
     float w[kMaxSlots];
     int32_t asg[kMaxSlots];
+    int32_t inv[kMaxSlots];
     int32_t uniq[kMaxSlots];
     int32_t off[kMaxSlots + 1];
-    int32_t cnt[kMaxExperts];
-    int32_t start[kMaxExperts];
     int32_t n_unique;
-    float lg[1];  // K * E logits follow (dynamic tail)
 };
-
-__host__ __device__ constexpr size_t select_smem_bytes(int K, int E) {
-    return sizeof(SelectSmem) + (size_t)K * E * sizeof(float);
-}
 
 // Copy n floats global -> LDS with every load of a pass in flight at once.
 __device__ __forceinline__ void stage_floats(float* dst, const float* src, int n, int tid, int nthr) {
@@ -217,19 +211,22 @@ __device__ __forceinline__ void stage_floats(float* dst, const float* src, int n
     }
 }
 
-// Top-k of row r by (key desc, index asc) with one wave.  Lane l owns experts
-// l*P .. l*P+P-1 (contiguous), so among equal keys the lowest lane holding
-// the maximum also holds the lowest index.  lr: the row's logits in LDS.
-__device__ void wave_select_row(const SelectArgs& a, const float* lr, int r, SelectSmem& sm) {
+// Top-k of row r by (key desc, index asc) with one wave.  Lane l owns the P
+// experts l*P .. l*P+P-1 (contiguous) and keeps them sorted; each round takes
+// the wave maximum of the lanes' heads.  Among equal keys the lowest lane
+// wins, which (contiguous ownership, stable in-lane order) is the lowest
+// expert index.  lr: the row's logits in LDS.
+template <int P>
+__device__ void wave_topk(const SelectArgs& a, const float* lr, int r, SelectSmem& sm) {
     const int lane = threadIdx.x & 63;
     const int E = a.E, k = a.k;
-    const int P = (E + 63) >> 6;
-    uint32_t kv[kMaxExperts / 64];
+    uint32_t sk[P];
+    int si[P];
 #pragma unroll
-    for (int p = 0; p < kMaxExperts / 64; ++p) {
+    for (int p = 0; p < P; ++p) {
         const int e = lane * P + p;
         uint32_t v = 0;
-        if (p < P && e < E) {
+        if (e < E) {
             const float l = lr[e];
             float key = l;
             if (a.score_fn == 1) {
@@ -238,29 +235,33 @@ __device__ void wave_select_row(const SelectArgs& a, const float* lr, int r, Sel
             }
             v = key_bits(key);
         }
-        kv[p] = v;
+        sk[p] = v;
+        si[p] = p;
     }
-    uint32_t best = 0;
-    int bi = 0;
+    // stable insertion network, descending
 #pragma unroll
-    for (int p = 0; p < kMaxExperts / 64; ++p)
-        if (kv[p] > best) { best = kv[p]; bi = p; }
-
+    for (int i = 1; i < P; ++i) {
+#pragma unroll
+        for (int j = i; j > 0; --j) {
+            const bool sw = sk[j] > sk[j - 1];
+            const uint32_t ka = sk[j], kb = sk[j - 1];
+            const int ia = si[j], ib = si[j - 1];
+            sk[j - 1] = sw ? ka : kb; sk[j] = sw ? kb : ka;
+            si[j - 1] = sw ? ia : ib; si[j] = sw ? ib : ia;
+        }
+    }
     int mine = 0;
     for (int j = 0; j < k; ++j) {
-        const uint32_t m = wave_max_u32(best);
-        const unsigned long long mask = __ballot(best == m);
+        const uint32_t head = sk[0];
+        const uint32_t m = wave_max_u32(head);
+        const unsigned long long mask = __ballot(head == m);
         const int L = __builtin_ctzll(mask);
-        const int e = L * P + __builtin_amdgcn_readlane(bi, L);
+        const int e = L * P + __builtin_amdgcn_readlane(si[0], L);
         if (lane == j) mine = e;
         if (lane == L) {
 #pragma unroll
-            for (int p = 0; p < kMaxExperts / 64; ++p)
-                if (p == bi) kv[p] = 0;
-            best = 0; bi = 0;
-#pragma unroll
-            for (int p = 0; p < kMaxExperts / 64; ++p)
-                if (kv[p] > best) { best = kv[p]; bi = p; }
+            for (int p = 0; p + 1 < P; ++p) { sk[p] = sk[p + 1]; si[p] = si[p + 1]; }
+            sk[P - 1] = 0;
         }
     }
     // mixture weights over the selection (routed scale not folded in)
@@ -286,163 +287,316 @@ __device__ void wave_select_row(const SelectArgs& a, const float* lr, int r, Sel
     }
 }
 
-// All rows' top-k, then the canonical dedup CSR, left in LDS (sm.uniq,
-// sm.off, sm.asg, sm.n_unique) and, if write_global, also in the SelectArgs
-// outputs.  Returns the number of unique experts.
-__device__ int select_and_dedup(const SelectArgs& a, SelectSmem& sm, bool write_global) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int K = a.K, k = a.k, E = a.E, n = K * k;
-    stage_floats(sm.lg, a.logits, K * E, tid, kBlock);
-    for (int e = tid; e < E; e += kBlock) sm.cnt[e] = 0;
-    __syncthreads();
-    for (int r = wave; r < K; r += kWaves) wave_select_row(a, sm.lg + r * E, r, sm);
-    __syncthreads();
-    for (int s = tid; s < n; s += kBlock) atomicAdd(&sm.cnt[sm.sel[s]], 1);
-    __syncthreads();
-    if (wave == 0) {
-        const int Q = (E + 63) >> 6;
-        int c = 0, f = 0;
-        for (int q = 0; q < Q; ++q) {
-            const int e = lane * Q + q;
-            if (e < E) { c += sm.cnt[e]; f += (sm.cnt[e] > 0); }
-        }
-        const int ci = wave_incl_scan(c), fi = wave_incl_scan(f);
-        int cs = ci - c, fs = fi - f;
-        for (int q = 0; q < Q; ++q) {
-            const int e = lane * Q + q;
-            if (e < E) {
-                const int cn = sm.cnt[e];
-                sm.start[e] = cs;
-                if (cn) { sm.uniq[fs] = e; sm.off[fs] = cs; }
-                cs += cn;
-                fs += (cn > 0);
+__device__ void wave_topk_rt(const SelectArgs& a, const float* lr, int r, SelectSmem& sm) {
+    const int P = (a.E + 63) >> 6;
+    if (P <= 1) wave_topk<1>(a, lr, r, sm);
+    else if (P <= 2) wave_topk<2>(a, lr, r, sm);
+    else if (P <= 4) wave_topk<4>(a, lr, r, sm);
+    else if (P <= 8) wave_topk<8>(a, lr, r, sm);
+    else wave_topk<16>(a, lr, r, sm);
+}
+
+// Canonical dedup of the n selected slots, in one wave, in registers: for
+// each slot s with expert id_s,
+//   rank  = #{t < s : id_t == id_s}          (order inside its expert group)
+//   start = #{t : id_t < id_s}               (CSR offset of the group)
+//   ulow  = #{distinct ids < id_s}           (position in the unique list)
+// Results go to sm.asg / sm.inv / sm.uniq / sm.off / sm.n_unique.
+__device__ void dedup_wave(SelectSmem& sm, int n) {
+    const int lane = threadIdx.x & 63;
+    constexpr int SPL = kMaxSlots / 64;
+    const int nj = (n + 63) >> 6;
+    int id[SPL], rank[SPL], start[SPL], ulow[SPL], first[SPL];
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+        const int s = lane + 64 * j;
+        id[j] = (j < nj && s < n) ? sm.sel[s] : 0x7FFFFFFF;
+        rank[j] = 0; start[j] = 0; ulow[j] = 0;
+    }
+#pragma unroll
+    for (int jt = 0; jt < SPL; ++jt) {
+        if (jt >= nj) break;
+        const int cnt = min(64, n - 64 * jt);
+        for (int tl = 0; tl < cnt; ++tl) {
+            const int it = __builtin_amdgcn_readlane(id[jt], tl);
+            const int t = 64 * jt + tl;
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) {
+                if (j < nj) {
+                    const int s = lane + 64 * j;
+                    rank[j] += (it == id[j] && t < s) ? 1 : 0;
+                    start[j] += (it < id[j]) ? 1 : 0;
+                }
             }
         }
-        const int U = __builtin_amdgcn_readlane(fi, 63);
-        if (lane == 0) { sm.n_unique = U; sm.off[U] = n; }
     }
-    __syncthreads();
-    const int U = sm.n_unique;
-    for (int s = tid; s < n; s += kBlock) {
-        const int e = sm.sel[s];
-        int rank = 0;
-        for (int t = 0; t < s; ++t) rank += (sm.sel[t] == e);
-        const int pos = sm.start[e] + rank;
-        sm.asg[pos] = s;
-        if (write_global) {
-            a.asg[pos] = s;
-            a.inv[s] = pos;
-            a.ids[s] = e;
-            a.w[s] = sm.w[s];
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) first[j] = (j < nj && lane + 64 * j < n && rank[j] == 0) ? 1 : 0;
+#pragma unroll
+    for (int jt = 0; jt < SPL; ++jt) {
+        if (jt >= nj) break;
+        const int cnt = min(64, n - 64 * jt);
+        for (int tl = 0; tl < cnt; ++tl) {
+            const int it = __builtin_amdgcn_readlane(id[jt], tl);
+            const int ft = __builtin_amdgcn_readlane(first[jt], tl);
+#pragma unroll
+            for (int j = 0; j < SPL; ++j)
+                if (j < nj) ulow[j] += (ft && it < id[j]) ? 1 : 0;
         }
     }
+    int U = 0;
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+        if (j < nj) {
+            const int s = lane + 64 * j;
+            if (s < n) {
+                const int pos = start[j] + rank[j];
+                sm.asg[pos] = s;
+                sm.inv[s] = pos;
+                if (first[j]) {
+                    sm.uniq[ulow[j]] = id[j];
+                    sm.off[ulow[j]] = start[j];
+                }
+            }
+            U += __builtin_popcountll(__ballot(first[j] != 0));
+        }
+    }
+    if (lane == 0) {
+        sm.off[U] = n;
+        sm.n_unique = U;
+    }
+}
+
+// All rows' top-k, then the canonical dedup CSR, left in LDS and, if
+// write_global, also in the SelectArgs outputs.  lg: K*E floats of LDS.
+// Returns the number of unique experts.
+__device__ int select_and_dedup(const SelectArgs& a, SelectSmem& sm, float* lg, bool write_global) {
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int K = a.K, k = a.k, E = a.E, n = K * k;
+    stage_floats(lg, a.logits, K * E, tid, kBlock);
+    __syncthreads();
+    for (int r = wave; r < K; r += kWaves) wave_topk_rt(a, lg + r * E, r, sm);
+    __syncthreads();
+    if (wave == 0) dedup_wave(sm, n);
+    __syncthreads();
+    const int U = sm.n_unique;
     if (write_global) {
+        for (int s = tid; s < n; s += kBlock) {
+            a.asg[s] = sm.asg[s];
+            a.inv[s] = sm.inv[s];
+            a.ids[s] = sm.sel[s];
+            a.w[s] = sm.w[s];
+        }
         for (int u = tid; u <= U; u += kBlock) {
             if (u < U) a.uniq[u] = sm.uniq[u];
             a.off[u] = sm.off[u];
         }
         if (tid == 0) *a.n_unique = U;
     }
-    __syncthreads();
     return U;
+}
+
+__host__ __device__ constexpr size_t select_smem_bytes(int K, int E) {
+    return (sizeof(SelectSmem) + 15) / 16 * 16 + (size_t)K * E * sizeof(float);
 }
 
 // Selection from caller-provided logits (one workgroup).
 __global__ __launch_bounds__(kBlock) void k_select(SelectArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     SelectSmem& sm = *reinterpret_cast<SelectSmem*>(smem);
-    select_and_dedup(a, sm, true);
+    float* lg = reinterpret_cast<float*>(smem + (sizeof(SelectSmem) + 15) / 16 * 16);
+    select_and_dedup(a, sm, lg, true);
 }
 
 // ---------------------------------------------------------------------------
-// gate/up tile: kWaves*kRowsPerWave*RPW rows of gate and of up for up to
-// MAXM rows of x; h = silu(x.Wg) * (x.Wu) in fp32
+// gate/up tile on the matrix cores: 16 rows of gate and of up for one expert
+// against up to 16 rows of x (v_mfma_f32_16x16x32_f16).
+//
+// Operands.  Each weight is decoded FP4 -> fp16 (v_cvt_scalef32_pk_f16_fp4,
+// scale operand 1) and multiplied by its E4M3 block scale with a packed fp16
+// multiply: an E2M1 value times an E4M3 value has at most 6 significant bits
+// and lies in [2^-10, 2688], so the fp16 product is exact.  x is converted
+// bf16 -> fp16 (exact for |x| in [2^-14, 65504]; smaller values lose low
+// bits).  Products accumulate in fp32; the tensor scale multiplies the sum.
+//
+// Layout.  Lane (i = lane % 16, kb = lane / 16).  A superblock is 256
+// columns; lane (i, kb) owns columns [sb*256 + kb*64, +64) of weight row
+// n0 + i: 32 contiguous code bytes and 4 scale bytes.  MFMA step s (0..7)
+// feeds the lane's codes 8s..8s+7 as its A k-block, and lane (j, kb) feeds
+// x row j at the same 8 columns as its B k-block; the contraction over k is
+// order independent, so this permutation of k is consistent on both sides.
+// The accumulator of lane (j, q) holds rows n0 + 4q .. +3 for x row j.  The
+// 4 waves split the superblocks and add their partial sums through LDS in a
+// fixed order.
 // ---------------------------------------------------------------------------
 
-struct GateUpCodes {
-    uint4 gc[kRowsPerWave], uc[kRowsPerWave];
-    uint32_t gsc[kRowsPerWave], usc[kRowsPerWave];
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kTileRows = 16;
+constexpr int kSbCols = 256;
+// each wave holds at most two superblocks in flight (hidden <= 2048)
+constexpr int kRedFloats = kWaves * 2 * 64 * 4;         // cross-wave partials
+constexpr int kMaxDynLds = 160 * 1024 - 1024;           // gfx950: 160 KiB per workgroup, minus static use
+
+// Code and scale registers of one superblock of one lane (gate and up).
+struct GuSb {
+    uint4 g0, g1, u0, u1;
+    uint32_t gs, us;
+};
+struct GuRegs {
+    GuSb sb0, sb1;  // this wave's superblocks wave and wave + kWaves
 };
 
-// lane -> (weight row inside a wave load, 32-column chunk)
-__device__ __forceinline__ void gu_lane(int H, int lane, int& CPR, int& RPW, int& q, int& chunk) {
-    CPR = H >> 5;   // chunks (16 code bytes) per weight row
-    RPW = 64 / CPR; // weight rows per wave load
-    q = lane / CPR;
-    chunk = lane % CPR;
-}
-
-__device__ __forceinline__ GateUpCodes gateup_load(const uint8_t* gq, const uint8_t* gs, const uint8_t* uq,
-                                                  const uint8_t* us, int H, int n0) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int CPR, RPW, q, chunk;
-    gu_lane(H, lane, CPR, RPW, q, chunk);
-    GateUpCodes c;
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-        const int n = n0 + (wave * kRowsPerWave + i) * RPW + q;
-        c.gc[i] = *reinterpret_cast<const uint4*>(gq + (size_t)n * (H / 2) + chunk * 16);
-        c.uc[i] = *reinterpret_cast<const uint4*>(uq + (size_t)n * (H / 2) + chunk * 16);
-        c.gsc[i] = *reinterpret_cast<const uint16_t*>(gs + (size_t)n * (H / 16) + chunk * 2);
-        c.usc[i] = *reinterpret_cast<const uint16_t*>(us + (size_t)n * (H / 16) + chunk * 2);
+__device__ __forceinline__ GuSb gu_load_sb(const uint8_t* gq, const uint8_t* gs, const uint8_t* uq,
+                                          const uint8_t* us, int H, int n0, int sb, bool live) {
+    const int lane = threadIdx.x & 63;
+    const int i = lane & 15, kb = lane >> 4;
+    GuSb r;
+    if (live) {
+        const int k0 = sb * kSbCols + kb * 64;
+        const size_t row = (size_t)(n0 + i);
+        const uint8_t* qg = gq + row * (H / 2) + k0 / 2;
+        const uint8_t* qu = uq + row * (H / 2) + k0 / 2;
+        r.g0 = *reinterpret_cast<const uint4*>(qg);
+        r.g1 = *reinterpret_cast<const uint4*>(qg + 16);
+        r.u0 = *reinterpret_cast<const uint4*>(qu);
+        r.u1 = *reinterpret_cast<const uint4*>(qu + 16);
+        r.gs = *reinterpret_cast<const uint32_t*>(gs + row * (H / 16) + k0 / 16);
+        r.us = *reinterpret_cast<const uint32_t*>(us + row * (H / 16) + k0 / 16);
+    } else {
+        r.g0 = r.g1 = r.u0 = r.u1 = make_uint4(0, 0, 0, 0);
+        r.gs = r.us = 0;
     }
-    return c;
+    return r;
 }
 
-// x: generic pointer to bf16 [.][H] (global or LDS); rowsel[m] its rows.
-template <int MAXM>
-__device__ __forceinline__ void gateup_compute(const GateUpCodes& c, float gts, float uts, int H, int n0,
-                                               const uint16_t* x, const int* rowsel, int m_cnt, float* hbase,
-                                               int hstride) {
+__device__ __forceinline__ GuRegs gu_load(const uint8_t* gq, const uint8_t* gs, const uint8_t* uq, const uint8_t* us,
+                                         int H, int n0) {
+    const int wave = threadIdx.x >> 6;
+    const int nsb = H / kSbCols;
+    GuRegs R;
+    R.sb0 = gu_load_sb(gq, gs, uq, us, H, n0, wave, wave < nsb);
+    R.sb1 = gu_load_sb(gq, gs, uq, us, H, n0, wave + kWaves, wave + kWaves < nsb);
+    return R;
+}
+
+__device__ __forceinline__ uint32_t pick_word(const uint4& lo, const uint4& hi, int s) {
+    const uint4& h = (s < 4) ? lo : hi;
+    switch (s & 3) {
+        case 0: return h.x;
+        case 1: return h.y;
+        case 2: return h.z;
+        default: return h.w;
+    }
+}
+
+// 8 FP4 codes (one dword) times one E4M3 scale -> 8 exact fp16 values
+__device__ __forceinline__ f16x8_t decode8_f16(uint32_t codes, _Float16 scale) {
+    const f16x2_t sc = {scale, scale};
+    const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * sc;
+    const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * sc;
+    const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * sc;
+    const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * sc;
+    f16x8_t r;
+    r[0] = p0.x; r[1] = p0.y; r[2] = p1.x; r[3] = p1.y;
+    r[4] = p2.x; r[5] = p2.y; r[6] = p3.x; r[7] = p3.y;
+    return r;
+}
+
+template <int SEL>
+__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t packed) {
+    return (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)packed, SEL);
+}
+
+// The eight MFMA steps of one superblock.
+__device__ __forceinline__ void gu_mfma_sb(const GuSb& r, const _Float16* xr, bool has_x, f32x4_t& accg,
+                                           f32x4_t& accu) {
+    const f16x8_t zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    const _Float16 g0 = e4m3_to_f16<0>(r.gs), g1 = e4m3_to_f16<1>(r.gs);
+    const _Float16 g2 = e4m3_to_f16<2>(r.gs), g3 = e4m3_to_f16<3>(r.gs);
+    const _Float16 u0 = e4m3_to_f16<0>(r.us), u1 = e4m3_to_f16<1>(r.us);
+    const _Float16 u2 = e4m3_to_f16<2>(r.us), u3 = e4m3_to_f16<3>(r.us);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const _Float16 gsc = (s < 2) ? g0 : (s < 4) ? g1 : (s < 6) ? g2 : g3;
+        const _Float16 usc = (s < 2) ? u0 : (s < 4) ? u1 : (s < 6) ? u2 : u3;
+        const f16x8_t ag = decode8_f16(pick_word(r.g0, r.g1, s), gsc);
+        const f16x8_t au = decode8_f16(pick_word(r.u0, r.u1, s), usc);
+        const f16x8_t b = has_x ? *reinterpret_cast<const f16x8_t*>(xr + 8 * s) : zero8;
+        accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(ag, b, accg, 0, 0, 0);
+        accu = __builtin_amdgcn_mfma_f32_16x16x32_f16(au, b, accu, 0, 0, 0);
+    }
+}
+
+// xh: fp16 x rows in LDS, row stride H; rows >= m_cnt are not read.
+// Writes h[j * hstride + n0 + r] for x rows j < m_cnt and the tile's 16 rows.
+__device__ __forceinline__ void gu_compute(const GuRegs& R, float gts, float uts, int H, int n0,
+                                           const _Float16* xh, int m_cnt, float* hbase, int hstride, float* red) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int CPR, RPW, q, chunk;
-    gu_lane(H, lane, CPR, RPW, q, chunk);
-    // this lane's 32 columns of every assigned row of x, as bf16 pairs
-    uint32_t xr[MAXM][16];
+    const int j = lane & 15, kb = lane >> 4;
+    const int nsb = H / kSbCols;
+    f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+    const _Float16* xr = xh + (size_t)j * H + kb * 64;
+    if (wave < nsb) gu_mfma_sb(R.sb0, xr + wave * kSbCols, j < m_cnt, accg, accu);
+    if (wave + kWaves < nsb) gu_mfma_sb(R.sb1, xr + (wave + kWaves) * kSbCols, j < m_cnt, accg, accu);
+    reinterpret_cast<f32x4_t*>(red)[(wave * 2 + 0) * 64 + lane] = accg;
+    reinterpret_cast<f32x4_t*>(red)[(wave * 2 + 1) * 64 + lane] = accu;
+    __syncthreads();
+    if (wave == 0 && j < m_cnt) {
+        f32x4_t g = reinterpret_cast<const f32x4_t*>(red)[lane];
+        f32x4_t u = reinterpret_cast<const f32x4_t*>(red)[64 + lane];
 #pragma unroll
-    for (int m = 0; m < MAXM; ++m) {
-        if (m < m_cnt) {
-            const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)rowsel[m] * H + chunk * 32);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const uint4 v = src[t];
-                xr[m][4 * t + 0] = v.x; xr[m][4 * t + 1] = v.y;
-                xr[m][4 * t + 2] = v.z; xr[m][4 * t + 3] = v.w;
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < 16; ++t) xr[m][t] = 0u;
+        for (int w = 1; w < kWaves; ++w) {
+            g += reinterpret_cast<const f32x4_t*>(red)[(w * 2 + 0) * 64 + lane];
+            u += reinterpret_cast<const f32x4_t*>(red)[(w * 2 + 1) * 64 + lane];
         }
+        float4 h;
+        float gv, uv;
+        gv = g[0] * gts; uv = u[0] * uts; h.x = gv / (1.0f + expf(-gv)) * uv;
+        gv = g[1] * gts; uv = u[1] * uts; h.y = gv / (1.0f + expf(-gv)) * uv;
+        gv = g[2] * gts; uv = u[2] * uts; h.z = gv / (1.0f + expf(-gv)) * uv;
+        gv = g[3] * gts; uv = u[3] * uts; h.w = gv / (1.0f + expf(-gv)) * uv;
+        *reinterpret_cast<float4*>(hbase + (size_t)j * hstride + n0 + 4 * kb) = h;
     }
+}
+
+__device__ __forceinline__ uint32_t bf16pair_to_f16pair(uint32_t v) {
+    const f16x2_t h = {(_Float16)__uint_as_float(v << 16), (_Float16)__uint_as_float(v & 0xFFFF0000u)};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// x rows (bf16, global or LDS) -> fp16 rows in LDS.  Row m comes from
+// source row asg[o0 + m] / k (the slots of one unique expert; asg in LDS), or
+// from row m when asg is null.  All loads of a pass are issued before use.
+__device__ __forceinline__ void stage_x_f16(const uint16_t* x, const int32_t* asg, int o0, int k, int m_cnt, int H,
+                                            _Float16* xh) {
+    const int tid = threadIdx.x;
+    const int per_row = H / 8;   // 16-byte pieces per row
+    const int total = m_cnt * per_row;
+    constexpr int U = 4;
+    for (int base = 0; base < total; base += U * kBlock) {
+        uint4 v[U];
 #pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-        const int n = n0 + (wave * kRowsPerWave + i) * RPW + q;
-        bf16x2_t wg[16], wu[16];
-        fp4x8_to_bf16(c.gc[i].x, wg + 0); fp4x8_to_bf16(c.gc[i].y, wg + 4);
-        fp4x8_to_bf16(c.gc[i].z, wg + 8); fp4x8_to_bf16(c.gc[i].w, wg + 12);
-        fp4x8_to_bf16(c.uc[i].x, wu + 0); fp4x8_to_bf16(c.uc[i].y, wu + 4);
-        fp4x8_to_bf16(c.uc[i].z, wu + 8); fp4x8_to_bf16(c.uc[i].w, wu + 12);
-        const float sg0 = e4m3_to_f32<0>(c.gsc[i]), sg1 = e4m3_to_f32<1>(c.gsc[i]);
-        const float su0 = e4m3_to_f32<0>(c.usc[i]), su1 = e4m3_to_f32<1>(c.usc[i]);
+        for (int q = 0; q < U; ++q) {
+            const int f = base + q * kBlock + tid;
+            v[q] = make_uint4(0, 0, 0, 0);
+            if (f < total) {
+                const int m = f / per_row, c = f % per_row;
+                const int src = asg ? asg[o0 + m] / k : m;
+                v[q] = *reinterpret_cast<const uint4*>(x + (size_t)src * H + c * 8);
+            }
+        }
 #pragma unroll
-        for (int m = 0; m < MAXM; ++m) {
-            if (m < m_cnt) {
-                float g0 = 0.f, g1 = 0.f, v0 = 0.f, v1 = 0.f;
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    g0 = dot2(wg[t], as_bf16x2(xr[m][t]), g0);
-                    v0 = dot2(wu[t], as_bf16x2(xr[m][t]), v0);
-                    g1 = dot2(wg[t + 8], as_bf16x2(xr[m][t + 8]), g1);
-                    v1 = dot2(wu[t + 8], as_bf16x2(xr[m][t + 8]), v1);
-                }
-                float pg = fmaf(g1, sg1, g0 * sg0);
-                float pu = fmaf(v1, su1, v0 * su0);
-                pg = group_sum_rt(pg, CPR);
-                pu = group_sum_rt(pu, CPR);
-                if (chunk == CPR - 1) {
-                    const float g = pg * gts, v = pu * uts;
-                    hbase[(size_t)m * hstride + n] = g / (1.0f + expf(-g)) * v;
-                }
+        for (int q = 0; q < U; ++q) {
+            const int f = base + q * kBlock + tid;
+            if (f < total) {
+                const int m = f / per_row, c = f % per_row;
+                uint4 o;
+                o.x = bf16pair_to_f16pair(v[q].x); o.y = bf16pair_to_f16pair(v[q].y);
+                o.z = bf16pair_to_f16pair(v[q].z); o.w = bf16pair_to_f16pair(v[q].w);
+                *reinterpret_cast<uint4*>(xh + (size_t)m * H + c * 8) = o;
             }
         }
     }
@@ -450,13 +604,14 @@ __device__ __forceinline__ void gateup_compute(const GateUpCodes& c, float gts, 
 
 // ---------------------------------------------------------------------------
 // k_router: router GEMV (one wave per expert row) in the first ceil(E/4)
-// workgroups, the shared expert's gate/up in the rest.  Both stage bf16 x in
-// LDS; when chaining layers x is the RMS-normalised previous output, with
-// the sums of squares taken from the down kernel's per-workgroup partials.
+// workgroups, the shared expert's gate/up tiles in the rest.  When chaining
+// layers, x is the RMS-normalised previous output (bf16), with the sums of
+// squares taken from the down kernel's per-workgroup partials.
 // ---------------------------------------------------------------------------
 
 constexpr int kRouterPieces = 4;  // 16-byte router pieces per lane (hidden <= 2048)
 
+// Builds this layer's bf16 x in LDS (xs, K*H) from x_in or from y_prev.
 __device__ void stage_x(const RouterArgs& a, uint16_t* xs, float* s_inv, bool publish, int publish_idx,
                         int publish_n) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -558,7 +713,7 @@ __global__ __launch_bounds__(kBlock) void k_router(RouterArgs a) {
                 const int p = lane * 8 + t * 512;
                 if (p < H) {
 #pragma unroll
-                    for (int r = 0; r < kMaxRows; ++r) {
+                    for (int r = 0; r < MAXM; ++r) {
                         if (r < K) {
                             const uint4 xv = *reinterpret_cast<const uint4*>(xs + r * H + p);
                             float s = acc[r];
@@ -572,7 +727,7 @@ __global__ __launch_bounds__(kBlock) void k_router(RouterArgs a) {
                 }
             }
 #pragma unroll
-            for (int r = 0; r < kMaxRows; ++r) {
+            for (int r = 0; r < MAXM; ++r) {
                 if (r < K) {
                     const float t = wave_sum(acc[r]);
                     if (lane == 0) a.logits[(size_t)r * E + e] = t;
@@ -580,44 +735,50 @@ __global__ __launch_bounds__(kBlock) void k_router(RouterArgs a) {
             }
         }
     } else {
-        // shared expert gate/up: weights requested before x is ready
-        const int n0 = (blockIdx.x - n_router_blocks) * a.slab;
-        const GateUpCodes c = gateup_load(a.sgate.q, a.sgate.s, a.sup.q, a.sup.s, H, n0);
+        // shared expert gate/up tile: weights requested before x is ready
+        const int n0 = (blockIdx.x - n_router_blocks) * kTileRows;
+        const GuRegs R = gu_load(a.sgate.q, a.sgate.s, a.sup.q, a.sup.s, H, n0);
         stage_x(a, xs, s_inv, false, 0, 1);
-        int rowsel[MAXM];
-#pragma unroll
-        for (int m = 0; m < MAXM; ++m) rowsel[m] = (m < K) ? m : 0;
-        gateup_compute<MAXM>(c, a.sgate.ts[0], a.sup.ts[0], H, n0, xs, rowsel, K, a.h_sh, a.Is);
+        _Float16* xh = reinterpret_cast<_Float16*>(smem + (size_t)K * H * 2);
+        float* red = reinterpret_cast<float*>(smem + (size_t)K * H * 4);
+        stage_x_f16(xs, nullptr, 0, 1, K, H, xh);
+        __syncthreads();
+        gu_compute(R, a.sgate.ts[0], a.sup.ts[0], H, n0, xh, K, a.h_sh, a.Is, red);
     }
 }
 
 // ---------------------------------------------------------------------------
 // k_gateup: every workgroup repeats the selection from the 2 KB of logits
 // (cheaper than a separate launch or a grid-wide fence), then loops over the
-// routed work items (unique expert, slab of intermediate rows)
+// routed work items (unique expert, 16 intermediate rows)
 // ---------------------------------------------------------------------------
 
-template <int MAXM>
+__host__ __device__ constexpr size_t gateup_smem_bytes(int K, int E, int H) {
+    return select_smem_bytes(K, E) + (size_t)K * H * 2 + (size_t)kRedFloats * 4;
+}
+
 __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     SelectSmem& sm = *reinterpret_cast<SelectSmem*>(smem);
-    const int U = select_and_dedup(a.sel, sm, blockIdx.x == 0);
+    float* lg = reinterpret_cast<float*>(smem + (sizeof(SelectSmem) + 15) / 16 * 16);
+    _Float16* xh = reinterpret_cast<_Float16*>(smem + select_smem_bytes(a.K, a.sel.E));
+    float* red = reinterpret_cast<float*>(smem + select_smem_bytes(a.K, a.sel.E) + (size_t)a.K * a.H * 2);
+    const int U = select_and_dedup(a.sel, sm, lg, blockIdx.x == 0);
     const int H = a.H, k = a.sel.k;
-    const int nsr = a.I / a.slab;
+    const int nsr = a.I / kTileRows;
     const int items = U * nsr;
     for (int it = blockIdx.x; it < items; it += gridDim.x) {
         const int u = it / nsr;
         const int e = sm.uniq[u];
         const int o0 = sm.off[u];
         const int m_cnt = sm.off[u + 1] - o0;
-        const int n0 = (it % nsr) * a.slab;
+        const int n0 = (it % nsr) * kTileRows;
         const size_t eq = (size_t)e * a.I * (H / 2), es = (size_t)e * a.I * (H / 16);
-        const GateUpCodes c = gateup_load(a.gate.q + eq, a.gate.s + es, a.up.q + eq, a.up.s + es, H, n0);
-        int rowsel[MAXM];
-#pragma unroll
-        for (int m = 0; m < MAXM; ++m) rowsel[m] = (m < m_cnt) ? sm.asg[o0 + m] / k : 0;
-        gateup_compute<MAXM>(c, a.gate.ts[e], a.up.ts[e], H, n0, a.x, rowsel, m_cnt, a.h + (size_t)o0 * a.I,
-                             a.I);
+        const GuRegs R = gu_load(a.gate.q + eq, a.gate.s + es, a.up.q + eq, a.up.s + es, H, n0);
+        stage_x_f16(a.x, sm.asg, o0, k, m_cnt, H, xh);
+        __syncthreads();
+        gu_compute(R, a.gate.ts[e], a.up.ts[e], H, n0, xh, m_cnt, a.h + (size_t)o0 * a.I, a.I, red);
+        __syncthreads();
     }
 }
 
@@ -679,6 +840,38 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
         const bool sh_here = has_sh && c1 > n;
         const int nT = (u_hi - u_lo) * gI + (sh_here ? gS : 0);
 
+        // codes, scales and tensor scales of this wave's first batch of tasks
+        // are requested before the h staging, so both round trips overlap
+        uint4 code[kDownBatch];
+        uint32_t scl[kDownBatch];
+        float tsv[kDownBatch];
+        auto load_batch = [&](int tb) {
+#pragma unroll
+            for (int i = 0; i < kDownBatch; ++i) {
+                const int t = (tb * kDownBatch + i) * kDownWaves + wave;
+                code[i] = make_uint4(0, 0, 0, 0);
+                scl[i] = 0;
+                tsv[i] = 0.0f;
+                if (t < nT) {
+                    const bool routed = t < (u_hi - u_lo) * gI;
+                    const int CPR = routed ? cprI : cprS;
+                    const int grp = routed ? t % gI : t - (u_hi - u_lo) * gI;
+                    const int e = routed ? s_uniq[u_lo + t / gI] : 0;
+                    const Fp4Mat& mat = routed ? a.down : a.sdown;
+                    const int cols = routed ? a.I : a.Is;
+                    const int q = lane / CPR, chunk = lane % CPR;
+                    const int nl = grp * (64 / CPR) + q;
+                    tsv[i] = mat.ts[e];
+                    if (nl < NH) {
+                        const size_t row = (size_t)e * H + n_base + nl;
+                        code[i] = *reinterpret_cast<const uint4*>(mat.q + row * (cols / 2) + chunk * 16);
+                        scl[i] = *reinterpret_cast<const uint16_t*>(mat.s + row * (cols / 16) + chunk * 2);
+                    }
+                }
+            }
+        };
+        load_batch(0);
+
         // stage h rows [c0, c1) into LDS (row stride RL floats), every load of
         // a pass in flight together
         {
@@ -707,36 +900,10 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
                 }
             }
         }
+        __syncthreads();  // staged h visible to every wave
 
         for (int tb = 0; tb * kDownWaves * kDownBatch < nT; ++tb) {
-            // codes and scales of this wave's batch of tasks
-            uint4 code[kDownBatch];
-            uint32_t scl[kDownBatch];
-            float tsv[kDownBatch];
-#pragma unroll
-            for (int i = 0; i < kDownBatch; ++i) {
-                const int t = (tb * kDownBatch + i) * kDownWaves + wave;
-                code[i] = make_uint4(0, 0, 0, 0);
-                scl[i] = 0;
-                tsv[i] = 0.0f;
-                if (t < nT) {
-                    const bool routed = t < (u_hi - u_lo) * gI;
-                    const int CPR = routed ? cprI : cprS;
-                    const int grp = routed ? t % gI : t - (u_hi - u_lo) * gI;
-                    const int e = routed ? s_uniq[u_lo + t / gI] : 0;
-                    const Fp4Mat& mat = routed ? a.down : a.sdown;
-                    const int cols = routed ? a.I : a.Is;
-                    const int q = lane / CPR, chunk = lane % CPR;
-                    const int nl = grp * (64 / CPR) + q;
-                    tsv[i] = mat.ts[e];
-                    if (nl < NH) {
-                        const size_t row = (size_t)e * H + n_base + nl;
-                        code[i] = *reinterpret_cast<const uint4*>(mat.q + row * (cols / 2) + chunk * 16);
-                        scl[i] = *reinterpret_cast<const uint16_t*>(mat.s + row * (cols / 16) + chunk * 2);
-                    }
-                }
-            }
-            if (tb == 0) __syncthreads();  // staged h visible to every wave
+            if (tb > 0) load_batch(tb);
 #pragma unroll
             for (int i = 0; i < kDownBatch; ++i) {
                 const int t = (tb * kDownBatch + i) * kDownWaves + wave;
@@ -757,30 +924,23 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
                 const float s0 = e4m3_to_f32<0>(scl[i]), s1 = e4m3_to_f32<1>(scl[i]);
                 for (int pp = p_lo; pp < p_hi; ++pp) {
                     const float4* hp = reinterpret_cast<const float4*>(hs + (size_t)(pp - c0) * RL + chunk * 32);
-                    float a0 = 0.f, a1 = 0.f;
+                    // four independent chains of eight products
+                    float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int t4 = 0; t4 < 4; ++t4) {
+                    for (int t4 = 0; t4 < 8; ++t4) {
                         const float4 hv = hp[t4];
-                        a0 = fmaf(wf[4 * t4 + 0], hv.x, a0);
-                        a0 = fmaf(wf[4 * t4 + 1], hv.y, a0);
-                        a0 = fmaf(wf[4 * t4 + 2], hv.z, a0);
-                        a0 = fmaf(wf[4 * t4 + 3], hv.w, a0);
+                        float& c = acc[t4 >> 1];
+                        c = fmaf(wf[4 * t4 + 0], hv.x, c);
+                        c = fmaf(wf[4 * t4 + 1], hv.y, c);
+                        c = fmaf(wf[4 * t4 + 2], hv.z, c);
+                        c = fmaf(wf[4 * t4 + 3], hv.w, c);
                     }
-#pragma unroll
-                    for (int t4 = 4; t4 < 8; ++t4) {
-                        const float4 hv = hp[t4];
-                        a1 = fmaf(wf[4 * t4 + 0], hv.x, a1);
-                        a1 = fmaf(wf[4 * t4 + 1], hv.y, a1);
-                        a1 = fmaf(wf[4 * t4 + 2], hv.z, a1);
-                        a1 = fmaf(wf[4 * t4 + 3], hv.w, a1);
-                    }
-                    float p = fmaf(a1, s1, a0 * s0);
+                    float p = fmaf(acc[2] + acc[3], s1, (acc[0] + acc[1]) * s0);
                     p = group_sum_rt(p, CPR);
                     if (nl < NH && chunk == CPR - 1) so[pp * NH + nl] = p * ts;
                 }
             }
         }
-        if (nT == 0) __syncthreads();  // (the batch loop did not run: publish the staging)
         __syncthreads();  // chunk done before its LDS rows are replaced
     }
 
@@ -841,7 +1001,13 @@ __global__ __launch_bounds__(kBlock) void k_dequant(Fp4Mat m, int n_experts, int
 // launchers
 // ---------------------------------------------------------------------------
 
-int gateup_slab_rows(int H) { return kWaves * kRowsPerWave * (64 / (H >> 5)); }
+int gateup_slab_rows(int) { return kTileRows; }
+
+bool lds_fits(int K, int E, int H) {
+    const size_t router = (size_t)K * H * 4 + (size_t)kRedFloats * 4;
+    return gateup_smem_bytes(K, E, H) <= (size_t)kMaxDynLds && router <= (size_t)kMaxDynLds &&
+           select_smem_bytes(K, E) <= (size_t)kMaxDynLds;
+}
 
 // Plain launch, or one whose start/stop events carry the kernel's own
 // dispatch timestamps.
@@ -857,7 +1023,6 @@ hipError_t launch(Kern k, dim3 grid, dim3 block, size_t smem, hipStream_t st, co
 // Dynamic LDS above the default per-launch limit: the selection stages
 // K*E logits (up to 64 KiB) next to its fixed tables; the down kernel stages
 // 64 KiB of h next to its static tables.
-constexpr int kSelectMaxDynLds = 96 * 1024;
 
 template <typename Kern>
 hipError_t set_lds(Kern k, int bytes) {
@@ -867,20 +1032,21 @@ hipError_t set_lds(Kern k, int bytes) {
 hipError_t init_kernels() {
     static hipError_t once = [] {
         hipError_t e;
-        if ((e = set_lds(k_select, kSelectMaxDynLds)) != hipSuccess) return e;
-        if ((e = set_lds(k_gateup<1>, kSelectMaxDynLds)) != hipSuccess) return e;
-        if ((e = set_lds(k_gateup<2>, kSelectMaxDynLds)) != hipSuccess) return e;
-        if ((e = set_lds(k_gateup<4>, kSelectMaxDynLds)) != hipSuccess) return e;
-        if ((e = set_lds(k_gateup<8>, kSelectMaxDynLds)) != hipSuccess) return e;
-        if ((e = set_lds(k_gateup<16>, kSelectMaxDynLds)) != hipSuccess) return e;
+        if ((e = set_lds(k_select, kMaxDynLds)) != hipSuccess) return e;
+        if ((e = set_lds(k_gateup, kMaxDynLds)) != hipSuccess) return e;
+        if ((e = set_lds(k_router<1>, kMaxDynLds)) != hipSuccess) return e;
+        if ((e = set_lds(k_router<2>, kMaxDynLds)) != hipSuccess) return e;
+        if ((e = set_lds(k_router<4>, kMaxDynLds)) != hipSuccess) return e;
+        if ((e = set_lds(k_router<8>, kMaxDynLds)) != hipSuccess) return e;
+        if ((e = set_lds(k_router<16>, kMaxDynLds)) != hipSuccess) return e;
         return set_lds(k_down, kDownHLdsBytes);
     }();
     return once;
 }
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t st, const Timing* t) {
-    const int grid = (a.E + kWaves - 1) / kWaves + (a.sgate.q ? a.Is / a.slab : 0);
-    const size_t smem = (size_t)a.K * a.H * 2;
+    const int grid = (a.E + kWaves - 1) / kWaves + (a.sgate.q ? a.Is / kTileRows : 0);
+    const size_t smem = (size_t)a.K * a.H * 4 + (a.sgate.q ? (size_t)kRedFloats * 4 : 0);
     const dim3 g(grid), b(kBlock);
     if (a.K <= 1) return launch(k_router<1>, g, b, smem, st, t, a);
     if (a.K <= 2) return launch(k_router<2>, g, b, smem, st, t, a);
@@ -894,15 +1060,9 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_gateup(const GateUpArgs& a, int max_unique, hipStream_t st, const Timing* t) {
-    int grid = max_unique * (a.I / a.slab);
+    int grid = max_unique * (a.I / kTileRows);
     if (grid > kGateUpMaxGrid) grid = kGateUpMaxGrid;
-    const dim3 g(grid), b(kBlock);
-    const size_t smem = select_smem_bytes(a.K, a.sel.E);
-    if (a.K <= 1) return launch(k_gateup<1>, g, b, smem, st, t, a);
-    if (a.K <= 2) return launch(k_gateup<2>, g, b, smem, st, t, a);
-    if (a.K <= 4) return launch(k_gateup<4>, g, b, smem, st, t, a);
-    if (a.K <= 8) return launch(k_gateup<8>, g, b, smem, st, t, a);
-    return launch(k_gateup<16>, g, b, smem, st, t, a);
+    return launch(k_gateup, dim3(grid), dim3(kBlock), gateup_smem_bytes(a.K, a.sel.E, a.H), st, t, a);
 }
 
 hipError_t launch_down(const DownArgs& a, hipStream_t st, const Timing* t) {
