@@ -191,6 +191,8 @@ struct SelectSmem {
     int32_t uniq[kMaxSlots];
     int32_t off[kMaxSlots + 1];
     int32_t n_unique;
+    uint32_t rowmask[kMaxExperts];   // rows that selected each expert
+    int32_t cstart[kMaxExperts];     // CSR offset of each expert
 };
 
 // Copy n floats global -> LDS with every load of a pass in flight at once.
@@ -296,74 +298,60 @@ __device__ void wave_topk_rt(const SelectArgs& a, const float* lr, int r, Select
     else wave_topk<16>(a, lr, r, sm);
 }
 
-// Canonical dedup of the n selected slots, in one wave, in registers: for
-// each slot s with expert id_s,
-//   rank  = #{t < s : id_t == id_s}          (order inside its expert group)
-//   start = #{t : id_t < id_s}               (CSR offset of the group)
-//   ulow  = #{distinct ids < id_s}           (position in the unique list)
+// Canonical dedup of the n = K*k selected slots with the whole workgroup.
+// A row never selects an expert twice, so expert e's slots are one per row
+// that picked it, in row order: with rowmask[e] the set of those rows,
+//   count(e) = popcount(rowmask[e]),
+//   rank of slot (r, j) inside its expert = popcount(rowmask[e] & (2^r - 1)).
+// Exclusive prefix sums over experts of count(e) and of (count(e) > 0) give
+// the CSR offset and the position in the ascending unique list.
 // Results go to sm.asg / sm.inv / sm.uniq / sm.off / sm.n_unique.
-__device__ void dedup_wave(SelectSmem& sm, int n) {
-    const int lane = threadIdx.x & 63;
-    constexpr int SPL = kMaxSlots / 64;
-    const int nj = (n + 63) >> 6;
-    int id[SPL], rank[SPL], start[SPL], ulow[SPL], first[SPL];
-#pragma unroll
-    for (int j = 0; j < SPL; ++j) {
-        const int s = lane + 64 * j;
-        id[j] = (j < nj && s < n) ? sm.sel[s] : 0x7FFFFFFF;
-        rank[j] = 0; start[j] = 0; ulow[j] = 0;
-    }
-#pragma unroll
-    for (int jt = 0; jt < SPL; ++jt) {
-        if (jt >= nj) break;
-        const int cnt = min(64, n - 64 * jt);
-        for (int tl = 0; tl < cnt; ++tl) {
-            const int it = __builtin_amdgcn_readlane(id[jt], tl);
-            const int t = 64 * jt + tl;
-#pragma unroll
-            for (int j = 0; j < SPL; ++j) {
-                if (j < nj) {
-                    const int s = lane + 64 * j;
-                    rank[j] += (it == id[j] && t < s) ? 1 : 0;
-                    start[j] += (it < id[j]) ? 1 : 0;
-                }
-            }
+__device__ void dedup_block(SelectSmem& sm, uint32_t* rowmask, int32_t* cstart, int n, int k, int E) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ int s_wsum[kWaves][2];
+    for (int e = tid; e < E; e += kBlock) rowmask[e] = 0u;
+    __syncthreads();
+    for (int s = tid; s < n; s += kBlock) atomicOr(&rowmask[sm.sel[s]], 1u << (s / k));
+    __syncthreads();
+    // each thread owns Q consecutive experts
+    const int Q = (E + kBlock - 1) / kBlock;
+    int c = 0, f = 0;
+    for (int q = 0; q < Q; ++q) {
+        const int e = tid * Q + q;
+        if (e < E) {
+            const int cn = __builtin_popcount(rowmask[e]);
+            c += cn;
+            f += (cn > 0);
         }
     }
-#pragma unroll
-    for (int j = 0; j < SPL; ++j) first[j] = (j < nj && lane + 64 * j < n && rank[j] == 0) ? 1 : 0;
-#pragma unroll
-    for (int jt = 0; jt < SPL; ++jt) {
-        if (jt >= nj) break;
-        const int cnt = min(64, n - 64 * jt);
-        for (int tl = 0; tl < cnt; ++tl) {
-            const int it = __builtin_amdgcn_readlane(id[jt], tl);
-            const int ft = __builtin_amdgcn_readlane(first[jt], tl);
-#pragma unroll
-            for (int j = 0; j < SPL; ++j)
-                if (j < nj) ulow[j] += (ft && it < id[j]) ? 1 : 0;
+    const int ci = wave_incl_scan(c), fi = wave_incl_scan(f);
+    if (lane == 63) { s_wsum[wave][0] = ci; s_wsum[wave][1] = fi; }
+    __syncthreads();
+    int cb = 0, fb = 0;
+    for (int w = 0; w < wave; ++w) { cb += s_wsum[w][0]; fb += s_wsum[w][1]; }
+    int cs = cb + ci - c, fs = fb + fi - f;
+    for (int q = 0; q < Q; ++q) {
+        const int e = tid * Q + q;
+        if (e < E) {
+            const int cn = __builtin_popcount(rowmask[e]);
+            cstart[e] = cs;
+            if (cn) { sm.uniq[fs] = e; sm.off[fs] = cs; }
+            cs += cn;
+            fs += (cn > 0);
         }
     }
-    int U = 0;
-#pragma unroll
-    for (int j = 0; j < SPL; ++j) {
-        if (j < nj) {
-            const int s = lane + 64 * j;
-            if (s < n) {
-                const int pos = start[j] + rank[j];
-                sm.asg[pos] = s;
-                sm.inv[s] = pos;
-                if (first[j]) {
-                    sm.uniq[ulow[j]] = id[j];
-                    sm.off[ulow[j]] = start[j];
-                }
-            }
-            U += __builtin_popcountll(__ballot(first[j] != 0));
-        }
-    }
-    if (lane == 0) {
-        sm.off[U] = n;
+    if (tid == kBlock - 1) {
+        int U = 0;
+        for (int w = 0; w < kWaves; ++w) U += s_wsum[w][1];
         sm.n_unique = U;
+        sm.off[U] = n;
+    }
+    __syncthreads();
+    for (int s = tid; s < n; s += kBlock) {
+        const int e = sm.sel[s], r = s / k;
+        const int pos = cstart[e] + __builtin_popcount(rowmask[e] & ((1u << r) - 1u));
+        sm.asg[pos] = s;
+        sm.inv[s] = pos;
     }
 }
 
@@ -377,7 +365,7 @@ __device__ int select_and_dedup(const SelectArgs& a, SelectSmem& sm, float* lg, 
     __syncthreads();
     for (int r = wave; r < K; r += kWaves) wave_topk_rt(a, lg + r * E, r, sm);
     __syncthreads();
-    if (wave == 0) dedup_wave(sm, n);
+    dedup_block(sm, sm.rowmask, sm.cstart, n, k, E);
     __syncthreads();
     const int U = sm.n_unique;
     if (write_global) {
@@ -438,6 +426,12 @@ constexpr int kTileRows = 16;
 constexpr int kSbCols = 256;
 // each wave holds at most two superblocks in flight (hidden <= 2048)
 constexpr int kRedFloats = kWaves * 2 * 64 * 4;         // cross-wave partials
+
+// Padded LDS layout of the fp16 x rows: 8 halfs of padding after every 64
+// columns and 32 after each row, so the 64 lanes of an MFMA B-operand read
+// (16 rows x 4 column blocks, 16 bytes each) spread over the banks.
+__host__ __device__ constexpr int xh_row_stride(int H) { return H + (H / 64) * 8 + 32; }
+__device__ __forceinline__ int xh_index(int m, int c, int H) { return m * xh_row_stride(H) + c + (c >> 6) * 8; }
 constexpr int kMaxDynLds = 160 * 1024 - 1024;           // gfx950: 160 KiB per workgroup, minus static use
 
 // Code and scale registers of one superblock of one lane (gate and up).
@@ -511,6 +505,8 @@ __device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t packed) {
 }
 
 // The eight MFMA steps of one superblock.
+// xr: this lane's x row in LDS at the superblock's first column of its
+// 64-column block (8 consecutive halfs per MFMA step, no padding inside).
 __device__ __forceinline__ void gu_mfma_sb(const GuSb& r, const _Float16* xr, bool has_x, f32x4_t& accg,
                                            f32x4_t& accu) {
     const f16x8_t zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -530,7 +526,7 @@ __device__ __forceinline__ void gu_mfma_sb(const GuSb& r, const _Float16* xr, bo
     }
 }
 
-// xh: fp16 x rows in LDS, row stride H; rows >= m_cnt are not read.
+// xh: fp16 x rows in LDS (padded layout, xh_index); rows >= m_cnt are not read.
 // Writes h[j * hstride + n0 + r] for x rows j < m_cnt and the tile's 16 rows.
 __device__ __forceinline__ void gu_compute(const GuRegs& R, float gts, float uts, int H, int n0,
                                            const _Float16* xh, int m_cnt, float* hbase, int hstride, float* red) {
@@ -538,9 +534,10 @@ __device__ __forceinline__ void gu_compute(const GuRegs& R, float gts, float uts
     const int j = lane & 15, kb = lane >> 4;
     const int nsb = H / kSbCols;
     f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-    const _Float16* xr = xh + (size_t)j * H + kb * 64;
-    if (wave < nsb) gu_mfma_sb(R.sb0, xr + wave * kSbCols, j < m_cnt, accg, accu);
-    if (wave + kWaves < nsb) gu_mfma_sb(R.sb1, xr + (wave + kWaves) * kSbCols, j < m_cnt, accg, accu);
+    if (wave < nsb)
+        gu_mfma_sb(R.sb0, xh + xh_index(j, wave * kSbCols + kb * 64, H), j < m_cnt, accg, accu);
+    if (wave + kWaves < nsb)
+        gu_mfma_sb(R.sb1, xh + xh_index(j, (wave + kWaves) * kSbCols + kb * 64, H), j < m_cnt, accg, accu);
     reinterpret_cast<f32x4_t*>(red)[(wave * 2 + 0) * 64 + lane] = accg;
     reinterpret_cast<f32x4_t*>(red)[(wave * 2 + 1) * 64 + lane] = accu;
     __syncthreads();
@@ -596,7 +593,7 @@ __device__ __forceinline__ void stage_x_f16(const uint16_t* x, const int32_t* as
                 uint4 o;
                 o.x = bf16pair_to_f16pair(v[q].x); o.y = bf16pair_to_f16pair(v[q].y);
                 o.z = bf16pair_to_f16pair(v[q].z); o.w = bf16pair_to_f16pair(v[q].w);
-                *reinterpret_cast<uint4*>(xh + (size_t)m * H + c * 8) = o;
+                *reinterpret_cast<uint4*>(xh + xh_index(m, c * 8, H)) = o;
             }
         }
     }
@@ -740,7 +737,7 @@ __global__ __launch_bounds__(kBlock) void k_router(RouterArgs a) {
         const GuRegs R = gu_load(a.sgate.q, a.sgate.s, a.sup.q, a.sup.s, H, n0);
         stage_x(a, xs, s_inv, false, 0, 1);
         _Float16* xh = reinterpret_cast<_Float16*>(smem + (size_t)K * H * 2);
-        float* red = reinterpret_cast<float*>(smem + (size_t)K * H * 4);
+        float* red = reinterpret_cast<float*>(smem + (size_t)K * H * 2 + (size_t)K * xh_row_stride(H) * 2);
         stage_x_f16(xs, nullptr, 0, 1, K, H, xh);
         __syncthreads();
         gu_compute(R, a.sgate.ts[0], a.sup.ts[0], H, n0, xh, K, a.h_sh, a.Is, red);
@@ -754,7 +751,7 @@ __global__ __launch_bounds__(kBlock) void k_router(RouterArgs a) {
 // ---------------------------------------------------------------------------
 
 __host__ __device__ constexpr size_t gateup_smem_bytes(int K, int E, int H) {
-    return select_smem_bytes(K, E) + (size_t)K * H * 2 + (size_t)kRedFloats * 4;
+    return select_smem_bytes(K, E) + (size_t)K * xh_row_stride(H) * 2 + (size_t)kRedFloats * 4;
 }
 
 __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
@@ -762,7 +759,7 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
     SelectSmem& sm = *reinterpret_cast<SelectSmem*>(smem);
     float* lg = reinterpret_cast<float*>(smem + (sizeof(SelectSmem) + 15) / 16 * 16);
     _Float16* xh = reinterpret_cast<_Float16*>(smem + select_smem_bytes(a.K, a.sel.E));
-    float* red = reinterpret_cast<float*>(smem + select_smem_bytes(a.K, a.sel.E) + (size_t)a.K * a.H * 2);
+    float* red = reinterpret_cast<float*>(smem + select_smem_bytes(a.K, a.sel.E) + (size_t)a.K * xh_row_stride(a.H) * 2);
     const int U = select_and_dedup(a.sel, sm, lg, blockIdx.x == 0);
     const int H = a.H, k = a.sel.k;
     const int nsr = a.I / kTileRows;
@@ -820,8 +817,11 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
     __syncthreads();
     const int U = s_U;
 
-    const int RL = max(a.I, has_sh ? a.Is : 0);   // LDS row stride of staged h
-    const int CAP = (kDownHLdsBytes / 4) / RL;      // rows per chunk
+    // staged h rows: 4 floats of padding after every 32-column chunk, so the
+    // 16 lanes of a weight row (one chunk each) do not share LDS banks
+    const int RL = max(a.I, has_sh ? a.Is : 0);
+    const int RLP = RL / 32 * 36;                   // padded LDS row stride
+    const int CAP = (kDownHLdsBytes / 4) / RLP;     // rows per chunk
     const int total_rows = n + (has_sh ? K : 0);
     const int cprI = a.I >> 5;
     const int gI = max(1, NH / (64 / cprI));
@@ -832,7 +832,9 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
         const int c1 = min(total_rows, c0 + CAP);
         // routed experts with slots in [c0, c1): a contiguous range of u
         int u_lo = 0, u_hi = 0;
-        if (c0 < n) {
+        if (c0 == 0 && c1 >= n) {
+            u_hi = U;
+        } else if (c0 < n) {
             while (u_lo < U && s_off[u_lo + 1] <= c0) ++u_lo;
             u_hi = u_lo;
             while (u_hi < U && s_off[u_hi] < min(c1, n)) ++u_hi;
@@ -875,7 +877,7 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
         // stage h rows [c0, c1) into LDS (row stride RL floats), every load of
         // a pass in flight together
         {
-            const int q4 = RL / 4;                  // float4 per staged row
+            const int q4 = RL / 4;                  // float4 per staged row (unpadded)
             const int nf4 = (c1 - c0) * q4;
             constexpr int SU = 8;
             for (int base = 0; base < nf4; base += SU * kDownThreads) {
@@ -896,7 +898,10 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
 #pragma unroll
                 for (int j = 0; j < SU; ++j) {
                     const int f = base + j * kDownThreads + tid;
-                    if (f < nf4) reinterpret_cast<float4*>(hs)[f] = v[j];
+                    if (f < nf4) {
+                        const int rr = f / q4, c4 = f % q4;
+                        *reinterpret_cast<float4*>(hs + (size_t)rr * RLP + (c4 >> 3) * 36 + (c4 & 7) * 4) = v[j];
+                    }
                 }
             }
         }
@@ -923,7 +928,7 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
                 fp4x8_to_f32(code[i].z, wf + 16); fp4x8_to_f32(code[i].w, wf + 24);
                 const float s0 = e4m3_to_f32<0>(scl[i]), s1 = e4m3_to_f32<1>(scl[i]);
                 for (int pp = p_lo; pp < p_hi; ++pp) {
-                    const float4* hp = reinterpret_cast<const float4*>(hs + (size_t)(pp - c0) * RL + chunk * 32);
+                    const float4* hp = reinterpret_cast<const float4*>(hs + (size_t)(pp - c0) * RLP + chunk * 36);
                     // four independent chains of eight products
                     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1004,7 +1009,7 @@ __global__ __launch_bounds__(kBlock) void k_dequant(Fp4Mat m, int n_experts, int
 int gateup_slab_rows(int) { return kTileRows; }
 
 bool lds_fits(int K, int E, int H) {
-    const size_t router = (size_t)K * H * 4 + (size_t)kRedFloats * 4;
+    const size_t router = (size_t)K * H * 2 + (size_t)K * xh_row_stride(H) * 2 + (size_t)kRedFloats * 4;
     return gateup_smem_bytes(K, E, H) <= (size_t)kMaxDynLds && router <= (size_t)kMaxDynLds &&
            select_smem_bytes(K, E) <= (size_t)kMaxDynLds;
 }
@@ -1046,7 +1051,8 @@ hipError_t init_kernels() {
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t st, const Timing* t) {
     const int grid = (a.E + kWaves - 1) / kWaves + (a.sgate.q ? a.Is / kTileRows : 0);
-    const size_t smem = (size_t)a.K * a.H * 4 + (a.sgate.q ? (size_t)kRedFloats * 4 : 0);
+    const size_t smem = (size_t)a.K * a.H * 2 +
+                        (a.sgate.q ? (size_t)a.K * xh_row_stride(a.H) * 2 + (size_t)kRedFloats * 4 : 0);
     const dim3 g(grid), b(kBlock);
     if (a.K <= 1) return launch(k_router<1>, g, b, smem, st, t, a);
     if (a.K <= 2) return launch(k_router<2>, g, b, smem, st, t, a);
