@@ -176,11 +176,7 @@ int enqueue_layer(const moe_cfg* c, const moe_layer_weights* w, const LayerIO& i
     ra.eps = c->rms_eps;
     ra.wr = w->router_w;
     ra.logits = L.logits;
-    ra.sgate = has_sh ? mat(w->sh_gate) : none;
-    ra.sup = has_sh ? mat(w->sh_up) : none;
-    ra.h_sh = L.h_sh;
-    ra.K = K; ra.H = c->hidden; ra.E = c->n_experts; ra.Is = c->shared_inter;
-    ra.slab = moe::gateup_slab_rows(c->hidden);
+    ra.K = K; ra.H = c->hidden; ra.E = c->n_experts;
     if ((e = moe::launch_router(ra, st, tm ? &tm[0] : nullptr)) != hipSuccess) return hip_fail(e, "router launch");
 
     moe::GateUpArgs ga{};
@@ -194,8 +190,10 @@ int enqueue_layer(const moe_cfg* c, const moe_layer_weights* w, const LayerIO& i
     ga.x = io.y_prev ? L.xbuf : io.x_in;
     ga.gate = mat(w->gate); ga.up = mat(w->up);
     ga.h = L.h;
-    ga.K = K; ga.H = c->hidden; ga.I = c->inter;
-    ga.slab = moe::gateup_slab_rows(c->hidden);
+    ga.sgate = has_sh ? mat(w->sh_gate) : none;
+    ga.sup = has_sh ? mat(w->sh_up) : none;
+    ga.h_sh = L.h_sh;
+    ga.K = K; ga.H = c->hidden; ga.I = c->inter; ga.Is = c->shared_inter;
     const int max_unique = std::min(c->n_experts, K * c->top_k);
     if ((e = moe::launch_gateup(ga, max_unique, st, tm ? &tm[1] : nullptr)) != hipSuccess)
         return hip_fail(e, "gate/up launch");

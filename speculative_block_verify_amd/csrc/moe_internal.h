@@ -14,7 +14,6 @@ constexpr int kMaxExperts = 1024;  // E
 constexpr int kMaxSlots = kMaxRows * kMaxTopK;
 constexpr int kBlock = 256;        // threads per workgroup (4 wave64)
 constexpr int kWaves = kBlock / 64;
-constexpr int kRowsPerWave = 4;    // weight rows each wave keeps in flight in gate/up
 constexpr int kDownRowsPerBlock = 8;
 constexpr int kDownThreads = 512;  // 8 wave64 per down workgroup
 constexpr int kDownHLdsBytes = 64 * 1024;  // h rows staged in LDS per chunk
@@ -41,7 +40,7 @@ struct SelectArgs {
     int K, E, k, score_fn, norm_topk;
 };
 
-// Router GEMV (+ the shared expert's gate/up, which needs only x).
+// Router GEMV (and the RMS normalisation of the previous layer's output).
 struct RouterArgs {
     const uint16_t* x_in;   // bf16 [K][H], read when y_prev == nullptr
     const float* y_prev;    // fp32 [K][H] to RMS-normalise into x, or nullptr
@@ -50,20 +49,19 @@ struct RouterArgs {
     float eps;
     const uint16_t* wr;     // bf16 [E][H]
     float* logits;          // [K][E]
-    Fp4Mat sgate, sup;      // [1][Is][H/2] (q == nullptr: no shared expert)
-    float* h_sh;            // [K][Is]
-    int K, H, E, Is;
-    int slab;               // shared gate/up rows per workgroup
+    int K, H, E;
 };
 
-// Routed gate/up + SwiGLU; every workgroup recomputes the selection.
+// Gate/up + SwiGLU: the shared expert's tiles, then the routed work items;
+// every routed workgroup recomputes the selection.
 struct GateUpArgs {
-    SelectArgs sel;         // its outputs are written by workgroup 0 only
+    SelectArgs sel;         // its outputs are written by the first routed workgroup only
     const uint16_t* x;      // bf16 [K][H]
     Fp4Mat gate, up;        // [E][I][H/2]
     float* h;               // [K*k][I], indexed by position in asg
-    int K, H, I;
-    int slab;               // weight rows (of gate and of up) per work item
+    Fp4Mat sgate, sup;      // [1][Is][H/2] (q == nullptr: no shared expert)
+    float* h_sh;            // [K][Is]
+    int K, H, I, Is;
 };
 
 struct DownArgs {

@@ -600,17 +600,16 @@ __device__ __forceinline__ void stage_x_f16(const uint16_t* x, const int32_t* as
 }
 
 // ---------------------------------------------------------------------------
-// k_router: router GEMV (one wave per expert row) in the first ceil(E/4)
-// workgroups, the shared expert's gate/up tiles in the rest.  When chaining
-// layers, x is the RMS-normalised previous output (bf16), with the sums of
-// squares taken from the down kernel's per-workgroup partials.
+// k_router: router GEMV, one wave per expert row, ceil(E/4) workgroups.
+// When chaining layers, x is the RMS-normalised previous output (bf16), with
+// the sums of squares taken from the down kernel's per-workgroup partials;
+// every workgroup normalises all rows and publishes its share of x.
 // ---------------------------------------------------------------------------
 
 constexpr int kRouterPieces = 4;  // 16-byte router pieces per lane (hidden <= 2048)
 
 // Builds this layer's bf16 x in LDS (xs, K*H) from x_in or from y_prev.
-__device__ void stage_x(const RouterArgs& a, uint16_t* xs, float* s_inv, bool publish, int publish_idx,
-                        int publish_n) {
+__device__ void stage_x(const RouterArgs& a, uint16_t* xs, float* s_inv, int publish_idx, int publish_n) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int K = a.K, H = a.H, KH = K * H;
     if (a.y_prev) {
@@ -656,7 +655,7 @@ __device__ void stage_x(const RouterArgs& a, uint16_t* xs, float* s_inv, bool pu
             }
         }
         __syncthreads();
-        if (publish) {  // this workgroup's share of the normalised x
+        {  // this workgroup's share of the normalised x
             const int per = (KH / 8 + publish_n - 1) / publish_n * 8;
             const int i0 = publish_idx * per;
             for (int i = i0 + tid * 8; i < min(KH, i0 + per); i += kBlock * 8)
@@ -690,7 +689,7 @@ __global__ __launch_bounds__(kBlock) void k_router(RouterArgs a) {
     const int K = a.K, H = a.H, E = a.E;
     const int n_router_blocks = (E + kWaves - 1) / kWaves;
 
-    if ((int)blockIdx.x < n_router_blocks) {
+    {
         // this wave's router row, requested before anything else
         const int e = blockIdx.x * kWaves + wave;
         uint4 wv[kRouterPieces];
@@ -700,7 +699,7 @@ __global__ __launch_bounds__(kBlock) void k_router(RouterArgs a) {
             wv[t] = (e < E && p < H) ? *reinterpret_cast<const uint4*>(a.wr + (size_t)e * H + p)
                                      : make_uint4(0, 0, 0, 0);
         }
-        stage_x(a, xs, s_inv, true, blockIdx.x, n_router_blocks);
+        stage_x(a, xs, s_inv, blockIdx.x, n_router_blocks);
         if (e < E) {
             float acc[kMaxRows];
 #pragma unroll
@@ -731,23 +730,15 @@ __global__ __launch_bounds__(kBlock) void k_router(RouterArgs a) {
                 }
             }
         }
-    } else {
-        // shared expert gate/up tile: weights requested before x is ready
-        const int n0 = (blockIdx.x - n_router_blocks) * kTileRows;
-        const GuRegs R = gu_load(a.sgate.q, a.sgate.s, a.sup.q, a.sup.s, H, n0);
-        stage_x(a, xs, s_inv, false, 0, 1);
-        _Float16* xh = reinterpret_cast<_Float16*>(smem + (size_t)K * H * 2);
-        float* red = reinterpret_cast<float*>(smem + (size_t)K * H * 2 + (size_t)K * xh_row_stride(H) * 2);
-        stage_x_f16(xs, nullptr, 0, 1, K, H, xh);
-        __syncthreads();
-        gu_compute(R, a.sgate.ts[0], a.sup.ts[0], H, n0, xh, K, a.h_sh, a.Is, red);
     }
 }
 
 // ---------------------------------------------------------------------------
-// k_gateup: every workgroup repeats the selection from the 2 KB of logits
-// (cheaper than a separate launch or a grid-wide fence), then loops over the
-// routed work items (unique expert, 16 intermediate rows)
+// k_gateup: the first Is/16 workgroups are the shared expert's gate/up tiles
+// (they need only x and skip the selection); every other workgroup repeats
+// the selection from the 2 KB of logits (cheaper than a separate launch or a
+// grid-wide fence), then loops over the routed work items (unique expert,
+// 16 intermediate rows)
 // ---------------------------------------------------------------------------
 
 __host__ __device__ constexpr size_t gateup_smem_bytes(int K, int E, int H) {
@@ -760,11 +751,22 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
     float* lg = reinterpret_cast<float*>(smem + (sizeof(SelectSmem) + 15) / 16 * 16);
     _Float16* xh = reinterpret_cast<_Float16*>(smem + select_smem_bytes(a.K, a.sel.E));
     float* red = reinterpret_cast<float*>(smem + select_smem_bytes(a.K, a.sel.E) + (size_t)a.K * xh_row_stride(a.H) * 2);
-    const int U = select_and_dedup(a.sel, sm, lg, blockIdx.x == 0);
     const int H = a.H, k = a.sel.k;
+    const int n_sh = a.sgate.q ? a.Is / kTileRows : 0;
+    if ((int)blockIdx.x < n_sh) {
+        // shared expert tile: weights requested before x is staged
+        const int n0 = blockIdx.x * kTileRows;
+        const GuRegs R = gu_load(a.sgate.q, a.sgate.s, a.sup.q, a.sup.s, H, n0);
+        stage_x_f16(a.x, nullptr, 0, 1, a.K, H, xh);
+        __syncthreads();
+        gu_compute(R, a.sgate.ts[0], a.sup.ts[0], H, n0, xh, a.K, a.h_sh, a.Is, red);
+        return;
+    }
+    const int rb = blockIdx.x - n_sh, n_rb = gridDim.x - n_sh;
+    const int U = select_and_dedup(a.sel, sm, lg, rb == 0);
     const int nsr = a.I / kTileRows;
     const int items = U * nsr;
-    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    for (int it = rb; it < items; it += n_rb) {
         const int u = it / nsr;
         const int e = sm.uniq[u];
         const int o0 = sm.off[u];
@@ -799,10 +801,20 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
     __shared__ float s_y[kMaxRows * NH];
     __shared__ int s_U;
     extern __shared__ __align__(16) float hs[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // wave index made visibly uniform: the task index, the expert and the
+    // matrix choice below then live in scalar registers
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.H, K = a.K, k = a.k, n = K * k;
     const int n_base = blockIdx.x * NH;
     const bool has_sh = a.sdown.q != nullptr;
+    // matrix pointers read once; the per-task choice below selects values
+    const uint8_t* const dq = a.down.q;
+    const uint8_t* const ds = a.down.s;
+    const float* const dts = a.down.ts;
+    const uint8_t* const sq = a.sdown.q;
+    const uint8_t* const ss = a.sdown.s;
+    const float* const sts = a.sdown.ts;
+    const int I = a.I, Is = a.Is;
 
     // routing metadata: independent loads, one round trip
     for (int i = tid; i <= n; i += kDownThreads) {
@@ -819,13 +831,15 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
 
     // staged h rows: 4 floats of padding after every 32-column chunk, so the
     // 16 lanes of a weight row (one chunk each) do not share LDS banks
-    const int RL = max(a.I, has_sh ? a.Is : 0);
+    const int RL = max(I, has_sh ? Is : 0);
     const int RLP = RL / 32 * 36;                   // padded LDS row stride
     const int CAP = (kDownHLdsBytes / 4) / RLP;     // rows per chunk
     const int total_rows = n + (has_sh ? K : 0);
-    const int cprI = a.I >> 5;
-    const int gI = max(1, NH / (64 / cprI));
-    const int cprS = has_sh ? (a.Is >> 5) : 1;
+    // lanes per weight row (one 32-column chunk each) and tasks per expert;
+    // all powers of two, so lane and task indices split with shifts
+    const int cprI = I >> 5, lgI = __builtin_ctz(cprI);
+    const int gI = max(1, NH / (64 / cprI)), lgG = __builtin_ctz(gI);
+    const int cprS = has_sh ? (Is >> 5) : 1, lgS = __builtin_ctz(cprS);
     const int gS = has_sh ? max(1, NH / (64 / cprS)) : 0;
 
     for (int c0 = 0; c0 < total_rows; c0 += CAP) {
@@ -847,82 +861,95 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
         uint4 code[kDownBatch];
         uint32_t scl[kDownBatch];
         float tsv[kDownBatch];
-        auto load_batch = [&](int tb) {
+        // every expert id of a batch is read from LDS before any of its
+        // global loads is issued: one LDS wait per batch
+        int ev[kDownBatch];
+        auto batch_ids = [&](int tb) {
 #pragma unroll
             for (int i = 0; i < kDownBatch; ++i) {
                 const int t = (tb * kDownBatch + i) * kDownWaves + wave;
-                code[i] = make_uint4(0, 0, 0, 0);
-                scl[i] = 0;
-                tsv[i] = 0.0f;
-                if (t < nT) {
-                    const bool routed = t < (u_hi - u_lo) * gI;
-                    const int CPR = routed ? cprI : cprS;
-                    const int grp = routed ? t % gI : t - (u_hi - u_lo) * gI;
-                    const int e = routed ? s_uniq[u_lo + t / gI] : 0;
-                    const Fp4Mat& mat = routed ? a.down : a.sdown;
-                    const int cols = routed ? a.I : a.Is;
-                    const int q = lane / CPR, chunk = lane % CPR;
-                    const int nl = grp * (64 / CPR) + q;
-                    tsv[i] = mat.ts[e];
-                    if (nl < NH) {
-                        const size_t row = (size_t)e * H + n_base + nl;
-                        code[i] = *reinterpret_cast<const uint4*>(mat.q + row * (cols / 2) + chunk * 16);
-                        scl[i] = *reinterpret_cast<const uint16_t*>(mat.s + row * (cols / 16) + chunk * 2);
-                    }
-                }
+                ev[i] = (t < (u_hi - u_lo) * gI) ? s_uniq[u_lo + (t >> lgG)] : 0;
             }
         };
+        auto load_batch = [&](int tb) {
+            // Loads are issued unconditionally (the counter of outstanding
+            // loads then stays known to the compiler): a task past the end
+            // reads row n_base of routed expert 0 and a lane past the
+            // workgroup's rows reads row n_base; neither result is stored.
+#pragma unroll
+            for (int i = 0; i < kDownBatch; ++i) {
+                const int t = (tb * kDownBatch + i) * kDownWaves + wave;
+                const bool routed = t < (u_hi - u_lo) * gI;
+                const bool shared_task = !routed && t < nT;
+                const int lgC = shared_task ? lgS : lgI;
+                const int grp = routed ? (t & (gI - 1)) : (shared_task ? t - (u_hi - u_lo) * gI : 0);
+                const int e = ev[i];
+                const uint8_t* mq = shared_task ? sq : dq;
+                const uint8_t* ms = shared_task ? ss : ds;
+                const float* mts = shared_task ? sts : dts;
+                const int cols = shared_task ? Is : I;
+                const int q = lane >> lgC, chunk = lane & ((1 << lgC) - 1);
+                const int nl = (grp << (6 - lgC)) + q;
+                const size_t row = (size_t)e * H + n_base + (nl < NH ? nl : 0);
+                tsv[i] = mts[e];
+                code[i] = *reinterpret_cast<const uint4*>(mq + row * (cols / 2) + chunk * 16);
+                scl[i] = *reinterpret_cast<const uint16_t*>(ms + row * (cols / 16) + chunk * 2);
+            }
+        };
+        // stage h rows [c0, c1) into LDS: one pass of SU float4 per thread
+        // covers a whole chunk (static_assert below), so the h loads, the
+        // first batch of code loads and then the LDS stores form one
+        // straight-line sequence with both round trips overlapped
+        constexpr int SU = 8;
+        static_assert(kDownHLdsBytes / 16 <= SU * kDownThreads, "h chunk exceeds one staging pass");
+        const int q4 = RL / 4;                  // float4 per staged row (unpadded)
+        const int nf4 = (c1 - c0) * q4;
+        // (loads unconditional at clamped addresses, as in load_batch;
+        // columns past a shorter row's length are staged as zeros)
+        batch_ids(0);
+        float4 hv4[SU];
+#pragma unroll
+        for (int j = 0; j < SU; ++j) {
+            const int f = min(j * kDownThreads + tid, nf4 - 1);
+            const int rr = c0 + f / q4, c4 = f % q4;
+            const bool shared_row = rr >= n;
+            const int len4 = (shared_row ? Is : I) / 4;
+            const int cc = min(c4, len4 - 1);
+            hv4[j] = shared_row ? reinterpret_cast<const float4*>(a.h_sh + (size_t)(rr - n) * Is)[cc]
+                                : reinterpret_cast<const float4*>(a.h + (size_t)rr * I)[cc];
+        }
         load_batch(0);
-
-        // stage h rows [c0, c1) into LDS (row stride RL floats), every load of
-        // a pass in flight together
-        {
-            const int q4 = RL / 4;                  // float4 per staged row (unpadded)
-            const int nf4 = (c1 - c0) * q4;
-            constexpr int SU = 8;
-            for (int base = 0; base < nf4; base += SU * kDownThreads) {
-                float4 v[SU];
 #pragma unroll
-                for (int j = 0; j < SU; ++j) {
-                    const int f = base + j * kDownThreads + tid;
-                    v[j] = make_float4(0, 0, 0, 0);
-                    if (f < nf4) {
-                        const int rr = c0 + f / q4, c4 = f % q4;
-                        const bool shared_row = rr >= n;
-                        const int len4 = (shared_row ? a.Is : a.I) / 4;
-                        if (c4 < len4)
-                            v[j] = shared_row ? reinterpret_cast<const float4*>(a.h_sh + (size_t)(rr - n) * a.Is)[c4]
-                                              : reinterpret_cast<const float4*>(a.h + (size_t)rr * a.I)[c4];
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < SU; ++j) {
-                    const int f = base + j * kDownThreads + tid;
-                    if (f < nf4) {
-                        const int rr = f / q4, c4 = f % q4;
-                        *reinterpret_cast<float4*>(hs + (size_t)rr * RLP + (c4 >> 3) * 36 + (c4 & 7) * 4) = v[j];
-                    }
-                }
+        for (int j = 0; j < SU; ++j) {
+            const int f = j * kDownThreads + tid;
+            if (f < nf4) {
+                const int rr = f / q4, c4 = f % q4;
+                const int len4 = ((c0 + rr) >= n ? Is : I) / 4;
+                *reinterpret_cast<float4*>(hs + (size_t)rr * RLP + (c4 >> 3) * 36 + (c4 & 7) * 4) =
+                    c4 < len4 ? hv4[j] : make_float4(0, 0, 0, 0);
             }
         }
         __syncthreads();  // staged h visible to every wave
 
         for (int tb = 0; tb * kDownWaves * kDownBatch < nT; ++tb) {
-            if (tb > 0) load_batch(tb);
+            if (tb > 0) {
+                batch_ids(tb);
+                load_batch(tb);
+            }
 #pragma unroll
             for (int i = 0; i < kDownBatch; ++i) {
                 const int t = (tb * kDownBatch + i) * kDownWaves + wave;
                 if (t >= nT) break;
                 const bool routed = t < (u_hi - u_lo) * gI;
-                const int CPR = routed ? cprI : cprS;
-                const int grp = routed ? t % gI : t - (u_hi - u_lo) * gI;
-                const int u = u_lo + (routed ? t / gI : 0);
+                const int lgC = routed ? lgI : lgS, CPR = 1 << lgC;
+                const int grp = routed ? (t & (gI - 1)) : t - (u_hi - u_lo) * gI;
+                const int u = u_lo + (routed ? (t >> lgG) : 0);
                 const float ts = tsv[i];
                 int p_lo, p_hi;
                 if (routed) { p_lo = max(s_off[u], c0); p_hi = min(s_off[u + 1], c1); }
                 else { p_lo = max(n, c0); p_hi = c1; }
-                const int q = lane / CPR, chunk = lane % CPR;
-                const int nl = grp * (64 / CPR) + q;
+                const int q = lane >> lgC, chunk = lane & (CPR - 1);
+                const int nl = (grp << (6 - lgC)) + q;
                 float wf[32];
                 fp4x8_to_f32(code[i].x, wf + 0); fp4x8_to_f32(code[i].y, wf + 8);
                 fp4x8_to_f32(code[i].z, wf + 16); fp4x8_to_f32(code[i].w, wf + 24);
@@ -941,7 +968,7 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
                         c = fmaf(wf[4 * t4 + 3], hv.w, c);
                     }
                     float p = fmaf(acc[2] + acc[3], s1, (acc[0] + acc[1]) * s0);
-                    p = group_sum_rt(p, CPR);
+                    p = (CPR == 16) ? group_sum<16>(p) : group_sum_rt(p, CPR);
                     if (nl < NH && chunk == CPR - 1) so[pp * NH + nl] = p * ts;
                 }
             }
@@ -1009,7 +1036,7 @@ __global__ __launch_bounds__(kBlock) void k_dequant(Fp4Mat m, int n_experts, int
 int gateup_slab_rows(int) { return kTileRows; }
 
 bool lds_fits(int K, int E, int H) {
-    const size_t router = (size_t)K * H * 2 + (size_t)K * xh_row_stride(H) * 2 + (size_t)kRedFloats * 4;
+    const size_t router = (size_t)K * H * 2;
     return gateup_smem_bytes(K, E, H) <= (size_t)kMaxDynLds && router <= (size_t)kMaxDynLds &&
            select_smem_bytes(K, E) <= (size_t)kMaxDynLds;
 }
@@ -1050,9 +1077,8 @@ hipError_t init_kernels() {
 }
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t st, const Timing* t) {
-    const int grid = (a.E + kWaves - 1) / kWaves + (a.sgate.q ? a.Is / kTileRows : 0);
-    const size_t smem = (size_t)a.K * a.H * 2 +
-                        (a.sgate.q ? (size_t)a.K * xh_row_stride(a.H) * 2 + (size_t)kRedFloats * 4 : 0);
+    const int grid = (a.E + kWaves - 1) / kWaves;
+    const size_t smem = (size_t)a.K * a.H * 2;
     const dim3 g(grid), b(kBlock);
     if (a.K <= 1) return launch(k_router<1>, g, b, smem, st, t, a);
     if (a.K <= 2) return launch(k_router<2>, g, b, smem, st, t, a);
@@ -1068,6 +1094,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
 hipError_t launch_gateup(const GateUpArgs& a, int max_unique, hipStream_t st, const Timing* t) {
     int grid = max_unique * (a.I / kTileRows);
     if (grid > kGateUpMaxGrid) grid = kGateUpMaxGrid;
+    grid += a.sgate.q ? a.Is / kTileRows : 0;
     return launch(k_gateup, dim3(grid), dim3(kBlock), gateup_smem_bytes(a.K, a.sel.E, a.H), st, t, a);
 }
 
