@@ -89,7 +89,9 @@ typedef struct moe_cfg {
     float routed_scale;    /* multiplies the weighted routed sum (2.5 on the
                               pages' checkpoint, 1.0 for plain softmax MoE) */
     float rms_eps;         /* RMSNorm epsilon between stacked layers */
-    int32_t max_rows;      /* largest K a workspace of this cfg serves */
+    int32_t max_rows;      /* largest K a workspace of this cfg serves
+                              (1..1024; above 16 the cfg must also meet the
+                              grouped-regime limits below) */
 } moe_cfg;
 
 typedef struct moe_layer_weights {
@@ -139,14 +141,34 @@ MOE_API size_t moe_verify_workspace_bytes(const moe_cfg* cfg);
 
 /* One layer (steps 1-8) on bf16 rows x [K][H].  residual (bf16 [K][H]) may be
  * NULL.  Writes y bf16 [K][H] (round to nearest even of y32) and, if y32 is
- * not NULL, the fp32 result.  dbg may be NULL. */
+ * not NULL, the fp32 result.  dbg may be NULL.
+ *
+ * Two shape regimes of the same computation, picked by K:
+ *  - K <= 16 (verify width): every unique expert is streamed once by
+ *    skinny kernels (three launches);
+ *  - K > 16 (prefill, e.g. the 512-row seed prefill of the mlxfast README,
+ *    "Why this challenge exists"): the T*k slots are grouped by expert into
+ *    tiles of up to 32 tokens and the expert GEMMs run on the matrix cores
+ *    (six launches).  Limits: inter and shared_inter multiples of 64 and at
+ *    most 1024 (MOE_ERR_UNSUPPORTED otherwise).  h enters the down GEMM as a
+ *    pair of fp16 values (hi + lo) of h scaled by a per-token power of two,
+ *    about 22 significant bits. */
 MOE_API int moe_verify_layer(const moe_cfg* cfg, const moe_layer_weights* w, const uint16_t* x, int32_t K,
                      const uint16_t* residual, uint16_t* y, float* y32, void* workspace,
                      size_t workspace_bytes, void* stream, const moe_debug* dbg);
 
+/* moe_verify_layer with the grouped (prefill) kernels at any K <= max_rows,
+ * including K <= 16: the same arguments, outputs and errors, plus the
+ * grouped-regime limits.  For tests and for callers that batch prefill rows
+ * in small groups. */
+MOE_API int moe_verify_layer_grouped(const moe_cfg* cfg, const moe_layer_weights* w, const uint16_t* x,
+                                     int32_t K, const uint16_t* residual, uint16_t* y, float* y32,
+                                     void* workspace, size_t workspace_bytes, void* stream,
+                                     const moe_debug* dbg);
+
 /* n_layers layers (steps 1-9).  layers is a HOST array of n_layers weight
  * structs.  Writes the last layer's output to y (bf16) and y32 (fp32, may be
- * NULL).  dbg may be NULL. */
+ * NULL).  dbg may be NULL.  K picks the regime as in moe_verify_layer. */
 MOE_API int moe_verify_stack(const moe_cfg* cfg, const moe_layer_weights* layers, int32_t n_layers,
                      const uint16_t* x, int32_t K, uint16_t* y, float* y32, void* workspace,
                      size_t workspace_bytes, void* stream, const moe_debug* dbg);
@@ -155,13 +177,17 @@ MOE_API int moe_verify_stack(const moe_cfg* cfg, const moe_layer_weights* layers
  * kernel launched so that a start/stop event pair carries that kernel's own
  * dispatch timestamps.  Synchronises `stream`, then writes the durations in
  * milliseconds to the HOST array kernel_ms[n_layers][3] (router + selection,
- * gate/up + SwiGLU, down + combine). */
+ * gate/up + SwiGLU, down + combine).  Verify width only (K <= 16;
+ * MOE_ERR_UNSUPPORTED above). */
 MOE_API int moe_verify_stack_timed(const moe_cfg* cfg, const moe_layer_weights* layers, int32_t n_layers,
                                    const uint16_t* x, int32_t K, uint16_t* y, float* y32, void* workspace,
                                    size_t workspace_bytes, void* stream, float* kernel_ms);
 
 /* Selection only (steps 2-3) from given fp32 logits [K][E] (device), with
- * the same device code the layer uses.  bias as in moe_layer_weights. */
+ * the same device code the layer uses.  bias as in moe_layer_weights.  For
+ * K > 16 the grouped regime's selection and grouping kernels run, and the
+ * workspace (sized by moe_verify_workspace_bytes) is required; for K <= 16
+ * workspace may be NULL. */
 MOE_API int moe_verify_route(const moe_cfg* cfg, const float* logits, const float* bias, int32_t K,
                      const moe_route_out* out, void* workspace, size_t workspace_bytes, void* stream);
 

@@ -56,8 +56,8 @@ class moe_debug(ctypes.Structure):
                 ("x_in", _c_void_p), ("y32", _c_void_p)]
 
 
-EXPORTS = ["moe_verify_workspace_bytes", "moe_verify_layer", "moe_verify_stack", "moe_verify_stack_timed",
-           "moe_verify_route",
+EXPORTS = ["moe_verify_workspace_bytes", "moe_verify_layer", "moe_verify_layer_grouped", "moe_verify_stack",
+           "moe_verify_stack_timed", "moe_verify_route",
            "moe_verify_dequant_nvfp4", "moe_stack_graph_create", "moe_stack_graph_launch",
            "moe_stack_graph_destroy", "moe_verify_weight_bytes", "moe_verify_last_error",
            "moe_verify_version"]
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.moe_verify_workspace_bytes.argtypes = [cfgp]
     L.moe_verify_layer.restype = ctypes.c_int
     L.moe_verify_layer.argtypes = [cfgp, wp, P, _i32, P, P, P, P, Z, P, ctypes.POINTER(moe_debug)]
+    L.moe_verify_layer_grouped.restype = ctypes.c_int
+    L.moe_verify_layer_grouped.argtypes = [cfgp, wp, P, _i32, P, P, P, P, Z, P, ctypes.POINTER(moe_debug)]
     L.moe_verify_stack.restype = ctypes.c_int
     L.moe_verify_stack.argtypes = [cfgp, wp, _i32, P, _i32, P, P, P, Z, P, ctypes.POINTER(moe_debug)]
     L.moe_verify_stack_timed.restype = ctypes.c_int
@@ -209,6 +211,18 @@ def moe_verify_layer(cfg: moe_cfg, weights: moe_layer_weights, x: torch.Tensor, 
                                   ctypes.byref(debug) if debug is not None else None))
 
 
+def moe_verify_layer_grouped(cfg: moe_cfg, weights: moe_layer_weights, x: torch.Tensor, y: torch.Tensor,
+                             workspace: torch.Tensor, y32: Optional[torch.Tensor] = None,
+                             residual: Optional[torch.Tensor] = None, debug: Optional[moe_debug] = None,
+                             stream=None) -> None:
+    K = x.shape[0]
+    _check(lib().moe_verify_layer_grouped(ctypes.byref(cfg), ctypes.byref(weights), _ptr(x, _BITS16, "x"), K,
+                                          _ptr(residual, _BITS16, "residual"), _ptr(y, _BITS16, "y"),
+                                          _ptr(y32, torch.float32, "y32"), _ptr(workspace, None, "workspace"),
+                                          workspace.numel() * workspace.element_size(), _stream(stream),
+                                          ctypes.byref(debug) if debug is not None else None))
+
+
 def _layer_array(layers: Sequence[moe_layer_weights]):
     arr = (moe_layer_weights * len(layers))(*layers)
     return arr
@@ -239,11 +253,13 @@ def moe_verify_stack_timed(cfg: moe_cfg, layers: Sequence[moe_layer_weights], x:
 
 
 def moe_verify_route(cfg: moe_cfg, logits: torch.Tensor, out: Dict[str, torch.Tensor],
-                     bias: Optional[torch.Tensor] = None, stream=None) -> None:
+                     bias: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> None:
     ro = moe_route_out(*[_ptr(out[k], None, k) for k in ("ids", "w", "n_unique", "uniq", "off", "asg", "inv")])
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().moe_verify_route(ctypes.byref(cfg), _ptr(logits, torch.float32, "logits"),
                                   _ptr(bias, torch.float32, "bias"), logits.shape[0], ctypes.byref(ro),
-                                  None, 0, _stream(stream)))
+                                  _ptr(workspace, None, "workspace"), nbytes, _stream(stream)))
 
 
 def moe_verify_dequant_nvfp4(m: Dict[str, torch.Tensor], out: torch.Tensor, stream=None) -> None:

@@ -44,6 +44,19 @@ int check_inter(int I, int H, const char* name) {
     return MOE_OK;
 }
 
+// Extra limits of the grouped (prefill) kernels.
+int check_grouped(const moe_cfg* c, int T) {
+    if (c->inter % moe::kGRows || c->inter > moe::kGMaxCols)
+        return fail(MOE_ERR_UNSUPPORTED, "inter=%d: the grouped path needs a multiple of %d up to %d", c->inter,
+                    moe::kGRows, moe::kGMaxCols);
+    if (c->shared_inter % moe::kGRows || c->shared_inter > moe::kGMaxCols)
+        return fail(MOE_ERR_UNSUPPORTED, "shared_inter=%d: the grouped path needs a multiple of %d up to %d",
+                    c->shared_inter, moe::kGRows, moe::kGMaxCols);
+    if (!moe::grouped_lds_fits(T, c->n_experts, c->inter, c->shared_inter))
+        return fail(MOE_ERR_UNSUPPORTED, "rows=%d x n_experts=%d exceeds the grouped LDS budget", T, c->n_experts);
+    return MOE_OK;
+}
+
 int check_cfg(const moe_cfg* c) {
     if (!c) return fail(MOE_ERR_INVALID, "cfg is NULL");
     if (c->hidden != 256 && c->hidden != 512 && c->hidden != 1024 && c->hidden != 2048)
@@ -65,11 +78,13 @@ int check_cfg(const moe_cfg* c) {
     if (!std::isfinite(c->routed_scale)) return fail(MOE_ERR_INVALID, "routed_scale not finite");
     if (!(c->rms_eps >= 0.0f) || !std::isfinite(c->rms_eps)) return fail(MOE_ERR_INVALID, "rms_eps invalid");
     if (c->max_rows < 1) return fail(MOE_ERR_INVALID, "max_rows=%d < 1", c->max_rows);
-    if (c->max_rows > moe::kMaxRows)
-        return fail(MOE_ERR_UNSUPPORTED, "max_rows=%d > %d (verify-width path)", c->max_rows, moe::kMaxRows);
-    if (!moe::lds_fits(c->max_rows, c->n_experts, c->hidden))
+    if (c->max_rows > moe::kMaxGroupedRows)
+        return fail(MOE_ERR_UNSUPPORTED, "max_rows=%d > %d", c->max_rows, moe::kMaxGroupedRows);
+    const int skinny_rows = c->max_rows < moe::kMaxRows ? c->max_rows : moe::kMaxRows;
+    if (!moe::lds_fits(skinny_rows, c->n_experts, c->hidden))
         return fail(MOE_ERR_UNSUPPORTED, "max_rows=%d x n_experts=%d x hidden=%d exceeds the LDS budget",
-                    c->max_rows, c->n_experts, c->hidden);
+                    skinny_rows, c->n_experts, c->hidden);
+    if (c->max_rows > moe::kMaxRows) return check_grouped(c, c->max_rows);
     return MOE_OK;
 }
 
@@ -121,6 +136,13 @@ struct Layout {
     float* ssq;
     uint16_t* xbuf;
     float* ybuf;
+    // grouped regime
+    uint16_t* xbuf2;        // second bf16 input buffer (stacked layers alternate)
+    int32_t* tiles;         // int4 [max tiles]
+    float* hmax;            // [R*k][I/64]
+    float* hmax_sh;         // [R][Is/64]
+    float* o;               // [R*k + R][H]
+    int max_tiles;
     size_t bytes;
 };
 
@@ -144,6 +166,12 @@ Layout layout(const moe_cfg* c, void* base) {
     L.ssq = reinterpret_cast<float*>(take(R * (H / moe::kDownRowsPerBlock) * 4));
     L.xbuf = reinterpret_cast<uint16_t*>(take(R * H * 2));
     L.ybuf = reinterpret_cast<float*>(take(R * H * 4));
+    L.xbuf2 = reinterpret_cast<uint16_t*>(take(R * H * 2));
+    L.max_tiles = moe::grouped_max_tiles((int)R, (int)E, (int)k, Is > 0);
+    L.tiles = reinterpret_cast<int32_t*>(take((size_t)L.max_tiles * 16));
+    L.hmax = reinterpret_cast<float*>(take(R * k * ((I + 63) / 64) * 4));
+    L.hmax_sh = reinterpret_cast<float*>(take(R * (Is ? (Is + 63) / 64 : 1) * 4));
+    L.o = reinterpret_cast<float*>(take((R * k + R) * H * 4));
     L.bytes = o;
     return L;
 }
@@ -213,6 +241,67 @@ int enqueue_layer(const moe_cfg* c, const moe_layer_weights* w, const LayerIO& i
     return MOE_OK;
 }
 
+// The grouped (prefill) kernels for one layer; x_next != nullptr also writes
+// the next stacked layer's bf16 RMS-normalised input.
+int enqueue_layer_grouped(const moe_cfg* c, const moe_layer_weights* w, const uint16_t* x, int K,
+                          const uint16_t* residual, float* y32, uint16_t* y, uint16_t* x_next, const Layout& L,
+                          hipStream_t st) {
+    hipError_t e;
+    const bool has_sh = c->shared_inter > 0;
+    const moe::Fp4Mat none{nullptr, nullptr, nullptr};
+    int32_t* n_unique = L.meta + moe::kMetaUnique;
+    int32_t* n_tiles = L.meta + moe::kMetaTiles;
+
+    moe::RouterArgs ra{};
+    ra.x_in = x;
+    ra.wr = w->router_w;
+    ra.logits = L.logits;
+    ra.K = K; ra.H = c->hidden; ra.E = c->n_experts;
+    if ((e = moe::launch_router(ra, st)) != hipSuccess) return hip_fail(e, "router launch");
+
+    moe::SelectArgs sa{};
+    sa.logits = L.logits; sa.bias = w->router_bias;
+    sa.ids = L.ids; sa.w = L.w;
+    sa.K = K; sa.E = c->n_experts; sa.k = c->top_k;
+    sa.score_fn = c->score_fn; sa.norm_topk = c->norm_topk;
+    if ((e = moe::launch_select_rows(sa, st)) != hipSuccess) return hip_fail(e, "row selection launch");
+
+    moe::GroupArgs ka{};
+    ka.ids = L.ids; ka.n_unique = n_unique; ka.uniq = L.uniq; ka.off = L.off; ka.asg = L.asg; ka.inv = L.inv;
+    ka.tiles = L.tiles; ka.n_tiles = n_tiles;
+    ka.T = K; ka.E = c->n_experts; ka.k = c->top_k; ka.has_shared = has_sh;
+    if ((e = moe::launch_group(ka, st)) != hipSuccess) return hip_fail(e, "grouping launch");
+
+    const int max_tiles = moe::grouped_max_tiles(K, c->n_experts, c->top_k, has_sh);
+    moe::GroupedGuArgs ga{};
+    ga.x = x;
+    ga.gate = mat(w->gate); ga.up = mat(w->up);
+    ga.sgate = has_sh ? mat(w->sh_gate) : none;
+    ga.sup = has_sh ? mat(w->sh_up) : none;
+    ga.uniq = L.uniq; ga.off = L.off; ga.asg = L.asg; ga.tiles = L.tiles; ga.n_tiles = n_tiles;
+    ga.h = L.h; ga.h_sh = L.h_sh;
+    ga.T = K; ga.H = c->hidden; ga.I = c->inter; ga.Is = c->shared_inter; ga.k = c->top_k;
+    if ((e = moe::launch_gateup_grouped(ga, L.hmax, L.hmax_sh, max_tiles, st)) != hipSuccess)
+        return hip_fail(e, "grouped gate/up launch");
+
+    moe::GroupedDownArgs da{};
+    da.down = mat(w->down);
+    da.sdown = has_sh ? mat(w->sh_down) : none;
+    da.uniq = L.uniq; da.off = L.off; da.tiles = L.tiles; da.n_tiles = n_tiles;
+    da.h = L.h; da.h_sh = L.h_sh; da.o = L.o;
+    da.T = K; da.H = c->hidden; da.I = c->inter; da.Is = c->shared_inter; da.k = c->top_k;
+    if ((e = moe::launch_down_grouped(da, L.hmax, L.hmax_sh, max_tiles, st)) != hipSuccess)
+        return hip_fail(e, "grouped down launch");
+
+    moe::CombineArgs ca{};
+    ca.o = L.o; ca.w = L.w; ca.inv = L.inv;
+    ca.residual = residual; ca.y32 = y32; ca.y = y; ca.x_next = x_next;
+    ca.eps = c->rms_eps; ca.rs = c->routed_scale;
+    ca.T = K; ca.H = c->hidden; ca.k = c->top_k; ca.has_shared = has_sh;
+    if ((e = moe::launch_combine(ca, st)) != hipSuccess) return hip_fail(e, "combine launch");
+    return MOE_OK;
+}
+
 int copy_debug(const moe_cfg* c, const moe_debug* d, int layer, int K, const Layout& L, const uint16_t* x_in,
                const float* y32, hipStream_t st) {
     if (!d) return MOE_OK;
@@ -263,6 +352,21 @@ int enqueue_stack(const moe_cfg* c, const moe_layer_weights* layers, int n_layer
     const Layout L = layout(c, ws);
     hipError_t e = moe::init_kernels();
     if (e != hipSuccess) return hip_fail(e, "kernel attributes");
+    if (K > moe::kMaxRows) {
+        // grouped regime: each layer's combine writes the next layer's input,
+        // alternating between two buffers so a layer's input stays readable
+        for (int l = 0; l < n_layers; ++l) {
+            const bool last = (l == n_layers - 1);
+            const uint16_t* xin = (l == 0) ? x : ((l & 1) ? L.xbuf : L.xbuf2);
+            uint16_t* xnext = last ? nullptr : ((l & 1) ? L.xbuf2 : L.xbuf);
+            float* yo = last ? (y32 ? y32 : L.ybuf) : L.ybuf;
+            int rc = enqueue_layer_grouped(c, &layers[l], xin, K, nullptr, yo, last ? y : nullptr, xnext, L, st);
+            if (rc) return rc;
+            rc = copy_debug(c, dbg, l, K, L, xin, yo, st);
+            if (rc) return rc;
+        }
+        return MOE_OK;
+    }
     for (int l = 0; l < n_layers; ++l) {
         const bool last = (l == n_layers - 1);
         LayerIO io{};
@@ -318,14 +422,36 @@ int moe_verify_layer(const moe_cfg* cfg, const moe_layer_weights* w, const uint1
     const Layout L = layout(cfg, workspace);
     hipError_t e = moe::init_kernels();
     if (e != hipSuccess) return hip_fail(e, "kernel attributes");
+    float* yo = y32 ? y32 : L.ybuf;
+    if (K > moe::kMaxRows) {
+        if ((rc = enqueue_layer_grouped(cfg, w, x, K, residual, yo, y, nullptr, L, st))) return rc;
+        return copy_debug(cfg, dbg, 0, K, L, x, yo, st);
+    }
     LayerIO io{};
     io.x_in = x;
     io.y_prev = nullptr;
     io.residual = residual;
-    io.y32 = y32 ? y32 : L.ybuf;
+    io.y32 = yo;
     io.y = y;
     if ((rc = enqueue_layer(cfg, w, io, K, L, st))) return rc;
     return copy_debug(cfg, dbg, 0, K, L, x, io.y32, st);
+}
+
+int moe_verify_layer_grouped(const moe_cfg* cfg, const moe_layer_weights* w, const uint16_t* x, int32_t K,
+                             const uint16_t* residual, uint16_t* y, float* y32, void* workspace,
+                             size_t workspace_bytes, void* stream, const moe_debug* dbg) {
+    int rc;
+    if ((rc = check_common(cfg, K, workspace, workspace_bytes))) return rc;
+    if ((rc = check_grouped(cfg, K))) return rc;
+    if ((rc = check_weights(cfg, w, 0))) return rc;
+    if ((rc = check_io(x, y, y32, residual))) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Layout L = layout(cfg, workspace);
+    hipError_t e = moe::init_kernels();
+    if (e != hipSuccess) return hip_fail(e, "kernel attributes");
+    float* yo = y32 ? y32 : L.ybuf;
+    if ((rc = enqueue_layer_grouped(cfg, w, x, K, residual, yo, y, nullptr, L, st))) return rc;
+    return copy_debug(cfg, dbg, 0, K, L, x, yo, st);
 }
 
 int moe_verify_stack(const moe_cfg* cfg, const moe_layer_weights* layers, int32_t n_layers, const uint16_t* x,
@@ -342,8 +468,6 @@ int moe_verify_stack(const moe_cfg* cfg, const moe_layer_weights* layers, int32_
 
 int moe_verify_route(const moe_cfg* cfg, const float* logits, const float* bias, int32_t K,
                      const moe_route_out* out, void* workspace, size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     int rc;
     if ((rc = check_cfg(cfg))) return rc;
     if (K < 1 || K > cfg->max_rows) return fail(MOE_ERR_INVALID, "K=%d outside [1, max_rows=%d]", K, cfg->max_rows);
@@ -352,6 +476,10 @@ int moe_verify_route(const moe_cfg* cfg, const float* logits, const float* bias,
     if (cfg->score_fn == MOE_SCORE_SOFTMAX && bias) return fail(MOE_ERR_INVALID, "bias given with softmax scoring");
     if (!out || !out->ids || !out->w || !out->n_unique || !out->uniq || !out->off || !out->asg || !out->inv)
         return fail(MOE_ERR_INVALID, "route outputs must all be non-NULL");
+    if (K > moe::kMaxRows) {
+        if ((rc = check_common(cfg, K, workspace, workspace_bytes))) return rc;
+        if ((rc = check_grouped(cfg, K))) return rc;
+    }
     hipError_t e = moe::init_kernels();
     if (e != hipSuccess) return hip_fail(e, "kernel attributes");
     moe::SelectArgs ra{};
@@ -361,8 +489,22 @@ int moe_verify_route(const moe_cfg* cfg, const float* logits, const float* bias,
     ra.uniq = out->uniq; ra.off = out->off; ra.asg = out->asg; ra.inv = out->inv;
     ra.K = K; ra.E = cfg->n_experts; ra.k = cfg->top_k;
     ra.score_fn = cfg->score_fn; ra.norm_topk = cfg->norm_topk;
-    e = moe::launch_select(ra, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "select launch");
+    if (K <= moe::kMaxRows) {
+        e = moe::launch_select(ra, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_fail(e, "select launch");
+        return MOE_OK;
+    }
+    // grouped regime: per-row selection, then the grouping workgroup (its
+    // tile list goes to the workspace)
+    const Layout L = layout(cfg, workspace);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((e = moe::launch_select_rows(ra, st)) != hipSuccess) return hip_fail(e, "row selection launch");
+    moe::GroupArgs ka{};
+    ka.ids = out->ids; ka.n_unique = out->n_unique; ka.uniq = out->uniq; ka.off = out->off;
+    ka.asg = out->asg; ka.inv = out->inv;
+    ka.tiles = L.tiles; ka.n_tiles = L.meta + moe::kMetaTiles;
+    ka.T = K; ka.E = cfg->n_experts; ka.k = cfg->top_k; ka.has_shared = cfg->shared_inter > 0;
+    if ((e = moe::launch_group(ka, st)) != hipSuccess) return hip_fail(e, "grouping launch");
     return MOE_OK;
 }
 
@@ -386,6 +528,8 @@ int moe_verify_stack_timed(const moe_cfg* cfg, const moe_layer_weights* layers, 
     if ((rc = check_common(cfg, K, workspace, workspace_bytes))) return rc;
     if (!layers || n_layers < 1) return fail(MOE_ERR_INVALID, "need n_layers >= 1 and a layer array");
     if (!kernel_ms) return fail(MOE_ERR_INVALID, "kernel_ms is NULL");
+    if (K > moe::kMaxRows)
+        return fail(MOE_ERR_UNSUPPORTED, "per-kernel timing covers the verify-width kernels (K <= %d)", moe::kMaxRows);
     for (int l = 0; l < n_layers; ++l)
         if ((rc = check_weights(cfg, &layers[l], l))) return rc;
     if ((rc = check_io(x, y, y32, nullptr))) return rc;

@@ -1,0 +1,581 @@
+// gfx950 (CDNA4) kernels of the NVFP4 MoE layer in the grouped (prefill)
+// regime: more than 16 rows, so each routed expert serves many tokens and the
+// expert GEMMs are dense contractions for the matrix cores (the 512-row seed
+// prefill of the mlxfast README, "Why this challenge exists"; PR #844
+// section 8 notes the stock grouped GEMM needs several tokens per expert).
+// Per layer, after the router GEMV (k_router over 16-row chunks):
+//   k_select_rows   top-k and mixture weights, one wave per row (the same
+//                   selection code as the verify-width path);
+//   k_group         one workgroup: the canonical CSR of the T*k slots by
+//                   expert (unique experts ascending, slots ascending) from
+//                   per-expert row bitmaps, and a tile list of up to 32
+//                   consecutive slots of one expert (plus the shared
+//                   expert's 32-token tiles);
+//   k_gateup_grouped  (tile, 64 intermediate rows) work items on the matrix
+//                   cores: FP4 codes decoded in registers to fp16 times their
+//                   E4M3 scale (exact), x columns staged in LDS as fp16,
+//                   v_mfma_f32_16x16x32_f16 with fp32 accumulation, SwiGLU
+//                   epilogue writing fp32 h and each token's max |h| per slab;
+//   k_down_grouped  (tile, 64 output rows) work items: h staged in LDS as a
+//                   pair of fp16 values hi + lo of h * 2^-sigma, sigma a
+//                   power of two per token chosen from its max |h| (so the
+//                   pair keeps about 22 significant bits and cannot
+//                   overflow), two MFMAs per k step into one fp32 accumulator,
+//                   2^sigma and the tensor scale applied to the sum;
+//   k_combine       one workgroup per row: y = rs * sum_j w_j o_j + shared
+//                   (+ residual) in rank order (PR #844 section 5 expression
+//                   order), y32 / bf16 y, and for stacked layers the next
+//                   layer's bf16 RMS-normalised input.
+#include <hip/hip_ext.h>
+
+#include "moe_device.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// k_select_rows: kWaves rows per workgroup
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kBlock) void k_select_rows(SelectArgs a) {
+    __shared__ SelectSmem sm;
+    extern __shared__ __align__(16) float lg[];  // [kWaves][E]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r0 = blockIdx.x * kWaves;
+    const int nr = min(kWaves, a.K - r0);
+    stage_floats(lg, a.logits + (size_t)r0 * a.E, nr * a.E, tid, kBlock);
+    __syncthreads();
+    if (wave < nr) {
+        wave_topk_rt(a, lg + wave * a.E, wave, sm);
+        // each lane reads back the entry it wrote itself
+        if (lane < a.k) {
+            a.ids[(size_t)(r0 + wave) * a.k + lane] = sm.sel[wave * a.k + lane];
+            a.w[(size_t)(r0 + wave) * a.k + lane] = sm.w[wave * a.k + lane];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_group: CSR + tile list (one workgroup of kGGroupThreads)
+//
+// A row never selects an expert twice, so expert e's slots are one per row
+// that picked it, in row order.  rm[e][w] is the bitmap of those rows:
+//   count(e) = popcount(rm[e][*]),
+//   rank of slot (r, j) inside its expert = popcount of rm[e] below bit r.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kGGroupThreads) void k_group(GroupArgs a) {
+    extern __shared__ uint32_t rm[];  // [E][W]
+    __shared__ int s_cstart[kMaxExperts];
+    __shared__ int s_wsum[kGGroupThreads / 64][3];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int T = a.T, E = a.E, k = a.k, n = T * k, W = (T + 31) >> 5;
+    for (int i = tid; i < E * W; i += kGGroupThreads) rm[i] = 0u;
+    __syncthreads();
+    for (int s = tid; s < n; s += kGGroupThreads) {
+        const int e = a.ids[s], r = s / k;
+        atomicOr(&rm[e * W + (r >> 5)], 1u << (r & 31));
+    }
+    __syncthreads();
+    // thread e (E <= kGGroupThreads): slot count, used flag, tile count
+    int c = 0;
+    if (tid < E)
+        for (int w = 0; w < W; ++w) c += __builtin_popcount(rm[tid * W + w]);
+    const int f = c > 0, nt = (c + kGChunk - 1) / kGChunk;
+    const int ci = wave_incl_scan(c), fi = wave_incl_scan(f), ti = wave_incl_scan(nt);
+    if (lane == 63) {
+        s_wsum[wave][0] = ci;
+        s_wsum[wave][1] = fi;
+        s_wsum[wave][2] = ti;
+    }
+    __syncthreads();
+    int cb = 0, fb = 0, tb = 0;
+    for (int w = 0; w < wave; ++w) {
+        cb += s_wsum[w][0];
+        fb += s_wsum[w][1];
+        tb += s_wsum[w][2];
+    }
+    const int cs = cb + ci - c, fs = fb + fi - f, tsn = tb + ti - nt;
+    int4* tiles = reinterpret_cast<int4*>(a.tiles);
+    if (tid < E) {
+        s_cstart[tid] = cs;
+        if (f) {
+            a.uniq[fs] = tid;
+            a.off[fs] = cs;
+            for (int t = 0; t < nt; ++t) tiles[tsn + t] = make_int4(tid, cs + t * kGChunk, min(kGChunk, c - t * kGChunk), 0);
+        }
+    }
+    if (tid == kGGroupThreads - 1) {
+        int U = 0, NT = 0;
+        for (int w = 0; w < kGGroupThreads / 64; ++w) {
+            U += s_wsum[w][1];
+            NT += s_wsum[w][2];
+        }
+        *a.n_unique = U;
+        a.off[U] = n;
+        int nsh = 0;
+        if (a.has_shared) {
+            nsh = (T + kGChunk - 1) / kGChunk;
+            for (int t = 0; t < nsh; ++t) tiles[NT + t] = make_int4(-1, t * kGChunk, min(kGChunk, T - t * kGChunk), 0);
+        }
+        *a.n_tiles = NT + nsh;
+    }
+    __syncthreads();
+    for (int s = tid; s < n; s += kGGroupThreads) {
+        const int e = a.ids[s], r = s / k;
+        const uint32_t* m = rm + e * W;
+        int rank = __builtin_popcount(m[r >> 5] & ((1u << (r & 31)) - 1u));
+        for (int w = 0; w < (r >> 5); ++w) rank += __builtin_popcount(m[w]);
+        const int pos = s_cstart[e] + rank;
+        a.asg[pos] = s;
+        a.inv[s] = pos;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// grouped gate/up
+//
+// Work item: (tile, 64-row slab of the intermediate dimension).  Wave w
+// computes rows n0 = slab*64 + 16w .. +15 of gate and of up for the tile's
+// tokens (up to 32: two 16-column MFMA tiles).  Lane (i = lane % 16,
+// kb = lane / 16) owns columns [sb*256 + kb*64, +64) of weight row n0 + i in
+// superblock sb (the layout of the verify-width tiles); its weights stream
+// through the superblocks with two superblocks in flight.  The tokens' x
+// columns of the current superblock sit in LDS as fp16 (double buffered),
+// rows padded to 528 bytes (16 bytes times an odd number) so the 16 rows an
+// MFMA B read touches fall in distinct bank groups.
+// ---------------------------------------------------------------------------
+
+constexpr int kGXStride = kSbCols + 8;  // halfs per staged token row
+
+__device__ __forceinline__ void gg_mfma_sb(const GuSb& r, const _Float16* xb, int ntt, f32x4_t* accg,
+                                           f32x4_t* accu) {
+    const int lane = threadIdx.x & 63, j = lane & 15, kb = lane >> 4;
+    const _Float16 g0 = e4m3_to_f16<0>(r.gs), g1 = e4m3_to_f16<1>(r.gs);
+    const _Float16 g2 = e4m3_to_f16<2>(r.gs), g3 = e4m3_to_f16<3>(r.gs);
+    const _Float16 u0 = e4m3_to_f16<0>(r.us), u1 = e4m3_to_f16<1>(r.us);
+    const _Float16 u2 = e4m3_to_f16<2>(r.us), u3 = e4m3_to_f16<3>(r.us);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const _Float16 gsc = (s < 2) ? g0 : (s < 4) ? g1 : (s < 6) ? g2 : g3;
+        const _Float16 usc = (s < 2) ? u0 : (s < 4) ? u1 : (s < 6) ? u2 : u3;
+        const f16x8_t ag = decode8_f16(pick_word(r.g0, r.g1, s), gsc);
+        const f16x8_t au = decode8_f16(pick_word(r.u0, r.u1, s), usc);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            if (tt < ntt) {
+                const f16x8_t b = *reinterpret_cast<const f16x8_t*>(xb + (tt * 16 + j) * kGXStride + kb * 64 + 8 * s);
+                accg[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ag, b, accg[tt], 0, 0, 0);
+                accu[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(au, b, accu[tt], 0, 0, 0);
+            }
+        }
+    }
+}
+
+template <int NSB>
+__global__ __launch_bounds__(kBlock) void k_gateup_grouped(GroupedGuArgs a, float* hmax, float* hmax_sh) {
+    __shared__ __align__(16) _Float16 xb[2][kGChunk * kGXStride];
+    __shared__ int s_tok[kGChunk];
+    __shared__ float s_max[kWaves][kGChunk];
+    constexpr int H = NSB * kSbCols;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j = lane & 15, q = lane >> 4;
+    // matrix pointers read once; per item the choice selects values
+    const uint8_t *const gq_r = a.gate.q, *const gs_r = a.gate.s, *const uq_r = a.up.q, *const us_r = a.up.s;
+    const uint8_t *const gq_s = a.sgate.q, *const gs_s = a.sgate.s, *const uq_s = a.sup.q, *const us_s = a.sup.s;
+    const float *const gts_r = a.gate.ts, *const uts_r = a.up.ts, *const gts_s = a.sgate.ts, *const uts_s = a.sup.ts;
+    const int I = a.I, Is = a.Is, kk = a.k;
+    const int nI = I / kGRows, nIs = max(Is / kGRows, 1);
+    const int n_tiles = *a.n_tiles;
+    const int n_sh = gq_s ? (a.T + kGChunk - 1) / kGChunk : 0;
+    const int n_rt = n_tiles - n_sh;
+    const int items = n_rt * nI + n_sh * nIs;
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const bool routed = it < n_rt * nI;
+        const int ti = routed ? it / nI : n_rt + (it - n_rt * nI) / nIs;
+        const int slab = routed ? it % nI : (it - n_rt * nI) % nIs;
+        const int4 tl = reinterpret_cast<const int4*>(a.tiles)[ti];
+        const int e = routed ? tl.x : 0, p0 = tl.y, cnt = tl.z;
+        const int rows = routed ? I : Is;
+        const size_t eq = (size_t)e * rows * (H / 2), es = (size_t)e * rows * (H / 16);
+        const uint8_t* gq = (routed ? gq_r : gq_s) + eq;
+        const uint8_t* gs = (routed ? gs_r : gs_s) + es;
+        const uint8_t* uq = (routed ? uq_r : uq_s) + eq;
+        const uint8_t* us = (routed ? us_r : us_s) + es;
+        const float gts = (routed ? gts_r : gts_s)[e], uts = (routed ? uts_r : uts_s)[e];
+        const int n0 = slab * kGRows + wave * 16;
+
+        // weights of the first two superblocks, then the tile's token rows
+        GuSb w[3];
+        w[0] = gu_load_sb(gq, gs, uq, us, H, n0, 0, true);
+        if (NSB > 1) w[1] = gu_load_sb(gq, gs, uq, us, H, n0, 1, true);
+        if (tid < kGChunk) s_tok[tid] = routed ? a.asg[p0 + min(tid, cnt - 1)] / kk : p0 + min(tid, cnt - 1);
+        __syncthreads();
+
+        // x columns of superblock sb: 32 tokens x 32 pieces of 16 bytes, four
+        // pieces per thread; loads at clamped (valid) rows, zeros stored for
+        // tokens past the tile
+        uint4 xv[4];
+        auto load_x = [&](int sb) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int f = t * kBlock + tid, m = f >> 5, c8 = f & 31;
+                xv[t] = *reinterpret_cast<const uint4*>(a.x + (size_t)s_tok[m] * H + sb * kSbCols + c8 * 8);
+            }
+        };
+        auto store_x = [&](int buf) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int f = t * kBlock + tid, m = f >> 5, c8 = f & 31;
+                uint4 o = make_uint4(0, 0, 0, 0);
+                if (m < cnt) {
+                    o.x = bf16pair_to_f16pair(xv[t].x);
+                    o.y = bf16pair_to_f16pair(xv[t].y);
+                    o.z = bf16pair_to_f16pair(xv[t].z);
+                    o.w = bf16pair_to_f16pair(xv[t].w);
+                }
+                *reinterpret_cast<uint4*>(&xb[buf][m * kGXStride + c8 * 8]) = o;
+            }
+        };
+        load_x(0);
+        store_x(0);
+        __syncthreads();
+
+        const int ntt = cnt > 16 ? 2 : 1;
+        f32x4_t accg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4_t accu[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) {
+            if (sb + 1 < NSB) load_x(sb + 1);
+            if (sb + 2 < NSB) w[(sb + 2) % 3] = gu_load_sb(gq, gs, uq, us, H, n0, sb + 2, true);
+            gg_mfma_sb(w[sb % 3], xb[sb & 1], ntt, accg, accu);
+            if (sb + 1 < NSB) store_x((sb + 1) & 1);
+            __syncthreads();
+        }
+
+        // SwiGLU epilogue: lane (j, q) holds rows n0 + 4q .. +3 of token j
+        float* hbase = routed ? a.h : a.h_sh;
+        const int hstride = routed ? I : Is;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int m = tt * 16 + j;
+            float4 hv = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (tt < ntt) {
+                float gv, uv;
+                gv = accg[tt][0] * gts; uv = accu[tt][0] * uts; hv.x = gv / (1.0f + expf(-gv)) * uv;
+                gv = accg[tt][1] * gts; uv = accu[tt][1] * uts; hv.y = gv / (1.0f + expf(-gv)) * uv;
+                gv = accg[tt][2] * gts; uv = accu[tt][2] * uts; hv.z = gv / (1.0f + expf(-gv)) * uv;
+                gv = accg[tt][3] * gts; uv = accu[tt][3] * uts; hv.w = gv / (1.0f + expf(-gv)) * uv;
+                if (m < cnt) *reinterpret_cast<float4*>(hbase + (size_t)(p0 + m) * hstride + n0 + 4 * q) = hv;
+            }
+            // max |h| of token m over this wave's 16 rows (lanes j, j+16, j+32, j+48)
+            float mx = fmaxf(fmaxf(fabsf(hv.x), fabsf(hv.y)), fmaxf(fabsf(hv.z), fabsf(hv.w)));
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            if (q == 0) s_max[wave][m] = mx;
+        }
+        __syncthreads();
+        if (tid < cnt) {
+            const float mx = fmaxf(fmaxf(s_max[0][tid], s_max[1][tid]), fmaxf(s_max[2][tid], s_max[3][tid]));
+            if (routed) hmax[(size_t)(p0 + tid) * nI + slab] = mx;
+            else hmax_sh[(size_t)(p0 + tid) * nIs + slab] = mx;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// grouped down
+//
+// Work item: (tile, 64-row slab of the output dimension).  Wave w computes
+// output rows n0 = slab*64 + 16w .. +15 for the tile's tokens.  Lane (i, kb)
+// holds the codes of row n0 + i at columns [sb*256 + kb*64, +64) of every
+// superblock of the intermediate dimension (at most kGMaxCols / 256).  The
+// tile's h rows are staged in LDS as hi = fp16(h * 2^-sigma) and
+// lo = fp16(h * 2^-sigma - hi), sigma per token such that its max |h| maps
+// into [2^14, 2^15); rows padded to (cols + 8) halfs.
+// ---------------------------------------------------------------------------
+
+constexpr int kGMaxSb = kGMaxCols / kSbCols;
+
+__global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedDownArgs a, const float* hmax, const float* hmax_sh) {
+    extern __shared__ __align__(16) _Float16 hb[];  // hi [32][S], then lo [32][S]
+    __shared__ int s_sig[kGChunk];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int i = lane & 15, kb = lane >> 4, j = lane & 15, q = lane >> 4;
+    const uint8_t *const dq_r = a.down.q, *const ds_r = a.down.s, *const dq_s = a.sdown.q, *const ds_s = a.sdown.s;
+    const float *const dts_r = a.down.ts, *const dts_s = a.sdown.ts;
+    const int H = a.H, I = a.I, Is = a.Is, T = a.T, kk = a.k;
+    const int S = max(I, Is) + 8;   // staged row stride in halfs
+    _Float16* hi = hb;
+    _Float16* lo = hb + kGChunk * S;
+    const int nH = H / kGRows;
+    const int n_tiles = *a.n_tiles;
+    const int n_sh = dq_s ? (T + kGChunk - 1) / kGChunk : 0;
+    const int n_rt = n_tiles - n_sh;
+    const int items = n_tiles * nH;
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const int ti = it / nH, slab = it % nH;
+        const bool routed = ti < n_rt;
+        const int4 tl = reinterpret_cast<const int4*>(a.tiles)[ti];
+        const int e = routed ? tl.x : 0, p0 = tl.y, cnt = tl.z;
+        const int cols = routed ? I : Is;
+        const int nsb = (cols + kSbCols - 1) / kSbCols;
+        const int nslab = cols / kGRows;
+        const uint8_t* mq = (routed ? dq_r : dq_s) + (size_t)e * H * (cols / 2);
+        const uint8_t* ms = (routed ? ds_r : ds_s) + (size_t)e * H * (cols / 16);
+        const float ts = (routed ? dts_r : dts_s)[e];
+        const int n0 = slab * kGRows + wave * 16;
+
+        // this lane's codes and scales of every superblock (64-column blocks
+        // past cols are zero)
+        uint4 c0[kGMaxSb], c1[kGMaxSb];
+        uint32_t sc[kGMaxSb];
+#pragma unroll
+        for (int sb = 0; sb < kGMaxSb; ++sb) {
+            c0[sb] = c1[sb] = make_uint4(0, 0, 0, 0);
+            sc[sb] = 0;
+            const int col = sb * kSbCols + kb * 64;
+            if (sb < nsb && col < cols) {
+                const size_t row = (size_t)(n0 + i);
+                const uint8_t* p = mq + row * (cols / 2) + col / 2;
+                c0[sb] = *reinterpret_cast<const uint4*>(p);
+                c1[sb] = *reinterpret_cast<const uint4*>(p + 16);
+                sc[sb] = *reinterpret_cast<const uint32_t*>(ms + row * (cols / 16) + col / 16);
+            }
+        }
+        // per-token scale exponent from the gate/up kernel's max |h| per slab
+        if (tid < kGChunk) {
+            float mx = 0.0f;
+            if (tid < cnt) {
+                const float* hm = routed ? hmax + (size_t)(p0 + tid) * nslab : hmax_sh + (size_t)(p0 + tid) * nslab;
+                for (int t = 0; t < nslab; ++t) mx = fmaxf(mx, hm[t]);
+            }
+            s_sig[tid] = (mx > 0.0f) ? ilogbf(mx) - 14 : 0;
+        }
+        __syncthreads();
+        // stage: one superblock (32 rows x 256 columns = 2048 float4) per pass
+        const float* hrow0 = routed ? a.h + (size_t)p0 * I : a.h_sh + (size_t)p0 * Is;
+        for (int sb = 0; sb < nsb; ++sb) {
+            float4 v[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int f = t * kBlock + tid, m = f >> 6, c4 = f & 63;
+                const int col = sb * kSbCols + c4 * 4;
+                v[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (col < cols) v[t] = *reinterpret_cast<const float4*>(hrow0 + (size_t)min(m, cnt - 1) * cols + col);
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int f = t * kBlock + tid, m = f >> 6, c4 = f & 63;
+                const int col = sb * kSbCols + c4 * 4;
+                if (col < cols) {
+                    const int sg = -s_sig[m];
+                    const bool live = m < cnt;
+                    const float x0 = live ? ldexpf(v[t].x, sg) : 0.f, x1 = live ? ldexpf(v[t].y, sg) : 0.f;
+                    const float x2 = live ? ldexpf(v[t].z, sg) : 0.f, x3 = live ? ldexpf(v[t].w, sg) : 0.f;
+                    const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1, h2 = (_Float16)x2, h3 = (_Float16)x3;
+                    f16x2_t a01 = {h0, h1}, a23 = {h2, h3};
+                    f16x2_t b01 = {(_Float16)(x0 - (float)h0), (_Float16)(x1 - (float)h1)};
+                    f16x2_t b23 = {(_Float16)(x2 - (float)h2), (_Float16)(x3 - (float)h3)};
+                    uint2 ph, pl;
+                    ph.x = __builtin_bit_cast(uint32_t, a01); ph.y = __builtin_bit_cast(uint32_t, a23);
+                    pl.x = __builtin_bit_cast(uint32_t, b01); pl.y = __builtin_bit_cast(uint32_t, b23);
+                    *reinterpret_cast<uint2*>(hi + m * S + col) = ph;
+                    *reinterpret_cast<uint2*>(lo + m * S + col) = pl;
+                }
+            }
+        }
+        __syncthreads();
+
+        const int ntt = cnt > 16 ? 2 : 1;
+        f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        const f16x8_t zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int sb = 0; sb < kGMaxSb; ++sb) {
+            if (sb < nsb) {
+                const int colb = sb * kSbCols + kb * 64;
+                const bool live = colb < cols;
+                const _Float16 s0 = e4m3_to_f16<0>(sc[sb]), s1 = e4m3_to_f16<1>(sc[sb]);
+                const _Float16 s2 = e4m3_to_f16<2>(sc[sb]), s3 = e4m3_to_f16<3>(sc[sb]);
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const _Float16 ssc = (s < 2) ? s0 : (s < 4) ? s1 : (s < 6) ? s2 : s3;
+                    const f16x8_t aw = decode8_f16(pick_word(c0[sb], c1[sb], s), ssc);
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) {
+                        if (tt < ntt) {
+                            const int m = tt * 16 + j;
+                            const f16x8_t bh = live ? *reinterpret_cast<const f16x8_t*>(hi + m * S + colb + 8 * s) : zero8;
+                            const f16x8_t bl = live ? *reinterpret_cast<const f16x8_t*>(lo + m * S + colb + 8 * s) : zero8;
+                            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, bh, acc[tt], 0, 0, 0);
+                            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, bl, acc[tt], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+        }
+        // lane (j, q) holds output rows n0 + 4q .. +3 of token j
+        float* obase = a.o + (size_t)(routed ? p0 : T * kk + p0) * H;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int m = tt * 16 + j;
+            if (tt < ntt && m < cnt) {
+                const int sg = s_sig[m];
+                float4 ov;
+                ov.x = ldexpf(acc[tt][0], sg) * ts;
+                ov.y = ldexpf(acc[tt][1], sg) * ts;
+                ov.z = ldexpf(acc[tt][2], sg) * ts;
+                ov.w = ldexpf(acc[tt][3], sg) * ts;
+                *reinterpret_cast<float4*>(obase + (size_t)m * H + n0 + 4 * q) = ov;
+            }
+        }
+        __syncthreads();  // staged rows and s_sig are replaced by the next item
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_combine: one workgroup per row
+// ---------------------------------------------------------------------------
+
+constexpr int kCombineMaxCols = 2048 / kBlock;  // columns per thread at the largest hidden size
+constexpr int kCombineBatch = 4;                // slots whose rows are loaded together
+
+__global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a) {
+    __shared__ float s_w[kMaxTopK];
+    __shared__ int s_o[kMaxTopK];
+    __shared__ float s_ss[kWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = blockIdx.x, H = a.H, k = a.k;
+    const int ncol = H / kBlock;
+    if (tid < k) {
+        s_w[tid] = a.w[(size_t)r * k + tid];
+        s_o[tid] = a.inv[(size_t)r * k + tid];
+    }
+    __syncthreads();
+    // y = rs * sum_j w_j o_j (j in rank order) + shared (+ residual)
+    float acc[kCombineMaxCols];
+#pragma unroll
+    for (int t = 0; t < kCombineMaxCols; ++t) acc[t] = 0.0f;
+    for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
+        float ov[kCombineBatch][kCombineMaxCols];
+#pragma unroll
+        for (int b = 0; b < kCombineBatch; ++b) {
+            const int jj = min(j0 + b, k - 1);
+            const float* orow = a.o + (size_t)s_o[jj] * H;
+#pragma unroll
+            for (int t = 0; t < kCombineMaxCols; ++t) ov[b][t] = (t < ncol) ? orow[t * kBlock + tid] : 0.0f;
+        }
+#pragma unroll
+        for (int b = 0; b < kCombineBatch; ++b) {
+            if (j0 + b < k) {
+                const float wv = s_w[j0 + b];
+#pragma unroll
+                for (int t = 0; t < kCombineMaxCols; ++t) acc[t] = fmaf(wv, ov[b][t], acc[t]);
+            }
+        }
+    }
+    float yv[kCombineMaxCols];
+    float ss = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kCombineMaxCols; ++t) {
+        yv[t] = 0.0f;
+        if (t < ncol) {
+            const int c = t * kBlock + tid;
+            float y = a.rs * acc[t];
+            if (a.has_shared) y += a.o[((size_t)a.T * k + r) * H + c];
+            if (a.residual) y += bf16_to_f32(a.residual[(size_t)r * H + c]);
+            a.y32[(size_t)r * H + c] = y;
+            if (a.y) a.y[(size_t)r * H + c] = f32_to_bf16_rne(y);
+            yv[t] = y;
+            ss = fmaf(y, y, ss);
+        }
+    }
+    if (!a.x_next) return;
+    // the next layer's input: bf16(y / sqrt(mean(y^2) + eps)), sums in a fixed order
+    ss = wave_sum(ss);
+    if (lane == 0) s_ss[wave] = ss;
+    __syncthreads();
+    const float tot = (s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3]);
+    const float sc = 1.0f / sqrtf(tot / (float)H + a.eps);
+#pragma unroll
+    for (int t = 0; t < kCombineMaxCols; ++t)
+        if (t < ncol) a.x_next[(size_t)r * H + t * kBlock + tid] = f32_to_bf16_rne(yv[t] * sc);
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+namespace {
+
+template <typename Kern, typename Args>
+hipError_t launch_plain(Kern k, dim3 grid, dim3 block, size_t smem, hipStream_t st, const Args& a) {
+    hipLaunchKernelGGL(k, grid, block, smem, st, a);
+    return hipGetLastError();
+}
+
+size_t group_lds(int T, int E) { return (size_t)E * ((T + 31) / 32) * 4; }
+size_t down_lds(int I, int Is) { return (size_t)2 * kGChunk * ((I > Is ? I : Is) + 8) * 2; }
+
+// largest dynamic LDS each kernel is launched with (static LDS comes on top)
+constexpr int kGroupMaxLds = kMaxExperts * (kMaxGroupedRows / 32) * 4;
+constexpr int kGDownMaxLds = 2 * kGChunk * (kGMaxCols + 8) * 2;
+
+}  // namespace
+
+int grouped_max_tiles(int T, int E, int k, bool has_shared) {
+    const int n = T * k;
+    return (n < E ? n : E) + (n + kGChunk - 1) / kGChunk + (has_shared ? (T + kGChunk - 1) / kGChunk : 0);
+}
+
+bool grouped_lds_fits(int T, int E, int I, int Is) {
+    return group_lds(T, E) <= (size_t)kGroupMaxLds && down_lds(I, Is) <= (size_t)kGDownMaxLds &&
+           (size_t)kWaves * E * 4 <= (size_t)kMaxDynLds;
+}
+
+hipError_t init_grouped_kernels() {
+    hipError_t e;
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_group),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, kGroupMaxLds)) != hipSuccess)
+        return e;
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(k_down_grouped),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, kGDownMaxLds);
+}
+
+hipError_t launch_select_rows(const SelectArgs& a, hipStream_t st) {
+    const int grid = (a.K + kWaves - 1) / kWaves;
+    return launch_plain(k_select_rows, dim3(grid), dim3(kBlock), (size_t)kWaves * a.E * 4, st, a);
+}
+
+hipError_t launch_group(const GroupArgs& a, hipStream_t st) {
+    return launch_plain(k_group, dim3(1), dim3(kGGroupThreads), group_lds(a.T, a.E), st, a);
+}
+
+hipError_t launch_gateup_grouped(const GroupedGuArgs& a, float* hmax, float* hmax_sh, int max_tiles,
+                                 hipStream_t st) {
+    const int per = (a.I > a.Is ? a.I : a.Is) / kGRows;
+    long long items = (long long)max_tiles * per;
+    const int grid = (int)(items < kGMaxGrid ? items : kGMaxGrid);
+    const dim3 g(grid), b(kBlock);
+    switch (a.H) {
+        case 256: hipLaunchKernelGGL(k_gateup_grouped<1>, g, b, 0, st, a, hmax, hmax_sh); break;
+        case 512: hipLaunchKernelGGL(k_gateup_grouped<2>, g, b, 0, st, a, hmax, hmax_sh); break;
+        case 1024: hipLaunchKernelGGL(k_gateup_grouped<4>, g, b, 0, st, a, hmax, hmax_sh); break;
+        case 2048: hipLaunchKernelGGL(k_gateup_grouped<8>, g, b, 0, st, a, hmax, hmax_sh); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_down_grouped(const GroupedDownArgs& a, const float* hmax, const float* hmax_sh, int max_tiles,
+                               hipStream_t st) {
+    long long items = (long long)max_tiles * (a.H / kGRows);
+    const int grid = (int)(items < kGMaxGrid ? items : kGMaxGrid);
+    hipLaunchKernelGGL(k_down_grouped, dim3(grid), dim3(kBlock), down_lds(a.I, a.Is), st, a, hmax, hmax_sh);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
+    return launch_plain(k_combine, dim3(a.T), dim3(kBlock), 0, st, a);
+}
+
+}  // namespace moe

@@ -19,6 +19,15 @@ constexpr int kDownThreads = 512;  // 8 wave64 per down workgroup
 constexpr int kDownHLdsBytes = 64 * 1024;  // h rows staged in LDS per chunk
 constexpr int kGateUpMaxGrid = 1024;       // routed gate/up workgroups loop over work items
 constexpr int kMetaUnique = 0;             // workspace word holding the unique-expert count
+constexpr int kMetaTiles = 1;              // workspace word holding the grouped tile count
+
+// Limits of the grouped (prefill) regime, used for K > kMaxRows rows.
+constexpr int kMaxGroupedRows = 1024;      // T
+constexpr int kGChunk = 32;                // tokens per grouped tile
+constexpr int kGRows = 64;                 // weight rows per grouped workgroup (4 waves x 16)
+constexpr int kGMaxCols = 1024;            // largest intermediate size the grouped down kernel stages
+constexpr int kGGroupThreads = 1024;       // the grouping workgroup
+constexpr int kGMaxGrid = 4096;            // grouped GEMM workgroups loop over work items beyond this
 
 struct Fp4Mat {
     const uint8_t* q;
@@ -82,6 +91,64 @@ struct DownArgs {
     float rs;
 };
 
+// --- grouped (prefill) regime ----------------------------------------------
+// Tile list: int2 {u, p0}.  Routed tiles first (u = index into uniq, p0 = the
+// first asg position of up to kGChunk consecutive slots of that expert), then
+// the shared expert's tiles (u = -1, p0 = first token).  tiles[kMetaTiles]
+// of the workspace meta holds the total count.
+
+struct GroupArgs {
+    const int32_t* ids;     // [T][k]
+    int32_t* n_unique;      // [1]
+    int32_t* uniq;          // [T*k]
+    int32_t* off;           // [T*k+1]
+    int32_t* asg;           // [T*k]
+    int32_t* inv;           // [T*k]
+    int32_t* tiles;         // int2 [max tiles]
+    int32_t* n_tiles;       // [1]
+    int T, E, k;
+    int has_shared;
+};
+
+struct GroupedGuArgs {
+    const uint16_t* x;      // bf16 [T][H]
+    Fp4Mat gate, up;        // [E][I][H/2]
+    Fp4Mat sgate, sup;      // [1][Is][H/2] (q == nullptr: no shared expert)
+    const int32_t* uniq;
+    const int32_t* off;
+    const int32_t* asg;
+    const int32_t* tiles;
+    const int32_t* n_tiles;
+    float* h;               // [T*k][I] by asg position
+    float* h_sh;            // [T][Is]
+    int T, H, I, Is, k;
+};
+
+struct GroupedDownArgs {
+    Fp4Mat down;            // [E][H][I/2]
+    Fp4Mat sdown;           // [1][H][Is/2]
+    const int32_t* uniq;
+    const int32_t* off;
+    const int32_t* tiles;
+    const int32_t* n_tiles;
+    const float* h;
+    const float* h_sh;
+    float* o;               // [T*k + T][H]: rows by asg position, then the shared rows by token
+    int T, H, I, Is, k;
+};
+
+struct CombineArgs {
+    const float* o;         // as GroupedDownArgs::o
+    const float* w;         // [T][k]
+    const int32_t* inv;     // [T*k]
+    const uint16_t* residual;  // bf16 [T][H] or nullptr
+    float* y32;             // [T][H]
+    uint16_t* y;            // bf16 [T][H] or nullptr
+    uint16_t* x_next;       // bf16 RMS-normalised y for the next layer, or nullptr
+    float eps, rs;
+    int T, H, k, has_shared;
+};
+
 // Optional kernel timing: start/stop events stamped from the kernel's own
 // dispatch (hipExtLaunchKernelGGL); nullptr = plain launch.
 struct Timing {
@@ -95,6 +162,19 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t st);  // logits given
 hipError_t launch_gateup(const GateUpArgs& a, int max_unique, hipStream_t st, const Timing* t = nullptr);
 hipError_t launch_down(const DownArgs& a, hipStream_t st, const Timing* t = nullptr);
 hipError_t launch_dequant(Fp4Mat m, int n_experts, int rows, int cols, float* out, hipStream_t st);
+
+// Grouped regime (moe_grouped.hip).
+hipError_t launch_select_rows(const SelectArgs& a, hipStream_t st);  // ids and w only
+hipError_t launch_group(const GroupArgs& a, hipStream_t st);
+// hmax [T*k][I/64] and hmax_sh [T][Is/64]: max |h| of each token per 64-row slab
+hipError_t launch_gateup_grouped(const GroupedGuArgs& a, float* hmax, float* hmax_sh, int max_tiles,
+                                 hipStream_t st);
+hipError_t launch_down_grouped(const GroupedDownArgs& a, const float* hmax, const float* hmax_sh, int max_tiles,
+                               hipStream_t st);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+hipError_t init_grouped_kernels();
+int grouped_max_tiles(int T, int E, int k, bool has_shared);
+bool grouped_lds_fits(int T, int E, int I, int Is);
 
 // One-time kernel attributes (dynamic LDS sizes).
 hipError_t init_kernels();

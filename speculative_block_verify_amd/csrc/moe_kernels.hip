@@ -1,25 +1,22 @@
-// gfx950 (CDNA4) kernels of the NVFP4 MoE block-verify layer.
-//
-// Per layer three launches:
-//   k_router  router GEMV (one wave per expert row, bf16 x staged in LDS,
-//             v_dot2_f32_bf16) and, in further workgroups, the shared
-//             expert's gate/up, which also needs only x;
-//   k_gateup  every workgroup first repeats the selection from the logits:
-//             top-k per row with a DPP wave argmax (PR #844 section 4 item 3
-//             router tail: argPartition + takeAlong) and the dedup CSR
-//             (section 8: the stock gather reads a repeated expert once per
-//             slot -- here each unique expert is streamed once); then work
-//             items (unique expert, slab of intermediate rows): 128-bit loads
-//             of packed E2M1 codes, in-register decode with
-//             v_cvt_scalef32_pk_bf16_fp4, dot2 against x held in registers,
-//             E4M3 block scale per 16 columns, tensor scale after the lane
-//             reduction, SwiGLU epilogue (silu(gate) * up, PR #844 section 4
-//             item 1) writing fp32 h;
+// gfx950 (CDNA4) kernels of the NVFP4 MoE block-verify layer, verify-width
+// regime (K <= 16 rows).  Per layer three launches:
+//   k_router  router GEMV, one wave per expert row, bf16 x staged in LDS,
+//             v_dot2_f32_bf16, fp32 accumulation; when chaining layers its
+//             prologue RMS-normalises the previous layer's output;
+//   k_gateup  the shared expert's gate/up tiles, then routed workgroups that
+//             each repeat the selection from the logits (top-k per row with a
+//             DPP wave argmax, after the router tail of PR #844 section 4:
+//             argPartition + takeAlong) and the dedup CSR (PR #844 section 8
+//             notes the stock gather reads a repeated expert once per slot;
+//             here each unique expert is streamed once), then loop over work
+//             items (unique expert, 16 intermediate rows) on the matrix cores:
+//             128-bit loads of packed E2M1 codes, in-register decode, fp16
+//             MFMA, SwiGLU epilogue writing fp32 h;
 //   k_down    one workgroup per 8 output rows: every unique expert's down
-//             rows for that slab (fp32 decode, fp32 h), per-slot partials
-//             in LDS, then the deterministic combine
+//             rows for that slab (fp32 decode, fp32 h), per-slot partials in
+//             LDS, then the deterministic combine
 //             y = rs * sum_j w_j o_j + shared (+ residual) in rank order
-//             (PR #844 section 4 item 4 and section 5 expression order).
+//             (PR #844 section 5 expression order).
 // The routed work list is data dependent (the number of unique experts is
 // known only on the device), so the gate/up grid is sized for the largest
 // possible count (capped; workgroups loop) and surplus workgroups finish
@@ -28,275 +25,10 @@
 // boundary inside a graph.
 #include <hip/hip_ext.h>
 
-#include "moe_internal.h"
+#include "moe_device.h"
 
 namespace moe {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// ---------------------------------------------------------------------------
-// scalar helpers
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
-// Order-preserving map of a float key onto uint32 (larger float -> larger
-// integer; -0 and +0 map together).  Real keys never map to 0, which marks
-// an empty or already-taken entry.
-__device__ __forceinline__ uint32_t key_bits(float f) {
-    uint32_t u = __float_as_uint(f + 0.0f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// E4M3FN byte -> fp32 (gfx950 converts OCP FP8 natively).
-template <int SEL>
-__device__ __forceinline__ float e4m3_to_f32(uint32_t packed) {
-    return __builtin_amdgcn_cvt_f32_fp8((int)packed, SEL);
-}
-
-// Eight E2M1 codes (one dword, column 2t in the low nibble of byte t) ->
-// four bf16 pairs (exact: every E2M1 value is a bf16).
-__device__ __forceinline__ void fp4x8_to_bf16(uint32_t v, bf16x2_t* out) {
-    out[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 0);
-    out[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 1);
-    out[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 2);
-    out[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 3);
-}
-
-__device__ __forceinline__ void fp4x8_to_f32(uint32_t v, float* out) {
-    f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 0);
-    f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 1);
-    f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 2);
-    f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 3);
-    out[0] = p0.x; out[1] = p0.y; out[2] = p1.x; out[3] = p1.y;
-    out[4] = p2.x; out[5] = p2.y; out[6] = p3.x; out[7] = p3.y;
-}
-
-__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
-
-__device__ __forceinline__ float dot2(bf16x2_t a, bf16x2_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
-}
-
-// ---------------------------------------------------------------------------
-// cross-lane helpers (wave64).  DPP row shifts accumulate inside 16-lane
-// rows; readlane combines the four rows.  Summation order is fixed, so every
-// result is deterministic.
-// ---------------------------------------------------------------------------
-
-template <int CTRL>
-__device__ __forceinline__ int dpp(int v) {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ float dppf(float v) {
-    return __int_as_float(dpp<CTRL>(__float_as_int(v)));
-}
-__device__ __forceinline__ float readlanef(float v, int l) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-
-// inclusive prefix sum inside each 16-lane row
-__device__ __forceinline__ float row_scan(float v) {
-    v += dppf<0x111>(v);
-    v += dppf<0x112>(v);
-    v += dppf<0x114>(v);
-    v += dppf<0x118>(v);
-    return v;
-}
-__device__ __forceinline__ int row_scan_i(int v) {
-    v += dpp<0x111>(v);
-    v += dpp<0x112>(v);
-    v += dpp<0x114>(v);
-    v += dpp<0x118>(v);
-    return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-    v = row_scan(v);
-    return (readlanef(v, 15) + readlanef(v, 31)) + (readlanef(v, 47) + readlanef(v, 63));
-}
-
-__device__ __forceinline__ int wave_incl_scan(int v) {
-    const int lane = threadIdx.x & 63;
-    v = row_scan_i(v);
-    const int t0 = __builtin_amdgcn_readlane(v, 15);
-    const int t1 = __builtin_amdgcn_readlane(v, 31);
-    const int t2 = __builtin_amdgcn_readlane(v, 47);
-    if (lane >= 16) v += t0;
-    if (lane >= 32) v += t1;
-    if (lane >= 48) v += t2;
-    return v;
-}
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, (uint32_t)dpp<0x111>((int)v));
-    v = max(v, (uint32_t)dpp<0x112>((int)v));
-    v = max(v, (uint32_t)dpp<0x114>((int)v));
-    v = max(v, (uint32_t)dpp<0x118>((int)v));
-    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
-    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
-    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
-    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-    return max(max(a, b), max(c, d));
-}
-
-// Sum over aligned groups of G lanes; valid in the last lane of each group.
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-    if constexpr (G == 64) {
-        return wave_sum(v);
-    } else if constexpr (G == 32) {
-        v = row_scan(v);
-        const float lo = readlanef(v, 15) + readlanef(v, 31);
-        const float hi = readlanef(v, 47) + readlanef(v, 63);
-        return (threadIdx.x & 32) ? hi : lo;
-    } else if constexpr (G == 16) {
-        return row_scan(v);
-    } else {
-#pragma unroll
-        for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-        return v;
-    }
-}
-
-__device__ __forceinline__ float group_sum_rt(float v, int G) {
-    switch (G) {
-        case 64: return group_sum<64>(v);
-        case 32: return group_sum<32>(v);
-        case 16: return group_sum<16>(v);
-        case 8: return group_sum<8>(v);
-        case 4: return group_sum<4>(v);
-        default: return group_sum<2>(v);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// selection + dedup (one workgroup of kBlock threads)
-// ---------------------------------------------------------------------------
-
-struct SelectSmem {
-    int32_t sel[kMaxSlots];
-    float w[kMaxSlots];
-    int32_t asg[kMaxSlots];
-    int32_t inv[kMaxSlots];
-    int32_t uniq[kMaxSlots];
-    int32_t off[kMaxSlots + 1];
-    int32_t n_unique;
-    uint32_t rowmask[kMaxExperts];   // rows that selected each expert
-    int32_t cstart[kMaxExperts];     // CSR offset of each expert
-};
-
-// Copy n floats global -> LDS with every load of a pass in flight at once.
-__device__ __forceinline__ void stage_floats(float* dst, const float* src, int n, int tid, int nthr) {
-    constexpr int U = 8;
-    for (int base = 0; base < n; base += U * nthr) {
-        float v[U];
-#pragma unroll
-        for (int j = 0; j < U; ++j) {
-            const int i = base + j * nthr + tid;
-            v[j] = (i < n) ? src[i] : 0.0f;
-        }
-#pragma unroll
-        for (int j = 0; j < U; ++j) {
-            const int i = base + j * nthr + tid;
-            if (i < n) dst[i] = v[j];
-        }
-    }
-}
-
-// Top-k of row r by (key desc, index asc) with one wave.  Lane l owns the P
-// experts l*P .. l*P+P-1 (contiguous) and keeps them sorted; each round takes
-// the wave maximum of the lanes' heads.  Among equal keys the lowest lane
-// wins, which (contiguous ownership, stable in-lane order) is the lowest
-// expert index.  lr: the row's logits in LDS.
-template <int P>
-__device__ void wave_topk(const SelectArgs& a, const float* lr, int r, SelectSmem& sm) {
-    const int lane = threadIdx.x & 63;
-    const int E = a.E, k = a.k;
-    uint32_t sk[P];
-    int si[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-        const int e = lane * P + p;
-        uint32_t v = 0;
-        if (e < E) {
-            const float l = lr[e];
-            float key = l;
-            if (a.score_fn == 1) {
-                const float sig = (float)(1.0 / (1.0 + exp(-(double)l)));
-                key = sig + a.bias[e];
-            }
-            v = key_bits(key);
-        }
-        sk[p] = v;
-        si[p] = p;
-    }
-    // stable insertion network, descending
-#pragma unroll
-    for (int i = 1; i < P; ++i) {
-#pragma unroll
-        for (int j = i; j > 0; --j) {
-            const bool sw = sk[j] > sk[j - 1];
-            const uint32_t ka = sk[j], kb = sk[j - 1];
-            const int ia = si[j], ib = si[j - 1];
-            sk[j - 1] = sw ? ka : kb; sk[j] = sw ? kb : ka;
-            si[j - 1] = sw ? ia : ib; si[j] = sw ? ib : ia;
-        }
-    }
-    int mine = 0;
-    for (int j = 0; j < k; ++j) {
-        const uint32_t head = sk[0];
-        const uint32_t m = wave_max_u32(head);
-        const unsigned long long mask = __ballot(head == m);
-        const int L = __builtin_ctzll(mask);
-        const int e = L * P + __builtin_amdgcn_readlane(si[0], L);
-        if (lane == j) mine = e;
-        if (lane == L) {
-#pragma unroll
-            for (int p = 0; p + 1 < P; ++p) { sk[p] = sk[p + 1]; si[p] = si[p + 1]; }
-            sk[P - 1] = 0;
-        }
-    }
-    // mixture weights over the selection (routed scale not folded in)
-    const float l = (lane < k) ? lr[mine] : 0.0f;
-    float wv;
-    if (a.score_fn == 0) {
-        const float lmax = readlanef(l, 0);  // rank 0 holds the largest logit
-        const float ex = (lane < k) ? expf(l - lmax) : 0.0f;
-        const float s = wave_sum(ex);
-        wv = ex / s;
-    } else {
-        const float sg = (lane < k) ? (float)(1.0 / (1.0 + exp(-(double)l))) : 0.0f;
-        if (a.norm_topk) {
-            const float s = wave_sum(sg);
-            wv = sg / s;
-        } else {
-            wv = sg;
-        }
-    }
-    if (lane < k) {
-        sm.sel[r * k + lane] = mine;
-        sm.w[r * k + lane] = wv;
-    }
-}
-
-__device__ void wave_topk_rt(const SelectArgs& a, const float* lr, int r, SelectSmem& sm) {
-    const int P = (a.E + 63) >> 6;
-    if (P <= 1) wave_topk<1>(a, lr, r, sm);
-    else if (P <= 2) wave_topk<2>(a, lr, r, sm);
-    else if (P <= 4) wave_topk<4>(a, lr, r, sm);
-    else if (P <= 8) wave_topk<8>(a, lr, r, sm);
-    else wave_topk<16>(a, lr, r, sm);
-}
 
 // Canonical dedup of the n = K*k selected slots with the whole workgroup.
 // A row never selects an expert twice, so expert e's slots are one per row
@@ -418,53 +150,12 @@ __global__ __launch_bounds__(kBlock) void k_select(SelectArgs a) {
 // fixed order.
 // ---------------------------------------------------------------------------
 
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kRedFloats = kWaves * 2 * 64 * 4;  // cross-wave partials of the gate/up tile
 
-constexpr int kTileRows = 16;
-constexpr int kSbCols = 256;
-// each wave holds at most two superblocks in flight (hidden <= 2048)
-constexpr int kRedFloats = kWaves * 2 * 64 * 4;         // cross-wave partials
-
-// Padded LDS layout of the fp16 x rows: 8 halfs of padding after every 64
-// columns and 32 after each row, so the 64 lanes of an MFMA B-operand read
-// (16 rows x 4 column blocks, 16 bytes each) spread over the banks.
-__host__ __device__ constexpr int xh_row_stride(int H) { return H + (H / 64) * 8 + 32; }
-__device__ __forceinline__ int xh_index(int m, int c, int H) { return m * xh_row_stride(H) + c + (c >> 6) * 8; }
-constexpr int kMaxDynLds = 160 * 1024 - 1024;           // gfx950: 160 KiB per workgroup, minus static use
-
-// Code and scale registers of one superblock of one lane (gate and up).
-struct GuSb {
-    uint4 g0, g1, u0, u1;
-    uint32_t gs, us;
-};
 struct GuRegs {
     GuSb sb0, sb1;  // this wave's superblocks wave and wave + kWaves
 };
 
-__device__ __forceinline__ GuSb gu_load_sb(const uint8_t* gq, const uint8_t* gs, const uint8_t* uq,
-                                          const uint8_t* us, int H, int n0, int sb, bool live) {
-    const int lane = threadIdx.x & 63;
-    const int i = lane & 15, kb = lane >> 4;
-    GuSb r;
-    if (live) {
-        const int k0 = sb * kSbCols + kb * 64;
-        const size_t row = (size_t)(n0 + i);
-        const uint8_t* qg = gq + row * (H / 2) + k0 / 2;
-        const uint8_t* qu = uq + row * (H / 2) + k0 / 2;
-        r.g0 = *reinterpret_cast<const uint4*>(qg);
-        r.g1 = *reinterpret_cast<const uint4*>(qg + 16);
-        r.u0 = *reinterpret_cast<const uint4*>(qu);
-        r.u1 = *reinterpret_cast<const uint4*>(qu + 16);
-        r.gs = *reinterpret_cast<const uint32_t*>(gs + row * (H / 16) + k0 / 16);
-        r.us = *reinterpret_cast<const uint32_t*>(us + row * (H / 16) + k0 / 16);
-    } else {
-        r.g0 = r.g1 = r.u0 = r.u1 = make_uint4(0, 0, 0, 0);
-        r.gs = r.us = 0;
-    }
-    return r;
-}
 
 __device__ __forceinline__ GuRegs gu_load(const uint8_t* gq, const uint8_t* gs, const uint8_t* uq, const uint8_t* us,
                                          int H, int n0) {
@@ -476,33 +167,6 @@ __device__ __forceinline__ GuRegs gu_load(const uint8_t* gq, const uint8_t* gs, 
     return R;
 }
 
-__device__ __forceinline__ uint32_t pick_word(const uint4& lo, const uint4& hi, int s) {
-    const uint4& h = (s < 4) ? lo : hi;
-    switch (s & 3) {
-        case 0: return h.x;
-        case 1: return h.y;
-        case 2: return h.z;
-        default: return h.w;
-    }
-}
-
-// 8 FP4 codes (one dword) times one E4M3 scale -> 8 exact fp16 values
-__device__ __forceinline__ f16x8_t decode8_f16(uint32_t codes, _Float16 scale) {
-    const f16x2_t sc = {scale, scale};
-    const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * sc;
-    const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * sc;
-    const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * sc;
-    const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * sc;
-    f16x8_t r;
-    r[0] = p0.x; r[1] = p0.y; r[2] = p1.x; r[3] = p1.y;
-    r[4] = p2.x; r[5] = p2.y; r[6] = p3.x; r[7] = p3.y;
-    return r;
-}
-
-template <int SEL>
-__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t packed) {
-    return (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)packed, SEL);
-}
 
 // The eight MFMA steps of one superblock.
 // xr: this lane's x row in LDS at the superblock's first column of its
@@ -559,10 +223,6 @@ __device__ __forceinline__ void gu_compute(const GuRegs& R, float gts, float uts
     }
 }
 
-__device__ __forceinline__ uint32_t bf16pair_to_f16pair(uint32_t v) {
-    const f16x2_t h = {(_Float16)__uint_as_float(v << 16), (_Float16)__uint_as_float(v & 0xFFFF0000u)};
-    return __builtin_bit_cast(uint32_t, h);
-}
 
 // x rows (bf16, global or LDS) -> fp16 rows in LDS.  Row m comes from
 // source row asg[o0 + m] / k (the slots of one unique expert; asg in LDS), or
@@ -608,10 +268,12 @@ __device__ __forceinline__ void stage_x_f16(const uint16_t* x, const int32_t* as
 
 constexpr int kRouterPieces = 4;  // 16-byte router pieces per lane (hidden <= 2048)
 
-// Builds this layer's bf16 x in LDS (xs, K*H) from x_in or from y_prev.
-__device__ void stage_x(const RouterArgs& a, uint16_t* xs, float* s_inv, int publish_idx, int publish_n) {
+// Builds this layer's bf16 x in LDS (xs, K*H) from x_in (rows of this
+// launch's chunk) or from y_prev.
+__device__ void stage_x(const RouterArgs& a, const uint16_t* x_in, int K, uint16_t* xs, float* s_inv,
+                        int publish_idx, int publish_n) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int K = a.K, H = a.H, KH = K * H;
+    const int H = a.H, KH = K * H;
     if (a.y_prev) {
         constexpr int CH = 2;  // float4 pairs (16 elements) per thread per pass
         float4 v[2 * CH];
@@ -668,7 +330,7 @@ __device__ void stage_x(const RouterArgs& a, uint16_t* xs, float* s_inv, int pub
 #pragma unroll
             for (int j = 0; j < CH; ++j) {
                 const int i = base + (j * kBlock + tid) * 8;
-                v[j] = (i < KH) ? *reinterpret_cast<const uint4*>(a.x_in + i) : make_uint4(0, 0, 0, 0);
+                v[j] = (i < KH) ? *reinterpret_cast<const uint4*>(x_in + i) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int j = 0; j < CH; ++j) {
@@ -680,13 +342,17 @@ __device__ void stage_x(const RouterArgs& a, uint16_t* xs, float* s_inv, int pub
     }
 }
 
+// gridDim.y > 1 splits the rows into chunks of MAXM (only without y_prev).
 template <int MAXM>
 __global__ __launch_bounds__(kBlock) void k_router(RouterArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
     __shared__ float s_inv[kMaxRows];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int K = a.K, H = a.H, E = a.E;
+    const int H = a.H, E = a.E;
+    const int r0 = blockIdx.y * MAXM;
+    const int K = min(MAXM, a.K - r0);
+    float* const logits = a.logits + (size_t)r0 * E;
     const int n_router_blocks = (E + kWaves - 1) / kWaves;
 
     {
@@ -699,7 +365,7 @@ __global__ __launch_bounds__(kBlock) void k_router(RouterArgs a) {
             wv[t] = (e < E && p < H) ? *reinterpret_cast<const uint4*>(a.wr + (size_t)e * H + p)
                                      : make_uint4(0, 0, 0, 0);
         }
-        stage_x(a, xs, s_inv, blockIdx.x, n_router_blocks);
+        stage_x(a, a.x_in + (size_t)r0 * H, K, xs, s_inv, blockIdx.x, n_router_blocks);
         if (e < E) {
             float acc[kMaxRows];
 #pragma unroll
@@ -726,7 +392,7 @@ __global__ __launch_bounds__(kBlock) void k_router(RouterArgs a) {
             for (int r = 0; r < MAXM; ++r) {
                 if (r < K) {
                     const float t = wave_sum(acc[r]);
-                    if (lane == 0) a.logits[(size_t)r * E + e] = t;
+                    if (lane == 0) logits[(size_t)r * E + e] = t;
                 }
             }
         }
@@ -1071,15 +737,19 @@ hipError_t init_kernels() {
         if ((e = set_lds(k_router<4>, kMaxDynLds)) != hipSuccess) return e;
         if ((e = set_lds(k_router<8>, kMaxDynLds)) != hipSuccess) return e;
         if ((e = set_lds(k_router<16>, kMaxDynLds)) != hipSuccess) return e;
-        return set_lds(k_down, kDownHLdsBytes);
+        if ((e = set_lds(k_down, kDownHLdsBytes)) != hipSuccess) return e;
+        return init_grouped_kernels();
     }();
     return once;
 }
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t st, const Timing* t) {
+    // more than kMaxRows rows (prefill, no y_prev): chunks of kMaxRows on grid y
     const int grid = (a.E + kWaves - 1) / kWaves;
-    const size_t smem = (size_t)a.K * a.H * 2;
-    const dim3 g(grid), b(kBlock);
+    const int chunks = (a.K + kMaxRows - 1) / kMaxRows;
+    if (chunks > 1 && a.y_prev) return hipErrorInvalidValue;
+    const size_t smem = (size_t)(a.K < kMaxRows ? a.K : kMaxRows) * a.H * 2;
+    const dim3 g(grid, chunks), b(kBlock);
     if (a.K <= 1) return launch(k_router<1>, g, b, smem, st, t, a);
     if (a.K <= 2) return launch(k_router<2>, g, b, smem, st, t, a);
     if (a.K <= 4) return launch(k_router<4>, g, b, smem, st, t, a);

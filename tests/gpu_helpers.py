@@ -31,8 +31,9 @@ CHAIN_Y_TOL = 1e-2
 LOGIT_RTOL = 1e-5
 
 
-def run_layer(cfg, wd, x, residual=None, ws=None):
-    """moe_verify_layer with every debug array; returns numpy arrays."""
+def run_layer(cfg, wd, x, residual=None, ws=None, grouped=False):
+    """moe_verify_layer (or moe_verify_layer_grouped) with every debug array;
+    returns numpy arrays."""
     K, H = x.shape
     E, k = cfg.n_experts, cfg.top_k
     dev = x.device
@@ -53,8 +54,8 @@ def run_layer(cfg, wd, x, residual=None, ws=None):
     y32 = torch.empty(K, H, dtype=torch.float32, device=dev)
     if ws is None:
         ws = api.alloc_workspace(cfg, dev)
-    api.moe_verify_layer(cfg, api.make_weights(wd), x, y, ws, y32=y32, residual=residual,
-                         debug=api.make_debug(**dbg_t))
+    fn = api.moe_verify_layer_grouped if grouped else api.moe_verify_layer
+    fn(cfg, api.make_weights(wd), x, y, ws, y32=y32, residual=residual, debug=api.make_debug(**dbg_t))
     torch.cuda.synchronize()
     out = {kk: v.cpu().numpy() for kk, v in dbg_t.items()}
     out["y"] = y.cpu().numpy().view(np.uint16)

@@ -57,7 +57,12 @@ def test_workspace_bytes_valid_and_invalid():
     assert n > 0 and n % 256 == 0
     assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(hidden=300))) == 0
     assert "hidden" in api.moe_verify_last_error()
-    assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(max_rows=17))) == 0
+    # up to 1024 rows; above 16 the grouped (prefill) limits apply too
+    assert api.moe_verify_workspace_bytes(_cfg(max_rows=512)) > n
+    assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(max_rows=1025))) == 0
+    assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(max_rows=17, inter=2048))) == 0
+    assert "grouped" in api.moe_verify_last_error()
+    assert api.moe_verify_workspace_bytes(_cfg(max_rows=16, inter=2048)) > 0
     assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(top_k=300))) == 0
     assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(inter=500))) == 0
     assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(score_fn=7))) == 0
@@ -106,6 +111,29 @@ def test_layer_argument_errors(case, code):
     elif case == "router_misaligned": w.router_w = FAKE + 4
     assert _layer(cfg, w, **kw) == code
     assert api.moe_verify_last_error()
+
+
+def test_grouped_layer_argument_errors():
+    L = api.lib()
+    cfg = _cfg(inter=2048)  # verify-width cfg; the grouped kernels stop at 1024
+    n = L.moe_verify_workspace_bytes(ctypes.byref(cfg))
+    rc = L.moe_verify_layer_grouped(ctypes.byref(cfg), ctypes.byref(_weights()), FAKE, 2, None, FAKE, None, FAKE,
+                                    n, None, None)
+    assert rc == api.MOE_ERR_UNSUPPORTED and "grouped" in api.moe_verify_last_error()
+    cfg = _cfg(max_rows=64)
+    n = L.moe_verify_workspace_bytes(ctypes.byref(cfg))
+    rc = L.moe_verify_layer_grouped(ctypes.byref(cfg), ctypes.byref(_weights()), FAKE, 65, None, FAKE, None, FAKE,
+                                    n, None, None)
+    assert rc == api.MOE_ERR_INVALID
+    # per-kernel timing is verify-width only
+    arr = (api.moe_layer_weights * 1)(_weights())
+    ms = (ctypes.c_float * 3)()
+    rc = L.moe_verify_stack_timed(ctypes.byref(cfg), arr, 1, FAKE, 32, FAKE, None, FAKE, n, None, ms)
+    assert rc == api.MOE_ERR_UNSUPPORTED
+    # the grouped route needs the workspace
+    out = api.moe_route_out(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    rc = L.moe_verify_route(ctypes.byref(cfg), FAKE, None, 32, ctypes.byref(out), None, 0, None)
+    assert rc == api.MOE_ERR_INVALID and "workspace" in api.moe_verify_last_error()
 
 
 def test_stack_and_route_argument_errors():

@@ -1,0 +1,195 @@
+"""GPU parity of the grouped (prefill) regime: more than 16 rows, the slots
+grouped by expert into tiles of up to 32 tokens, expert GEMMs on the matrix
+cores.  Same oracle and comparison rules as the verify-width tests
+(tests/gpu_helpers.py); every input is seeded and synthetic.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from speculative_block_verify_amd import api, inputs
+from tests import gpu_helpers as gh
+from tests.conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+DEV = "cuda"
+TINY_SH = inputs.MoEShape(hidden=256, n_experts=16, top_k=2, inter=128, shared_inter=128)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# selection + grouping from given logits, bit-exact
+# ---------------------------------------------------------------------------
+
+
+def _route(K, E, k, logits, shared=512):
+    shape = inputs.MoEShape(hidden=256, n_experts=E, top_k=k, inter=128, shared_inter=shared)
+    cfg = api.make_cfg(shape, K)
+    n = K * k
+    out = {"ids": torch.empty(n, dtype=torch.int32, device=DEV), "w": torch.empty(n, dtype=torch.float32, device=DEV),
+           "n_unique": torch.empty(1, dtype=torch.int32, device=DEV),
+           "uniq": torch.empty(n, dtype=torch.int32, device=DEV),
+           "off": torch.empty(n + 1, dtype=torch.int32, device=DEV),
+           "asg": torch.empty(n, dtype=torch.int32, device=DEV), "inv": torch.empty(n, dtype=torch.int32, device=DEV)}
+    lt = torch.as_tensor(logits, dtype=torch.float32).contiguous()
+    ws = api.alloc_workspace(cfg, DEV)
+    api.moe_verify_route(cfg, lt.to(DEV), out, workspace=ws)
+    torch.cuda.synchronize()
+    got = {kk: v.cpu().numpy() for kk, v in out.items()}
+    ids, w = orc.topk(lt.numpy(), k, 0, 1, None)
+    np.testing.assert_array_equal(got["ids"].reshape(K, k), ids)
+    np.testing.assert_allclose(got["w"].reshape(K, k), w, rtol=1e-6, atol=1e-7)
+    d = orc.dedup(ids, E)
+    U = d["n_unique"]
+    assert int(got["n_unique"][0]) == U
+    np.testing.assert_array_equal(got["uniq"][:U], d["uniq"])
+    np.testing.assert_array_equal(got["off"][:U + 1], d["off"])
+    np.testing.assert_array_equal(got["asg"], d["asg"])
+    np.testing.assert_array_equal(got["inv"], d["inv"])
+    return U
+
+
+@pytest.mark.parametrize("K,E,k", [(17, 16, 2), (64, 256, 8), (300, 256, 8), (1024, 64, 4), (40, 1024, 32)])
+def test_grouped_route_random_logits(K, E, k):
+    say("case: grouped route K=%d E=%d k=%d" % (K, E, k))
+    rng = np.random.default_rng(K + 7 * E + k)
+    _route(K, E, k, rng.standard_normal((K, E)).astype(np.float32))
+
+
+def test_grouped_route_ties_and_one_hot_experts():
+    say("case: grouped route ties")
+    K, E, k = 96, 256, 8
+    rng = np.random.default_rng(5)
+    l = rng.standard_normal((K, E)).astype(np.float32)
+    l[:40] = 0.0                       # 40 all-tied rows: experts 0..7, 40 tokens each (two tiles)
+    l[40:50] = np.float32(-1e30)
+    l[40:50, 200:208] = 1.0            # ten rows on experts 200..207
+    U = _route(K, E, k, l)
+    assert U >= 16
+
+
+# ---------------------------------------------------------------------------
+# layers
+# ---------------------------------------------------------------------------
+
+
+def _layer(shape, K, seed, grouped=True, x=None, score_fn=0, rs=1.0, residual=False, label=""):
+    say("case: grouped layer %s K=%d seed=%d" % (label, K, seed))
+    w = inputs.gen_layer(shape, seed, 0, device=DEV, with_bias=(score_fn == 1))
+    x = inputs.gen_x(K, shape.hidden, seed, device=DEV) if x is None else x
+    res = inputs.gen_x(K, shape.hidden, seed + 1, device=DEV, tag="res") if residual else None
+    cfg = api.make_cfg(shape, max(K, 17), score_fn=score_fn, routed_scale=rs)
+    gpu = gh.run_layer(cfg, w, x, residual=res, grouped=grouped)
+    orec = orc.moe_layer(w, x.cpu(), shape.top_k, score_fn, 1, rs, None if res is None else res.cpu())
+    bias = None if score_fn == 0 else w["router_bias"].cpu().numpy()
+    rep = gh.compare_layer(gpu, orec, shape.top_k, shape.n_experts, score_fn, bias, label=label)
+    np.testing.assert_array_equal(gpu["y"], gh.bf16_of(gpu["y32"]))
+    np.testing.assert_array_equal(gpu["y32"], gpu["y32_out"])
+    say("  report:", rep, "n_unique", int(gpu["n_unique"][0]))
+    return gpu, orec
+
+
+@pytest.mark.parametrize("K", [1, 3, 16, 17, 40, 100])
+def test_grouped_layer_tiny_shapes(K):
+    # hidden 256, 16 experts, top-2, intermediate 128, shared 128; K <= 16 runs
+    # the grouped kernels through moe_verify_layer_grouped
+    _layer(TINY_SH, K, 200 + K, label="tiny+shared")
+
+
+def test_grouped_layer_no_shared_expert():
+    _layer(inputs.MoEShape(512, 32, 4, 256, 0), 50, 9, label="no shared")
+
+
+def test_grouped_layer_correlated_rows_span_several_tiles():
+    # rows 1..K/2 are row 0 plus small noise: their experts get ~40+ tokens
+    # each, so one expert spans two or three 32-token tiles with a ragged tail
+    K = 90
+    x = inputs.gen_x_correlated(K, inputs.LAGUNA.hidden, 77, device=DEV)
+    gpu, _ = _layer(inputs.LAGUNA, K, 77, x=x, label="correlated")
+    counts = np.diff(gpu["off"][: int(gpu["n_unique"][0]) + 1])
+    assert counts.max() > 32
+
+
+def test_grouped_layer_sigmoid_bias_scale_and_residual():
+    _layer(inputs.LAGUNA, 48, 21, score_fn=1, rs=2.5, residual=True, label="sigmoid")
+
+
+def test_grouped_and_verify_width_paths_agree_at_16_rows():
+    say("case: grouped vs verify width K=16")
+    shape = inputs.LAGUNA
+    w = inputs.gen_layer(shape, 41, 0, device=DEV)
+    x = inputs.gen_x(16, shape.hidden, 41, device=DEV)
+    cfg = api.make_cfg(shape, 16)
+    a = gh.run_layer(cfg, w, x, grouped=False)
+    b = gh.run_layer(cfg, w, x, grouped=True)
+    np.testing.assert_array_equal(a["logits"], b["logits"])  # same router kernel
+    for kk in ("ids", "w", "n_unique", "uniq", "off", "asg", "inv"):
+        np.testing.assert_array_equal(a[kk], b[kk], err_msg=kk)
+    scale = np.abs(a["y32"]).max()
+    assert np.abs(a["y32"] - b["y32"]).max() <= 2 * gh.Y_TOL * scale
+
+
+def test_grouped_layer_bitwise_invariants():
+    say("case: grouped invariants")
+    shape = inputs.LAGUNA
+    w = inputs.gen_layer(shape, 43, 0, device=DEV)
+    cfg = api.make_cfg(shape, 64)
+    x = inputs.gen_x(64, shape.hidden, 43, device=DEV)
+    a = gh.run_layer(cfg, w, x)
+    b = gh.run_layer(cfg, w, x)
+    np.testing.assert_array_equal(a["y32"], b["y32"])
+    x1 = inputs.gen_x(1, shape.hidden, 44, device=DEV).repeat(40, 1).contiguous()
+    c = gh.run_layer(cfg, w, x1)
+    for r in range(1, 40):
+        np.testing.assert_array_equal(c["y32"][0], c["y32"][r])
+
+
+def test_grouped_stack_tiny_free_running():
+    say("case: grouped stack tiny 6 layers K=40")
+    shape, L, K = TINY_SH, 6, 40
+    layers = inputs.gen_stack(shape, L, 61, device=DEV)
+    x = inputs.gen_x(K, shape.hidden, 61, device=DEV)
+    cfg = api.make_cfg(shape, K)
+    gpu = gh.run_stack_debug(cfg, layers, x, L)
+    host = [{kk: (None if v is None else ({a: b.cpu() for a, b in v.items()} if isinstance(v, dict) else v.cpu()))
+             for kk, v in w.items()} for w in layers]
+    reps = gh.compare_stack(gpu, host, x.cpu().numpy(), shape.top_k, shape.n_experts, label="grouped stack")
+    say("  reports:", reps)
+    np.testing.assert_array_equal(gpu["y32_out"], gpu["y32"][L - 1])
+
+
+# ---------------------------------------------------------------------------
+# the prefill configuration at full size: 512 rows, hidden 2048, 256 experts,
+# top-8, intermediate 512, shared 512 -- sampled rows against the oracle
+# (rows are independent, so the oracle evaluates the sampled rows alone)
+# ---------------------------------------------------------------------------
+
+
+def test_grouped_prefill_512_rows_sampled():
+    say("case: prefill 512 rows")
+    shape, T = inputs.LAGUNA, 512
+    w = inputs.gen_layer(shape, 512, 0, device=DEV)
+    x = inputs.gen_x(T, shape.hidden, 512, device=DEV)
+    cfg = api.make_cfg(shape, T)
+    gpu = gh.run_layer(cfg, w, x)
+    U = int(gpu["n_unique"][0])
+    counts = np.diff(gpu["off"][: U + 1])
+    say("  experts used %d, tokens per expert min %d mean %.1f max %d" % (U, counts.min(), counts.mean(),
+                                                                        counts.max()))
+    np.testing.assert_array_equal(gpu["y"], gh.bf16_of(gpu["y32"]))
+    # the CSR is checked in full against the oracle's dedup of the GPU's own ids
+    d = orc.dedup(gpu["ids"], shape.n_experts)
+    assert U == d["n_unique"]
+    np.testing.assert_array_equal(gpu["asg"], d["asg"])
+    np.testing.assert_array_equal(gpu["inv"], d["inv"])
+    rows = np.random.default_rng(3).choice(T, 12, replace=False)
+    rows.sort()
+    orec = orc.moe_layer(w, x[rows].cpu(), shape.top_k)
+    sub = {kk: gpu[kk][rows] for kk in ("logits", "ids", "w", "y32")}
+    rep = gh.compare_layer(sub, orec, shape.top_k, shape.n_experts, label="prefill rows %s" % rows.tolist())
+    say("  report:", rep)
