@@ -50,7 +50,8 @@ def gateup_bytes(shape, n_unique, K):
     return b + K * H * 2 + (K * k * I + K * Is) * 4
 
 
-KERNEL_SOURCES = ("speculative_block_verify_amd/csrc/moe_kernels.hip", "speculative_block_verify_amd/csrc/moe_internal.h")
+KERNEL_SOURCES = ("speculative_block_verify_amd/csrc/moe_kernels.hip", "speculative_block_verify_amd/csrc/moe_device.h",
+                  "speculative_block_verify_amd/csrc/moe_internal.h")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_gateup_moe_stack_k2_hbm_traffic.txt")
 
 
@@ -96,6 +97,72 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4, "launches": 5}))
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
+
+
+def prefill(args):
+    """One MoE layer on 512 token rows (the prefill-sized grouped GEMM):
+    hidden 2048, 256 experts, top-8, intermediate 512, shared 512.  The layer
+    weights rotate over n_layers distinct sets and the inputs over a pool, so
+    the 456 MB of each layer are streamed from HBM.  value = algorithmic bytes
+    (router, every unique routed expert once, shared expert, activations) /
+    time; mfma_util = the expert FLOPs (gate, up and down on the matrix cores,
+    2 per multiply-add) / time / the dense fp16 peak."""
+    import torch
+    from speculative_block_verify_amd import api, inputs
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    shape, T, NL, POOL, SEED = inputs.LAGUNA, 512, args.prefill_layers, 4, 4096
+    layers = inputs.gen_stack(shape, NL, SEED, device=dev)
+    xs = [inputs.gen_x(T, shape.hidden, SEED + 1 + i, device=dev) for i in range(POOL)]
+    cfg = api.make_cfg(shape, T)
+    ws = api.alloc_workspace(cfg, dev)
+    wts = [api.make_weights(w) for w in layers]
+    y = torch.empty(T, shape.hidden, dtype=torch.int16, device=dev)
+    y32 = torch.empty(T, shape.hidden, dtype=torch.float32, device=dev)
+    H, I, Is, E, k = shape.hidden, shape.inter, shape.shared_inter, shape.n_experts, shape.top_k
+    nu = torch.empty(1, dtype=torch.int32, device=dev)
+    step_bytes, step_flops = [], []
+    for s in range(NL * POOL):
+        api.moe_verify_layer(cfg, wts[s % NL], xs[s % POOL], y, ws, y32=y32, debug=api.make_debug(n_unique=nu))
+        torch.cuda.synchronize()
+        U = int(nu.item())
+        step_bytes.append(api.moe_verify_weight_bytes(cfg, U, T))
+        step_flops.append(2.0 * (T * k * 3 * I * H + T * 3 * Is * H))
+    for s in range(args.warmup):
+        api.moe_verify_layer(cfg, wts[s % NL], xs[s % POOL], y, ws, y32=y32)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record(stream)
+    for s in range(args.steps):
+        api.moe_verify_layer(cfg, wts[s % NL], xs[s % POOL], y, ws, y32=y32)
+        ev[s + 1].record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev[0].elapsed_time(ev[-1])
+    per = [ev[s].elapsed_time(ev[s + 1]) for s in range(args.steps)]
+    nb = sum(step_bytes[s % (NL * POOL)] for s in range(args.steps))
+    nf = sum(step_flops[s % (NL * POOL)] for s in range(args.steps))
+    gbs = nb / (total_ms / 1e3) / 1e9
+    tflops = nf / (total_ms / 1e3) / 1e12
+    log("prefill: %d layers of 512 rows in %.3f ms: %.1f GB/s, %.1f TFLOP/s" % (args.steps, total_ms, gbs, tflops))
+    print(json.dumps({
+        "metric": "prefill grouped GEMM: weight GB/s and % HBM peak, MFMA utilisation (512 rows)",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16 mfma / f32 acc", "data": "synthetic",
+        "config": {"workload": "one NVFP4 MoE layer on 512 token rows (prefill grouped GEMM)", "rows": T,
+                   "hidden": H, "experts": E, "top_k": k, "inter": I, "shared_inter": Is,
+                   "layer_weight_sets": NL, "input_pool": POOL},
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "us_per_layer": {"mean": round(total_ms / args.steps * 1e3, 2),
+                         "median": round(statistics.median(per) * 1e3, 2)},
+        "bytes_per_layer": round(sum(step_bytes) / len(step_bytes)),
+        "expert_tflops": round(tflops, 2),
+        "mfma_util": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+    }), flush=True)
+
+
 def cpu_baseline(layers, xs, shape, K, budget_s):
     """The oracle (single-threaded C, fp64) chained through the same 40-layer
     stack, input after input of the pool, until budget_s seconds of CPU work;
@@ -135,6 +202,9 @@ def main():
     ap.add_argument("--timing-steps", type=int, default=16, help="steps of the per-kernel timing pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--workload", choices=("stack", "prefill"), default="stack",
+                    help="stack: the 40-layer K=2 verify stack (default); prefill: one 512-row layer")
+    ap.add_argument("--prefill-layers", type=int, default=8, help="distinct weight sets the prefill mode rotates")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this path runs on a single MI355X and has no multi-GPU mode "
@@ -142,6 +212,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.workload == "prefill":
+        prefill(args)
         return
 
     import torch
