@@ -188,6 +188,11 @@ __device__ __forceinline__ void stage_floats(float* dst, const float* src, int n
     }
 }
 
+// Count of set bits of a 64-lane mask in the lanes below this one.
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // Top-k of row r by (key desc, index asc) with one wave.  Lane l owns the P
 // experts l*P .. l*P+P-1 (contiguous) and keeps them sorted; each round takes
 // the wave maximum of the lanes' heads.  Among equal keys the lowest lane

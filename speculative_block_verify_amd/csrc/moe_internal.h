@@ -67,7 +67,7 @@ struct GateUpArgs {
     SelectArgs sel;         // its outputs are written by the first routed workgroup only
     const uint16_t* x;      // bf16 [K][H]
     Fp4Mat gate, up;        // [E][I][H/2]
-    float* h;               // [K*k][I], indexed by position in asg
+    float* h;               // [K*k][I], indexed by slot r*k+j
     Fp4Mat sgate, sup;      // [1][Is][H/2] (q == nullptr: no shared expert)
     float* h_sh;            // [K][Is]
     int K, H, I, Is;
@@ -80,8 +80,9 @@ struct DownArgs {
     const int32_t* uniq;
     const int32_t* off;
     const int32_t* inv;
+    const int32_t* asg;
     const float* w;         // [K][k]
-    const float* h;
+    const float* h;         // [K*k][I] by slot
     const float* h_sh;
     const uint16_t* residual;  // bf16 [K][H] or nullptr
     float* y32;             // [K][H]

@@ -90,30 +90,47 @@ __device__ void dedup_block(SelectSmem& sm, uint32_t* rowmask, int32_t* cstart, 
 // All rows' top-k, then the canonical dedup CSR, left in LDS and, if
 // write_global, also in the SelectArgs outputs.  lg: K*E floats of LDS.
 // Returns the number of unique experts.
-__device__ int select_and_dedup(const SelectArgs& a, SelectSmem& sm, float* lg, bool write_global) {
-    const int tid = threadIdx.x, wave = tid >> 6;
-    const int K = a.K, k = a.k, E = a.E, n = K * k;
-    stage_floats(lg, a.logits, K * E, tid, kBlock);
-    __syncthreads();
-    for (int r = wave; r < K; r += kWaves) wave_topk_rt(a, lg + r * E, r, sm);
-    __syncthreads();
-    dedup_block(sm, sm.rowmask, sm.cstart, n, k, E);
+// Top-k of every row (lg: the K*E logits already in LDS), one wave per row.
+__device__ void select_rows(const SelectArgs& a, SelectSmem& sm, const float* lg) {
+    const int wave = threadIdx.x >> 6;
+    for (int r = wave; r < a.K; r += kWaves) wave_topk_rt(a, lg + r * a.E, r, sm);
+}
+template <int P>
+__device__ void select_rows_p(const SelectArgs& a, SelectSmem& sm, const float* lg) {
+    const int wave = threadIdx.x >> 6;
+    for (int r = wave; r < a.K; r += kWaves) wave_topk<P>(a, lg + r * a.E, r, sm);
+}
+
+// The canonical dedup CSR of the selection in sm (whole workgroup), written
+// with ids and w to the SelectArgs outputs.  Returns the unique count.
+__device__ int dedup_publish(const SelectArgs& a, SelectSmem& sm) {
+    const int tid = threadIdx.x;
+    const int k = a.k, n = a.K * k;
+    dedup_block(sm, sm.rowmask, sm.cstart, n, k, a.E);
     __syncthreads();
     const int U = sm.n_unique;
-    if (write_global) {
-        for (int s = tid; s < n; s += kBlock) {
-            a.asg[s] = sm.asg[s];
-            a.inv[s] = sm.inv[s];
-            a.ids[s] = sm.sel[s];
-            a.w[s] = sm.w[s];
-        }
-        for (int u = tid; u <= U; u += kBlock) {
-            if (u < U) a.uniq[u] = sm.uniq[u];
-            a.off[u] = sm.off[u];
-        }
-        if (tid == 0) *a.n_unique = U;
+    for (int s = tid; s < n; s += kBlock) {
+        a.asg[s] = sm.asg[s];
+        a.inv[s] = sm.inv[s];
+        a.ids[s] = sm.sel[s];
+        a.w[s] = sm.w[s];
     }
+    for (int u = tid; u <= U; u += kBlock) {
+        if (u < U) a.uniq[u] = sm.uniq[u];
+        a.off[u] = sm.off[u];
+    }
+    if (tid == 0) *a.n_unique = U;
     return U;
+}
+
+// All rows' top-k, then the canonical dedup CSR, published to the SelectArgs
+// outputs.  lg: K*E floats of LDS.
+__device__ int select_and_dedup(const SelectArgs& a, SelectSmem& sm, float* lg) {
+    stage_floats(lg, a.logits, a.K * a.E, threadIdx.x, kBlock);
+    __syncthreads();
+    select_rows(a, sm, lg);
+    __syncthreads();
+    return dedup_publish(a, sm);
 }
 
 __host__ __device__ constexpr size_t select_smem_bytes(int K, int E) {
@@ -125,7 +142,7 @@ __global__ __launch_bounds__(kBlock) void k_select(SelectArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     SelectSmem& sm = *reinterpret_cast<SelectSmem*>(smem);
     float* lg = reinterpret_cast<float*>(smem + (sizeof(SelectSmem) + 15) / 16 * 16);
-    select_and_dedup(a, sm, lg, true);
+    select_and_dedup(a, sm, lg);
 }
 
 // ---------------------------------------------------------------------------
@@ -192,16 +209,28 @@ __device__ __forceinline__ void gu_mfma_sb(const GuSb& r, const _Float16* xr, bo
 
 // xh: fp16 x rows in LDS (padded layout, xh_index); rows >= m_cnt are not read.
 // Writes h[j * hstride + n0 + r] for x rows j < m_cnt and the tile's 16 rows.
+// xh: fp16 x rows in LDS (padded layout, xh_index).  MFMA column j < m_cnt
+// takes x row xrows[j] and its h goes to row hrows[j] of hbase (identity
+// maps when null).  Writes h[hrows[j]][n0 .. n0+15].
 __device__ __forceinline__ void gu_compute(const GuRegs& R, float gts, float uts, int H, int n0,
-                                           const _Float16* xh, int m_cnt, float* hbase, int hstride, float* red) {
+                                           const _Float16* xh, int m_cnt, const int* xrows, const int* hrows,
+                                           float* hbase, int hstride, float* red) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane & 15, kb = lane >> 4;
     const int nsb = H / kSbCols;
+    const int xr = (j < m_cnt) ? (xrows ? xrows[j] : j) : 0;
     f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-    if (wave < nsb)
-        gu_mfma_sb(R.sb0, xh + xh_index(j, wave * kSbCols + kb * 64, H), j < m_cnt, accg, accu);
-    if (wave + kWaves < nsb)
-        gu_mfma_sb(R.sb1, xh + xh_index(j, (wave + kWaves) * kSbCols + kb * 64, H), j < m_cnt, accg, accu);
+    // this wave's superblocks wave and wave + kWaves (one copy of the MFMA body)
+#pragma nounroll
+    for (int t = 0; t < 2; ++t) {
+        const int sb = wave + t * kWaves;
+        // field-wise selection keeps the registers out of scratch memory
+        GuSb c;
+        c.g0 = t ? R.sb1.g0 : R.sb0.g0; c.g1 = t ? R.sb1.g1 : R.sb0.g1;
+        c.u0 = t ? R.sb1.u0 : R.sb0.u0; c.u1 = t ? R.sb1.u1 : R.sb0.u1;
+        c.gs = t ? R.sb1.gs : R.sb0.gs; c.us = t ? R.sb1.us : R.sb0.us;
+        if (sb < nsb) gu_mfma_sb(c, xh + xh_index(xr, sb * kSbCols + kb * 64, H), j < m_cnt, accg, accu);
+    }
     reinterpret_cast<f32x4_t*>(red)[(wave * 2 + 0) * 64 + lane] = accg;
     reinterpret_cast<f32x4_t*>(red)[(wave * 2 + 1) * 64 + lane] = accu;
     __syncthreads();
@@ -219,14 +248,44 @@ __device__ __forceinline__ void gu_compute(const GuRegs& R, float gts, float uts
         gv = g[1] * gts; uv = u[1] * uts; h.y = gv / (1.0f + expf(-gv)) * uv;
         gv = g[2] * gts; uv = u[2] * uts; h.z = gv / (1.0f + expf(-gv)) * uv;
         gv = g[3] * gts; uv = u[3] * uts; h.w = gv / (1.0f + expf(-gv)) * uv;
-        *reinterpret_cast<float4*>(hbase + (size_t)j * hstride + n0 + 4 * kb) = h;
+        const int hr = hrows ? hrows[j] : j;
+        *reinterpret_cast<float4*>(hbase + (size_t)hr * hstride + n0 + 4 * kb) = h;
     }
 }
 
+// The router logits (nl floats -> lg) and the K bf16 x rows (-> fp16 xh) in
+// one pass, every load of a pass in flight together.
+__device__ __forceinline__ void stage_logits_x(float* lg, const float* logits, int nl, _Float16* xh,
+                                               const uint16_t* x, int K, int H) {
+    const int tid = threadIdx.x;
+    const int per_row = H / 8;
+    const int nx = K * per_row;
+    const int n = nl > nx ? nl : nx;
+    constexpr int U = 4;
+    for (int base = 0; base < n; base += U * kBlock) {
+        float lv[U];
+        uint4 xv[U];
+#pragma unroll
+        for (int q = 0; q < U; ++q) {
+            const int i = base + q * kBlock + tid;
+            lv[q] = (i < nl) ? logits[i] : 0.0f;
+            xv[q] = (i < nx) ? *reinterpret_cast<const uint4*>(x + (size_t)(i / per_row) * H + (i % per_row) * 8)
+                             : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < U; ++q) {
+            const int i = base + q * kBlock + tid;
+            if (i < nl) lg[i] = lv[q];
+            if (i < nx) {
+                uint4 o;
+                o.x = bf16pair_to_f16pair(xv[q].x); o.y = bf16pair_to_f16pair(xv[q].y);
+                o.z = bf16pair_to_f16pair(xv[q].z); o.w = bf16pair_to_f16pair(xv[q].w);
+                *reinterpret_cast<uint4*>(xh + xh_index(i / per_row, (i % per_row) * 8, H)) = o;
+            }
+        }
+    }
+}
 
-// x rows (bf16, global or LDS) -> fp16 rows in LDS.  Row m comes from
-// source row asg[o0 + m] / k (the slots of one unique expert; asg in LDS), or
-// from row m when asg is null.  All loads of a pass are issued before use.
 __device__ __forceinline__ void stage_x_f16(const uint16_t* x, const int32_t* asg, int o0, int k, int m_cnt, int H,
                                             _Float16* xh) {
     const int tid = threadIdx.x;
@@ -400,51 +459,105 @@ __global__ __launch_bounds__(kBlock) void k_router(RouterArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_gateup: the first Is/16 workgroups are the shared expert's gate/up tiles
-// (they need only x and skip the selection); every other workgroup repeats
-// the selection from the 2 KB of logits (cheaper than a separate launch or a
-// grid-wide fence), then loops over the routed work items (unique expert,
-// 16 intermediate rows)
+// k_gateup: the last Is/16 workgroups are the shared expert's gate/up tiles
+// (they need only x and skip the selection).  Every other workgroup stages
+// the logits and x of all rows, repeats the top-k of every row (cheaper than
+// a separate launch or a grid-wide fence) and loops over work items
+// (slot r*k+j, 16 intermediate rows).  An item is done by the slot of the
+// first row that selected its expert, for every row that selected it, so
+// each unique expert is streamed once; items of later rows' slots of the
+// same expert are skipped.  h rows are indexed by slot.  The first routed
+// workgroup also writes the canonical dedup CSR (for the down kernel) while
+// its own weight loads are in flight.
 // ---------------------------------------------------------------------------
 
 __host__ __device__ constexpr size_t gateup_smem_bytes(int K, int E, int H) {
     return select_smem_bytes(K, E) + (size_t)K * xh_row_stride(H) * 2 + (size_t)kRedFloats * 4;
 }
 
+template <int P>
 __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int s_xrows[kWaves][kMaxRows];
+    __shared__ int s_hrows[kWaves][kMaxRows];
     SelectSmem& sm = *reinterpret_cast<SelectSmem*>(smem);
     float* lg = reinterpret_cast<float*>(smem + (sizeof(SelectSmem) + 15) / 16 * 16);
     _Float16* xh = reinterpret_cast<_Float16*>(smem + select_smem_bytes(a.K, a.sel.E));
     float* red = reinterpret_cast<float*>(smem + select_smem_bytes(a.K, a.sel.E) + (size_t)a.K * xh_row_stride(a.H) * 2);
-    const int H = a.H, k = a.sel.k;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int H = a.H, K = a.K, k = a.sel.k, I = a.I;
+    // routed workgroups first (dispatched first, two per compute unit), the
+    // shared expert's Is/16 tiles last
     const int n_sh = a.sgate.q ? a.Is / kTileRows : 0;
-    if ((int)blockIdx.x < n_sh) {
+    const int n_rb = gridDim.x - n_sh, rb = blockIdx.x;
+    const bool shared_blk = rb >= n_rb;
+    const int sh_tile = rb - n_rb;
+    const int nsr = I / kTileRows;
+    GuRegs R;
+    float gts = 0.0f, uts = 0.0f;  // tensor scales, requested with the weights
+    if (shared_blk) {
         // shared expert tile: weights requested before x is staged
-        const int n0 = blockIdx.x * kTileRows;
-        const GuRegs R = gu_load(a.sgate.q, a.sgate.s, a.sup.q, a.sup.s, H, n0);
-        stage_x_f16(a.x, nullptr, 0, 1, a.K, H, xh);
+        R = gu_load(a.sgate.q, a.sgate.s, a.sup.q, a.sup.s, H, sh_tile * kTileRows);
+        gts = a.sgate.ts[0];
+        uts = a.sup.ts[0];
+        stage_x_f16(a.x, nullptr, 0, 1, K, H, xh);
         __syncthreads();
-        gu_compute(R, a.sgate.ts[0], a.sup.ts[0], H, n0, xh, a.K, a.h_sh, a.Is, red);
-        return;
-    }
-    const int rb = blockIdx.x - n_sh, n_rb = gridDim.x - n_sh;
-    const int U = select_and_dedup(a.sel, sm, lg, rb == 0);
-    const int nsr = a.I / kTileRows;
-    const int items = U * nsr;
-    for (int it = rb; it < items; it += n_rb) {
-        const int u = it / nsr;
-        const int e = sm.uniq[u];
-        const int o0 = sm.off[u];
-        const int m_cnt = sm.off[u + 1] - o0;
-        const int n0 = (it % nsr) * kTileRows;
-        const size_t eq = (size_t)e * a.I * (H / 2), es = (size_t)e * a.I * (H / 16);
-        const GuRegs R = gu_load(a.gate.q + eq, a.gate.s + es, a.up.q + eq, a.up.s + es, H, n0);
-        stage_x_f16(a.x, sm.asg, o0, k, m_cnt, H, xh);
+    } else {
+        stage_logits_x(lg, a.sel.logits, K * a.sel.E, xh, a.x, K, H);
         __syncthreads();
-        gu_compute(R, a.gate.ts[e], a.up.ts[e], H, n0, xh, m_cnt, a.h + (size_t)o0 * a.I, a.I, red);
+        select_rows_p<P>(a.sel, sm, lg);
         __syncthreads();
     }
+    const int items = shared_blk ? 1 : K * k * nsr;
+    const int step = shared_blk ? 1 : n_rb;
+    bool published = shared_blk || rb != 0;
+    for (int it = shared_blk ? 0 : rb; it < items; it += step) {
+        int n0, m_cnt, e = 0;
+        bool owner = true;
+        const int* xrows = nullptr;
+        const int* hrows = nullptr;
+        if (shared_blk) {
+            n0 = sh_tile * kTileRows;
+            m_cnt = K;
+        } else {
+            const int s = it / nsr, r = s / k;
+            e = sm.sel[s];
+            n0 = (it % nsr) * kTileRows;
+            // rows that selected e (every wave computes the same mask)
+            bool has = false;
+            int jj = 0;
+            if (lane < K)
+                for (int j = 0; j < k; ++j)
+                    if (sm.sel[lane * k + j] == e) { has = true; jj = j; }
+            const unsigned long long mask = __ballot(has);
+            owner = (__ffsll((long long)mask) - 1) == r;
+            if (owner) {
+                const size_t eq = (size_t)e * I * (H / 2), es = (size_t)e * I * (H / 16);
+                R = gu_load(a.gate.q + eq, a.gate.s + es, a.up.q + eq, a.up.s + es, H, n0);
+                gts = a.gate.ts[e];
+                uts = a.up.ts[e];
+                m_cnt = __popcll(mask);
+                if (has) {
+                    const int pos = lanes_below(mask);
+                    s_xrows[wave][pos] = lane;
+                    s_hrows[wave][pos] = lane * k + jj;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                xrows = s_xrows[wave];
+                hrows = s_hrows[wave];
+            }
+        }
+        if (!published) {
+            dedup_publish(a.sel, sm);
+            published = true;
+        }
+        if (!owner) continue;
+        gu_compute(R, gts, uts, H, n0, xh, m_cnt, xrows, hrows, shared_blk ? a.h_sh : a.h, shared_blk ? a.Is : I, red);
+        __syncthreads();
+    }
+    if (!published) dedup_publish(a.sel, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -455,14 +568,15 @@ constexpr int kDownWaves = kDownThreads / 64;
 constexpr int kDownBatch = 6;  // tasks per wave whose codes are in flight together
 
 // The h rows are processed in chunks that fit kDownHLdsBytes: positions
-// 0..n-1 are the routed slots in dedup order (row length I), n..n+K-1 the
-// shared expert's rows (row length Is).
+// 0..n-1 are the routed slots in dedup order (h row asg[p], length I),
+// n..n+K-1 the shared expert's rows (length Is).
 __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
     constexpr int NH = kDownRowsPerBlock;
     __shared__ float so[(kMaxSlots + kMaxRows) * NH];
     __shared__ int s_uniq[kMaxSlots];
     __shared__ int s_off[kMaxSlots + 1];
     __shared__ int s_inv[kMaxSlots];
+    __shared__ int s_asg[kMaxSlots];
     __shared__ float s_w[kMaxSlots];
     __shared__ float s_y[kMaxRows * NH];
     __shared__ int s_U;
@@ -487,6 +601,7 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
         if (i < n) {
             s_uniq[i] = a.uniq[i];
             s_inv[i] = a.inv[i];
+            s_asg[i] = a.asg[i];
             s_w[i] = a.w[i];
         }
         s_off[i] = a.off[i];
@@ -582,7 +697,7 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
             const int len4 = (shared_row ? Is : I) / 4;
             const int cc = min(c4, len4 - 1);
             hv4[j] = shared_row ? reinterpret_cast<const float4*>(a.h_sh + (size_t)(rr - n) * Is)[cc]
-                                : reinterpret_cast<const float4*>(a.h + (size_t)rr * I)[cc];
+                                : reinterpret_cast<const float4*>(a.h + (size_t)s_asg[rr] * I)[cc];
         }
         load_batch(0);
 #pragma unroll
@@ -731,7 +846,11 @@ hipError_t init_kernels() {
     static hipError_t once = [] {
         hipError_t e;
         if ((e = set_lds(k_select, kMaxDynLds)) != hipSuccess) return e;
-        if ((e = set_lds(k_gateup, kMaxDynLds)) != hipSuccess) return e;
+        if ((e = set_lds(k_gateup<1>, kMaxDynLds)) != hipSuccess) return e;
+        if ((e = set_lds(k_gateup<2>, kMaxDynLds)) != hipSuccess) return e;
+        if ((e = set_lds(k_gateup<4>, kMaxDynLds)) != hipSuccess) return e;
+        if ((e = set_lds(k_gateup<8>, kMaxDynLds)) != hipSuccess) return e;
+        if ((e = set_lds(k_gateup<16>, kMaxDynLds)) != hipSuccess) return e;
         if ((e = set_lds(k_router<1>, kMaxDynLds)) != hipSuccess) return e;
         if ((e = set_lds(k_router<2>, kMaxDynLds)) != hipSuccess) return e;
         if ((e = set_lds(k_router<4>, kMaxDynLds)) != hipSuccess) return e;
@@ -762,10 +881,18 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_gateup(const GateUpArgs& a, int max_unique, hipStream_t st, const Timing* t) {
-    int grid = max_unique * (a.I / kTileRows);
+    (void)max_unique;
+    int grid = a.K * a.sel.k * (a.I / kTileRows);  // work items: (slot, 16 intermediate rows)
     if (grid > kGateUpMaxGrid) grid = kGateUpMaxGrid;
     grid += a.sgate.q ? a.Is / kTileRows : 0;
-    return launch(k_gateup, dim3(grid), dim3(kBlock), gateup_smem_bytes(a.K, a.sel.E, a.H), st, t, a);
+    const dim3 g(grid), b(kBlock);
+    const size_t smem = gateup_smem_bytes(a.K, a.sel.E, a.H);
+    const int P = (a.sel.E + 63) >> 6;  // experts per lane of the top-k
+    if (P <= 1) return launch(k_gateup<1>, g, b, smem, st, t, a);
+    if (P <= 2) return launch(k_gateup<2>, g, b, smem, st, t, a);
+    if (P <= 4) return launch(k_gateup<4>, g, b, smem, st, t, a);
+    if (P <= 8) return launch(k_gateup<8>, g, b, smem, st, t, a);
+    return launch(k_gateup<16>, g, b, smem, st, t, a);
 }
 
 hipError_t launch_down(const DownArgs& a, hipStream_t st, const Timing* t) {
