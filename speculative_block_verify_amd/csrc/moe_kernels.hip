@@ -258,7 +258,7 @@ __device__ __forceinline__ void gu_compute(const GuRegs& R, float gts, float uts
 __device__ __forceinline__ void stage_logits_x(float* lg, const float* logits, int nl, _Float16* xh,
                                                const uint16_t* x, int K, int H) {
     const int tid = threadIdx.x;
-    const int per_row = H / 8;
+    const int per_row = H / 8, lpr = __builtin_ctz(per_row);  // 16-byte pieces per row (a power of two)
     const int nx = K * per_row;
     const int n = nl > nx ? nl : nx;
     constexpr int U = 4;
@@ -269,7 +269,7 @@ __device__ __forceinline__ void stage_logits_x(float* lg, const float* logits, i
         for (int q = 0; q < U; ++q) {
             const int i = base + q * kBlock + tid;
             lv[q] = (i < nl) ? logits[i] : 0.0f;
-            xv[q] = (i < nx) ? *reinterpret_cast<const uint4*>(x + (size_t)(i / per_row) * H + (i % per_row) * 8)
+            xv[q] = (i < nx) ? *reinterpret_cast<const uint4*>(x + (size_t)(i >> lpr) * H + (i & (per_row - 1)) * 8)
                              : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
@@ -280,7 +280,7 @@ __device__ __forceinline__ void stage_logits_x(float* lg, const float* logits, i
                 uint4 o;
                 o.x = bf16pair_to_f16pair(xv[q].x); o.y = bf16pair_to_f16pair(xv[q].y);
                 o.z = bf16pair_to_f16pair(xv[q].z); o.w = bf16pair_to_f16pair(xv[q].w);
-                *reinterpret_cast<uint4*>(xh + xh_index(i / per_row, (i % per_row) * 8, H)) = o;
+                *reinterpret_cast<uint4*>(xh + xh_index(i >> lpr, (i & (per_row - 1)) * 8, H)) = o;
             }
         }
     }
@@ -289,7 +289,7 @@ __device__ __forceinline__ void stage_logits_x(float* lg, const float* logits, i
 __device__ __forceinline__ void stage_x_f16(const uint16_t* x, const int32_t* asg, int o0, int k, int m_cnt, int H,
                                             _Float16* xh) {
     const int tid = threadIdx.x;
-    const int per_row = H / 8;   // 16-byte pieces per row
+    const int per_row = H / 8, lpr = __builtin_ctz(per_row);  // 16-byte pieces per row (a power of two)
     const int total = m_cnt * per_row;
     constexpr int U = 4;
     for (int base = 0; base < total; base += U * kBlock) {
@@ -299,7 +299,7 @@ __device__ __forceinline__ void stage_x_f16(const uint16_t* x, const int32_t* as
             const int f = base + q * kBlock + tid;
             v[q] = make_uint4(0, 0, 0, 0);
             if (f < total) {
-                const int m = f / per_row, c = f % per_row;
+                const int m = f >> lpr, c = f & (per_row - 1);
                 const int src = asg ? asg[o0 + m] / k : m;
                 v[q] = *reinterpret_cast<const uint4*>(x + (size_t)src * H + c * 8);
             }
@@ -308,7 +308,7 @@ __device__ __forceinline__ void stage_x_f16(const uint16_t* x, const int32_t* as
         for (int q = 0; q < U; ++q) {
             const int f = base + q * kBlock + tid;
             if (f < total) {
-                const int m = f / per_row, c = f % per_row;
+                const int m = f >> lpr, c = f & (per_row - 1);
                 uint4 o;
                 o.x = bf16pair_to_f16pair(v[q].x); o.y = bf16pair_to_f16pair(v[q].y);
                 o.z = bf16pair_to_f16pair(v[q].z); o.w = bf16pair_to_f16pair(v[q].w);
@@ -683,7 +683,8 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
         // straight-line sequence with both round trips overlapped
         constexpr int SU = 8;
         static_assert(kDownHLdsBytes / 16 <= SU * kDownThreads, "h chunk exceeds one staging pass");
-        const int q4 = RL / 4;                  // float4 per staged row (unpadded)
+        const int q4 = RL / 4;                  // float4 per staged row (unpadded, a power of two)
+        const int lq4 = __builtin_ctz(q4);
         const int nf4 = (c1 - c0) * q4;
         // (loads unconditional at clamped addresses, as in load_batch;
         // columns past a shorter row's length are staged as zeros)
@@ -692,7 +693,7 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
 #pragma unroll
         for (int j = 0; j < SU; ++j) {
             const int f = min(j * kDownThreads + tid, nf4 - 1);
-            const int rr = c0 + f / q4, c4 = f % q4;
+            const int rr = c0 + (f >> lq4), c4 = f & (q4 - 1);
             const bool shared_row = rr >= n;
             const int len4 = (shared_row ? Is : I) / 4;
             const int cc = min(c4, len4 - 1);
@@ -704,7 +705,7 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
         for (int j = 0; j < SU; ++j) {
             const int f = j * kDownThreads + tid;
             if (f < nf4) {
-                const int rr = f / q4, c4 = f % q4;
+                const int rr = f >> lq4, c4 = f & (q4 - 1);
                 const int len4 = ((c0 + rr) >= n ? Is : I) / 4;
                 *reinterpret_cast<float4*>(hs + (size_t)rr * RLP + (c4 >> 3) * 36 + (c4 & 7) * 4) =
                     c4 < len4 ? hv4[j] : make_float4(0, 0, 0, 0);
