@@ -332,7 +332,7 @@ constexpr int kRouterPieces = 4;  // 16-byte router pieces per lane (hidden <= 2
 __device__ void stage_x(const RouterArgs& a, const uint16_t* x_in, int K, uint16_t* xs, float* s_inv,
                         int publish_idx, int publish_n) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int H = a.H, KH = K * H;
+    const int H = a.H, KH = K * H, lgH = __builtin_ctz(H);  // H is a power of two
     if (a.y_prev) {
         constexpr int CH = 2;  // float4 pairs (16 elements) per thread per pass
         float4 v[2 * CH];
@@ -364,7 +364,7 @@ __device__ void stage_x(const RouterArgs& a, const uint16_t* x_in, int K, uint16
             for (int j = 0; j < CH; ++j) {
                 const int i = base + (j * kBlock + tid) * 8;
                 if (i < KH) {
-                    const float sc = s_inv[i / H];
+                    const float sc = s_inv[i >> lgH];
                     const float4 p = v[2 * j], q = v[2 * j + 1];
                     uint4 o;
                     o.x = (uint32_t)f32_to_bf16_rne(p.x * sc) | ((uint32_t)f32_to_bf16_rne(p.y * sc) << 16);
