@@ -257,7 +257,7 @@ int enqueue_layer_grouped(const moe_cfg* c, const moe_layer_weights* w, const ui
     ra.wr = w->router_w;
     ra.logits = L.logits;
     ra.K = K; ra.H = c->hidden; ra.E = c->n_experts;
-    if ((e = moe::launch_router(ra, st)) != hipSuccess) return hip_fail(e, "router launch");
+    if ((e = moe::launch_router_mfma(ra, st)) != hipSuccess) return hip_fail(e, "router launch");
 
     moe::SelectArgs sa{};
     sa.logits = L.logits; sa.bias = w->router_bias;

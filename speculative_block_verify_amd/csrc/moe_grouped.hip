@@ -33,6 +33,79 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
+// k_router_mfma: logits = x Wr^T for many rows on the matrix cores
+//
+// Workgroup tile: 32 rows x 32 experts, 8 waves; wave w sums the columns
+// [w*H/8, (w+1)*H/8) for the whole tile (four 16x16 accumulators), with
+// every operand load of the wave issued before its first MFMA, and the eight
+// partial tiles are added in wave order through LDS.  MFMA step over 32
+// columns c..c+31: lane (i, kb) feeds row i's columns c + 8kb .. +7 of x as
+// its A k-block and of the router as its B k-block.  bf16 products are exact
+// in fp32; rows past T and experts past E are read at clamped indices and
+// not stored.
+// ---------------------------------------------------------------------------
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kRouterWaves = 8;
+
+template <int H>
+__global__ __launch_bounds__(kRouterWaves * 64) void k_router_mfma(RouterArgs a) {
+    __shared__ f32x4_t part[kRouterWaves - 1][4][64];
+    constexpr int NS = H / kRouterWaves / 32;  // MFMA steps per wave
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int i = lane & 15, kb = lane >> 4;
+    const int T = a.K, E = a.E;
+    const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
+    const int c0 = wave * (H / kRouterWaves) + 8 * kb;
+    const uint16_t* xr0 = a.x_in + (size_t)min(t0 + i, T - 1) * H + c0;
+    const uint16_t* xr1 = a.x_in + (size_t)min(t0 + 16 + i, T - 1) * H + c0;
+    const uint16_t* wr0 = a.wr + (size_t)min(e0 + i, E - 1) * H + c0;
+    const uint16_t* wr1 = a.wr + (size_t)min(e0 + 16 + i, E - 1) * H + c0;
+    uint4 x0[NS], x1[NS], w0[NS], w1[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        x0[s] = *reinterpret_cast<const uint4*>(xr0 + 32 * s);
+        x1[s] = *reinterpret_cast<const uint4*>(xr1 + 32 * s);
+        w0[s] = *reinterpret_cast<const uint4*>(wr0 + 32 * s);
+        w1[s] = *reinterpret_cast<const uint4*>(wr1 + 32 * s);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the MFMAs
+    f32x4_t acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, x0[s]), a1 = __builtin_bit_cast(bf16x8_t, x1[s]);
+        const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, w0[s]), b1 = __builtin_bit_cast(bf16x8_t, w1[s]);
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b1, acc[1], 0, 0, 0);
+        acc[2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b0, acc[2], 0, 0, 0);
+        acc[3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[3], 0, 0, 0);
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) part[wave - 1][t][lane] = acc[t];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // accumulator t = 2 * (row half) + (expert half); lane (j = lane % 16,
+        // q = lane / 16) holds rows 4q .. 4q+3 of expert column j
+        const int j = lane & 15, q = lane >> 4;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f32x4_t v = acc[t];
+#pragma unroll
+            for (int w = 0; w < kRouterWaves - 1; ++w) v += part[w][t][lane];
+            const int e = e0 + 16 * (t & 1) + j;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = t0 + 16 * (t >> 1) + 4 * q + r;
+                if (row < T && e < E) a.logits[(size_t)row * E + e] = v[r];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // k_select_rows: kWaves rows per workgroup
 // ---------------------------------------------------------------------------
 
@@ -285,63 +358,69 @@ __global__ __launch_bounds__(kBlock) void k_gateup_grouped(GroupedGuArgs a, floa
 // ---------------------------------------------------------------------------
 // grouped down
 //
-// Work item: (tile, 64-row slab of the output dimension).  Wave w computes
-// output rows n0 = slab*64 + 16w .. +15 for the tile's tokens.  Lane (i, kb)
-// holds the codes of row n0 + i at columns [sb*256 + kb*64, +64) of every
-// superblock of the intermediate dimension (at most kGMaxCols / 256).  The
-// tile's h rows are staged in LDS as hi = fp16(h * 2^-sigma) and
-// lo = fp16(h * 2^-sigma - hi), sigma per token such that its max |h| maps
-// into [2^14, 2^15); rows padded to (cols + 8) halfs.
+// Work item: (tile, group of G 64-row slabs of the output dimension).  The
+// tile's h rows are staged in LDS once per item as hi = fp16(h * 2^-sigma)
+// and lo = fp16(h * 2^-sigma - hi), sigma per token such that its max |h|
+// maps into [2^14, 2^15); staged rows span NSB whole superblocks, zero past
+// the row's length, stride NSB*256 + 8 halfs.  Then the item walks its
+// slabs: wave w computes output rows slab*64 + 16w .. +15 for the tile's
+// tokens; lane (i, kb) holds the codes of row n0 + i at columns
+// [sb*256 + kb*64, +64) of every superblock, and the next slab's codes are
+// in flight while the current slab is on the matrix cores.
 // ---------------------------------------------------------------------------
 
-constexpr int kGMaxSb = kGMaxCols / kSbCols;
+constexpr int kGMaxSb = kGMaxCols / kSbCols;  // superblocks of the longest staged h row
 
+template <int NSB>
+struct DownCodes {
+    uint4 c0[NSB], c1[NSB];
+    uint32_t sc[NSB];
+};
+
+template <int NSB, int G>
 __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedDownArgs a, const float* hmax, const float* hmax_sh) {
     extern __shared__ __align__(16) _Float16 hb[];  // hi [32][S], then lo [32][S]
     __shared__ int s_sig[kGChunk];
+    constexpr int S = NSB * kSbCols + 8;  // staged row stride in halfs
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i = lane & 15, kb = lane >> 4, j = lane & 15, q = lane >> 4;
     const uint8_t *const dq_r = a.down.q, *const ds_r = a.down.s, *const dq_s = a.sdown.q, *const ds_s = a.sdown.s;
     const float *const dts_r = a.down.ts, *const dts_s = a.sdown.ts;
     const int H = a.H, I = a.I, Is = a.Is, T = a.T, kk = a.k;
-    const int S = max(I, Is) + 8;   // staged row stride in halfs
     _Float16* hi = hb;
     _Float16* lo = hb + kGChunk * S;
-    const int nH = H / kGRows;
+    const int nG = H / (kGRows * G), lgG = __builtin_ctz(nG);  // slab groups per tile (a power of two)
     const int n_tiles = *a.n_tiles;
     const int n_sh = dq_s ? (T + kGChunk - 1) / kGChunk : 0;
     const int n_rt = n_tiles - n_sh;
-    const int items = n_tiles * nH;
+    const int items = n_tiles * nG;
     for (int it = blockIdx.x; it < items; it += gridDim.x) {
-        const int ti = it / nH, slab = it % nH;
+        const int ti = it >> lgG, grp = it & (nG - 1);
         const bool routed = ti < n_rt;
         const int4 tl = reinterpret_cast<const int4*>(a.tiles)[ti];
         const int e = routed ? tl.x : 0, p0 = tl.y, cnt = tl.z;
         const int cols = routed ? I : Is;
-        const int nsb = (cols + kSbCols - 1) / kSbCols;
         const int nslab = cols / kGRows;
         const uint8_t* mq = (routed ? dq_r : dq_s) + (size_t)e * H * (cols / 2);
         const uint8_t* ms = (routed ? ds_r : ds_s) + (size_t)e * H * (cols / 16);
         const float ts = (routed ? dts_r : dts_s)[e];
-        const int n0 = slab * kGRows + wave * 16;
 
-        // this lane's codes and scales of every superblock (64-column blocks
-        // past cols are zero)
-        uint4 c0[kGMaxSb], c1[kGMaxSb];
-        uint32_t sc[kGMaxSb];
+        // codes of slab g of this item (loads at clamped columns past the
+        // row's length: their products meet the zero columns of the staged h)
+        auto load_codes = [&](int g, DownCodes<NSB>& c) {
+            const size_t row = (size_t)((grp * G + g) * kGRows + wave * 16 + i);
 #pragma unroll
-        for (int sb = 0; sb < kGMaxSb; ++sb) {
-            c0[sb] = c1[sb] = make_uint4(0, 0, 0, 0);
-            sc[sb] = 0;
-            const int col = sb * kSbCols + kb * 64;
-            if (sb < nsb && col < cols) {
-                const size_t row = (size_t)(n0 + i);
+            for (int sb = 0; sb < NSB; ++sb) {
+                const int col = min(sb * kSbCols + kb * 64, cols - 64);
                 const uint8_t* p = mq + row * (cols / 2) + col / 2;
-                c0[sb] = *reinterpret_cast<const uint4*>(p);
-                c1[sb] = *reinterpret_cast<const uint4*>(p + 16);
-                sc[sb] = *reinterpret_cast<const uint32_t*>(ms + row * (cols / 16) + col / 16);
+                c.c0[sb] = *reinterpret_cast<const uint4*>(p);
+                c.c1[sb] = *reinterpret_cast<const uint4*>(p + 16);
+                c.sc[sb] = *reinterpret_cast<const uint32_t*>(ms + row * (cols / 16) + col / 16);
             }
-        }
+        };
+        DownCodes<NSB> cA, cB;
+        load_codes(0, cA);
+
         // per-token scale exponent from the gate/up kernel's max |h| per slab
         if (tid < kGChunk) {
             float mx = 0.0f;
@@ -354,79 +433,88 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedDownArgs a, cons
         __syncthreads();
         // stage: one superblock (32 rows x 256 columns = 2048 float4) per pass
         const float* hrow0 = routed ? a.h + (size_t)p0 * I : a.h_sh + (size_t)p0 * Is;
-        for (int sb = 0; sb < nsb; ++sb) {
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) {
             float4 v[8];
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const int f = t * kBlock + tid, m = f >> 6, c4 = f & 63;
-                const int col = sb * kSbCols + c4 * 4;
-                v[t] = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (col < cols) v[t] = *reinterpret_cast<const float4*>(hrow0 + (size_t)min(m, cnt - 1) * cols + col);
+                const int col = min(sb * kSbCols + c4 * 4, cols - 4);
+                v[t] = *reinterpret_cast<const float4*>(hrow0 + (size_t)min(m, cnt - 1) * cols + col);
             }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const int f = t * kBlock + tid, m = f >> 6, c4 = f & 63;
                 const int col = sb * kSbCols + c4 * 4;
-                if (col < cols) {
-                    const int sg = -s_sig[m];
-                    const bool live = m < cnt;
-                    const float x0 = live ? ldexpf(v[t].x, sg) : 0.f, x1 = live ? ldexpf(v[t].y, sg) : 0.f;
-                    const float x2 = live ? ldexpf(v[t].z, sg) : 0.f, x3 = live ? ldexpf(v[t].w, sg) : 0.f;
-                    const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1, h2 = (_Float16)x2, h3 = (_Float16)x3;
-                    f16x2_t a01 = {h0, h1}, a23 = {h2, h3};
-                    f16x2_t b01 = {(_Float16)(x0 - (float)h0), (_Float16)(x1 - (float)h1)};
-                    f16x2_t b23 = {(_Float16)(x2 - (float)h2), (_Float16)(x3 - (float)h3)};
-                    uint2 ph, pl;
-                    ph.x = __builtin_bit_cast(uint32_t, a01); ph.y = __builtin_bit_cast(uint32_t, a23);
-                    pl.x = __builtin_bit_cast(uint32_t, b01); pl.y = __builtin_bit_cast(uint32_t, b23);
-                    *reinterpret_cast<uint2*>(hi + m * S + col) = ph;
-                    *reinterpret_cast<uint2*>(lo + m * S + col) = pl;
-                }
+                const int sg = -s_sig[m];
+                const bool live = m < cnt && col < cols;
+                const float x0 = live ? ldexpf(v[t].x, sg) : 0.f, x1 = live ? ldexpf(v[t].y, sg) : 0.f;
+                const float x2 = live ? ldexpf(v[t].z, sg) : 0.f, x3 = live ? ldexpf(v[t].w, sg) : 0.f;
+                const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1, h2 = (_Float16)x2, h3 = (_Float16)x3;
+                f16x2_t a01 = {h0, h1}, a23 = {h2, h3};
+                f16x2_t b01 = {(_Float16)(x0 - (float)h0), (_Float16)(x1 - (float)h1)};
+                f16x2_t b23 = {(_Float16)(x2 - (float)h2), (_Float16)(x3 - (float)h3)};
+                uint2 ph, pl;
+                ph.x = __builtin_bit_cast(uint32_t, a01); ph.y = __builtin_bit_cast(uint32_t, a23);
+                pl.x = __builtin_bit_cast(uint32_t, b01); pl.y = __builtin_bit_cast(uint32_t, b23);
+                *reinterpret_cast<uint2*>(hi + m * S + col) = ph;
+                *reinterpret_cast<uint2*>(lo + m * S + col) = pl;
             }
         }
         __syncthreads();
 
         const int ntt = cnt > 16 ? 2 : 1;
-        f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        const f16x8_t zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+        float* obase = a.o + (size_t)(routed ? p0 : T * kk + p0) * H;
+        auto compute = [&](int g, const DownCodes<NSB>& c) {
+            f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            // every superblock of the staged row, also past a shorter row's
+            // length (zero h there): no data-dependent branch around the chain
 #pragma unroll
-        for (int sb = 0; sb < kGMaxSb; ++sb) {
-            if (sb < nsb) {
+            for (int sb = 0; sb < NSB; ++sb) {
                 const int colb = sb * kSbCols + kb * 64;
-                const bool live = colb < cols;
-                const _Float16 s0 = e4m3_to_f16<0>(sc[sb]), s1 = e4m3_to_f16<1>(sc[sb]);
-                const _Float16 s2 = e4m3_to_f16<2>(sc[sb]), s3 = e4m3_to_f16<3>(sc[sb]);
+                const _Float16 s0 = e4m3_to_f16<0>(c.sc[sb]), s1 = e4m3_to_f16<1>(c.sc[sb]);
+                const _Float16 s2 = e4m3_to_f16<2>(c.sc[sb]), s3 = e4m3_to_f16<3>(c.sc[sb]);
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
                     const _Float16 ssc = (s < 2) ? s0 : (s < 4) ? s1 : (s < 6) ? s2 : s3;
-                    const f16x8_t aw = decode8_f16(pick_word(c0[sb], c1[sb], s), ssc);
+                    const f16x8_t aw = decode8_f16(pick_word(c.c0[sb], c.c1[sb], s), ssc);
 #pragma unroll
                     for (int tt = 0; tt < 2; ++tt) {
                         if (tt < ntt) {
                             const int m = tt * 16 + j;
-                            const f16x8_t bh = live ? *reinterpret_cast<const f16x8_t*>(hi + m * S + colb + 8 * s) : zero8;
-                            const f16x8_t bl = live ? *reinterpret_cast<const f16x8_t*>(lo + m * S + colb + 8 * s) : zero8;
+                            const f16x8_t bh = *reinterpret_cast<const f16x8_t*>(hi + m * S + colb + 8 * s);
+                            const f16x8_t bl = *reinterpret_cast<const f16x8_t*>(lo + m * S + colb + 8 * s);
                             acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, bh, acc[tt], 0, 0, 0);
                             acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, bl, acc[tt], 0, 0, 0);
                         }
                     }
                 }
             }
-        }
-        // lane (j, q) holds output rows n0 + 4q .. +3 of token j
-        float* obase = a.o + (size_t)(routed ? p0 : T * kk + p0) * H;
+            // lane (j, q) holds output rows n0 + 4q .. +3 of token j
+            const int n0 = (grp * G + g) * kGRows + wave * 16;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int m = tt * 16 + j;
-            if (tt < ntt && m < cnt) {
-                const int sg = s_sig[m];
-                float4 ov;
-                ov.x = ldexpf(acc[tt][0], sg) * ts;
-                ov.y = ldexpf(acc[tt][1], sg) * ts;
-                ov.z = ldexpf(acc[tt][2], sg) * ts;
-                ov.w = ldexpf(acc[tt][3], sg) * ts;
-                *reinterpret_cast<float4*>(obase + (size_t)m * H + n0 + 4 * q) = ov;
+            for (int tt = 0; tt < 2; ++tt) {
+                const int m = tt * 16 + j;
+                if (tt < ntt && m < cnt) {
+                    const int sg = s_sig[m];
+                    float4 ov;
+                    ov.x = ldexpf(acc[tt][0], sg) * ts;
+                    ov.y = ldexpf(acc[tt][1], sg) * ts;
+                    ov.z = ldexpf(acc[tt][2], sg) * ts;
+                    ov.w = ldexpf(acc[tt][3], sg) * ts;
+                    *reinterpret_cast<float4*>(obase + (size_t)m * H + n0 + 4 * q) = ov;
+                }
             }
+        };
+        // slabs in pairs: the other register set's loads are always issued
+        // (the last slab's codes again at the end, an L2 hit) so the compiler
+        // keeps an exact count of loads in flight
+#pragma unroll 1
+        for (int g = 0; g < G; g += 2) {
+            load_codes(g + 1 < G ? g + 1 : G - 1, cB);
+            compute(g, cA);
+            load_codes(g + 2 < G ? g + 2 : G - 1, cA);
+            if (g + 1 < G) compute(g + 1, cB);
         }
         __syncthreads();  // staged rows and s_sig are replaced by the next item
     }
@@ -514,11 +602,18 @@ hipError_t launch_plain(Kern k, dim3 grid, dim3 block, size_t smem, hipStream_t 
 }
 
 size_t group_lds(int T, int E) { return (size_t)E * ((T + 31) / 32) * 4; }
-size_t down_lds(int I, int Is) { return (size_t)2 * kGChunk * ((I > Is ? I : Is) + 8) * 2; }
+// superblocks of the longest staged h row, and the grouped down kernel's
+// output slabs per work item
+int down_nsb(int I, int Is) { return ((I > Is ? I : Is) + kSbCols - 1) / kSbCols; }
+int down_g(int H) { return H >= 8 * kGRows ? 8 : 4; }
+size_t down_lds(int I, int Is) {
+    const int nsb = down_nsb(I, Is);
+    return (size_t)2 * kGChunk * ((nsb == 3 ? 4 : nsb) * kSbCols + 8) * 2;
+}
 
 // largest dynamic LDS each kernel is launched with (static LDS comes on top)
 constexpr int kGroupMaxLds = kMaxExperts * (kMaxGroupedRows / 32) * 4;
-constexpr int kGDownMaxLds = 2 * kGChunk * (kGMaxCols + 8) * 2;
+constexpr int kGDownMaxLds = 2 * kGChunk * (kGMaxSb * kSbCols + 8) * 2;
 
 }  // namespace
 
@@ -537,8 +632,27 @@ hipError_t init_grouped_kernels() {
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_group),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, kGroupMaxLds)) != hipSuccess)
         return e;
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(k_down_grouped),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, kGDownMaxLds);
+    const void* downs[] = {reinterpret_cast<const void*>(k_down_grouped<1, 4>),
+                           reinterpret_cast<const void*>(k_down_grouped<2, 4>),
+                           reinterpret_cast<const void*>(k_down_grouped<4, 4>),
+                           reinterpret_cast<const void*>(k_down_grouped<1, 8>),
+                           reinterpret_cast<const void*>(k_down_grouped<2, 8>),
+                           reinterpret_cast<const void*>(k_down_grouped<4, 8>)};
+    for (const void* f : downs)
+        if ((e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kGDownMaxLds)) != hipSuccess)
+            return e;
+    return hipSuccess;
+}
+
+hipError_t launch_router_mfma(const RouterArgs& a, hipStream_t st) {
+    const dim3 g((a.K + 31) / 32, (a.E + 31) / 32), b(kRouterWaves * 64);
+    switch (a.H) {
+        case 256: return launch_plain(k_router_mfma<256>, g, b, 0, st, a);
+        case 512: return launch_plain(k_router_mfma<512>, g, b, 0, st, a);
+        case 1024: return launch_plain(k_router_mfma<1024>, g, b, 0, st, a);
+        case 2048: return launch_plain(k_router_mfma<2048>, g, b, 0, st, a);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_select_rows(const SelectArgs& a, hipStream_t st) {
@@ -568,9 +682,20 @@ hipError_t launch_gateup_grouped(const GroupedGuArgs& a, float* hmax, float* hma
 
 hipError_t launch_down_grouped(const GroupedDownArgs& a, const float* hmax, const float* hmax_sh, int max_tiles,
                                hipStream_t st) {
-    long long items = (long long)max_tiles * (a.H / kGRows);
+    const int G = down_g(a.H), nsb = down_nsb(a.I, a.Is);
+    long long items = (long long)max_tiles * (a.H / (kGRows * G));
     const int grid = (int)(items < kGMaxGrid ? items : kGMaxGrid);
-    hipLaunchKernelGGL(k_down_grouped, dim3(grid), dim3(kBlock), down_lds(a.I, a.Is), st, a, hmax, hmax_sh);
+    const dim3 g(grid), b(kBlock);
+    const size_t lds = down_lds(a.I, a.Is);
+    if (G == 8) {
+        if (nsb == 1) hipLaunchKernelGGL((k_down_grouped<1, 8>), g, b, lds, st, a, hmax, hmax_sh);
+        else if (nsb == 2) hipLaunchKernelGGL((k_down_grouped<2, 8>), g, b, lds, st, a, hmax, hmax_sh);
+        else hipLaunchKernelGGL((k_down_grouped<4, 8>), g, b, lds, st, a, hmax, hmax_sh);
+    } else {
+        if (nsb == 1) hipLaunchKernelGGL((k_down_grouped<1, 4>), g, b, lds, st, a, hmax, hmax_sh);
+        else if (nsb == 2) hipLaunchKernelGGL((k_down_grouped<2, 4>), g, b, lds, st, a, hmax, hmax_sh);
+        else hipLaunchKernelGGL((k_down_grouped<4, 4>), g, b, lds, st, a, hmax, hmax_sh);
+    }
     return hipGetLastError();
 }
 

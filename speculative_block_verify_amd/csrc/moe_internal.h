@@ -165,6 +165,7 @@ hipError_t launch_down(const DownArgs& a, hipStream_t st, const Timing* t = null
 hipError_t launch_dequant(Fp4Mat m, int n_experts, int rows, int cols, float* out, hipStream_t st);
 
 // Grouped regime (moe_grouped.hip).
+hipError_t launch_router_mfma(const RouterArgs& a, hipStream_t st);  // many rows, plain bf16 x_in only
 hipError_t launch_select_rows(const SelectArgs& a, hipStream_t st);  // ids and w only
 hipError_t launch_group(const GroupArgs& a, hipStream_t st);
 // hmax [T*k][I/64] and hmax_sh [T][Is/64]: max |h| of each token per 64-row slab
