@@ -19,6 +19,9 @@ FLAGS = [
     "-shared",
     # packed fp32 VALU ops stay off on this part (plain float code only)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: no AGPR <-> VGPR copies where a
+    # branch (a second 16-token tile) joins an MFMA chain
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-fvisibility=hidden",
     "-Wall",
     "-Wno-unused-command-line-argument",

@@ -142,6 +142,7 @@ struct Layout {
     float* hmax;            // [R*k][I/64]
     float* hmax_sh;         // [R][Is/64]
     float* o;               // [R*k + R][H]
+    uint16_t* xh;           // fp16 copy of the layer input [R][H]
     int max_tiles;
     size_t bytes;
 };
@@ -172,6 +173,7 @@ Layout layout(const moe_cfg* c, void* base) {
     L.hmax = reinterpret_cast<float*>(take(R * k * ((I + 63) / 64) * 4));
     L.hmax_sh = reinterpret_cast<float*>(take(R * (Is ? (Is + 63) / 64 : 1) * 4));
     L.o = reinterpret_cast<float*>(take((R * k + R) * H * 4));
+    L.xh = reinterpret_cast<uint16_t*>(take(R * H * 2));
     L.bytes = o;
     return L;
 }
@@ -256,6 +258,7 @@ int enqueue_layer_grouped(const moe_cfg* c, const moe_layer_weights* w, const ui
     ra.x_in = x;
     ra.wr = w->router_w;
     ra.logits = L.logits;
+    ra.x_f16 = L.xh;
     ra.K = K; ra.H = c->hidden; ra.E = c->n_experts;
     if ((e = moe::launch_router_mfma(ra, st)) != hipSuccess) return hip_fail(e, "router launch");
 
@@ -274,7 +277,7 @@ int enqueue_layer_grouped(const moe_cfg* c, const moe_layer_weights* w, const ui
 
     const int max_tiles = moe::grouped_max_tiles(K, c->n_experts, c->top_k, has_sh);
     moe::GroupedGuArgs ga{};
-    ga.x = x;
+    ga.x = L.xh;
     ga.gate = mat(w->gate); ga.up = mat(w->up);
     ga.sgate = has_sh ? mat(w->sh_gate) : none;
     ga.sup = has_sh ? mat(w->sh_up) : none;

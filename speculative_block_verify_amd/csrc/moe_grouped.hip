@@ -71,6 +71,20 @@ __global__ __launch_bounds__(kRouterWaves * 64) void k_router_mfma(RouterArgs a)
         w1[s] = *reinterpret_cast<const uint4*>(wr1 + 32 * s);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the MFMAs
+    // the first column of workgroups also writes the fp16 copy of x that the
+    // grouped gate/up kernel stages (bf16 -> fp16 once per row, not per tile)
+    if (a.x_f16 && blockIdx.y == 0) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            uint4 h0, h1;
+            h0.x = bf16pair_to_f16pair(x0[s].x); h0.y = bf16pair_to_f16pair(x0[s].y);
+            h0.z = bf16pair_to_f16pair(x0[s].z); h0.w = bf16pair_to_f16pair(x0[s].w);
+            h1.x = bf16pair_to_f16pair(x1[s].x); h1.y = bf16pair_to_f16pair(x1[s].y);
+            h1.z = bf16pair_to_f16pair(x1[s].z); h1.w = bf16pair_to_f16pair(x1[s].w);
+            if (t0 + i < T) *reinterpret_cast<uint4*>(a.x_f16 + (size_t)(t0 + i) * H + c0 + 32 * s) = h0;
+            if (t0 + 16 + i < T) *reinterpret_cast<uint4*>(a.x_f16 + (size_t)(t0 + 16 + i) * H + c0 + 32 * s) = h1;
+        }
+    }
     f32x4_t acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -212,13 +226,15 @@ __global__ __launch_bounds__(kGGroupThreads) void k_group(GroupArgs a) {
 // tokens (up to 32: two 16-column MFMA tiles).  Lane (i = lane % 16,
 // kb = lane / 16) owns columns [sb*256 + kb*64, +64) of weight row n0 + i in
 // superblock sb (the layout of the verify-width tiles); its weights stream
-// through the superblocks with two superblocks in flight.  The tokens' x
+// through the superblocks with four superblocks in flight.  The tokens' x
 // columns of the current superblock sit in LDS as fp16 (double buffered),
 // rows padded to 528 bytes (16 bytes times an odd number) so the 16 rows an
 // MFMA B read touches fall in distinct bank groups.
 // ---------------------------------------------------------------------------
 
 constexpr int kGXStride = kSbCols + 8;  // halfs per staged token row
+constexpr int kGuMaxItems = 16;          // work items of one persistent gate/up workgroup
+constexpr int kGuGrid = 512;             // persistent gate/up workgroups (two per compute unit)
 
 __device__ __forceinline__ void gg_mfma_sb(const GuSb& r, const _Float16* xb, int ntt, f32x4_t* accg,
                                            f32x4_t* accu) {
@@ -233,99 +249,127 @@ __device__ __forceinline__ void gg_mfma_sb(const GuSb& r, const _Float16* xb, in
         const _Float16 usc = (s < 2) ? u0 : (s < 4) ? u1 : (s < 6) ? u2 : u3;
         const f16x8_t ag = decode8_f16(pick_word(r.g0, r.g1, s), gsc);
         const f16x8_t au = decode8_f16(pick_word(r.u0, r.u1, s), usc);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            if (tt < ntt) {
-                const f16x8_t b = *reinterpret_cast<const f16x8_t*>(xb + (tt * 16 + j) * kGXStride + kb * 64 + 8 * s);
-                accg[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ag, b, accg[tt], 0, 0, 0);
-                accu[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(au, b, accu[tt], 0, 0, 0);
-            }
+        const f16x8_t b0 = *reinterpret_cast<const f16x8_t*>(xb + j * kGXStride + kb * 64 + 8 * s);
+        accg[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ag, b0, accg[0], 0, 0, 0);
+        accu[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(au, b0, accu[0], 0, 0, 0);
+        if (ntt > 1) {
+            const f16x8_t b1 = *reinterpret_cast<const f16x8_t*>(xb + (16 + j) * kGXStride + kb * 64 + 8 * s);
+            accg[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ag, b1, accg[1], 0, 0, 0);
+            accu[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(au, b1, accu[1], 0, 0, 0);
         }
     }
 }
 
 template <int NSB>
-__global__ __launch_bounds__(kBlock) void k_gateup_grouped(GroupedGuArgs a, float* hmax, float* hmax_sh) {
-    __shared__ __align__(16) _Float16 xb[2][kGChunk * kGXStride];
-    __shared__ int s_tok[kGChunk];
-    __shared__ float s_max[kWaves][kGChunk];
+__global__ __launch_bounds__(kBlock, 2) void k_gateup_grouped(GroupedGuArgs a, float* hmax, float* hmax_sh) {
     constexpr int H = NSB * kSbCols;
+    // weight superblocks in registers (RING - 1 in flight ahead of the
+    // MFMAs) and x superblocks loaded ahead of their LDS store; both divide
+    // NSB, so a step's ring slot is fixed by its superblock index alone
+    constexpr int RING = NSB < 4 ? NSB : 4;
+    constexpr int XL = NSB < 2 ? 1 : 2;
+    __shared__ __align__(16) _Float16 xb[2][kGChunk * kGXStride];
+    __shared__ int s_tok[kGuMaxItems][kGChunk];
+    __shared__ int4 s_item[kGuMaxItems];   // {expert or -1 (shared), first asg position, tokens, slab}
+    __shared__ float2 s_ts[kGuMaxItems];   // gate and up tensor scales
+    __shared__ float s_max[kWaves][kGChunk];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int j = lane & 15, q = lane >> 4;
-    // matrix pointers read once; per item the choice selects values
     const uint8_t *const gq_r = a.gate.q, *const gs_r = a.gate.s, *const uq_r = a.up.q, *const us_r = a.up.s;
     const uint8_t *const gq_s = a.sgate.q, *const gs_s = a.sgate.s, *const uq_s = a.sup.q, *const us_s = a.sup.s;
-    const float *const gts_r = a.gate.ts, *const uts_r = a.up.ts, *const gts_s = a.sgate.ts, *const uts_s = a.sup.ts;
     const int I = a.I, Is = a.Is, kk = a.k;
     const int nI = I / kGRows, nIs = max(Is / kGRows, 1);
     const int n_tiles = *a.n_tiles;
     const int n_sh = gq_s ? (a.T + kGChunk - 1) / kGChunk : 0;
     const int n_rt = n_tiles - n_sh;
     const int items = n_rt * nI + n_sh * nIs;
-    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int G = gridDim.x;
+    // this workgroup's items: blockIdx.x + k * G for k < n_my (<= kGuMaxItems by launch)
+    const int n_my = items > (int)blockIdx.x ? min((items - 1 - (int)blockIdx.x) / G + 1, kGuMaxItems) : 0;
+    if (n_my == 0) return;
+
+    // every item's descriptor, tensor scales and token rows into LDS up
+    // front: later lookups are LDS reads, never waits behind weight loads
+    if (tid < n_my) {
+        const int it = blockIdx.x + tid * G;
         const bool routed = it < n_rt * nI;
         const int ti = routed ? it / nI : n_rt + (it - n_rt * nI) / nIs;
         const int slab = routed ? it % nI : (it - n_rt * nI) % nIs;
         const int4 tl = reinterpret_cast<const int4*>(a.tiles)[ti];
-        const int e = routed ? tl.x : 0, p0 = tl.y, cnt = tl.z;
+        const int e = routed ? tl.x : -1;
+        s_item[tid] = make_int4(e, tl.y, tl.z, slab);
+        s_ts[tid] = routed ? make_float2(a.gate.ts[e], a.up.ts[e]) : make_float2(a.sgate.ts[0], a.sup.ts[0]);
+    }
+    __syncthreads();
+    for (int t = tid; t < n_my * kGChunk; t += kBlock) {
+        const int k = t >> 5, m = t & 31;
+        const int4 d = s_item[k];
+        const int pos = d.y + min(m, d.z - 1);
+        s_tok[k][m] = d.x >= 0 ? a.asg[pos] / kk : pos;
+    }
+    __syncthreads();
+
+    // The workgroup's items form one stream of n_my * NSB superblock steps;
+    // weights and x are loaded ahead along that stream, across item
+    // boundaries (past the last item: the last item again, L2 hits).
+    auto load_w = [&](int k, int sb) {
+        const int4 d = s_item[min(k, n_my - 1)];
+        const bool routed = d.x >= 0;
         const int rows = routed ? I : Is;
-        const size_t eq = (size_t)e * rows * (H / 2), es = (size_t)e * rows * (H / 16);
-        const uint8_t* gq = (routed ? gq_r : gq_s) + eq;
-        const uint8_t* gs = (routed ? gs_r : gs_s) + es;
-        const uint8_t* uq = (routed ? uq_r : uq_s) + eq;
-        const uint8_t* us = (routed ? us_r : us_s) + es;
-        const float gts = (routed ? gts_r : gts_s)[e], uts = (routed ? uts_r : uts_s)[e];
-        const int n0 = slab * kGRows + wave * 16;
-
-        // weights of the first two superblocks, then the tile's token rows
-        GuSb w[3];
-        w[0] = gu_load_sb(gq, gs, uq, us, H, n0, 0, true);
-        if (NSB > 1) w[1] = gu_load_sb(gq, gs, uq, us, H, n0, 1, true);
-        if (tid < kGChunk) s_tok[tid] = routed ? a.asg[p0 + min(tid, cnt - 1)] / kk : p0 + min(tid, cnt - 1);
-        __syncthreads();
-
-        // x columns of superblock sb: 32 tokens x 32 pieces of 16 bytes, four
-        // pieces per thread; loads at clamped (valid) rows, zeros stored for
-        // tokens past the tile
-        uint4 xv[4];
-        auto load_x = [&](int sb) {
+        const size_t eq = (size_t)(routed ? d.x : 0) * rows * (H / 2), es = (size_t)(routed ? d.x : 0) * rows * (H / 16);
+        const int n0 = d.w * kGRows + wave * 16;
+        return gu_load_sb((routed ? gq_r : gq_s) + eq, (routed ? gs_r : gs_s) + es, (routed ? uq_r : uq_s) + eq,
+                          (routed ? us_r : us_s) + es, H, n0, sb, true);
+    };
+    // fp16 x columns of superblock sb of item k: 32 tokens x 32 pieces of 16
+    // bytes, four pieces per thread, at the tokens' rows (clamped)
+    auto load_x = [&](int k, int sb, uint4 (&v)[4]) {
+        const int kc = min(k, n_my - 1);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int f = t * kBlock + tid, m = f >> 5, c8 = f & 31;
-                xv[t] = *reinterpret_cast<const uint4*>(a.x + (size_t)s_tok[m] * H + sb * kSbCols + c8 * 8);
-            }
-        };
-        auto store_x = [&](int buf) {
+        for (int t = 0; t < 4; ++t) {
+            const int f = t * kBlock + tid, m = f >> 5, c8 = f & 31;
+            v[t] = *reinterpret_cast<const uint4*>(a.x + (size_t)s_tok[kc][m] * H + sb * kSbCols + c8 * 8);
+        }
+    };
+    // zeros for tokens past the item's tile
+    auto store_x = [&](int buf, int k, const uint4 (&v)[4]) {
+        const int cnt = s_item[min(k, n_my - 1)].z;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int f = t * kBlock + tid, m = f >> 5, c8 = f & 31;
-                uint4 o = make_uint4(0, 0, 0, 0);
-                if (m < cnt) {
-                    o.x = bf16pair_to_f16pair(xv[t].x);
-                    o.y = bf16pair_to_f16pair(xv[t].y);
-                    o.z = bf16pair_to_f16pair(xv[t].z);
-                    o.w = bf16pair_to_f16pair(xv[t].w);
-                }
-                *reinterpret_cast<uint4*>(&xb[buf][m * kGXStride + c8 * 8]) = o;
-            }
-        };
-        load_x(0);
-        store_x(0);
-        __syncthreads();
+        for (int t = 0; t < 4; ++t) {
+            const int f = t * kBlock + tid, m = f >> 5, c8 = f & 31;
+            *reinterpret_cast<uint4*>(&xb[buf][m * kGXStride + c8 * 8]) = m < cnt ? v[t] : make_uint4(0, 0, 0, 0);
+        }
+    };
 
+    GuSb w[RING];
+    uint4 xv[XL][4];
+#pragma unroll
+    for (int p = 0; p < XL; ++p) load_x(p / NSB, p % NSB, xv[p]);
+#pragma unroll
+    for (int p = 0; p < RING - 1; ++p) w[p] = load_w(p / NSB, p % NSB);
+    store_x(0, 0, xv[0]);
+    __syncthreads();
+
+    for (int k = 0; k < n_my; ++k) {
+        const int4 d = s_item[k];
+        const bool routed = d.x >= 0;
+        const int p0 = d.y, cnt = d.z, slab = d.w;
         const int ntt = cnt > 16 ? 2 : 1;
         f32x4_t accg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         f32x4_t accu[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb) {
-            if (sb + 1 < NSB) load_x(sb + 1);
-            if (sb + 2 < NSB) w[(sb + 2) % 3] = gu_load_sb(gq, gs, uq, us, H, n0, sb + 2, true);
-            gg_mfma_sb(w[sb % 3], xb[sb & 1], ntt, accg, accu);
-            if (sb + 1 < NSB) store_x((sb + 1) & 1);
+            load_x(k + (sb + XL) / NSB, (sb + XL) % NSB, xv[(sb + XL) % XL]);
+            if (RING > 1) w[(sb + RING - 1) % RING] = load_w(k + (sb + RING - 1) / NSB, (sb + RING - 1) % NSB);
+            else w[0] = load_w(k, sb);
+            gg_mfma_sb(w[sb % RING], xb[(k * NSB + sb) & 1], ntt, accg, accu);
+            store_x((k * NSB + sb + 1) & 1, k + (sb + 1) / NSB, xv[(sb + 1) % XL]);
             __syncthreads();
         }
 
         // SwiGLU epilogue: lane (j, q) holds rows n0 + 4q .. +3 of token j
+        const float gts = s_ts[k].x, uts = s_ts[k].y;
+        const int n0 = slab * kGRows + wave * 16;
         float* hbase = routed ? a.h : a.h_sh;
         const int hstride = routed ? I : Is;
 #pragma unroll
@@ -667,9 +711,12 @@ hipError_t launch_group(const GroupArgs& a, hipStream_t st) {
 hipError_t launch_gateup_grouped(const GroupedGuArgs& a, float* hmax, float* hmax_sh, int max_tiles,
                                  hipStream_t st) {
     const int per = (a.I > a.Is ? a.I : a.Is) / kGRows;
-    long long items = (long long)max_tiles * per;
-    const int grid = (int)(items < kGMaxGrid ? items : kGMaxGrid);
-    const dim3 g(grid), b(kBlock);
+    const long long items = (long long)max_tiles * per;
+    // persistent workgroups, each walking at most kGuMaxItems items
+    long long grid = items < kGuGrid ? items : kGuGrid;
+    const long long need = (items + kGuMaxItems - 1) / kGuMaxItems;
+    if (grid < need) grid = need;
+    const dim3 g((unsigned)grid), b(kBlock);
     switch (a.H) {
         case 256: hipLaunchKernelGGL(k_gateup_grouped<1>, g, b, 0, st, a, hmax, hmax_sh); break;
         case 512: hipLaunchKernelGGL(k_gateup_grouped<2>, g, b, 0, st, a, hmax, hmax_sh); break;

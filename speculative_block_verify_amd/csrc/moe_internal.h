@@ -58,6 +58,7 @@ struct RouterArgs {
     float eps;
     const uint16_t* wr;     // bf16 [E][H]
     float* logits;          // [K][E]
+    uint16_t* x_f16;        // fp16 bit patterns [K][H] of x_in, or nullptr (many-row router only)
     int K, H, E;
 };
 
@@ -112,7 +113,7 @@ struct GroupArgs {
 };
 
 struct GroupedGuArgs {
-    const uint16_t* x;      // bf16 [T][H]
+    const uint16_t* x;      // fp16 bit patterns [T][H] (the router's copy of the layer input)
     Fp4Mat gate, up;        // [E][I][H/2]
     Fp4Mat sgate, sup;      // [1][Is][H/2] (q == nullptr: no shared expert)
     const int32_t* uniq;
