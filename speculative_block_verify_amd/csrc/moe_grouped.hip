@@ -71,9 +71,10 @@ __global__ __launch_bounds__(kRouterWaves * 64) void k_router_mfma(RouterArgs a)
         w1[s] = *reinterpret_cast<const uint4*>(wr1 + 32 * s);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the MFMAs
-    // the first column of workgroups also writes the fp16 copy of x that the
-    // grouped gate/up kernel stages (bf16 -> fp16 once per row, not per tile)
-    if (a.x_f16 && blockIdx.y == 0) {
+    // the fp16 copy of x that the grouped gate/up kernel stages (bf16 -> fp16
+    // once per row, not per tile): each wave's column range is written by
+    // one workgroup of the row tile's column of workgroups
+    if (a.x_f16 && wave % gridDim.y == blockIdx.y) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             uint4 h0, h1;
@@ -568,8 +569,8 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedDownArgs a, cons
 // k_combine: one workgroup per row
 // ---------------------------------------------------------------------------
 
-constexpr int kCombineMaxCols = 2048 / kBlock;  // columns per thread at the largest hidden size
-constexpr int kCombineBatch = 4;                // slots whose rows are loaded together
+constexpr int kCombineV4 = 2048 / 4 / kBlock;  // float4 per thread at the largest hidden size
+constexpr int kCombineBatch = 8;                // slots whose rows are loaded together
 
 __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a) {
     __shared__ float s_w[kMaxTopK];
@@ -577,48 +578,71 @@ __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a) {
     __shared__ float s_ss[kWaves];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = blockIdx.x, H = a.H, k = a.k;
-    const int ncol = H / kBlock;
+    const int n4 = H / 4;  // float4 per row; thread tid owns float4 t * kBlock + tid
     if (tid < k) {
         s_w[tid] = a.w[(size_t)r * k + tid];
         s_o[tid] = a.inv[(size_t)r * k + tid];
     }
-    __syncthreads();
-    // y = rs * sum_j w_j o_j (j in rank order) + shared (+ residual)
-    float acc[kCombineMaxCols];
+    // the shared expert's row is requested with the first batch of slots
+    float4 sh[kCombineV4];
 #pragma unroll
-    for (int t = 0; t < kCombineMaxCols; ++t) acc[t] = 0.0f;
+    for (int t = 0; t < kCombineV4; ++t) {
+        const int i4 = min(t * kBlock + tid, n4 - 1);
+        sh[t] = a.has_shared ? reinterpret_cast<const float4*>(a.o + ((size_t)a.T * k + r) * H)[i4]
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+    // y = rs * sum_j w_j o_j (j in rank order) + shared (+ residual), per element
+    float4 acc[kCombineV4];
+#pragma unroll
+    for (int t = 0; t < kCombineV4; ++t) acc[t] = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
-        float ov[kCombineBatch][kCombineMaxCols];
+        float4 ov[kCombineBatch][kCombineV4];
 #pragma unroll
         for (int b = 0; b < kCombineBatch; ++b) {
-            const int jj = min(j0 + b, k - 1);
-            const float* orow = a.o + (size_t)s_o[jj] * H;
+            const float4* orow = reinterpret_cast<const float4*>(a.o + (size_t)s_o[min(j0 + b, k - 1)] * H);
 #pragma unroll
-            for (int t = 0; t < kCombineMaxCols; ++t) ov[b][t] = (t < ncol) ? orow[t * kBlock + tid] : 0.0f;
+            for (int t = 0; t < kCombineV4; ++t) ov[b][t] = orow[min(t * kBlock + tid, n4 - 1)];
         }
 #pragma unroll
         for (int b = 0; b < kCombineBatch; ++b) {
             if (j0 + b < k) {
                 const float wv = s_w[j0 + b];
 #pragma unroll
-                for (int t = 0; t < kCombineMaxCols; ++t) acc[t] = fmaf(wv, ov[b][t], acc[t]);
+                for (int t = 0; t < kCombineV4; ++t) {
+                    acc[t].x = fmaf(wv, ov[b][t].x, acc[t].x);
+                    acc[t].y = fmaf(wv, ov[b][t].y, acc[t].y);
+                    acc[t].z = fmaf(wv, ov[b][t].z, acc[t].z);
+                    acc[t].w = fmaf(wv, ov[b][t].w, acc[t].w);
+                }
             }
         }
     }
-    float yv[kCombineMaxCols];
+    float4 yv[kCombineV4];
     float ss = 0.0f;
 #pragma unroll
-    for (int t = 0; t < kCombineMaxCols; ++t) {
-        yv[t] = 0.0f;
-        if (t < ncol) {
-            const int c = t * kBlock + tid;
-            float y = a.rs * acc[t];
-            if (a.has_shared) y += a.o[((size_t)a.T * k + r) * H + c];
-            if (a.residual) y += bf16_to_f32(a.residual[(size_t)r * H + c]);
-            a.y32[(size_t)r * H + c] = y;
-            if (a.y) a.y[(size_t)r * H + c] = f32_to_bf16_rne(y);
+    for (int t = 0; t < kCombineV4; ++t) {
+        yv[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int i4 = t * kBlock + tid;
+        if (i4 < n4) {
+            const size_t c = (size_t)r * H + 4 * i4;
+            float4 y;
+            y.x = a.rs * acc[t].x; y.y = a.rs * acc[t].y; y.z = a.rs * acc[t].z; y.w = a.rs * acc[t].w;
+            if (a.has_shared) { y.x += sh[t].x; y.y += sh[t].y; y.z += sh[t].z; y.w += sh[t].w; }
+            if (a.residual) {
+                const uint2 rb = *reinterpret_cast<const uint2*>(a.residual + c);
+                y.x += __uint_as_float(rb.x << 16); y.y += __uint_as_float(rb.x & 0xFFFF0000u);
+                y.z += __uint_as_float(rb.y << 16); y.w += __uint_as_float(rb.y & 0xFFFF0000u);
+            }
+            *reinterpret_cast<float4*>(a.y32 + c) = y;
+            if (a.y) {
+                uint2 o;
+                o.x = (uint32_t)f32_to_bf16_rne(y.x) | ((uint32_t)f32_to_bf16_rne(y.y) << 16);
+                o.y = (uint32_t)f32_to_bf16_rne(y.z) | ((uint32_t)f32_to_bf16_rne(y.w) << 16);
+                *reinterpret_cast<uint2*>(a.y + c) = o;
+            }
             yv[t] = y;
-            ss = fmaf(y, y, ss);
+            ss = fmaf(y.x, y.x, ss); ss = fmaf(y.y, y.y, ss); ss = fmaf(y.z, y.z, ss); ss = fmaf(y.w, y.w, ss);
         }
     }
     if (!a.x_next) return;
@@ -629,8 +653,15 @@ __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a) {
     const float tot = (s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3]);
     const float sc = 1.0f / sqrtf(tot / (float)H + a.eps);
 #pragma unroll
-    for (int t = 0; t < kCombineMaxCols; ++t)
-        if (t < ncol) a.x_next[(size_t)r * H + t * kBlock + tid] = f32_to_bf16_rne(yv[t] * sc);
+    for (int t = 0; t < kCombineV4; ++t) {
+        const int i4 = t * kBlock + tid;
+        if (i4 < n4) {
+            uint2 o;
+            o.x = (uint32_t)f32_to_bf16_rne(yv[t].x * sc) | ((uint32_t)f32_to_bf16_rne(yv[t].y * sc) << 16);
+            o.y = (uint32_t)f32_to_bf16_rne(yv[t].z * sc) | ((uint32_t)f32_to_bf16_rne(yv[t].w * sc) << 16);
+            *reinterpret_cast<uint2*>(a.x_next + (size_t)r * H + 4 * i4) = o;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
