@@ -142,6 +142,15 @@ __global__ __launch_bounds__(kBlock) void k_select_rows(SelectArgs a) {
     }
 }
 
+// The grouping kernel's dynamic LDS: 4 bytes per (expert, 32-row word) of
+// bitmap, plus 2 bytes of prefix count when that still fits.
+constexpr int kGroupMaxLds = kMaxExperts * (kMaxGroupedRows / 32) * 4;
+constexpr int kGroupLdsSlots = 4096;  // slot lists up to this length are ordered in LDS
+constexpr int kGroupRegSlots = 8;     // slots per grouping thread whose expert ids stay in registers
+__host__ __device__ inline bool group_pc_fits(int T, int E) {
+    return (size_t)E * ((T + 31) / 32) * 6 <= (size_t)kGroupMaxLds;
+}
+
 // ---------------------------------------------------------------------------
 // k_group: CSR + tile list (one workgroup of kGGroupThreads)
 //
@@ -152,22 +161,47 @@ __global__ __launch_bounds__(kBlock) void k_select_rows(SelectArgs a) {
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(kGGroupThreads) void k_group(GroupArgs a) {
-    extern __shared__ uint32_t rm[];  // [E][W]
+    // [E][W] row bitmaps, then (when group_pc_fits) [E][W] 16-bit prefix
+    // popcounts: slots of expert e in rows below word w
+    extern __shared__ uint32_t rm[];
     __shared__ int s_cstart[kMaxExperts];
     __shared__ int s_wsum[kGGroupThreads / 64][3];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int T = a.T, E = a.E, k = a.k, n = T * k, W = (T + 31) >> 5;
+    const bool use_pc = group_pc_fits(T, E);
+    uint16_t* pc = reinterpret_cast<uint16_t*>(rm + E * W);
+    // the slot list is assembled in the static LDS buffer when it fits
+    __shared__ int s_asg[kGroupLdsSlots];
+    const bool use_lds_asg = n <= kGroupLdsSlots;
+    // this thread's slots s = tid + i * kGGroupThreads; the expert ids of the
+    // first kGroupRegSlots stay in registers, later ones are read again
+    constexpr int kSlots = kMaxGroupedRows * kMaxTopK / kGGroupThreads;
+    int ev[kGroupRegSlots];
+#pragma unroll
+    for (int i = 0; i < kGroupRegSlots; ++i) {
+        const int s = tid + i * kGGroupThreads;
+        ev[i] = s < n ? a.ids[s] : 0;
+    }
+    auto expert_of = [&](int i, int s) { return i < kGroupRegSlots ? ev[i < kGroupRegSlots ? i : 0] : a.ids[s]; };
     for (int i = tid; i < E * W; i += kGGroupThreads) rm[i] = 0u;
     __syncthreads();
-    for (int s = tid; s < n; s += kGGroupThreads) {
-        const int e = a.ids[s], r = s / k;
-        atomicOr(&rm[e * W + (r >> 5)], 1u << (r & 31));
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) {
+        const int s = tid + i * kGGroupThreads;
+        if (s < n) {
+            const int r = s / k;
+            atomicOr(&rm[expert_of(i, s) * W + (r >> 5)], 1u << (r & 31));
+        }
     }
     __syncthreads();
-    // thread e (E <= kGGroupThreads): slot count, used flag, tile count
+    // thread e (E <= kGGroupThreads): slot count (and prefix per word), used
+    // flag, tile count
     int c = 0;
     if (tid < E)
-        for (int w = 0; w < W; ++w) c += __builtin_popcount(rm[tid * W + w]);
+        for (int w = 0; w < W; ++w) {
+            if (use_pc) pc[tid * W + w] = (uint16_t)c;
+            c += __builtin_popcount(rm[tid * W + w]);
+        }
     const int f = c > 0, nt = (c + kGChunk - 1) / kGChunk;
     const int ci = wave_incl_scan(c), fi = wave_incl_scan(f), ti = wave_incl_scan(nt);
     if (lane == 63) {
@@ -208,14 +242,30 @@ __global__ __launch_bounds__(kGGroupThreads) void k_group(GroupArgs a) {
         *a.n_tiles = NT + nsh;
     }
     __syncthreads();
-    for (int s = tid; s < n; s += kGGroupThreads) {
-        const int e = a.ids[s], r = s / k;
-        const uint32_t* m = rm + e * W;
-        int rank = __builtin_popcount(m[r >> 5] & ((1u << (r & 31)) - 1u));
-        for (int w = 0; w < (r >> 5); ++w) rank += __builtin_popcount(m[w]);
-        const int pos = s_cstart[e] + rank;
-        a.asg[pos] = s;
-        a.inv[s] = pos;
+    // rank of slot (r, j) inside its expert = slots of the expert in rows
+    // below the word holding row r, plus the bits below r in that word
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) {
+        const int s = tid + i * kGGroupThreads;
+        if (s < n) {
+            const int e = expert_of(i, s), r = s / k;
+            const uint32_t* m = rm + e * W;
+            int rank = __builtin_popcount(m[r >> 5] & ((1u << (r & 31)) - 1u));
+            if (use_pc) {
+                rank += pc[e * W + (r >> 5)];
+            } else {
+                for (int w = 0; w < (r >> 5); ++w) rank += __builtin_popcount(m[w]);
+            }
+            const int pos = s_cstart[e] + rank;
+            if (use_lds_asg) s_asg[pos] = s;
+            else a.asg[pos] = s;
+            a.inv[s] = pos;
+        }
+    }
+    if (use_lds_asg) {
+        // the slot list leaves in position order: contiguous stores
+        __syncthreads();
+        for (int p = tid; p < n; p += kGGroupThreads) a.asg[p] = s_asg[p];
     }
 }
 
@@ -676,7 +726,7 @@ hipError_t launch_plain(Kern k, dim3 grid, dim3 block, size_t smem, hipStream_t 
     return hipGetLastError();
 }
 
-size_t group_lds(int T, int E) { return (size_t)E * ((T + 31) / 32) * 4; }
+size_t group_lds(int T, int E) { return (size_t)E * ((T + 31) / 32) * (group_pc_fits(T, E) ? 6 : 4); }
 // superblocks of the longest staged h row, and the grouped down kernel's
 // output slabs per work item
 int down_nsb(int I, int Is) { return ((I > Is ? I : Is) + kSbCols - 1) / kSbCols; }
@@ -687,7 +737,6 @@ size_t down_lds(int I, int Is) {
 }
 
 // largest dynamic LDS each kernel is launched with (static LDS comes on top)
-constexpr int kGroupMaxLds = kMaxExperts * (kMaxGroupedRows / 32) * 4;
 constexpr int kGDownMaxLds = 2 * kGChunk * (kGMaxSb * kSbCols + 8) * 2;
 
 }  // namespace
