@@ -513,38 +513,53 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedDownArgs a, cons
                 c.sc[sb] = *reinterpret_cast<const uint32_t*>(ms + row * (cols / 16) + col / 16);
             }
         };
-        DownCodes<NSB> cA, cB;
-        load_codes(0, cA);
-
-        // per-token scale exponent from the gate/up kernel's max |h| per slab
-        if (tid < kGChunk) {
-            float mx = 0.0f;
-            if (tid < cnt) {
-                const float* hm = routed ? hmax + (size_t)(p0 + tid) * nslab : hmax_sh + (size_t)(p0 + tid) * nslab;
-                for (int t = 0; t < nslab; ++t) mx = fmaxf(mx, hm[t]);
-            }
-            s_sig[tid] = (mx > 0.0f) ? ilogbf(mx) - 14 : 0;
-        }
-        __syncthreads();
-        // stage: one superblock (32 rows x 256 columns = 2048 float4) per pass
-        const float* hrow0 = routed ? a.h + (size_t)p0 * I : a.h_sh + (size_t)p0 * Is;
+        // The item's loads in the order they are consumed (vector loads
+        // complete in issue order): max |h| entries, the tile's h rows, then
+        // the codes of the first slab.  Entry (token m, slab sl) of max |h|
+        // goes to thread 16m + sl of each half of the workgroup (clamped).
+        const float* hmb = routed ? hmax : hmax_sh;
+        float hmv[2];
 #pragma unroll
-        for (int sb = 0; sb < NSB; ++sb) {
-            float4 v[8];
+        for (int u = 0; u < 2; ++u) {
+            const int idx = u * kBlock + tid, m = idx >> 4, sl = idx & 15;
+            hmv[u] = hmb[(size_t)(p0 + min(m, cnt - 1)) * nslab + min(sl, nslab - 1)];
+        }
+        const float* hrow0 = routed ? a.h + (size_t)p0 * I : a.h_sh + (size_t)p0 * Is;
+        float4 v[NSB][8];  // one superblock is 32 rows x 256 columns = 2048 float4
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const int f = t * kBlock + tid, m = f >> 6, c4 = f & 63;
                 const int col = min(sb * kSbCols + c4 * 4, cols - 4);
-                v[t] = *reinterpret_cast<const float4*>(hrow0 + (size_t)min(m, cnt - 1) * cols + col);
+                v[sb][t] = *reinterpret_cast<const float4*>(hrow0 + (size_t)min(m, cnt - 1) * cols + col);
             }
+        DownCodes<NSB> cA, cB;
+        load_codes(0, cA);
+
+        // per-token scale exponent: max over the token's slabs (16 lanes)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int idx = u * kBlock + tid, m = idx >> 4, sl = idx & 15;
+            float mx = (m < cnt && sl < nslab) ? hmv[u] : 0.0f;
+            mx = fmaxf(mx, __shfl_xor(mx, 8, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 4, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 2, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 1, 16));
+            if (sl == 0) s_sig[m] = (mx > 0.0f) ? ilogbf(mx) - 14 : 0;
+        }
+        __syncthreads();
+        // stage h as the fp16 pair, zero past the row's length and the tokens
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) {
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const int f = t * kBlock + tid, m = f >> 6, c4 = f & 63;
                 const int col = sb * kSbCols + c4 * 4;
                 const int sg = -s_sig[m];
                 const bool live = m < cnt && col < cols;
-                const float x0 = live ? ldexpf(v[t].x, sg) : 0.f, x1 = live ? ldexpf(v[t].y, sg) : 0.f;
-                const float x2 = live ? ldexpf(v[t].z, sg) : 0.f, x3 = live ? ldexpf(v[t].w, sg) : 0.f;
+                const float x0 = live ? ldexpf(v[sb][t].x, sg) : 0.f, x1 = live ? ldexpf(v[sb][t].y, sg) : 0.f;
+                const float x2 = live ? ldexpf(v[sb][t].z, sg) : 0.f, x3 = live ? ldexpf(v[sb][t].w, sg) : 0.f;
                 const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1, h2 = (_Float16)x2, h3 = (_Float16)x3;
                 f16x2_t a01 = {h0, h1}, a23 = {h2, h3};
                 f16x2_t b01 = {(_Float16)(x0 - (float)h0), (_Float16)(x1 - (float)h1)};
