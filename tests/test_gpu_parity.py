@@ -152,7 +152,7 @@ def test_layer_full_size_k2():
     _layer_case(inputs.LAGUNA, 2, 7, label="full")
 
 
-@pytest.mark.parametrize("K", [1, 4, 16])
+@pytest.mark.parametrize("K", [1, 4, 8, 16])
 def test_layer_full_size_k_sweep_correlated_rows(K):
     x = inputs.gen_x_correlated(K, inputs.LAGUNA.hidden, 31 + K, device=DEV)
     gpu, _, _ = _layer_case(inputs.LAGUNA, K, 31 + K, x=x, label="ksweep")

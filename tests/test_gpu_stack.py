@@ -59,6 +59,13 @@ def test_stack_full_size_4_layers_k2():
     _stack_case(inputs.LAGUNA, 4, 2, 9, "full-4", 4)
 
 
+@pytest.mark.parametrize("K", [1, 8, 16])
+def test_stack_full_size_6_layers_row_counts(K):
+    # verify widths other than the benchmark's two rows, through the RMSNorm
+    # glue (sum-of-squares partials of every row) and the stack entry point
+    _stack_case(inputs.LAGUNA, 6, K, 40 + K, "full-6-K%d" % K, 6)
+
+
 def test_stack_full_size_40_layers_graph_matches_direct_and_oracle():
     """The benchmark's configuration: 40 full-size layers, K = 2, launched as
     a captured graph.  The graph's output must equal the direct call bit for
