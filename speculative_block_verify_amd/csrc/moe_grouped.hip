@@ -35,8 +35,9 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // k_router_mfma: logits = x Wr^T for many rows on the matrix cores
 //
-// Workgroup tile: 32 rows x 32 experts, 8 waves; wave w sums the columns
-// [w*H/8, (w+1)*H/8) for the whole tile (four 16x16 accumulators), with
+// Workgroup tile: 32 rows x 16 experts (a grid that covers every compute
+// unit at 512 rows), 8 waves; wave w sums the columns [w*H/8, (w+1)*H/8)
+// for the whole tile (two 16x16 accumulators), with
 // every operand load of the wave issued before its first MFMA, and the eight
 // partial tiles are added in wave order through LDS.  MFMA step over 32
 // columns c..c+31: lane (i, kb) feeds row i's columns c + 8kb .. +7 of x as
@@ -51,24 +52,22 @@ constexpr int kRouterWaves = 8;
 
 template <int H>
 __global__ __launch_bounds__(kRouterWaves * 64) void k_router_mfma(RouterArgs a) {
-    __shared__ f32x4_t part[kRouterWaves - 1][4][64];
+    __shared__ f32x4_t part[kRouterWaves - 1][2][64];
     constexpr int NS = H / kRouterWaves / 32;  // MFMA steps per wave
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i = lane & 15, kb = lane >> 4;
     const int T = a.K, E = a.E;
-    const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
+    const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 16;
     const int c0 = wave * (H / kRouterWaves) + 8 * kb;
     const uint16_t* xr0 = a.x_in + (size_t)min(t0 + i, T - 1) * H + c0;
     const uint16_t* xr1 = a.x_in + (size_t)min(t0 + 16 + i, T - 1) * H + c0;
     const uint16_t* wr0 = a.wr + (size_t)min(e0 + i, E - 1) * H + c0;
-    const uint16_t* wr1 = a.wr + (size_t)min(e0 + 16 + i, E - 1) * H + c0;
-    uint4 x0[NS], x1[NS], w0[NS], w1[NS];
+    uint4 x0[NS], x1[NS], w0[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         x0[s] = *reinterpret_cast<const uint4*>(xr0 + 32 * s);
         x1[s] = *reinterpret_cast<const uint4*>(xr1 + 32 * s);
         w0[s] = *reinterpret_cast<const uint4*>(wr0 + 32 * s);
-        w1[s] = *reinterpret_cast<const uint4*>(wr1 + 32 * s);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the MFMAs
     // the fp16 copy of x that the grouped gate/up kernel stages (bf16 -> fp16
@@ -86,34 +85,32 @@ __global__ __launch_bounds__(kRouterWaves * 64) void k_router_mfma(RouterArgs a)
             if (t0 + 16 + i < T) *reinterpret_cast<uint4*>(a.x_f16 + (size_t)(t0 + 16 + i) * H + c0 + 32 * s) = h1;
         }
     }
-    f32x4_t acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, x0[s]), a1 = __builtin_bit_cast(bf16x8_t, x1[s]);
-        const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, w0[s]), b1 = __builtin_bit_cast(bf16x8_t, w1[s]);
+        const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, w0[s]);
         acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b1, acc[1], 0, 0, 0);
-        acc[2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b0, acc[2], 0, 0, 0);
-        acc[3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[3], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b0, acc[1], 0, 0, 0);
     }
     if (wave > 0) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) part[wave - 1][t][lane] = acc[t];
+        for (int t = 0; t < 2; ++t) part[wave - 1][t][lane] = acc[t];
     }
     __syncthreads();
     if (wave == 0) {
-        // accumulator t = 2 * (row half) + (expert half); lane (j = lane % 16,
-        // q = lane / 16) holds rows 4q .. 4q+3 of expert column j
+        // accumulator t = row half; lane (j = lane % 16, q = lane / 16) holds
+        // rows 4q .. 4q+3 of expert column j
         const int j = lane & 15, q = lane >> 4;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < 2; ++t) {
             f32x4_t v = acc[t];
 #pragma unroll
             for (int w = 0; w < kRouterWaves - 1; ++w) v += part[w][t][lane];
-            const int e = e0 + 16 * (t & 1) + j;
+            const int e = e0 + j;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = t0 + 16 * (t >> 1) + 4 * q + r;
+                const int row = t0 + 16 * t + 4 * q + r;
                 if (row < T && e < E) a.logits[(size_t)row * E + e] = v[r];
             }
         }
@@ -784,7 +781,7 @@ hipError_t init_grouped_kernels() {
 }
 
 hipError_t launch_router_mfma(const RouterArgs& a, hipStream_t st) {
-    const dim3 g((a.K + 31) / 32, (a.E + 31) / 32), b(kRouterWaves * 64);
+    const dim3 g((a.K + 31) / 32, (a.E + 15) / 16), b(kRouterWaves * 64);
     switch (a.H) {
         case 256: return launch_plain(k_router_mfma<256>, g, b, 0, st, a);
         case 512: return launch_plain(k_router_mfma<512>, g, b, 0, st, a);
