@@ -192,8 +192,10 @@ struct LayerIO {
     uint16_t* y;             // bf16 output or nullptr
 };
 
+// next_router: the router rows of the layer that follows in a stack (the down
+// kernel requests them ahead of that layer's router launch), or nullptr.
 int enqueue_layer(const moe_cfg* c, const moe_layer_weights* w, const LayerIO& io, int K, const Layout& L,
-                  hipStream_t st, const moe::Timing* tm = nullptr) {
+                  hipStream_t st, const moe::Timing* tm = nullptr, const uint16_t* next_router = nullptr) {
     hipError_t e;
     const bool has_sh = c->shared_inter > 0;
     const moe::Fp4Mat none{nullptr, nullptr, nullptr};
@@ -239,6 +241,8 @@ int enqueue_layer(const moe_cfg* c, const moe_layer_weights* w, const LayerIO& i
     da.ssq = L.ssq;
     da.K = K; da.H = c->hidden; da.I = c->inter; da.Is = c->shared_inter; da.k = c->top_k;
     da.rs = c->routed_scale;
+    da.prefetch = reinterpret_cast<const uint8_t*>(next_router);
+    da.prefetch_bytes = next_router ? 2 * c->n_experts * c->hidden : 0;
     if ((e = moe::launch_down(da, st, tm ? &tm[2] : nullptr)) != hipSuccess) return hip_fail(e, "down launch");
     return MOE_OK;
 }
@@ -378,7 +382,8 @@ int enqueue_stack(const moe_cfg* c, const moe_layer_weights* layers, int n_layer
         io.residual = nullptr;
         io.y32 = last ? (y32 ? y32 : L.ybuf) : L.ybuf;
         io.y = last ? y : nullptr;
-        int rc = enqueue_layer(c, &layers[l], io, K, L, st, tm ? tm + 3 * l : nullptr);
+        int rc = enqueue_layer(c, &layers[l], io, K, L, st, tm ? tm + 3 * l : nullptr,
+                               last ? nullptr : layers[l + 1].router_w);
         if (rc) return rc;
         rc = copy_debug(c, dbg, l, K, L, l == 0 ? x : L.xbuf, io.y32, st);
         if (rc) return rc;

@@ -193,6 +193,18 @@ __device__ __forceinline__ int lanes_below(unsigned long long m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Selection key of expert e with router logit l, as an order-preserving
+// integer: the logit (softmax scoring) or sigmoid(l) + bias[e] (sigmoid
+// scoring, the router tail of PR #844 section 4).
+__device__ __forceinline__ uint32_t select_key(const SelectArgs& a, float l, int e) {
+    float key = l;
+    if (a.score_fn == 1) {
+        const float sig = (float)(1.0 / (1.0 + exp(-(double)l)));
+        key = sig + a.bias[e];
+    }
+    return key_bits(key);
+}
+
 // Top-k of row r by (key desc, index asc) with one wave.  Lane l owns the P
 // experts l*P .. l*P+P-1 (contiguous) and keeps them sorted; each round takes
 // the wave maximum of the lanes' heads.  Among equal keys the lowest lane
@@ -209,13 +221,7 @@ __device__ void wave_topk(const SelectArgs& a, const float* lr, int r, SelectSme
         const int e = lane * P + p;
         uint32_t v = 0;
         if (e < E) {
-            const float l = lr[e];
-            float key = l;
-            if (a.score_fn == 1) {
-                const float sig = (float)(1.0 / (1.0 + exp(-(double)l)));
-                key = sig + a.bias[e];
-            }
-            v = key_bits(key);
+            v = select_key(a, lr[e], e);
         }
         sk[p] = v;
         si[p] = p;

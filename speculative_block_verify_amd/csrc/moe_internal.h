@@ -68,7 +68,7 @@ struct GateUpArgs {
     SelectArgs sel;         // its outputs are written by the first routed workgroup only
     const uint16_t* x;      // bf16 [K][H]
     Fp4Mat gate, up;        // [E][I][H/2]
-    float* h;               // [K*k][I], indexed by slot r*k+j
+    float* h;               // [K*k][I], rows by position in the canonical dedup order
     Fp4Mat sgate, sup;      // [1][Is][H/2] (q == nullptr: no shared expert)
     float* h_sh;            // [K][Is]
     int K, H, I, Is;
@@ -83,12 +83,14 @@ struct DownArgs {
     const int32_t* inv;
     const int32_t* asg;
     const float* w;         // [K][k]
-    const float* h;         // [K*k][I] by slot
+    const float* h;         // [K*k][I], rows by dedup position
     const float* h_sh;
     const uint16_t* residual;  // bf16 [K][H] or nullptr
     float* y32;             // [K][H]
     uint16_t* y;            // bf16 [K][H] or nullptr
     float* ssq;             // [K][H / kDownRowsPerBlock] per-workgroup sums of y^2
+    const uint8_t* prefetch;   // bytes the next launch reads first (the next layer's router), or nullptr
+    int prefetch_bytes;        // multiple of 16
     int K, H, I, Is, k;
     float rs;
 };

@@ -466,9 +466,10 @@ __global__ __launch_bounds__(kBlock) void k_router(RouterArgs a) {
 // (slot r*k+j, 16 intermediate rows).  An item is done by the slot of the
 // first row that selected its expert, for every row that selected it, so
 // each unique expert is streamed once; items of later rows' slots of the
-// same expert are skipped.  h rows are indexed by slot.  The first routed
-// workgroup also writes the canonical dedup CSR (for the down kernel) while
-// its own weight loads are in flight.
+// same expert are skipped.  h rows are indexed by position in the canonical
+// dedup order (expert ascending, then row), which each item derives from the
+// selection in LDS.  The first routed workgroup also writes the canonical
+// dedup CSR (for the down kernel) while its own weight loads are in flight.
 // ---------------------------------------------------------------------------
 
 __host__ __device__ constexpr size_t gateup_smem_bytes(int K, int E, int H) {
@@ -479,13 +480,12 @@ template <int P>
 __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_xrows[kWaves][kMaxRows];
-    __shared__ int s_hrows[kWaves][kMaxRows];
     SelectSmem& sm = *reinterpret_cast<SelectSmem*>(smem);
     float* lg = reinterpret_cast<float*>(smem + (sizeof(SelectSmem) + 15) / 16 * 16);
     _Float16* xh = reinterpret_cast<_Float16*>(smem + select_smem_bytes(a.K, a.sel.E));
     float* red = reinterpret_cast<float*>(smem + select_smem_bytes(a.K, a.sel.E) + (size_t)a.K * xh_row_stride(a.H) * 2);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int H = a.H, K = a.K, k = a.sel.k, I = a.I;
+    const int H = a.H, K = a.K, k = a.sel.k, I = a.I, n = K * k;
     // routed workgroups first (dispatched first, two per compute unit), the
     // shared expert's Is/16 tiles last
     const int n_sh = a.sgate.q ? a.Is / kTileRows : 0;
@@ -512,41 +512,42 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
     const int step = shared_blk ? 1 : n_rb;
     bool published = shared_blk || rb != 0;
     for (int it = shared_blk ? 0 : rb; it < items; it += step) {
-        int n0, m_cnt, e = 0;
+        int n0, m_cnt, e = 0, off_e = 0;
         bool owner = true;
         const int* xrows = nullptr;
-        const int* hrows = nullptr;
         if (shared_blk) {
             n0 = sh_tile * kTileRows;
             m_cnt = K;
         } else {
-            const int s = it / nsr, r = s / k;
+            const int s = it / nsr;
             e = sm.sel[s];
             n0 = (it % nsr) * kTileRows;
-            // rows that selected e (every wave computes the same mask)
-            bool has = false;
-            int jj = 0;
-            if (lane < K)
-                for (int j = 0; j < k; ++j)
-                    if (sm.sel[lane * k + j] == e) { has = true; jj = j; }
-            const unsigned long long mask = __ballot(has);
-            owner = (__ffsll((long long)mask) - 1) == r;
+            // Every slot compared with e, one slot per lane (every wave
+            // computes the same masks): the first slot of e, its slots in
+            // ascending order (one per row that selected it), and the number
+            // of slots whose expert is below e, which is where e's rows start
+            // in the canonical dedup order.  h rows are written there, so the
+            // down kernel reads them without the dedup lists.
+            int first = -1, cnt = 0;
+            for (int b = 0; b < n; b += 64) {
+                const int v = (b + lane < n) ? sm.sel[b + lane] : 0x7fffffff;
+                const unsigned long long meq = __ballot(v == e);
+                off_e += __popcll(__ballot(v < e));
+                if (v == e) s_xrows[wave][cnt + lanes_below(meq)] = (b + lane) / k;
+                if (first < 0 && meq) first = b + __builtin_ctzll(meq);
+                cnt += __popcll(meq);
+            }
+            owner = first == s;  // the item belongs to e's first slot
             if (owner) {
                 const size_t eq = (size_t)e * I * (H / 2), es = (size_t)e * I * (H / 16);
                 R = gu_load(a.gate.q + eq, a.gate.s + es, a.up.q + eq, a.up.s + es, H, n0);
                 gts = a.gate.ts[e];
                 uts = a.up.ts[e];
-                m_cnt = __popcll(mask);
-                if (has) {
-                    const int pos = lanes_below(mask);
-                    s_xrows[wave][pos] = lane;
-                    s_hrows[wave][pos] = lane * k + jj;
-                }
+                m_cnt = cnt;
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 xrows = s_xrows[wave];
-                hrows = s_hrows[wave];
             }
         }
         if (!published) {
@@ -554,7 +555,8 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
             published = true;
         }
         if (!owner) continue;
-        gu_compute(R, gts, uts, H, n0, xh, m_cnt, xrows, hrows, shared_blk ? a.h_sh : a.h, shared_blk ? a.Is : I, red);
+        gu_compute(R, gts, uts, H, n0, xh, m_cnt, xrows, nullptr,
+                   shared_blk ? a.h_sh : a.h + (size_t)off_e * I, shared_blk ? a.Is : I, red);
         __syncthreads();
     }
     if (!published) dedup_publish(a.sel, sm);
@@ -568,15 +570,14 @@ constexpr int kDownWaves = kDownThreads / 64;
 constexpr int kDownBatch = 6;  // tasks per wave whose codes are in flight together
 
 // The h rows are processed in chunks that fit kDownHLdsBytes: positions
-// 0..n-1 are the routed slots in dedup order (h row asg[p], length I),
-// n..n+K-1 the shared expert's rows (length Is).
+// 0..n-1 are the routed slots in dedup order (h row p, length I), n..n+K-1
+// the shared expert's rows (length Is).
 __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
     constexpr int NH = kDownRowsPerBlock;
     __shared__ float so[(kMaxSlots + kMaxRows) * NH];
     __shared__ int s_uniq[kMaxSlots];
     __shared__ int s_off[kMaxSlots + 1];
     __shared__ int s_inv[kMaxSlots];
-    __shared__ int s_asg[kMaxSlots];
     __shared__ float s_w[kMaxSlots];
     __shared__ float s_y[kMaxRows * NH];
     __shared__ int s_U;
@@ -596,19 +597,15 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
     const float* const sts = a.sdown.ts;
     const int I = a.I, Is = a.Is;
 
-    // routing metadata: independent loads, one round trip
-    for (int i = tid; i <= n; i += kDownThreads) {
-        if (i < n) {
-            s_uniq[i] = a.uniq[i];
-            s_inv[i] = a.inv[i];
-            s_asg[i] = a.asg[i];
-            s_w[i] = a.w[i];
-        }
-        s_off[i] = a.off[i];
+    // Bytes the next launch reads first (the next layer's router rows),
+    // requested now so that they are in the memory-side cache when it starts;
+    // the value is consumed only by an empty asm statement at the end.
+    uint4 pf = make_uint4(0, 0, 0, 0);
+    if (a.prefetch) {
+        const int n16 = a.prefetch_bytes >> 4;
+        const int i = min((int)(blockIdx.x * kDownThreads + tid), n16 - 1);
+        pf = reinterpret_cast<const uint4*>(a.prefetch)[i];
     }
-    if (tid == 0) s_U = *a.n_unique;
-    __syncthreads();
-    const int U = s_U;
 
     // staged h rows: 4 floats of padding after every 32-column chunk, so the
     // 16 lanes of a weight row (one chunk each) do not share LDS banks
@@ -616,6 +613,53 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
     const int RLP = RL / 32 * 36;                   // padded LDS row stride
     const int CAP = (kDownHLdsBytes / 4) / RLP;     // rows per chunk
     const int total_rows = n + (has_sh ? K : 0);
+    // Positions 0..n-1 are the routed rows of h in dedup order, n..n+K-1 the
+    // shared expert's rows: neither needs the routing metadata, so the first
+    // chunk of h is requested before it.  One pass of SU float4 per thread
+    // covers a whole chunk (static_assert below); the loads are issued
+    // unconditionally (the counter of outstanding loads then stays known to
+    // the compiler) at clamped addresses, and columns past a shorter row's
+    // length are staged as zeros.
+    constexpr int SU = 8;
+    static_assert(kDownHLdsBytes / 16 <= SU * kDownThreads, "h chunk exceeds one staging pass");
+    const int q4 = RL / 4;                  // float4 per staged row (unpadded, a power of two)
+    const int lq4 = __builtin_ctz(q4);
+    float4 hv4[SU];
+    auto load_h = [&](int c0, int c1) {
+        const int nf4 = (c1 - c0) * q4;
+#pragma unroll
+        for (int j = 0; j < SU; ++j) {
+            const int f = min(j * kDownThreads + tid, nf4 - 1);
+            const int rr = c0 + (f >> lq4), c4 = f & (q4 - 1);
+            const bool shared_row = rr >= n;
+            const int len4 = (shared_row ? Is : I) / 4;
+            const int cc = min(c4, len4 - 1);
+            hv4[j] = shared_row ? reinterpret_cast<const float4*>(a.h_sh + (size_t)(rr - n) * Is)[cc]
+                                : reinterpret_cast<const float4*>(a.h + (size_t)rr * I)[cc];
+        }
+    };
+    load_h(0, min(total_rows, CAP));
+
+    // routing metadata: every load of a thread issued before any is used
+    // (one round trip; n + 1 <= kMaxSlots + 1 <= 2 * kDownThreads)
+    static_assert(kMaxSlots + 1 <= 2 * kDownThreads, "metadata exceeds two entries per thread");
+    {
+        const int i0 = tid, i1 = tid + kDownThreads;
+        const int j0 = min(i0, n - 1), j1 = min(i1, n - 1);
+        const int u0 = a.uniq[j0], u1 = a.uniq[j1];
+        const int v0 = a.inv[j0], v1 = a.inv[j1];
+        const float w0 = a.w[j0], w1 = a.w[j1];
+        const int o0 = a.off[min(i0, n)], o1 = a.off[min(i1, n)];
+        const int nu = *a.n_unique;
+        if (i0 < n) { s_uniq[i0] = u0; s_inv[i0] = v0; s_w[i0] = w0; }
+        if (i1 < n) { s_uniq[i1] = u1; s_inv[i1] = v1; s_w[i1] = w1; }
+        if (i0 <= n) s_off[i0] = o0;
+        if (i1 <= n) s_off[i1] = o1;
+        if (tid == 0) s_U = nu;
+    }
+    __syncthreads();
+    const int U = s_U;
+
     // lanes per weight row (one 32-column chunk each) and tasks per expert;
     // all powers of two, so lane and task indices split with shifts
     const int cprI = I >> 5, lgI = __builtin_ctz(cprI);
@@ -638,7 +682,6 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
         const int nT = (u_hi - u_lo) * gI + (sh_here ? gS : 0);
 
         // codes, scales and tensor scales of this wave's first batch of tasks
-        // are requested before the h staging, so both round trips overlap
         uint4 code[kDownBatch];
         uint32_t scl[kDownBatch];
         float tsv[kDownBatch];
@@ -677,30 +720,13 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
                 scl[i] = *reinterpret_cast<const uint16_t*>(ms + row * (cols / 16) + chunk * 2);
             }
         };
-        // stage h rows [c0, c1) into LDS: one pass of SU float4 per thread
-        // covers a whole chunk (static_assert below), so the h loads, the
-        // first batch of code loads and then the LDS stores form one
-        // straight-line sequence with both round trips overlapped
-        constexpr int SU = 8;
-        static_assert(kDownHLdsBytes / 16 <= SU * kDownThreads, "h chunk exceeds one staging pass");
-        const int q4 = RL / 4;                  // float4 per staged row (unpadded, a power of two)
-        const int lq4 = __builtin_ctz(q4);
-        const int nf4 = (c1 - c0) * q4;
-        // (loads unconditional at clamped addresses, as in load_batch;
-        // columns past a shorter row's length are staged as zeros)
+        // A later chunk of h (more than CAP rows) is requested here, after
+        // the previous chunk's closing barrier; this chunk's weight loads go
+        // out before its h is written to LDS.
+        if (c0 > 0) load_h(c0, c1);
         batch_ids(0);
-        float4 hv4[SU];
-#pragma unroll
-        for (int j = 0; j < SU; ++j) {
-            const int f = min(j * kDownThreads + tid, nf4 - 1);
-            const int rr = c0 + (f >> lq4), c4 = f & (q4 - 1);
-            const bool shared_row = rr >= n;
-            const int len4 = (shared_row ? Is : I) / 4;
-            const int cc = min(c4, len4 - 1);
-            hv4[j] = shared_row ? reinterpret_cast<const float4*>(a.h_sh + (size_t)(rr - n) * Is)[cc]
-                                : reinterpret_cast<const float4*>(a.h + (size_t)s_asg[rr] * I)[cc];
-        }
         load_batch(0);
+        const int nf4 = (c1 - c0) * q4;
 #pragma unroll
         for (int j = 0; j < SU; ++j) {
             const int f = j * kDownThreads + tid;
@@ -777,6 +803,7 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
         for (int nl = 0; nl < NH; ++nl) ss = fmaf(s_y[tid * NH + nl], s_y[tid * NH + nl], ss);
         a.ssq[tid * gridDim.x + blockIdx.x] = ss;
     }
+    asm volatile("" ::"v"(pf.x), "v"(pf.y), "v"(pf.z), "v"(pf.w));  // the prefetch stays issued
 }
 
 // ---------------------------------------------------------------------------
