@@ -112,16 +112,17 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
     return v;
 }
 
+// Wave maximum: inclusive max-scan inside each 16-lane row, then the
+// row_bcast:15 / row_bcast:31 steps carry rows 0-2 into lane 63 (lanes a
+// step does not update keep their value: 0 is the identity of the maximum).
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     v = max(v, (uint32_t)dpp<0x111>((int)v));
     v = max(v, (uint32_t)dpp<0x112>((int)v));
     v = max(v, (uint32_t)dpp<0x114>((int)v));
     v = max(v, (uint32_t)dpp<0x118>((int)v));
-    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
-    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
-    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
-    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-    return max(max(a, b), max(c, d));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Sum over aligned groups of G lanes; valid in the last lane of each group.
@@ -211,7 +212,7 @@ __device__ __forceinline__ uint32_t select_key(const SelectArgs& a, float l, int
 // wins, which (contiguous ownership, stable in-lane order) is the lowest
 // expert index.  lr: the row's logits in LDS.
 template <int P>
-__device__ void wave_topk(const SelectArgs& a, const float* lr, int r, SelectSmem& sm) {
+__device__ void wave_topk(const SelectArgs& a, const float* lr, int r, SelectSmem& sm, bool weights = true) {
     const int lane = threadIdx.x & 63;
     const int E = a.E, k = a.k;
     uint32_t sk[P];
@@ -251,6 +252,10 @@ __device__ void wave_topk(const SelectArgs& a, const float* lr, int r, SelectSme
             for (int p = 0; p + 1 < P; ++p) { sk[p] = sk[p + 1]; si[p] = si[p + 1]; }
             sk[P - 1] = 0;
         }
+    }
+    if (!weights) {  // the caller needs the experts only
+        if (lane < k) sm.sel[r * k + lane] = mine;
+        return;
     }
     // mixture weights over the selection (routed scale not folded in)
     const float l = (lane < k) ? lr[mine] : 0.0f;

@@ -96,9 +96,9 @@ __device__ void select_rows(const SelectArgs& a, SelectSmem& sm, const float* lg
     for (int r = wave; r < a.K; r += kWaves) wave_topk_rt(a, lg + r * a.E, r, sm);
 }
 template <int P>
-__device__ void select_rows_p(const SelectArgs& a, SelectSmem& sm, const float* lg) {
+__device__ void select_rows_p(const SelectArgs& a, SelectSmem& sm, const float* lg, bool weights) {
     const int wave = threadIdx.x >> 6;
-    for (int r = wave; r < a.K; r += kWaves) wave_topk<P>(a, lg + r * a.E, r, sm);
+    for (int r = wave; r < a.K; r += kWaves) wave_topk<P>(a, lg + r * a.E, r, sm, weights);
 }
 
 // The canonical dedup CSR of the selection in sm (whole workgroup), written
@@ -220,17 +220,11 @@ __device__ __forceinline__ void gu_compute(const GuRegs& R, float gts, float uts
     const int nsb = H / kSbCols;
     const int xr = (j < m_cnt) ? (xrows ? xrows[j] : j) : 0;
     f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-    // this wave's superblocks wave and wave + kWaves (one copy of the MFMA body)
-#pragma nounroll
-    for (int t = 0; t < 2; ++t) {
-        const int sb = wave + t * kWaves;
-        // field-wise selection keeps the registers out of scratch memory
-        GuSb c;
-        c.g0 = t ? R.sb1.g0 : R.sb0.g0; c.g1 = t ? R.sb1.g1 : R.sb0.g1;
-        c.u0 = t ? R.sb1.u0 : R.sb0.u0; c.u1 = t ? R.sb1.u1 : R.sb0.u1;
-        c.gs = t ? R.sb1.gs : R.sb0.gs; c.us = t ? R.sb1.us : R.sb0.us;
-        if (sb < nsb) gu_mfma_sb(c, xh + xh_index(xr, sb * kSbCols + kb * 64, H), j < m_cnt, accg, accu);
-    }
+    // this wave's superblocks wave and wave + kWaves, in load order: the
+    // first is multiplied while the second's loads are still in flight
+    if (wave < nsb) gu_mfma_sb(R.sb0, xh + xh_index(xr, wave * kSbCols + kb * 64, H), j < m_cnt, accg, accu);
+    if (wave + kWaves < nsb)
+        gu_mfma_sb(R.sb1, xh + xh_index(xr, (wave + kWaves) * kSbCols + kb * 64, H), j < m_cnt, accg, accu);
     reinterpret_cast<f32x4_t*>(red)[(wave * 2 + 0) * 64 + lane] = accg;
     reinterpret_cast<f32x4_t*>(red)[(wave * 2 + 1) * 64 + lane] = accu;
     __syncthreads();
@@ -505,7 +499,7 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
     } else {
         stage_logits_x(lg, a.sel.logits, K * a.sel.E, xh, a.x, K, H);
         __syncthreads();
-        select_rows_p<P>(a.sel, sm, lg);
+        select_rows_p<P>(a.sel, sm, lg, rb == 0);  // weights: only the workgroup that publishes them
         __syncthreads();
     }
     const int items = shared_blk ? 1 : K * k * nsr;
@@ -615,11 +609,10 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
     const int total_rows = n + (has_sh ? K : 0);
     // Positions 0..n-1 are the routed rows of h in dedup order, n..n+K-1 the
     // shared expert's rows: neither needs the routing metadata, so the first
-    // chunk of h is requested before it.  One pass of SU float4 per thread
-    // covers a whole chunk (static_assert below); the loads are issued
-    // unconditionally (the counter of outstanding loads then stays known to
-    // the compiler) at clamped addresses, and columns past a shorter row's
-    // length are staged as zeros.
+    // chunk of h is requested before it.  Up to SU passes of one float4 per
+    // thread cover a whole chunk (static_assert below); inside a pass the
+    // loads are unconditional at clamped addresses, and columns past a
+    // shorter row's length are staged as zeros.
     constexpr int SU = 8;
     static_assert(kDownHLdsBytes / 16 <= SU * kDownThreads, "h chunk exceeds one staging pass");
     const int q4 = RL / 4;                  // float4 per staged row (unpadded, a power of two)
@@ -629,13 +622,15 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
         const int nf4 = (c1 - c0) * q4;
 #pragma unroll
         for (int j = 0; j < SU; ++j) {
-            const int f = min(j * kDownThreads + tid, nf4 - 1);
-            const int rr = c0 + (f >> lq4), c4 = f & (q4 - 1);
-            const bool shared_row = rr >= n;
-            const int len4 = (shared_row ? Is : I) / 4;
-            const int cc = min(c4, len4 - 1);
-            hv4[j] = shared_row ? reinterpret_cast<const float4*>(a.h_sh + (size_t)(rr - n) * Is)[cc]
-                                : reinterpret_cast<const float4*>(a.h + (size_t)rr * I)[cc];
+            if (j * kDownThreads < nf4) {  // uniform: passes past the chunk are skipped
+                const int f = min(j * kDownThreads + tid, nf4 - 1);
+                const int rr = c0 + (f >> lq4), c4 = f & (q4 - 1);
+                const bool shared_row = rr >= n;
+                const int len4 = (shared_row ? Is : I) / 4;
+                const int cc = min(c4, len4 - 1);
+                hv4[j] = shared_row ? reinterpret_cast<const float4*>(a.h_sh + (size_t)(rr - n) * Is)[cc]
+                                    : reinterpret_cast<const float4*>(a.h + (size_t)rr * I)[cc];
+            }
         }
     };
     load_h(0, min(total_rows, CAP));
