@@ -71,6 +71,15 @@ extern "C" {
 #define MOE_SCORE_SOFTMAX 0       /* select on logits; weights = softmax over the selection */
 #define MOE_SCORE_SIGMOID_BIAS 1  /* select on fp32 sigmoid(logit) + bias; weights = sigmoid */
 
+/* Shape regime (moe_cfg.regime): the same computation by two kernel families.
+ * AUTO runs the verify-width kernels below 8 rows and the grouped kernels
+ * from 8 rows (when the shape meets the grouped limits; always above 16);
+ * VERIFY forces the verify-width kernels (K <= 16, MOE_ERR_UNSUPPORTED
+ * above); GROUPED forces the grouped kernels at any K (their limits apply). */
+#define MOE_REGIME_AUTO 0
+#define MOE_REGIME_VERIFY 1
+#define MOE_REGIME_GROUPED 2
+
 typedef struct moe_nvfp4 {
     const uint8_t* q;
     const uint8_t* s;
@@ -92,6 +101,7 @@ typedef struct moe_cfg {
     int32_t max_rows;      /* largest K a workspace of this cfg serves
                               (1..1024; above 16 the cfg must also meet the
                               grouped-regime limits below) */
+    int32_t regime;        /* MOE_REGIME_*: which kernels serve K rows */
 } moe_cfg;
 
 typedef struct moe_layer_weights {
@@ -143,16 +153,19 @@ MOE_API size_t moe_verify_workspace_bytes(const moe_cfg* cfg);
  * NULL.  Writes y bf16 [K][H] (round to nearest even of y32) and, if y32 is
  * not NULL, the fp32 result.  dbg may be NULL.
  *
- * Two shape regimes of the same computation, picked by K:
- *  - K <= 16 (verify width): every unique expert is streamed once by
+ * Two shape regimes of the same computation, picked by K and cfg->regime
+ * (MOE_REGIME_*; AUTO: verify width below 8 rows, grouped from 8 rows when
+ * the shape meets the grouped limits, grouped above 16 rows):
+ *  - verify width (K <= 16): every unique expert is streamed once by
  *    skinny kernels (three launches);
- *  - K > 16 (prefill, e.g. the 512-row seed prefill of the mlxfast README,
- *    "Why this challenge exists"): the T*k slots are grouped by expert into
- *    tiles of up to 32 tokens and the expert GEMMs run on the matrix cores
- *    (six launches).  Limits: inter and shared_inter multiples of 64 and at
- *    most 1024 (MOE_ERR_UNSUPPORTED otherwise).  h enters the down GEMM as a
- *    pair of fp16 values (hi + lo) of h scaled by a per-token power of two,
- *    about 22 significant bits. */
+ *  - grouped (prefill, e.g. the 512-row seed prefill of the mlxfast README,
+ *    "Why this challenge exists", and wide verify blocks): the T*k slots are
+ *    grouped by expert into tiles of up to 32 tokens and the expert GEMMs
+ *    run on the matrix cores (six launches).  Limits: inter and shared_inter
+ *    multiples of 64 and at most 1024 (MOE_ERR_UNSUPPORTED when the grouped
+ *    kernels are required).  h enters the down GEMM as a pair of fp16 values
+ *    (hi + lo) of h scaled by a per-token power of two, about 22 significant
+ *    bits. */
 MOE_API int moe_verify_layer(const moe_cfg* cfg, const moe_layer_weights* w, const uint16_t* x, int32_t K,
                      const uint16_t* residual, uint16_t* y, float* y32, void* workspace,
                      size_t workspace_bytes, void* stream, const moe_debug* dbg);
@@ -168,7 +181,8 @@ MOE_API int moe_verify_layer_grouped(const moe_cfg* cfg, const moe_layer_weights
 
 /* n_layers layers (steps 1-9).  layers is a HOST array of n_layers weight
  * structs.  Writes the last layer's output to y (bf16) and y32 (fp32, may be
- * NULL).  dbg may be NULL.  K picks the regime as in moe_verify_layer. */
+ * NULL).  dbg may be NULL.  K and cfg->regime pick the kernels as in
+ * moe_verify_layer. */
 MOE_API int moe_verify_stack(const moe_cfg* cfg, const moe_layer_weights* layers, int32_t n_layers,
                      const uint16_t* x, int32_t K, uint16_t* y, float* y32, void* workspace,
                      size_t workspace_bytes, void* stream, const moe_debug* dbg);
@@ -177,8 +191,8 @@ MOE_API int moe_verify_stack(const moe_cfg* cfg, const moe_layer_weights* layers
  * kernel launched so that a start/stop event pair carries that kernel's own
  * dispatch timestamps.  Synchronises `stream`, then writes the durations in
  * milliseconds to the HOST array kernel_ms[n_layers][3] (router + selection,
- * gate/up + SwiGLU, down + combine).  Verify width only (K <= 16;
- * MOE_ERR_UNSUPPORTED above). */
+ * gate/up + SwiGLU, down + combine).  Verify-width kernels only
+ * (MOE_ERR_UNSUPPORTED when K and cfg->regime pick the grouped ones). */
 MOE_API int moe_verify_stack_timed(const moe_cfg* cfg, const moe_layer_weights* layers, int32_t n_layers,
                                    const uint16_t* x, int32_t K, uint16_t* y, float* y32, void* workspace,
                                    size_t workspace_bytes, void* stream, float* kernel_ms);

@@ -24,6 +24,9 @@ MOE_ERR_HIP = -3
 MOE_ERR_WORKSPACE = -4
 MOE_SCORE_SOFTMAX = 0
 MOE_SCORE_SIGMOID_BIAS = 1
+MOE_REGIME_AUTO = 0
+MOE_REGIME_VERIFY = 1
+MOE_REGIME_GROUPED = 2
 
 _c_void_p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -36,7 +39,8 @@ class moe_nvfp4(ctypes.Structure):
 class moe_cfg(ctypes.Structure):
     _fields_ = [("hidden", _i32), ("n_experts", _i32), ("top_k", _i32), ("inter", _i32),
                 ("shared_inter", _i32), ("score_fn", _i32), ("norm_topk", _i32),
-                ("routed_scale", ctypes.c_float), ("rms_eps", ctypes.c_float), ("max_rows", _i32)]
+                ("routed_scale", ctypes.c_float), ("rms_eps", ctypes.c_float), ("max_rows", _i32),
+                ("regime", _i32)]
 
 
 class moe_layer_weights(ctypes.Structure):
@@ -146,9 +150,9 @@ def _stream(stream=None):
 
 
 def make_cfg(shape, max_rows: int, score_fn: int = MOE_SCORE_SOFTMAX, norm_topk: int = 1,
-             routed_scale: float = 1.0, rms_eps: float = 1e-6) -> moe_cfg:
+             routed_scale: float = 1.0, rms_eps: float = 1e-6, regime: int = MOE_REGIME_AUTO) -> moe_cfg:
     return moe_cfg(shape.hidden, shape.n_experts, shape.top_k, shape.inter, shape.shared_inter,
-                   score_fn, norm_topk, routed_scale, rms_eps, max_rows)
+                   score_fn, norm_topk, routed_scale, rms_eps, max_rows, regime)
 
 
 def _mat(m) -> moe_nvfp4:

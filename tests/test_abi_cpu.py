@@ -36,13 +36,13 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_struct_layouts_match_header_sizes():
-    # pointer-only structs: 3 / 2 + 6*3 / 7 / 10 pointers; cfg: 10 x 4 bytes
+    # pointer-only structs: 3 / 2 + 6*3 / 7 / 10 pointers; cfg: 11 x 4 bytes
     P = ctypes.sizeof(ctypes.c_void_p)
     assert ctypes.sizeof(api.moe_nvfp4) == 3 * P
     assert ctypes.sizeof(api.moe_layer_weights) == 20 * P
     assert ctypes.sizeof(api.moe_route_out) == 7 * P
     assert ctypes.sizeof(api.moe_debug) == 10 * P
-    assert ctypes.sizeof(api.moe_cfg) == 40
+    assert ctypes.sizeof(api.moe_cfg) == 44
 
 
 def _cfg(**kw):
@@ -67,6 +67,7 @@ def test_workspace_bytes_valid_and_invalid():
     assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(inter=500))) == 0
     assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(score_fn=7))) == 0
     assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(norm_topk=0))) == 0
+    assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(regime=3))) == 0
 
 
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
@@ -166,3 +167,19 @@ def test_weight_bytes_counts_unique_experts_once():
     assert one == 3 * (512 * 2048 // 2 + 512 * 2048 // 16 + 4)
     full = api.moe_verify_weight_bytes(cfg, 16, 2)
     assert full == 17 * one + 2 * 256 * 2048 + 4 * 2 * 2048
+
+
+def test_regime_argument_errors():
+    # checked before any device work: the verify-width kernels serve at most
+    # 16 rows; forcing the grouped kernels applies their shape limits at any K
+    L = api.lib()
+    cfg = _cfg(max_rows=17, regime=api.MOE_REGIME_VERIFY)
+    n = L.moe_verify_workspace_bytes(ctypes.byref(cfg))
+    assert n > 0
+    assert _layer(cfg, _weights(), K=17, ws_bytes=n) == api.MOE_ERR_UNSUPPORTED
+    assert "MOE_REGIME_VERIFY" in api.moe_verify_last_error()
+    cfg = _cfg(inter=2048, regime=api.MOE_REGIME_GROUPED)
+    n = L.moe_verify_workspace_bytes(ctypes.byref(cfg))
+    assert n > 0
+    assert _layer(cfg, _weights(), K=2, ws_bytes=n) == api.MOE_ERR_UNSUPPORTED
+    assert "grouped" in api.moe_verify_last_error()

@@ -124,7 +124,7 @@ def test_grouped_and_verify_width_paths_agree_at_16_rows():
     shape = inputs.LAGUNA
     w = inputs.gen_layer(shape, 41, 0, device=DEV)
     x = inputs.gen_x(16, shape.hidden, 41, device=DEV)
-    cfg = api.make_cfg(shape, 16)
+    cfg = api.make_cfg(shape, 16, regime=api.MOE_REGIME_VERIFY)
     a = gh.run_layer(cfg, w, x, grouped=False)
     b = gh.run_layer(cfg, w, x, grouped=True)
     # the two regimes run different router kernels (VALU GEMV, MFMA GEMM):

@@ -119,12 +119,12 @@ def test_route_sigmoid_bias(norm):
 # ---------------------------------------------------------------------------
 
 
-def _layer_case(shape, K, seed, score_fn=0, rs=1.0, residual=False, x=None, label=""):
-    say("case: layer %s K=%d seed=%d score_fn=%d" % (label, K, seed, score_fn))
+def _layer_case(shape, K, seed, score_fn=0, rs=1.0, residual=False, x=None, label="", regime=api.MOE_REGIME_AUTO):
+    say("case: layer %s K=%d seed=%d score_fn=%d regime=%d" % (label, K, seed, score_fn, regime))
     w = inputs.gen_layer(shape, seed, 0, device=DEV, with_bias=(score_fn == 1))
     x = inputs.gen_x(K, shape.hidden, seed, device=DEV) if x is None else x
     res = inputs.gen_x(K, shape.hidden, seed + 1, device=DEV, tag="res") if residual else None
-    cfg = api.make_cfg(shape, K, score_fn=score_fn, routed_scale=rs)
+    cfg = api.make_cfg(shape, K, score_fn=score_fn, routed_scale=rs, regime=regime)
     gpu = gh.run_layer(cfg, w, x, residual=res)
     orec = orc.moe_layer(w, x.cpu(), shape.top_k, score_fn, 1, rs, None if res is None else res.cpu())
     bias = None if score_fn == 0 else w["router_bias"].cpu().numpy()
@@ -143,8 +143,9 @@ def test_layer_tiny_config():
 
 @pytest.mark.parametrize("K", [1, 2, 3, 8, 16])
 def test_layer_tiny_shapes_many_rows(K):
+    # the verify-width kernels at every row count they serve
     shape = inputs.MoEShape(hidden=256, n_experts=16, top_k=2, inter=128, shared_inter=128)
-    _layer_case(shape, K, 100 + K, label="tiny+shared")
+    _layer_case(shape, K, 100 + K, label="tiny+shared", regime=api.MOE_REGIME_VERIFY)
 
 
 def test_layer_full_size_k2():
@@ -152,10 +153,14 @@ def test_layer_full_size_k2():
     _layer_case(inputs.LAGUNA, 2, 7, label="full")
 
 
-@pytest.mark.parametrize("K", [1, 4, 8, 16])
-def test_layer_full_size_k_sweep_correlated_rows(K):
+@pytest.mark.parametrize("K,regime", [(1, api.MOE_REGIME_AUTO), (4, api.MOE_REGIME_AUTO),
+                                      (8, api.MOE_REGIME_VERIFY), (8, api.MOE_REGIME_AUTO),
+                                      (16, api.MOE_REGIME_VERIFY), (16, api.MOE_REGIME_AUTO)])
+def test_layer_full_size_k_sweep_correlated_rows(K, regime):
+    # from 8 rows the automatic regime runs the grouped kernels; the
+    # verify-width kernels are also checked at those widths
     x = inputs.gen_x_correlated(K, inputs.LAGUNA.hidden, 31 + K, device=DEV)
-    gpu, _, _ = _layer_case(inputs.LAGUNA, K, 31 + K, x=x, label="ksweep")
+    gpu, _, _ = _layer_case(inputs.LAGUNA, K, 31 + K, x=x, label="ksweep", regime=regime)
     assert int(gpu["n_unique"][0]) <= K * 8
 
 
@@ -190,7 +195,7 @@ def test_invariants_identical_rows_permutation_rerun():
     say("case: invariants")
     shape = inputs.LAGUNA
     w = inputs.gen_layer(shape, 23, 0, device=DEV)
-    cfg = api.make_cfg(shape, 8)
+    cfg = api.make_cfg(shape, 8, regime=api.MOE_REGIME_VERIFY)  # the grouped kernels: test_gpu_grouped
     x1 = inputs.gen_x(1, shape.hidden, 23, device=DEV)
     yi = _run_y32(cfg, w, x1.repeat(8, 1).contiguous())
     for r in range(1, 8):

@@ -29,11 +29,11 @@ def _host_layers(layers_dev):
                for k, v in w.items()}
 
 
-def _stack_case(shape, n_layers, K, seed, label, min_alive_layers):
-    say("case: stack %s L=%d K=%d seed=%d" % (label, n_layers, K, seed))
+def _stack_case(shape, n_layers, K, seed, label, min_alive_layers, regime=api.MOE_REGIME_AUTO):
+    say("case: stack %s L=%d K=%d seed=%d regime=%d" % (label, n_layers, K, seed, regime))
     layers = inputs.gen_stack(shape, n_layers, seed, device=DEV)
     x = inputs.gen_x(K, shape.hidden, seed, device=DEV)
-    cfg = api.make_cfg(shape, K)
+    cfg = api.make_cfg(shape, K, regime=regime)
     gpu = gh.run_stack_debug(cfg, layers, x, n_layers)
     np.testing.assert_array_equal(gpu["y32_out"], gpu["y32"][-1])
     np.testing.assert_array_equal(gpu["y"], gh.bf16_of(gpu["y32_out"]))
@@ -59,11 +59,14 @@ def test_stack_full_size_4_layers_k2():
     _stack_case(inputs.LAGUNA, 4, 2, 9, "full-4", 4)
 
 
-@pytest.mark.parametrize("K", [1, 8, 16])
-def test_stack_full_size_6_layers_row_counts(K):
+@pytest.mark.parametrize("K,regime", [(1, api.MOE_REGIME_AUTO), (8, api.MOE_REGIME_VERIFY), (8, api.MOE_REGIME_AUTO),
+                                      (16, api.MOE_REGIME_VERIFY), (16, api.MOE_REGIME_AUTO)])
+def test_stack_full_size_6_layers_row_counts(K, regime):
     # verify widths other than the benchmark's two rows, through the RMSNorm
-    # glue (sum-of-squares partials of every row) and the stack entry point
-    _stack_case(inputs.LAGUNA, 6, K, 40 + K, "full-6-K%d" % K, 6)
+    # glue (sum-of-squares partials of every row, or the grouped combine's
+    # normalised next input from 8 rows in the automatic regime) and the stack
+    # entry point
+    _stack_case(inputs.LAGUNA, 6, K, 40 + K, "full-6-K%d-r%d" % (K, regime), 6, regime=regime)
 
 
 def test_stack_full_size_40_layers_graph_matches_direct_and_oracle():
