@@ -16,7 +16,7 @@ constexpr int kBlock = 256;        // threads per workgroup (4 wave64)
 constexpr int kWaves = kBlock / 64;
 constexpr int kDownRowsPerBlock = 8;
 constexpr int kDownThreads = 512;  // 8 wave64 per down workgroup
-constexpr int kDownHLdsBytes = 64 * 1024;  // h rows staged in LDS per chunk
+constexpr int kDownHLdsBytes = 128 * 1024;  // most h rows staged in LDS per chunk (one down workgroup per compute unit)
 constexpr int kGateUpMaxGrid = 1024;       // routed gate/up workgroups loop over work items
 constexpr int kMetaUnique = 0;             // workspace word holding the unique-expert count
 constexpr int kMetaTiles = 1;              // workspace word holding the grouped tile count
@@ -91,6 +91,7 @@ struct DownArgs {
     float* ssq;             // [K][H / kDownRowsPerBlock] per-workgroup sums of y^2
     const uint8_t* prefetch;   // bytes the next launch reads first (the next layer's router), or nullptr
     int prefetch_bytes;        // multiple of 16
+    int h_lds_bytes;           // dynamic LDS of the launch: h rows staged per chunk (set by launch_down)
     int K, H, I, Is, k;
     float rs;
 };

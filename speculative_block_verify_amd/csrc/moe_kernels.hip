@@ -566,6 +566,9 @@ constexpr int kDownBatch = 6;  // tasks per wave whose codes are in flight toget
 // The h rows are processed in chunks that fit kDownHLdsBytes: positions
 // 0..n-1 are the routed slots in dedup order (h row p, length I), n..n+K-1
 // the shared expert's rows (length Is).
+// SU: staging passes of one float4 per thread that cover one chunk of h
+// (a.h_lds_bytes / 16 <= SU * kDownThreads, guaranteed by launch_down).
+template <int SU>
 __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
     constexpr int NH = kDownRowsPerBlock;
     __shared__ float so[(kMaxSlots + kMaxRows) * NH];
@@ -605,16 +608,15 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
     // 16 lanes of a weight row (one chunk each) do not share LDS banks
     const int RL = max(I, has_sh ? Is : 0);
     const int RLP = RL / 32 * 36;                   // padded LDS row stride
-    const int CAP = (kDownHLdsBytes / 4) / RLP;     // rows per chunk
+    const int CAP = (a.h_lds_bytes / 4) / RLP;      // rows per chunk
     const int total_rows = n + (has_sh ? K : 0);
     // Positions 0..n-1 are the routed rows of h in dedup order, n..n+K-1 the
     // shared expert's rows: neither needs the routing metadata, so the first
     // chunk of h is requested before it.  Up to SU passes of one float4 per
-    // thread cover a whole chunk (static_assert below); inside a pass the
-    // loads are unconditional at clamped addresses, and columns past a
-    // shorter row's length are staged as zeros.
-    constexpr int SU = 8;
-    static_assert(kDownHLdsBytes / 16 <= SU * kDownThreads, "h chunk exceeds one staging pass");
+    // thread cover a whole chunk; inside a pass the loads are unconditional
+    // at clamped addresses, and columns past a shorter row's length are
+    // staged as zeros.
+    static_assert(kDownHLdsBytes / 16 <= 16 * kDownThreads, "the largest h chunk exceeds 16 staging passes");
     const int q4 = RL / 4;                  // float4 per staged row (unpadded, a power of two)
     const int lq4 = __builtin_ctz(q4);
     float4 hv4[SU];
@@ -879,7 +881,8 @@ hipError_t init_kernels() {
         if ((e = set_lds(k_router<4>, kMaxDynLds)) != hipSuccess) return e;
         if ((e = set_lds(k_router<8>, kMaxDynLds)) != hipSuccess) return e;
         if ((e = set_lds(k_router<16>, kMaxDynLds)) != hipSuccess) return e;
-        if ((e = set_lds(k_down, kDownHLdsBytes)) != hipSuccess) return e;
+        if ((e = set_lds(k_down<8>, kDownHLdsBytes)) != hipSuccess) return e;
+        if ((e = set_lds(k_down<16>, kDownHLdsBytes)) != hipSuccess) return e;
         return init_grouped_kernels();
     }();
     return once;
@@ -919,7 +922,17 @@ hipError_t launch_gateup(const GateUpArgs& a, int max_unique, hipStream_t st, co
 }
 
 hipError_t launch_down(const DownArgs& a, hipStream_t st, const Timing* t) {
-    return launch(k_down, dim3(a.H / kDownRowsPerBlock), dim3(kDownThreads), kDownHLdsBytes, st, t, a);
+    // LDS for the h rows one launch stages (all of them when they fit in
+    // kDownHLdsBytes, else chunks of that size): padded rows of max(I, Is)
+    // floats, 36 per 32 columns
+    const int n_rows = a.K * a.k + (a.sdown.q ? a.K : 0);
+    const int RL = a.I > a.Is ? a.I : a.Is;
+    const long long need = (long long)n_rows * (RL / 32 * 36) * 4;
+    DownArgs b = a;
+    b.h_lds_bytes = (int)(need < kDownHLdsBytes ? need : kDownHLdsBytes);
+    const dim3 g(a.H / kDownRowsPerBlock), blk(kDownThreads);
+    if (b.h_lds_bytes <= 8 * kDownThreads * 16) return launch(k_down<8>, g, blk, (size_t)b.h_lds_bytes, st, t, b);
+    return launch(k_down<16>, g, blk, (size_t)b.h_lds_bytes, st, t, b);
 }
 
 hipError_t launch_dequant(Fp4Mat m, int n_experts, int rows, int cols, float* out, hipStream_t st) {
