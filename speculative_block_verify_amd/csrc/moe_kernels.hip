@@ -906,19 +906,34 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
     return launch(k_select, dim3(1), dim3(kBlock), select_smem_bytes(a.K, a.E), st, nullptr, a);
 }
 
+// Routed gate/up workgroups: one per work item (slot, 16 intermediate rows),
+// but no more than fit on the chip at once next to the shared expert's
+// tiles (the rest loop over items): a second dispatch round of workgroups
+// would repeat the selection after the first round's weights have streamed.
+template <typename Kern>
+hipError_t launch_gateup_k(Kern k, const GateUpArgs& a, hipStream_t st, const Timing* t) {
+    const size_t smem = gateup_smem_bytes(a.K, a.sel.E, a.H);
+    const int n_sh = a.sgate.q ? a.Is / kTileRows : 0;
+    int grid = a.K * a.sel.k * (a.I / kTileRows);
+    if (grid > kGateUpMaxGrid) grid = kGateUpMaxGrid;
+    int dev = 0, n_cu = 0, per_cu = 0;
+    hipError_t e;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kBlock, smem)) != hipSuccess) return e;
+    const int fit = per_cu * n_cu - n_sh;
+    if (fit >= 1 && grid > fit) grid = fit;
+    return launch(k, dim3(grid + n_sh), dim3(kBlock), smem, st, t, a);
+}
+
 hipError_t launch_gateup(const GateUpArgs& a, int max_unique, hipStream_t st, const Timing* t) {
     (void)max_unique;
-    int grid = a.K * a.sel.k * (a.I / kTileRows);  // work items: (slot, 16 intermediate rows)
-    if (grid > kGateUpMaxGrid) grid = kGateUpMaxGrid;
-    grid += a.sgate.q ? a.Is / kTileRows : 0;
-    const dim3 g(grid), b(kBlock);
-    const size_t smem = gateup_smem_bytes(a.K, a.sel.E, a.H);
     const int P = (a.sel.E + 63) >> 6;  // experts per lane of the top-k
-    if (P <= 1) return launch(k_gateup<1>, g, b, smem, st, t, a);
-    if (P <= 2) return launch(k_gateup<2>, g, b, smem, st, t, a);
-    if (P <= 4) return launch(k_gateup<4>, g, b, smem, st, t, a);
-    if (P <= 8) return launch(k_gateup<8>, g, b, smem, st, t, a);
-    return launch(k_gateup<16>, g, b, smem, st, t, a);
+    if (P <= 1) return launch_gateup_k(k_gateup<1>, a, st, t);
+    if (P <= 2) return launch_gateup_k(k_gateup<2>, a, st, t);
+    if (P <= 4) return launch_gateup_k(k_gateup<4>, a, st, t);
+    if (P <= 8) return launch_gateup_k(k_gateup<8>, a, st, t);
+    return launch_gateup_k(k_gateup<16>, a, st, t);
 }
 
 hipError_t launch_down(const DownArgs& a, hipStream_t st, const Timing* t) {
