@@ -265,7 +265,7 @@ int enqueue_layer(const moe_cfg* c, const moe_layer_weights* w, const LayerIO& i
     da.down = mat(w->down);
     da.sdown = has_sh ? mat(w->sh_down) : none;
     da.n_unique = L.meta + moe::kMetaUnique;
-    da.uniq = L.uniq; da.off = L.off; da.inv = L.inv; da.asg = L.asg;
+    da.uniq = L.uniq; da.off = L.off; da.inv = L.inv;
     da.w = L.w; da.h = L.h; da.h_sh = L.h_sh;
     da.residual = io.residual;
     da.y32 = io.y32; da.y = io.y;

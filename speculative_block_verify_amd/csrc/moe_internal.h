@@ -81,7 +81,6 @@ struct DownArgs {
     const int32_t* uniq;
     const int32_t* off;
     const int32_t* inv;
-    const int32_t* asg;
     const float* w;         // [K][k]
     const float* h;         // [K*k][I], rows by dedup position
     const float* h_sh;
