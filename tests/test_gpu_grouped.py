@@ -201,3 +201,21 @@ def test_grouped_prefill_512_rows_sampled():
     sub = {kk: gpu[kk][rows] for kk in ("logits", "ids", "w", "y32")}
     rep = gh.compare_layer(sub, orec, shape.top_k, shape.n_experts, label="prefill rows %s" % rows.tolist())
     say("  report:", rep)
+
+
+@pytest.mark.parametrize("K,grouped_auto", [(7, False), (8, True)])
+def test_automatic_regime_switch_at_8_rows(K, grouped_auto):
+    """From 8 rows the automatic regime runs the grouped kernels: its output is
+    then bitwise the forced-grouped entry's; below 8 rows it is bitwise the
+    forced verify-width kernels'."""
+    say("case: automatic regime K=%d" % K)
+    shape = inputs.LAGUNA
+    w = inputs.gen_layer(shape, 71 + K, 0, device=DEV)
+    x = inputs.gen_x(K, shape.hidden, 71 + K, device=DEV)
+    auto = gh.run_layer(api.make_cfg(shape, K), w, x)
+    if grouped_auto:
+        ref = gh.run_layer(api.make_cfg(shape, K), w, x, grouped=True)
+    else:
+        ref = gh.run_layer(api.make_cfg(shape, K, regime=api.MOE_REGIME_VERIFY), w, x)
+    for kk in ("ids", "n_unique", "uniq", "off", "asg", "inv", "y32", "y"):
+        np.testing.assert_array_equal(auto[kk], ref[kk], err_msg=kk)

@@ -91,3 +91,36 @@ def test_stack_full_size_40_layers_graph_matches_direct_and_oracle():
         torch.cuda.synchronize()
         del junk
     g.close()
+
+
+def test_stack_graph_grouped_regime_16_rows_matches_direct():
+    """The K sweep's widest point as the benchmark runs it: 16 correlated rows,
+    where the automatic regime picks the grouped kernels, replayed as a
+    captured graph.  Every replay (with eager work in between) must equal the
+    direct stack call bit for bit; the direct call itself is checked against
+    the oracle by the row-count stack tests."""
+    say("case: stack graph grouped regime K=16 L=6")
+    shape, n_layers, K = inputs.LAGUNA, 6, 16
+    layers = inputs.gen_stack(shape, n_layers, 61, device=DEV)
+    x = inputs.gen_x_correlated(K, shape.hidden, 61, device=DEV)
+    cfg = api.make_cfg(shape, K)
+    wts = [api.make_weights(w) for w in layers]
+    y = torch.empty(K, shape.hidden, dtype=torch.int16, device=DEV)
+    y32 = torch.empty(K, shape.hidden, dtype=torch.float32, device=DEV)
+    ws = api.alloc_workspace(cfg, DEV)
+    api.moe_verify_stack(cfg, wts, x, y, ws, y32=y32)
+    torch.cuda.synchronize()
+    want32, want = y32.cpu().numpy().copy(), y.cpu().numpy().copy()
+    assert np.isfinite(want32).all()
+    g = api.StackGraph(cfg, wts, x, y, ws, y32=y32)
+    for rep in range(3):
+        y32.fill_(float("nan"))
+        g.launch()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y32.cpu().numpy(), want32)
+        np.testing.assert_array_equal(y.cpu().numpy(), want)
+        junk = torch.randn(1 << 20, device=DEV).sum()
+        api.moe_verify_stack(cfg, wts[:2], x, y, ws, y32=y32)
+        torch.cuda.synchronize()
+        del junk
+    g.close()
