@@ -64,7 +64,7 @@ extern "C" {
 
 #define MOE_OK 0
 #define MOE_ERR_INVALID (-1)      /* null/misaligned pointer, K out of range, bad enum */
-#define MOE_ERR_UNSUPPORTED (-2)  /* a shape this build does not implement */
+#define MOE_ERR_UNSUPPORTED (-2)  /* a shape this library does not implement */
 #define MOE_ERR_HIP (-3)          /* a HIP runtime call failed (text has hipGetErrorString) */
 #define MOE_ERR_WORKSPACE (-4)    /* workspace smaller than moe_verify_workspace_bytes() */
 
