@@ -164,10 +164,12 @@ def prefill(args):
     }), flush=True)
 
 
-def cpu_baseline(layers, xs, shape, K, budget_s):
+def cpu_baseline(layers, xs, shape, K, budget_s, gpu_layer0=None):
     """The oracle (single-threaded C, fp64) chained through the same 40-layer
     stack, input after input of the pool, until budget_s seconds of CPU work;
-    GB/s over the same algorithmic byte definition as the GPU figure."""
+    GB/s over the same algorithmic byte definition as the GPU figure.  With
+    gpu_layer0 (the GPU's fp32 output of the first layer on the first input),
+    also the parity of that layer against the oracle's."""
     import oracle as orc
     import numpy as np
     from speculative_block_verify_amd import api
@@ -175,12 +177,18 @@ def cpu_baseline(layers, xs, shape, K, budget_s):
     host = [{k: (None if v is None else ({kk: vv.cpu() for kk, vv in v.items()} if isinstance(v, dict) else v.cpu()))
              for k, v in w.items()} for w in layers]
     t_total, n_bytes, n_layers, n_inputs = 0.0, 0, 0, 0
+    parity = None
     while t_total < budget_s and n_inputs < len(xs):
         xo = xs[n_inputs].cpu().numpy().view(np.uint16)
         n_inputs += 1
         for wh in host:
             t0 = time.perf_counter()
             rec = orc.moe_layer(wh, xo, shape.top_k)
+            if gpu_layer0 is not None and parity is None:
+                ref = np.asarray(rec["y"], dtype=np.float64)
+                d = np.asarray(gpu_layer0, dtype=np.float64) - ref
+                parity = {"layer": 0, "input": 0, "max_abs_over_max_ref": float(np.abs(d).max() / np.abs(ref).max()),
+                          "rel_l2": float(np.linalg.norm(d) / np.linalg.norm(ref)), "bar": 2e-3}
             xo = orc.rmsnorm_bf16(rec["y"])
             t_total += time.perf_counter() - t0
             U = orc.dedup(rec["ids"], shape.n_experts)["n_unique"]
@@ -190,7 +198,7 @@ def cpu_baseline(layers, xs, shape, K, budget_s):
                 break
     return {"value": n_bytes / t_total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": "%d layer evaluations (the 40-layer stack chained over %d inputs of the pool), K=%d; "
-                      "%.1f s single-threaded" % (n_layers, n_inputs, K, t_total)}
+                      "%.1f s single-threaded" % (n_layers, n_inputs, K, t_total)}, parity
 
 
 def main():
@@ -247,9 +255,15 @@ def main():
 
     # unique-expert counts per (input, layer) from the dedup pass
     nu = torch.empty(L, dtype=torch.int32, device=dev)
+    y32_layers = torch.empty(L, K, shape.hidden, dtype=torch.float32, device=dev)
     step_bytes, gu_bytes, uniques = [], [], []
+    gpu_layer0 = None
     for i in range(POOL):
-        api.moe_verify_stack(cfg, wts, xs[i], y, ws, y32=y32, debug=api.make_debug(n_unique=nu))
+        dbg = api.make_debug(n_unique=nu, y32=y32_layers) if i == 0 else api.make_debug(n_unique=nu)
+        api.moe_verify_stack(cfg, wts, xs[i], y, ws, y32=y32, debug=dbg)
+        if i == 0:
+            torch.cuda.synchronize()
+            gpu_layer0 = y32_layers[0].cpu().numpy()
         torch.cuda.synchronize()
         U = nu.cpu().tolist()
         uniques.append(U)
@@ -337,9 +351,12 @@ def main():
             "traffic": measured_traffic() if K == 2 else None, "bytes_per_launch": round(gu_avg_bytes)},
         "wall_s": round(wall, 4),
     }
+    result["seed"] = SEED
+    result["device"] = torch.cuda.get_device_name(dev)
+    result["rocm"] = torch.version.hip
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the host (%.0f s budget)" % args.cpu_seconds)
-        result["cpu_baseline"] = cpu_baseline(layers, xs, shape, K, args.cpu_seconds)
+        result["cpu_baseline"], result["parity"] = cpu_baseline(layers, xs, shape, K, args.cpu_seconds, gpu_layer0)
     print(json.dumps(result), flush=True)
 
 
