@@ -15,7 +15,7 @@ constexpr int kMaxSlots = kMaxRows * kMaxTopK;
 constexpr int kBlock = 256;        // threads per workgroup (4 wave64)
 constexpr int kWaves = kBlock / 64;
 constexpr int kDownRowsPerBlock = 8;
-constexpr int kDownThreads = 512;  // 8 wave64 per down workgroup
+constexpr int kDownThreads = 1024;  // 16 wave64 per down workgroup
 constexpr int kDownHLdsBytes = 128 * 1024;  // most h rows staged in LDS per chunk (one down workgroup per compute unit)
 constexpr int kGateUpMaxGrid = 1024;       // routed gate/up workgroups loop over work items
 constexpr int kMetaUnique = 0;             // workspace word holding the unique-expert count

@@ -561,7 +561,10 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
 // ---------------------------------------------------------------------------
 
 constexpr int kDownWaves = kDownThreads / 64;
-constexpr int kDownBatch = 6;  // tasks per wave whose codes are in flight together
+constexpr int kDownBatch = 3;  // tasks per wave whose codes are in flight together
+// staging passes of the two down instantiations: up to 64 KB of h, and the largest chunk
+constexpr int kDownSuSmall = 64 * 1024 / (16 * kDownThreads);
+constexpr int kDownSuBig = kDownHLdsBytes / (16 * kDownThreads);
 
 // The h rows are processed in chunks that fit kDownHLdsBytes: positions
 // 0..n-1 are the routed slots in dedup order (h row p, length I), n..n+K-1
@@ -881,8 +884,8 @@ hipError_t init_kernels() {
         if ((e = set_lds(k_router<4>, kMaxDynLds)) != hipSuccess) return e;
         if ((e = set_lds(k_router<8>, kMaxDynLds)) != hipSuccess) return e;
         if ((e = set_lds(k_router<16>, kMaxDynLds)) != hipSuccess) return e;
-        if ((e = set_lds(k_down<8>, kDownHLdsBytes)) != hipSuccess) return e;
-        if ((e = set_lds(k_down<16>, kDownHLdsBytes)) != hipSuccess) return e;
+        if ((e = set_lds(k_down<kDownSuSmall>, kDownHLdsBytes)) != hipSuccess) return e;
+        if ((e = set_lds(k_down<kDownSuBig>, kDownHLdsBytes)) != hipSuccess) return e;
         return init_grouped_kernels();
     }();
     return once;
@@ -946,8 +949,9 @@ hipError_t launch_down(const DownArgs& a, hipStream_t st, const Timing* t) {
     DownArgs b = a;
     b.h_lds_bytes = (int)(need < kDownHLdsBytes ? need : kDownHLdsBytes);
     const dim3 g(a.H / kDownRowsPerBlock), blk(kDownThreads);
-    if (b.h_lds_bytes <= 8 * kDownThreads * 16) return launch(k_down<8>, g, blk, (size_t)b.h_lds_bytes, st, t, b);
-    return launch(k_down<16>, g, blk, (size_t)b.h_lds_bytes, st, t, b);
+    if (b.h_lds_bytes <= kDownSuSmall * kDownThreads * 16)
+        return launch(k_down<kDownSuSmall>, g, blk, (size_t)b.h_lds_bytes, st, t, b);
+    return launch(k_down<kDownSuBig>, g, blk, (size_t)b.h_lds_bytes, st, t, b);
 }
 
 hipError_t launch_dequant(Fp4Mat m, int n_experts, int rows, int cols, float* out, hipStream_t st) {
