@@ -560,20 +560,28 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
 // k_down (+ combine)
 // ---------------------------------------------------------------------------
 
-constexpr int kDownWaves = kDownThreads / 64;
-constexpr int kDownBatch = 3;  // tasks per wave whose codes are in flight together
-// staging passes of the two down instantiations: up to 64 KB of h, and the largest chunk
+// Two down shapes.  Up to 64 KB of staged h (K <= 2 at the 2048-hidden
+// shape): 16 waves with three tasks per wave in flight, which issues the
+// weight loads from more waves at once.  Larger chunks: 8 waves with six
+// tasks each, since 16 staging registers of h per thread at 16 waves would
+// exceed the 128 VGPRs a wave may hold there and spill.
+constexpr int kDownThreadsBig = 512;
+constexpr int kDownBatchSmall = 3;  // tasks per wave whose codes are in flight together
+constexpr int kDownBatchBig = 6;
+// staging passes of one float4 per thread that cover a chunk of each shape
 constexpr int kDownSuSmall = 64 * 1024 / (16 * kDownThreads);
-constexpr int kDownSuBig = kDownHLdsBytes / (16 * kDownThreads);
+constexpr int kDownSuBig = kDownHLdsBytes / (16 * kDownThreadsBig);
 
 // The h rows are processed in chunks that fit kDownHLdsBytes: positions
 // 0..n-1 are the routed slots in dedup order (h row p, length I), n..n+K-1
 // the shared expert's rows (length Is).
 // SU: staging passes of one float4 per thread that cover one chunk of h
-// (a.h_lds_bytes / 16 <= SU * kDownThreads, guaranteed by launch_down).
-template <int SU>
-__global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
+// (a.h_lds_bytes / 16 <= SU * NT, guaranteed by launch_down); NT threads per
+// workgroup; NB tasks per wave whose loads are in flight together.
+template <int SU, int NT, int NB>
+__global__ __launch_bounds__(NT) void k_down(DownArgs a) {
     constexpr int NH = kDownRowsPerBlock;
+    constexpr int kDownWaves = NT / 64;
     __shared__ float so[(kMaxSlots + kMaxRows) * NH];
     __shared__ int s_uniq[kMaxSlots];
     __shared__ int s_off[kMaxSlots + 1];
@@ -603,7 +611,7 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
     uint4 pf = make_uint4(0, 0, 0, 0);
     if (a.prefetch) {
         const int n16 = a.prefetch_bytes >> 4;
-        const int i = min((int)(blockIdx.x * kDownThreads + tid), n16 - 1);
+        const int i = min((int)(blockIdx.x * NT + tid), n16 - 1);
         pf = reinterpret_cast<const uint4*>(a.prefetch)[i];
     }
 
@@ -619,7 +627,7 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
     // thread cover a whole chunk; inside a pass the loads are unconditional
     // at clamped addresses, and columns past a shorter row's length are
     // staged as zeros.
-    static_assert(kDownHLdsBytes / 16 <= 16 * kDownThreads, "the largest h chunk exceeds 16 staging passes");
+    static_assert(SU <= 16, "more than 16 staging passes of h");
     const int q4 = RL / 4;                  // float4 per staged row (unpadded, a power of two)
     const int lq4 = __builtin_ctz(q4);
     float4 hv4[SU];
@@ -627,8 +635,8 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
         const int nf4 = (c1 - c0) * q4;
 #pragma unroll
         for (int j = 0; j < SU; ++j) {
-            if (j * kDownThreads < nf4) {  // uniform: passes past the chunk are skipped
-                const int f = min(j * kDownThreads + tid, nf4 - 1);
+            if (j * NT < nf4) {  // uniform: passes past the chunk are skipped
+                const int f = min(j * NT + tid, nf4 - 1);
                 const int rr = c0 + (f >> lq4), c4 = f & (q4 - 1);
                 const bool shared_row = rr >= n;
                 const int len4 = (shared_row ? Is : I) / 4;
@@ -641,10 +649,10 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
     load_h(0, min(total_rows, CAP));
 
     // routing metadata: every load of a thread issued before any is used
-    // (one round trip; n + 1 <= kMaxSlots + 1 <= 2 * kDownThreads)
-    static_assert(kMaxSlots + 1 <= 2 * kDownThreads, "metadata exceeds two entries per thread");
+    // (one round trip; n + 1 <= kMaxSlots + 1 <= 2 * NT)
+    static_assert(kMaxSlots + 1 <= 2 * NT, "metadata exceeds two entries per thread");
     {
-        const int i0 = tid, i1 = tid + kDownThreads;
+        const int i0 = tid, i1 = tid + NT;
         const int j0 = min(i0, n - 1), j1 = min(i1, n - 1);
         const int u0 = a.uniq[j0], u1 = a.uniq[j1];
         const int v0 = a.inv[j0], v1 = a.inv[j1];
@@ -682,16 +690,16 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
         const int nT = (u_hi - u_lo) * gI + (sh_here ? gS : 0);
 
         // codes, scales and tensor scales of this wave's first batch of tasks
-        uint4 code[kDownBatch];
-        uint32_t scl[kDownBatch];
-        float tsv[kDownBatch];
+        uint4 code[NB];
+        uint32_t scl[NB];
+        float tsv[NB];
         // every expert id of a batch is read from LDS before any of its
         // global loads is issued: one LDS wait per batch
-        int ev[kDownBatch];
+        int ev[NB];
         auto batch_ids = [&](int tb) {
 #pragma unroll
-            for (int i = 0; i < kDownBatch; ++i) {
-                const int t = (tb * kDownBatch + i) * kDownWaves + wave;
+            for (int i = 0; i < NB; ++i) {
+                const int t = (tb * NB + i) * kDownWaves + wave;
                 ev[i] = (t < (u_hi - u_lo) * gI) ? s_uniq[u_lo + (t >> lgG)] : 0;
             }
         };
@@ -701,8 +709,8 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
             // reads row n_base of routed expert 0 and a lane past the
             // workgroup's rows reads row n_base; neither result is stored.
 #pragma unroll
-            for (int i = 0; i < kDownBatch; ++i) {
-                const int t = (tb * kDownBatch + i) * kDownWaves + wave;
+            for (int i = 0; i < NB; ++i) {
+                const int t = (tb * NB + i) * kDownWaves + wave;
                 const bool routed = t < (u_hi - u_lo) * gI;
                 const bool shared_task = !routed && t < nT;
                 const int lgC = shared_task ? lgS : lgI;
@@ -729,7 +737,7 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
         const int nf4 = (c1 - c0) * q4;
 #pragma unroll
         for (int j = 0; j < SU; ++j) {
-            const int f = j * kDownThreads + tid;
+            const int f = j * NT + tid;
             if (f < nf4) {
                 const int rr = f >> lq4, c4 = f & (q4 - 1);
                 const int len4 = ((c0 + rr) >= n ? Is : I) / 4;
@@ -739,14 +747,14 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
         }
         __syncthreads();  // staged h visible to every wave
 
-        for (int tb = 0; tb * kDownWaves * kDownBatch < nT; ++tb) {
+        for (int tb = 0; tb * kDownWaves * NB < nT; ++tb) {
             if (tb > 0) {
                 batch_ids(tb);
                 load_batch(tb);
             }
 #pragma unroll
-            for (int i = 0; i < kDownBatch; ++i) {
-                const int t = (tb * kDownBatch + i) * kDownWaves + wave;
+            for (int i = 0; i < NB; ++i) {
+                const int t = (tb * NB + i) * kDownWaves + wave;
                 if (t >= nT) break;
                 const bool routed = t < (u_hi - u_lo) * gI;
                 const int lgC = routed ? lgI : lgS, CPR = 1 << lgC;
@@ -785,7 +793,7 @@ __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a) {
     }
 
     // combine: y = rs * sum_j w_j o_j (rank order) + shared (+ residual)
-    for (int i = tid; i < K * NH; i += kDownThreads) {
+    for (int i = tid; i < K * NH; i += NT) {
         const int r = i / NH, nl = i % NH, nn = n_base + nl;
         float acc = 0.0f;
         for (int j = 0; j < k; ++j) acc = fmaf(s_w[r * k + j], so[s_inv[r * k + j] * NH + nl], acc);
@@ -884,8 +892,10 @@ hipError_t init_kernels() {
         if ((e = set_lds(k_router<4>, kMaxDynLds)) != hipSuccess) return e;
         if ((e = set_lds(k_router<8>, kMaxDynLds)) != hipSuccess) return e;
         if ((e = set_lds(k_router<16>, kMaxDynLds)) != hipSuccess) return e;
-        if ((e = set_lds(k_down<kDownSuSmall>, kDownHLdsBytes)) != hipSuccess) return e;
-        if ((e = set_lds(k_down<kDownSuBig>, kDownHLdsBytes)) != hipSuccess) return e;
+        if ((e = set_lds(k_down<kDownSuSmall, kDownThreads, kDownBatchSmall>, kDownHLdsBytes)) != hipSuccess)
+            return e;
+        if ((e = set_lds(k_down<kDownSuBig, kDownThreadsBig, kDownBatchBig>, kDownHLdsBytes)) != hipSuccess)
+            return e;
         return init_grouped_kernels();
     }();
     return once;
@@ -948,10 +958,12 @@ hipError_t launch_down(const DownArgs& a, hipStream_t st, const Timing* t) {
     const long long need = (long long)n_rows * (RL / 32 * 36) * 4;
     DownArgs b = a;
     b.h_lds_bytes = (int)(need < kDownHLdsBytes ? need : kDownHLdsBytes);
-    const dim3 g(a.H / kDownRowsPerBlock), blk(kDownThreads);
+    const dim3 g(a.H / kDownRowsPerBlock);
     if (b.h_lds_bytes <= kDownSuSmall * kDownThreads * 16)
-        return launch(k_down<kDownSuSmall>, g, blk, (size_t)b.h_lds_bytes, st, t, b);
-    return launch(k_down<kDownSuBig>, g, blk, (size_t)b.h_lds_bytes, st, t, b);
+        return launch(k_down<kDownSuSmall, kDownThreads, kDownBatchSmall>, g, dim3(kDownThreads),
+                      (size_t)b.h_lds_bytes, st, t, b);
+    return launch(k_down<kDownSuBig, kDownThreadsBig, kDownBatchBig>, g, dim3(kDownThreadsBig),
+                  (size_t)b.h_lds_bytes, st, t, b);
 }
 
 hipError_t launch_dequant(Fp4Mat m, int n_experts, int rows, int cols, float* out, hipStream_t st) {
