@@ -560,16 +560,19 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
 // k_down (+ combine)
 // ---------------------------------------------------------------------------
 
-// Two down shapes.  Up to 64 KB of staged h (K <= 2 at the 2048-hidden
-// shape): 16 waves with three tasks per wave in flight, which issues the
-// weight loads from more waves at once.  Larger chunks: 8 waves with six
-// tasks each, since 16 staging registers of h per thread at 16 waves would
-// exceed the 128 VGPRs a wave may hold there and spill.
+// Three down shapes by the size of the staged h chunk.  16 waves issue the
+// weight loads from more waves at once: up to 64 KB of h (K <= 2 at the
+// 2048-hidden shape) with three tasks per wave in flight, up to 96 KB (K = 4)
+// with four, so that all of a chunk's tasks go out in one batch.  Larger
+// chunks: 8 waves with six tasks each, since at 16 waves the eight staging
+// registers of h per thread would exceed the 128 VGPRs a wave may hold there.
 constexpr int kDownThreadsBig = 512;
 constexpr int kDownBatchSmall = 3;  // tasks per wave whose codes are in flight together
+constexpr int kDownBatchMid = 4;
 constexpr int kDownBatchBig = 6;
 // staging passes of one float4 per thread that cover a chunk of each shape
 constexpr int kDownSuSmall = 64 * 1024 / (16 * kDownThreads);
+constexpr int kDownSuMid = 96 * 1024 / (16 * kDownThreads);
 constexpr int kDownSuBig = kDownHLdsBytes / (16 * kDownThreadsBig);
 
 // The h rows are processed in chunks that fit kDownHLdsBytes: positions
@@ -607,7 +610,9 @@ __global__ __launch_bounds__(NT) void k_down(DownArgs a) {
 
     // Bytes the next launch reads first (the next layer's router rows),
     // requested now so that they are in the memory-side cache when it starts;
-    // the value is consumed only by an empty asm statement at the end.
+    // the value is consumed only by an empty asm statement once the routing
+    // metadata below has arrived (vector loads complete in issue order, so
+    // that adds no wait, and the registers are free for the rest).
     uint4 pf = make_uint4(0, 0, 0, 0);
     if (a.prefetch) {
         const int n16 = a.prefetch_bytes >> 4;
@@ -628,16 +633,19 @@ __global__ __launch_bounds__(NT) void k_down(DownArgs a) {
     // at clamped addresses, and columns past a shorter row's length are
     // staged as zeros.
     static_assert(SU <= 16, "more than 16 staging passes of h");
+    static_assert(NT >= 512, "a staged row (up to 2048 floats) must fit in one pass");
     const int q4 = RL / 4;                  // float4 per staged row (unpadded, a power of two)
     const int lq4 = __builtin_ctz(q4);
+    // q4 <= NT, so a pass covers NT / q4 whole rows and this thread's row
+    // offset and column are the same in every pass
+    const int rpp = NT >> lq4, r0 = tid >> lq4, c4 = tid & (q4 - 1);
     float4 hv4[SU];
     auto load_h = [&](int c0, int c1) {
-        const int nf4 = (c1 - c0) * q4;
+        const int nr = c1 - c0;
 #pragma unroll
         for (int j = 0; j < SU; ++j) {
-            if (j * NT < nf4) {  // uniform: passes past the chunk are skipped
-                const int f = min(j * NT + tid, nf4 - 1);
-                const int rr = c0 + (f >> lq4), c4 = f & (q4 - 1);
+            if (j * rpp < nr) {  // uniform: passes past the chunk are skipped
+                const int rr = c0 + min(j * rpp + r0, nr - 1);
                 const bool shared_row = rr >= n;
                 const int len4 = (shared_row ? Is : I) / 4;
                 const int cc = min(c4, len4 - 1);
@@ -665,6 +673,7 @@ __global__ __launch_bounds__(NT) void k_down(DownArgs a) {
         if (i1 <= n) s_off[i1] = o1;
         if (tid == 0) s_U = nu;
     }
+    asm volatile("" ::"v"(pf.x), "v"(pf.y), "v"(pf.z), "v"(pf.w));  // the prefetch stays issued
     __syncthreads();
     const int U = s_U;
 
@@ -734,15 +743,16 @@ __global__ __launch_bounds__(NT) void k_down(DownArgs a) {
         if (c0 > 0) load_h(c0, c1);
         batch_ids(0);
         load_batch(0);
-        const int nf4 = (c1 - c0) * q4;
+        {
+            // one LDS address per thread, advanced by a uniform stride per pass
+            float* dst = hs + r0 * RLP + (c4 >> 3) * 36 + (c4 & 7) * 4;
 #pragma unroll
-        for (int j = 0; j < SU; ++j) {
-            const int f = j * NT + tid;
-            if (f < nf4) {
-                const int rr = f >> lq4, c4 = f & (q4 - 1);
-                const int len4 = ((c0 + rr) >= n ? Is : I) / 4;
-                *reinterpret_cast<float4*>(hs + (size_t)rr * RLP + (c4 >> 3) * 36 + (c4 & 7) * 4) =
-                    c4 < len4 ? hv4[j] : make_float4(0, 0, 0, 0);
+            for (int j = 0; j < SU; ++j) {
+                const int rr = j * rpp + r0;
+                if (rr < c1 - c0) {
+                    const int len4 = ((c0 + rr) >= n ? Is : I) / 4;
+                    *reinterpret_cast<float4*>(dst + j * rpp * RLP) = c4 < len4 ? hv4[j] : make_float4(0, 0, 0, 0);
+                }
             }
         }
         __syncthreads();  // staged h visible to every wave
@@ -811,7 +821,6 @@ __global__ __launch_bounds__(NT) void k_down(DownArgs a) {
         for (int nl = 0; nl < NH; ++nl) ss = fmaf(s_y[tid * NH + nl], s_y[tid * NH + nl], ss);
         a.ssq[tid * gridDim.x + blockIdx.x] = ss;
     }
-    asm volatile("" ::"v"(pf.x), "v"(pf.y), "v"(pf.z), "v"(pf.w));  // the prefetch stays issued
 }
 
 // ---------------------------------------------------------------------------
@@ -896,6 +905,8 @@ hipError_t init_kernels() {
             return e;
         if ((e = set_lds(k_down<kDownSuBig, kDownThreadsBig, kDownBatchBig>, kDownHLdsBytes)) != hipSuccess)
             return e;
+        if ((e = set_lds(k_down<kDownSuMid, kDownThreads, kDownBatchMid>, kDownHLdsBytes)) != hipSuccess)
+            return e;
         return init_grouped_kernels();
     }();
     return once;
@@ -961,6 +972,9 @@ hipError_t launch_down(const DownArgs& a, hipStream_t st, const Timing* t) {
     const dim3 g(a.H / kDownRowsPerBlock);
     if (b.h_lds_bytes <= kDownSuSmall * kDownThreads * 16)
         return launch(k_down<kDownSuSmall, kDownThreads, kDownBatchSmall>, g, dim3(kDownThreads),
+                      (size_t)b.h_lds_bytes, st, t, b);
+    if (b.h_lds_bytes <= kDownSuMid * kDownThreads * 16)
+        return launch(k_down<kDownSuMid, kDownThreads, kDownBatchMid>, g, dim3(kDownThreads),
                       (size_t)b.h_lds_bytes, st, t, b);
     return launch(k_down<kDownSuBig, kDownThreadsBig, kDownBatchBig>, g, dim3(kDownThreadsBig),
                   (size_t)b.h_lds_bytes, st, t, b);
