@@ -153,12 +153,16 @@ def test_layer_full_size_k2():
     _layer_case(inputs.LAGUNA, 2, 7, label="full")
 
 
-@pytest.mark.parametrize("K,regime", [(1, api.MOE_REGIME_AUTO), (4, api.MOE_REGIME_AUTO),
+@pytest.mark.parametrize("K,regime", [(1, api.MOE_REGIME_AUTO), (3, api.MOE_REGIME_AUTO), (4, api.MOE_REGIME_AUTO),
+                                      (5, api.MOE_REGIME_AUTO),
                                       (8, api.MOE_REGIME_VERIFY), (8, api.MOE_REGIME_AUTO),
                                       (16, api.MOE_REGIME_VERIFY), (16, api.MOE_REGIME_AUTO)])
 def test_layer_full_size_k_sweep_correlated_rows(K, regime):
     # from 8 rows the automatic regime runs the grouped kernels; the
-    # verify-width kernels are also checked at those widths
+    # verify-width kernels are also checked at those widths.  The down
+    # kernel's staged h (K*8 + K rows of 2304 bytes) picks its shape by size:
+    # 3 rows (62 KB) the largest 64 KB case, 4 rows (83 KB) the 96 KB case,
+    # 5 rows (104 KB) the first 8-wave case, 16 rows three chunks
     x = inputs.gen_x_correlated(K, inputs.LAGUNA.hidden, 31 + K, device=DEV)
     gpu, _, _ = _layer_case(inputs.LAGUNA, K, 31 + K, x=x, label="ksweep", regime=regime)
     assert int(gpu["n_unique"][0]) <= K * 8
