@@ -59,13 +59,14 @@ def test_stack_full_size_4_layers_k2():
     _stack_case(inputs.LAGUNA, 4, 2, 9, "full-4", 4)
 
 
-@pytest.mark.parametrize("K,regime", [(1, api.MOE_REGIME_AUTO), (8, api.MOE_REGIME_VERIFY), (8, api.MOE_REGIME_AUTO),
+@pytest.mark.parametrize("K,regime", [(1, api.MOE_REGIME_AUTO), (4, api.MOE_REGIME_AUTO), (5, api.MOE_REGIME_AUTO),
+                                      (8, api.MOE_REGIME_VERIFY), (8, api.MOE_REGIME_AUTO),
                                       (16, api.MOE_REGIME_VERIFY), (16, api.MOE_REGIME_AUTO)])
 def test_stack_full_size_6_layers_row_counts(K, regime):
     # verify widths other than the benchmark's two rows, through the RMSNorm
     # glue (sum-of-squares partials of every row, or the grouped combine's
     # normalised next input from 8 rows in the automatic regime) and the stack
-    # entry point
+    # entry point; 4 and 5 rows run the down kernel's 96 KB and 8-wave shapes
     _stack_case(inputs.LAGUNA, 6, K, 40 + K, "full-6-K%d-r%d" % (K, regime), 6, regime=regime)
 
 
