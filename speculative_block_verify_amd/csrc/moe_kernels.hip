@@ -560,17 +560,20 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
 // k_down (+ combine)
 // ---------------------------------------------------------------------------
 
-// Three down shapes by the size of the staged h chunk.  16 waves issue the
-// weight loads from more waves at once: up to 64 KB of h (K <= 2 at the
-// 2048-hidden shape) with three tasks per wave in flight, up to 96 KB (K = 4)
-// with four, so that all of a chunk's tasks go out in one batch.  Larger
-// chunks: 8 waves with six tasks each, since at 16 waves the eight staging
-// registers of h per thread would exceed the 128 VGPRs a wave may hold there.
+// Four down shapes by the size of the staged h chunk.  16 waves issue the
+// weight loads from more waves at once: up to 32 KB of h (K = 1 at the
+// 2048-hidden shape) with two tasks per wave in flight, up to 64 KB (K = 2)
+// with three, up to 96 KB (K = 4) with four, so that all of a chunk's tasks
+// go out in one batch with few unused slots.  Larger chunks: 8 waves with six
+// tasks each, since at 16 waves the eight staging registers of h per thread
+// would exceed the 128 VGPRs a wave may hold there.
 constexpr int kDownThreadsBig = 512;
-constexpr int kDownBatchSmall = 3;  // tasks per wave whose codes are in flight together
+constexpr int kDownBatchTiny = 2;   // tasks per wave whose codes are in flight together
+constexpr int kDownBatchSmall = 3;
 constexpr int kDownBatchMid = 4;
 constexpr int kDownBatchBig = 6;
 // staging passes of one float4 per thread that cover a chunk of each shape
+constexpr int kDownSuTiny = 32 * 1024 / (16 * kDownThreads);
 constexpr int kDownSuSmall = 64 * 1024 / (16 * kDownThreads);
 constexpr int kDownSuMid = 96 * 1024 / (16 * kDownThreads);
 constexpr int kDownSuBig = kDownHLdsBytes / (16 * kDownThreadsBig);
@@ -907,6 +910,8 @@ hipError_t init_kernels() {
             return e;
         if ((e = set_lds(k_down<kDownSuMid, kDownThreads, kDownBatchMid>, kDownHLdsBytes)) != hipSuccess)
             return e;
+        if ((e = set_lds(k_down<kDownSuTiny, kDownThreads, kDownBatchTiny>, kDownHLdsBytes)) != hipSuccess)
+            return e;
         return init_grouped_kernels();
     }();
     return once;
@@ -970,6 +975,9 @@ hipError_t launch_down(const DownArgs& a, hipStream_t st, const Timing* t) {
     DownArgs b = a;
     b.h_lds_bytes = (int)(need < kDownHLdsBytes ? need : kDownHLdsBytes);
     const dim3 g(a.H / kDownRowsPerBlock);
+    if (b.h_lds_bytes <= kDownSuTiny * kDownThreads * 16)
+        return launch(k_down<kDownSuTiny, kDownThreads, kDownBatchTiny>, g, dim3(kDownThreads),
+                      (size_t)b.h_lds_bytes, st, t, b);
     if (b.h_lds_bytes <= kDownSuSmall * kDownThreads * 16)
         return launch(k_down<kDownSuSmall, kDownThreads, kDownBatchSmall>, g, dim3(kDownThreads),
                       (size_t)b.h_lds_bytes, st, t, b);
