@@ -88,6 +88,13 @@ uint16_t orc_f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+/* n doubles -> binary32 -> bf16 (round to nearest even each time): the bf16
+ * output of a layer next to its fp32 result. */
+void orc_bf16_round(const double* y, int n, uint16_t* out) {
+    int i;
+    for (i = 0; i < n; ++i) out[i] = orc_f32_to_bf16((float)y[i]);
+}
+
 static double g_e2m1[16];
 static double g_e4m3[256];
 static int g_tables_ready = 0;
@@ -324,16 +331,24 @@ void orc_moe_layer(int K, int H, int E, int k, int I, int Is,
 }
 
 /* ------------------------------------------------------------------------ */
-/* O-9 stack glue: x_next = bf16(fp32(y / sqrt(mean(y^2) + eps))), gamma = 1  */
+/* O-9 stack glue: x_next = bf16(fp32(gamma * y / sqrt(mean(y^2) + eps)))    */
 /* ------------------------------------------------------------------------ */
 
-void orc_rmsnorm_bf16(const double* y, int K, int H, double eps, uint16_t* xout) {
+/* RMSNorm of each row of y (double), times the per-column weight gamma
+ * (bf16 [H]; NULL = all ones), rounded once to binary32 and then to bf16.
+ * The mean of squares runs over the row itself, before gamma: gamma scales
+ * the normalised row, it does not enter the norm. */
+void orc_rmsnorm_bf16(const double* y, int K, int H, double eps, const uint16_t* gamma, uint16_t* xout) {
     int r, n;
     for (r = 0; r < K; ++r) {
         const double* yr = y + (size_t)r * H;
         double ss = 0.0, inv;
         for (n = 0; n < H; ++n) ss += yr[n] * yr[n];
         inv = 1.0 / sqrt(ss / H + eps);
-        for (n = 0; n < H; ++n) xout[(size_t)r * H + n] = orc_f32_to_bf16((float)(yr[n] * inv));
+        for (n = 0; n < H; ++n) {
+            double v = yr[n] * inv;
+            if (gamma) v *= orc_bf16(gamma[n]);
+            xout[(size_t)r * H + n] = orc_f32_to_bf16((float)v);
+        }
     }
 }

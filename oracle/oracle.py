@@ -70,7 +70,8 @@ def lib():
         L.orc_expert_ffn.argtypes = [P, I, I] + [P, P, P] * 3 + [I, P]
         L.orc_moe_layer.restype = None
         L.orc_moe_layer.argtypes = [I] * 8 + [D, P, P, P] + [P, P, P] * 6 + [P, P, P, P, P]
-        L.orc_rmsnorm_bf16.restype = None; L.orc_rmsnorm_bf16.argtypes = [P, I, I, D, P]
+        L.orc_rmsnorm_bf16.restype = None; L.orc_rmsnorm_bf16.argtypes = [P, I, I, D, P, P]
+        L.orc_bf16_round.restype = None; L.orc_bf16_round.argtypes = [P, I, P]
         _lib = L
     return _lib
 
@@ -220,28 +221,53 @@ def moe_layer(w: Dict[str, object], x, top_k: int, score_fn: int = SCORE_SOFTMAX
     return {"logits": logits, "ids": ids, "w": wts, "y": y, "y32": y.astype(np.float32)}
 
 
-def rmsnorm_bf16(y, eps: float = 1e-6) -> np.ndarray:
+def rmsnorm_bf16(y, eps: float = 1e-6, gamma=None) -> np.ndarray:
+    """bf16(fp32(gamma * y / sqrt(mean(y^2) + eps))) per row; gamma bf16 [H]
+    bit patterns or None (ones)."""
     ya = np.ascontiguousarray(np.asarray(y, np.float64))
     K, H = ya.shape
+    g = _np(gamma, np.uint16)
+    if g is not None and g.size != H:
+        raise ValueError("gamma has %d entries, expected %d" % (g.size, H))
     out = np.empty((K, H), np.uint16)
-    lib().orc_rmsnorm_bf16(_p(ya), K, H, float(eps), _p(out))
+    lib().orc_rmsnorm_bf16(_p(ya), K, H, float(eps), _p(g), _p(out))
+    return out
+
+
+def bf16_round(y) -> np.ndarray:
+    """bf16 bit patterns of y rounded to binary32, then to bf16 (nearest, ties
+    to even): the bf16 output y of a layer next to its fp32 result."""
+    ya = np.ascontiguousarray(np.asarray(y, np.float64))
+    out = np.empty(ya.shape, np.uint16)
+    lib().orc_bf16_round(_p(ya), ya.size, _p(out))
     return out
 
 
 def moe_stack(layers: List[Dict[str, object]], x, top_k: int, eps: float = 1e-6,
               score_fn: int = SCORE_SOFTMAX, norm_topk: int = 1,
-              routed_scale: float = 1.0) -> List[Dict[str, np.ndarray]]:
-    """Free-running stack: layer l+1 consumes bf16(RMSNorm(y_l)) (gamma = 1,
-    no residual); the stack output is the last layer's y before any norm.
-    Returns one record per layer, each with its bf16 input under 'x_in'."""
+              routed_scale: float = 1.0, residual=None) -> List[Dict[str, np.ndarray]]:
+    """Free-running stack.  Layer l+1 consumes bf16(RMSNorm(y_l)) scaled by
+    layer l's norm weight ('norm_w', bf16 [H]; absent = ones); the stack
+    output is the last layer's y before any norm.
+
+    residual None: no residual anywhere.  residual given (bf16 [K, H]): the
+    decoder's residual stream of PR #844 section 4 item 4 -- layer 0 adds
+    `residual`, layer l >= 1 adds the previous layer's bf16 output
+    bf16(y_{l-1}), so the stream carried between layers is each layer's bf16
+    output.  Returns one record per layer with its bf16 input under 'x_in'
+    and its residual input (or None) under 'res_in'."""
     out = []
     xa = _np(x, np.uint16)
+    res = _np(residual, np.uint16)
     for l, w in enumerate(layers):
-        rec = moe_layer(w, xa, top_k, score_fn, norm_topk, routed_scale)
+        rec = moe_layer(w, xa, top_k, score_fn, norm_topk, routed_scale, residual=res)
         rec["x_in"] = xa
+        rec["res_in"] = res
         out.append(rec)
         if l + 1 < len(layers):
-            xa = rmsnorm_bf16(rec["y"], eps)
+            xa = rmsnorm_bf16(rec["y"], eps, w.get("norm_w"))
+            if res is not None:
+                res = bf16_round(rec["y"])
     return out
 
 

@@ -25,6 +25,10 @@ MUTATIONS = {
     "bias_in_weights": ("double v = 1.0 / (1.0 + exp(-(double)l[ids[(size_t)r * k + j]]));",
                         "double v = 1.0 / (1.0 + exp(-(double)l[ids[(size_t)r * k + j]])) + bias[ids[(size_t)r * k + j]];"),
     "dedup_slot_order": ("asg[pos] = s;\n                inv[s] = pos;", "asg[pos] = n - 1 - s;\n                inv[n - 1 - s] = pos;"),
+    "gamma_inside_norm": ("for (n = 0; n < H; ++n) ss += yr[n] * yr[n];",
+                          "for (n = 0; n < H; ++n) ss += yr[n] * yr[n] * (gamma ? orc_bf16(gamma[n]) * orc_bf16(gamma[n]) : 1.0);"),
+    "gamma_reversed": ("if (gamma) v *= orc_bf16(gamma[n]);", "if (gamma) v *= orc_bf16(gamma[H - 1 - n]);"),
+    "residual_dropped": ("yr[n] += orc_bf16(residual[(size_t)r * H + n]);", "yr[n] += 0.0 * orc_bf16(residual[(size_t)r * H + n]);"),
     "router_transposed": ("orc_bf16(wr[(size_t)e * H + h])", "orc_bf16(wr[(size_t)h * E % (E * H) + e])"),
     "down_transposed": ("orc_nvfp4_weight(dq, ds, dts, H, I, e, n, i)", "orc_nvfp4_weight(dq, ds, dts, H, I, e, (n + 1) % H, i)"),
 }

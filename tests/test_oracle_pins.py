@@ -359,13 +359,84 @@ def test_rmsnorm_output_has_unit_rms_and_is_scale_invariant():
     assert np.all(ref.bf16_to_f64(orc.rmsnorm_bf16(c, 0.0)) == 1.0)
 
 
+def test_rmsnorm_gamma_scales_the_normalised_row():
+    """RMSNorm with a weight: x = gamma * y / rms(y).  Pins: dividing the
+    output by gamma restores unit RMS (so gamma neither enters the norm nor
+    lands on another column), gamma = ones equals no gamma, and a
+    power-of-two gamma scales the bf16 output exactly."""
+    rng = np.random.default_rng(3)
+    H = 256
+    y = rng.standard_normal((3, H)) * 5.0
+    gv = rng.uniform(0.5, 2.0, H)
+    gamma = ref.f32_to_bf16_bits(gv)
+    x = ref.bf16_to_f64(orc.rmsnorm_bf16(y, 1e-6, gamma))
+    ratio = x / ref.bf16_to_f64(gamma)[None, :]
+    np.testing.assert_allclose(np.sqrt((ratio ** 2).mean(1)), 1.0, atol=2 ** -8)
+    # column by column: each output is its own column's gamma times the plain norm
+    plain = ref.bf16_to_f64(orc.rmsnorm_bf16(y, 1e-6))
+    np.testing.assert_allclose(ratio, plain, rtol=2 ** -7)
+    ones = ref.f32_to_bf16_bits(np.ones(H))
+    np.testing.assert_array_equal(orc.rmsnorm_bf16(y, 1e-6, ones), orc.rmsnorm_bf16(y, 1e-6))
+    twos = ref.f32_to_bf16_bits(np.full(H, 2.0))
+    np.testing.assert_array_equal(ref.bf16_to_f64(orc.rmsnorm_bf16(y, 1e-6, twos)), 2.0 * plain)
+
+
 def test_stack_feeds_normalised_output_forward():
     layers = inputs.gen_stack(SMALL, 3, 55)
     x = inputs.gen_x(2, SMALL.hidden, 55)
     recs = orc.moe_stack(layers, x, SMALL.top_k)
     for l in range(1, 3):
         np.testing.assert_array_equal(recs[l]["x_in"], orc.rmsnorm_bf16(recs[l - 1]["y"]))
+        assert recs[l]["res_in"] is None
     np.testing.assert_array_equal(recs[0]["x_in"], x.numpy().view(np.uint16))
+
+
+def _silent(layer):
+    """A copy of a layer whose down projections (routed and shared) have
+    tensor scale 0: every expert FFN then outputs exactly zero."""
+    w = dict(layer)
+    for m in ("down", "sh_down"):
+        if w.get(m) is not None:
+            w[m] = dict(w[m], ts=torch.zeros_like(w[m]["ts"]))
+    return w
+
+
+def test_stack_residual_stream_passes_through_silent_layers():
+    """Residual stream (the decoder residual of PR #844 section 4 item 4):
+    with every FFN output zero, each layer's output is exactly its residual
+    input, so the stream carries the initial residual unchanged; after a
+    live layer 0, a silent layer 1 outputs layer 0's bf16 output (not the
+    initial residual); without a residual, silent layers output zero."""
+    layers = inputs.gen_stack(SMALL, 3, 56)
+    x = inputs.gen_x(2, SMALL.hidden, 56)
+    res = inputs.gen_x(2, SMALL.hidden, 57, tag="res")
+    r64 = ref.bf16_to_f64(res.numpy())
+    recs = orc.moe_stack([_silent(w) for w in layers], x, SMALL.top_k, residual=res)
+    for l in range(3):
+        np.testing.assert_array_equal(recs[l]["y"], r64)
+        np.testing.assert_array_equal(recs[l]["res_in"], res.numpy().view(np.uint16))
+    recs = orc.moe_stack([layers[0], _silent(layers[1])], x, SMALL.top_k, residual=res)
+    y0 = recs[0]["y"]
+    assert np.abs(y0 - r64).max() > 1e-3          # layer 0 adds its FFN output
+    np.testing.assert_array_equal(recs[1]["y"], ref.bf16_to_f64(ref.f32_to_bf16_bits(y0.astype(np.float32))))
+    recs = orc.moe_stack([_silent(w) for w in layers], x, SMALL.top_k)
+    for l in range(3):
+        assert np.all(recs[l]["y"] == 0.0)
+
+
+def test_stack_uses_each_layers_norm_weight():
+    """Layer l's norm weight scales the input of layer l + 1 only."""
+    layers = inputs.gen_stack(SMALL, 3, 58)
+    rng = np.random.default_rng(58)
+    for w in layers:
+        w["norm_w"] = torch.as_tensor(ref.f32_to_bf16_bits(rng.uniform(0.5, 2.0, SMALL.hidden)).astype(np.int16))
+    x = inputs.gen_x(2, SMALL.hidden, 58)
+    recs = orc.moe_stack(layers, x, SMALL.top_k)
+    for l in range(1, 3):
+        g = ref.bf16_to_f64(layers[l - 1]["norm_w"].numpy())
+        ratio = ref.bf16_to_f64(recs[l]["x_in"]) / g[None, :]
+        plain = ref.bf16_to_f64(orc.rmsnorm_bf16(recs[l - 1]["y"]))
+        np.testing.assert_allclose(ratio, plain, rtol=2 ** -7, atol=1e-30)
 
 
 # ---------------------------------------------------------------------------
