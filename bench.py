@@ -52,7 +52,7 @@ def gateup_bytes(shape, n_unique, K):
 
 
 KERNEL_SOURCES = ("speculative_block_verify_amd/csrc/moe_kernels.hip", "speculative_block_verify_amd/csrc/moe_device.h",
-                  "speculative_block_verify_amd/csrc/moe_internal.h")
+                  "speculative_block_verify_amd/csrc/moe_internal.h", "speculative_block_verify_amd/csrc/moe_abi.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_gateup_moe_stack_k2_hbm_traffic.txt")
 
 
@@ -99,6 +99,72 @@ def copy_calibration(mib):
 
 
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
+DTYPE = "nvfp4 weights, bf16 x, f16-MFMA/f32-acc gate-up, f32 down"
+
+
+def host_info():
+    """The host the oracle runs on: logical cores, CPU model."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"host_cores": os.cpu_count(), "cpu_model": model,
+            "affinity_cores": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
+def weight_hashes(layers):
+    """xxh3-64 of each layer's packed weight bytes (router, every NVFP4
+    matrix's codes, scales and tensor scales, norm weight), in a fixed
+    order: the record names the exact inputs it measured."""
+    import xxhash
+    out = []
+    for w in layers:
+        h = xxhash.xxh3_64()
+        for name in ("router_w", "router_bias", "gate", "up", "down", "sh_gate", "sh_up", "sh_down", "norm_w"):
+            v = w.get(name)
+            if v is None:
+                continue
+            for t in ([v[k] for k in ("q", "s", "ts")] if isinstance(v, dict) else [v]):
+                h.update(t.contiguous().cpu().numpy().tobytes())
+        out.append(h.hexdigest())
+    return out
+
+
+def stream_read_ceiling(dev, gib=4, reps=5):
+    """A measured streaming-read rate on this GPU: the library's plain read
+    kernel (moe_verify_stream_read) over a gib-GiB buffer, best of reps."""
+    import torch
+    from speculative_block_verify_amd import api
+    buf = torch.empty(gib * (1 << 30), dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    api.moe_verify_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        api.moe_verify_stream_read(buf, sink)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    del buf
+    torch.cuda.empty_cache()
+    return round(gib * (1 << 30) / (best / 1e3) / 1e9, 1)
+
+
+def near_tie_rows(logits, k, rtol=1e-5):
+    """Rows whose k-th and (k+1)-th largest router logits differ by less than
+    rtol * max|logit| (selection there may legitimately go either way)."""
+    import numpy as np
+    l = np.sort(np.asarray(logits, np.float64), axis=-1)[..., ::-1]
+    gap = l[..., k - 1] - l[..., k]
+    return int((gap < rtol * np.abs(l).max(axis=-1)).sum())
 
 
 def prefill(args):
@@ -151,7 +217,7 @@ def prefill(args):
         "metric": "prefill grouped GEMM: weight GB/s and % HBM peak, MFMA utilisation (512 rows)",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(total_ms / args.steps, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f16 mfma / f32 acc", "data": "synthetic",
+        "vs_baseline": None, "dtype": DTYPE, "data": "synthetic",
         "config": {"workload": "one NVFP4 MoE layer on 512 token rows (prefill grouped GEMM)", "rows": T,
                    "hidden": H, "experts": E, "top_k": k, "inter": I, "shared_inter": Is,
                    "layer_weight_sets": NL, "input_pool": POOL},
@@ -164,41 +230,87 @@ def prefill(args):
     }), flush=True)
 
 
-def cpu_baseline(layers, xs, shape, K, budget_s, gpu_layer0=None):
-    """The oracle (single-threaded C, fp64) chained through the same 40-layer
-    stack, input after input of the pool, until budget_s seconds of CPU work;
-    GB/s over the same algorithmic byte definition as the GPU figure.  With
-    gpu_layer0 (the GPU's fp32 output of the first layer on the first input),
-    also the parity of that layer against the oracle's."""
+def cpu_baseline(layers, x0, shape, K, runs=3, gpu_layer0=None, gpu_us_per_stack=None, gpu_gbs=None):
+    """The oracle (single-threaded C, fp64), pinned to one host core, chained
+    through the whole 40-layer stack on the pool's first input, `runs` times;
+    the median run gives µs per stack and GB/s over the same algorithmic
+    byte definition as the GPU figure.  With gpu_layer0 (the GPU's fp32
+    output of the first layer on that input), also the parity of that layer
+    against the oracle's."""
     import oracle as orc
     import numpy as np
     from speculative_block_verify_amd import api
     cfg = api.make_cfg(shape, K)
     host = [{k: (None if v is None else ({kk: vv.cpu() for kk, vv in v.items()} if isinstance(v, dict) else v.cpu()))
              for k, v in w.items()} for w in layers]
-    t_total, n_bytes, n_layers, n_inputs = 0.0, 0, 0, 0
-    parity = None
-    while t_total < budget_s and n_inputs < len(xs):
-        xo = xs[n_inputs].cpu().numpy().view(np.uint16)
-        n_inputs += 1
-        for wh in host:
-            t0 = time.perf_counter()
-            rec = orc.moe_layer(wh, xo, shape.top_k)
-            if gpu_layer0 is not None and parity is None:
-                ref = np.asarray(rec["y"], dtype=np.float64)
-                d = np.asarray(gpu_layer0, dtype=np.float64) - ref
-                parity = {"layer": 0, "input": 0, "max_abs_over_max_ref": float(np.abs(d).max() / np.abs(ref).max()),
-                          "rel_l2": float(np.linalg.norm(d) / np.linalg.norm(ref)), "bar": 2e-3}
-            xo = orc.rmsnorm_bf16(rec["y"])
-            t_total += time.perf_counter() - t0
-            U = orc.dedup(rec["ids"], shape.n_experts)["n_unique"]
-            n_bytes += api.moe_verify_weight_bytes(cfg, U, K)
-            n_layers += 1
-            if t_total >= budget_s:
-                break
-    return {"value": n_bytes / t_total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "%d layer evaluations (the 40-layer stack chained over %d inputs of the pool), K=%d; "
-                      "%.1f s single-threaded" % (n_layers, n_inputs, K, t_total)}, parity
+    info = host_info()
+    core = None
+    old_aff = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else None
+    if old_aff:
+        core = max(old_aff)
+        os.sched_setaffinity(0, {core})
+    times, parity, n_bytes = [], None, 0
+    try:
+        for run in range(runs):
+            xo = x0.cpu().numpy().view(np.uint16)
+            t_run, b_run = 0.0, 0
+            for l, wh in enumerate(host):
+                t0 = time.perf_counter()
+                rec = orc.moe_layer(wh, xo, shape.top_k)
+                xo = orc.rmsnorm_bf16(rec["y"])
+                t_run += time.perf_counter() - t0
+                if gpu_layer0 is not None and parity is None:
+                    ref = np.asarray(rec["y"], dtype=np.float64)
+                    d = np.asarray(gpu_layer0, dtype=np.float64) - ref
+                    parity = {"layer": 0, "input": 0,
+                              "max_abs_over_max_ref": float(np.abs(d).max() / np.abs(ref).max()),
+                              "rel_l2": float(np.linalg.norm(d) / np.linalg.norm(ref)), "bar": 2e-3}
+                b_run += api.moe_verify_weight_bytes(cfg, orc.dedup(rec["ids"], shape.n_experts)["n_unique"], K)
+            times.append(t_run)
+            n_bytes = b_run
+            log("bench: oracle run %d: %.2f s for the %d-layer stack" % (run + 1, t_run, len(host)))
+    finally:
+        if old_aff:
+            os.sched_setaffinity(0, old_aff)
+    med = statistics.median(times)
+    us_stack = med * 1e6
+    out = {"value": round(n_bytes / med / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": "the %d-layer stack chained on the first input of the pool, K=%d, %d runs, median; "
+                     "single-threaded C (fp64), pinned to core %s" % (len(host), K, runs, core),
+           "us_per_stack": round(us_stack, 1), "us_per_layer": round(us_stack / len(host), 1),
+           "runs_s": [round(t, 3) for t in times], "pinned_core": core}
+    out.update(info)
+    if gpu_us_per_stack:
+        out["gpu_speedup"] = round(us_stack / gpu_us_per_stack, 1)
+    return out, parity
+
+
+def single_layer_timing(cfg, wts, xs, y, ws, y32, reps=3):
+    """One verify layer (the 2-row configuration) on its own: a graph per
+    weight set (each a one-layer stack), launched in rotation over the 40
+    sets and the input pool, every launch bracketed by events on the stream.
+    Returns the median and min µs per layer."""
+    import torch
+    from speculative_block_verify_amd import api
+    graphs = [[api.StackGraph(cfg, [w], x, y, ws, y32=y32) for x in xs[:2]] for w in wts]
+    stream = torch.cuda.current_stream()
+    for g in graphs:
+        g[0].launch()
+    torch.cuda.synchronize()
+    times = []
+    for r in range(reps):
+        for i, g in enumerate(graphs):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g[(i + r) % 2].launch()
+            b.record(stream)
+            times.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in times)
+    for g in graphs:
+        for h in g:
+            h.close()
+    return {"median": round(statistics.median(ms) * 1e3, 2), "min": round(ms[0] * 1e3, 2), "launches": len(ms)}
 
 
 def main():
@@ -206,8 +318,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the single-layer timing, the streaming-read ceiling and the weight hashes")
     ap.add_argument("--timing-steps", type=int, default=16, help="steps of the per-kernel timing pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
@@ -253,24 +366,35 @@ def main():
     y = torch.empty(K, shape.hidden, dtype=torch.int16, device=dev)
     y32 = torch.empty(K, shape.hidden, dtype=torch.float32, device=dev)
 
-    # unique-expert counts per (input, layer) from the dedup pass
+    # unique-expert counts and router logits per (input, layer) from the
+    # debug copies of a direct stack call
+    import numpy as np
     nu = torch.empty(L, dtype=torch.int32, device=dev)
     y32_layers = torch.empty(L, K, shape.hidden, dtype=torch.float32, device=dev)
-    step_bytes, gu_bytes, uniques = [], [], []
+    lg_layers = torch.empty(L, K, shape.n_experts, dtype=torch.float32, device=dev)
+    step_bytes, gu_bytes, uniques, logits_all = [], [], [], []
     gpu_layer0 = None
     for i in range(POOL):
-        dbg = api.make_debug(n_unique=nu, y32=y32_layers) if i == 0 else api.make_debug(n_unique=nu)
+        dbg = api.make_debug(n_unique=nu, logits=lg_layers, **({"y32": y32_layers} if i == 0 else {}))
         api.moe_verify_stack(cfg, wts, xs[i], y, ws, y32=y32, debug=dbg)
-        if i == 0:
-            torch.cuda.synchronize()
-            gpu_layer0 = y32_layers[0].cpu().numpy()
         torch.cuda.synchronize()
+        if i == 0:
+            gpu_layer0 = y32_layers[0].cpu().numpy()
         U = nu.cpu().tolist()
         uniques.append(U)
+        logits_all.append(lg_layers.cpu().numpy())
         step_bytes.append(sum(api.moe_verify_weight_bytes(cfg, u, K) for u in U))
         gu_bytes.append([gateup_bytes(shape, u, K) for u in U])
+    logits_all = np.stack(logits_all)                     # [POOL, L, K, E]
+    u_by_layer = np.asarray(uniques, np.float64).mean(axis=0)
     log("bench: unique experts per layer (mean) %.2f; bytes per step %.4f GB" % (
-        sum(map(sum, uniques)) / (POOL * L), sum(step_bytes) / POOL / 1e9))
+        u_by_layer.mean(), sum(step_bytes) / POOL / 1e9))
+    ties = near_tie_rows(logits_all, shape.top_k)
+    logit_dev = None
+    if K > 2:
+        # realised deviation of the correlated rows' logits from row 0's
+        cp = logits_all[:, :, 1:K // 2 + 1, :] - logits_all[:, :, :1, :]
+        logit_dev = [round(float(v), 5) for v in cp.std(axis=(0, 2, 3))]
 
     graphs = [api.StackGraph(cfg, wts, xs[i], y, ws, y32=y32) for i in range(POOL)]
     for s in range(args.warmup):
@@ -291,6 +415,8 @@ def main():
     total_ms = evs[0].elapsed_time(evs[-1])
     total_bytes = sum(step_bytes[s % POOL] for s in range(args.steps))
     gbs = total_bytes / (total_ms / 1e3) / 1e9
+    med_ms = statistics.median(per_step_ms)
+    stalls = sum(1 for t in per_step_ms if t > 4 * med_ms)
     log("bench: %d steps in %.3f ms (wall %.3f ms): %.1f GB/s, %.1f us/stack" % (
         args.steps, total_ms, wall * 1e3, gbs, total_ms / args.steps * 1e3))
 
@@ -320,6 +446,17 @@ def main():
     for g in graphs:
         g.close()
 
+    one_layer = None
+    if K == 2 and not args.no_extras:
+        one_layer = single_layer_timing(cfg, wts, xs, y, ws, y32)
+        one_layer["gbs"] = round(sum(step_bytes) / POOL / L / (one_layer["median"] / 1e6) / 1e9, 1)
+        log("bench: single layer %.2f us (median), %.1f GB/s" % (one_layer["median"], one_layer["gbs"]))
+    ceiling = None if args.no_extras else stream_read_ceiling(dev)
+    if ceiling:
+        log("bench: streaming-read ceiling %.1f GB/s" % ceiling)
+    hashes = None if args.no_extras else weight_hashes(layers)
+
+    us_stack = total_ms / args.steps * 1e3
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -331,7 +468,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": DTYPE,
         "data": "synthetic",
         "config": {"workload": "40-layer NVFP4 MoE verify stack, K=%d rows%s" % (
                        K, "" if K == 2 else " (K sweep: rows 1..K/2 repeat row 0 plus noise)"), "hidden": shape.hidden,
@@ -339,24 +476,33 @@ def main():
                    "shared_inter": shape.shared_inter, "layers": L, "rows": K, "input_pool": POOL,
                    "weights": "NVFP4 (E2M1 + E4M3/16 + fp32 tensor scale), bf16 router/activations"},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "us_per_stack": {"mean": round(total_ms / args.steps * 1e3, 2),
-                         "median": round(statistics.median(per_step_ms) * 1e3, 2),
+        "us_per_stack": {"mean": round(us_stack, 2),
+                         "median": round(med_ms * 1e3, 2),
                          "min": round(min(per_step_ms) * 1e3, 2), "max": round(max(per_step_ms) * 1e3, 2)},
+        "stall_steps_over_4x_median": stalls,
         "bytes_per_step": round(sum(step_bytes) / POOL),
-        "unique_experts_per_layer": round(sum(map(sum, uniques)) / (POOL * L), 3),
+        "unique_experts_per_layer": round(float(u_by_layer.mean()), 3),
+        "unique_experts_by_layer": [round(float(u), 2) for u in u_by_layer],
+        "no_dedup_slots_per_layer": K * shape.top_k,
+        "near_tie_rows": {"count": ties, "of": int(POOL * L * K), "rule": "k-th/(k+1)-th logit gap < 1e-5 max|l|"},
         "kernel_us": None if avg is None else {k: round(v * 1e3, 3) for k, v in avg.items()},
+        "single_layer_us": one_layer,
+        "stream_read_ceiling_gbs": ceiling,
         "roofline": None if avg is None else {
             "bound": "hbm", "kernel": "k_gateup", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic() if K == 2 else None, "bytes_per_launch": round(gu_avg_bytes)},
         "wall_s": round(wall, 4),
     }
+    if logit_dev is not None:
+        result["correlated_row_logit_dev_by_layer"] = logit_dev
     result["seed"] = SEED
+    result["weight_xxh3_by_layer"] = hashes
     result["device"] = torch.cuda.get_device_name(dev)
     result["rocm"] = torch.version.hip
     if not args.no_cpu_baseline:
-        log("bench: timing the oracle on the host (%.0f s budget)" % args.cpu_seconds)
-        result["cpu_baseline"], result["parity"] = cpu_baseline(layers, xs, shape, K, args.cpu_seconds, gpu_layer0)
+        log("bench: timing the oracle on the host (3 runs of the stack on one pinned core)")
+        result["cpu_baseline"], result["parity"] = cpu_baseline(layers, xs[0], shape, K, 3, gpu_layer0, us_stack, gbs)
     print(json.dumps(result), flush=True)
 
 

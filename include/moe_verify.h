@@ -23,8 +23,21 @@
  *        y[r] = routed_scale * sum_j w[r][j] * o[r][j]  + shared[r]
  *               (+ residual[r])
  *      summed over j in rank order (deterministic; no atomics).
- *   9. stack glue: layer l+1 consumes bf16(RMSNorm(y_l)), eps = rms_eps,
- *      gamma = 1, no residual; the stack returns the last layer's y.
+ *   9. stack glue: layer l+1 consumes bf16(gamma_l * RMSNorm(y_l)), eps =
+ *      rms_eps, gamma_l = layer l's norm_w (ones when NULL); optionally the
+ *      decoder's residual stream (PR #844 section 4 item 4): layer 0 adds
+ *      the caller's residual, layer l >= 1 adds bf16(y_{l-1}); the stack
+ *      returns the last layer's y.
+ *
+ * Activation range.  bf16 activations of any finite magnitude are accepted.
+ * On the matrix cores (gate/up) each row enters as fp16 of x * 2^-sig, sig
+ * = ilogb(max_row |x|) - 14: values within 2^-28 of the row's largest
+ * magnitude are exact, smaller ones keep an absolute precision of
+ * 2^-24 * 2^sig (below 2^-38 of the row maximum), nothing overflows; the
+ * sums are multiplied by 2^sig.  Intermediates are fp32: outputs whose true
+ * value exceeds the fp32 range (SwiGLU is quadratic in x, so |x| beyond
+ * about 1e17 at the benchmark's weight scale) come out infinite, as in any
+ * fp32 evaluation.
  *
  * Conventions for every entry point.
  *  - All array pointers are DEVICE pointers owned by the caller; the structs
@@ -110,6 +123,10 @@ typedef struct moe_layer_weights {
                                   must be NULL otherwise */
     moe_nvfp4 gate, up, down;  /* E experts */
     moe_nvfp4 sh_gate, sh_up, sh_down;  /* one expert; all NULL iff shared_inter == 0 */
+    const uint16_t* norm_w;    /* stack only: bf16 [H] RMSNorm weight applied to this
+                                  layer's output to form the next layer's input;
+                                  NULL = ones.  Ignored for the last layer of a
+                                  stack and by the single-layer entry points. */
 } moe_layer_weights;
 
 /* Outputs of the selection step (device arrays, K = rows of the call):
@@ -131,7 +148,9 @@ typedef struct moe_route_out {
 /* Optional per-layer copies of intermediates (device arrays, any may be
  * NULL).  For a stack of L layers each array holds L consecutive per-layer
  * blocks of the sizes in moe_route_out (logits: [K][E] fp32), plus
- * x_in [K][H] bf16 (the layer's input) and y32 [K][H] fp32 (its output). */
+ * x_in [K][H] bf16 (the layer's input), y32 [K][H] fp32 (its output) and
+ * res_in [K][H] bf16 (the residual it added; written only when the call has
+ * a residual). */
 typedef struct moe_debug {
     float* logits;
     int32_t* ids;
@@ -143,6 +162,7 @@ typedef struct moe_debug {
     int32_t* inv;
     uint16_t* x_in;
     float* y32;
+    uint16_t* res_in;
 } moe_debug;
 
 /* Bytes of device workspace that layer/stack/route calls with this cfg need
@@ -180,12 +200,16 @@ MOE_API int moe_verify_layer_grouped(const moe_cfg* cfg, const moe_layer_weights
                                      const moe_debug* dbg);
 
 /* n_layers layers (steps 1-9).  layers is a HOST array of n_layers weight
- * structs.  Writes the last layer's output to y (bf16) and y32 (fp32, may be
- * NULL).  dbg may be NULL.  K and cfg->regime pick the kernels as in
- * moe_verify_layer. */
+ * structs.  x bf16 [K][H] is layer 0's input.  residual (bf16 [K][H]) NULL:
+ * no residual anywhere; given: the residual stream -- layer 0 adds
+ * `residual`, layer l >= 1 adds layer l-1's bf16 output (the decoder
+ * residual of PR #844 section 4 item 4 carried through the stack).  Layer
+ * l+1's input is bf16(norm_w_l * RMSNorm(y_l)).  Writes the last layer's
+ * output to y (bf16) and y32 (fp32, may be NULL).  dbg may be NULL.  K and
+ * cfg->regime pick the kernels as in moe_verify_layer. */
 MOE_API int moe_verify_stack(const moe_cfg* cfg, const moe_layer_weights* layers, int32_t n_layers,
-                     const uint16_t* x, int32_t K, uint16_t* y, float* y32, void* workspace,
-                     size_t workspace_bytes, void* stream, const moe_debug* dbg);
+                     const uint16_t* x, const uint16_t* residual, int32_t K, uint16_t* y, float* y32,
+                     void* workspace, size_t workspace_bytes, void* stream, const moe_debug* dbg);
 
 /* Profiling aid: the work of moe_verify_stack (no debug copies), with each
  * kernel launched so that a start/stop event pair carries that kernel's own
@@ -194,8 +218,17 @@ MOE_API int moe_verify_stack(const moe_cfg* cfg, const moe_layer_weights* layers
  * gate/up + SwiGLU, down + combine).  Verify-width kernels only
  * (MOE_ERR_UNSUPPORTED when K and cfg->regime pick the grouped ones). */
 MOE_API int moe_verify_stack_timed(const moe_cfg* cfg, const moe_layer_weights* layers, int32_t n_layers,
-                                   const uint16_t* x, int32_t K, uint16_t* y, float* y32, void* workspace,
-                                   size_t workspace_bytes, void* stream, float* kernel_ms);
+                                   const uint16_t* x, const uint16_t* residual, int32_t K, uint16_t* y,
+                                   float* y32, void* workspace, size_t workspace_bytes, void* stream,
+                                   float* kernel_ms);
+
+/* Measurement aid: read `bytes` (a positive multiple of 16) of device memory
+ * at src (16-byte aligned) once, as a plain streaming read with every
+ * workgroup keeping several 16-byte loads per thread in flight; the XOR of
+ * the data is XORed into the device word *sink (so the reads cannot be
+ * dropped).  Timed by the caller: the read ceiling the layer's bandwidth
+ * figures are compared with.  Asynchronous on `stream`. */
+MOE_API int moe_verify_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 /* Selection only (steps 2-3) from given fp32 logits [K][E] (device), with
  * the same device code the layer uses.  bias as in moe_layer_weights.  For
@@ -206,18 +239,24 @@ MOE_API int moe_verify_route(const moe_cfg* cfg, const float* logits, const floa
                      const moe_route_out* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Step 4 alone: dequantise n_experts expert matrices of rows x cols into
- * fp32 out [E][rows][cols] with the decode the GEMM kernels use
- * (e2m1 * e4m3 exactly, then one fp32 multiply by ts). */
+ * fp32 out [E][rows][cols]: e2m1(code) * e4m3(scale), then one fp32 multiply
+ * by ts.  The product is formed by each decode the GEMM kernels use -- the
+ * fp32 convert and multiply of the down kernels, the bf16 convert, and the
+ * fp16 operand decode of the gate/up matrix-core tiles (fp16 convert, then a
+ * packed fp16 multiply by the scale) -- and is NaN where they disagree.
+ * (In the GEMMs the tensor scale, and in the verify-width down kernel also
+ * the block scale, multiply partial sums rather than each weight.) */
 MOE_API int moe_verify_dequant_nvfp4(const moe_nvfp4* m, int32_t n_experts, int32_t rows, int32_t cols,
                              float* out, void* stream);
 
-/* A captured stack launch (hipGraph).  It bakes in cfg, the weight pointers,
- * K, x, y, y32 and the workspace; re-create it when any of them changes.
- * A handle must not be launched from two threads at once. */
+/* A captured stack launch (hipGraph) of moe_verify_stack.  It bakes in cfg,
+ * the weight pointers, K, x, residual, y, y32 and the workspace; re-create
+ * it when any of them changes.  A handle must not be launched from two
+ * threads at once. */
 typedef struct moe_stack_graph moe_stack_graph;
 MOE_API int moe_stack_graph_create(const moe_cfg* cfg, const moe_layer_weights* layers, int32_t n_layers,
-                           const uint16_t* x, int32_t K, uint16_t* y, float* y32, void* workspace,
-                           size_t workspace_bytes, void* stream, moe_stack_graph** out);
+                           const uint16_t* x, const uint16_t* residual, int32_t K, uint16_t* y, float* y32,
+                           void* workspace, size_t workspace_bytes, void* stream, moe_stack_graph** out);
 MOE_API int moe_stack_graph_launch(moe_stack_graph* g, void* stream);
 MOE_API void moe_stack_graph_destroy(moe_stack_graph* g);
 

@@ -46,7 +46,8 @@ class moe_cfg(ctypes.Structure):
 class moe_layer_weights(ctypes.Structure):
     _fields_ = [("router_w", _c_void_p), ("router_bias", _c_void_p),
                 ("gate", moe_nvfp4), ("up", moe_nvfp4), ("down", moe_nvfp4),
-                ("sh_gate", moe_nvfp4), ("sh_up", moe_nvfp4), ("sh_down", moe_nvfp4)]
+                ("sh_gate", moe_nvfp4), ("sh_up", moe_nvfp4), ("sh_down", moe_nvfp4),
+                ("norm_w", _c_void_p)]
 
 
 class moe_route_out(ctypes.Structure):
@@ -57,11 +58,11 @@ class moe_route_out(ctypes.Structure):
 class moe_debug(ctypes.Structure):
     _fields_ = [("logits", _c_void_p), ("ids", _c_void_p), ("w", _c_void_p), ("n_unique", _c_void_p),
                 ("uniq", _c_void_p), ("off", _c_void_p), ("asg", _c_void_p), ("inv", _c_void_p),
-                ("x_in", _c_void_p), ("y32", _c_void_p)]
+                ("x_in", _c_void_p), ("y32", _c_void_p), ("res_in", _c_void_p)]
 
 
 EXPORTS = ["moe_verify_workspace_bytes", "moe_verify_layer", "moe_verify_layer_grouped", "moe_verify_stack",
-           "moe_verify_stack_timed", "moe_verify_route",
+           "moe_verify_stack_timed", "moe_verify_route", "moe_verify_stream_read",
            "moe_verify_dequant_nvfp4", "moe_stack_graph_create", "moe_stack_graph_launch",
            "moe_stack_graph_destroy", "moe_verify_weight_bytes", "moe_verify_last_error",
            "moe_verify_version"]
@@ -87,15 +88,17 @@ def lib() -> ctypes.CDLL:
     L.moe_verify_layer_grouped.restype = ctypes.c_int
     L.moe_verify_layer_grouped.argtypes = [cfgp, wp, P, _i32, P, P, P, P, Z, P, ctypes.POINTER(moe_debug)]
     L.moe_verify_stack.restype = ctypes.c_int
-    L.moe_verify_stack.argtypes = [cfgp, wp, _i32, P, _i32, P, P, P, Z, P, ctypes.POINTER(moe_debug)]
+    L.moe_verify_stack.argtypes = [cfgp, wp, _i32, P, P, _i32, P, P, P, Z, P, ctypes.POINTER(moe_debug)]
     L.moe_verify_stack_timed.restype = ctypes.c_int
-    L.moe_verify_stack_timed.argtypes = [cfgp, wp, _i32, P, _i32, P, P, P, Z, P, ctypes.POINTER(ctypes.c_float)]
+    L.moe_verify_stack_timed.argtypes = [cfgp, wp, _i32, P, P, _i32, P, P, P, Z, P, ctypes.POINTER(ctypes.c_float)]
     L.moe_verify_route.restype = ctypes.c_int
     L.moe_verify_route.argtypes = [cfgp, P, P, _i32, ctypes.POINTER(moe_route_out), P, Z, P]
+    L.moe_verify_stream_read.restype = ctypes.c_int
+    L.moe_verify_stream_read.argtypes = [P, Z, P, P]
     L.moe_verify_dequant_nvfp4.restype = ctypes.c_int
     L.moe_verify_dequant_nvfp4.argtypes = [ctypes.POINTER(moe_nvfp4), _i32, _i32, _i32, P, P]
     L.moe_stack_graph_create.restype = ctypes.c_int
-    L.moe_stack_graph_create.argtypes = [cfgp, wp, _i32, P, _i32, P, P, P, Z, P, ctypes.POINTER(P)]
+    L.moe_stack_graph_create.argtypes = [cfgp, wp, _i32, P, P, _i32, P, P, P, Z, P, ctypes.POINTER(P)]
     L.moe_stack_graph_launch.restype = ctypes.c_int
     L.moe_stack_graph_launch.argtypes = [P, P]
     L.moe_stack_graph_destroy.restype = None
@@ -126,15 +129,26 @@ def _check(rc: int) -> None:
 # ---------------------------------------------------------------------------
 
 
-def _ptr(t: Optional[torch.Tensor], dtype=None, name: str = "tensor") -> Optional[int]:
+def _ptr(t: Optional[torch.Tensor], dtype=None, name: str = "tensor", numel: Optional[int] = None,
+         device: Optional[torch.device] = None) -> Optional[int]:
+    """Device pointer of a contiguous GPU tensor, after checking its dtype,
+    its size (at least numel elements) and that it lives on `device` (when
+    given).  Raises before anything reaches the library: a host pointer or a
+    short buffer would otherwise become an out-of-bounds GPU access."""
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch tensor" % name)
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor (is on %s)" % (name, t.device))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, the call's tensors are on %s" % (name, t.device, device))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
+    if numel is not None and t.numel() < numel:
+        raise ValueError("%s has %d elements, needs at least %d" % (name, t.numel(), numel))
     return t.data_ptr()
 
 
@@ -155,27 +169,96 @@ def make_cfg(shape, max_rows: int, score_fn: int = MOE_SCORE_SOFTMAX, norm_topk:
                    score_fn, norm_topk, routed_scale, rms_eps, max_rows, regime)
 
 
-def _mat(m) -> moe_nvfp4:
+def _check_mat(m, name: str, E: int, rows: int, cols: int, device, shapes_only: bool = False) -> None:
+    want = {"q": (E, rows, cols // 2), "s": (E, rows, cols // 16), "ts": (E,)}
+    for k, shp in want.items():
+        t = m[k]
+        if not isinstance(t, torch.Tensor) or tuple(t.shape) != shp:
+            raise ValueError("%s.%s has shape %s, expected %s" % (
+                name, k, None if not isinstance(t, torch.Tensor) else tuple(t.shape), shp))
+        if not shapes_only:
+            _ptr(t, torch.float32 if k == "ts" else torch.uint8, "%s.%s" % (name, k), device=device)
+
+
+def _mat(m, name: str = "matrix") -> moe_nvfp4:
     if m is None:
         return moe_nvfp4(None, None, None)
-    return moe_nvfp4(_ptr(m["q"], torch.uint8, "q"), _ptr(m["s"], torch.uint8, "s"),
-                     _ptr(m["ts"], torch.float32, "ts"))
+    return moe_nvfp4(_ptr(m["q"], torch.uint8, name + ".q"), _ptr(m["s"], torch.uint8, name + ".s"),
+                     _ptr(m["ts"], torch.float32, name + ".ts"))
 
 
-def make_weights(w: Dict[str, object]) -> moe_layer_weights:
+def check_weights(w: Dict[str, object], cfg: moe_cfg, device=None) -> None:
+    """Shapes, dtypes and device of one layer's weight tensors against cfg
+    (every shape first, then dtypes and devices)."""
+    H, E, I, Is = cfg.hidden, cfg.n_experts, cfg.inter, cfg.shared_inter
+    mats = [("gate", E, I, H), ("up", E, I, H), ("down", E, H, I)]
+    if Is > 0:
+        mats += [("sh_gate", 1, Is, H), ("sh_up", 1, Is, H), ("sh_down", 1, H, Is)]
+    rw = w["router_w"]
+    if not isinstance(rw, torch.Tensor) or tuple(rw.shape) != (E, H):
+        raise ValueError("router_w must have shape (%d, %d)" % (E, H))
+    for nm, e, rows, cols in mats:
+        if w.get(nm) is None:
+            raise ValueError("%s missing" % nm)
+        _check_mat(w[nm], nm, e, rows, cols, device, shapes_only=True)
+    _ptr(rw, _BITS16, "router_w", device=device)
+    if w.get("router_bias") is not None:
+        _ptr(w["router_bias"], torch.float32, "router_bias", numel=E, device=device)
+    for nm, e, rows, cols in mats:
+        _check_mat(w[nm], nm, e, rows, cols, device)
+    if w.get("norm_w") is not None:
+        _ptr(w["norm_w"], _BITS16, "norm_w", numel=H, device=device)
+
+
+def make_weights(w: Dict[str, object], cfg: Optional[moe_cfg] = None) -> moe_layer_weights:
     """Weight struct for one layer from a dict of device tensors (the layout
-    documented in include/moe_verify.h).  The tensors must stay alive."""
+    documented in include/moe_verify.h; 'norm_w' optional).  With cfg, the
+    tensors' shapes are checked against it.  The tensors must stay alive."""
+    if cfg is not None:
+        check_weights(w, cfg)
     return moe_layer_weights(_ptr(w["router_w"], _BITS16, "router_w"),
                              _ptr(w.get("router_bias"), torch.float32, "router_bias"),
-                             _mat(w["gate"]), _mat(w["up"]), _mat(w["down"]),
-                             _mat(w.get("sh_gate")), _mat(w.get("sh_up")), _mat(w.get("sh_down")))
+                             _mat(w["gate"], "gate"), _mat(w["up"], "up"), _mat(w["down"], "down"),
+                             _mat(w.get("sh_gate"), "sh_gate"), _mat(w.get("sh_up"), "sh_up"),
+                             _mat(w.get("sh_down"), "sh_down"), _ptr(w.get("norm_w"), _BITS16, "norm_w"))
+
+
+# per-layer sizes of the debug arrays, in elements, for K rows
+def _debug_sizes(cfg: moe_cfg, K: int) -> Dict[str, int]:
+    n, H = K * cfg.top_k, cfg.hidden
+    return {"logits": K * cfg.n_experts, "ids": n, "w": n, "n_unique": 1, "uniq": n, "off": n + 1, "asg": n,
+            "inv": n, "x_in": K * H, "y32": K * H, "res_in": K * H}
 
 
 def make_debug(**arrays) -> moe_debug:
     d = moe_debug()
     for k, v in arrays.items():
-        setattr(d, k, _ptr(v, None, k))
+        if v is not None and not isinstance(v, torch.Tensor):
+            raise TypeError("%s must be a torch tensor" % k)
+        setattr(d, k, None if v is None else v.data_ptr())
+    d._tensors = dict(arrays)
     return d
+
+
+def _check_debug(debug: Optional[moe_debug], cfg: moe_cfg, K: int, layers: int, device) -> None:
+    if debug is None:
+        return
+    sizes = _debug_sizes(cfg, K)
+    for k, t in getattr(debug, "_tensors", {}).items():
+        if k not in sizes:
+            raise ValueError("unknown debug array %s" % k)
+        _ptr(t, None, "debug." + k, numel=sizes[k] * layers, device=device)
+
+
+def _rows(x: torch.Tensor, cfg: moe_cfg, name: str = "x") -> int:
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.shape[1] != cfg.hidden:
+        raise ValueError("%s must be a 2-D tensor [K, %d]" % (name, cfg.hidden))
+    return x.shape[0]
+
+
+def _ws(workspace: torch.Tensor, device) -> tuple:
+    _ptr(workspace, None, "workspace", device=device)
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
 # ---------------------------------------------------------------------------
@@ -203,28 +286,33 @@ def moe_verify_weight_bytes(cfg: moe_cfg, n_unique: int, K: int, with_shared: bo
     return lib().moe_verify_weight_bytes(ctypes.byref(cfg), n_unique, K, int(with_shared), int(with_router))
 
 
+def _layer_call(fn, cfg: moe_cfg, weights: moe_layer_weights, x: torch.Tensor, y: torch.Tensor,
+                workspace: torch.Tensor, y32, residual, debug, stream) -> None:
+    K = _rows(x, cfg)
+    dev = x.device
+    KH = K * cfg.hidden
+    px = _ptr(x, _BITS16, "x", device=dev)
+    py = _ptr(y, _BITS16, "y", numel=KH, device=dev)
+    py32 = _ptr(y32, torch.float32, "y32", numel=KH, device=dev)
+    pr = _ptr(residual, _BITS16, "residual", numel=KH, device=dev)
+    _check_debug(debug, cfg, K, 1, dev)
+    pw, nw = _ws(workspace, dev)
+    _check(fn(ctypes.byref(cfg), ctypes.byref(weights), px, K, pr, py, py32, pw, nw, _stream(stream),
+              ctypes.byref(debug) if debug is not None else None))
+
+
 def moe_verify_layer(cfg: moe_cfg, weights: moe_layer_weights, x: torch.Tensor, y: torch.Tensor,
                      workspace: torch.Tensor, y32: Optional[torch.Tensor] = None,
                      residual: Optional[torch.Tensor] = None, debug: Optional[moe_debug] = None,
                      stream=None) -> None:
-    K = x.shape[0]
-    _check(lib().moe_verify_layer(ctypes.byref(cfg), ctypes.byref(weights), _ptr(x, _BITS16, "x"), K,
-                                  _ptr(residual, _BITS16, "residual"), _ptr(y, _BITS16, "y"),
-                                  _ptr(y32, torch.float32, "y32"), _ptr(workspace, None, "workspace"),
-                                  workspace.numel() * workspace.element_size(), _stream(stream),
-                                  ctypes.byref(debug) if debug is not None else None))
+    _layer_call(lib().moe_verify_layer, cfg, weights, x, y, workspace, y32, residual, debug, stream)
 
 
 def moe_verify_layer_grouped(cfg: moe_cfg, weights: moe_layer_weights, x: torch.Tensor, y: torch.Tensor,
                              workspace: torch.Tensor, y32: Optional[torch.Tensor] = None,
                              residual: Optional[torch.Tensor] = None, debug: Optional[moe_debug] = None,
                              stream=None) -> None:
-    K = x.shape[0]
-    _check(lib().moe_verify_layer_grouped(ctypes.byref(cfg), ctypes.byref(weights), _ptr(x, _BITS16, "x"), K,
-                                          _ptr(residual, _BITS16, "residual"), _ptr(y, _BITS16, "y"),
-                                          _ptr(y32, torch.float32, "y32"), _ptr(workspace, None, "workspace"),
-                                          workspace.numel() * workspace.element_size(), _stream(stream),
-                                          ctypes.byref(debug) if debug is not None else None))
+    _layer_call(lib().moe_verify_layer_grouped, cfg, weights, x, y, workspace, y32, residual, debug, stream)
 
 
 def _layer_array(layers: Sequence[moe_layer_weights]):
@@ -232,60 +320,91 @@ def _layer_array(layers: Sequence[moe_layer_weights]):
     return arr
 
 
+def _stack_io(cfg: moe_cfg, layers, x, y, y32, residual):
+    if len(layers) < 1:
+        raise ValueError("need at least one layer")
+    K = _rows(x, cfg)
+    dev = x.device
+    KH = K * cfg.hidden
+    return (K, dev, _ptr(x, _BITS16, "x", device=dev), _ptr(residual, _BITS16, "residual", numel=KH, device=dev),
+            _ptr(y, _BITS16, "y", numel=KH, device=dev), _ptr(y32, torch.float32, "y32", numel=KH, device=dev))
+
+
 def moe_verify_stack(cfg: moe_cfg, layers: Sequence[moe_layer_weights], x: torch.Tensor, y: torch.Tensor,
                      workspace: torch.Tensor, y32: Optional[torch.Tensor] = None,
-                     debug: Optional[moe_debug] = None, stream=None) -> None:
+                     debug: Optional[moe_debug] = None, stream=None,
+                     residual: Optional[torch.Tensor] = None) -> None:
+    K, dev, px, pr, py, py32 = _stack_io(cfg, layers, x, y, y32, residual)
+    _check_debug(debug, cfg, K, len(layers), dev)
+    pw, nw = _ws(workspace, dev)
     arr = _layer_array(layers)
-    _check(lib().moe_verify_stack(ctypes.byref(cfg), arr, len(layers), _ptr(x, _BITS16, "x"), x.shape[0],
-                                  _ptr(y, _BITS16, "y"), _ptr(y32, torch.float32, "y32"),
-                                  _ptr(workspace, None, "workspace"),
-                                  workspace.numel() * workspace.element_size(), _stream(stream),
-                                  ctypes.byref(debug) if debug is not None else None))
+    _check(lib().moe_verify_stack(ctypes.byref(cfg), arr, len(layers), px, pr, K, py, py32, pw, nw,
+                                  _stream(stream), ctypes.byref(debug) if debug is not None else None))
 
 
 def moe_verify_stack_timed(cfg: moe_cfg, layers: Sequence[moe_layer_weights], x: torch.Tensor, y: torch.Tensor,
-                           workspace: torch.Tensor, y32: Optional[torch.Tensor] = None, stream=None):
+                           workspace: torch.Tensor, y32: Optional[torch.Tensor] = None, stream=None,
+                           residual: Optional[torch.Tensor] = None):
     """Returns per-kernel durations in ms as a list of (route, gateup, down)
     per layer."""
+    K, dev, px, pr, py, py32 = _stack_io(cfg, layers, x, y, y32, residual)
+    pw, nw = _ws(workspace, dev)
     arr = _layer_array(layers)
     ms = (ctypes.c_float * (3 * len(layers)))()
-    _check(lib().moe_verify_stack_timed(ctypes.byref(cfg), arr, len(layers), _ptr(x, _BITS16, "x"), x.shape[0],
-                                        _ptr(y, _BITS16, "y"), _ptr(y32, torch.float32, "y32"),
-                                        _ptr(workspace, None, "workspace"),
-                                        workspace.numel() * workspace.element_size(), _stream(stream), ms))
+    _check(lib().moe_verify_stack_timed(ctypes.byref(cfg), arr, len(layers), px, pr, K, py, py32, pw, nw,
+                                        _stream(stream), ms))
     return [(ms[3 * l], ms[3 * l + 1], ms[3 * l + 2]) for l in range(len(layers))]
 
 
 def moe_verify_route(cfg: moe_cfg, logits: torch.Tensor, out: Dict[str, torch.Tensor],
                      bias: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                      stream=None) -> None:
-    ro = moe_route_out(*[_ptr(out[k], None, k) for k in ("ids", "w", "n_unique", "uniq", "off", "asg", "inv")])
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().moe_verify_route(ctypes.byref(cfg), _ptr(logits, torch.float32, "logits"),
-                                  _ptr(bias, torch.float32, "bias"), logits.shape[0], ctypes.byref(ro),
-                                  _ptr(workspace, None, "workspace"), nbytes, _stream(stream)))
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2 or logits.shape[1] != cfg.n_experts:
+        raise ValueError("logits must be a 2-D tensor [K, %d]" % cfg.n_experts)
+    K, dev = logits.shape[0], logits.device
+    n = K * cfg.top_k
+    sizes = {"ids": n, "w": n, "n_unique": 1, "uniq": n, "off": n + 1, "asg": n, "inv": n}
+    ro = moe_route_out(*[_ptr(out[k], None, k, numel=sizes[k], device=dev)
+                         for k in ("ids", "w", "n_unique", "uniq", "off", "asg", "inv")])
+    pw, nw = (None, 0) if workspace is None else _ws(workspace, dev)
+    _check(lib().moe_verify_route(ctypes.byref(cfg), _ptr(logits, torch.float32, "logits", device=dev),
+                                  _ptr(bias, torch.float32, "bias", numel=cfg.n_experts, device=dev), K,
+                                  ctypes.byref(ro), pw, nw, _stream(stream)))
 
 
 def moe_verify_dequant_nvfp4(m: Dict[str, torch.Tensor], out: torch.Tensor, stream=None) -> None:
     E, rows, half = m["q"].shape
+    dev = m["q"].device
+    _check_mat(m, "matrix", E, rows, half * 2, dev)
     mm = _mat(m)
-    _check(lib().moe_verify_dequant_nvfp4(ctypes.byref(mm), E, rows, half * 2, _ptr(out, torch.float32, "out"),
+    _check(lib().moe_verify_dequant_nvfp4(ctypes.byref(mm), E, rows, half * 2,
+                                          _ptr(out, torch.float32, "out", numel=E * rows * half * 2, device=dev),
                                           _stream(stream)))
+
+
+def moe_verify_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Stream every byte of src (a GPU tensor, size a multiple of 16 bytes)
+    once; sink: a one-element int32 GPU tensor."""
+    dev = src.device
+    nbytes = src.numel() * src.element_size()
+    _check(lib().moe_verify_stream_read(_ptr(src, None, "src", device=dev), nbytes,
+                                        _ptr(sink, torch.int32, "sink", numel=1, device=dev), _stream(stream)))
 
 
 class StackGraph:
     """moe_stack_graph_create / _launch / _destroy."""
 
     def __init__(self, cfg: moe_cfg, layers: Sequence[moe_layer_weights], x: torch.Tensor, y: torch.Tensor,
-                 workspace: torch.Tensor, y32: Optional[torch.Tensor] = None, stream=None):
-        self._keep = (cfg, list(layers), x, y, workspace, y32)
+                 workspace: torch.Tensor, y32: Optional[torch.Tensor] = None, stream=None,
+                 residual: Optional[torch.Tensor] = None):
+        self.handle = _c_void_p()
+        self._keep = (cfg, list(layers), x, y, workspace, y32, residual)
+        K, dev, px, pr, py, py32 = _stack_io(cfg, layers, x, y, y32, residual)
+        pw, nw = _ws(workspace, dev)
         arr = _layer_array(layers)
         h = _c_void_p()
-        _check(lib().moe_stack_graph_create(ctypes.byref(cfg), arr, len(layers), _ptr(x, _BITS16, "x"),
-                                            x.shape[0], _ptr(y, _BITS16, "y"), _ptr(y32, torch.float32, "y32"),
-                                            _ptr(workspace, None, "workspace"),
-                                            workspace.numel() * workspace.element_size(), _stream(stream),
-                                            ctypes.byref(h)))
+        _check(lib().moe_stack_graph_create(ctypes.byref(cfg), arr, len(layers), px, pr, K, py, py32, pw, nw,
+                                            _stream(stream), ctypes.byref(h)))
         self.handle = h
 
     def launch(self, stream=None) -> None:

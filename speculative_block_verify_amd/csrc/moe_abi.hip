@@ -130,6 +130,8 @@ int check_weights(const moe_cfg* c, const moe_layer_weights* w, int layer) {
     if (!w) return fail(MOE_ERR_INVALID, "weights of layer %d are NULL", layer);
     if (!w->router_w || !aligned16(w->router_w))
         return fail(MOE_ERR_INVALID, "layer %d: router_w NULL or not 16-byte aligned", layer);
+    if (w->norm_w && !aligned16(w->norm_w))
+        return fail(MOE_ERR_INVALID, "layer %d: norm_w not 16-byte aligned", layer);
     if (c->score_fn == MOE_SCORE_SIGMOID_BIAS && !w->router_bias)
         return fail(MOE_ERR_INVALID, "layer %d: sigmoid scoring needs router_bias", layer);
     if (c->score_fn == MOE_SCORE_SOFTMAX && w->router_bias)
@@ -167,13 +169,15 @@ struct Layout {
     float* ssq;
     uint16_t* xbuf;
     float* ybuf;
+    uint16_t* ybf;          // bf16 [R][H]: the residual stream between stacked layers
     // grouped regime
     uint16_t* xbuf2;        // second bf16 input buffer (stacked layers alternate)
     int32_t* tiles;         // int4 [max tiles]
     float* hmax;            // [R*k][I/64]
     float* hmax_sh;         // [R][Is/64]
     float* o;               // [R*k + R][H]
-    uint16_t* xh;           // fp16 copy of the layer input [R][H]
+    uint16_t* xh;           // fp16 copy of the layer input [R][H] (x * 2^-xsig per row)
+    int32_t* xsig;          // [R] power-of-two exponent of each row of xh
     int max_tiles;
     size_t bytes;
 };
@@ -198,6 +202,7 @@ Layout layout(const moe_cfg* c, void* base) {
     L.ssq = reinterpret_cast<float*>(take(R * (H / moe::kDownRowsPerBlock) * 4));
     L.xbuf = reinterpret_cast<uint16_t*>(take(R * H * 2));
     L.ybuf = reinterpret_cast<float*>(take(R * H * 4));
+    L.ybf = reinterpret_cast<uint16_t*>(take(R * H * 2));
     L.xbuf2 = reinterpret_cast<uint16_t*>(take(R * H * 2));
     L.max_tiles = moe::grouped_max_tiles((int)R, (int)E, (int)k, Is > 0);
     L.tiles = reinterpret_cast<int32_t*>(take((size_t)L.max_tiles * 16));
@@ -205,6 +210,7 @@ Layout layout(const moe_cfg* c, void* base) {
     L.hmax_sh = reinterpret_cast<float*>(take(R * (Is ? (Is + 63) / 64 : 1) * 4));
     L.o = reinterpret_cast<float*>(take((R * k + R) * H * 4));
     L.xh = reinterpret_cast<uint16_t*>(take(R * H * 2));
+    L.xsig = reinterpret_cast<int32_t*>(take(R * 4));
     L.bytes = o;
     return L;
 }
@@ -218,6 +224,7 @@ moe::Fp4Mat mat(const moe_nvfp4& m) { return moe::Fp4Mat{m.q, m.s, m.ts}; }
 struct LayerIO {
     const uint16_t* x_in;    // bf16 input (first layer / single layer), or nullptr
     const float* y_prev;     // fp32 output of the previous layer to normalise, or nullptr
+    const uint16_t* gamma;   // the previous layer's norm weight (with y_prev), or nullptr
     const uint16_t* residual;
     float* y32;              // fp32 output (required)
     uint16_t* y;             // bf16 output or nullptr
@@ -235,6 +242,7 @@ int enqueue_layer(const moe_cfg* c, const moe_layer_weights* w, const LayerIO& i
     ra.x_in = io.x_in;
     ra.y_prev = io.y_prev;
     ra.ssq = L.ssq;
+    ra.gamma = io.gamma;
     ra.x_out = L.xbuf;
     ra.eps = c->rms_eps;
     ra.wr = w->router_w;
@@ -283,6 +291,8 @@ int enqueue_layer(const moe_cfg* c, const moe_layer_weights* w, const LayerIO& i
 int enqueue_layer_grouped(const moe_cfg* c, const moe_layer_weights* w, const uint16_t* x, int K,
                           const uint16_t* residual, float* y32, uint16_t* y, uint16_t* x_next, const Layout& L,
                           hipStream_t st) {
+    // x_next (stacked layers) is this layer's output normalised with its
+    // norm weight
     hipError_t e;
     const bool has_sh = c->shared_inter > 0;
     const moe::Fp4Mat none{nullptr, nullptr, nullptr};
@@ -294,6 +304,7 @@ int enqueue_layer_grouped(const moe_cfg* c, const moe_layer_weights* w, const ui
     ra.wr = w->router_w;
     ra.logits = L.logits;
     ra.x_f16 = L.xh;
+    ra.x_sig = L.xsig;
     ra.K = K; ra.H = c->hidden; ra.E = c->n_experts;
     if ((e = moe::launch_router_mfma(ra, st)) != hipSuccess) return hip_fail(e, "router launch");
 
@@ -313,6 +324,7 @@ int enqueue_layer_grouped(const moe_cfg* c, const moe_layer_weights* w, const ui
     const int max_tiles = moe::grouped_max_tiles(K, c->n_experts, c->top_k, has_sh);
     moe::GroupedGuArgs ga{};
     ga.x = L.xh;
+    ga.x_sig = L.xsig;
     ga.gate = mat(w->gate); ga.up = mat(w->up);
     ga.sgate = has_sh ? mat(w->sh_gate) : none;
     ga.sup = has_sh ? mat(w->sh_up) : none;
@@ -334,6 +346,7 @@ int enqueue_layer_grouped(const moe_cfg* c, const moe_layer_weights* w, const ui
     moe::CombineArgs ca{};
     ca.o = L.o; ca.w = L.w; ca.inv = L.inv;
     ca.residual = residual; ca.y32 = y32; ca.y = y; ca.x_next = x_next;
+    ca.gamma = x_next ? w->norm_w : nullptr;
     ca.eps = c->rms_eps; ca.rs = c->routed_scale;
     ca.T = K; ca.H = c->hidden; ca.k = c->top_k; ca.has_shared = has_sh;
     if ((e = moe::launch_combine(ca, st)) != hipSuccess) return hip_fail(e, "combine launch");
@@ -365,6 +378,17 @@ int copy_debug(const moe_cfg* c, const moe_debug* d, int layer, int K, const Lay
     return MOE_OK;
 }
 
+// The layer's residual input, copied before the layer runs (in a stack the
+// residual stream is updated in place by the layer).
+int copy_debug_residual(const moe_cfg* c, const moe_debug* d, int layer, int K, const uint16_t* residual,
+                        hipStream_t st) {
+    if (!d || !d->res_in || !residual) return MOE_OK;
+    const size_t bytes = (size_t)K * c->hidden * 2;
+    hipError_t e = hipMemcpyAsync(d->res_in + (size_t)layer * K * c->hidden, residual, bytes,
+                                  hipMemcpyDeviceToDevice, st);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "debug copy");
+}
+
 int check_common(const moe_cfg* c, int K, void* ws, size_t ws_bytes) {
     int rc = check_cfg(c);
     if (rc) return rc;
@@ -384,12 +408,17 @@ int check_io(const void* x, const void* y, const void* y32, const void* residual
     return MOE_OK;
 }
 
-int enqueue_stack(const moe_cfg* c, const moe_layer_weights* layers, int n_layers, const uint16_t* x, int K,
-                  uint16_t* y, float* y32, void* ws, hipStream_t st, const moe_debug* dbg,
-                  const moe::Timing* tm = nullptr) {
+// residual == nullptr: no residual.  Otherwise the residual stream: layer 0
+// adds `residual`, layer l >= 1 adds layer l-1's bf16 output, which the
+// layers keep in L.ybf (each layer reads an element of it and then writes
+// its own output there, in the same thread).
+int enqueue_stack(const moe_cfg* c, const moe_layer_weights* layers, int n_layers, const uint16_t* x,
+                  const uint16_t* residual, int K, uint16_t* y, float* y32, void* ws, hipStream_t st,
+                  const moe_debug* dbg, const moe::Timing* tm = nullptr) {
     const Layout L = layout(c, ws);
     hipError_t e = moe::init_kernels();
     if (e != hipSuccess) return hip_fail(e, "kernel attributes");
+    const bool stream_res = residual != nullptr;
     if (use_grouped(c, K)) {
         // grouped regime: each layer's combine writes the next layer's input,
         // alternating between two buffers so a layer's input stays readable
@@ -398,7 +427,11 @@ int enqueue_stack(const moe_cfg* c, const moe_layer_weights* layers, int n_layer
             const uint16_t* xin = (l == 0) ? x : ((l & 1) ? L.xbuf : L.xbuf2);
             uint16_t* xnext = last ? nullptr : ((l & 1) ? L.xbuf2 : L.xbuf);
             float* yo = last ? (y32 ? y32 : L.ybuf) : L.ybuf;
-            int rc = enqueue_layer_grouped(c, &layers[l], xin, K, nullptr, yo, last ? y : nullptr, xnext, L, st);
+            const uint16_t* res = stream_res ? (l == 0 ? residual : L.ybf) : nullptr;
+            uint16_t* yb = last ? y : (stream_res ? L.ybf : nullptr);
+            int rc = copy_debug_residual(c, dbg, l, K, res, st);
+            if (rc) return rc;
+            rc = enqueue_layer_grouped(c, &layers[l], xin, K, res, yo, yb, xnext, L, st);
             if (rc) return rc;
             rc = copy_debug(c, dbg, l, K, L, xin, yo, st);
             if (rc) return rc;
@@ -410,11 +443,14 @@ int enqueue_stack(const moe_cfg* c, const moe_layer_weights* layers, int n_layer
         LayerIO io{};
         io.x_in = (l == 0) ? x : nullptr;
         io.y_prev = (l == 0) ? nullptr : L.ybuf;
-        io.residual = nullptr;
+        io.gamma = (l == 0) ? nullptr : layers[l - 1].norm_w;
+        io.residual = stream_res ? (l == 0 ? residual : L.ybf) : nullptr;
         io.y32 = last ? (y32 ? y32 : L.ybuf) : L.ybuf;
-        io.y = last ? y : nullptr;
-        int rc = enqueue_layer(c, &layers[l], io, K, L, st, tm ? tm + 3 * l : nullptr,
-                               last ? nullptr : layers[l + 1].router_w);
+        io.y = last ? y : (stream_res ? L.ybf : nullptr);
+        int rc = copy_debug_residual(c, dbg, l, K, io.residual, st);
+        if (rc) return rc;
+        rc = enqueue_layer(c, &layers[l], io, K, L, st, tm ? tm + 3 * l : nullptr,
+                           last ? nullptr : layers[l + 1].router_w);
         if (rc) return rc;
         rc = copy_debug(c, dbg, l, K, L, l == 0 ? x : L.xbuf, io.y32, st);
         if (rc) return rc;
@@ -430,7 +466,7 @@ int enqueue_stack(const moe_cfg* c, const moe_layer_weights* layers, int n_layer
 
 extern "C" {
 
-int moe_verify_version(void) { return 100; }
+int moe_verify_version(void) { return 200; }
 
 const char* moe_verify_last_error(void) { return g_err.c_str(); }
 
@@ -463,6 +499,7 @@ int moe_verify_layer(const moe_cfg* cfg, const moe_layer_weights* w, const uint1
     hipError_t e = moe::init_kernels();
     if (e != hipSuccess) return hip_fail(e, "kernel attributes");
     float* yo = y32 ? y32 : L.ybuf;
+    if ((rc = copy_debug_residual(cfg, dbg, 0, K, residual, st))) return rc;
     if (use_grouped(cfg, K)) {
         if ((rc = enqueue_layer_grouped(cfg, w, x, K, residual, yo, y, nullptr, L, st))) return rc;
         return copy_debug(cfg, dbg, 0, K, L, x, yo, st);
@@ -490,21 +527,23 @@ int moe_verify_layer_grouped(const moe_cfg* cfg, const moe_layer_weights* w, con
     hipError_t e = moe::init_kernels();
     if (e != hipSuccess) return hip_fail(e, "kernel attributes");
     float* yo = y32 ? y32 : L.ybuf;
+    if ((rc = copy_debug_residual(cfg, dbg, 0, K, residual, st))) return rc;
     if ((rc = enqueue_layer_grouped(cfg, w, x, K, residual, yo, y, nullptr, L, st))) return rc;
     return copy_debug(cfg, dbg, 0, K, L, x, yo, st);
 }
 
 int moe_verify_stack(const moe_cfg* cfg, const moe_layer_weights* layers, int32_t n_layers, const uint16_t* x,
-                     int32_t K, uint16_t* y, float* y32, void* workspace, size_t workspace_bytes, void* stream,
-                     const moe_debug* dbg) {
+                     const uint16_t* residual, int32_t K, uint16_t* y, float* y32, void* workspace,
+                     size_t workspace_bytes, void* stream, const moe_debug* dbg) {
     int rc;
     if ((rc = check_common(cfg, K, workspace, workspace_bytes))) return rc;
     if ((rc = check_regime(cfg, K))) return rc;
     if (!layers || n_layers < 1) return fail(MOE_ERR_INVALID, "need n_layers >= 1 and a layer array");
     for (int l = 0; l < n_layers; ++l)
         if ((rc = check_weights(cfg, &layers[l], l))) return rc;
-    if ((rc = check_io(x, y, y32, nullptr))) return rc;
-    return enqueue_stack(cfg, layers, n_layers, x, K, y, y32, workspace, static_cast<hipStream_t>(stream), dbg);
+    if ((rc = check_io(x, y, y32, residual))) return rc;
+    return enqueue_stack(cfg, layers, n_layers, x, residual, K, y, y32, workspace, static_cast<hipStream_t>(stream),
+                         dbg);
 }
 
 int moe_verify_route(const moe_cfg* cfg, const float* logits, const float* bias, int32_t K,
@@ -562,9 +601,18 @@ int moe_verify_dequant_nvfp4(const moe_nvfp4* m, int32_t n_experts, int32_t rows
     return MOE_OK;
 }
 
+int moe_verify_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+    if (!src || !aligned16(src)) return fail(MOE_ERR_INVALID, "src NULL or not 16-byte aligned");
+    if (!sink) return fail(MOE_ERR_INVALID, "sink is NULL");
+    if (bytes == 0 || bytes % 16) return fail(MOE_ERR_INVALID, "bytes=%zu must be a positive multiple of 16", bytes);
+    hipError_t e = moe::launch_stream_read(src, bytes / 16, sink, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "stream read launch");
+    return MOE_OK;
+}
+
 int moe_verify_stack_timed(const moe_cfg* cfg, const moe_layer_weights* layers, int32_t n_layers,
-                           const uint16_t* x, int32_t K, uint16_t* y, float* y32, void* workspace,
-                           size_t workspace_bytes, void* stream, float* kernel_ms) {
+                           const uint16_t* x, const uint16_t* residual, int32_t K, uint16_t* y, float* y32,
+                           void* workspace, size_t workspace_bytes, void* stream, float* kernel_ms) {
     int rc;
     if ((rc = check_common(cfg, K, workspace, workspace_bytes))) return rc;
     if ((rc = check_regime(cfg, K))) return rc;
@@ -575,7 +623,7 @@ int moe_verify_stack_timed(const moe_cfg* cfg, const moe_layer_weights* layers, 
                     "ones under this cfg)", K);
     for (int l = 0; l < n_layers; ++l)
         if ((rc = check_weights(cfg, &layers[l], l))) return rc;
-    if ((rc = check_io(x, y, y32, nullptr))) return rc;
+    if ((rc = check_io(x, y, y32, residual))) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int n_ev = 3 * n_layers;
     moe::Timing* tm = new moe::Timing[n_ev]();
@@ -589,7 +637,7 @@ int moe_verify_stack_timed(const moe_cfg* cfg, const moe_layer_weights* layers, 
         }
     }
     if (e == hipSuccess) {
-        rc = enqueue_stack(cfg, layers, n_layers, x, K, y, y32, workspace, st, nullptr, tm);
+        rc = enqueue_stack(cfg, layers, n_layers, x, residual, K, y, y32, workspace, st, nullptr, tm);
         if (!rc && (e = hipStreamSynchronize(st)) != hipSuccess) rc = hip_fail(e, "synchronize");
         for (int i = 0; !rc && i < n_ev; ++i) {
             float ms = 0.0f;
@@ -613,8 +661,8 @@ struct moe_stack_graph {
 };
 
 int moe_stack_graph_create(const moe_cfg* cfg, const moe_layer_weights* layers, int32_t n_layers,
-                           const uint16_t* x, int32_t K, uint16_t* y, float* y32, void* workspace,
-                           size_t workspace_bytes, void* stream, moe_stack_graph** out) {
+                           const uint16_t* x, const uint16_t* residual, int32_t K, uint16_t* y, float* y32,
+                           void* workspace, size_t workspace_bytes, void* stream, moe_stack_graph** out) {
     int rc;
     if (!out) return fail(MOE_ERR_INVALID, "out is NULL");
     *out = nullptr;
@@ -623,7 +671,7 @@ int moe_stack_graph_create(const moe_cfg* cfg, const moe_layer_weights* layers, 
     if (!layers || n_layers < 1) return fail(MOE_ERR_INVALID, "need n_layers >= 1 and a layer array");
     for (int l = 0; l < n_layers; ++l)
         if ((rc = check_weights(cfg, &layers[l], l))) return rc;
-    if ((rc = check_io(x, y, y32, nullptr))) return rc;
+    if ((rc = check_io(x, y, y32, residual))) return rc;
     hipError_t e = moe::init_kernels();
     if (e != hipSuccess) return hip_fail(e, "kernel attributes");
     hipStream_t cap;
@@ -633,7 +681,7 @@ int moe_stack_graph_create(const moe_cfg* cfg, const moe_layer_weights* layers, 
         (void)hipStreamDestroy(cap);
         return hip_fail(e, "begin capture");
     }
-    rc = enqueue_stack(cfg, layers, n_layers, x, K, y, y32, workspace, cap, nullptr);
+    rc = enqueue_stack(cfg, layers, n_layers, x, residual, K, y, y32, workspace, cap, nullptr);
     hipGraph_t graph = nullptr;
     e = hipStreamEndCapture(cap, &graph);
     (void)hipStreamDestroy(cap);

@@ -331,9 +331,57 @@ __device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t packed) {
     return (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)packed, SEL);
 }
 
-__device__ __forceinline__ uint32_t bf16pair_to_f16pair(uint32_t v) {
-    const f16x2_t h = {(_Float16)__uint_as_float(v << 16), (_Float16)__uint_as_float(v & 0xFFFF0000u)};
+// ---------------------------------------------------------------------------
+// x on the matrix cores.  bf16 activations enter the fp16 MFMA operands
+// scaled by a power of two per row, 2^-sig with sig = ilogb(max_row |x|) - 14,
+// so the row's largest magnitude lands in [2^14, 2^15): every bf16 value
+// whose scaled magnitude is at least 2^-14 (those within 2^-28 of the row
+// maximum) converts exactly, nothing overflows, and the accumulators are
+// multiplied by 2^sig before the tensor scale.  Smaller values keep an
+// absolute precision of 2^-24 * 2^sig, under 2^-38 of the row maximum.
+// ---------------------------------------------------------------------------
+
+// bf16 ones for every hidden column: the norm weight when none is given (one
+// copy per translation unit).
+static __device__ __align__(16) const uint16_t kBf16Ones[2048] = {
+#define MOE_ONES8 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80
+#define MOE_ONES64 MOE_ONES8, MOE_ONES8, MOE_ONES8, MOE_ONES8, MOE_ONES8, MOE_ONES8, MOE_ONES8, MOE_ONES8
+#define MOE_ONES512 MOE_ONES64, MOE_ONES64, MOE_ONES64, MOE_ONES64, MOE_ONES64, MOE_ONES64, MOE_ONES64, MOE_ONES64
+    MOE_ONES512, MOE_ONES512, MOE_ONES512, MOE_ONES512
+#undef MOE_ONES512
+#undef MOE_ONES64
+#undef MOE_ONES8
+};
+
+// Larger of the two bf16 magnitudes in a packed pair, as magnitude bits
+// (their integer order is the order of the magnitudes).
+__device__ __forceinline__ uint32_t bf16pair_maxabs(uint32_t v) {
+    return max(v & 0x7FFFu, (v >> 16) & 0x7FFFu);
+}
+__device__ __forceinline__ uint32_t bf16x8_maxabs(const uint4& v) {
+    return max(max(bf16pair_maxabs(v.x), bf16pair_maxabs(v.y)), max(bf16pair_maxabs(v.z), bf16pair_maxabs(v.w)));
+}
+
+// sig of a row from the magnitude bits of its largest |x| (0 for an all-zero
+// row; a row holding an infinity or NaN keeps sig 0 and propagates it).
+__device__ __forceinline__ int row_sigma(uint32_t maxbits) {
+    if (maxbits == 0u || maxbits >= 0x7F80u) return 0;
+    return ilogbf(__uint_as_float(maxbits << 16)) - 14;
+}
+
+// A packed bf16 pair -> packed fp16 pair of the values times 2^-sig.
+__device__ __forceinline__ uint32_t bf16pair_to_f16pair_scaled(uint32_t v, int neg_sig) {
+    const f16x2_t h = {(_Float16)ldexpf(__uint_as_float(v << 16), neg_sig),
+                       (_Float16)ldexpf(__uint_as_float(v & 0xFFFF0000u), neg_sig)};
     return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ uint4 bf16x8_to_f16x8_scaled(const uint4& v, int neg_sig) {
+    uint4 o;
+    o.x = bf16pair_to_f16pair_scaled(v.x, neg_sig);
+    o.y = bf16pair_to_f16pair_scaled(v.y, neg_sig);
+    o.z = bf16pair_to_f16pair_scaled(v.z, neg_sig);
+    o.w = bf16pair_to_f16pair_scaled(v.w, neg_sig);
+    return o;
 }
 
 // Code and scale registers of one superblock of one lane (gate and up).

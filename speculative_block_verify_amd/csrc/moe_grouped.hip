@@ -13,7 +13,8 @@
 //                   expert's 32-token tiles);
 //   k_gateup_grouped  (tile, 64 intermediate rows) work items on the matrix
 //                   cores: FP4 codes decoded in registers to fp16 times their
-//                   E4M3 scale (exact), x columns staged in LDS as fp16,
+//                   E4M3 scale (exact), x columns staged in LDS as fp16 (the
+//                   router's copy, x * 2^-sig per row, undone in the epilogue),
 //                   v_mfma_f32_16x16x32_f16 with fp32 accumulation, SwiGLU
 //                   epilogue writing fp32 h and each token's max |h| per slab;
 //   k_down_grouped  (tile, 64 output rows) work items: h staged in LDS as a
@@ -53,6 +54,7 @@ constexpr int kRouterWaves = 8;
 template <int H>
 __global__ __launch_bounds__(kRouterWaves * 64) void k_router_mfma(RouterArgs a) {
     __shared__ f32x4_t part[kRouterWaves - 1][2][64];
+    __shared__ uint32_t s_xmax[kRouterWaves][32];  // per wave: largest |x| of each of the tile's rows
     constexpr int NS = H / kRouterWaves / 32;  // MFMA steps per wave
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i = lane & 15, kb = lane >> 4;
@@ -70,21 +72,6 @@ __global__ __launch_bounds__(kRouterWaves * 64) void k_router_mfma(RouterArgs a)
         w0[s] = *reinterpret_cast<const uint4*>(wr0 + 32 * s);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the MFMAs
-    // the fp16 copy of x that the grouped gate/up kernel stages (bf16 -> fp16
-    // once per row, not per tile): each wave's column range is written by
-    // one workgroup of the row tile's column of workgroups
-    if (a.x_f16 && wave % gridDim.y == blockIdx.y) {
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            uint4 h0, h1;
-            h0.x = bf16pair_to_f16pair(x0[s].x); h0.y = bf16pair_to_f16pair(x0[s].y);
-            h0.z = bf16pair_to_f16pair(x0[s].z); h0.w = bf16pair_to_f16pair(x0[s].w);
-            h1.x = bf16pair_to_f16pair(x1[s].x); h1.y = bf16pair_to_f16pair(x1[s].y);
-            h1.z = bf16pair_to_f16pair(x1[s].z); h1.w = bf16pair_to_f16pair(x1[s].w);
-            if (t0 + i < T) *reinterpret_cast<uint4*>(a.x_f16 + (size_t)(t0 + i) * H + c0 + 32 * s) = h0;
-            if (t0 + 16 + i < T) *reinterpret_cast<uint4*>(a.x_f16 + (size_t)(t0 + 16 + i) * H + c0 + 32 * s) = h1;
-        }
-    }
     f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -97,7 +84,50 @@ __global__ __launch_bounds__(kRouterWaves * 64) void k_router_mfma(RouterArgs a)
 #pragma unroll
         for (int t = 0; t < 2; ++t) part[wave - 1][t][lane] = acc[t];
     }
+    if (a.x_f16) {
+        // largest |x| of rows i and 16 + i over this wave's columns (lanes
+        // i, i + 16, i + 32, i + 48 hold them)
+        uint32_t m0 = 0u, m1 = 0u;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            m0 = max(m0, bf16x8_maxabs(x0[s]));
+            m1 = max(m1, bf16x8_maxabs(x1[s]));
+        }
+        m0 = max(m0, (uint32_t)__shfl_xor((int)m0, 16, 64));
+        m0 = max(m0, (uint32_t)__shfl_xor((int)m0, 32, 64));
+        m1 = max(m1, (uint32_t)__shfl_xor((int)m1, 16, 64));
+        m1 = max(m1, (uint32_t)__shfl_xor((int)m1, 32, 64));
+        if (kb == 0) {
+            s_xmax[wave][i] = m0;
+            s_xmax[wave][16 + i] = m1;
+        }
+    }
     __syncthreads();
+    if (a.x_f16) {
+        // The fp16 copy of x that the grouped gate/up kernel stages (bf16 ->
+        // fp16 once per row, not per tile), scaled by the row's 2^-sig: each
+        // wave's column range is written by one workgroup of the row tile's
+        // column of workgroups (every one of them finds the same maxima).
+        uint32_t m0 = 0u, m1 = 0u;
+#pragma unroll
+        for (int w = 0; w < kRouterWaves; ++w) {
+            m0 = max(m0, s_xmax[w][i]);
+            m1 = max(m1, s_xmax[w][16 + i]);
+        }
+        const int sg0 = row_sigma(m0), sg1 = row_sigma(m1);
+        if (wave % gridDim.y == blockIdx.y) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const uint4 h0 = bf16x8_to_f16x8_scaled(x0[s], -sg0), h1 = bf16x8_to_f16x8_scaled(x1[s], -sg1);
+                if (t0 + i < T) *reinterpret_cast<uint4*>(a.x_f16 + (size_t)(t0 + i) * H + c0 + 32 * s) = h0;
+                if (t0 + 16 + i < T) *reinterpret_cast<uint4*>(a.x_f16 + (size_t)(t0 + 16 + i) * H + c0 + 32 * s) = h1;
+            }
+        }
+        if (blockIdx.y == 0 && wave == 0 && kb == 0) {
+            if (t0 + i < T) a.x_sig[t0 + i] = sg0;
+            if (t0 + 16 + i < T) a.x_sig[t0 + 16 + i] = sg1;
+        }
+    }
     if (wave == 0) {
         // accumulator t = row half; lane (j = lane % 16, q = lane / 16) holds
         // rows 4q .. 4q+3 of expert column j
@@ -318,6 +348,7 @@ __global__ __launch_bounds__(kBlock, 2) void k_gateup_grouped(GroupedGuArgs a, f
     constexpr int XL = NSB < 2 ? 1 : 2;
     __shared__ __align__(16) _Float16 xb[2][kGChunk * kGXStride];
     __shared__ int s_tok[kGuMaxItems][kGChunk];
+    __shared__ int s_tsig[kGuMaxItems][kGChunk];  // each token's x row exponent (the fp16 copy is x * 2^-sig)
     __shared__ int4 s_item[kGuMaxItems];   // {expert or -1 (shared), first asg position, tokens, slab}
     __shared__ float2 s_ts[kGuMaxItems];   // gate and up tensor scales
     __shared__ float s_max[kWaves][kGChunk];
@@ -353,7 +384,9 @@ __global__ __launch_bounds__(kBlock, 2) void k_gateup_grouped(GroupedGuArgs a, f
         const int k = t >> 5, m = t & 31;
         const int4 d = s_item[k];
         const int pos = d.y + min(m, d.z - 1);
-        s_tok[k][m] = d.x >= 0 ? a.asg[pos] / kk : pos;
+        const int tok = d.x >= 0 ? a.asg[pos] / kk : pos;
+        s_tok[k][m] = tok;
+        s_tsig[k][m] = a.x_sig[tok];
     }
     __syncthreads();
 
@@ -425,11 +458,13 @@ __global__ __launch_bounds__(kBlock, 2) void k_gateup_grouped(GroupedGuArgs a, f
             const int m = tt * 16 + j;
             float4 hv = make_float4(0.f, 0.f, 0.f, 0.f);
             if (tt < ntt) {
+                // undo the token's power-of-two x scale, then the tensor scales
+                const int sg = s_tsig[k][m];
                 float gv, uv;
-                gv = accg[tt][0] * gts; uv = accu[tt][0] * uts; hv.x = gv / (1.0f + expf(-gv)) * uv;
-                gv = accg[tt][1] * gts; uv = accu[tt][1] * uts; hv.y = gv / (1.0f + expf(-gv)) * uv;
-                gv = accg[tt][2] * gts; uv = accu[tt][2] * uts; hv.z = gv / (1.0f + expf(-gv)) * uv;
-                gv = accg[tt][3] * gts; uv = accu[tt][3] * uts; hv.w = gv / (1.0f + expf(-gv)) * uv;
+                gv = ldexpf(accg[tt][0], sg) * gts; uv = ldexpf(accu[tt][0], sg) * uts; hv.x = gv / (1.0f + expf(-gv)) * uv;
+                gv = ldexpf(accg[tt][1], sg) * gts; uv = ldexpf(accu[tt][1], sg) * uts; hv.y = gv / (1.0f + expf(-gv)) * uv;
+                gv = ldexpf(accg[tt][2], sg) * gts; uv = ldexpf(accu[tt][2], sg) * uts; hv.z = gv / (1.0f + expf(-gv)) * uv;
+                gv = ldexpf(accg[tt][3], sg) * gts; uv = ldexpf(accu[tt][3], sg) * uts; hv.w = gv / (1.0f + expf(-gv)) * uv;
                 if (m < cnt) *reinterpret_cast<float4*>(hbase + (size_t)(p0 + m) * hstride + n0 + 4 * q) = hv;
             }
             // max |h| of token m over this wave's 16 rows (lanes j, j+16, j+32, j+48)
@@ -718,9 +753,13 @@ __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a) {
     for (int t = 0; t < kCombineV4; ++t) {
         const int i4 = t * kBlock + tid;
         if (i4 < n4) {
+            // x_next = bf16((y * inv_rms) * gamma), fp32 products
+            const uint2 g = *reinterpret_cast<const uint2*>((a.gamma ? a.gamma : kBf16Ones) + 4 * i4);
             uint2 o;
-            o.x = (uint32_t)f32_to_bf16_rne(yv[t].x * sc) | ((uint32_t)f32_to_bf16_rne(yv[t].y * sc) << 16);
-            o.y = (uint32_t)f32_to_bf16_rne(yv[t].z * sc) | ((uint32_t)f32_to_bf16_rne(yv[t].w * sc) << 16);
+            o.x = (uint32_t)f32_to_bf16_rne(yv[t].x * sc * bf16_to_f32(g.x & 0xFFFFu)) |
+                  ((uint32_t)f32_to_bf16_rne(yv[t].y * sc * bf16_to_f32(g.x >> 16)) << 16);
+            o.y = (uint32_t)f32_to_bf16_rne(yv[t].z * sc * bf16_to_f32(g.y & 0xFFFFu)) |
+                  ((uint32_t)f32_to_bf16_rne(yv[t].w * sc * bf16_to_f32(g.y >> 16)) << 16);
             *reinterpret_cast<uint2*>(a.x_next + (size_t)r * H + 4 * i4) = o;
         }
     }

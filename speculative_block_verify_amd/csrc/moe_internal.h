@@ -54,11 +54,13 @@ struct RouterArgs {
     const uint16_t* x_in;   // bf16 [K][H], read when y_prev == nullptr
     const float* y_prev;    // fp32 [K][H] to RMS-normalise into x, or nullptr
     const float* ssq;       // [K][H / kDownRowsPerBlock] partial sums of squares of y_prev
+    const uint16_t* gamma;  // bf16 [H] norm weight applied to the normalised y_prev, or nullptr (ones)
     uint16_t* x_out;        // bf16 [K][H] normalised x (written when y_prev != nullptr)
     float eps;
     const uint16_t* wr;     // bf16 [E][H]
     float* logits;          // [K][E]
-    uint16_t* x_f16;        // fp16 bit patterns [K][H] of x_in, or nullptr (many-row router only)
+    uint16_t* x_f16;        // fp16 bit patterns [K][H] of x_in * 2^-x_sig[row], or nullptr (many-row router only)
+    int32_t* x_sig;         // [K] per-row power-of-two exponent of that copy (with x_f16)
     int K, H, E;
 };
 
@@ -115,7 +117,8 @@ struct GroupArgs {
 };
 
 struct GroupedGuArgs {
-    const uint16_t* x;      // fp16 bit patterns [T][H] (the router's copy of the layer input)
+    const uint16_t* x;      // fp16 bit patterns [T][H] of x * 2^-x_sig (the router's copy of the layer input)
+    const int32_t* x_sig;   // [T] the row's power-of-two exponent
     Fp4Mat gate, up;        // [E][I][H/2]
     Fp4Mat sgate, sup;      // [1][Is][H/2] (q == nullptr: no shared expert)
     const int32_t* uniq;
@@ -149,6 +152,7 @@ struct CombineArgs {
     float* y32;             // [T][H]
     uint16_t* y;            // bf16 [T][H] or nullptr
     uint16_t* x_next;       // bf16 RMS-normalised y for the next layer, or nullptr
+    const uint16_t* gamma;  // bf16 [H] norm weight of x_next, or nullptr (ones)
     float eps, rs;
     int T, H, k, has_shared;
 };
@@ -166,6 +170,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t st);  // logits given
 hipError_t launch_gateup(const GateUpArgs& a, int max_unique, hipStream_t st, const Timing* t = nullptr);
 hipError_t launch_down(const DownArgs& a, hipStream_t st, const Timing* t = nullptr);
 hipError_t launch_dequant(Fp4Mat m, int n_experts, int rows, int cols, float* out, hipStream_t st);
+hipError_t launch_stream_read(const void* src, size_t n16, uint32_t* sink, hipStream_t st);
 
 // Grouped regime (moe_grouped.hip).
 hipError_t launch_router_mfma(const RouterArgs& a, hipStream_t st);  // many rows, plain bf16 x_in only

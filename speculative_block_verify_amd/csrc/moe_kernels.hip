@@ -152,9 +152,11 @@ __global__ __launch_bounds__(kBlock) void k_select(SelectArgs a) {
 // Operands.  Each weight is decoded FP4 -> fp16 (v_cvt_scalef32_pk_f16_fp4,
 // scale operand 1) and multiplied by its E4M3 block scale with a packed fp16
 // multiply: an E2M1 value times an E4M3 value has at most 6 significant bits
-// and lies in [2^-10, 2688], so the fp16 product is exact.  x is converted
-// bf16 -> fp16 (exact for |x| in [2^-14, 65504]; smaller values lose low
-// bits).  Products accumulate in fp32; the tensor scale multiplies the sum.
+// and lies in [2^-10, 2688], so the fp16 product is exact.  x enters as fp16
+// of x * 2^-sig with a per-row power of two (convert_rows: exact for every value
+// within 2^-28 of the row's largest magnitude, no overflow at any bf16
+// magnitude).  Products accumulate in fp32; 2^sig and the tensor scale
+// multiply the sum.
 //
 // Layout.  Lane (i = lane % 16, kb = lane / 16).  A superblock is 256
 // columns; lane (i, kb) owns columns [sb*256 + kb*64, +64) of weight row
@@ -213,8 +215,8 @@ __device__ __forceinline__ void gu_mfma_sb(const GuSb& r, const _Float16* xr, bo
 // takes x row xrows[j] and its h goes to row hrows[j] of hbase (identity
 // maps when null).  Writes h[hrows[j]][n0 .. n0+15].
 __device__ __forceinline__ void gu_compute(const GuRegs& R, float gts, float uts, int H, int n0,
-                                           const _Float16* xh, int m_cnt, const int* xrows, const int* hrows,
-                                           float* hbase, int hstride, float* red) {
+                                           const _Float16* xh, const int* xsig, int m_cnt, const int* xrows,
+                                           const int* hrows, float* hbase, int hstride, float* red) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane & 15, kb = lane >> 4;
     const int nsb = H / kSbCols;
@@ -236,18 +238,28 @@ __device__ __forceinline__ void gu_compute(const GuRegs& R, float gts, float uts
             g += reinterpret_cast<const f32x4_t*>(red)[(w * 2 + 0) * 64 + lane];
             u += reinterpret_cast<const f32x4_t*>(red)[(w * 2 + 1) * 64 + lane];
         }
+        // undo the x row's power-of-two scale, then the tensor scales
+        const int sg = xsig[xr];
         float4 h;
         float gv, uv;
-        gv = g[0] * gts; uv = u[0] * uts; h.x = gv / (1.0f + expf(-gv)) * uv;
-        gv = g[1] * gts; uv = u[1] * uts; h.y = gv / (1.0f + expf(-gv)) * uv;
-        gv = g[2] * gts; uv = u[2] * uts; h.z = gv / (1.0f + expf(-gv)) * uv;
-        gv = g[3] * gts; uv = u[3] * uts; h.w = gv / (1.0f + expf(-gv)) * uv;
+        gv = ldexpf(g[0], sg) * gts; uv = ldexpf(u[0], sg) * uts; h.x = gv / (1.0f + expf(-gv)) * uv;
+        gv = ldexpf(g[1], sg) * gts; uv = ldexpf(u[1], sg) * uts; h.y = gv / (1.0f + expf(-gv)) * uv;
+        gv = ldexpf(g[2], sg) * gts; uv = ldexpf(u[2], sg) * uts; h.z = gv / (1.0f + expf(-gv)) * uv;
+        gv = ldexpf(g[3], sg) * gts; uv = ldexpf(u[3], sg) * uts; h.w = gv / (1.0f + expf(-gv)) * uv;
         const int hr = hrows ? hrows[j] : j;
         *reinterpret_cast<float4*>(hbase + (size_t)hr * hstride + n0 + 4 * kb) = h;
     }
 }
 
-// The router logits (nl floats -> lg) and the K bf16 x rows (-> fp16 xh) in
+// x staging for the matrix cores, in two phases around a workgroup barrier.
+// Phase 1 (stage_logits_x / stage_x_raw): the K bf16 x rows go to LDS
+// unconverted, in the padded fp16 layout.  Phase 2 (convert_rows, after the
+// barrier): whole rows, one per wave at a time -- the wave finds the row's
+// largest |x| (DPP maximum), scales the row by 2^-sig and converts it to
+// fp16 in place; sig goes to xsig[row].  No wave waits for another here, so
+// the waves that select no row convert while the others select.
+
+// The router logits (nl floats -> lg) and the K bf16 x rows (-> raw xh) in
 // one pass, every load of a pass in flight together.
 __device__ __forceinline__ void stage_logits_x(float* lg, const float* logits, int nl, _Float16* xh,
                                                const uint16_t* x, int K, int H) {
@@ -270,52 +282,46 @@ __device__ __forceinline__ void stage_logits_x(float* lg, const float* logits, i
         for (int q = 0; q < U; ++q) {
             const int i = base + q * kBlock + tid;
             if (i < nl) lg[i] = lv[q];
-            if (i < nx) {
-                uint4 o;
-                o.x = bf16pair_to_f16pair(xv[q].x); o.y = bf16pair_to_f16pair(xv[q].y);
-                o.z = bf16pair_to_f16pair(xv[q].z); o.w = bf16pair_to_f16pair(xv[q].w);
-                *reinterpret_cast<uint4*>(xh + xh_index(i >> lpr, (i & (per_row - 1)) * 8, H)) = o;
-            }
+            if (i < nx) *reinterpret_cast<uint4*>(xh + xh_index(i >> lpr, (i & (per_row - 1)) * 8, H)) = xv[q];
         }
     }
 }
 
-__device__ __forceinline__ void stage_x_f16(const uint16_t* x, const int32_t* asg, int o0, int k, int m_cnt, int H,
-                                            _Float16* xh) {
-    const int tid = threadIdx.x;
-    const int per_row = H / 8, lpr = __builtin_ctz(per_row);  // 16-byte pieces per row (a power of two)
-    const int total = m_cnt * per_row;
-    constexpr int U = 4;
-    for (int base = 0; base < total; base += U * kBlock) {
-        uint4 v[U];
+// The K bf16 x rows alone (-> raw xh).
+__device__ __forceinline__ void stage_x_raw(const uint16_t* x, int K, int H, _Float16* xh) {
+    stage_logits_x(nullptr, nullptr, 0, xh, x, K, H);
+}
+
+// Phase 2 by waves w0 .. w0 + nw - 1 (the calling wave converts rows
+// wave - w0, + nw, ...).  H <= 2048: at most four pieces per lane.
+__device__ __forceinline__ void convert_rows(_Float16* xh, int K, int H, int* xsig, int w0, int nw) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (wave < w0 || wave >= w0 + nw) return;
+    const int per_row = H / 8;
+    for (int r = wave - w0; r < K; r += nw) {
+        uint4 v[4];
+        uint32_t m = 0u;
 #pragma unroll
-        for (int q = 0; q < U; ++q) {
-            const int f = base + q * kBlock + tid;
-            v[q] = make_uint4(0, 0, 0, 0);
-            if (f < total) {
-                const int m = f >> lpr, c = f & (per_row - 1);
-                const int src = asg ? asg[o0 + m] / k : m;
-                v[q] = *reinterpret_cast<const uint4*>(x + (size_t)src * H + c * 8);
-            }
+        for (int j = 0; j < 4; ++j) {
+            const int c = lane + 64 * j;
+            v[j] = (c < per_row) ? *reinterpret_cast<const uint4*>(xh + xh_index(r, c * 8, H)) : make_uint4(0, 0, 0, 0);
+            m = max(m, bf16x8_maxabs(v[j]));
         }
+        const int sg = row_sigma(wave_max_u32(m));
+        if (lane == 0) xsig[r] = sg;
 #pragma unroll
-        for (int q = 0; q < U; ++q) {
-            const int f = base + q * kBlock + tid;
-            if (f < total) {
-                const int m = f >> lpr, c = f & (per_row - 1);
-                uint4 o;
-                o.x = bf16pair_to_f16pair(v[q].x); o.y = bf16pair_to_f16pair(v[q].y);
-                o.z = bf16pair_to_f16pair(v[q].z); o.w = bf16pair_to_f16pair(v[q].w);
-                *reinterpret_cast<uint4*>(xh + xh_index(m, c * 8, H)) = o;
-            }
+        for (int j = 0; j < 4; ++j) {
+            const int c = lane + 64 * j;
+            if (c < per_row) *reinterpret_cast<uint4*>(xh + xh_index(r, c * 8, H)) = bf16x8_to_f16x8_scaled(v[j], -sg);
         }
     }
 }
 
 // ---------------------------------------------------------------------------
 // k_router: router GEMV, one wave per expert row, ceil(E/4) workgroups.
-// When chaining layers, x is the RMS-normalised previous output (bf16), with
-// the sums of squares taken from the down kernel's per-workgroup partials;
+// When chaining layers, x is the RMS-normalised previous output times the
+// norm weight (bf16), with the sums of squares taken from the down kernel's
+// per-workgroup partials;
 // every workgroup normalises all rows and publishes its share of x.
 // ---------------------------------------------------------------------------
 
@@ -330,6 +336,8 @@ __device__ void stage_x(const RouterArgs& a, const uint16_t* x_in, int K, uint16
     if (a.y_prev) {
         constexpr int CH = 2;  // float4 pairs (16 elements) per thread per pass
         float4 v[2 * CH];
+        uint4 gv[CH];          // the norm weight of the same 8 columns (bf16)
+        const uint16_t* const gam = a.gamma ? a.gamma : kBf16Ones;
         auto load_pass = [&](int base) {
 #pragma unroll
             for (int j = 0; j < CH; ++j) {
@@ -337,6 +345,7 @@ __device__ void stage_x(const RouterArgs& a, const uint16_t* x_in, int K, uint16
                 const bool ok = i < KH;
                 v[2 * j] = ok ? *reinterpret_cast<const float4*>(a.y_prev + i) : make_float4(0, 0, 0, 0);
                 v[2 * j + 1] = ok ? *reinterpret_cast<const float4*>(a.y_prev + i + 4) : make_float4(0, 0, 0, 0);
+                gv[j] = *reinterpret_cast<const uint4*>(gam + (i & (H - 1)));
             }
         };
         load_pass(0);
@@ -358,13 +367,19 @@ __device__ void stage_x(const RouterArgs& a, const uint16_t* x_in, int K, uint16
             for (int j = 0; j < CH; ++j) {
                 const int i = base + (j * kBlock + tid) * 8;
                 if (i < KH) {
+                    // x = bf16((y * inv_rms) * gamma), fp32 products
                     const float sc = s_inv[i >> lgH];
                     const float4 p = v[2 * j], q = v[2 * j + 1];
+                    const uint4 g = gv[j];
                     uint4 o;
-                    o.x = (uint32_t)f32_to_bf16_rne(p.x * sc) | ((uint32_t)f32_to_bf16_rne(p.y * sc) << 16);
-                    o.y = (uint32_t)f32_to_bf16_rne(p.z * sc) | ((uint32_t)f32_to_bf16_rne(p.w * sc) << 16);
-                    o.z = (uint32_t)f32_to_bf16_rne(q.x * sc) | ((uint32_t)f32_to_bf16_rne(q.y * sc) << 16);
-                    o.w = (uint32_t)f32_to_bf16_rne(q.z * sc) | ((uint32_t)f32_to_bf16_rne(q.w * sc) << 16);
+                    o.x = (uint32_t)f32_to_bf16_rne(p.x * sc * bf16_to_f32(g.x & 0xFFFFu)) |
+                          ((uint32_t)f32_to_bf16_rne(p.y * sc * bf16_to_f32(g.x >> 16)) << 16);
+                    o.y = (uint32_t)f32_to_bf16_rne(p.z * sc * bf16_to_f32(g.y & 0xFFFFu)) |
+                          ((uint32_t)f32_to_bf16_rne(p.w * sc * bf16_to_f32(g.y >> 16)) << 16);
+                    o.z = (uint32_t)f32_to_bf16_rne(q.x * sc * bf16_to_f32(g.z & 0xFFFFu)) |
+                          ((uint32_t)f32_to_bf16_rne(q.y * sc * bf16_to_f32(g.z >> 16)) << 16);
+                    o.w = (uint32_t)f32_to_bf16_rne(q.z * sc * bf16_to_f32(g.w & 0xFFFFu)) |
+                          ((uint32_t)f32_to_bf16_rne(q.w * sc * bf16_to_f32(g.w >> 16)) << 16);
                     *reinterpret_cast<uint4*>(xs + i) = o;
                 }
             }
@@ -474,6 +489,7 @@ template <int P>
 __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_xrows[kWaves][kMaxRows];
+    __shared__ int s_xsig[kMaxRows];
     SelectSmem& sm = *reinterpret_cast<SelectSmem*>(smem);
     float* lg = reinterpret_cast<float*>(smem + (sizeof(SelectSmem) + 15) / 16 * 16);
     _Float16* xh = reinterpret_cast<_Float16*>(smem + select_smem_bytes(a.K, a.sel.E));
@@ -494,12 +510,18 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
         R = gu_load(a.sgate.q, a.sgate.s, a.sup.q, a.sup.s, H, sh_tile * kTileRows);
         gts = a.sgate.ts[0];
         uts = a.sup.ts[0];
-        stage_x_f16(a.x, nullptr, 0, 1, K, H, xh);
+        stage_x_raw(a.x, K, H, xh);
+        __syncthreads();
+        convert_rows(xh, K, H, s_xsig, 0, kWaves);
         __syncthreads();
     } else {
         stage_logits_x(lg, a.sel.logits, K * a.sel.E, xh, a.x, K, H);
         __syncthreads();
         select_rows_p<P>(a.sel, sm, lg, rb == 0);  // weights: only the workgroup that publishes them
+        // x conversion by the waves that select no row (all waves after
+        // their rows when every wave selects)
+        if (K < kWaves) convert_rows(xh, K, H, s_xsig, K, kWaves - K);
+        else convert_rows(xh, K, H, s_xsig, 0, kWaves);
         __syncthreads();
     }
     const int items = shared_blk ? 1 : K * k * nsr;
@@ -549,7 +571,7 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
             published = true;
         }
         if (!owner) continue;
-        gu_compute(R, gts, uts, H, n0, xh, m_cnt, xrows, nullptr,
+        gu_compute(R, gts, uts, H, n0, xh, s_xsig, m_cnt, xrows, nullptr,
                    shared_blk ? a.h_sh : a.h + (size_t)off_e * I, shared_blk ? a.Is : I, red);
         __syncthreads();
     }
@@ -827,8 +849,13 @@ __global__ __launch_bounds__(NT) void k_down(DownArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_dequant: the decode of the GEMM kernels, written out (bf16 and fp32
-// decode paths are both evaluated; a disagreement is reported as NaN)
+// k_dequant: the decodes of the GEMM kernels, written out.  Three routes
+// reach e2m1(code) * e4m3(scale): the fp32 convert then an fp32 multiply
+// (the down kernels' weights), the bf16 convert, and the fp16 operand
+// decode of the gate/up matrix-core tiles (decode8_f16: fp16 convert, then
+// a packed fp16 multiply by the fp16 scale).  A disagreement between them
+// is reported as NaN; the product is then multiplied by the tensor scale in
+// fp32.
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(kBlock) void k_dequant(Fp4Mat m, int n_experts, int rows, int cols, float* out) {
@@ -846,16 +873,61 @@ __global__ __launch_bounds__(kBlock) void k_dequant(Fp4Mat m, int n_experts, int
         fp4x8_to_f32(c.z, wf + 16); fp4x8_to_f32(c.w, wf + 24);
         fp4x8_to_bf16(c.x, wb + 0); fp4x8_to_bf16(c.y, wb + 4);
         fp4x8_to_bf16(c.z, wb + 8); fp4x8_to_bf16(c.w, wb + 12);
+        const _Float16 h0 = e4m3_to_f16<0>(sc), h1 = e4m3_to_f16<1>(sc);
+        const f16x8_t d0 = decode8_f16(c.x, h0), d1 = decode8_f16(c.y, h0);
+        const f16x8_t d2 = decode8_f16(c.z, h1), d3 = decode8_f16(c.w, h1);
         const float s0 = e4m3_to_f32<0>(sc), s1 = e4m3_to_f32<1>(sc);
         const float ts = m.ts[e];
         float* o = out + row * cols + chunk * 32;
 #pragma unroll
         for (int t = 0; t < 32; ++t) {
             const float fb = (float)((t & 1) ? wb[t >> 1].y : wb[t >> 1].x);
-            const float v = (fb == wf[t]) ? wf[t] : __builtin_nanf("");
-            o[t] = (v * (t < 16 ? s0 : s1)) * ts;
+            const f16x8_t& d = (t < 8) ? d0 : (t < 16) ? d1 : (t < 24) ? d2 : d3;
+            const float prod = wf[t] * (t < 16 ? s0 : s1);
+            const bool agree = fb == wf[t] && (float)d[t & 7] == prod;
+            o[t] = (agree ? prod : __builtin_nanf("")) * ts;
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// k_stream_read: a plain streaming read of n16 16-byte pieces (the measured
+// read ceiling next to the benchmark's figures).  Each thread keeps 8 loads
+// in flight per step, grid-strided; the XOR of everything read leaves as one
+// atomic per workgroup so the loads cannot be dropped.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kBlock) void k_stream_read(const uint4* __restrict__ p, size_t n16, uint32_t* sink) {
+    constexpr int U = 8;
+    __shared__ uint32_t s_x[kWaves];
+    const size_t stride = (size_t)gridDim.x * kBlock;
+    uint32_t acc = 0u;
+    size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x;
+    for (; i + (U - 1) * stride < n16; i += U * stride) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = p[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n16; i += stride) {
+        const uint4 v = p[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o, 64);
+    if ((threadIdx.x & 63) == 0) s_x[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) atomicXor(sink, s_x[0] ^ s_x[1] ^ s_x[2] ^ s_x[3]);
+}
+
+hipError_t launch_stream_read(const void* src, size_t n16, uint32_t* sink, hipStream_t st) {
+    int dev = 0, n_cu = 0;
+    hipError_t e;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_stream_read, dim3(n_cu * 8), dim3(kBlock), 0, st, reinterpret_cast<const uint4*>(src), n16,
+                       sink);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

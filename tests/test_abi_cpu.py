@@ -32,16 +32,16 @@ def test_header_declares_the_expected_surface():
 def test_library_exports_every_declared_symbol(L):
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert api.moe_verify_version() >= 100
+    assert api.moe_verify_version() == 200
 
 
 def test_struct_layouts_match_header_sizes():
-    # pointer-only structs: 3 / 2 + 6*3 / 7 / 10 pointers; cfg: 11 x 4 bytes
+    # pointer-only structs: 3 / 2 + 6*3 + 1 / 7 / 11 pointers; cfg: 11 x 4 bytes
     P = ctypes.sizeof(ctypes.c_void_p)
     assert ctypes.sizeof(api.moe_nvfp4) == 3 * P
-    assert ctypes.sizeof(api.moe_layer_weights) == 20 * P
+    assert ctypes.sizeof(api.moe_layer_weights) == 21 * P
     assert ctypes.sizeof(api.moe_route_out) == 7 * P
-    assert ctypes.sizeof(api.moe_debug) == 10 * P
+    assert ctypes.sizeof(api.moe_debug) == 11 * P
     assert ctypes.sizeof(api.moe_cfg) == 44
 
 
@@ -129,7 +129,7 @@ def test_grouped_layer_argument_errors():
     # per-kernel timing is verify-width only
     arr = (api.moe_layer_weights * 1)(_weights())
     ms = (ctypes.c_float * 3)()
-    rc = L.moe_verify_stack_timed(ctypes.byref(cfg), arr, 1, FAKE, 32, FAKE, None, FAKE, n, None, ms)
+    rc = L.moe_verify_stack_timed(ctypes.byref(cfg), arr, 1, FAKE, None, 32, FAKE, None, FAKE, n, None, ms)
     assert rc == api.MOE_ERR_UNSUPPORTED
     # the grouped route needs the workspace
     out = api.moe_route_out(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
@@ -142,10 +142,16 @@ def test_stack_and_route_argument_errors():
     L = api.lib()
     arr = (api.moe_layer_weights * 2)(_weights(), _weights(shared=False))
     n = L.moe_verify_workspace_bytes(ctypes.byref(cfg))
-    rc = L.moe_verify_stack(ctypes.byref(cfg), arr, 2, FAKE, 2, FAKE, None, FAKE, n, None, None)
+    rc = L.moe_verify_stack(ctypes.byref(cfg), arr, 2, FAKE, None, 2, FAKE, None, FAKE, n, None, None)
     assert rc == api.MOE_ERR_INVALID and "layer 1" in api.moe_verify_last_error()
-    rc = L.moe_verify_stack(ctypes.byref(cfg), arr, 0, FAKE, 2, FAKE, None, FAKE, n, None, None)
+    rc = L.moe_verify_stack(ctypes.byref(cfg), arr, 0, FAKE, None, 2, FAKE, None, FAKE, n, None, None)
     assert rc == api.MOE_ERR_INVALID
+    arr2 = (api.moe_layer_weights * 2)(_weights(), _weights())
+    rc = L.moe_verify_stack(ctypes.byref(cfg), arr2, 2, FAKE, FAKE + 8, 2, FAKE, None, FAKE, n, None, None)
+    assert rc == api.MOE_ERR_INVALID and "residual" in api.moe_verify_last_error()
+    arr2[1].norm_w = FAKE + 2
+    rc = L.moe_verify_stack(ctypes.byref(cfg), arr2, 2, FAKE, None, 2, FAKE, None, FAKE, n, None, None)
+    assert rc == api.MOE_ERR_INVALID and "norm_w" in api.moe_verify_last_error()
     out = api.moe_route_out(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
     rc = L.moe_verify_route(ctypes.byref(cfg), FAKE, None, 2, ctypes.byref(out), None, 0, None)
     assert rc == api.MOE_ERR_INVALID
@@ -155,7 +161,8 @@ def test_stack_and_route_argument_errors():
     m = api.moe_nvfp4(FAKE, FAKE, FAKE)
     assert L.moe_verify_dequant_nvfp4(ctypes.byref(m), 1, 4, 48, FAKE, None) == api.MOE_ERR_INVALID
     h = ctypes.c_void_p()
-    rc = L.moe_stack_graph_create(ctypes.byref(cfg), arr, 2, FAKE, 2, FAKE, None, FAKE, n, None, ctypes.byref(h))
+    rc = L.moe_stack_graph_create(ctypes.byref(cfg), arr, 2, FAKE, None, 2, FAKE, None, FAKE, n, None,
+                                  ctypes.byref(h))
     assert rc == api.MOE_ERR_INVALID and not h.value
     assert L.moe_stack_graph_launch(None, None) == api.MOE_ERR_INVALID
     L.moe_stack_graph_destroy(None)
@@ -183,3 +190,73 @@ def test_regime_argument_errors():
     assert n > 0
     assert _layer(cfg, _weights(), K=2, ws_bytes=n) == api.MOE_ERR_UNSUPPORTED
     assert "grouped" in api.moe_verify_last_error()
+
+
+# ---------------------------------------------------------------------------
+# The Python binding validates tensors before anything reaches the library
+# (host tensors, wrong shapes, short buffers), so no host pointer or short
+# buffer becomes a GPU access.  CPU tensors are enough to see every error.
+# ---------------------------------------------------------------------------
+
+import torch  # noqa: E402
+
+
+def _host_layer(shape=inputs.TINY):
+    return inputs.gen_layer(shape, 0, 0)
+
+
+def test_binding_rejects_host_tensors_and_bad_shapes():
+    shape = inputs.TINY
+    cfg = api.make_cfg(shape, 2)
+    w = _host_layer()
+    x = inputs.gen_x(2, shape.hidden, 0)
+    y = torch.empty(2, shape.hidden, dtype=torch.int16)
+    ws = torch.empty(1024, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        api.make_weights(w)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        api.check_weights(w, cfg)
+    bad = dict(w, gate=dict(w["gate"], q=w["gate"]["q"][:, :, :-1]))
+    with pytest.raises(ValueError, match="gate.q has shape"):
+        api.check_weights(bad, cfg)
+    with pytest.raises(ValueError, match="router_w must have shape"):
+        api.check_weights(dict(w, router_w=w["router_w"][:, :-8]), cfg)
+    wts = api.moe_layer_weights()
+    with pytest.raises(ValueError, match=r"\[K, 256\]"):
+        api.moe_verify_layer(cfg, wts, x[:, :128], y, ws)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        api.moe_verify_layer(cfg, wts, x, y, ws)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        api.moe_verify_stack(cfg, [wts], x, y, ws)
+    with pytest.raises(ValueError, match="at least one layer"):
+        api.moe_verify_stack(cfg, [], x, y, ws)
+    with pytest.raises(TypeError, match="dtype"):
+        api.moe_verify_layer(cfg, wts, x.float(), y, ws)
+    out = {k: torch.empty(8, dtype=torch.int32) for k in ("ids", "w", "n_unique", "uniq", "off", "asg", "inv")}
+    with pytest.raises(ValueError, match=r"\[K, 16\]"):
+        api.moe_verify_route(cfg, torch.zeros(2, 8), out)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        api.moe_verify_route(cfg, torch.zeros(2, 16), out)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        api.moe_verify_dequant_nvfp4(w["gate"], torch.empty(16 * 128 * 256))
+
+
+def test_binding_size_checks_use_k_and_hidden():
+    # the size rules themselves, on the marshalling helper: a GPU-less
+    # container cannot make GPU tensors, so the device check comes first
+    cfg = api.make_cfg(inputs.TINY, 2)
+    sizes = api._debug_sizes(cfg, 2)
+    assert sizes["logits"] == 2 * 16 and sizes["off"] == 2 * 2 + 1 and sizes["x_in"] == 2 * 256
+    assert sizes["res_in"] == sizes["y32"] == 2 * 256
+    with pytest.raises(ValueError, match="unknown debug array"):
+        api._check_debug(api.make_debug(bogus=torch.empty(1)), cfg, 2, 1, None)
+
+
+def test_stream_read_argument_errors():
+    L = api.lib()
+    sink = FAKE
+    assert L.moe_verify_stream_read(None, 16, sink, None) == api.MOE_ERR_INVALID
+    assert L.moe_verify_stream_read(FAKE + 4, 16, sink, None) == api.MOE_ERR_INVALID
+    assert L.moe_verify_stream_read(FAKE, 24, sink, None) == api.MOE_ERR_INVALID
+    assert L.moe_verify_stream_read(FAKE, 0, sink, None) == api.MOE_ERR_INVALID
+    assert L.moe_verify_stream_read(FAKE, 16, None, None) == api.MOE_ERR_INVALID

@@ -40,3 +40,22 @@ def test_gateup_bytes_decompose_the_step_bytes(U, K):
     down = (U + 1) * bench.nvfp4_bytes(H, I)
     assert step == U * 2 * bench.nvfp4_bytes(I, H) + 2 * bench.nvfp4_bytes(Is, H) + down + 2 * shape.n_experts * H \
         + 2 * 2 * K * H
+
+
+def test_near_tie_rows_counts_the_kth_gap():
+    import numpy as np
+    l = np.zeros((2, 3, 16), np.float32)
+    l[..., :] = np.arange(16, dtype=np.float32)[::-1]     # well separated
+    l[0, 1, 8] = l[0, 1, 7] - 1e-6                          # rank 8 nearly ties rank 7 (k = 8)
+    assert bench.near_tie_rows(l, 8) == 1
+    assert bench.near_tie_rows(l, 4) == 0
+
+
+def test_host_info_names_cores_and_model():
+    info = bench.host_info()
+    assert info["host_cores"] >= 1 and isinstance(info["cpu_model"], str)
+    assert bench.DTYPE.startswith("nvfp4 weights")
+
+
+def test_kernel_source_hash_covers_the_launch_glue():
+    assert any(p.endswith("moe_abi.hip") for p in bench.KERNEL_SOURCES)

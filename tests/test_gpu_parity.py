@@ -50,6 +50,31 @@ def test_dequant_matches_oracle_bit_exact():
         np.testing.assert_array_equal(got[e], want)
 
 
+def test_dequant_every_code_and_scale_by_every_decode_route():
+    """Every E2M1 code times every finite E4M3 scale, through the three
+    decode routes of the GEMM kernels (fp32, bf16, and the fp16 operand decode
+    of the matrix-core gate/up tiles; the kernel marks any disagreement NaN),
+    bit-exact against the oracle's fp64 decode rounded to fp32."""
+    say("case: dequant every code x scale")
+    rows = 256
+    codes = np.arange(16, dtype=np.uint8)
+    blk = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)      # 16 codes in 8 bytes
+    q = np.tile(np.concatenate([blk, blk]), (2, rows, 1))            # two 16-column blocks per row
+    sb = np.arange(rows, dtype=np.uint8)
+    sb[0x7F], sb[0xFF] = 0x7E, 0xFE                                  # the two NaN codes -> largest finite
+    s = np.repeat(sb[None, :, None], 2, axis=2).repeat(2, axis=0)
+    m = {"q": torch.as_tensor(q.copy()), "s": torch.as_tensor(s.copy()),
+         "ts": torch.tensor([1.0, 3.0e-5], dtype=torch.float32)}
+    md = api.to_device(m)
+    out = torch.empty(2, rows, 32, dtype=torch.float32, device=DEV)
+    api.moe_verify_dequant_nvfp4(md, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert not np.isnan(got).any(), "decode routes disagree"
+    for e in range(2):
+        np.testing.assert_array_equal(got[e], orc.dequant(m, e).astype(np.float32))
+
+
 # ---------------------------------------------------------------------------
 # a2 + a3: selection and dedup from given logits, bit-exact
 # ---------------------------------------------------------------------------
@@ -172,6 +197,42 @@ def test_layer_sigmoid_bias_scale_and_residual():
     # the pages' live router form: sigmoid + selection bias, renormalised,
     # routed scale 2.5, decoder residual fused into the combine
     _layer_case(inputs.LAGUNA, 2, 17, score_fn=1, rs=2.5, residual=True, label="sigmoid")
+
+
+def _scaled_x(K, H, seed, scale):
+    g = torch.Generator().manual_seed(seed)
+    return inputs.bf16_bits(torch.randn(K, H, generator=g) * scale)
+
+
+def range_cases(H):
+    """Activation rows far outside fp16's range: magnitudes around 1e15
+    (beyond 65504), around 1e-10 and 1e-7 (below fp16's normal range 2^-14,
+    the first below its smallest subnormal), and rows mixing a few large
+    entries with ordinary ones, or one ordinary entry with tiny ones."""
+    big = _scaled_x(2, H, 1, 1e15)
+    tiny = _scaled_x(2, H, 2, 1e-10)
+    small = _scaled_x(2, H, 3, 1e-7)
+    mixed = _scaled_x(3, H, 4, 1.0).view(torch.int16)
+    f = inputs.bf16_bits(torch.tensor([3e5, -2.5e5, 1e5, -7e4])).view(torch.int16)
+    mixed[0, :4] = f
+    mixed[1] = _scaled_x(1, H, 5, 1e-7)[0]
+    mixed[1, 7] = inputs.bf16_bits(torch.tensor([1.0]))[0]
+    return [("big", big), ("tiny", tiny), ("small", small), ("mixed", mixed.contiguous())]
+
+
+@pytest.mark.parametrize("case", ["big", "tiny", "small", "mixed"])
+def test_layer_activation_range_beyond_fp16(case):
+    # the gate/up matrix cores take x as fp16 under a per-row power-of-two
+    # scale: rows of any bf16 magnitude match the oracle
+    H = inputs.LAGUNA.hidden
+    x = dict(range_cases(H))[case].to(DEV)
+    gpu, orec, rep = _layer_case(inputs.LAGUNA, x.shape[0], 19, x=x, label="range-" + case,
+                                 regime=api.MOE_REGIME_VERIFY)
+    assert np.isfinite(gpu["y32"]).all()
+    # and each row at the bar of its own largest output (rows of very
+    # different magnitude share the layer)
+    err = np.abs(gpu["y32"].astype(np.float64) - orec["y"]).max(axis=1)
+    assert np.all(err <= 2e-3 * np.abs(orec["y"]).max(axis=1)), err / np.abs(orec["y"]).max(axis=1)
 
 
 def test_layer_other_shapes():
