@@ -199,6 +199,24 @@ MOE_API int moe_verify_layer_grouped(const moe_cfg* cfg, const moe_layer_weights
                                      void* workspace, size_t workspace_bytes, void* stream,
                                      const moe_debug* dbg);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_verify_layer with the same arguments, outputs and errors, but no
+ * workspace argument -- its scratch is a fixed device array inside the
+ * library, moe_verify_noalloc_scratch_bytes() bytes (4 MiB: the full-size
+ * layer up to 32 rows), one per GPU, held until the process ends.  A cfg
+ * whose workspace (moe_verify_workspace_bytes) exceeds it returns
+ * MOE_ERR_UNSUPPORTED before any device work.  The call allocates nothing:
+ * the array's device address is looked up once per device (with that
+ * device current) on the first call there.  Every call on a GPU shares that
+ * GPU's array and nothing in it needs to start at zero; calls that overlap
+ * on one GPU (two streams, two threads) race on it and must be serialised
+ * by the caller. */
+MOE_API int moe_verify_layer_noalloc(const moe_cfg* cfg, const moe_layer_weights* w, const uint16_t* x, int32_t K,
+                                     const uint16_t* residual, uint16_t* y, float* y32, void* stream,
+                                     const moe_debug* dbg);
+MOE_API size_t moe_verify_noalloc_scratch_bytes(void);
+
 /* n_layers layers (steps 1-9).  layers is a HOST array of n_layers weight
  * structs.  x bf16 [K][H] is layer 0's input.  residual (bf16 [K][H]) NULL:
  * no residual anywhere; given: the residual stream -- layer 0 adds

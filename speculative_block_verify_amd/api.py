@@ -62,6 +62,7 @@ class moe_debug(ctypes.Structure):
 
 
 EXPORTS = ["moe_verify_workspace_bytes", "moe_verify_layer", "moe_verify_layer_grouped", "moe_verify_stack",
+           "moe_verify_layer_noalloc", "moe_verify_noalloc_scratch_bytes",
            "moe_verify_stack_timed", "moe_verify_route", "moe_verify_stream_read",
            "moe_verify_dequant_nvfp4", "moe_stack_graph_create", "moe_stack_graph_launch",
            "moe_stack_graph_destroy", "moe_verify_weight_bytes", "moe_verify_last_error",
@@ -87,6 +88,10 @@ def lib() -> ctypes.CDLL:
     L.moe_verify_layer.argtypes = [cfgp, wp, P, _i32, P, P, P, P, Z, P, ctypes.POINTER(moe_debug)]
     L.moe_verify_layer_grouped.restype = ctypes.c_int
     L.moe_verify_layer_grouped.argtypes = [cfgp, wp, P, _i32, P, P, P, P, Z, P, ctypes.POINTER(moe_debug)]
+    L.moe_verify_layer_noalloc.restype = ctypes.c_int
+    L.moe_verify_layer_noalloc.argtypes = [cfgp, wp, P, _i32, P, P, P, P, ctypes.POINTER(moe_debug)]
+    L.moe_verify_noalloc_scratch_bytes.restype = Z
+    L.moe_verify_noalloc_scratch_bytes.argtypes = []
     L.moe_verify_stack.restype = ctypes.c_int
     L.moe_verify_stack.argtypes = [cfgp, wp, _i32, P, P, _i32, P, P, P, Z, P, ctypes.POINTER(moe_debug)]
     L.moe_verify_stack_timed.restype = ctypes.c_int
@@ -313,6 +318,26 @@ def moe_verify_layer_grouped(cfg: moe_cfg, weights: moe_layer_weights, x: torch.
                              residual: Optional[torch.Tensor] = None, debug: Optional[moe_debug] = None,
                              stream=None) -> None:
     _layer_call(lib().moe_verify_layer_grouped, cfg, weights, x, y, workspace, y32, residual, debug, stream)
+
+
+def moe_verify_layer_noalloc(cfg: moe_cfg, weights: moe_layer_weights, x: torch.Tensor, y: torch.Tensor,
+                             y32: Optional[torch.Tensor] = None, residual: Optional[torch.Tensor] = None,
+                             debug: Optional[moe_debug] = None, stream=None) -> None:
+    """moe_verify_layer on the library's fixed scratch array (no workspace)."""
+    K = _rows(x, cfg)
+    dev = x.device
+    KH = K * cfg.hidden
+    px = _ptr(x, _BITS16, "x", device=dev)
+    py = _ptr(y, _BITS16, "y", numel=KH, device=dev)
+    py32 = _ptr(y32, torch.float32, "y32", numel=KH, device=dev)
+    pr = _ptr(residual, _BITS16, "residual", numel=KH, device=dev)
+    _check_debug(debug, cfg, K, 1, dev)
+    _check(lib().moe_verify_layer_noalloc(ctypes.byref(cfg), ctypes.byref(weights), px, K, pr, py, py32,
+                                          _stream(stream), ctypes.byref(debug) if debug is not None else None))
+
+
+def moe_verify_noalloc_scratch_bytes() -> int:
+    return lib().moe_verify_noalloc_scratch_bytes()
 
 
 def _layer_array(layers: Sequence[moe_layer_weights]):

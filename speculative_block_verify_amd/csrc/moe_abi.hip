@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/moe_verify.h"
@@ -458,6 +459,39 @@ int enqueue_stack(const moe_cfg* c, const moe_layer_weights* layers, int n_layer
     return MOE_OK;
 }
 
+// ---------------------------------------------------------------------------
+// the allocation-free entry point's scratch: a fixed device array (each GPU
+// the library runs on holds its own copy until the process ends).  In host
+// code `scratch` only names the symbol; its device address on each GPU comes
+// from hipGetSymbolAddress with that GPU current, kept per device.
+// ---------------------------------------------------------------------------
+
+constexpr size_t kScratchBytes = size_t(4) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch array (looked up on the first
+// call on that device).
+int scratch_of_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "get device");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "scratch symbol address");
+        if (!p) return fail(MOE_ERR_HIP, "scratch symbol address is NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -513,6 +547,21 @@ int moe_verify_layer(const moe_cfg* cfg, const moe_layer_weights* w, const uint1
     if ((rc = enqueue_layer(cfg, w, io, K, L, st))) return rc;
     return copy_debug(cfg, dbg, 0, K, L, x, io.y32, st);
 }
+
+int moe_verify_layer_noalloc(const moe_cfg* cfg, const moe_layer_weights* w, const uint16_t* x, int32_t K,
+                             const uint16_t* residual, uint16_t* y, float* y32, void* stream, const moe_debug* dbg) {
+    int rc;
+    if ((rc = check_cfg(cfg))) return rc;
+    const size_t need = layout(cfg, nullptr).bytes;
+    if (need > kScratchBytes)
+        return fail(MOE_ERR_UNSUPPORTED, "this cfg needs %zu bytes of scratch; the allocation-free entry holds %zu "
+                    "(lower max_rows)", need, kScratchBytes);
+    void* ws = nullptr;
+    if ((rc = scratch_of_current_device(&ws))) return rc;
+    return moe_verify_layer(cfg, w, x, K, residual, y, y32, ws, kScratchBytes, stream, dbg);
+}
+
+size_t moe_verify_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int moe_verify_layer_grouped(const moe_cfg* cfg, const moe_layer_weights* w, const uint16_t* x, int32_t K,
                              const uint16_t* residual, uint16_t* y, float* y32, void* workspace,

@@ -260,3 +260,12 @@ def test_stream_read_argument_errors():
     assert L.moe_verify_stream_read(FAKE, 24, sink, None) == api.MOE_ERR_INVALID
     assert L.moe_verify_stream_read(FAKE, 0, sink, None) == api.MOE_ERR_INVALID
     assert L.moe_verify_stream_read(FAKE, 16, None, None) == api.MOE_ERR_INVALID
+
+
+def test_noalloc_entry_rejects_a_cfg_beyond_its_scratch_before_device_work():
+    L = api.lib()
+    assert L.moe_verify_noalloc_scratch_bytes() == 4 << 20
+    cfg = _cfg(max_rows=64)  # 7.6 MB of workspace at the full-size shape
+    rc = L.moe_verify_layer_noalloc(ctypes.byref(cfg), ctypes.byref(_weights()), FAKE, 2, None, FAKE, None, None,
+                                    None)
+    assert rc == api.MOE_ERR_UNSUPPORTED and "scratch" in api.moe_verify_last_error()
