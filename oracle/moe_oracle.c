@@ -352,3 +352,67 @@ void orc_rmsnorm_bf16(const double* y, int K, int H, double eps, const uint16_t*
         }
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Verify-row lm_head and greedy acceptance (the step after the MoE stack)   */
+/* ------------------------------------------------------------------------ */
+
+/* lm_head over every verify row: logits[r][v] = sum_h x[r][h] * W[v][h],
+ * bf16 inputs, double accumulation.  W: bf16 [V][H] (100,352 x 2048 on the
+ * pages: 0.41 GB, PR #844 section 2).  Every row gets its logits (PR #844
+ * section 5, trap 1: the verifier needs one greedy token per verify row). */
+void orc_lm_head(const uint16_t* x, const uint16_t* w, int K, int V, int H, double* logits) {
+    int r, v, h;
+    double* xd = (double*)malloc(sizeof(double) * (size_t)K * H);
+    for (r = 0; r < K; ++r)
+        for (h = 0; h < H; ++h) xd[(size_t)r * H + h] = orc_bf16(x[(size_t)r * H + h]);
+    for (v = 0; v < V; ++v) {
+        const uint16_t* wv = w + (size_t)v * H;
+        for (r = 0; r < K; ++r) {
+            const double* xr = xd + (size_t)r * H;
+            double acc = 0.0;
+            for (h = 0; h < H; ++h) acc += xr[h] * orc_bf16(wv[h]);
+            logits[(size_t)r * V + v] = acc;
+        }
+    }
+    free(xd);
+}
+
+/* Greedy verification of one block of K rows.  Row r's greedy token is the
+ * argmax of its logits (ties to the lower token id).  Row r's input token is
+ * the draft token draft[r-1] for r >= 1 (row 0 holds the last token already
+ * emitted), so draft[j-1] is checked against row j-1's prediction: it is
+ * accepted when it equals that greedy token or when its logit is a true
+ * top-logit tie, within tie_tol of the row's maximum (the mlxfast README,
+ * "Correctness fixtures": exact match, or a true top-logit tie within the
+ * harness's 1e-6 logit tolerance; tie_tol = 0 is plain greedy).  Decoding
+ * advances by the longest accepted prefix (README: "decode advances by the
+ * longest correct prefix") plus the target's own greedy token at the first
+ * row not covered by it.
+ * Outputs: target[K] greedy tokens; emitted[0..n) = the accepted draft
+ * tokens then that greedy token; *n_emitted = accepted + 1.  Returns the
+ * number of accepted draft tokens. */
+int orc_greedy_accept(const double* logits, int K, int V, const int32_t* draft, double tie_tol,
+                      int32_t* target, int32_t* emitted, int32_t* n_emitted) {
+    int r, v, a = 0;
+    for (r = 0; r < K; ++r) {
+        const double* l = logits + (size_t)r * V;
+        int best = 0;
+        for (v = 1; v < V; ++v)
+            if (l[v] > l[best]) best = v;
+        target[r] = best;
+    }
+    while (a < K - 1) {
+        const double* l = logits + (size_t)a * V;
+        int d = draft[a];
+        if (d == target[a] || (d >= 0 && d < V && l[d] >= l[target[a]] - tie_tol)) {
+            emitted[a] = d;
+            ++a;
+        } else {
+            break;
+        }
+    }
+    emitted[a] = target[a];
+    *n_emitted = a + 1;
+    return a;
+}

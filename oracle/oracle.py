@@ -72,6 +72,8 @@ def lib():
         L.orc_moe_layer.argtypes = [I] * 8 + [D, P, P, P] + [P, P, P] * 6 + [P, P, P, P, P]
         L.orc_rmsnorm_bf16.restype = None; L.orc_rmsnorm_bf16.argtypes = [P, I, I, D, P, P]
         L.orc_bf16_round.restype = None; L.orc_bf16_round.argtypes = [P, I, P]
+        L.orc_lm_head.restype = None; L.orc_lm_head.argtypes = [P, P, I, I, I, P]
+        L.orc_greedy_accept.restype = I; L.orc_greedy_accept.argtypes = [P, I, I, P, D, P, P, P]
         _lib = L
     return _lib
 
@@ -269,6 +271,44 @@ def moe_stack(layers: List[Dict[str, object]], x, top_k: int, eps: float = 1e-6,
             if res is not None:
                 res = bf16_round(rec["y"])
     return out
+
+
+# ---------------------------------------------------------------------------
+# verify-row lm_head and greedy acceptance
+# ---------------------------------------------------------------------------
+
+
+def lm_head(x, w) -> np.ndarray:
+    """float64 logits [K, V] = bf16 x [K, H] . bf16 W [V, H]^T."""
+    xa = _np(x, np.uint16); wa = _np(w, np.uint16)
+    K, H = xa.shape
+    V = wa.shape[0]
+    if wa.shape[1] != H:
+        raise ValueError("W has %d columns, x has %d" % (wa.shape[1], H))
+    out = np.empty((K, V), np.float64)
+    lib().orc_lm_head(_p(xa), _p(wa), K, V, H, _p(out))
+    return out
+
+
+def greedy_accept(logits, draft, tie_tol: float = 1e-6):
+    """Greedy verification of one block (orc_greedy_accept): returns
+    {'target': [K], 'accepted': a, 'emitted': [a + 1]}."""
+    l = np.ascontiguousarray(np.asarray(logits, np.float64))
+    K, V = l.shape
+    d = np.ascontiguousarray(np.asarray(draft, np.int32).reshape(-1))
+    if d.size != max(K - 1, 0):
+        raise ValueError("need K - 1 = %d draft tokens, got %d" % (K - 1, d.size))
+    tgt = np.empty(K, np.int32)
+    em = np.empty(K, np.int32)
+    n = np.zeros(1, np.int32)
+    a = lib().orc_greedy_accept(_p(l), K, V, _p(d) if d.size else None, float(tie_tol), _p(tgt), _p(em), _p(n))
+    return {"target": tgt, "accepted": int(a), "emitted": em[: int(n[0])].copy()}
+
+
+def lm_head_bytes(vocab: int, hidden: int, K: int) -> int:
+    """Algorithmic HBM bytes of one verify step's lm_head: the bf16 matrix
+    once, the K bf16 rows in."""
+    return vocab * hidden * 2 + K * hidden * 2
 
 
 # ---------------------------------------------------------------------------

@@ -29,6 +29,10 @@ MUTATIONS = {
                           "for (n = 0; n < H; ++n) ss += yr[n] * yr[n] * (gamma ? orc_bf16(gamma[n]) * orc_bf16(gamma[n]) : 1.0);"),
     "gamma_reversed": ("if (gamma) v *= orc_bf16(gamma[n]);", "if (gamma) v *= orc_bf16(gamma[H - 1 - n]);"),
     "residual_dropped": ("yr[n] += orc_bf16(residual[(size_t)r * H + n]);", "yr[n] += 0.0 * orc_bf16(residual[(size_t)r * H + n]);"),
+    "argmax_ties_to_higher": ("if (l[v] > l[best]) best = v;", "if (l[v] >= l[best]) best = v;"),
+    "bonus_token_row": ("emitted[a] = target[a];", "emitted[a] = target[a > 0 ? a - 1 : 0];"),
+    "tie_rule_sign": ("l[d] >= l[target[a]] - tie_tol", "l[d] >= l[target[a]] + tie_tol"),
+    "lm_head_transposed": ("acc += xr[h] * orc_bf16(wv[h]);", "acc += xr[h] * orc_bf16(w[((size_t)h * V + v) % ((size_t)V * H)]);"),
     "router_transposed": ("orc_bf16(wr[(size_t)e * H + h])", "orc_bf16(wr[(size_t)h * E % (E * H) + e])"),
     "down_transposed": ("orc_nvfp4_weight(dq, ds, dts, H, I, e, n, i)", "orc_nvfp4_weight(dq, ds, dts, H, I, e, (n + 1) % H, i)"),
 }

@@ -467,3 +467,75 @@ def test_layer_step_bytes_at_two_rows():
     # 16 unique experts + shared + router + x/y at K = 2
     b = orc.layer_step_bytes(2048, 256, 512, 512, 16, 2)
     assert b == 17 * (3 * 589_824 + 12) + 2 * 256 * 2048 + 4 * 2 * 2048
+
+
+# ---------------------------------------------------------------------------
+# Verify-row lm_head and greedy acceptance
+# ---------------------------------------------------------------------------
+
+
+def test_lm_head_matches_float64_matmul():
+    rng = np.random.default_rng(21)
+    K, V, H = 3, 301, 256
+    x = ref.f32_to_bf16_bits(rng.standard_normal((K, H)))
+    w = ref.f32_to_bf16_bits(rng.standard_normal((V, H)) * 0.02)
+    got = orc.lm_head(x, w)
+    want = ref.bf16_to_f64(x) @ ref.bf16_to_f64(w).T
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+def test_greedy_target_is_first_maximum_like_numpy_argmax():
+    rng = np.random.default_rng(22)
+    l = np.round(rng.standard_normal((6, 500)) * 4) / 4      # many exact ties
+    l[2] = 0.0                                               # all tied -> token 0
+    out = orc.greedy_accept(l, np.zeros(5, np.int32))
+    np.testing.assert_array_equal(out["target"], np.argmax(l, axis=1))
+    assert out["target"][2] == 0
+
+
+def _block(K, V, tgt, margin=1.0):
+    l = np.zeros((K, V))
+    for r, t in enumerate(tgt):
+        l[r, t] = margin
+    return l
+
+
+def test_greedy_acceptance_longest_prefix_and_bonus_token():
+    V = 50
+    tgt = [7, 11, 13, 17]
+    l = _block(4, V, tgt)
+    # all three drafts match the previous rows' greedy tokens: 3 accepted + bonus
+    o = orc.greedy_accept(l, [7, 11, 13])
+    assert o["accepted"] == 3 and list(o["emitted"]) == [7, 11, 13, 17]
+    # first draft rejected: the target's own token at row 0 only
+    o = orc.greedy_accept(l, [8, 11, 13])
+    assert o["accepted"] == 0 and list(o["emitted"]) == [7]
+    # a later match after a mismatch does not count (prefix)
+    o = orc.greedy_accept(l, [7, 12, 13])
+    assert o["accepted"] == 1 and list(o["emitted"]) == [7, 11]
+    # one row: no draft, the greedy token
+    o = orc.greedy_accept(l[:1], [])
+    assert o["accepted"] == 0 and list(o["emitted"]) == [7]
+
+
+def test_greedy_acceptance_true_ties_within_the_pages_tolerance():
+    """A draft token whose logit is within 1e-6 of the row's top logit is a
+    true tie and is accepted; 2e-6 below is not; with tolerance 0 only exact
+    ties count."""
+    V = 20
+    l = _block(2, V, [4, 9])
+    l[0, 5] = 1.0 - 0.5e-6
+    o = orc.greedy_accept(l, [5], tie_tol=1e-6)
+    assert o["target"][0] == 4 and o["accepted"] == 1 and list(o["emitted"]) == [5, 9]
+    assert orc.greedy_accept(l, [5], tie_tol=0.0)["accepted"] == 0
+    l[0, 5] = 1.0 - 2e-6
+    assert orc.greedy_accept(l, [5], tie_tol=1e-6)["accepted"] == 0
+    l[0, 5] = 1.0                                  # exact tie, higher id: not the argmax, still a true tie
+    o = orc.greedy_accept(l, [5], tie_tol=0.0)
+    assert o["target"][0] == 4 and o["accepted"] == 1
+
+
+def test_lm_head_bytes_reproduce_the_page_number():
+    g = json.load(open(os.path.join(GOLDEN, "page_byte_budget.json")))
+    b = orc.lm_head_bytes(g["vocab"], 2048, 0)
+    assert b == 411_041_792 and round(b / 1e9, 2) == g["lm_head_approx_GB"]
