@@ -230,6 +230,93 @@ def prefill(args):
     }), flush=True)
 
 
+def lmhead(args):
+    """The verify step's head: lm_head over K verify rows (vocabulary 100352,
+    hidden 2048, bf16: 0.41 GB), argmax per row and greedy acceptance, one
+    call per step.  Two copies of the matrix rotate (822 MB against a 256 MB
+    memory-side cache) with a pool of inputs.  value = algorithmic bytes (the
+    matrix once, the rows in) / time per step."""
+    import numpy as np
+    import torch
+    import oracle as orc
+    from speculative_block_verify_amd import api, inputs
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K, V, H, POOL, SEED = args.rows, inputs.VOCAB, 2048, 4, 31
+    ws_ = [inputs.gen_lm_head(V, H, SEED + c, device=dev) for c in range(2)]
+    xs = [inputs.gen_x(K, H, SEED + 10 + i, device=dev) for i in range(POOL)]
+    drafts = [inputs.gen_tokens(max(K - 1, 1), V, SEED + 20 + i, device=dev) for i in range(POOL)]
+    out = api.alloc_greedy_out(K, dev)
+    wsp = torch.empty(api.moe_verify_lm_head_workspace_bytes(V, K), dtype=torch.uint8, device=dev)
+
+    def step(s):
+        api.moe_verify_lm_head_greedy(xs[s % POOL], ws_[s % 2], out, wsp, draft=drafts[s % POOL] if K > 1 else None)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record(stream)
+    for s in range(args.steps):
+        step(s)
+        ev[s + 1].record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev[0].elapsed_time(ev[-1])
+    per = [ev[s].elapsed_time(ev[s + 1]) for s in range(args.steps)]
+    nbytes = orc.lm_head_bytes(V, H, K)
+    gbs = nbytes / (total_ms / args.steps / 1e3) / 1e9
+    med = statistics.median(per)
+    log("lmhead: %d steps, %.2f us per step (median %.2f), %.1f GB/s" % (args.steps, total_ms / args.steps * 1e3,
+                                                                          med * 1e3, gbs))
+    result = {
+        "metric": "verify-row lm_head + greedy acceptance: weight GB/s and % HBM peak",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 weights and rows, bf16-MFMA/f32-acc", "data": "synthetic",
+        "config": {"workload": "verify-row lm_head (vocabulary 100352 x hidden 2048, bf16) + argmax + greedy "
+                               "acceptance, K=%d rows" % K, "rows": K, "vocab": V, "hidden": H,
+                   "weight_copies": 2, "input_pool": POOL},
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "us_per_step": {"mean": round(total_ms / args.steps * 1e3, 2), "median": round(med * 1e3, 2),
+                        "min": round(min(per) * 1e3, 2), "max": round(max(per) * 1e3, 2)},
+        "stall_steps_over_4x_median": sum(1 for t in per if t > 4 * med),
+        "bytes_per_step": nbytes,
+        "roofline": {"bound": "hbm", "kernel": "k_lm_head + k_greedy_finalize (whole step)",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": nbytes},
+        "seed": SEED, "device": torch.cuda.get_device_name(dev), "rocm": torch.version.hip,
+    }
+    if not args.no_extras:
+        result["stream_read_ceiling_gbs"] = stream_read_ceiling(dev)
+    if not args.no_cpu_baseline:
+        xo = xs[0].cpu().numpy().view(np.uint16)
+        wo = ws_[0].cpu().numpy().view(np.uint16)
+        do = drafts[0].cpu().numpy()[: K - 1]
+        old_aff = os.sched_getaffinity(0)
+        core = max(old_aff)
+        os.sched_setaffinity(0, {core})
+        times = []
+        try:
+            for r in range(3):
+                t0 = time.perf_counter()
+                lo = orc.lm_head(xo, wo)
+                orc.greedy_accept(lo, do)
+                times.append(time.perf_counter() - t0)
+                log("lmhead: oracle run %d: %.2f s" % (r + 1, times[-1]))
+        finally:
+            os.sched_setaffinity(0, old_aff)
+        med_s = statistics.median(times)
+        cb = {"value": round(nbytes / med_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+              "sample": "one verify step (lm_head over %d rows + greedy acceptance), 3 runs, median; single-threaded "
+                        "C (fp64), pinned to core %d" % (K, core),
+              "us_per_step": round(med_s * 1e6, 1), "runs_s": [round(t, 3) for t in times], "pinned_core": core,
+              "gpu_speedup": round(med_s * 1e6 / (total_ms / args.steps * 1e3), 1)}
+        cb.update(host_info())
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+
+
 def cpu_baseline(layers, x0, shape, K, runs=3, gpu_layer0=None, gpu_us_per_stack=None, gpu_gbs=None):
     """The oracle (single-threaded C, fp64), pinned to one host core, chained
     through the whole 40-layer stack on the pool's first input, `runs` times;
@@ -324,8 +411,9 @@ def main():
     ap.add_argument("--timing-steps", type=int, default=16, help="steps of the per-kernel timing pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
-    ap.add_argument("--workload", choices=("stack", "prefill"), default="stack",
-                    help="stack: the 40-layer K=2 verify stack (default); prefill: one 512-row layer")
+    ap.add_argument("--workload", choices=("stack", "prefill", "lmhead"), default="stack",
+                    help="stack: the 40-layer K=2 verify stack (default); prefill: one 512-row layer; lmhead: the "
+                         "verify rows' lm_head + greedy acceptance")
     ap.add_argument("--prefill-layers", type=int, default=8, help="distinct weight sets the prefill mode rotates")
     ap.add_argument("--rows", type=int, default=2, choices=(1, 2, 4, 8, 16),
                     help="verify rows K of the stack workload: 2 (default) is the headline configuration with "
@@ -341,6 +429,9 @@ def main():
         return
     if args.workload == "prefill":
         prefill(args)
+        return
+    if args.workload == "lmhead":
+        lmhead(args)
         return
 
     import torch

@@ -278,6 +278,42 @@ MOE_API int moe_stack_graph_create(const moe_cfg* cfg, const moe_layer_weights* 
 MOE_API int moe_stack_graph_launch(moe_stack_graph* g, void* stream);
 MOE_API void moe_stack_graph_destroy(moe_stack_graph* g);
 
+/* ------------------------------------------------------------------------
+ * The step after the MoE stack: the verify rows' lm_head and greedy block
+ * acceptance.  logits[r][v] = sum_h x[r][h] * W[v][h] for EVERY verify row
+ * (PR #844 section 5, trap 1: the verifier needs one greedy token per verify
+ * row; section 2: W is bf16 [100352][2048], 0.41 GB), bf16 inputs with fp32
+ * accumulation; row r's greedy token is its argmax (ties to the lower token
+ * id).  Row r >= 1's input token is the draft token draft[r-1], so draft[j]
+ * is accepted when it equals row j's greedy token or its logit is a true
+ * top-logit tie, within tie_tol of row j's maximum (mlxfast README,
+ * "Correctness fixtures": exact match, or a tie within 1e-6; 0 = plain
+ * greedy); decode advances by the longest accepted prefix (README) plus the
+ * greedy token of the first row not covered by it.  A draft token outside
+ * [0, vocab) is never accepted.
+ * ------------------------------------------------------------------------ */
+typedef struct moe_greedy_out {
+    int32_t* target;        /* [K] greedy token of each row */
+    float* target_logit;    /* [K] its logit */
+    int32_t* n_accepted;    /* [1] accepted draft tokens a (0 .. K-1) */
+    int32_t* emitted;       /* [K] the a accepted draft tokens, then row a's greedy token (first a + 1 valid) */
+    int32_t* n_emitted;     /* [1] a + 1 */
+} moe_greedy_out;
+
+/* Device workspace of moe_verify_lm_head_greedy (0 when the arguments are
+ * invalid). */
+MOE_API size_t moe_verify_lm_head_workspace_bytes(int32_t vocab, int32_t K);
+
+/* x bf16 [K][hidden] device rows (K in [1, 16]; hidden 256, 512, 1024 or
+ * 2048), w bf16 [vocab][hidden] device, draft int32 [K-1] device (NULL
+ * allowed when K == 1), logits fp32 [K][vocab] device or NULL (then only the
+ * greedy results are written), out: device arrays (struct in host memory).
+ * Asynchronous on `stream`; errors as elsewhere (MOE_ERR_WORKSPACE when
+ * workspace_bytes is short). */
+MOE_API int moe_verify_lm_head_greedy(const uint16_t* x, int32_t K, const uint16_t* w, int32_t vocab, int32_t hidden,
+                                      const int32_t* draft, float tie_tol, float* logits, const moe_greedy_out* out,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Algorithmic HBM bytes of one layer step: the router (if with_router), each
  * of n_unique routed experts once, the shared expert (if with_shared and
  * cfg->shared_inter > 0), x in and y out (bf16, K rows).  NVFP4 matrices

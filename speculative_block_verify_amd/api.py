@@ -55,6 +55,11 @@ class moe_route_out(ctypes.Structure):
                 ("off", _c_void_p), ("asg", _c_void_p), ("inv", _c_void_p)]
 
 
+class moe_greedy_out(ctypes.Structure):
+    _fields_ = [("target", _c_void_p), ("target_logit", _c_void_p), ("n_accepted", _c_void_p),
+                ("emitted", _c_void_p), ("n_emitted", _c_void_p)]
+
+
 class moe_debug(ctypes.Structure):
     _fields_ = [("logits", _c_void_p), ("ids", _c_void_p), ("w", _c_void_p), ("n_unique", _c_void_p),
                 ("uniq", _c_void_p), ("off", _c_void_p), ("asg", _c_void_p), ("inv", _c_void_p),
@@ -63,6 +68,7 @@ class moe_debug(ctypes.Structure):
 
 EXPORTS = ["moe_verify_workspace_bytes", "moe_verify_layer", "moe_verify_layer_grouped", "moe_verify_stack",
            "moe_verify_layer_noalloc", "moe_verify_noalloc_scratch_bytes",
+           "moe_verify_lm_head_workspace_bytes", "moe_verify_lm_head_greedy",
            "moe_verify_stack_timed", "moe_verify_route", "moe_verify_stream_read",
            "moe_verify_dequant_nvfp4", "moe_stack_graph_create", "moe_stack_graph_launch",
            "moe_stack_graph_destroy", "moe_verify_weight_bytes", "moe_verify_last_error",
@@ -92,6 +98,11 @@ def lib() -> ctypes.CDLL:
     L.moe_verify_layer_noalloc.argtypes = [cfgp, wp, P, _i32, P, P, P, P, ctypes.POINTER(moe_debug)]
     L.moe_verify_noalloc_scratch_bytes.restype = Z
     L.moe_verify_noalloc_scratch_bytes.argtypes = []
+    L.moe_verify_lm_head_workspace_bytes.restype = Z
+    L.moe_verify_lm_head_workspace_bytes.argtypes = [_i32, _i32]
+    L.moe_verify_lm_head_greedy.restype = ctypes.c_int
+    L.moe_verify_lm_head_greedy.argtypes = [P, _i32, P, _i32, _i32, P, ctypes.c_float, P,
+                                            ctypes.POINTER(moe_greedy_out), P, Z, P]
     L.moe_verify_stack.restype = ctypes.c_int
     L.moe_verify_stack.argtypes = [cfgp, wp, _i32, P, P, _i32, P, P, P, Z, P, ctypes.POINTER(moe_debug)]
     L.moe_verify_stack_timed.restype = ctypes.c_int
@@ -414,6 +425,46 @@ def moe_verify_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -
     nbytes = src.numel() * src.element_size()
     _check(lib().moe_verify_stream_read(_ptr(src, None, "src", device=dev), nbytes,
                                         _ptr(sink, torch.int32, "sink", numel=1, device=dev), _stream(stream)))
+
+
+def moe_verify_lm_head_workspace_bytes(vocab: int, K: int) -> int:
+    n = lib().moe_verify_lm_head_workspace_bytes(vocab, K)
+    if n == 0:
+        raise MoEError(MOE_ERR_INVALID, moe_verify_last_error())
+    return n
+
+
+GREEDY_FIELDS = ("target", "target_logit", "n_accepted", "emitted", "n_emitted")
+
+
+def alloc_greedy_out(K: int, device="cuda") -> Dict[str, torch.Tensor]:
+    return {"target": torch.empty(K, dtype=torch.int32, device=device),
+            "target_logit": torch.empty(K, dtype=torch.float32, device=device),
+            "n_accepted": torch.empty(1, dtype=torch.int32, device=device),
+            "emitted": torch.empty(K, dtype=torch.int32, device=device),
+            "n_emitted": torch.empty(1, dtype=torch.int32, device=device)}
+
+
+def moe_verify_lm_head_greedy(x: torch.Tensor, w: torch.Tensor, out: Dict[str, torch.Tensor],
+                              workspace: torch.Tensor, draft: Optional[torch.Tensor] = None,
+                              tie_tol: float = 1e-6, logits: Optional[torch.Tensor] = None, stream=None) -> None:
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor [K, hidden]")
+    if not isinstance(w, torch.Tensor) or w.dim() != 2 or w.shape[1] != x.shape[1]:
+        raise ValueError("w must be a 2-D tensor [vocab, %d]" % x.shape[1])
+    K, H = x.shape
+    V = w.shape[0]
+    dev = x.device
+    sizes = {"target": K, "target_logit": K, "n_accepted": 1, "emitted": K, "n_emitted": 1}
+    types = {"target": torch.int32, "target_logit": torch.float32, "n_accepted": torch.int32,
+             "emitted": torch.int32, "n_emitted": torch.int32}
+    go = moe_greedy_out(*[_ptr(out[k], types[k], k, numel=sizes[k], device=dev) for k in GREEDY_FIELDS])
+    pd = _ptr(draft, torch.int32, "draft", numel=K - 1, device=dev) if K > 1 else None
+    pw, nw = _ws(workspace, dev)
+    _check(lib().moe_verify_lm_head_greedy(_ptr(x, _BITS16, "x", device=dev), K, _ptr(w, _BITS16, "w", device=dev),
+                                           V, H, pd, float(tie_tol),
+                                           _ptr(logits, torch.float32, "logits", numel=K * V, device=dev),
+                                           ctypes.byref(go), pw, nw, _stream(stream)))
 
 
 class StackGraph:

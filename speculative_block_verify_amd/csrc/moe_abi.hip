@@ -650,6 +650,38 @@ int moe_verify_dequant_nvfp4(const moe_nvfp4* m, int32_t n_experts, int32_t rows
     return MOE_OK;
 }
 
+size_t moe_verify_lm_head_workspace_bytes(int32_t vocab, int32_t K) {
+    if (vocab < 1 || K < 1 || K > moe::kLmHeadMaxRows) {
+        fail(MOE_ERR_INVALID, "need vocab >= 1 and K in [1, %d]", moe::kLmHeadMaxRows);
+        return 0;
+    }
+    return align256(moe::lm_head_workspace_bytes(vocab, K));
+}
+
+int moe_verify_lm_head_greedy(const uint16_t* x, int32_t K, const uint16_t* w, int32_t vocab, int32_t hidden,
+                              const int32_t* draft, float tie_tol, float* logits, const moe_greedy_out* out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    if (K < 1 || K > moe::kLmHeadMaxRows) return fail(MOE_ERR_INVALID, "K=%d outside [1, %d]", K, moe::kLmHeadMaxRows);
+    if (hidden != 256 && hidden != 512 && hidden != 1024 && hidden != 2048)
+        return fail(MOE_ERR_UNSUPPORTED, "hidden=%d: supported 256, 512, 1024, 2048", hidden);
+    if (vocab < 1 || (long long)vocab * hidden > (1ll << 40)) return fail(MOE_ERR_INVALID, "vocab=%d invalid", vocab);
+    if (!x || !aligned16(x)) return fail(MOE_ERR_INVALID, "x NULL or not 16-byte aligned");
+    if (!w || !aligned16(w)) return fail(MOE_ERR_INVALID, "w NULL or not 16-byte aligned");
+    if (K > 1 && !draft) return fail(MOE_ERR_INVALID, "K=%d rows need K-1 draft tokens", K);
+    if (!(tie_tol >= 0.0f) || !std::isfinite(tie_tol)) return fail(MOE_ERR_INVALID, "tie_tol must be finite and >= 0");
+    if (logits && !aligned16(logits)) return fail(MOE_ERR_INVALID, "logits not 16-byte aligned");
+    if (!out || !out->target || !out->target_logit || !out->n_accepted || !out->emitted || !out->n_emitted)
+        return fail(MOE_ERR_INVALID, "greedy outputs must all be non-NULL");
+    const size_t need = align256(moe::lm_head_workspace_bytes(vocab, K));
+    if (!workspace || !aligned16(workspace)) return fail(MOE_ERR_INVALID, "workspace NULL or not 16-byte aligned");
+    if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    hipError_t e = moe::launch_lm_head_greedy(x, K, w, vocab, hidden, K > 1 ? draft : nullptr, tie_tol, logits,
+                                              out->target, out->target_logit, out->n_accepted, out->emitted,
+                                              out->n_emitted, workspace, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "lm_head launch");
+    return MOE_OK;
+}
+
 int moe_verify_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
     if (!src || !aligned16(src)) return fail(MOE_ERR_INVALID, "src NULL or not 16-byte aligned");
     if (!sink) return fail(MOE_ERR_INVALID, "sink is NULL");

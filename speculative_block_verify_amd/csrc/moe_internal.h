@@ -186,6 +186,15 @@ hipError_t init_grouped_kernels();
 int grouped_max_tiles(int T, int E, int k, bool has_shared);
 bool grouped_lds_fits(int T, int E, int I, int Is);
 
+// Verify-row lm_head + greedy acceptance (lm_head.hip).  workspace: at
+// least lm_head_workspace_bytes(V, K) bytes, 16-byte aligned.
+hipError_t launch_lm_head_greedy(const uint16_t* x, int K, const uint16_t* w, int V, int H, const int32_t* draft,
+                                 float tie_tol, float* logits, int32_t* target, float* target_logit,
+                                 int32_t* n_accepted, int32_t* emitted, int32_t* n_emitted, void* workspace,
+                                 hipStream_t st);
+size_t lm_head_workspace_bytes(int V, int K);
+constexpr int kLmHeadMaxRows = 16;
+
 // One-time kernel attributes (dynamic LDS sizes).
 hipError_t init_kernels();
 

@@ -184,3 +184,27 @@ def gen_stack(shape: MoEShape, n_layers: int, seed: int, device="cpu",
               with_bias: bool = False) -> List[Dict[str, object]]:
     return [gen_layer(shape, seed, l, device, with_bias) for l in range(n_layers)]
 
+
+
+# ---------------------------------------------------------------------------
+# The verify step's head: lm_head weights and draft tokens
+# ---------------------------------------------------------------------------
+
+VOCAB = 100352      # the pages' lm_head: bf16 [100352, 2048], 0.41 GB
+
+
+def gen_lm_head(vocab: int, hidden: int, seed: int, device="cpu") -> torch.Tensor:
+    """bf16 lm_head weights [vocab, hidden] ~ N(0, 0.02^2), as int16 bit
+    patterns (generated in chunks of rows)."""
+    out = torch.empty(vocab, hidden, dtype=torch.int16, device=device)
+    step = max(1, (1 << 24) // hidden)
+    for v0 in range(0, vocab, step):
+        v1 = min(vocab, v0 + step)
+        out[v0:v1] = bf16_bits(_randn((v1 - v0, hidden), device, seed, "lm_head", v0) * WEIGHT_STD)
+    return out
+
+
+def gen_tokens(n: int, vocab: int, seed: int, device="cpu") -> torch.Tensor:
+    """n uniform token ids in [0, vocab) (int32)."""
+    g = _gen(device, seed, "tokens")
+    return torch.randint(0, vocab, (n,), generator=g, device=device, dtype=torch.int32)

@@ -269,3 +269,27 @@ def test_noalloc_entry_rejects_a_cfg_beyond_its_scratch_before_device_work():
     rc = L.moe_verify_layer_noalloc(ctypes.byref(cfg), ctypes.byref(_weights()), FAKE, 2, None, FAKE, None, None,
                                     None)
     assert rc == api.MOE_ERR_UNSUPPORTED and "scratch" in api.moe_verify_last_error()
+
+
+def test_lm_head_argument_errors():
+    L = api.lib()
+    assert ctypes.sizeof(api.moe_greedy_out) == 5 * ctypes.sizeof(ctypes.c_void_p)
+    n = L.moe_verify_lm_head_workspace_bytes(100352, 2)
+    assert n > 0 and n % 256 == 0
+    assert L.moe_verify_lm_head_workspace_bytes(100352, 17) == 0
+    assert L.moe_verify_lm_head_workspace_bytes(0, 2) == 0
+    out = api.moe_greedy_out(FAKE, FAKE, FAKE, FAKE, FAKE)
+
+    def call(x=FAKE, K=2, w=FAKE, V=100352, H=2048, draft=FAKE, tol=1e-6, logits=None, o=out, ws=FAKE, nb=n):
+        return L.moe_verify_lm_head_greedy(x, K, w, V, H, draft, tol, logits, ctypes.byref(o), ws, nb, None)
+
+    assert call(K=0) == api.MOE_ERR_INVALID
+    assert call(K=17) == api.MOE_ERR_INVALID
+    assert call(H=3000) == api.MOE_ERR_UNSUPPORTED
+    assert call(x=FAKE + 2) == api.MOE_ERR_INVALID
+    assert call(draft=None) == api.MOE_ERR_INVALID and "draft" in api.moe_verify_last_error()
+    assert call(tol=-1.0) == api.MOE_ERR_INVALID
+    assert call(tol=float("nan")) == api.MOE_ERR_INVALID
+    assert call(logits=FAKE + 4) == api.MOE_ERR_INVALID
+    assert call(nb=n - 16) == api.MOE_ERR_WORKSPACE
+    assert call(o=api.moe_greedy_out(FAKE, FAKE, None, FAKE, FAKE)) == api.MOE_ERR_INVALID

@@ -1,0 +1,162 @@
+"""GPU parity of the verify step's head: the lm_head over every verify row
+and greedy block acceptance (moe_verify_lm_head_greedy) against the oracle.
+
+Rules (written out here): logits within the fp32 summation bound
+n * 2^-24 * sum_h |x_h w_vh| of the oracle's fp64 values; greedy tokens
+bit-exact except on rows whose oracle top-two gap is within twice that
+bound, where the GPU's token must be one of the tied ones; acceptance and
+emitted tokens equal to the oracle's walk on those rows' tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from speculative_block_verify_amd import api, inputs
+from tests import refdecode as ref
+from tests.conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def oracle_logits(x, w, threads=16):
+    """orc.lm_head over vocabulary chunks on parallel host threads (each
+    vocabulary row's logit depends on that row alone)."""
+    from concurrent.futures import ThreadPoolExecutor
+    xa = np.ascontiguousarray(x.cpu().numpy()).view(np.uint16)
+    wa = np.ascontiguousarray(w.cpu().numpy()).view(np.uint16)
+    V = wa.shape[0]
+    b = np.linspace(0, V, min(threads, V) + 1).astype(int)
+    parts = [(lo, hi) for lo, hi in zip(b[:-1], b[1:]) if hi > lo]
+    with ThreadPoolExecutor(len(parts)) as ex:
+        res = list(ex.map(lambda p: orc.lm_head(xa, np.ascontiguousarray(wa[p[0]:p[1]])), parts))
+    return np.concatenate(res, axis=1)
+
+
+def fp32_bound(x, w):
+    xa = np.abs(ref.bf16_to_f64(np.ascontiguousarray(x.cpu().numpy()).view(np.uint16)))
+    wa = np.abs(ref.bf16_to_f64(np.ascontiguousarray(w.cpu().numpy()).view(np.uint16)))
+    return x.shape[1] * 2.0 ** -24 * (xa @ wa.T)
+
+
+def run(x, w, draft, tie_tol=1e-6, with_logits=True):
+    K = x.shape[0]
+    V = w.shape[0]
+    out = api.alloc_greedy_out(K, DEV)
+    ws = torch.empty(api.moe_verify_lm_head_workspace_bytes(V, K), dtype=torch.uint8, device=DEV)
+    logits = torch.full((K, V), float("nan"), dtype=torch.float32, device=DEV) if with_logits else None
+    api.moe_verify_lm_head_greedy(x, w, out, ws, draft=draft, tie_tol=tie_tol, logits=logits)
+    torch.cuda.synchronize()
+    r = {k: v.cpu().numpy() for k, v in out.items()}
+    r["logits"] = None if logits is None else logits.cpu().numpy()
+    return r
+
+
+def check(gpu, ol, bound, draft, tie_tol, label):
+    K, V = ol.shape
+    if gpu["logits"] is not None:
+        err = np.abs(gpu["logits"].astype(np.float64) - ol)
+        assert np.all(err <= bound), "%s logits: worst %.3g vs bound %.3g" % (label, err.max(), bound.max())
+    top = np.sort(ol, axis=1)[:, ::-1]
+    tie = (top[:, 0] - top[:, 1]) <= 2 * bound.max(axis=1)
+    want = np.argmax(ol, axis=1)
+    tg = gpu["target"]
+    np.testing.assert_array_equal(tg[~tie], want[~tie], err_msg=label + " greedy tokens")
+    for r in np.nonzero(tie)[0]:
+        assert ol[r, tg[r]] >= top[r, 0] - 2 * bound[r].max(), label + " invalid near-tie token"
+    np.testing.assert_allclose(gpu["target_logit"], ol[np.arange(K), tg], rtol=0, atol=bound.max())
+    d = np.zeros(0, np.int32) if draft is None else draft.cpu().numpy()
+    o = orc.greedy_accept(ol, d, tie_tol)
+    rows = o["accepted"] + 1
+    if not tie[:rows].any():
+        assert int(gpu["n_accepted"][0]) == o["accepted"], label + " accepted"
+        assert int(gpu["n_emitted"][0]) == o["accepted"] + 1
+        np.testing.assert_array_equal(gpu["emitted"][:rows], o["emitted"], err_msg=label + " emitted")
+    return {"near_tie_rows": int(tie.sum()), "accepted": int(gpu["n_accepted"][0]),
+            "worst_logit_err_over_bound": float(np.max(np.abs(gpu["logits"] - ol) / bound))
+            if gpu["logits"] is not None else None}
+
+
+@pytest.mark.parametrize("K,V,H", [(1, 16, 256), (2, 1000, 256), (3, 4099, 512), (16, 777, 2048), (2, 64, 1024),
+                                   (5, 6001, 2048)])
+def test_lm_head_shapes(K, V, H):
+    # several tiles per wave, ragged last tiles (V not a multiple of 16 or 4),
+    # one to sixteen rows
+    say("case: lm_head K=%d V=%d H=%d" % (K, V, H))
+    seed = K * 1000 + V
+    x = inputs.gen_x(K, H, seed, device=DEV)
+    w = inputs.gen_lm_head(V, H, seed, device=DEV)
+    ol = oracle_logits(x, w)
+    bound = fp32_bound(x, w)
+    # drafts: the oracle's greedy tokens (every draft accepted), then one
+    # with a mismatch in the middle
+    want = np.argmax(ol, axis=1).astype(np.int32)
+    for label, d in (("all-match", want[: K - 1]), ("mismatch", np.where(np.arange(K - 1) == (K - 1) // 2,
+                                                                         (want[: K - 1] + 1) % V, want[: K - 1]))):
+        draft = torch.as_tensor(np.ascontiguousarray(d, np.int32)).to(DEV) if K > 1 else None
+        gpu = run(x, w, draft)
+        rep = check(gpu, ol, bound, draft, 1e-6, "K=%d V=%d %s" % (K, V, label))
+        say("  %s: %s" % (label, rep))
+
+
+def test_lm_head_draft_tokens_out_of_range_are_rejected():
+    K, V, H = 4, 300, 256
+    x = inputs.gen_x(K, H, 5, device=DEV)
+    w = inputs.gen_lm_head(V, H, 5, device=DEV)
+    ol = oracle_logits(x, w)
+    want = np.argmax(ol, axis=1).astype(np.int32)
+    for bad in (-1, V, 1 << 30):
+        d = want[: K - 1].copy()
+        d[1] = bad
+        gpu = run(x, w, torch.as_tensor(d).to(DEV))
+        assert int(gpu["n_accepted"][0]) == 1 and list(gpu["emitted"][:2]) == [want[0], want[1]]
+
+
+def test_lm_head_exact_tie_takes_lower_token_and_accepts_the_tied_draft():
+    """Duplicate vocabulary rows tie exactly: the greedy token is the lower
+    id, and a draft of the higher id is a true top-logit tie (accepted)."""
+    K, V, H = 3, 2000, 512
+    x = inputs.gen_x(K, H, 7, device=DEV)
+    w = inputs.gen_lm_head(V, H, 7, device=DEV)
+    # rows 300 and 1700 become x[0]'s direction (the largest logit of row 0)
+    xr = ref.bf16_to_f64(x[0].cpu().numpy().view(np.uint16))
+    top = torch.as_tensor(ref.f32_to_bf16_bits(xr * 0.05).astype(np.int16)).to(DEV)
+    w[300] = top
+    w[1700] = top
+    ol = oracle_logits(x, w)
+    assert np.argmax(ol[0]) == 300 and ol[0, 300] == ol[0, 1700]
+    want = np.argmax(ol, axis=1).astype(np.int32)
+    d = np.array([1700, want[1]], np.int32)
+    for tol in (0.0, 1e-6):
+        gpu = run(x, w, torch.as_tensor(d).to(DEV), tie_tol=tol)
+        assert gpu["target"][0] == 300
+        assert int(gpu["n_accepted"][0]) == 2 and list(gpu["emitted"]) == [1700, want[1], want[2]]
+        check(gpu, ol, fp32_bound(x, w), torch.as_tensor(d), tol, "tie tol=%g" % tol)
+
+
+@pytest.mark.parametrize("K", [1, 2, 4, 8])
+def test_lm_head_full_size(K):
+    """The pages' lm_head: vocabulary 100352, hidden 2048 (0.41 GB bf16).
+    Every logit of every row against the oracle; the call without a logits
+    buffer (the hot path) gives the same greedy results.  Up to 4 rows run
+    the row-streaming vector kernel, 8 rows the matrix-core tiles."""
+    say("case: lm_head full size K=%d" % K)
+    V, H = inputs.VOCAB, 2048
+    x = inputs.gen_x(K, H, 100 + K, device=DEV)
+    w = inputs.gen_lm_head(V, H, 100, device=DEV)
+    ol = oracle_logits(x, w)
+    bound = fp32_bound(x, w)
+    want = np.argmax(ol, axis=1).astype(np.int32)
+    draft = torch.as_tensor(np.ascontiguousarray(want[: K - 1])).to(DEV)
+    gpu = run(x, w, draft)
+    rep = check(gpu, ol, bound, draft, 1e-6, "full K=%d" % K)
+    say("  report:", rep)
+    lean = run(x, w, draft, with_logits=False)
+    for k in api.GREEDY_FIELDS:
+        np.testing.assert_array_equal(lean[k], gpu[k], err_msg=k)
