@@ -317,7 +317,82 @@ def lmhead(args):
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(layers, x0, shape, K, runs=3, gpu_layer0=None, gpu_us_per_stack=None, gpu_gbs=None):
+def layer_ksweep(args):
+    """Dedup at real expert reuse: single verify layers (the 40 weight sets of
+    the stack) on correlated rows -- rows 1..K/2 are row 0 plus noise that
+    moves the router logits by ~N(0, 0.01^2), so those rows pick nearly the
+    same experts.  Each layer is its own graph, timed launch by launch with
+    events.  Per K: unique experts U against the K*k slots a gather without
+    dedup streams, and the bytes each reads."""
+    import numpy as np
+    import torch
+    from speculative_block_verify_amd import api, inputs
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    shape, L, SEED = inputs.LAGUNA, 40, 2024
+    layers = inputs.gen_stack(shape, L, SEED, device=dev)
+    sweep = []
+    for K in (1, 2, 4, 8, 16):
+        cfg = api.make_cfg(shape, K)
+        ws = api.alloc_workspace(cfg, dev)
+        wts = [api.make_weights(w, cfg) for w in layers]
+        xs = [inputs.gen_x_correlated(K, shape.hidden, SEED + 100 * K + l, device=dev) for l in range(L)]
+        y = torch.empty(K, shape.hidden, dtype=torch.int16, device=dev)
+        y32 = torch.empty(K, shape.hidden, dtype=torch.float32, device=dev)
+        nu = torch.empty(1, dtype=torch.int32, device=dev)
+        U = []
+        for l in range(L):
+            api.moe_verify_layer(cfg, wts[l], xs[l], y, ws, y32=y32, debug=api.make_debug(n_unique=nu))
+            torch.cuda.synchronize()
+            U.append(int(nu.item()))
+        graphs = [api.StackGraph(cfg, [wts[l]], xs[l], y, ws, y32=y32) for l in range(L)]
+        for g in graphs:
+            g.launch()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        evs = []
+        for r in range(args.layer_reps):
+            for g in graphs:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                g.launch()
+                b.record(stream)
+                evs.append((a, b))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in evs)
+        for g in graphs:
+            g.close()
+        med_us = statistics.median(ms) * 1e3
+        b_dedup = statistics.mean(api.moe_verify_weight_bytes(cfg, u, K) for u in U)
+        b_slots = api.moe_verify_weight_bytes(cfg, K * shape.top_k, K)
+        ent = {"rows": K, "regime": "grouped" if K >= 8 else "verify width",
+               "us_per_layer": {"median": round(med_us, 2), "min": round(ms[0] * 1e3, 2)},
+               "unique_experts_mean": round(float(np.mean(U)), 2), "unique_experts_min": int(min(U)),
+               "unique_experts_max": int(max(U)), "no_dedup_slots": K * shape.top_k,
+               "bytes_per_layer": round(b_dedup), "bytes_per_layer_no_dedup": b_slots,
+               "dedup_byte_saving": round(1.0 - b_dedup / b_slots, 4),
+               "gbs": round(b_dedup / (med_us / 1e6) / 1e9, 1)}
+        log("layer-ksweep: K=%d U=%.2f of %d slots (saves %.1f%% of bytes), %.2f us per layer, %.1f GB/s" % (
+            K, ent["unique_experts_mean"], K * shape.top_k, 100 * ent["dedup_byte_saving"], med_us, ent["gbs"]))
+        sweep.append(ent)
+        del ws
+    k2 = [e for e in sweep if e["rows"] == 2][0]
+    print(json.dumps({
+        "metric": "single MoE verify layer on correlated rows: weight GB/s and unique experts vs slots, K sweep",
+        "value": k2["gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.layer_reps * L, "warmup": 1,
+        "ms_per_step": round(k2["us_per_layer"]["median"] / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": DTYPE, "data": "synthetic",
+        "config": {"workload": "one NVFP4 MoE verify layer per launch over the 40 weight sets of the stack, "
+                               "rows 1..K/2 = row 0 + noise (router logits ~N(0, 0.01^2) apart)",
+                   "hidden": shape.hidden, "experts": shape.n_experts, "top_k": shape.top_k,
+                   "inter": shape.inter, "shared_inter": shape.shared_inter, "weight_sets": L},
+        "pct_hbm_peak": round(100 * k2["gbs"] / HBM_PEAK_GBS, 2),
+        "sweep": sweep, "seed": SEED, "device": torch.cuda.get_device_name(dev), "rocm": torch.version.hip,
+    }), flush=True)
+
+
+def cpu_baseline(layers, x0, shape, K, runs=3, gpu_layer0=None, gpu_us_per_stack=None, gpu_gbs=None,
+                 score_fn=0, rs=1.0, residual=None):
     """The oracle (single-threaded C, fp64), pinned to one host core, chained
     through the whole 40-layer stack on the pool's first input, `runs` times;
     the median run gives µs per stack and GB/s over the same algorithmic
@@ -340,11 +415,14 @@ def cpu_baseline(layers, x0, shape, K, runs=3, gpu_layer0=None, gpu_us_per_stack
     try:
         for run in range(runs):
             xo = x0.cpu().numpy().view(np.uint16)
+            ro = None if residual is None else residual.cpu().numpy().view(np.uint16)
             t_run, b_run = 0.0, 0
             for l, wh in enumerate(host):
                 t0 = time.perf_counter()
-                rec = orc.moe_layer(wh, xo, shape.top_k)
-                xo = orc.rmsnorm_bf16(rec["y"])
+                rec = orc.moe_layer(wh, xo, shape.top_k, score_fn, 1, rs, residual=ro)
+                xo = orc.rmsnorm_bf16(rec["y"], 1e-6, wh.get("norm_w"))
+                if ro is not None:
+                    ro = orc.bf16_round(rec["y"])
                 t_run += time.perf_counter() - t0
                 if gpu_layer0 is not None and parity is None:
                     ref = np.asarray(rec["y"], dtype=np.float64)
@@ -411,10 +489,14 @@ def main():
     ap.add_argument("--timing-steps", type=int, default=16, help="steps of the per-kernel timing pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
-    ap.add_argument("--workload", choices=("stack", "prefill", "lmhead"), default="stack",
+    ap.add_argument("--workload", choices=("stack", "prefill", "lmhead", "layer-ksweep"), default="stack",
                     help="stack: the 40-layer K=2 verify stack (default); prefill: one 512-row layer; lmhead: the "
                          "verify rows' lm_head + greedy acceptance")
     ap.add_argument("--prefill-layers", type=int, default=8, help="distinct weight sets the prefill mode rotates")
+    ap.add_argument("--layer-reps", type=int, default=5, help="launches of each layer graph in the layer K sweep")
+    ap.add_argument("--mode", choices=("softmax", "laguna"), default="softmax",
+                    help="stack workload router: softmax top-8 (the benchmark configuration) or the pages' Laguna "
+                         "tail (sigmoid + selection bias, routed scale 2.5) with norm weights and the residual stream")
     ap.add_argument("--rows", type=int, default=2, choices=(1, 2, 4, 8, 16),
                     help="verify rows K of the stack workload: 2 (default) is the headline configuration with "
                          "independent rows; 1, 4, 8, 16 are the K sweep, whose rows 1..K/2 repeat row 0 plus small "
@@ -433,6 +515,9 @@ def main():
     if args.workload == "lmhead":
         lmhead(args)
         return
+    if args.workload == "layer-ksweep":
+        layer_ksweep(args)
+        return
 
     import torch
     from speculative_block_verify_amd import api, inputs
@@ -440,8 +525,14 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     shape, L, K, POOL, SEED = inputs.LAGUNA, 40, args.rows, 8, 2024
+    laguna = args.mode == "laguna"
     t0 = time.time()
-    layers = inputs.gen_stack(shape, L, SEED, device=dev)
+    layers = inputs.gen_stack(shape, L, SEED, device=dev, with_bias=laguna)
+    residual = None
+    if laguna:
+        for w, g in zip(layers, inputs.gen_norm_weights(L, shape.hidden, SEED, device=dev)):
+            w["norm_w"] = g
+        residual = inputs.gen_x(K, shape.hidden, SEED, device=dev, tag="res")
     if K == 2:
         xs = [inputs.gen_x(K, shape.hidden, SEED + 1 + i, device=dev) for i in range(POOL)]
     else:
@@ -451,9 +542,11 @@ def main():
         L, sum(sum(t.numel() for t in (w[m].values() if isinstance(w[m], dict) else [w[m]]))
                for w in layers for m in w if w[m] is not None) / 1e9, time.time() - t0))
 
-    cfg = api.make_cfg(shape, K)
+    score_fn = api.MOE_SCORE_SIGMOID_BIAS if laguna else api.MOE_SCORE_SOFTMAX
+    rs = 2.5 if laguna else 1.0
+    cfg = api.make_cfg(shape, K, score_fn=score_fn, routed_scale=rs)
     ws = api.alloc_workspace(cfg, dev)
-    wts = [api.make_weights(w) for w in layers]
+    wts = [api.make_weights(w, cfg) for w in layers]
     y = torch.empty(K, shape.hidden, dtype=torch.int16, device=dev)
     y32 = torch.empty(K, shape.hidden, dtype=torch.float32, device=dev)
 
@@ -467,7 +560,7 @@ def main():
     gpu_layer0 = None
     for i in range(POOL):
         dbg = api.make_debug(n_unique=nu, logits=lg_layers, **({"y32": y32_layers} if i == 0 else {}))
-        api.moe_verify_stack(cfg, wts, xs[i], y, ws, y32=y32, debug=dbg)
+        api.moe_verify_stack(cfg, wts, xs[i], y, ws, y32=y32, debug=dbg, residual=residual)
         torch.cuda.synchronize()
         if i == 0:
             gpu_layer0 = y32_layers[0].cpu().numpy()
@@ -480,14 +573,19 @@ def main():
     u_by_layer = np.asarray(uniques, np.float64).mean(axis=0)
     log("bench: unique experts per layer (mean) %.2f; bytes per step %.4f GB" % (
         u_by_layer.mean(), sum(step_bytes) / POOL / 1e9))
-    ties = near_tie_rows(logits_all, shape.top_k)
+    if laguna:
+        # selection keys of the sigmoid router tail: sigmoid(logit) + bias
+        bias = np.stack([w["router_bias"].cpu().numpy() for w in layers])[None, :, None, :]
+        ties = near_tie_rows(1.0 / (1.0 + np.exp(-logits_all.astype(np.float64))) + bias, shape.top_k, 1e-6)
+    else:
+        ties = near_tie_rows(logits_all, shape.top_k)
     logit_dev = None
     if K > 2:
         # realised deviation of the correlated rows' logits from row 0's
         cp = logits_all[:, :, 1:K // 2 + 1, :] - logits_all[:, :, :1, :]
         logit_dev = [round(float(v), 5) for v in cp.std(axis=(0, 2, 3))]
 
-    graphs = [api.StackGraph(cfg, wts, xs[i], y, ws, y32=y32) for i in range(POOL)]
+    graphs = [api.StackGraph(cfg, wts, xs[i], y, ws, y32=y32, residual=residual) for i in range(POOL)]
     for s in range(args.warmup):
         graphs[s % POOL].launch()
     torch.cuda.synchronize()
@@ -519,7 +617,7 @@ def main():
     avg, achieved, gu_avg_bytes = None, None, None
     try:
         for s in range(args.timing_steps):
-            ms = api.moe_verify_stack_timed(cfg, wts, xs[s % POOL], y, ws, y32=y32)
+            ms = api.moe_verify_stack_timed(cfg, wts, xs[s % POOL], y, ws, y32=y32, residual=residual)
             for l, (a, b, c) in enumerate(ms):
                 kt["route"].append(a); kt["gateup"].append(b); kt["down"].append(c)
                 gu_rates.append(gu_bytes[s % POOL][l])
@@ -538,7 +636,7 @@ def main():
         g.close()
 
     one_layer = None
-    if K == 2 and not args.no_extras:
+    if K == 2 and not args.no_extras and not laguna:
         one_layer = single_layer_timing(cfg, wts, xs, y, ws, y32)
         one_layer["gbs"] = round(sum(step_bytes) / POOL / L / (one_layer["median"] / 1e6) / 1e9, 1)
         log("bench: single layer %.2f us (median), %.1f GB/s" % (one_layer["median"], one_layer["gbs"]))
@@ -561,8 +659,12 @@ def main():
         "vs_baseline": None,
         "dtype": DTYPE,
         "data": "synthetic",
-        "config": {"workload": "40-layer NVFP4 MoE verify stack, K=%d rows%s" % (
-                       K, "" if K == 2 else " (K sweep: rows 1..K/2 repeat row 0 plus noise)"), "hidden": shape.hidden,
+        "config": {"workload": "40-layer NVFP4 MoE verify stack, K=%d rows%s%s" % (
+                       K, "" if K == 2 else " (K sweep: rows 1..K/2 repeat row 0 plus noise)",
+                       ", Laguna router tail (sigmoid + selection bias, normalised top-8, routed scale 2.5), "
+                       "norm weights, residual stream" if laguna else ""), "hidden": shape.hidden,
+                   "score_fn": "sigmoid+bias" if laguna else "softmax", "routed_scale": rs,
+                   "residual_stream": laguna,
                    "experts": shape.n_experts, "top_k": shape.top_k, "inter": shape.inter,
                    "shared_inter": shape.shared_inter, "layers": L, "rows": K, "input_pool": POOL,
                    "weights": "NVFP4 (E2M1 + E4M3/16 + fp32 tensor scale), bf16 router/activations"},
@@ -593,7 +695,8 @@ def main():
     result["rocm"] = torch.version.hip
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the host (3 runs of the stack on one pinned core)")
-        result["cpu_baseline"], result["parity"] = cpu_baseline(layers, xs[0], shape, K, 3, gpu_layer0, us_stack, gbs)
+        result["cpu_baseline"], result["parity"] = cpu_baseline(layers, xs[0], shape, K, 3, gpu_layer0, us_stack, gbs,
+                                                                score_fn, rs, residual)
     print(json.dumps(result), flush=True)
 
 

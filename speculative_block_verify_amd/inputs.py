@@ -208,3 +208,9 @@ def gen_tokens(n: int, vocab: int, seed: int, device="cpu") -> torch.Tensor:
     """n uniform token ids in [0, vocab) (int32)."""
     g = _gen(device, seed, "tokens")
     return torch.randint(0, vocab, (n,), generator=g, device=device, dtype=torch.int32)
+
+
+def gen_norm_weights(n_layers: int, hidden: int, seed: int, device="cpu") -> List[torch.Tensor]:
+    """bf16 RMSNorm weights per layer, ~ N(1, 0.1^2) (synthetic; the pages
+    give no values), as int16 bit patterns."""
+    return [bf16_bits(1.0 + 0.1 * _randn((hidden,), device, seed, l, "norm_w")) for l in range(n_layers)]
