@@ -42,10 +42,11 @@ def nvfp4_bytes(rows, cols):
 
 
 def gateup_bytes(shape, n_unique, K):
-    """Algorithmic HBM bytes of one gate/up launch: gate + up of every unique
-    expert and the shared expert, x read once, h written once."""
+    """Algorithmic HBM bytes of one router + gate/up launch: the bf16 router
+    rows, gate + up of every unique expert and of the shared expert, x read
+    once, h written once."""
     H, I, Is, k = shape.hidden, shape.inter, shape.shared_inter, shape.top_k
-    b = n_unique * 2 * nvfp4_bytes(I, H)
+    b = 2 * shape.n_experts * H + n_unique * 2 * nvfp4_bytes(I, H)
     if Is:
         b += 2 * nvfp4_bytes(Is, H)
     return b + K * H * 2 + (K * k * I + K * Is) * 4
@@ -53,7 +54,7 @@ def gateup_bytes(shape, n_unique, K):
 
 KERNEL_SOURCES = ("speculative_block_verify_amd/csrc/moe_kernels.hip", "speculative_block_verify_amd/csrc/moe_device.h",
                   "speculative_block_verify_amd/csrc/moe_internal.h", "speculative_block_verify_amd/csrc/moe_abi.hip")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_gateup_moe_stack_k2_hbm_traffic.txt")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_route_gateup_moe_stack_k2_hbm_traffic.txt")
 
 
 def kernel_source_hash():
@@ -65,7 +66,7 @@ def kernel_source_hash():
 
 
 def measured_traffic():
-    """HBM bytes per k_gateup launch from the committed rocprofv3 counter
+    """HBM bytes per k_route_gateup launch from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, each scaled by the plain-copy
     calibration), or None when the summary is missing or was taken on other
     kernel sources than the ones built now."""
@@ -612,14 +613,14 @@ def main():
     # per-kernel timing pass: same inputs, kernels stamped by their own
     # dispatch (verify-width kernels; from 8 rows the stack runs the grouped
     # kernels, which this pass does not cover)
-    kt = {"route": [], "gateup": [], "down": []}
+    kt = {"route_gateup": [], "down": []}
     gu_rates = []
     avg, achieved, gu_avg_bytes = None, None, None
     try:
         for s in range(args.timing_steps):
             ms = api.moe_verify_stack_timed(cfg, wts, xs[s % POOL], y, ws, y32=y32, residual=residual)
-            for l, (a, b, c) in enumerate(ms):
-                kt["route"].append(a); kt["gateup"].append(b); kt["down"].append(c)
+            for l, (a, b) in enumerate(ms):
+                kt["route_gateup"].append(a); kt["down"].append(b)
                 gu_rates.append(gu_bytes[s % POOL][l])
     except api.MoEError as err:
         if err.code != api.MOE_ERR_UNSUPPORTED:
@@ -628,9 +629,9 @@ def main():
     if gu_rates:
         avg = {k: sum(v) / len(v) for k, v in kt.items()}
         gu_avg_bytes = sum(gu_rates) / len(gu_rates)
-        achieved = gu_avg_bytes / (avg["gateup"] / 1e3) / 1e9
-        log("bench: kernel averages (us): route %.2f gateup %.2f down %.2f; gateup %.1f GB/s" % (
-            avg["route"] * 1e3, avg["gateup"] * 1e3, avg["down"] * 1e3, achieved))
+        achieved = gu_avg_bytes / (avg["route_gateup"] / 1e3) / 1e9
+        log("bench: kernel averages (us): router+gateup %.2f down %.2f; router+gateup %.1f GB/s" % (
+            avg["route_gateup"] * 1e3, avg["down"] * 1e3, achieved))
 
     for g in graphs:
         g.close()
@@ -682,7 +683,7 @@ def main():
         "single_layer_us": one_layer,
         "stream_read_ceiling_gbs": ceiling,
         "roofline": None if avg is None else {
-            "bound": "hbm", "kernel": "k_gateup", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "bound": "hbm", "kernel": "k_route_gateup", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic() if K == 2 else None, "bytes_per_launch": round(gu_avg_bytes)},
         "wall_s": round(wall, 4),

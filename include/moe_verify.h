@@ -163,6 +163,8 @@ typedef struct moe_debug {
     uint16_t* x_in;
     float* y32;
     uint16_t* res_in;
+    int32_t* status;    /* [1] per layer: 0, or nonzero when an in-kernel hand-off
+                           wait gave up (the layer's results are then invalid) */
 } moe_debug;
 
 /* Bytes of device workspace that layer/stack/route calls with this cfg need
@@ -177,7 +179,9 @@ MOE_API size_t moe_verify_workspace_bytes(const moe_cfg* cfg);
  * (MOE_REGIME_*; AUTO: verify width below 8 rows, grouped from 8 rows when
  * the shape meets the grouped limits, grouped above 16 rows):
  *  - verify width (K <= 16): every unique expert is streamed once by
- *    skinny kernels (three launches);
+ *    skinny kernels (two launches per layer: router + selection + gate/up,
+ *    whose gate/up workgroups wait for the router workgroups of the same
+ *    launch through a bounded in-kernel hand-off, then down + combine);
  *  - grouped (prefill, e.g. the 512-row seed prefill of the mlxfast README,
  *    "Why this challenge exists", and wide verify blocks): the T*k slots are
  *    grouped by expert into tiles of up to 32 tokens and the expert GEMMs
@@ -232,8 +236,9 @@ MOE_API int moe_verify_stack(const moe_cfg* cfg, const moe_layer_weights* layers
 /* Profiling aid: the work of moe_verify_stack (no debug copies), with each
  * kernel launched so that a start/stop event pair carries that kernel's own
  * dispatch timestamps.  Synchronises `stream`, then writes the durations in
- * milliseconds to the HOST array kernel_ms[n_layers][3] (router + selection,
- * gate/up + SwiGLU, down + combine).  Verify-width kernels only
+ * milliseconds to the HOST array kernel_ms[n_layers][2] (router + selection
+ * + gate/up + SwiGLU, down + combine), and returns MOE_ERR_HIP if an
+ * in-kernel hand-off wait gave up.  Verify-width kernels only
  * (MOE_ERR_UNSUPPORTED when K and cfg->regime pick the grouped ones). */
 MOE_API int moe_verify_stack_timed(const moe_cfg* cfg, const moe_layer_weights* layers, int32_t n_layers,
                                    const uint16_t* x, const uint16_t* residual, int32_t K, uint16_t* y,

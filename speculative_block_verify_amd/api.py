@@ -63,7 +63,7 @@ class moe_greedy_out(ctypes.Structure):
 class moe_debug(ctypes.Structure):
     _fields_ = [("logits", _c_void_p), ("ids", _c_void_p), ("w", _c_void_p), ("n_unique", _c_void_p),
                 ("uniq", _c_void_p), ("off", _c_void_p), ("asg", _c_void_p), ("inv", _c_void_p),
-                ("x_in", _c_void_p), ("y32", _c_void_p), ("res_in", _c_void_p)]
+                ("x_in", _c_void_p), ("y32", _c_void_p), ("res_in", _c_void_p), ("status", _c_void_p)]
 
 
 EXPORTS = ["moe_verify_workspace_bytes", "moe_verify_layer", "moe_verify_layer_grouped", "moe_verify_stack",
@@ -243,7 +243,7 @@ def make_weights(w: Dict[str, object], cfg: Optional[moe_cfg] = None) -> moe_lay
 def _debug_sizes(cfg: moe_cfg, K: int) -> Dict[str, int]:
     n, H = K * cfg.top_k, cfg.hidden
     return {"logits": K * cfg.n_experts, "ids": n, "w": n, "n_unique": 1, "uniq": n, "off": n + 1, "asg": n,
-            "inv": n, "x_in": K * H, "y32": K * H, "res_in": K * H}
+            "inv": n, "x_in": K * H, "y32": K * H, "res_in": K * H, "status": 1}
 
 
 def make_debug(**arrays) -> moe_debug:
@@ -381,15 +381,15 @@ def moe_verify_stack(cfg: moe_cfg, layers: Sequence[moe_layer_weights], x: torch
 def moe_verify_stack_timed(cfg: moe_cfg, layers: Sequence[moe_layer_weights], x: torch.Tensor, y: torch.Tensor,
                            workspace: torch.Tensor, y32: Optional[torch.Tensor] = None, stream=None,
                            residual: Optional[torch.Tensor] = None):
-    """Returns per-kernel durations in ms as a list of (route, gateup, down)
-    per layer."""
+    """Returns per-kernel durations in ms as a list of (router + gate/up,
+    down) per layer."""
     K, dev, px, pr, py, py32 = _stack_io(cfg, layers, x, y, y32, residual)
     pw, nw = _ws(workspace, dev)
     arr = _layer_array(layers)
-    ms = (ctypes.c_float * (3 * len(layers)))()
+    ms = (ctypes.c_float * (2 * len(layers)))()
     _check(lib().moe_verify_stack_timed(ctypes.byref(cfg), arr, len(layers), px, pr, K, py, py32, pw, nw,
                                         _stream(stream), ms))
-    return [(ms[3 * l], ms[3 * l + 1], ms[3 * l + 2]) for l in range(len(layers))]
+    return [(ms[2 * l], ms[2 * l + 1]) for l in range(len(layers))]
 
 
 def moe_verify_route(cfg: moe_cfg, logits: torch.Tensor, out: Dict[str, torch.Tensor],

@@ -14,7 +14,6 @@
 //                    workgroup leaves one (logit, token) per row.
 //   k_greedy_finalize  one workgroup: the argmax over the workgroups'
 //                    partial results, then the acceptance walk.
-#include <hip/hip_ext.h>
 
 #include "moe_device.h"
 

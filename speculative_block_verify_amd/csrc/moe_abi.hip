@@ -158,6 +158,7 @@ int check_weights(const moe_cfg* c, const moe_layer_weights* w, int layer) {
 
 struct Layout {
     int32_t* meta;
+    uint32_t* handoff;      // the router/gate-up hand-off counter, then its flags, 2 KB apart
     float* logits;
     int32_t* ids;
     float* w;
@@ -192,6 +193,7 @@ Layout layout(const moe_cfg* c, void* base) {
     auto take = [&](size_t bytes) { char* r = p ? p + o : nullptr; o += align256(bytes); return r; };
     L.meta = reinterpret_cast<int32_t*>(take(16 * 4));
     L.logits = reinterpret_cast<float*>(take(R * E * 4));
+    L.handoff = reinterpret_cast<uint32_t*>(take((size_t)moe::kHandoffFlagStride * 4 * (1 + moe::kHandoffFlags)));
     L.ids = reinterpret_cast<int32_t*>(take(R * k * 4));
     L.w = reinterpret_cast<float*>(take(R * k * 4));
     L.uniq = reinterpret_cast<int32_t*>(take(R * k * 4));
@@ -218,6 +220,14 @@ Layout layout(const moe_cfg* c, void* base) {
 
 moe::Fp4Mat mat(const moe_nvfp4& m) { return moe::Fp4Mat{m.q, m.s, m.ts}; }
 
+// Every call starts the router/gate-up hand-off counter and the status word
+// at zero (the workspace may hold anything); within a call each down kernel
+// resets the counter for the next layer.
+int start_call(const Layout& L, hipStream_t st) {
+    hipError_t e = moe::launch_handoff_reset(L.handoff, L.meta + moe::kMetaStatus, st);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "reset launch");
+}
+
 // ---------------------------------------------------------------------------
 // one layer on the stream
 // ---------------------------------------------------------------------------
@@ -238,20 +248,20 @@ int enqueue_layer(const moe_cfg* c, const moe_layer_weights* w, const LayerIO& i
     hipError_t e;
     const bool has_sh = c->shared_inter > 0;
     const moe::Fp4Mat none{nullptr, nullptr, nullptr};
+    uint32_t* counter = L.handoff;
+    int32_t* status = L.meta + moe::kMetaStatus;
 
-    moe::RouterArgs ra{};
-    ra.x_in = io.x_in;
-    ra.y_prev = io.y_prev;
-    ra.ssq = L.ssq;
-    ra.gamma = io.gamma;
-    ra.x_out = L.xbuf;
-    ra.eps = c->rms_eps;
-    ra.wr = w->router_w;
-    ra.logits = L.logits;
-    ra.K = K; ra.H = c->hidden; ra.E = c->n_experts;
-    if ((e = moe::launch_router(ra, st, tm ? &tm[0] : nullptr)) != hipSuccess) return hip_fail(e, "router launch");
-
-    moe::GateUpArgs ga{};
+    moe::RouteGateUpArgs ra{};
+    ra.r.x_in = io.x_in;
+    ra.r.y_prev = io.y_prev;
+    ra.r.ssq = L.ssq;
+    ra.r.gamma = io.gamma;
+    ra.r.x_out = L.xbuf;
+    ra.r.eps = c->rms_eps;
+    ra.r.wr = w->router_w;
+    ra.r.logits = L.logits;
+    ra.r.K = K; ra.r.H = c->hidden; ra.r.E = c->n_experts;
+    moe::GateUpArgs& ga = ra.g;
     ga.sel.logits = L.logits;
     ga.sel.bias = w->router_bias;
     ga.sel.ids = L.ids; ga.sel.w = L.w;
@@ -259,16 +269,19 @@ int enqueue_layer(const moe_cfg* c, const moe_layer_weights* w, const LayerIO& i
     ga.sel.uniq = L.uniq; ga.sel.off = L.off; ga.sel.asg = L.asg; ga.sel.inv = L.inv;
     ga.sel.K = K; ga.sel.E = c->n_experts; ga.sel.k = c->top_k;
     ga.sel.score_fn = c->score_fn; ga.sel.norm_topk = c->norm_topk;
-    ga.x = io.y_prev ? L.xbuf : io.x_in;
+    ga.x = nullptr;
     ga.gate = mat(w->gate); ga.up = mat(w->up);
     ga.h = L.h;
     ga.sgate = has_sh ? mat(w->sh_gate) : none;
     ga.sup = has_sh ? mat(w->sh_up) : none;
     ga.h_sh = L.h_sh;
     ga.K = K; ga.H = c->hidden; ga.I = c->inter; ga.Is = c->shared_inter;
-    const int max_unique = std::min(c->n_experts, K * c->top_k);
-    if ((e = moe::launch_gateup(ga, max_unique, st, tm ? &tm[1] : nullptr)) != hipSuccess)
-        return hip_fail(e, "gate/up launch");
+    ra.counter = counter;
+    ra.status = status;
+    ra.n_router = (c->n_experts + moe::kWaves - 1) / moe::kWaves;
+    ra.spin_limit = moe::kRouteSpinLimit;
+    if ((e = moe::launch_route_gateup(ra, st, tm ? &tm[0] : nullptr)) != hipSuccess)
+        return hip_fail(e, "router + gate/up launch");
 
     moe::DownArgs da{};
     da.down = mat(w->down);
@@ -283,7 +296,8 @@ int enqueue_layer(const moe_cfg* c, const moe_layer_weights* w, const LayerIO& i
     da.rs = c->routed_scale;
     da.prefetch = reinterpret_cast<const uint8_t*>(next_router);
     da.prefetch_bytes = next_router ? 2 * c->n_experts * c->hidden : 0;
-    if ((e = moe::launch_down(da, st, tm ? &tm[2] : nullptr)) != hipSuccess) return hip_fail(e, "down launch");
+    da.counter = counter;
+    if ((e = moe::launch_down(da, st, tm ? &tm[1] : nullptr)) != hipSuccess) return hip_fail(e, "down launch");
     return MOE_OK;
 }
 
@@ -370,6 +384,7 @@ int copy_debug(const moe_cfg* c, const moe_debug* d, int layer, int K, const Lay
         {d->inv ? d->inv + layer * n : nullptr, L.inv, n * 4},
         {d->x_in ? d->x_in + layer * K * H : nullptr, x_in, K * H * 2},
         {d->y32 ? d->y32 + layer * K * H : nullptr, y32, K * H * 4},
+        {d->status ? d->status + layer : nullptr, L.meta + moe::kMetaStatus, 4},
     };
     for (const Item& it : items) {
         if (!it.dst) continue;
@@ -419,6 +434,8 @@ int enqueue_stack(const moe_cfg* c, const moe_layer_weights* layers, int n_layer
     const Layout L = layout(c, ws);
     hipError_t e = moe::init_kernels();
     if (e != hipSuccess) return hip_fail(e, "kernel attributes");
+    int rc0 = start_call(L, st);
+    if (rc0) return rc0;
     const bool stream_res = residual != nullptr;
     if (use_grouped(c, K)) {
         // grouped regime: each layer's combine writes the next layer's input,
@@ -450,7 +467,7 @@ int enqueue_stack(const moe_cfg* c, const moe_layer_weights* layers, int n_layer
         io.y = last ? y : (stream_res ? L.ybf : nullptr);
         int rc = copy_debug_residual(c, dbg, l, K, io.residual, st);
         if (rc) return rc;
-        rc = enqueue_layer(c, &layers[l], io, K, L, st, tm ? tm + 3 * l : nullptr,
+        rc = enqueue_layer(c, &layers[l], io, K, L, st, tm ? tm + 2 * l : nullptr,
                            last ? nullptr : layers[l + 1].router_w);
         if (rc) return rc;
         rc = copy_debug(c, dbg, l, K, L, l == 0 ? x : L.xbuf, io.y32, st);
@@ -533,6 +550,7 @@ int moe_verify_layer(const moe_cfg* cfg, const moe_layer_weights* w, const uint1
     hipError_t e = moe::init_kernels();
     if (e != hipSuccess) return hip_fail(e, "kernel attributes");
     float* yo = y32 ? y32 : L.ybuf;
+    if ((rc = start_call(L, st))) return rc;
     if ((rc = copy_debug_residual(cfg, dbg, 0, K, residual, st))) return rc;
     if (use_grouped(cfg, K)) {
         if ((rc = enqueue_layer_grouped(cfg, w, x, K, residual, yo, y, nullptr, L, st))) return rc;
@@ -576,6 +594,7 @@ int moe_verify_layer_grouped(const moe_cfg* cfg, const moe_layer_weights* w, con
     hipError_t e = moe::init_kernels();
     if (e != hipSuccess) return hip_fail(e, "kernel attributes");
     float* yo = y32 ? y32 : L.ybuf;
+    if ((rc = start_call(L, st))) return rc;
     if ((rc = copy_debug_residual(cfg, dbg, 0, K, residual, st))) return rc;
     if ((rc = enqueue_layer_grouped(cfg, w, x, K, residual, yo, y, nullptr, L, st))) return rc;
     return copy_debug(cfg, dbg, 0, K, L, x, yo, st);
@@ -706,7 +725,7 @@ int moe_verify_stack_timed(const moe_cfg* cfg, const moe_layer_weights* layers, 
         if ((rc = check_weights(cfg, &layers[l], l))) return rc;
     if ((rc = check_io(x, y, y32, residual))) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int n_ev = 3 * n_layers;
+    const int n_ev = 2 * n_layers;
     moe::Timing* tm = new moe::Timing[n_ev]();
     hipError_t e = hipSuccess;
     int made = 0;
@@ -724,6 +743,14 @@ int moe_verify_stack_timed(const moe_cfg* cfg, const moe_layer_weights* layers, 
             float ms = 0.0f;
             if ((e = hipEventElapsedTime(&ms, tm[i].start, tm[i].stop)) != hipSuccess) rc = hip_fail(e, "elapsed time");
             kernel_ms[i] = ms;
+        }
+        if (!rc) {
+            int32_t status = 0;
+            const Layout L = layout(cfg, workspace);
+            if ((e = hipMemcpy(&status, L.meta + moe::kMetaStatus, 4, hipMemcpyDeviceToHost)) != hipSuccess)
+                rc = hip_fail(e, "status read");
+            else if (status)
+                rc = fail(MOE_ERR_HIP, "a router/gate-up hand-off wait gave up (status %d)", status);
         }
     } else {
         rc = hip_fail(e, "event create");

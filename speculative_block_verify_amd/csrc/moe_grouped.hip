@@ -3,7 +3,7 @@
 // expert GEMMs are dense contractions for the matrix cores (the 512-row seed
 // prefill of the mlxfast README, "Why this challenge exists"; PR #844
 // section 8 notes the stock grouped GEMM needs several tokens per expert).
-// Per layer, after the router GEMV (k_router over 16-row chunks):
+// Per layer, after the router GEMV on the matrix cores (k_router_mfma):
 //   k_select_rows   top-k and mixture weights, one wave per row (the same
 //                   selection code as the verify-width path);
 //   k_group         one workgroup: the canonical CSR of the T*k slots by
@@ -27,7 +27,6 @@
 //                   (+ residual) in rank order (PR #844 section 5 expression
 //                   order), y32 / bf16 y, and for stacked layers the next
 //                   layer's bf16 RMS-normalised input.
-#include <hip/hip_ext.h>
 
 #include "moe_device.h"
 

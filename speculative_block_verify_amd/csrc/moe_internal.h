@@ -76,6 +76,16 @@ struct GateUpArgs {
     int K, H, I, Is;
 };
 
+// Router + gate/up in one launch (k_route_gateup).
+struct RouteGateUpArgs {
+    RouterArgs r;           // router rows, x_in or y_prev/ssq/gamma, logits (written), x_out
+    GateUpArgs g;           // selection + gate/up; g.x is not read (x is formed from r)
+    uint32_t* counter;      // hand-off counter, zero at launch; flag f at counter[kHandoffFlagStride * (1 + f)]
+    int32_t* status;        // set to 1 when a bounded wait gives up
+    int n_router;           // router workgroups (E / 4, rounded up)
+    int spin_limit;         // polls of a bounded wait
+};
+
 struct DownArgs {
     Fp4Mat down;            // [E][H][I/2]
     Fp4Mat sdown;           // [1][H][Is/2]
@@ -93,6 +103,7 @@ struct DownArgs {
     const uint8_t* prefetch;   // bytes the next launch reads first (the next layer's router), or nullptr
     int prefetch_bytes;        // multiple of 16
     int h_lds_bytes;           // dynamic LDS of the launch: h rows staged per chunk (set by launch_down)
+    uint32_t* counter;         // the router/gate-up hand-off counter to reset, or nullptr
     int K, H, I, Is, k;
     float rs;
 };
@@ -165,10 +176,14 @@ struct Timing {
 };
 
 // Launchers (moe_kernels.hip).  Each returns the hipError_t of the launch.
-hipError_t launch_router(const RouterArgs& a, hipStream_t st, const Timing* t = nullptr);
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);  // logits given
-hipError_t launch_gateup(const GateUpArgs& a, int max_unique, hipStream_t st, const Timing* t = nullptr);
 hipError_t launch_down(const DownArgs& a, hipStream_t st, const Timing* t = nullptr);
+hipError_t launch_route_gateup(const RouteGateUpArgs& a, hipStream_t st, const Timing* t = nullptr);
+hipError_t launch_handoff_reset(uint32_t* counter, int32_t* status, hipStream_t st);
+constexpr int kHandoffFlags = 32;          // flags the last router workgroup raises
+constexpr int kHandoffFlagStride = 512;    // words between the counter and each flag (2 KB)
+constexpr int kMetaStatus = 3;             // workspace word: nonzero after a bounded wait gave up
+constexpr int kRouteSpinLimit = 1 << 22;   // polls (with a short sleep each) before a wait gives up
 hipError_t launch_dequant(Fp4Mat m, int n_experts, int rows, int cols, float* out, hipStream_t st);
 hipError_t launch_stream_read(const void* src, size_t n16, uint32_t* sink, hipStream_t st);
 

@@ -1,17 +1,18 @@
 // gfx950 (CDNA4) kernels of the NVFP4 MoE block-verify layer, verify-width
-// regime (K <= 16 rows).  Per layer three launches:
-//   k_router  router GEMV, one wave per expert row, bf16 x staged in LDS,
-//             v_dot2_f32_bf16, fp32 accumulation; when chaining layers its
-//             prologue RMS-normalises the previous layer's output;
-//   k_gateup  the shared expert's gate/up tiles, then routed workgroups that
-//             each repeat the selection from the logits (top-k per row with a
+// regime (K <= 16 rows).  Per layer two launches:
+//   k_route_gateup  router workgroups (router GEMV, one wave per expert row,
+//             bf16 x staged in LDS, v_dot2_f32_bf16, fp32 accumulation;
+//             when chaining layers x is the RMS-normalised previous output)
+//             hand their logits over inside the launch to the shared
+//             expert's gate/up tiles and the routed workgroups, which each
+//             repeat the selection from the logits (top-k per row with a
 //             DPP wave argmax, after the router tail of PR #844 section 4:
 //             argPartition + takeAlong) and the dedup CSR (PR #844 section 8
 //             notes the stock gather reads a repeated expert once per slot;
 //             here each unique expert is streamed once), then loop over work
-//             items (unique expert, 16 intermediate rows) on the matrix cores:
-//             128-bit loads of packed E2M1 codes, in-register decode, fp16
-//             MFMA, SwiGLU epilogue writing fp32 h;
+//             items (unique expert, 16 intermediate rows) on the matrix
+//             cores: 128-bit loads of packed E2M1 codes, in-register decode,
+//             fp16 MFMA, SwiGLU epilogue writing fp32 h;
 //   k_down    one workgroup per 8 output rows: every unique expert's down
 //             rows for that slab (fp32 decode, fp32 h), per-slot partials in
 //             LDS, then the deterministic combine
@@ -22,7 +23,9 @@
 // possible count (capped; workgroups loop) and surplus workgroups finish
 // after the selection.  No kernel uses a device-wide fence: on this part an
 // agent-scope release writes back the L2 and costs far more than a launch
-// boundary inside a graph.
+// boundary inside a graph; the in-launch hand-off uses agent-scope relaxed
+// stores completed with a wait on the memory counters instead.
+
 #include <hip/hip_ext.h>
 
 #include "moe_device.h"
@@ -252,45 +255,12 @@ __device__ __forceinline__ void gu_compute(const GuRegs& R, float gts, float uts
 }
 
 // x staging for the matrix cores, in two phases around a workgroup barrier.
-// Phase 1 (stage_logits_x / stage_x_raw): the K bf16 x rows go to LDS
+// Phase 1 (stage_x with padded = true): the K bf16 x rows go to LDS
 // unconverted, in the padded fp16 layout.  Phase 2 (convert_rows, after the
 // barrier): whole rows, one per wave at a time -- the wave finds the row's
 // largest |x| (DPP maximum), scales the row by 2^-sig and converts it to
 // fp16 in place; sig goes to xsig[row].  No wave waits for another here, so
 // the waves that select no row convert while the others select.
-
-// The router logits (nl floats -> lg) and the K bf16 x rows (-> raw xh) in
-// one pass, every load of a pass in flight together.
-__device__ __forceinline__ void stage_logits_x(float* lg, const float* logits, int nl, _Float16* xh,
-                                               const uint16_t* x, int K, int H) {
-    const int tid = threadIdx.x;
-    const int per_row = H / 8, lpr = __builtin_ctz(per_row);  // 16-byte pieces per row (a power of two)
-    const int nx = K * per_row;
-    const int n = nl > nx ? nl : nx;
-    constexpr int U = 4;
-    for (int base = 0; base < n; base += U * kBlock) {
-        float lv[U];
-        uint4 xv[U];
-#pragma unroll
-        for (int q = 0; q < U; ++q) {
-            const int i = base + q * kBlock + tid;
-            lv[q] = (i < nl) ? logits[i] : 0.0f;
-            xv[q] = (i < nx) ? *reinterpret_cast<const uint4*>(x + (size_t)(i >> lpr) * H + (i & (per_row - 1)) * 8)
-                             : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int q = 0; q < U; ++q) {
-            const int i = base + q * kBlock + tid;
-            if (i < nl) lg[i] = lv[q];
-            if (i < nx) *reinterpret_cast<uint4*>(xh + xh_index(i >> lpr, (i & (per_row - 1)) * 8, H)) = xv[q];
-        }
-    }
-}
-
-// The K bf16 x rows alone (-> raw xh).
-__device__ __forceinline__ void stage_x_raw(const uint16_t* x, int K, int H, _Float16* xh) {
-    stage_logits_x(nullptr, nullptr, 0, xh, x, K, H);
-}
 
 // Phase 2 by waves w0 .. w0 + nw - 1 (the calling wave converts rows
 // wave - w0, + nw, ...).  H <= 2048: at most four pieces per lane.
@@ -318,21 +288,24 @@ __device__ __forceinline__ void convert_rows(_Float16* xh, int K, int H, int* xs
 }
 
 // ---------------------------------------------------------------------------
-// k_router: router GEMV, one wave per expert row, ceil(E/4) workgroups.
-// When chaining layers, x is the RMS-normalised previous output times the
-// norm weight (bf16), with the sums of squares taken from the down kernel's
-// per-workgroup partials;
-// every workgroup normalises all rows and publishes its share of x.
+// Router x.  When chaining layers, x is the RMS-normalised previous output
+// times the norm weight (bf16), with the sums of squares taken from the down
+// kernel's per-workgroup partials; every workgroup that needs x normalises
+// all rows itself, and each router workgroup publishes its share of x.
 // ---------------------------------------------------------------------------
 
 constexpr int kRouterPieces = 4;  // 16-byte router pieces per lane (hidden <= 2048)
 
-// Builds this layer's bf16 x in LDS (xs, K*H) from x_in (rows of this
-// launch's chunk) or from y_prev.
+// Builds this layer's bf16 x in LDS from x_in (rows of this launch's chunk)
+// or from y_prev: dense rows xs[K][H] (padded = false) or the padded layout
+// of the matrix-core x operand (padded = true, xh_index).  With publish_n >
+// 0 the workgroup also writes its share publish_idx of x to x_out.  Every
+// caller runs the same arithmetic, so every workgroup holds the same bits.
 __device__ void stage_x(const RouterArgs& a, const uint16_t* x_in, int K, uint16_t* xs, float* s_inv,
-                        int publish_idx, int publish_n) {
+                        int publish_idx, int publish_n, bool padded = false) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int H = a.H, KH = K * H, lgH = __builtin_ctz(H);  // H is a power of two
+    auto dst = [&](int i) { return padded ? xs + xh_index(i >> lgH, i & (H - 1), H) : xs + i; };
     if (a.y_prev) {
         constexpr int CH = 2;  // float4 pairs (16 elements) per thread per pass
         float4 v[2 * CH];
@@ -380,16 +353,16 @@ __device__ void stage_x(const RouterArgs& a, const uint16_t* x_in, int K, uint16
                           ((uint32_t)f32_to_bf16_rne(q.y * sc * bf16_to_f32(g.z >> 16)) << 16);
                     o.w = (uint32_t)f32_to_bf16_rne(q.z * sc * bf16_to_f32(g.w & 0xFFFFu)) |
                           ((uint32_t)f32_to_bf16_rne(q.w * sc * bf16_to_f32(g.w >> 16)) << 16);
-                    *reinterpret_cast<uint4*>(xs + i) = o;
+                    *reinterpret_cast<uint4*>(dst(i)) = o;
                 }
             }
         }
         __syncthreads();
-        {  // this workgroup's share of the normalised x
+        if (publish_n > 0) {  // this workgroup's share of the normalised x
             const int per = (KH / 8 + publish_n - 1) / publish_n * 8;
             const int i0 = publish_idx * per;
             for (int i = i0 + tid * 8; i < min(KH, i0 + per); i += kBlock * 8)
-                *reinterpret_cast<uint4*>(a.x_out + i) = *reinterpret_cast<const uint4*>(xs + i);
+                *reinterpret_cast<uint4*>(a.x_out + i) = *reinterpret_cast<const uint4*>(dst(i));
         }
     } else {
         constexpr int CH = 4;
@@ -403,41 +376,79 @@ __device__ void stage_x(const RouterArgs& a, const uint16_t* x_in, int K, uint16
 #pragma unroll
             for (int j = 0; j < CH; ++j) {
                 const int i = base + (j * kBlock + tid) * 8;
-                if (i < KH) *reinterpret_cast<uint4*>(xs + i) = v[j];
+                if (i < KH) *reinterpret_cast<uint4*>(dst(i)) = v[j];
             }
         }
         __syncthreads();
     }
 }
 
-// gridDim.y > 1 splits the rows into chunks of MAXM (only without y_prev).
-template <int MAXM>
-__global__ __launch_bounds__(kBlock) void k_router(RouterArgs a) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-    __shared__ float s_inv[kMaxRows];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int H = a.H, E = a.E;
-    const int r0 = blockIdx.y * MAXM;
-    const int K = min(MAXM, a.K - r0);
-    float* const logits = a.logits + (size_t)r0 * E;
-    const int n_router_blocks = (E + kWaves - 1) / kWaves;
+// Gate/up LDS: the selection's tables and staged logits, the padded fp16 x
+// rows, the SwiGLU reduction scratch.
+__host__ __device__ constexpr size_t gateup_smem_bytes(int K, int E, int H) {
+    return select_smem_bytes(K, E) + (size_t)K * xh_row_stride(H) * 2 + (size_t)kRedFloats * 4;
+}
 
-    {
-        // this wave's router row, requested before anything else
-        const int e = blockIdx.x * kWaves + wave;
+// ---------------------------------------------------------------------------
+// k_route_gateup: the router and the gate/up of one layer in one launch.
+//   workgroups [0, n_router): the router GEMV (one wave per expert row);
+//     each publishes its logits with agent-scope write-through
+//     stores, waits until they have completed, then adds one to the hand-off
+//     counter; the one that completes the count raises kHandoffFlags flags;
+//   [n_router, n_router + Is/16): the shared expert's gate/up tiles (they
+//     need x only);
+//   the rest: routed gate/up workgroups.  They normalise x themselves while
+//     the router runs, wait (bounded) for their flag (workgroup b polls flag
+//     b % kHandoffFlags, so few poll any one address), read the logits with
+//     agent-scope loads, repeat the top-k of every row (cheaper than a
+//     separate launch or a grid-wide fence) and loop over work items (slot
+//     r*k+j, 16 intermediate rows).  An item is done by the slot of the
+//     first row that selected its expert, for every row that selected it,
+//     so each unique expert is streamed once; items of later rows' slots of
+//     the same expert are skipped.  h rows are indexed by position in the
+//     canonical dedup order (expert ascending, then row), which each item
+//     derives from the selection in LDS.  The first routed workgroup also
+//     writes the canonical dedup CSR (for the down kernel) while its own
+//     weight loads are in flight.
+// Workgroups are dispatched in index order, so every router workgroup is
+// resident before any workgroup that waits for it.  The counter is zero at
+// launch (the previous layer's down kernel, or the call's first kernel,
+// resets it).  A wait past its bound sets *status and goes on, so the
+// launch always ends (the results are then invalid and the host reports
+// the status).
+// ---------------------------------------------------------------------------
+
+// dynamic LDS limit of k_route_gateup: its static arrays (row lists, row
+// scales, selection scratch) stay within 8 KB of the 160 KB
+constexpr int kRgMaxDynLds = 160 * 1024 - 8 * 1024;
+
+template <int P, int MAXM>
+__global__ __launch_bounds__(kBlock) void k_route_gateup(RouteGateUpArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int s_xrows[kWaves][kMaxRows];
+    __shared__ int s_xsig[kMaxRows];
+    __shared__ float s_inv[kMaxRows];
+    const GateUpArgs& g = a.g;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int H = g.H, K = g.K, k = g.sel.k, I = g.I, n = K * k, E = g.sel.E;
+    const int bid = blockIdx.x;
+
+    if (bid < a.n_router) {
+        // ---- router workgroup: this wave's router row, requested first
+        uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+        const int e = bid * kWaves + wave;
         uint4 wv[kRouterPieces];
 #pragma unroll
         for (int t = 0; t < kRouterPieces; ++t) {
             const int p = lane * 8 + t * 512;
-            wv[t] = (e < E && p < H) ? *reinterpret_cast<const uint4*>(a.wr + (size_t)e * H + p)
+            wv[t] = (e < E && p < H) ? *reinterpret_cast<const uint4*>(a.r.wr + (size_t)e * H + p)
                                      : make_uint4(0, 0, 0, 0);
         }
-        stage_x(a, a.x_in + (size_t)r0 * H, K, xs, s_inv, blockIdx.x, n_router_blocks);
+        stage_x(a.r, a.r.x_in, K, xs, s_inv, bid, a.n_router);
         if (e < E) {
-            float acc[kMaxRows];
+            float acc[MAXM];
 #pragma unroll
-            for (int r = 0; r < kMaxRows; ++r) acc[r] = 0.0f;
+            for (int r = 0; r < MAXM; ++r) acc[r] = 0.0f;
 #pragma unroll
             for (int t = 0; t < kRouterPieces; ++t) {
                 const int p = lane * 8 + t * 512;
@@ -460,66 +471,80 @@ __global__ __launch_bounds__(kBlock) void k_router(RouterArgs a) {
             for (int r = 0; r < MAXM; ++r) {
                 if (r < K) {
                     const float t = wave_sum(acc[r]);
-                    if (lane == 0) logits[(size_t)r * E + e] = t;
+                    if (lane == 0)
+                        __hip_atomic_store(reinterpret_cast<uint32_t*>(a.r.logits) + (size_t)r * E + e,
+                                           __float_as_uint(t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
         }
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's logits have reached the coherent level
+        __syncthreads();
+        // the last router workgroup to finish raises every flag (one per
+        // 2 KB, so the waiting workgroups poll many addresses, not one)
+        if (wave == 0) {
+            uint32_t old = 0u;
+            if (lane == 0) old = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            old = (uint32_t)__builtin_amdgcn_readfirstlane((int)old);
+            if (old == (uint32_t)(a.n_router - 1) && lane < kHandoffFlags)
+                __hip_atomic_store(a.counter + kHandoffFlagStride * (1 + lane), 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return;
     }
-}
 
-// ---------------------------------------------------------------------------
-// k_gateup: the last Is/16 workgroups are the shared expert's gate/up tiles
-// (they need only x and skip the selection).  Every other workgroup stages
-// the logits and x of all rows, repeats the top-k of every row (cheaper than
-// a separate launch or a grid-wide fence) and loops over work items
-// (slot r*k+j, 16 intermediate rows).  An item is done by the slot of the
-// first row that selected its expert, for every row that selected it, so
-// each unique expert is streamed once; items of later rows' slots of the
-// same expert are skipped.  h rows are indexed by position in the canonical
-// dedup order (expert ascending, then row), which each item derives from the
-// selection in LDS.  The first routed workgroup also writes the canonical
-// dedup CSR (for the down kernel) while its own weight loads are in flight.
-// ---------------------------------------------------------------------------
-
-__host__ __device__ constexpr size_t gateup_smem_bytes(int K, int E, int H) {
-    return select_smem_bytes(K, E) + (size_t)K * xh_row_stride(H) * 2 + (size_t)kRedFloats * 4;
-}
-
-template <int P>
-__global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ int s_xrows[kWaves][kMaxRows];
-    __shared__ int s_xsig[kMaxRows];
+    // ---- gate/up workgroups (gateup_smem_bytes layout)
     SelectSmem& sm = *reinterpret_cast<SelectSmem*>(smem);
     float* lg = reinterpret_cast<float*>(smem + (sizeof(SelectSmem) + 15) / 16 * 16);
-    _Float16* xh = reinterpret_cast<_Float16*>(smem + select_smem_bytes(a.K, a.sel.E));
-    float* red = reinterpret_cast<float*>(smem + select_smem_bytes(a.K, a.sel.E) + (size_t)a.K * xh_row_stride(a.H) * 2);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int H = a.H, K = a.K, k = a.sel.k, I = a.I, n = K * k;
-    // routed workgroups first (dispatched first, two per compute unit), the
-    // shared expert's Is/16 tiles last
-    const int n_sh = a.sgate.q ? a.Is / kTileRows : 0;
-    const int n_rb = gridDim.x - n_sh, rb = blockIdx.x;
-    const bool shared_blk = rb >= n_rb;
-    const int sh_tile = rb - n_rb;
+    _Float16* xh = reinterpret_cast<_Float16*>(smem + select_smem_bytes(K, E));
+    float* red = reinterpret_cast<float*>(smem + select_smem_bytes(K, E) + (size_t)K * xh_row_stride(H) * 2);
+    const int n_sh = g.sgate.q ? g.Is / kTileRows : 0;
+    const bool shared_blk = bid < a.n_router + n_sh;
+    const int sh_tile = bid - a.n_router;
+    const int n_rb = gridDim.x - a.n_router - n_sh, rb = bid - a.n_router - n_sh;
     const int nsr = I / kTileRows;
     GuRegs R;
-    float gts = 0.0f, uts = 0.0f;  // tensor scales, requested with the weights
+    float gts = 0.0f, uts = 0.0f;
     if (shared_blk) {
-        // shared expert tile: weights requested before x is staged
-        R = gu_load(a.sgate.q, a.sgate.s, a.sup.q, a.sup.s, H, sh_tile * kTileRows);
-        gts = a.sgate.ts[0];
-        uts = a.sup.ts[0];
-        stage_x_raw(a.x, K, H, xh);
-        __syncthreads();
+        // shared expert tile: weights requested before x is formed
+        R = gu_load(g.sgate.q, g.sgate.s, g.sup.q, g.sup.s, H, sh_tile * kTileRows);
+        gts = g.sgate.ts[0];
+        uts = g.sup.ts[0];
+        stage_x(a.r, a.r.x_in, K, reinterpret_cast<uint16_t*>(xh), s_inv, 0, 0, true);
         convert_rows(xh, K, H, s_xsig, 0, kWaves);
         __syncthreads();
     } else {
-        stage_logits_x(lg, a.sel.logits, K * a.sel.E, xh, a.x, K, H);
+        stage_x(a.r, a.r.x_in, K, reinterpret_cast<uint16_t*>(xh), s_inv, 0, 0, true);
+        if (tid == 0) {
+            const uint32_t* flag = a.counter + kHandoffFlagStride * (1 + bid % kHandoffFlags);
+            int spins = 0;
+            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+                if (++spins > a.spin_limit) {
+                    __hip_atomic_store(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
         __syncthreads();
-        select_rows_p<P>(a.sel, sm, lg, rb == 0);  // weights: only the workgroup that publishes them
-        // x conversion by the waves that select no row (all waves after
-        // their rows when every wave selects)
+        {
+            const uint32_t* src = reinterpret_cast<const uint32_t*>(g.sel.logits);
+            constexpr int U = 4;
+            for (int base = 0; base < K * E; base += U * kBlock) {
+                uint32_t v[U];
+#pragma unroll
+                for (int q = 0; q < U; ++q) {
+                    const int i = base + q * kBlock + tid;
+                    v[q] = i < K * E ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+                }
+#pragma unroll
+                for (int q = 0; q < U; ++q) {
+                    const int i = base + q * kBlock + tid;
+                    if (i < K * E) lg[i] = __uint_as_float(v[q]);
+                }
+            }
+        }
+        __syncthreads();
+        select_rows_p<P>(g.sel, sm, lg, rb == 0);  // weights: only the workgroup that publishes them
         if (K < kWaves) convert_rows(xh, K, H, s_xsig, K, kWaves - K);
         else convert_rows(xh, K, H, s_xsig, 0, kWaves);
         __syncthreads();
@@ -556,9 +581,9 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
             owner = first == s;  // the item belongs to e's first slot
             if (owner) {
                 const size_t eq = (size_t)e * I * (H / 2), es = (size_t)e * I * (H / 16);
-                R = gu_load(a.gate.q + eq, a.gate.s + es, a.up.q + eq, a.up.s + es, H, n0);
-                gts = a.gate.ts[e];
-                uts = a.up.ts[e];
+                R = gu_load(g.gate.q + eq, g.gate.s + es, g.up.q + eq, g.up.s + es, H, n0);
+                gts = g.gate.ts[e];
+                uts = g.up.ts[e];
                 m_cnt = cnt;
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
@@ -567,15 +592,29 @@ __global__ __launch_bounds__(kBlock) void k_gateup(GateUpArgs a) {
             }
         }
         if (!published) {
-            dedup_publish(a.sel, sm);
+            dedup_publish(g.sel, sm);
             published = true;
         }
         if (!owner) continue;
         gu_compute(R, gts, uts, H, n0, xh, s_xsig, m_cnt, xrows, nullptr,
-                   shared_blk ? a.h_sh : a.h + (size_t)off_e * I, shared_blk ? a.Is : I, red);
+                   shared_blk ? g.h_sh : g.h + (size_t)off_e * I, shared_blk ? g.Is : I, red);
         __syncthreads();
     }
-    if (!published) dedup_publish(a.sel, sm);
+    if (!published) dedup_publish(g.sel, sm);
+}
+
+// The hand-off counter and its flags to zero (thread t < 1 + kHandoffFlags
+// clears one word).
+__device__ __forceinline__ void handoff_clear(uint32_t* counter, int t) {
+    if (t <= kHandoffFlags)
+        __hip_atomic_store(counter + kHandoffFlagStride * t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The call's first kernel: the hand-off counter, its flags and the status
+// word to zero.
+__global__ void k_handoff_reset(uint32_t* counter, int32_t* status) {
+    handoff_clear(counter, threadIdx.x);
+    if (threadIdx.x == 0) __hip_atomic_store(status, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -623,6 +662,9 @@ __global__ __launch_bounds__(NT) void k_down(DownArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.H, K = a.K, k = a.k, n = K * k;
     const int n_base = blockIdx.x * NH;
+    // the router/gate-up launch of this layer has ended: its hand-off
+    // counter starts the next layer at zero
+    if (a.counter && blockIdx.x == 0) handoff_clear(a.counter, tid);
     const bool has_sh = a.sdown.q != nullptr;
     // matrix pointers read once; the per-task choice below selects values
     const uint8_t* const dq = a.down.q;
@@ -938,7 +980,7 @@ int gateup_slab_rows(int) { return kTileRows; }
 
 bool lds_fits(int K, int E, int H) {
     const size_t router = (size_t)K * H * 2;
-    return gateup_smem_bytes(K, E, H) <= (size_t)kMaxDynLds && router <= (size_t)kMaxDynLds &&
+    return gateup_smem_bytes(K, E, H) <= (size_t)kRgMaxDynLds && router <= (size_t)kRgMaxDynLds &&
            select_smem_bytes(K, E) <= (size_t)kMaxDynLds;
 }
 
@@ -966,16 +1008,12 @@ hipError_t init_kernels() {
     static hipError_t once = [] {
         hipError_t e;
         if ((e = set_lds(k_select, kMaxDynLds)) != hipSuccess) return e;
-        if ((e = set_lds(k_gateup<1>, kMaxDynLds)) != hipSuccess) return e;
-        if ((e = set_lds(k_gateup<2>, kMaxDynLds)) != hipSuccess) return e;
-        if ((e = set_lds(k_gateup<4>, kMaxDynLds)) != hipSuccess) return e;
-        if ((e = set_lds(k_gateup<8>, kMaxDynLds)) != hipSuccess) return e;
-        if ((e = set_lds(k_gateup<16>, kMaxDynLds)) != hipSuccess) return e;
-        if ((e = set_lds(k_router<1>, kMaxDynLds)) != hipSuccess) return e;
-        if ((e = set_lds(k_router<2>, kMaxDynLds)) != hipSuccess) return e;
-        if ((e = set_lds(k_router<4>, kMaxDynLds)) != hipSuccess) return e;
-        if ((e = set_lds(k_router<8>, kMaxDynLds)) != hipSuccess) return e;
-        if ((e = set_lds(k_router<16>, kMaxDynLds)) != hipSuccess) return e;
+#define MOE_SET_RG(P)                                                                       \
+        if ((e = set_lds(k_route_gateup<P, 2>, kRgMaxDynLds)) != hipSuccess) return e;         \
+        if ((e = set_lds(k_route_gateup<P, 4>, kRgMaxDynLds)) != hipSuccess) return e;         \
+        if ((e = set_lds(k_route_gateup<P, kMaxRows>, kRgMaxDynLds)) != hipSuccess) return e;
+        MOE_SET_RG(1) MOE_SET_RG(2) MOE_SET_RG(4) MOE_SET_RG(8) MOE_SET_RG(16)
+#undef MOE_SET_RG
         if ((e = set_lds(k_down<kDownSuSmall, kDownThreads, kDownBatchSmall>, kDownHLdsBytes)) != hipSuccess)
             return e;
         if ((e = set_lds(k_down<kDownSuBig, kDownThreadsBig, kDownBatchBig>, kDownHLdsBytes)) != hipSuccess)
@@ -989,52 +1027,51 @@ hipError_t init_kernels() {
     return once;
 }
 
-hipError_t launch_router(const RouterArgs& a, hipStream_t st, const Timing* t) {
-    // more than kMaxRows rows (prefill, no y_prev): chunks of kMaxRows on grid y
-    const int grid = (a.E + kWaves - 1) / kWaves;
-    const int chunks = (a.K + kMaxRows - 1) / kMaxRows;
-    if (chunks > 1 && a.y_prev) return hipErrorInvalidValue;
-    const size_t smem = (size_t)(a.K < kMaxRows ? a.K : kMaxRows) * a.H * 2;
-    const dim3 g(grid, chunks), b(kBlock);
-    if (a.K <= 1) return launch(k_router<1>, g, b, smem, st, t, a);
-    if (a.K <= 2) return launch(k_router<2>, g, b, smem, st, t, a);
-    if (a.K <= 4) return launch(k_router<4>, g, b, smem, st, t, a);
-    if (a.K <= 8) return launch(k_router<8>, g, b, smem, st, t, a);
-    return launch(k_router<16>, g, b, smem, st, t, a);
-}
-
 hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
     return launch(k_select, dim3(1), dim3(kBlock), select_smem_bytes(a.K, a.E), st, nullptr, a);
 }
 
-// Routed gate/up workgroups: one per work item (slot, 16 intermediate rows),
-// but no more than fit on the chip at once next to the shared expert's
-// tiles (the rest loop over items): a second dispatch round of workgroups
-// would repeat the selection after the first round's weights have streamed.
+// The fused router + gate/up launch: n_router router workgroups, the
+// shared expert's tiles, then routed workgroups, one per work item (slot,
+// 16 intermediate rows) but no more than fit on the chip at once next to
+// the others (the rest loop over items): a second dispatch round would
+// repeat the selection after the first round's weights have streamed, and
+// a waiting workgroup must never keep a router workgroup from starting.
 template <typename Kern>
-hipError_t launch_gateup_k(Kern k, const GateUpArgs& a, hipStream_t st, const Timing* t) {
-    const size_t smem = gateup_smem_bytes(a.K, a.sel.E, a.H);
-    const int n_sh = a.sgate.q ? a.Is / kTileRows : 0;
-    int grid = a.K * a.sel.k * (a.I / kTileRows);
+hipError_t launch_route_gateup_k(Kern k, const RouteGateUpArgs& a, hipStream_t st, const Timing* t) {
+    const size_t smem = gateup_smem_bytes(a.g.K, a.g.sel.E, a.g.H);
+    const int n_sh = a.g.sgate.q ? a.g.Is / kTileRows : 0;
+    int grid = a.g.K * a.g.sel.k * (a.g.I / kTileRows);
     if (grid > kGateUpMaxGrid) grid = kGateUpMaxGrid;
     int dev = 0, n_cu = 0, per_cu = 0;
     hipError_t e;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
     if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kBlock, smem)) != hipSuccess) return e;
-    const int fit = per_cu * n_cu - n_sh;
+    const int fit = per_cu * n_cu - n_sh - a.n_router;
     if (fit >= 1 && grid > fit) grid = fit;
-    return launch(k, dim3(grid + n_sh), dim3(kBlock), smem, st, t, a);
+    return launch(k, dim3(a.n_router + n_sh + grid), dim3(kBlock), smem, st, t, a);
 }
 
-hipError_t launch_gateup(const GateUpArgs& a, int max_unique, hipStream_t st, const Timing* t) {
-    (void)max_unique;
-    const int P = (a.sel.E + 63) >> 6;  // experts per lane of the top-k
-    if (P <= 1) return launch_gateup_k(k_gateup<1>, a, st, t);
-    if (P <= 2) return launch_gateup_k(k_gateup<2>, a, st, t);
-    if (P <= 4) return launch_gateup_k(k_gateup<4>, a, st, t);
-    if (P <= 8) return launch_gateup_k(k_gateup<8>, a, st, t);
-    return launch_gateup_k(k_gateup<16>, a, st, t);
+template <int P>
+hipError_t launch_route_gateup_p(const RouteGateUpArgs& a, hipStream_t st, const Timing* t) {
+    if (a.g.K <= 2) return launch_route_gateup_k(k_route_gateup<P, 2>, a, st, t);
+    if (a.g.K <= 4) return launch_route_gateup_k(k_route_gateup<P, 4>, a, st, t);
+    return launch_route_gateup_k(k_route_gateup<P, kMaxRows>, a, st, t);
+}
+
+hipError_t launch_route_gateup(const RouteGateUpArgs& a, hipStream_t st, const Timing* t) {
+    const int P = (a.g.sel.E + 63) >> 6;  // experts per lane of the top-k
+    if (P <= 1) return launch_route_gateup_p<1>(a, st, t);
+    if (P <= 2) return launch_route_gateup_p<2>(a, st, t);
+    if (P <= 4) return launch_route_gateup_p<4>(a, st, t);
+    if (P <= 8) return launch_route_gateup_p<8>(a, st, t);
+    return launch_route_gateup_p<16>(a, st, t);
+}
+
+hipError_t launch_handoff_reset(uint32_t* counter, int32_t* status, hipStream_t st) {
+    hipLaunchKernelGGL(k_handoff_reset, dim3(1), dim3(64), 0, st, counter, status);
+    return hipGetLastError();
 }
 
 hipError_t launch_down(const DownArgs& a, hipStream_t st, const Timing* t) {

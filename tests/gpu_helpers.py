@@ -56,6 +56,7 @@ def run_layer(cfg, wd, x, residual=None, ws=None, grouped=False):
         "inv": torch.empty(n, dtype=torch.int32, device=dev),
         "x_in": torch.empty(K, H, dtype=torch.int16, device=dev),
         "y32": torch.empty(K, H, dtype=torch.float32, device=dev),
+        "status": torch.full((1,), -1, dtype=torch.int32, device=dev),
     }
     y = torch.empty(K, H, dtype=torch.int16, device=dev)
     y32 = torch.empty(K, H, dtype=torch.float32, device=dev)
@@ -65,6 +66,7 @@ def run_layer(cfg, wd, x, residual=None, ws=None, grouped=False):
     fn(cfg, api.make_weights(wd), x, y, ws, y32=y32, residual=residual, debug=api.make_debug(**dbg_t))
     torch.cuda.synchronize()
     out = {kk: v.cpu().numpy() for kk, v in dbg_t.items()}
+    assert np.all(out["status"] == 0), "an in-kernel hand-off wait gave up"
     out["y"] = y.cpu().numpy().view(np.uint16)
     out["y32_out"] = y32.cpu().numpy()
     out["ids"] = out["ids"].reshape(K, k)
@@ -89,6 +91,7 @@ def run_stack_debug(cfg, layers_dev, x, n_layers, residual=None):
         "inv": torch.empty(L, n, dtype=torch.int32, device=dev),
         "x_in": torch.empty(L, K, H, dtype=torch.int16, device=dev),
         "y32": torch.empty(L, K, H, dtype=torch.float32, device=dev),
+        "status": torch.full((L,), -1, dtype=torch.int32, device=dev),
     }
     if residual is not None:
         dbg_t["res_in"] = torch.empty(L, K, H, dtype=torch.int16, device=dev)
@@ -99,6 +102,7 @@ def run_stack_debug(cfg, layers_dev, x, n_layers, residual=None):
                          debug=api.make_debug(**dbg_t), residual=residual)
     torch.cuda.synchronize()
     out = {kk: v.cpu().numpy() for kk, v in dbg_t.items()}
+    assert np.all(out["status"] == 0), "an in-kernel hand-off wait gave up: %s" % out["status"]
     out["y"] = y.cpu().numpy().view(np.uint16)
     out["y32_out"] = y32.cpu().numpy()
     return out

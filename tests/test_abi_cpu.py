@@ -36,12 +36,12 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_struct_layouts_match_header_sizes():
-    # pointer-only structs: 3 / 2 + 6*3 + 1 / 7 / 11 pointers; cfg: 11 x 4 bytes
+    # pointer-only structs: 3 / 2 + 6*3 + 1 / 7 / 12 pointers; cfg: 11 x 4 bytes
     P = ctypes.sizeof(ctypes.c_void_p)
     assert ctypes.sizeof(api.moe_nvfp4) == 3 * P
     assert ctypes.sizeof(api.moe_layer_weights) == 21 * P
     assert ctypes.sizeof(api.moe_route_out) == 7 * P
-    assert ctypes.sizeof(api.moe_debug) == 11 * P
+    assert ctypes.sizeof(api.moe_debug) == 12 * P
     assert ctypes.sizeof(api.moe_cfg) == 44
 
 

@@ -34,8 +34,10 @@ def test_gateup_bytes_decompose_the_step_bytes(U, K):
     cfg = api.make_cfg(shape, K)
     step = api.moe_verify_weight_bytes(cfg, U, K)  # router + routed + shared + activations
     gu = bench.gateup_bytes(shape, U, K)
-    # the gate/up launch: gate + up of each unique expert and the shared one, x in, h out
-    assert gu == U * 2 * bench.nvfp4_bytes(I, H) + 2 * bench.nvfp4_bytes(Is, H) + K * H * 2 + (K * k * I + K * Is) * 4
+    # the router + gate/up launch: the bf16 router, gate + up of each unique
+    # expert and the shared one, x in, h out
+    assert gu == 2 * shape.n_experts * H + U * 2 * bench.nvfp4_bytes(I, H) + 2 * bench.nvfp4_bytes(Is, H) \
+        + K * H * 2 + (K * k * I + K * Is) * 4
     # the step: those matrices, the down matrices, the bf16 router, x in and y out once each
     down = (U + 1) * bench.nvfp4_bytes(H, I)
     assert step == U * 2 * bench.nvfp4_bytes(I, H) + 2 * bench.nvfp4_bytes(Is, H) + down + 2 * shape.n_experts * H \
