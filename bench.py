@@ -495,6 +495,9 @@ def main():
                          "verify rows' lm_head + greedy acceptance")
     ap.add_argument("--prefill-layers", type=int, default=8, help="distinct weight sets the prefill mode rotates")
     ap.add_argument("--layer-reps", type=int, default=5, help="launches of each layer graph in the layer K sweep")
+    ap.add_argument("--one-launch", action="store_true",
+                    help="stack: run each layer of at most 2 rows as one launch (router, gate/up and down "
+                         "workgroups; slower than the default two launches on MI355X)")
     ap.add_argument("--mode", choices=("softmax", "laguna"), default="softmax",
                     help="stack workload router: softmax top-8 (the benchmark configuration) or the pages' Laguna "
                          "tail (sigmoid + selection bias, routed scale 2.5) with norm weights and the residual stream")
@@ -545,7 +548,8 @@ def main():
 
     score_fn = api.MOE_SCORE_SIGMOID_BIAS if laguna else api.MOE_SCORE_SOFTMAX
     rs = 2.5 if laguna else 1.0
-    cfg = api.make_cfg(shape, K, score_fn=score_fn, routed_scale=rs)
+    cfg = api.make_cfg(shape, K, score_fn=score_fn, routed_scale=rs,
+                       regime=api.MOE_REGIME_VERIFY_ONE_LAUNCH if args.one_launch else api.MOE_REGIME_AUTO)
     ws = api.alloc_workspace(cfg, dev)
     wts = [api.make_weights(w, cfg) for w in layers]
     y = torch.empty(K, shape.hidden, dtype=torch.int16, device=dev)
@@ -557,7 +561,7 @@ def main():
     nu = torch.empty(L, dtype=torch.int32, device=dev)
     y32_layers = torch.empty(L, K, shape.hidden, dtype=torch.float32, device=dev)
     lg_layers = torch.empty(L, K, shape.n_experts, dtype=torch.float32, device=dev)
-    step_bytes, gu_bytes, uniques, logits_all = [], [], [], []
+    step_bytes, gu_bytes, layer_bytes, uniques, logits_all = [], [], [], [], []
     gpu_layer0 = None
     for i in range(POOL):
         dbg = api.make_debug(n_unique=nu, logits=lg_layers, **({"y32": y32_layers} if i == 0 else {}))
@@ -568,7 +572,8 @@ def main():
         U = nu.cpu().tolist()
         uniques.append(U)
         logits_all.append(lg_layers.cpu().numpy())
-        step_bytes.append(sum(api.moe_verify_weight_bytes(cfg, u, K) for u in U))
+        layer_bytes.append([api.moe_verify_weight_bytes(cfg, u, K) for u in U])
+        step_bytes.append(sum(layer_bytes[-1]))
         gu_bytes.append([gateup_bytes(shape, u, K) for u in U])
     logits_all = np.stack(logits_all)                     # [POOL, L, K, E]
     u_by_layer = np.asarray(uniques, np.float64).mean(axis=0)
@@ -612,16 +617,20 @@ def main():
 
     # per-kernel timing pass: same inputs, kernels stamped by their own
     # dispatch (verify-width kernels; from 8 rows the stack runs the grouped
-    # kernels, which this pass does not cover)
+    # kernels, which this pass does not cover).  A layer of at most 2 rows is
+    # one launch (router, gate/up and down workgroups): its down entry is 0
+    # and its algorithmic bytes are the whole layer's.
     kt = {"route_gateup": [], "down": []}
-    gu_rates = []
+    gu_rates, one_launch = [], None
     avg, achieved, gu_avg_bytes = None, None, None
     try:
         for s in range(args.timing_steps):
             ms = api.moe_verify_stack_timed(cfg, wts, xs[s % POOL], y, ws, y32=y32, residual=residual)
+            if one_launch is None:
+                one_launch = all(b == 0.0 for _, b in ms)
             for l, (a, b) in enumerate(ms):
                 kt["route_gateup"].append(a); kt["down"].append(b)
-                gu_rates.append(gu_bytes[s % POOL][l])
+                gu_rates.append((layer_bytes if one_launch else gu_bytes)[s % POOL][l])
     except api.MoEError as err:
         if err.code != api.MOE_ERR_UNSUPPORTED:
             raise
@@ -630,8 +639,12 @@ def main():
         avg = {k: sum(v) / len(v) for k, v in kt.items()}
         gu_avg_bytes = sum(gu_rates) / len(gu_rates)
         achieved = gu_avg_bytes / (avg["route_gateup"] / 1e3) / 1e9
-        log("bench: kernel averages (us): router+gateup %.2f down %.2f; router+gateup %.1f GB/s" % (
-            avg["route_gateup"] * 1e3, avg["down"] * 1e3, achieved))
+        if one_launch:
+            avg = {"layer": avg["route_gateup"]}
+            log("bench: kernel average (us): one-launch layer %.2f; %.1f GB/s" % (avg["layer"] * 1e3, achieved))
+        else:
+            log("bench: kernel averages (us): router+gateup %.2f down %.2f; router+gateup %.1f GB/s" % (
+                avg["route_gateup"] * 1e3, avg["down"] * 1e3, achieved))
 
     for g in graphs:
         g.close()
@@ -683,7 +696,8 @@ def main():
         "single_layer_us": one_layer,
         "stream_read_ceiling_gbs": ceiling,
         "roofline": None if avg is None else {
-            "bound": "hbm", "kernel": "k_route_gateup", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "bound": "hbm", "kernel": "k_route_gateup" + (" (whole layer: router, gate/up, down)" if one_launch else ""),
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic() if K == 2 else None, "bytes_per_launch": round(gu_avg_bytes)},
         "wall_s": round(wall, 4),

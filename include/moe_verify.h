@@ -88,10 +88,14 @@ extern "C" {
  * AUTO runs the verify-width kernels below 8 rows and the grouped kernels
  * from 8 rows (when the shape meets the grouped limits; always above 16);
  * VERIFY forces the verify-width kernels (K <= 16, MOE_ERR_UNSUPPORTED
- * above); GROUPED forces the grouped kernels at any K (their limits apply). */
+ * above); GROUPED forces the grouped kernels at any K (their limits apply).
+ * VERIFY_ONE_LAUNCH is VERIFY with a layer of at most 2 rows run as one
+ * launch when its down tasks fit the launch (same results bit for bit; the
+ * two-launch layer is faster on MI355X, so AUTO and VERIFY use it). */
 #define MOE_REGIME_AUTO 0
 #define MOE_REGIME_VERIFY 1
 #define MOE_REGIME_GROUPED 2
+#define MOE_REGIME_VERIFY_ONE_LAUNCH 3
 
 typedef struct moe_nvfp4 {
     const uint8_t* q;
@@ -179,9 +183,12 @@ MOE_API size_t moe_verify_workspace_bytes(const moe_cfg* cfg);
  * (MOE_REGIME_*; AUTO: verify width below 8 rows, grouped from 8 rows when
  * the shape meets the grouped limits, grouped above 16 rows):
  *  - verify width (K <= 16): every unique expert is streamed once by
- *    skinny kernels (two launches per layer: router + selection + gate/up,
- *    whose gate/up workgroups wait for the router workgroups of the same
- *    launch through a bounded in-kernel hand-off, then down + combine);
+ *    skinny kernels: router + selection + gate/up in one launch, whose
+ *    gate/up workgroups wait for the router workgroups of the same launch
+ *    through a bounded in-kernel hand-off, then down + combine (with
+ *    MOE_REGIME_VERIFY_ONE_LAUNCH at K <= 2 the down workgroups are part of
+ *    the same launch, holding their down weights while gate/up runs and
+ *    waiting, bounded, for every gate/up workgroup's h);
  *  - grouped (prefill, e.g. the 512-row seed prefill of the mlxfast README,
  *    "Why this challenge exists", and wide verify blocks): the T*k slots are
  *    grouped by expert into tiles of up to 32 tokens and the expert GEMMs
@@ -207,8 +214,8 @@ MOE_API int moe_verify_layer_grouped(const moe_cfg* cfg, const moe_layer_weights
  * capture, tight serving loops, harnesses that forbid hipMalloc):
  * moe_verify_layer with the same arguments, outputs and errors, but no
  * workspace argument -- its scratch is a fixed device array inside the
- * library, moe_verify_noalloc_scratch_bytes() bytes (4 MiB: the full-size
- * layer up to 32 rows), one per GPU, held until the process ends.  A cfg
+ * library, moe_verify_noalloc_scratch_bytes() bytes (5 MiB: the full-size
+ * layer up to 40 rows), one per GPU, held until the process ends.  A cfg
  * whose workspace (moe_verify_workspace_bytes) exceeds it returns
  * MOE_ERR_UNSUPPORTED before any device work.  The call allocates nothing:
  * the array's device address is looked up once per device (with that
@@ -237,7 +244,8 @@ MOE_API int moe_verify_stack(const moe_cfg* cfg, const moe_layer_weights* layers
  * kernel launched so that a start/stop event pair carries that kernel's own
  * dispatch timestamps.  Synchronises `stream`, then writes the durations in
  * milliseconds to the HOST array kernel_ms[n_layers][2] (router + selection
- * + gate/up + SwiGLU, down + combine), and returns MOE_ERR_HIP if an
+ * + gate/up + SwiGLU, down + combine; a one-launch layer reports the whole
+ * launch first and 0 second), and returns MOE_ERR_HIP if an
  * in-kernel hand-off wait gave up.  Verify-width kernels only
  * (MOE_ERR_UNSUPPORTED when K and cfg->regime pick the grouped ones). */
 MOE_API int moe_verify_stack_timed(const moe_cfg* cfg, const moe_layer_weights* layers, int32_t n_layers,

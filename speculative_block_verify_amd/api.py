@@ -27,6 +27,7 @@ MOE_SCORE_SIGMOID_BIAS = 1
 MOE_REGIME_AUTO = 0
 MOE_REGIME_VERIFY = 1
 MOE_REGIME_GROUPED = 2
+MOE_REGIME_VERIFY_ONE_LAUNCH = 3
 
 _c_void_p = ctypes.c_void_p
 _i32 = ctypes.c_int32

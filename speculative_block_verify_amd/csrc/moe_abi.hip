@@ -72,18 +72,27 @@ bool grouped_shape_ok(const moe_cfg* c, int T) {
 // rows (2005 against 1664 us).
 constexpr int kAutoGroupedRows = 8;
 
-// Which kernels serve K rows under cfg: false = the three verify-width
-// launches (K <= 16), true = the grouped launches.
+// Which kernels serve K rows under cfg: false = the verify-width launches
+// (K <= 16), true = the grouped launches.
 bool use_grouped(const moe_cfg* c, int K) {
     if (K > moe::kMaxRows || c->regime == MOE_REGIME_GROUPED) return true;
-    if (c->regime == MOE_REGIME_VERIFY) return false;
+    if (c->regime == MOE_REGIME_VERIFY || c->regime == MOE_REGIME_VERIFY_ONE_LAUNCH) return false;
     return K >= kAutoGroupedRows && grouped_shape_ok(c, K);
+}
+
+// At verify width: whether a layer is one launch (router, gate/up and down
+// workgroups with in-kernel hand-offs) rather than router + gate/up, then
+// down.  Only on request: on MI355X the one-launch layer measured 931
+// against 925 us per 40-layer stack at K = 2 and 801 against 759 at K = 1.
+bool use_fused_down(const moe_cfg* c, int K) {
+    return c->regime == MOE_REGIME_VERIFY_ONE_LAUNCH &&
+           moe::fused_down_fits(K, c->top_k, c->n_experts, c->hidden, c->inter, c->shared_inter);
 }
 
 // The regime's own limits at K rows (after check_common).
 int check_regime(const moe_cfg* c, int K) {
-    if (c->regime == MOE_REGIME_VERIFY && K > moe::kMaxRows)
-        return fail(MOE_ERR_UNSUPPORTED, "MOE_REGIME_VERIFY serves at most %d rows (K=%d)", moe::kMaxRows, K);
+    if ((c->regime == MOE_REGIME_VERIFY || c->regime == MOE_REGIME_VERIFY_ONE_LAUNCH) && K > moe::kMaxRows)
+        return fail(MOE_ERR_UNSUPPORTED, "the verify-width regimes serve at most %d rows (K=%d)", moe::kMaxRows, K);
     return use_grouped(c, K) ? check_grouped(c, K) : MOE_OK;
 }
 
@@ -108,7 +117,8 @@ int check_cfg(const moe_cfg* c) {
     if (!std::isfinite(c->routed_scale)) return fail(MOE_ERR_INVALID, "routed_scale not finite");
     if (!(c->rms_eps >= 0.0f) || !std::isfinite(c->rms_eps)) return fail(MOE_ERR_INVALID, "rms_eps invalid");
     if (c->max_rows < 1) return fail(MOE_ERR_INVALID, "max_rows=%d < 1", c->max_rows);
-    if (c->regime != MOE_REGIME_AUTO && c->regime != MOE_REGIME_VERIFY && c->regime != MOE_REGIME_GROUPED)
+    if (c->regime != MOE_REGIME_AUTO && c->regime != MOE_REGIME_VERIFY && c->regime != MOE_REGIME_GROUPED &&
+        c->regime != MOE_REGIME_VERIFY_ONE_LAUNCH)
         return fail(MOE_ERR_INVALID, "regime=%d not a MOE_REGIME_*", c->regime);
     if (c->max_rows > moe::kMaxGroupedRows)
         return fail(MOE_ERR_UNSUPPORTED, "max_rows=%d > %d", c->max_rows, moe::kMaxGroupedRows);
@@ -158,7 +168,7 @@ int check_weights(const moe_cfg* c, const moe_layer_weights* w, int layer) {
 
 struct Layout {
     int32_t* meta;
-    uint32_t* handoff;      // the router/gate-up hand-off counter, then its flags, 2 KB apart
+    uint32_t* handoff;      // two sets of hand-off words (moe::kHandoffSetWords each)
     float* logits;
     int32_t* ids;
     float* w;
@@ -193,7 +203,7 @@ Layout layout(const moe_cfg* c, void* base) {
     auto take = [&](size_t bytes) { char* r = p ? p + o : nullptr; o += align256(bytes); return r; };
     L.meta = reinterpret_cast<int32_t*>(take(16 * 4));
     L.logits = reinterpret_cast<float*>(take(R * E * 4));
-    L.handoff = reinterpret_cast<uint32_t*>(take((size_t)moe::kHandoffFlagStride * 4 * (1 + moe::kHandoffFlags)));
+    L.handoff = reinterpret_cast<uint32_t*>(take((size_t)2 * moe::kHandoffSetWords * 4));
     L.ids = reinterpret_cast<int32_t*>(take(R * k * 4));
     L.w = reinterpret_cast<float*>(take(R * k * 4));
     L.uniq = reinterpret_cast<int32_t*>(take(R * k * 4));
@@ -220,9 +230,10 @@ Layout layout(const moe_cfg* c, void* base) {
 
 moe::Fp4Mat mat(const moe_nvfp4& m) { return moe::Fp4Mat{m.q, m.s, m.ts}; }
 
-// Every call starts the router/gate-up hand-off counter and the status word
-// at zero (the workspace may hold anything); within a call each down kernel
-// resets the counter for the next layer.
+// Every call starts both hand-off sets and the status word at zero (the
+// workspace may hold anything).  Within a call, layer l uses set l % 2: a
+// separate down kernel clears the router words of set 0 for the next layer,
+// a one-launch layer clears the other set for the next layer.
 int start_call(const Layout& L, hipStream_t st) {
     hipError_t e = moe::launch_handoff_reset(L.handoff, L.meta + moe::kMetaStatus, st);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "reset launch");
@@ -243,12 +254,15 @@ struct LayerIO {
 
 // next_router: the router rows of the layer that follows in a stack (the down
 // kernel requests them ahead of that layer's router launch), or nullptr.
+// layer: the layer's index in the call (its parity picks the hand-off set).
 int enqueue_layer(const moe_cfg* c, const moe_layer_weights* w, const LayerIO& io, int K, const Layout& L,
-                  hipStream_t st, const moe::Timing* tm = nullptr, const uint16_t* next_router = nullptr) {
+                  hipStream_t st, const moe::Timing* tm = nullptr, const uint16_t* next_router = nullptr,
+                  int layer = 0) {
     hipError_t e;
     const bool has_sh = c->shared_inter > 0;
+    const bool fused = use_fused_down(c, K);
     const moe::Fp4Mat none{nullptr, nullptr, nullptr};
-    uint32_t* counter = L.handoff;
+    uint32_t* counter = fused ? L.handoff + (size_t)(layer & 1) * moe::kHandoffSetWords : L.handoff;
     int32_t* status = L.meta + moe::kMetaStatus;
 
     moe::RouteGateUpArgs ra{};
@@ -280,10 +294,8 @@ int enqueue_layer(const moe_cfg* c, const moe_layer_weights* w, const LayerIO& i
     ra.status = status;
     ra.n_router = (c->n_experts + moe::kWaves - 1) / moe::kWaves;
     ra.spin_limit = moe::kRouteSpinLimit;
-    if ((e = moe::launch_route_gateup(ra, st, tm ? &tm[0] : nullptr)) != hipSuccess)
-        return hip_fail(e, "router + gate/up launch");
 
-    moe::DownArgs da{};
+    moe::DownArgs& da = ra.d;
     da.down = mat(w->down);
     da.sdown = has_sh ? mat(w->sh_down) : none;
     da.n_unique = L.meta + moe::kMetaUnique;
@@ -296,6 +308,16 @@ int enqueue_layer(const moe_cfg* c, const moe_layer_weights* w, const LayerIO& i
     da.rs = c->routed_scale;
     da.prefetch = reinterpret_cast<const uint8_t*>(next_router);
     da.prefetch_bytes = next_router ? 2 * c->n_experts * c->hidden : 0;
+    if (fused) {
+        // one launch: the down workgroups follow the gate/up ones
+        ra.n_down = c->hidden / moe::kDownRowsPerBlock;
+        ra.clear = L.handoff + (size_t)((layer + 1) & 1) * moe::kHandoffSetWords;
+        if ((e = moe::launch_route_gateup(ra, st, tm ? &tm[0] : nullptr)) != hipSuccess)
+            return hip_fail(e, "layer launch");
+        return MOE_OK;
+    }
+    if ((e = moe::launch_route_gateup(ra, st, tm ? &tm[0] : nullptr)) != hipSuccess)
+        return hip_fail(e, "router + gate/up launch");
     da.counter = counter;
     if ((e = moe::launch_down(da, st, tm ? &tm[1] : nullptr)) != hipSuccess) return hip_fail(e, "down launch");
     return MOE_OK;
@@ -468,7 +490,7 @@ int enqueue_stack(const moe_cfg* c, const moe_layer_weights* layers, int n_layer
         int rc = copy_debug_residual(c, dbg, l, K, io.residual, st);
         if (rc) return rc;
         rc = enqueue_layer(c, &layers[l], io, K, L, st, tm ? tm + 2 * l : nullptr,
-                           last ? nullptr : layers[l + 1].router_w);
+                           last ? nullptr : layers[l + 1].router_w, l);
         if (rc) return rc;
         rc = copy_debug(c, dbg, l, K, L, l == 0 ? x : L.xbuf, io.y32, st);
         if (rc) return rc;
@@ -483,7 +505,7 @@ int enqueue_stack(const moe_cfg* c, const moe_layer_weights* layers, int n_layer
 // from hipGetSymbolAddress with that GPU current, kept per device.
 // ---------------------------------------------------------------------------
 
-constexpr size_t kScratchBytes = size_t(4) << 20;
+constexpr size_t kScratchBytes = size_t(5) << 20;
 constexpr int kMaxDevices = 64;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
@@ -739,9 +761,12 @@ int moe_verify_stack_timed(const moe_cfg* cfg, const moe_layer_weights* layers, 
     if (e == hipSuccess) {
         rc = enqueue_stack(cfg, layers, n_layers, x, residual, K, y, y32, workspace, st, nullptr, tm);
         if (!rc && (e = hipStreamSynchronize(st)) != hipSuccess) rc = hip_fail(e, "synchronize");
+        const bool fused = use_fused_down(cfg, K);
         for (int i = 0; !rc && i < n_ev; ++i) {
             float ms = 0.0f;
-            if ((e = hipEventElapsedTime(&ms, tm[i].start, tm[i].stop)) != hipSuccess) rc = hip_fail(e, "elapsed time");
+            // a one-launch layer has no separate down kernel: its entry is 0
+            if (!(fused && (i & 1)) && (e = hipEventElapsedTime(&ms, tm[i].start, tm[i].stop)) != hipSuccess)
+                rc = hip_fail(e, "elapsed time");
             kernel_ms[i] = ms;
         }
         if (!rc) {

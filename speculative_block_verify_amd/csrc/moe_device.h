@@ -212,7 +212,8 @@ __device__ __forceinline__ uint32_t select_key(const SelectArgs& a, float l, int
 // wins, which (contiguous ownership, stable in-lane order) is the lowest
 // expert index.  lr: the row's logits in LDS.
 template <int P>
-__device__ void wave_topk(const SelectArgs& a, const float* lr, int r, SelectSmem& sm, bool weights = true) {
+__device__ __forceinline__ void wave_topk(const SelectArgs& a, const float* lr, int r, SelectSmem& sm,
+                                          bool weights = true) {
     const int lane = threadIdx.x & 63;
     const int E = a.E, k = a.k;
     uint32_t sk[P];

@@ -76,16 +76,6 @@ struct GateUpArgs {
     int K, H, I, Is;
 };
 
-// Router + gate/up in one launch (k_route_gateup).
-struct RouteGateUpArgs {
-    RouterArgs r;           // router rows, x_in or y_prev/ssq/gamma, logits (written), x_out
-    GateUpArgs g;           // selection + gate/up; g.x is not read (x is formed from r)
-    uint32_t* counter;      // hand-off counter, zero at launch; flag f at counter[kHandoffFlagStride * (1 + f)]
-    int32_t* status;        // set to 1 when a bounded wait gives up
-    int n_router;           // router workgroups (E / 4, rounded up)
-    int spin_limit;         // polls of a bounded wait
-};
-
 struct DownArgs {
     Fp4Mat down;            // [E][H][I/2]
     Fp4Mat sdown;           // [1][H][Is/2]
@@ -106,6 +96,35 @@ struct DownArgs {
     uint32_t* counter;         // the router/gate-up hand-off counter to reset, or nullptr
     int K, H, I, Is, k;
     float rs;
+};
+
+// Hand-off words of one layer launch, each kHandoffFlagStride words apart
+// (slot i at counter[kHandoffFlagStride * i]): the router arrival counter,
+// the flags it raises, the gate/up completion counters, their second-level
+// counter and the flags that releases.
+constexpr int kHandoffFlags = 32;          // flags per fan-out
+constexpr int kHandoffFlagStride = 512;    // words between two hand-off slots (2 KB)
+constexpr int kSlotRouterCount = 0;
+constexpr int kSlotRouterFlag = 1;                                   // + f, f < kHandoffFlags
+constexpr int kSlotDoneCount = kSlotRouterFlag + kHandoffFlags;      // + c, c < kHandoffFlags
+constexpr int kSlotDoneLevel2 = kSlotDoneCount + kHandoffFlags;
+constexpr int kSlotDownFlag = kSlotDoneLevel2 + 1;                   // + f, f < kHandoffFlags
+constexpr int kHandoffSlots = kSlotDownFlag + kHandoffFlags;
+constexpr int kHandoffSetWords = kHandoffSlots * kHandoffFlagStride;  // one set; the workspace holds two
+constexpr int kFusedDownTasks = 9;         // down tasks per wave whose weights one down workgroup holds
+
+// Router + gate/up in one launch (k_route_gateup), optionally with the down
+// projection and combine as a third group of workgroups (n_down > 0).
+struct RouteGateUpArgs {
+    RouterArgs r;           // router rows, x_in or y_prev/ssq/gamma, logits (written), x_out
+    GateUpArgs g;           // selection + gate/up; g.x is not read (x is formed from r)
+    DownArgs d;             // with n_down > 0: down + combine (its routing metadata and counter are not read)
+    uint32_t* counter;      // this launch's hand-off set, zero at launch
+    uint32_t* clear;        // a set to zero for the next launch (n_down > 0), or nullptr
+    int32_t* status;        // set to 1 when a bounded wait gives up
+    int n_router;           // router workgroups (E / 4, rounded up)
+    int n_down;             // down workgroups (H / kDownRowsPerBlock), or 0
+    int spin_limit;         // polls of a bounded wait
 };
 
 // --- grouped (prefill) regime ----------------------------------------------
@@ -179,9 +198,8 @@ struct Timing {
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);  // logits given
 hipError_t launch_down(const DownArgs& a, hipStream_t st, const Timing* t = nullptr);
 hipError_t launch_route_gateup(const RouteGateUpArgs& a, hipStream_t st, const Timing* t = nullptr);
-hipError_t launch_handoff_reset(uint32_t* counter, int32_t* status, hipStream_t st);
-constexpr int kHandoffFlags = 32;          // flags the last router workgroup raises
-constexpr int kHandoffFlagStride = 512;    // words between the counter and each flag (2 KB)
+hipError_t launch_handoff_reset(uint32_t* sets, int32_t* status, hipStream_t st);  // both sets
+bool fused_down_fits(int K, int k, int E, int H, int I, int Is);  // the down role in the router + gate/up launch
 constexpr int kMetaStatus = 3;             // workspace word: nonzero after a bounded wait gave up
 constexpr int kRouteSpinLimit = 1 << 22;   // polls (with a short sleep each) before a wait gives up
 hipError_t launch_dequant(Fp4Mat m, int n_experts, int rows, int cols, float* out, hipStream_t st);

@@ -25,6 +25,10 @@
 // agent-scope release writes back the L2 and costs far more than a launch
 // boundary inside a graph; the in-launch hand-off uses agent-scope relaxed
 // stores completed with a wait on the memory counters instead.
+// On request (at most 2 rows) k_route_gateup also carries the down
+// projection as a third group of workgroups (down_role), making the layer
+// one launch; it computes the same bits but measured slower than the two
+// launches, so it is not the default.
 
 #include <hip/hip_ext.h>
 
@@ -41,7 +45,7 @@ namespace moe {
 // Exclusive prefix sums over experts of count(e) and of (count(e) > 0) give
 // the CSR offset and the position in the ascending unique list.
 // Results go to sm.asg / sm.inv / sm.uniq / sm.off / sm.n_unique.
-__device__ void dedup_block(SelectSmem& sm, uint32_t* rowmask, int32_t* cstart, int n, int k, int E) {
+__device__ __forceinline__ void dedup_block(SelectSmem& sm, uint32_t* rowmask, int32_t* cstart, int n, int k, int E) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ int s_wsum[kWaves][2];
     for (int e = tid; e < E; e += kBlock) rowmask[e] = 0u;
@@ -99,14 +103,14 @@ __device__ void select_rows(const SelectArgs& a, SelectSmem& sm, const float* lg
     for (int r = wave; r < a.K; r += kWaves) wave_topk_rt(a, lg + r * a.E, r, sm);
 }
 template <int P>
-__device__ void select_rows_p(const SelectArgs& a, SelectSmem& sm, const float* lg, bool weights) {
+__device__ __forceinline__ void select_rows_p(const SelectArgs& a, SelectSmem& sm, const float* lg, bool weights) {
     const int wave = threadIdx.x >> 6;
     for (int r = wave; r < a.K; r += kWaves) wave_topk<P>(a, lg + r * a.E, r, sm, weights);
 }
 
 // The canonical dedup CSR of the selection in sm (whole workgroup), written
 // with ids and w to the SelectArgs outputs.  Returns the unique count.
-__device__ int dedup_publish(const SelectArgs& a, SelectSmem& sm) {
+__device__ __forceinline__ int dedup_publish(const SelectArgs& a, SelectSmem& sm) {
     const int tid = threadIdx.x;
     const int k = a.k, n = a.K * k;
     dedup_block(sm, sm.rowmask, sm.cstart, n, k, a.E);
@@ -250,7 +254,13 @@ __device__ __forceinline__ void gu_compute(const GuRegs& R, float gts, float uts
         gv = ldexpf(g[2], sg) * gts; uv = ldexpf(u[2], sg) * uts; h.z = gv / (1.0f + expf(-gv)) * uv;
         gv = ldexpf(g[3], sg) * gts; uv = ldexpf(u[3], sg) * uts; h.w = gv / (1.0f + expf(-gv)) * uv;
         const int hr = hrows ? hrows[j] : j;
-        *reinterpret_cast<float4*>(hbase + (size_t)hr * hstride + n0 + 4 * kb) = h;
+        // written through to the device-coherent level: a down workgroup of
+        // the same launch may read it (after the completion hand-off)
+        uint64_t* dst = reinterpret_cast<uint64_t*>(hbase + (size_t)hr * hstride + n0 + 4 * kb);
+        __hip_atomic_store(dst, (uint64_t)__float_as_uint(h.x) | ((uint64_t)__float_as_uint(h.y) << 32),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst + 1, (uint64_t)__float_as_uint(h.z) | ((uint64_t)__float_as_uint(h.w) << 32),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -301,7 +311,7 @@ constexpr int kRouterPieces = 4;  // 16-byte router pieces per lane (hidden <= 2
 // of the matrix-core x operand (padded = true, xh_index).  With publish_n >
 // 0 the workgroup also writes its share publish_idx of x to x_out.  Every
 // caller runs the same arithmetic, so every workgroup holds the same bits.
-__device__ void stage_x(const RouterArgs& a, const uint16_t* x_in, int K, uint16_t* xs, float* s_inv,
+__device__ __forceinline__ void stage_x(const RouterArgs& a, const uint16_t* x_in, int K, uint16_t* xs, float* s_inv,
                         int publish_idx, int publish_n, bool padded = false) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int H = a.H, KH = K * H, lgH = __builtin_ctz(H);  // H is a power of two
@@ -390,6 +400,259 @@ __host__ __device__ constexpr size_t gateup_smem_bytes(int K, int E, int H) {
 }
 
 // ---------------------------------------------------------------------------
+// The down role of the fused layer launch (k_route_gateup with DOWN): one
+// workgroup per kDownRowsPerBlock output rows, as k_down, but resident while
+// gate/up runs.  It repeats the selection and dedup (from the hand-off
+// logits, like a routed workgroup), requests the down weights of all its
+// tasks into registers, waits for the gate/up completion flag, stages h
+// (written through by the gate/up workgroups, read with device-coherent
+// loads) in LDS and finishes as k_down: per-slot partial rows, the
+// rank-order combine, y, y32 and the next layer's sum-of-squares partials.
+// h is staged unpadded; float4 column c4 of a row sits at c4 ^ ((c4 >> 3) & 7)
+// so the 16 chunk lanes of a weight row read distinct banks.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int h_swz(int c4) { return c4 ^ ((c4 >> 3) & 7); }
+
+// Cache-policy bits of a load that reads the device-coherent level (what
+// agent-scope atomic loads use on this part: sc1).
+constexpr int kCachePolicyAgent = 16;
+
+constexpr int kFusedMaxP = 4;  // experts per top-k lane (E <= 256) of the one-launch layer
+constexpr int kFusedDownIlp = 1;  // down tasks of a wave computed interleaved (3: 133 registers)
+
+// The down role's dynamic LDS: h rows (max(I, Is) floats each) and per-slot
+// partial rows from offset 0 (over the selection's tables once they are
+// done), then the routing lists copied out of those tables, and y.
+__host__ __device__ constexpr size_t fused_down_lists_offset(int K, int k, int E, int I, int Is) {
+    return ((size_t)(K * k + K) * (size_t)((I > Is ? I : Is) + kDownRowsPerBlock) * 4 > select_smem_bytes(K, E)
+                ? (size_t)(K * k + K) * (size_t)((I > Is ? I : Is) + kDownRowsPerBlock) * 4
+                : select_smem_bytes(K, E)) /
+               16 * 16 + 16;
+}
+__host__ __device__ constexpr size_t fused_down_lds_bytes(int K, int k, int E, int I, int Is) {
+    return fused_down_lists_offset(K, k, E, I, Is) + (size_t)(4 * K * k + 2) * 4 + (size_t)K * kDownRowsPerBlock * 4;
+}
+
+// Bounded wait of thread 0 for a hand-off flag; status := 1 if it gives up.
+__device__ __forceinline__ void wait_flag(const uint32_t* flag, int32_t* status, int spin_limit) {
+    if (threadIdx.x == 0) {
+        int spins = 0;
+        while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+            if (++spins > spin_limit) {
+                __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    __syncthreads();
+}
+
+// The K*E router logits of this launch into LDS with device-coherent loads.
+__device__ __forceinline__ void load_handoff_logits(float* lg, const float* logits, int n) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(logits);
+    const int tid = threadIdx.x;
+    constexpr int U = 4;
+    for (int base = 0; base < n; base += U * kBlock) {
+        uint32_t v[U];
+#pragma unroll
+        for (int q = 0; q < U; ++q) {
+            const int i = base + q * kBlock + tid;
+            v[q] = i < n ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+        }
+#pragma unroll
+        for (int q = 0; q < U; ++q) {
+            const int i = base + q * kBlock + tid;
+            if (i < n) lg[i] = __uint_as_float(v[q]);
+        }
+    }
+}
+
+template <int P>
+__device__ __forceinline__ void down_role(const RouteGateUpArgs& a, unsigned char* smem, int db) {
+    constexpr int NH = kDownRowsPerBlock;
+    constexpr int NB = kFusedDownTasks;
+    const DownArgs& d = a.d;
+    const SelectArgs& sel = a.g.sel;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = d.H, K = d.K, k = d.k, n = K * k, E = sel.E, I = d.I, Is = d.Is;
+    const bool has_sh = d.sdown.q != nullptr;
+    const int n_base = db * NH;
+    const int RL = max(I, has_sh ? Is : 0);
+    const int total_rows = n + (has_sh ? K : 0);
+    // dynamic LDS: h rows, then per-slot partial rows, routing lists, y
+    float* hs = reinterpret_cast<float*>(smem);
+    float* so = hs + (size_t)total_rows * RL;
+    int* d_pe = reinterpret_cast<int*>(smem + fused_down_lists_offset(K, k, E, I, Is));  // expert of each h row
+    int* d_inv = d_pe + n;
+    float* d_w = reinterpret_cast<float*>(d_inv + n);
+    float* s_y = d_w + n;
+    SelectSmem& sm = *reinterpret_cast<SelectSmem*>(smem);
+    float* lg = reinterpret_cast<float*>(smem + (sizeof(SelectSmem) + 15) / 16 * 16);
+
+    // the next layer's router rows, requested into the memory-side cache
+    uint4 pf = make_uint4(0, 0, 0, 0);
+    if (d.prefetch) {
+        const int n16 = d.prefetch_bytes >> 4;
+        const int i = min(db * kBlock + tid, n16 - 1);
+        pf = reinterpret_cast<const uint4*>(d.prefetch)[i];
+    }
+
+    // ---- selection and dedup from the router's logits
+    wait_flag(a.counter + kHandoffFlagStride * (kSlotRouterFlag + blockIdx.x % kHandoffFlags), a.status,
+              a.spin_limit);
+    load_handoff_logits(lg, sel.logits, K * E);
+    asm volatile("" ::"v"(pf.x), "v"(pf.y), "v"(pf.z), "v"(pf.w));  // the prefetch stays issued
+    __syncthreads();
+    select_rows_p<P>(sel, sm, lg, true);
+    __syncthreads();
+    dedup_block(sm, sm.rowmask, sm.cstart, n, k, E);
+    __syncthreads();
+    for (int i = tid; i < n; i += kBlock) {
+        d_pe[i] = sm.sel[sm.asg[i]];
+        d_inv[i] = sm.inv[i];
+        d_w[i] = sm.w[i];
+    }
+    __syncthreads();
+
+    // ---- the down weights of this wave's tasks, requested before the wait.
+    // A task is one h row p (routed rows in dedup order, then the shared
+    // rows) and 64 / CPR of this workgroup's output rows (gI tasks per h
+    // row); task t belongs to wave t % kWaves.  A routed expert picked by
+    // both rows has two tasks per row group that read the same weights (the
+    // second read hits the cache).  Routed and shared rows have the same
+    // length here (I == Is), so every task has the same lane map.
+    const int CPR = I >> 5, lgI = __builtin_ctz(CPR);
+    const int gI = max(1, NH / (64 / CPR)), lgG = __builtin_ctz(gI);
+    const int nT = total_rows * gI;
+    const int q = lane >> lgI, chunk = lane & (CPR - 1);
+    uint4 code[NB];
+    uint32_t scl[NB];
+    float tsv[NB];
+    int pt[NB];  // the task's h row (wave-uniform)
+    {
+        int ev[NB];  // the task's expert (wave-uniform: tensor scales become scalar loads)
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int t = min(i * kWaves + wave, nT - 1);
+            pt[i] = t >> lgG;
+            ev[i] = __builtin_amdgcn_readfirstlane(pt[i] < n ? d_pe[pt[i]] : 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            // unconditional loads (a task past the end repeats the last
+            // task's addresses; its result is not stored)
+            const int t = min(i * kWaves + wave, nT - 1);
+            const bool shared_task = pt[i] >= n;
+            const int e = ev[i];
+            const uint8_t* mq = shared_task ? d.sdown.q : d.down.q;
+            const uint8_t* ms = shared_task ? d.sdown.s : d.down.s;
+            const float* mts = shared_task ? d.sdown.ts : d.down.ts;
+            const int nl = ((t & (gI - 1)) << (6 - lgI)) + q;
+            const size_t row = (size_t)e * H + n_base + (nl < NH ? nl : 0);
+            tsv[i] = mts[e];
+            code[i] = *reinterpret_cast<const uint4*>(mq + row * (I / 2) + chunk * 16);
+            scl[i] = *reinterpret_cast<const uint16_t*>(ms + row * (I / 16) + chunk * 2);
+        }
+    }
+
+    // ---- every gate/up workgroup has written h
+    wait_flag(a.counter + kHandoffFlagStride * (kSlotDownFlag + blockIdx.x % kHandoffFlags), a.status,
+              a.spin_limit);
+    {
+        // h rows (routed rows by dedup position, then the shared rows) into
+        // LDS straight from the device-coherent level (global_load_lds with
+        // the agent-scope cache bit): one wave instruction fills 64
+        // consecutive float4 slots, slot j of row `row` taking column float4
+        // h_swz(j) (the swizzle is its own inverse); no registers hold h.
+        const int q4 = RL >> 2, lq4 = __builtin_ctz(q4);
+        const int slots = total_rows * q4;
+        for (int m = wave; m * 64 < slots; m += kWaves) {
+            const int j = m * 64 + lane;
+            if (j < slots) {
+                const int row = j >> lq4, c4 = h_swz(j & (q4 - 1));
+                const bool shared_row = row >= n;
+                const int len4 = (shared_row ? Is : I) >> 2;
+                const float* src = shared_row ? d.h_sh + (size_t)(row - n) * Is : d.h + (size_t)row * I;
+                __builtin_amdgcn_global_load_lds(
+                    (__attribute__((address_space(1))) void*)(src + 4 * min(c4, len4 - 1)),
+                    (__attribute__((address_space(3))) void*)(hs + (size_t)m * 256), 16, 0, kCachePolicyAgent);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();
+
+    // ---- tasks: the partial rows of this workgroup's output rows for every
+    // h row, each (task) in k_down's arithmetic and order, kFusedDownIlp
+    // tasks interleaved column block by column block (independent chains,
+    // so a wave's LDS reads and FMAs overlap)
+    {
+        const int sw = chunk & 7;
+        static_assert(NB % kFusedDownIlp == 0, "task groups");
+#pragma unroll
+        for (int i0 = 0; i0 < NB; i0 += kFusedDownIlp) {
+            float acc[kFusedDownIlp][4];
+#pragma unroll
+            for (int i = 0; i < kFusedDownIlp; ++i) acc[i][0] = acc[i][1] = acc[i][2] = acc[i][3] = 0.0f;
+#pragma unroll
+            for (int t4 = 0; t4 < 8; ++t4) {
+#pragma unroll
+                for (int i = 0; i < kFusedDownIlp; ++i) {
+                    const uint4& cd = code[i0 + i];
+                    const uint32_t wd = t4 < 2 ? cd.x : t4 < 4 ? cd.y : t4 < 6 ? cd.z : cd.w;
+                    f32x2_t wa, wb;  // the word's low or high four columns
+                    if (t4 & 1) {
+                        wa = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, 1.0f, 2);
+                        wb = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, 1.0f, 3);
+                    } else {
+                        wa = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, 1.0f, 0);
+                        wb = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, 1.0f, 1);
+                    }
+                    const float4 hv =
+                        reinterpret_cast<const float4*>(hs + (size_t)pt[i0 + i] * RL + chunk * 32)[t4 ^ sw];
+                    float& c = acc[i][t4 >> 1];
+                    c = fmaf(wa.x, hv.x, c);
+                    c = fmaf(wa.y, hv.y, c);
+                    c = fmaf(wb.x, hv.z, c);
+                    c = fmaf(wb.y, hv.w, c);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kFusedDownIlp; ++i) {
+                const int t = (i0 + i) * kWaves + wave;
+                const float s0 = e4m3_to_f32<0>(scl[i0 + i]), s1 = e4m3_to_f32<1>(scl[i0 + i]);
+                float pv = fmaf(acc[i][2] + acc[i][3], s1, (acc[i][0] + acc[i][1]) * s0);
+                pv = (CPR == 16) ? group_sum<16>(pv) : group_sum_rt(pv, CPR);
+                const int nl = ((t & (gI - 1)) << (6 - lgI)) + q;
+                if (t < nT && nl < NH && chunk == CPR - 1) so[pt[i0 + i] * NH + nl] = pv * tsv[i0 + i];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- combine: y = rs * sum_j w_j o_j (rank order) + shared (+ residual)
+    for (int i = tid; i < K * NH; i += kBlock) {
+        const int r = i / NH, nl = i % NH, nn = n_base + nl;
+        float acc = 0.0f;
+        for (int j = 0; j < k; ++j) acc = fmaf(d_w[r * k + j], so[d_inv[r * k + j] * NH + nl], acc);
+        float y = d.rs * acc;
+        if (has_sh) y += so[(n + r) * NH + nl];
+        if (d.residual) y += bf16_to_f32(d.residual[(size_t)r * H + nn]);
+        d.y32[(size_t)r * H + nn] = y;
+        if (d.y) d.y[(size_t)r * H + nn] = f32_to_bf16_rne(y);
+        s_y[i] = y;
+    }
+    __syncthreads();
+    if (d.ssq && tid < K) {
+        float ss = 0.0f;
+        for (int nl = 0; nl < NH; ++nl) ss = fmaf(s_y[tid * NH + nl], s_y[tid * NH + nl], ss);
+        d.ssq[tid * a.n_down + db] = ss;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // k_route_gateup: the router and the gate/up of one layer in one launch.
 //   workgroups [0, n_router): the router GEMV (one wave per expert row);
 //     each publishes its logits with agent-scope write-through
@@ -422,7 +685,7 @@ __host__ __device__ constexpr size_t gateup_smem_bytes(int K, int E, int H) {
 // scales, selection scratch) stay within 8 KB of the 160 KB
 constexpr int kRgMaxDynLds = 160 * 1024 - 8 * 1024;
 
-template <int P, int MAXM>
+template <int P, int MAXM, bool DOWN>
 __global__ __launch_bounds__(kBlock) void k_route_gateup(RouteGateUpArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_xrows[kWaves][kMaxRows];
@@ -435,6 +698,8 @@ __global__ __launch_bounds__(kBlock) void k_route_gateup(RouteGateUpArgs a) {
 
     if (bid < a.n_router) {
         // ---- router workgroup: this wave's router row, requested first
+        if (DOWN && bid == 0 && a.clear && tid < kHandoffSlots)  // the next launch's hand-off set
+            __hip_atomic_store(a.clear + kHandoffFlagStride * tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
         const int e = bid * kWaves + wave;
         uint4 wv[kRouterPieces];
@@ -483,10 +748,12 @@ __global__ __launch_bounds__(kBlock) void k_route_gateup(RouteGateUpArgs a) {
         // 2 KB, so the waiting workgroups poll many addresses, not one)
         if (wave == 0) {
             uint32_t old = 0u;
-            if (lane == 0) old = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0)
+                old = __hip_atomic_fetch_add(a.counter + kHandoffFlagStride * kSlotRouterCount, 1u, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
             old = (uint32_t)__builtin_amdgcn_readfirstlane((int)old);
             if (old == (uint32_t)(a.n_router - 1) && lane < kHandoffFlags)
-                __hip_atomic_store(a.counter + kHandoffFlagStride * (1 + lane), 1u, __ATOMIC_RELAXED,
+                __hip_atomic_store(a.counter + kHandoffFlagStride * (kSlotRouterFlag + lane), 1u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
         return;
@@ -498,9 +765,13 @@ __global__ __launch_bounds__(kBlock) void k_route_gateup(RouteGateUpArgs a) {
     _Float16* xh = reinterpret_cast<_Float16*>(smem + select_smem_bytes(K, E));
     float* red = reinterpret_cast<float*>(smem + select_smem_bytes(K, E) + (size_t)K * xh_row_stride(H) * 2);
     const int n_sh = g.sgate.q ? g.Is / kTileRows : 0;
+    const int n_rb = gridDim.x - a.n_router - n_sh - (DOWN ? a.n_down : 0), rb = bid - a.n_router - n_sh;
+    if (DOWN && rb >= n_rb) {
+        down_role<P>(a, smem, rb - n_rb);
+        return;
+    }
     const bool shared_blk = bid < a.n_router + n_sh;
     const int sh_tile = bid - a.n_router;
-    const int n_rb = gridDim.x - a.n_router - n_sh, rb = bid - a.n_router - n_sh;
     const int nsr = I / kTileRows;
     GuRegs R;
     float gts = 0.0f, uts = 0.0f;
@@ -514,35 +785,8 @@ __global__ __launch_bounds__(kBlock) void k_route_gateup(RouteGateUpArgs a) {
         __syncthreads();
     } else {
         stage_x(a.r, a.r.x_in, K, reinterpret_cast<uint16_t*>(xh), s_inv, 0, 0, true);
-        if (tid == 0) {
-            const uint32_t* flag = a.counter + kHandoffFlagStride * (1 + bid % kHandoffFlags);
-            int spins = 0;
-            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-                if (++spins > a.spin_limit) {
-                    __hip_atomic_store(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
-            }
-        }
-        __syncthreads();
-        {
-            const uint32_t* src = reinterpret_cast<const uint32_t*>(g.sel.logits);
-            constexpr int U = 4;
-            for (int base = 0; base < K * E; base += U * kBlock) {
-                uint32_t v[U];
-#pragma unroll
-                for (int q = 0; q < U; ++q) {
-                    const int i = base + q * kBlock + tid;
-                    v[q] = i < K * E ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-                }
-#pragma unroll
-                for (int q = 0; q < U; ++q) {
-                    const int i = base + q * kBlock + tid;
-                    if (i < K * E) lg[i] = __uint_as_float(v[q]);
-                }
-            }
-        }
+        wait_flag(a.counter + kHandoffFlagStride * (kSlotRouterFlag + bid % kHandoffFlags), a.status, a.spin_limit);
+        load_handoff_logits(lg, g.sel.logits, K * E);
         __syncthreads();
         select_rows_p<P>(g.sel, sm, lg, rb == 0);  // weights: only the workgroup that publishes them
         if (K < kWaves) convert_rows(xh, K, H, s_xsig, K, kWaves - K);
@@ -601,19 +845,49 @@ __global__ __launch_bounds__(kBlock) void k_route_gateup(RouteGateUpArgs a) {
         __syncthreads();
     }
     if (!published) dedup_publish(g.sel, sm);
+    if (DOWN) {
+        // Completion: gate/up workgroup i adds one to counter i % m (m =
+        // min(32, gate/up workgroups)); the one that completes a counter adds
+        // one to the second level, and the one that completes that raises
+        // the down workgroups' flags.  Every h store of this workgroup has
+        // completed first.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (wave == 0) {
+            const int n_gu = n_sh + n_rb;
+            const int m = min(kHandoffFlags, n_gu);
+            const int gi = bid - a.n_router;
+            const int c = gi % m;
+            const uint32_t expect = (uint32_t)(n_gu / m + (c < n_gu % m ? 1 : 0));
+            uint32_t last = 0u;
+            if (lane == 0) {
+                const uint32_t o1 = __hip_atomic_fetch_add(a.counter + kHandoffFlagStride * (kSlotDoneCount + c), 1u,
+                                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (o1 == expect - 1u) {
+                    const uint32_t o2 = __hip_atomic_fetch_add(a.counter + kHandoffFlagStride * kSlotDoneLevel2, 1u,
+                                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    last = (o2 == (uint32_t)(m - 1)) ? 1u : 0u;
+                }
+            }
+            last = (uint32_t)__builtin_amdgcn_readfirstlane((int)last);
+            if (last && lane < kHandoffFlags)
+                __hip_atomic_store(a.counter + kHandoffFlagStride * (kSlotDownFlag + lane), 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
-// The hand-off counter and its flags to zero (thread t < 1 + kHandoffFlags
-// clears one word).
+// The router hand-off words (arrival counter and flags) of a set to zero
+// (thread t <= kHandoffFlags clears one word).
 __device__ __forceinline__ void handoff_clear(uint32_t* counter, int t) {
     if (t <= kHandoffFlags)
         __hip_atomic_store(counter + kHandoffFlagStride * t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The call's first kernel: the hand-off counter, its flags and the status
-// word to zero.
-__global__ void k_handoff_reset(uint32_t* counter, int32_t* status) {
-    handoff_clear(counter, threadIdx.x);
+// The call's first kernel: both hand-off sets and the status word to zero.
+__global__ void k_handoff_reset(uint32_t* sets, int32_t* status) {
+    for (int t = threadIdx.x; t < 2 * kHandoffSlots; t += blockDim.x)
+        __hip_atomic_store(sets + kHandoffFlagStride * t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (threadIdx.x == 0) __hip_atomic_store(status, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -1008,12 +1282,15 @@ hipError_t init_kernels() {
     static hipError_t once = [] {
         hipError_t e;
         if ((e = set_lds(k_select, kMaxDynLds)) != hipSuccess) return e;
-#define MOE_SET_RG(P)                                                                       \
-        if ((e = set_lds(k_route_gateup<P, 2>, kRgMaxDynLds)) != hipSuccess) return e;         \
-        if ((e = set_lds(k_route_gateup<P, 4>, kRgMaxDynLds)) != hipSuccess) return e;         \
-        if ((e = set_lds(k_route_gateup<P, kMaxRows>, kRgMaxDynLds)) != hipSuccess) return e;
+#define MOE_SET_RG(P)                                                                          \
+        if ((e = set_lds(k_route_gateup<P, 2, false>, kRgMaxDynLds)) != hipSuccess) return e;     \
+        if ((e = set_lds(k_route_gateup<P, 4, false>, kRgMaxDynLds)) != hipSuccess) return e;     \
+        if ((e = set_lds(k_route_gateup<P, kMaxRows, false>, kRgMaxDynLds)) != hipSuccess) return e;
         MOE_SET_RG(1) MOE_SET_RG(2) MOE_SET_RG(4) MOE_SET_RG(8) MOE_SET_RG(16)
 #undef MOE_SET_RG
+        if ((e = set_lds(k_route_gateup<1, 2, true>, kRgMaxDynLds)) != hipSuccess) return e;
+        if ((e = set_lds(k_route_gateup<2, 2, true>, kRgMaxDynLds)) != hipSuccess) return e;
+        if ((e = set_lds(k_route_gateup<4, 2, true>, kRgMaxDynLds)) != hipSuccess) return e;
         if ((e = set_lds(k_down<kDownSuSmall, kDownThreads, kDownBatchSmall>, kDownHLdsBytes)) != hipSuccess)
             return e;
         if ((e = set_lds(k_down<kDownSuBig, kDownThreadsBig, kDownBatchBig>, kDownHLdsBytes)) != hipSuccess)
@@ -1039,7 +1316,11 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
 // a waiting workgroup must never keep a router workgroup from starting.
 template <typename Kern>
 hipError_t launch_route_gateup_k(Kern k, const RouteGateUpArgs& a, hipStream_t st, const Timing* t) {
-    const size_t smem = gateup_smem_bytes(a.g.K, a.g.sel.E, a.g.H);
+    size_t smem = gateup_smem_bytes(a.g.K, a.g.sel.E, a.g.H);
+    if (a.n_down > 0) {
+        const size_t dn = fused_down_lds_bytes(a.g.K, a.g.sel.k, a.g.sel.E, a.g.I, a.g.sgate.q ? a.g.Is : 0);
+        if (dn > smem) smem = dn;
+    }
     const int n_sh = a.g.sgate.q ? a.g.Is / kTileRows : 0;
     int grid = a.g.K * a.g.sel.k * (a.g.I / kTileRows);
     if (grid > kGateUpMaxGrid) grid = kGateUpMaxGrid;
@@ -1048,16 +1329,24 @@ hipError_t launch_route_gateup_k(Kern k, const RouteGateUpArgs& a, hipStream_t s
     if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
     if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kBlock, smem)) != hipSuccess) return e;
-    const int fit = per_cu * n_cu - n_sh - a.n_router;
+    const int fit = per_cu * n_cu - n_sh - a.n_router - a.n_down;
     if (fit >= 1 && grid > fit) grid = fit;
-    return launch(k, dim3(a.n_router + n_sh + grid), dim3(kBlock), smem, st, t, a);
+    return launch(k, dim3(a.n_router + n_sh + grid + a.n_down), dim3(kBlock), smem, st, t, a);
 }
 
 template <int P>
 hipError_t launch_route_gateup_p(const RouteGateUpArgs& a, hipStream_t st, const Timing* t) {
-    if (a.g.K <= 2) return launch_route_gateup_k(k_route_gateup<P, 2>, a, st, t);
-    if (a.g.K <= 4) return launch_route_gateup_k(k_route_gateup<P, 4>, a, st, t);
-    return launch_route_gateup_k(k_route_gateup<P, kMaxRows>, a, st, t);
+    if (a.n_down > 0) {
+        if constexpr (P <= kFusedMaxP) {
+            if (a.g.K > 2) return hipErrorInvalidValue;
+            return launch_route_gateup_k(k_route_gateup<P, 2, true>, a, st, t);
+        } else {
+            return hipErrorInvalidValue;
+        }
+    }
+    if (a.g.K <= 2) return launch_route_gateup_k(k_route_gateup<P, 2, false>, a, st, t);
+    if (a.g.K <= 4) return launch_route_gateup_k(k_route_gateup<P, 4, false>, a, st, t);
+    return launch_route_gateup_k(k_route_gateup<P, kMaxRows, false>, a, st, t);
 }
 
 hipError_t launch_route_gateup(const RouteGateUpArgs& a, hipStream_t st, const Timing* t) {
@@ -1069,8 +1358,26 @@ hipError_t launch_route_gateup(const RouteGateUpArgs& a, hipStream_t st, const T
     return launch_route_gateup_p<16>(a, st, t);
 }
 
-hipError_t launch_handoff_reset(uint32_t* counter, int32_t* status, hipStream_t st) {
-    hipLaunchKernelGGL(k_handoff_reset, dim3(1), dim3(64), 0, st, counter, status);
+// Whether the down projection can run as the third workgroup group of the
+// router + gate/up launch: at most two rows, every down task of a workgroup
+// (one per h row and row group) held in registers (kFusedDownTasks per
+// wave), the h rows and the routing
+// lists within the launch's LDS, and H / kDownRowsPerBlock down workgroups
+// resident next to the others; up to 256 experts (wider top-k lanes would
+// push the launch past 128 registers per lane) and a shared expert, if any,
+// as wide as a routed one.
+bool fused_down_fits(int K, int k, int E, int H, int I, int Is) {
+    if (K > 2 || (E + 63) / 64 > kFusedMaxP || (Is > 0 && Is != I)) return false;
+    const int NH = kDownRowsPerBlock;
+    const int cpr = I / 32, gI = (NH / (64 / cpr)) > 1 ? NH / (64 / cpr) : 1;
+    if ((K * k + (Is > 0 ? K : 0)) * gI > kWaves * kFusedDownTasks) return false;
+    const size_t lds = fused_down_lds_bytes(K, k, E, I, Is);
+    if (lds > (size_t)kRgMaxDynLds) return false;
+    return true;
+}
+
+hipError_t launch_handoff_reset(uint32_t* sets, int32_t* status, hipStream_t st) {
+    hipLaunchKernelGGL(k_handoff_reset, dim3(1), dim3(kBlock), 0, st, sets, status);
     return hipGetLastError();
 }
 

@@ -67,7 +67,7 @@ def test_workspace_bytes_valid_and_invalid():
     assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(inter=500))) == 0
     assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(score_fn=7))) == 0
     assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(norm_topk=0))) == 0
-    assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(regime=3))) == 0
+    assert api.lib().moe_verify_workspace_bytes(ctypes.byref(_cfg(regime=4))) == 0
 
 
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
@@ -184,7 +184,11 @@ def test_regime_argument_errors():
     n = L.moe_verify_workspace_bytes(ctypes.byref(cfg))
     assert n > 0
     assert _layer(cfg, _weights(), K=17, ws_bytes=n) == api.MOE_ERR_UNSUPPORTED
-    assert "MOE_REGIME_VERIFY" in api.moe_verify_last_error()
+    assert "verify-width" in api.moe_verify_last_error()
+    cfg = _cfg(max_rows=17, regime=api.MOE_REGIME_VERIFY_ONE_LAUNCH)
+    assert _layer(cfg, _weights(), K=17, ws_bytes=L.moe_verify_workspace_bytes(ctypes.byref(cfg))) == \
+        api.MOE_ERR_UNSUPPORTED
+    assert "verify-width" in api.moe_verify_last_error()
     cfg = _cfg(inter=2048, regime=api.MOE_REGIME_GROUPED)
     n = L.moe_verify_workspace_bytes(ctypes.byref(cfg))
     assert n > 0
@@ -264,7 +268,7 @@ def test_stream_read_argument_errors():
 
 def test_noalloc_entry_rejects_a_cfg_beyond_its_scratch_before_device_work():
     L = api.lib()
-    assert L.moe_verify_noalloc_scratch_bytes() == 4 << 20
+    assert L.moe_verify_noalloc_scratch_bytes() == 5 << 20
     cfg = _cfg(max_rows=64)  # 7.6 MB of workspace at the full-size shape
     rc = L.moe_verify_layer_noalloc(ctypes.byref(cfg), ctypes.byref(_weights()), FAKE, 2, None, FAKE, None, None,
                                     None)
