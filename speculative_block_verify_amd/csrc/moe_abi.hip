@@ -230,8 +230,8 @@ Layout layout(const moe_cfg* c, void* base) {
 
 moe::Fp4Mat mat(const moe_nvfp4& m) { return moe::Fp4Mat{m.q, m.s, m.ts}; }
 
-// Every call starts both hand-off sets and the status word at zero (the
-// workspace may hold anything).  Within a call, layer l uses set l % 2: a
+// Every verify-width call starts both hand-off sets and the status word at
+// zero (the workspace may hold anything).  Within a call, layer l uses set l % 2: a
 // separate down kernel clears the router words of set 0 for the next layer,
 // a one-launch layer clears the other set for the next layer.
 int start_call(const Layout& L, hipStream_t st) {
@@ -355,6 +355,7 @@ int enqueue_layer_grouped(const moe_cfg* c, const moe_layer_weights* w, const ui
     moe::GroupArgs ka{};
     ka.ids = L.ids; ka.n_unique = n_unique; ka.uniq = L.uniq; ka.off = L.off; ka.asg = L.asg; ka.inv = L.inv;
     ka.tiles = L.tiles; ka.n_tiles = n_tiles;
+    ka.status = L.meta + moe::kMetaStatus;
     ka.T = K; ka.E = c->n_experts; ka.k = c->top_k; ka.has_shared = has_sh;
     if ((e = moe::launch_group(ka, st)) != hipSuccess) return hip_fail(e, "grouping launch");
 
@@ -456,7 +457,9 @@ int enqueue_stack(const moe_cfg* c, const moe_layer_weights* layers, int n_layer
     const Layout L = layout(c, ws);
     hipError_t e = moe::init_kernels();
     if (e != hipSuccess) return hip_fail(e, "kernel attributes");
-    int rc0 = start_call(L, st);
+    // the grouped kernels use no hand-off (their grouping kernel clears the
+    // status word)
+    int rc0 = use_grouped(c, K) ? MOE_OK : start_call(L, st);
     if (rc0) return rc0;
     const bool stream_res = residual != nullptr;
     if (use_grouped(c, K)) {
@@ -572,7 +575,7 @@ int moe_verify_layer(const moe_cfg* cfg, const moe_layer_weights* w, const uint1
     hipError_t e = moe::init_kernels();
     if (e != hipSuccess) return hip_fail(e, "kernel attributes");
     float* yo = y32 ? y32 : L.ybuf;
-    if ((rc = start_call(L, st))) return rc;
+    if (!use_grouped(cfg, K) && (rc = start_call(L, st))) return rc;
     if ((rc = copy_debug_residual(cfg, dbg, 0, K, residual, st))) return rc;
     if (use_grouped(cfg, K)) {
         if ((rc = enqueue_layer_grouped(cfg, w, x, K, residual, yo, y, nullptr, L, st))) return rc;
@@ -616,7 +619,6 @@ int moe_verify_layer_grouped(const moe_cfg* cfg, const moe_layer_weights* w, con
     hipError_t e = moe::init_kernels();
     if (e != hipSuccess) return hip_fail(e, "kernel attributes");
     float* yo = y32 ? y32 : L.ybuf;
-    if ((rc = start_call(L, st))) return rc;
     if ((rc = copy_debug_residual(cfg, dbg, 0, K, residual, st))) return rc;
     if ((rc = enqueue_layer_grouped(cfg, w, x, K, residual, yo, y, nullptr, L, st))) return rc;
     return copy_debug(cfg, dbg, 0, K, L, x, yo, st);

@@ -195,6 +195,7 @@ __global__ __launch_bounds__(kGGroupThreads) void k_group(GroupArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int T = a.T, E = a.E, k = a.k, n = T * k, W = (T + 31) >> 5;
     const bool use_pc = group_pc_fits(T, E);
+    if (a.status && tid == 0) *a.status = 0;
     uint16_t* pc = reinterpret_cast<uint16_t*>(rm + E * W);
     // the slot list is assembled in the static LDS buffer when it fits
     __shared__ int s_asg[kGroupLdsSlots];

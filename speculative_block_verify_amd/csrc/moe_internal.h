@@ -142,6 +142,7 @@ struct GroupArgs {
     int32_t* inv;           // [T*k]
     int32_t* tiles;         // int2 [max tiles]
     int32_t* n_tiles;       // [1]
+    int32_t* status;        // the call's hand-off status word, set to 0 (no hand-off here), or nullptr
     int T, E, k;
     int has_shared;
 };

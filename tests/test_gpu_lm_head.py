@@ -158,5 +158,28 @@ def test_lm_head_full_size(K):
     rep = check(gpu, ol, bound, draft, 1e-6, "full K=%d" % K)
     say("  report:", rep)
     lean = run(x, w, draft, with_logits=False)
+    ne = int(gpu["n_emitted"][0])
     for k in api.GREEDY_FIELDS:
-        np.testing.assert_array_equal(lean[k], gpu[k], err_msg=k)
+        lk, gk = (lean[k][:ne], gpu[k][:ne]) if k == "emitted" else (lean[k], gpu[k])  # the valid prefix
+        np.testing.assert_array_equal(lk, gk, err_msg=k)
+
+
+def test_lm_head_workspace_reused_across_calls():
+    """Many calls through one workspace, with different rows and drafts,
+    each match a call on a fresh workspace."""
+    K, V, H = 3, 4099, 512
+    w = inputs.gen_lm_head(V, H, 61, device=DEV)
+    ws = torch.empty(api.moe_verify_lm_head_workspace_bytes(V, K), dtype=torch.uint8, device=DEV)
+    for rep in range(6):
+        say("case: lm_head workspace reuse, call %d" % rep)
+        x = inputs.gen_x(K, H, 70 + rep, device=DEV)
+        draft = inputs.gen_tokens(K - 1, V, 80 + rep, device=DEV)
+        out = api.alloc_greedy_out(K, DEV)
+        api.moe_verify_lm_head_greedy(x, w, out, ws, draft=draft)
+        fresh = run(x, w, draft, with_logits=False)
+        torch.cuda.synchronize()
+        got = {k: v.cpu().numpy() for k, v in out.items()}
+        ne = int(fresh["n_emitted"][0])
+        for k in api.GREEDY_FIELDS:
+            g, f = (got[k][:ne], fresh[k][:ne]) if k == "emitted" else (got[k], fresh[k])  # the valid prefix
+            np.testing.assert_array_equal(g, f, err_msg="%s call %d" % (k, rep))
