@@ -298,12 +298,11 @@ MOE_API void moe_stack_graph_destroy(moe_stack_graph* g);
  * row; section 2: W is bf16 [100352][2048], 0.41 GB), bf16 inputs with fp32
  * accumulation; row r's greedy token is its argmax (ties to the lower token
  * id).  Row r >= 1's input token is the draft token draft[r-1], so draft[j]
- * is accepted when it equals row j's greedy token or its logit is a true
- * top-logit tie, within tie_tol of row j's maximum (mlxfast README,
- * "Correctness fixtures": exact match, or a tie within 1e-6; 0 = plain
- * greedy); decode advances by the longest accepted prefix (README) plus the
- * greedy token of the first row not covered by it.  A draft token outside
- * [0, vocab) is never accepted.
+ * is accepted when it equals row j's greedy token or its logit ties row j's
+ * maximum within tie_tol (mlxfast README, "Correctness fixtures": an exact
+ * match, or a top-logit tie within 1e-6; 0 = plain greedy); a step keeps the
+ * longest accepted prefix plus the greedy token of the first row it does not
+ * cover.  A draft token outside [0, vocab) is never accepted.
  * ------------------------------------------------------------------------ */
 typedef struct moe_greedy_out {
     int32_t* target;        /* [K] greedy token of each row */

@@ -382,13 +382,12 @@ void orc_lm_head(const uint16_t* x, const uint16_t* w, int K, int V, int H, doub
  * argmax of its logits (ties to the lower token id).  Row r's input token is
  * the draft token draft[r-1] for r >= 1 (row 0 holds the last token already
  * emitted), so draft[j-1] is checked against row j-1's prediction: it is
- * accepted when it equals that greedy token or when its logit is a true
- * top-logit tie, within tie_tol of the row's maximum (the mlxfast README,
- * "Correctness fixtures": exact match, or a true top-logit tie within the
- * harness's 1e-6 logit tolerance; tie_tol = 0 is plain greedy).  Decoding
- * advances by the longest accepted prefix (README: "decode advances by the
- * longest correct prefix") plus the target's own greedy token at the first
- * row not covered by it.
+ * accepted when it equals that greedy token or when its logit ties the row's
+ * maximum within tie_tol (the mlxfast README, "Correctness fixtures", accepts
+ * a token on an exact match and on a tie of the top logit within a 1e-6
+ * tolerance; tie_tol = 0 is plain greedy).  Per the README's description of
+ * the DFlash track, a step keeps the accepted prefix; it then adds the
+ * target's own greedy token at the first row that prefix does not cover.
  * Outputs: target[K] greedy tokens; emitted[0..n) = the accepted draft
  * tokens then that greedy token; *n_emitted = accepted + 1.  Returns the
  * number of accepted draft tokens. */

@@ -1,8 +1,8 @@
 // gfx950 kernels of the verify step's head: the lm_head GEMV over every
 // verify row and greedy block acceptance (PR #844 section 5, trap 1: the
 // verifier takes the argmax of every row, one greedy token per verify row;
-// mlxfast README: decode advances by the longest correct prefix, and a token
-// counts as correct on an exact match or a true top-logit tie within 1e-6).
+// mlxfast README: a step keeps the longest accepted prefix, and a token is
+// accepted on an exact match or on a tie of the top logit within 1e-6).
 //
 //   k_lm_head        logits = x W^T for up to 16 rows on the matrix cores
 //                    (v_mfma_f32_16x16x32_bf16; bf16 products are exact in

@@ -120,7 +120,7 @@ def test_lm_head_draft_tokens_out_of_range_are_rejected():
 
 def test_lm_head_exact_tie_takes_lower_token_and_accepts_the_tied_draft():
     """Duplicate vocabulary rows tie exactly: the greedy token is the lower
-    id, and a draft of the higher id is a true top-logit tie (accepted)."""
+    id, and a draft of the higher id ties the top logit exactly (accepted)."""
     K, V, H = 3, 2000, 512
     x = inputs.gen_x(K, H, 7, device=DEV)
     w = inputs.gen_lm_head(V, H, 7, device=DEV)
