@@ -331,6 +331,40 @@ void orc_moe_layer(int K, int H, int E, int k, int I, int Is,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Dense first layer (README "Why this challenge exists": the target's layer */
+/* 0 has a dense SwiGLU MLP of intermediate 8192 instead of the MoE block)   */
+/* ------------------------------------------------------------------------ */
+
+/* y[t] = W_down (silu(W_gate x_t) .* (W_up x_t)) (+ residual[t]), every
+ * weight bf16: gate/up [I][H], down [H][I]; double throughout.  The
+ * residual, when given (bf16 [T][H]), is added last, as in the MoE layer. */
+void orc_dense_mlp(const uint16_t* x, int T, int H, int I, const uint16_t* wg, const uint16_t* wu,
+                   const uint16_t* wd, const uint16_t* residual, double* y) {
+    int t, i, c, n;
+    double* xd = (double*)malloc(sizeof(double) * (size_t)H);
+    double* hbuf = (double*)malloc(sizeof(double) * (size_t)I);
+    for (t = 0; t < T; ++t) {
+        for (c = 0; c < H; ++c) xd[c] = orc_bf16(x[(size_t)t * H + c]);
+        for (i = 0; i < I; ++i) {
+            double g = 0.0, v = 0.0;
+            for (c = 0; c < H; ++c) {
+                g += xd[c] * orc_bf16(wg[(size_t)i * H + c]);
+                v += xd[c] * orc_bf16(wu[(size_t)i * H + c]);
+            }
+            hbuf[i] = silu(g) * v;
+        }
+        for (n = 0; n < H; ++n) {
+            double acc = 0.0;
+            for (i = 0; i < I; ++i) acc += hbuf[i] * orc_bf16(wd[(size_t)n * I + i]);
+            if (residual) acc += orc_bf16(residual[(size_t)t * H + n]);
+            y[(size_t)t * H + n] = acc;
+        }
+    }
+    free(xd);
+    free(hbuf);
+}
+
+/* ------------------------------------------------------------------------ */
 /* O-9 stack glue: x_next = bf16(fp32(gamma * y / sqrt(mean(y^2) + eps)))    */
 /* ------------------------------------------------------------------------ */
 

@@ -74,6 +74,7 @@ def lib():
         L.orc_bf16_round.restype = None; L.orc_bf16_round.argtypes = [P, I, P]
         L.orc_lm_head.restype = None; L.orc_lm_head.argtypes = [P, P, I, I, I, P]
         L.orc_greedy_accept.restype = I; L.orc_greedy_accept.argtypes = [P, I, I, P, D, P, P, P]
+        L.orc_dense_mlp.restype = None; L.orc_dense_mlp.argtypes = [P, I, I, I, P, P, P, P, P]
         _lib = L
     return _lib
 
@@ -270,6 +271,44 @@ def moe_stack(layers: List[Dict[str, object]], x, top_k: int, eps: float = 1e-6,
             xa = rmsnorm_bf16(rec["y"], eps, w.get("norm_w"))
             if res is not None:
                 res = bf16_round(rec["y"])
+    return out
+
+
+def dense_mlp(w: Dict[str, object], x, residual=None) -> Dict[str, np.ndarray]:
+    """The target's dense first layer (README "Why this challenge exists":
+    a SwiGLU MLP of intermediate 8192 in place of the MoE block), bf16
+    weights w['gate'], w['up'] [I, H] and w['down'] [H, I]; float64
+    y [T, H] = down . (silu(gate . x) * (up . x)) (+ residual)."""
+    xa = _np(x, np.uint16)
+    T, H = xa.shape
+    wg, wu, wd = _np(w["gate"], np.uint16), _np(w["up"], np.uint16), _np(w["down"], np.uint16)
+    I = wg.shape[0]
+    if wg.shape != (I, H) or wu.shape != (I, H) or wd.shape != (H, I):
+        raise ValueError("dense MLP weights have shapes %s %s %s for hidden %d" % (wg.shape, wu.shape, wd.shape, H))
+    res = _np(residual, np.uint16)
+    y = np.empty((T, H), np.float64)
+    lib().orc_dense_mlp(_p(xa), T, H, I, _p(wg), _p(wu), _p(wd), _p(res), _p(y))
+    return {"y": y, "y32": y.astype(np.float32)}
+
+
+def dense_moe_stack(dense: Dict[str, object], layers: List[Dict[str, object]], x, top_k: int, eps: float = 1e-6,
+                    score_fn: int = SCORE_SOFTMAX, norm_topk: int = 1, routed_scale: float = 1.0,
+                    residual=None) -> List[Dict[str, np.ndarray]]:
+    """The prefill stack of the target: the dense first layer, then the MoE
+    layers, with the same glue between every pair (bf16(RMSNorm(y) * the
+    layer's norm weight 'norm_w')) and the same residual stream as
+    moe_stack.  Records: the dense layer's first (its 'y', 'y32', 'x_in',
+    'res_in'), then one per MoE layer."""
+    xa = _np(x, np.uint16)
+    res = _np(residual, np.uint16)
+    rec = dense_mlp(dense, xa, residual=res)
+    rec["x_in"] = xa
+    rec["res_in"] = res
+    out = [rec]
+    if layers:
+        x1 = rmsnorm_bf16(rec["y"], eps, dense.get("norm_w"))
+        r1 = None if res is None else bf16_round(rec["y"])
+        out += moe_stack(layers, x1, top_k, eps, score_fn, norm_topk, routed_scale, residual=r1)
     return out
 
 

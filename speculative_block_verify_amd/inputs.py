@@ -193,6 +193,18 @@ def gen_stack(shape: MoEShape, n_layers: int, seed: int, device="cpu",
 VOCAB = 100352      # the pages' lm_head: bf16 [100352, 2048], 0.41 GB
 
 
+DENSE_INTER = 8192    # the target's dense first layer (README "Why this challenge exists")
+
+
+def gen_dense(hidden: int, inter: int, seed: int, device="cpu") -> Dict[str, object]:
+    """The dense first layer's bf16 SwiGLU weights ~ N(0, 0.02^2) as int16 bit
+    patterns: gate/up [inter, hidden], down [hidden, inter]; no norm weight."""
+    return {"gate": bf16_bits(_randn((inter, hidden), device, seed, "dense_gate") * WEIGHT_STD),
+            "up": bf16_bits(_randn((inter, hidden), device, seed, "dense_up") * WEIGHT_STD),
+            "down": bf16_bits(_randn((hidden, inter), device, seed, "dense_down") * WEIGHT_STD),
+            "norm_w": None}
+
+
 def gen_lm_head(vocab: int, hidden: int, seed: int, device="cpu") -> torch.Tensor:
     """bf16 lm_head weights [vocab, hidden] ~ N(0, 0.02^2), as int16 bit
     patterns (generated in chunks of rows)."""

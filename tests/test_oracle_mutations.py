@@ -35,6 +35,12 @@ MUTATIONS = {
     "lm_head_transposed": ("acc += xr[h] * orc_bf16(wv[h]);", "acc += xr[h] * orc_bf16(w[((size_t)h * V + v) % ((size_t)V * H)]);"),
     "router_transposed": ("orc_bf16(wr[(size_t)e * H + h])", "orc_bf16(wr[(size_t)h * E % (E * H) + e])"),
     "down_transposed": ("orc_nvfp4_weight(dq, ds, dts, H, I, e, n, i)", "orc_nvfp4_weight(dq, ds, dts, H, I, e, (n + 1) % H, i)"),
+    "dense_silu_on_up": ("            hbuf[i] = silu(g) * v;", "            hbuf[i] = g * silu(v);"),
+    "dense_down_transposed": ("acc += hbuf[i] * orc_bf16(wd[(size_t)n * I + i]);",
+                              "acc += hbuf[i] * orc_bf16(wd[((size_t)i * H + n) % ((size_t)H * I)]);"),
+    "dense_residual_dropped": ("if (residual) acc += orc_bf16(residual[(size_t)t * H + n]);",
+                               "if (residual) acc += 0.0 * orc_bf16(residual[(size_t)t * H + n]);"),
+    "dense_gate_from_up": ("g += xd[c] * orc_bf16(wg[(size_t)i * H + c]);", "g += xd[c] * orc_bf16(wu[(size_t)i * H + c]);"),
 }
 
 

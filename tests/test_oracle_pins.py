@@ -474,6 +474,64 @@ def test_layer_step_bytes_at_two_rows():
 # ---------------------------------------------------------------------------
 
 
+# ---------------------------------------------------------------------------
+# the dense first layer and the prefill stack (README "Why this challenge
+# exists": layer 0 is a dense SwiGLU MLP)
+# ---------------------------------------------------------------------------
+
+
+def test_dense_mlp_matches_numpy_swiglu_with_residual():
+    w = inputs.gen_dense(64, 96, 71)
+    x = inputs.gen_x(3, 64, 71)
+    res = inputs.gen_x(3, 64, 72, tag="res")
+    got = orc.dense_mlp(w, x, residual=res)["y"]
+    dec = lambda t: ref.bf16_to_f64(t.numpy())  # noqa: E731
+    want = ref.swiglu_ffn(dec(x), dec(w["gate"]), dec(w["up"]), dec(w["down"])) + dec(res)
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(orc.dense_mlp(w, x)["y"], want - dec(res), rtol=1e-10, atol=1e-13)
+
+
+def test_dense_mlp_closed_forms():
+    """One intermediate unit: y[t][n] = down[n] * silu(g_t) * u_t; zero up
+    weights: y is the residual exactly; doubled down weights: y doubles."""
+    H = 32
+    w = inputs.gen_dense(H, 1, 73)
+    x = inputs.gen_x(2, H, 73)
+    dec = lambda t: ref.bf16_to_f64(np.asarray(t))  # noqa: E731
+    x64 = dec(x.numpy())
+    g = x64 @ dec(w["gate"].numpy())[0]
+    u = x64 @ dec(w["up"].numpy())[0]
+    want = (g / (1.0 + np.exp(-g)) * u)[:, None] * dec(w["down"].numpy())[:, 0][None, :]
+    np.testing.assert_allclose(orc.dense_mlp(w, x)["y"], want, rtol=1e-12, atol=1e-15)
+    w = inputs.gen_dense(H, 40, 74)
+    res = inputs.gen_x(2, H, 75, tag="res")
+    zero_up = dict(w, up=torch.zeros_like(w["up"]))
+    np.testing.assert_array_equal(orc.dense_mlp(zero_up, x, residual=res)["y"], dec(res.numpy()))
+    two = ref.f32_to_bf16_bits(2.0 * ref.bf16_to_f64(w["down"].numpy()))
+    doubled = dict(w, down=torch.as_tensor(two.astype(np.int16)))
+    np.testing.assert_array_equal(orc.dense_mlp(doubled, x)["y"], 2.0 * orc.dense_mlp(w, x)["y"])
+
+
+def test_dense_moe_stack_glue():
+    """The dense layer's record equals dense_mlp on the stack input; the
+    first MoE layer consumes bf16(gamma_0 * RMSNorm(y_0)) and, with a
+    residual stream, the residual bf16(y_0)."""
+    H = SMALL.hidden
+    dense = inputs.gen_dense(H, 64, 76)
+    rng = np.random.default_rng(76)
+    dense["norm_w"] = torch.as_tensor(ref.f32_to_bf16_bits(rng.uniform(0.5, 2.0, H)).astype(np.int16))
+    layers = inputs.gen_stack(SMALL, 2, 77)
+    x = inputs.gen_x(2, H, 78)
+    res = inputs.gen_x(2, H, 79, tag="res")
+    recs = orc.dense_moe_stack(dense, layers, x, SMALL.top_k, residual=res)
+    assert len(recs) == 3
+    np.testing.assert_array_equal(recs[0]["y"], orc.dense_mlp(dense, x, residual=res)["y"])
+    np.testing.assert_array_equal(recs[1]["x_in"], orc.rmsnorm_bf16(recs[0]["y"], 1e-6, dense["norm_w"]))
+    np.testing.assert_array_equal(recs[1]["res_in"], ref.f32_to_bf16_bits(recs[0]["y"].astype(np.float32)))
+    np.testing.assert_array_equal(recs[2]["x_in"], orc.rmsnorm_bf16(recs[1]["y"], 1e-6, layers[0].get("norm_w")))
+    assert len(orc.dense_moe_stack(dense, [], x, SMALL.top_k)) == 1
+
+
 def test_lm_head_matches_float64_matmul():
     rng = np.random.default_rng(21)
     K, V, H = 3, 301, 256
