@@ -231,6 +231,115 @@ def prefill(args):
     }), flush=True)
 
 
+def prefill_stack(args):
+    """The 512-row seed prefill through the target's whole FFN stack: the
+    dense first layer (bf16 SwiGLU, intermediate 8192) and 39 MoE layers on
+    the grouped kernels, one moe_prefill_stack call per step over a pool of
+    inputs (every layer's weights are streamed once per step: 17.9 GB, far
+    beyond the memory-side cache).  value = algorithmic bytes (the dense
+    layer's weights, each MoE layer's router, unique routed experts and
+    shared expert, activations) / time per step; tokens/s = 512 / time."""
+    import numpy as np
+    import torch
+    import oracle as orc
+    from speculative_block_verify_amd import api, inputs
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    shape, T, NL, POOL, SEED, DI = inputs.LAGUNA, 512, 39, 4, 5120, inputs.DENSE_INTER
+    H, I, Is, E, k = shape.hidden, shape.inter, shape.shared_inter, shape.n_experts, shape.top_k
+    dense = inputs.gen_dense(H, DI, SEED, device=dev)
+    layers = inputs.gen_stack(shape, NL, SEED + 1, device=dev)
+    xs = [inputs.gen_x(T, H, SEED + 10 + i, device=dev) for i in range(POOL)]
+    cfg = api.make_cfg(shape, T)
+    wts = [api.make_weights(w) for w in layers]
+    ws = torch.empty(api.moe_prefill_workspace_bytes(cfg, DI), dtype=torch.uint8, device=dev)
+    y = torch.empty(T, H, dtype=torch.int16, device=dev)
+    y32 = torch.empty(T, H, dtype=torch.float32, device=dev)
+    nu = torch.empty(NL, dtype=torch.int32, device=dev)
+    dense_bytes = 3 * H * DI * 2 + 2 * T * H * 2
+    step_bytes = []
+    for i in range(POOL):
+        api.moe_prefill_stack(cfg, dense, wts, xs[i], y, ws, y32=y32, debug=api.make_debug(n_unique=nu))
+        torch.cuda.synchronize()
+        step_bytes.append(dense_bytes + sum(api.moe_verify_weight_bytes(cfg, int(u), T) for u in nu.cpu().tolist()))
+    flops = 2.0 * (3 * T * H * DI + NL * (T * k * 3 * I * H + T * 3 * Is * H + T * E * H))
+    for s in range(args.warmup):
+        api.moe_prefill_stack(cfg, dense, wts, xs[s % POOL], y, ws, y32=y32)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record(stream)
+    for s in range(args.steps):
+        api.moe_prefill_stack(cfg, dense, wts, xs[s % POOL], y, ws, y32=y32)
+        ev[s + 1].record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev[0].elapsed_time(ev[-1])
+    per = [ev[s].elapsed_time(ev[s + 1]) for s in range(args.steps)]
+    med = statistics.median(per)
+    nb = sum(step_bytes[s % POOL] for s in range(args.steps))
+    gbs = nb / (total_ms / 1e3) / 1e9
+    tok_s = T * args.steps / (total_ms / 1e3)
+    # the dense layer alone (same inputs, its own calls)
+    dws = torch.empty(api.moe_dense_workspace_bytes(H, DI, T), dtype=torch.uint8, device=dev)
+    xn = torch.empty(T, H, dtype=torch.int16, device=dev)
+    dev_ev = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
+    for s in range(3):
+        api.moe_dense_mlp(xs[s % POOL], dense, y, y32, dws, x_next=xn)
+    dev_ev[0].record(stream)
+    for s in range(20):
+        api.moe_dense_mlp(xs[s % POOL], dense, y, y32, dws, x_next=xn)
+        dev_ev[s + 1].record(stream)
+    torch.cuda.synchronize()
+    dense_us = statistics.median(dev_ev[s].elapsed_time(dev_ev[s + 1]) for s in range(20)) * 1e3
+    dense_tflops = 2.0 * 3 * T * H * DI / (dense_us / 1e6) / 1e12
+    log("prefill-stack: %d steps, %.1f us per stack (median %.1f), %.1f GB/s, %.0f tokens/s; dense layer %.1f us "
+        "(%.1f TFLOP/s)" % (args.steps, total_ms / args.steps * 1e3, med * 1e3, gbs, tok_s, dense_us, dense_tflops))
+    result = {
+        "metric": "prefill FFN stack (dense layer + 39 MoE layers, 512 rows): weight GB/s and % HBM peak, tokens/s",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": DTYPE + "; dense layer bf16-MFMA/f32-acc", "data": "synthetic",
+        "config": {"workload": "512-row prefill through the dense first layer (bf16 SwiGLU, intermediate 8192) and "
+                               "39 NVFP4 MoE layers (grouped kernels)", "rows": T, "hidden": H,
+                   "dense_inter": DI, "moe_layers": NL, "experts": E, "top_k": k, "inter": I, "shared_inter": Is,
+                   "input_pool": POOL},
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(tok_s, 1),
+        "us_per_stack": {"mean": round(total_ms / args.steps * 1e3, 2), "median": round(med * 1e3, 2),
+                         "min": round(min(per) * 1e3, 2), "max": round(max(per) * 1e3, 2)},
+        "stall_steps_over_4x_median": sum(1 for t in per if t > 4 * med),
+        "bytes_per_step": round(sum(step_bytes) / len(step_bytes)),
+        "tflops": round(flops / (med / 1e3) / 1e12, 2),
+        "dense_layer_us": round(dense_us, 2), "dense_layer_tflops": round(dense_tflops, 2),
+        "seed": SEED, "device": torch.cuda.get_device_name(dev), "rocm": torch.version.hip,
+    }
+    if not args.no_cpu_baseline:
+        # the oracle on one row through the whole stack (rows are independent)
+        x0 = xs[0][:1].cpu().numpy().view(np.uint16)
+        dh = {kk: (None if v is None else v.cpu()) for kk, v in dense.items()}
+        lh = [{kk: (None if v is None else ({q: t.cpu() for q, t in v.items()} if isinstance(v, dict) else v.cpu()))
+               for kk, v in w.items()} for w in layers]
+        old_aff = os.sched_getaffinity(0)
+        core = max(old_aff)
+        os.sched_setaffinity(0, {core})
+        times = []
+        try:
+            for _ in range(3):
+                t1 = time.perf_counter()
+                orc.dense_moe_stack(dh, lh, x0, k)
+                times.append(time.perf_counter() - t1)
+        finally:
+            os.sched_setaffinity(0, old_aff)
+        med_s = statistics.median(times)
+        result["cpu_baseline"] = {
+            "value": round(1.0 / med_s, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "one row through the dense layer and the 39 MoE layers (rows are independent), 3 runs, median; "
+                      "single-threaded C (fp64), pinned to core %d" % core,
+            "us_per_token": round(med_s * 1e6, 1), "runs_s": [round(t, 3) for t in times], "pinned_core": core,
+            "host_cores": os.cpu_count(), "gpu_speedup": round(tok_s * med_s, 1)}
+    print(json.dumps(result), flush=True)
+
+
 def lmhead(args):
     """The verify step's head: lm_head over K verify rows (vocabulary 100352,
     hidden 2048, bf16: 0.41 GB), argmax per row and greedy acceptance, one
@@ -490,9 +599,12 @@ def main():
     ap.add_argument("--timing-steps", type=int, default=16, help="steps of the per-kernel timing pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
-    ap.add_argument("--workload", choices=("stack", "prefill", "lmhead", "layer-ksweep"), default="stack",
-                    help="stack: the 40-layer K=2 verify stack (default); prefill: one 512-row layer; lmhead: the "
-                         "verify rows' lm_head + greedy acceptance")
+    ap.add_argument("--workload", choices=("stack", "prefill", "prefill-stack", "lmhead", "layer-ksweep"),
+                    default="stack",
+                    help="stack: the 40-layer K=2 verify stack (default); prefill: one 512-row MoE layer; "
+                         "prefill-stack: 512 rows through the dense first layer and 39 MoE layers; lmhead: the "
+                         "verify rows' lm_head + greedy acceptance; layer-ksweep: one layer per launch on correlated "
+                         "rows, K = 1..16")
     ap.add_argument("--prefill-layers", type=int, default=8, help="distinct weight sets the prefill mode rotates")
     ap.add_argument("--layer-reps", type=int, default=5, help="launches of each layer graph in the layer K sweep")
     ap.add_argument("--one-launch", action="store_true",
@@ -518,6 +630,9 @@ def main():
         return
     if args.workload == "lmhead":
         lmhead(args)
+        return
+    if args.workload == "prefill-stack":
+        prefill_stack(args)
         return
     if args.workload == "layer-ksweep":
         layer_ksweep(args)

@@ -334,6 +334,58 @@ MOE_API size_t moe_verify_weight_bytes(const moe_cfg* cfg, int32_t n_unique, int
                                int32_t with_router);
 
 /* Text of the last error on this thread ("" if none). */
+/* ------------------------------------------------------------------------
+ * The target's dense first layer and the prefill stack (mlxfast README, "Why
+ * this challenge exists": layer 0 carries a dense SwiGLU MLP of intermediate
+ * 8192 ahead of the MoE layers; PR #844 section 3: the 512-row seed prefill
+ * runs through the same layers).  y[t] = W_down (silu(W_gate x_t) .*
+ * (W_up x_t)) (+ residual[t]): bf16 weights and rows, fp32 sums of exact
+ * bf16 products on the matrix cores; h enters the down GEMM as two bf16
+ * values (hi + lo: 16 significant bits, any magnitude).
+ * ------------------------------------------------------------------------ */
+typedef struct moe_dense_weights {
+    const uint16_t* gate;    /* bf16 [inter][hidden] */
+    const uint16_t* up;      /* bf16 [inter][hidden] */
+    const uint16_t* down;    /* bf16 [hidden][inter] */
+    const uint16_t* norm_w;  /* bf16 [hidden] RMSNorm weight applied to this layer's
+                                output to form the next input; NULL = ones */
+} moe_dense_weights;
+
+/* Device workspace of moe_dense_mlp for up to max_rows rows; 0 (see
+ * moe_verify_last_error) when the shape is unsupported: hidden a multiple of
+ * 64 in [64, 2048], inter a multiple of 256, max_rows >= 1. */
+MOE_API size_t moe_dense_workspace_bytes(int32_t hidden, int32_t inter, int32_t max_rows);
+
+/* The dense layer on bf16 rows x [T][hidden] (T >= 1; all arrays device,
+ * 16-byte aligned).  residual (bf16 [T][hidden]) may be NULL.  Writes y bf16
+ * [T][hidden] (RNE of y32), y32 fp32 [T][hidden] (required) and, when x_next
+ * is not NULL, the next stacked layer's input bf16(norm_w * y32 /
+ * sqrt(mean(y32^2) + eps)) with fp32 arithmetic.  The workspace holds at
+ * least moe_dense_workspace_bytes(hidden, inter, T).  Asynchronous on
+ * `stream`; errors as elsewhere. */
+MOE_API int moe_dense_mlp(const uint16_t* x, int32_t T, int32_t hidden, int32_t inter, const moe_dense_weights* w,
+                          const uint16_t* residual, float eps, uint16_t* y, float* y32, uint16_t* x_next,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device workspace of moe_prefill_stack: the MoE layers' workspace for cfg,
+ * then the dense layer's for cfg->max_rows rows and its output buffers; 0
+ * when cfg or the dense shape is invalid. */
+MOE_API size_t moe_prefill_workspace_bytes(const moe_cfg* cfg, int32_t dense_inter);
+
+/* The prefill stack: the dense layer on x (T rows), then n_layers >= 1 MoE
+ * layers exactly as moe_verify_stack runs them on the dense layer's
+ * normalised output (the kernels cfg->regime picks for T rows).  The glue
+ * between the dense layer and the first MoE layer is the stack's (the dense
+ * weights' norm_w, cfg->rms_eps); with a residual, the dense layer adds it
+ * and the first MoE layer adds bf16 of the dense output (the residual
+ * stream).  y/y32 as moe_verify_stack.  dense_y32 (nullable, fp32
+ * [T][hidden]) receives the dense layer's output; dbg (nullable) covers the
+ * MoE layers as moe_verify_stack's does. */
+MOE_API int moe_prefill_stack(const moe_cfg* cfg, const moe_dense_weights* dense, int32_t dense_inter,
+                              const moe_layer_weights* layers, int32_t n_layers, const uint16_t* x,
+                              const uint16_t* residual, int32_t T, uint16_t* y, float* y32, float* dense_y32,
+                              void* workspace, size_t workspace_bytes, void* stream, const moe_debug* dbg);
+
 MOE_API const char* moe_verify_last_error(void);
 
 /* ABI version (major * 100 + minor). */

@@ -61,6 +61,10 @@ class moe_greedy_out(ctypes.Structure):
                 ("emitted", _c_void_p), ("n_emitted", _c_void_p)]
 
 
+class moe_dense_weights(ctypes.Structure):
+    _fields_ = [("gate", _c_void_p), ("up", _c_void_p), ("down", _c_void_p), ("norm_w", _c_void_p)]
+
+
 class moe_debug(ctypes.Structure):
     _fields_ = [("logits", _c_void_p), ("ids", _c_void_p), ("w", _c_void_p), ("n_unique", _c_void_p),
                 ("uniq", _c_void_p), ("off", _c_void_p), ("asg", _c_void_p), ("inv", _c_void_p),
@@ -72,8 +76,8 @@ EXPORTS = ["moe_verify_workspace_bytes", "moe_verify_layer", "moe_verify_layer_g
            "moe_verify_lm_head_workspace_bytes", "moe_verify_lm_head_greedy",
            "moe_verify_stack_timed", "moe_verify_route", "moe_verify_stream_read",
            "moe_verify_dequant_nvfp4", "moe_stack_graph_create", "moe_stack_graph_launch",
-           "moe_stack_graph_destroy", "moe_verify_weight_bytes", "moe_verify_last_error",
-           "moe_verify_version"]
+           "moe_stack_graph_destroy", "moe_verify_weight_bytes", "moe_dense_workspace_bytes", "moe_dense_mlp",
+           "moe_prefill_workspace_bytes", "moe_prefill_stack", "moe_verify_last_error", "moe_verify_version"]
 
 _lib = None
 
@@ -122,6 +126,16 @@ def lib() -> ctypes.CDLL:
     L.moe_stack_graph_destroy.argtypes = [P]
     L.moe_verify_weight_bytes.restype = Z
     L.moe_verify_weight_bytes.argtypes = [cfgp, _i32, _i32, _i32, _i32]
+    dwp = ctypes.POINTER(moe_dense_weights)
+    L.moe_dense_workspace_bytes.restype = Z
+    L.moe_dense_workspace_bytes.argtypes = [_i32, _i32, _i32]
+    L.moe_dense_mlp.restype = ctypes.c_int
+    L.moe_dense_mlp.argtypes = [P, _i32, _i32, _i32, dwp, P, ctypes.c_float, P, P, P, P, Z, P]
+    L.moe_prefill_workspace_bytes.restype = Z
+    L.moe_prefill_workspace_bytes.argtypes = [cfgp, _i32]
+    L.moe_prefill_stack.restype = ctypes.c_int
+    L.moe_prefill_stack.argtypes = [cfgp, dwp, _i32, wp, _i32, P, P, _i32, P, P, P, P, Z, P,
+                                    ctypes.POINTER(moe_debug)]
     L.moe_verify_last_error.restype = ctypes.c_char_p
     L.moe_verify_last_error.argtypes = []
     L.moe_verify_version.restype = ctypes.c_int
@@ -466,6 +480,78 @@ def moe_verify_lm_head_greedy(x: torch.Tensor, w: torch.Tensor, out: Dict[str, t
                                            V, H, pd, float(tie_tol),
                                            _ptr(logits, torch.float32, "logits", numel=K * V, device=dev),
                                            ctypes.byref(go), pw, nw, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# the dense first layer and the prefill stack
+# ---------------------------------------------------------------------------
+
+
+def make_dense_weights(w: Dict[str, object], hidden: Optional[int] = None) -> moe_dense_weights:
+    """ctypes view of the dense layer's bf16 weights (w['gate'], w['up']
+    [inter, hidden], w['down'] [hidden, inter], optional w['norm_w'] [hidden]),
+    after checking their shapes and that they share one GPU."""
+    g, u, d = w["gate"], w["up"], w["down"]
+    for name, t in (("gate", g), ("up", u), ("down", d)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2:
+            raise ValueError("dense %s must be a 2-D tensor" % name)
+    I, H = g.shape
+    if hidden is not None and H != hidden:
+        raise ValueError("dense gate has %d columns, hidden is %d" % (H, hidden))
+    if tuple(u.shape) != (I, H) or tuple(d.shape) != (H, I):
+        raise ValueError("dense up %s / down %s do not match gate %s" % (tuple(u.shape), tuple(d.shape), (I, H)))
+    dev = g.device
+    nw = w.get("norm_w")
+    return moe_dense_weights(_ptr(g, _BITS16, "dense gate", device=dev), _ptr(u, _BITS16, "dense up", device=dev),
+                             _ptr(d, _BITS16, "dense down", device=dev),
+                             _ptr(nw, _BITS16, "dense norm_w", numel=H, device=dev))
+
+
+def moe_dense_workspace_bytes(hidden: int, inter: int, max_rows: int) -> int:
+    n = lib().moe_dense_workspace_bytes(hidden, inter, max_rows)
+    if n == 0:
+        raise MoEError(MOE_ERR_UNSUPPORTED, moe_verify_last_error())
+    return n
+
+
+def moe_dense_mlp(x: torch.Tensor, w: Dict[str, object], y: torch.Tensor, y32: torch.Tensor,
+                  workspace: torch.Tensor, residual: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                  x_next: Optional[torch.Tensor] = None, stream=None) -> None:
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor [T, hidden]")
+    T, H = x.shape
+    dw = make_dense_weights(w, H)
+    I = w["gate"].shape[0]
+    dev = x.device
+    pw, nw = _ws(workspace, dev)
+    _check(lib().moe_dense_mlp(_ptr(x, _BITS16, "x", device=dev), T, H, I, ctypes.byref(dw),
+                               _ptr(residual, _BITS16, "residual", numel=T * H, device=dev), float(eps),
+                               _ptr(y, _BITS16, "y", numel=T * H, device=dev),
+                               _ptr(y32, torch.float32, "y32", numel=T * H, device=dev),
+                               _ptr(x_next, _BITS16, "x_next", numel=T * H, device=dev), pw, nw, _stream(stream)))
+
+
+def moe_prefill_workspace_bytes(cfg: moe_cfg, dense_inter: int) -> int:
+    n = lib().moe_prefill_workspace_bytes(ctypes.byref(cfg), dense_inter)
+    if n == 0:
+        raise MoEError(MOE_ERR_UNSUPPORTED, moe_verify_last_error())
+    return n
+
+
+def moe_prefill_stack(cfg: moe_cfg, dense: Dict[str, object], layers: Sequence[moe_layer_weights], x: torch.Tensor,
+                      y: torch.Tensor, workspace: torch.Tensor, y32: Optional[torch.Tensor] = None,
+                      dense_y32: Optional[torch.Tensor] = None, residual: Optional[torch.Tensor] = None,
+                      debug: Optional[moe_debug] = None, stream=None) -> None:
+    """The dense first layer, then the MoE layers (moe_prefill_stack)."""
+    T, dev, px, pr, py, py32 = _stack_io(cfg, layers, x, y, y32, residual)
+    _check_debug(debug, cfg, T, len(layers), dev)
+    dw = make_dense_weights(dense, cfg.hidden)
+    I = dense["gate"].shape[0]
+    pw, nw = _ws(workspace, dev)
+    arr = _layer_array(layers)
+    _check(lib().moe_prefill_stack(ctypes.byref(cfg), ctypes.byref(dw), I, arr, len(layers), px, pr, T, py, py32,
+                                   _ptr(dense_y32, torch.float32, "dense_y32", numel=T * cfg.hidden, device=dev),
+                                   pw, nw, _stream(stream), ctypes.byref(debug) if debug is not None else None))
 
 
 class StackGraph:

@@ -542,7 +542,7 @@ int scratch_of_current_device(void** out) {
 
 extern "C" {
 
-int moe_verify_version(void) { return 200; }
+int moe_verify_version(void) { return 210; }
 
 const char* moe_verify_last_error(void) { return g_err.c_str(); }
 
@@ -636,6 +636,115 @@ int moe_verify_stack(const moe_cfg* cfg, const moe_layer_weights* layers, int32_
     if ((rc = check_io(x, y, y32, residual))) return rc;
     return enqueue_stack(cfg, layers, n_layers, x, residual, K, y, y32, workspace, static_cast<hipStream_t>(stream),
                          dbg);
+}
+
+// ---------------------------------------------------------------------------
+// the dense first layer and the prefill stack
+// ---------------------------------------------------------------------------
+
+namespace {
+
+int check_dense_shape(int H, int I) {
+    if (!moe::dense_shape_ok(H, I))
+        return fail(MOE_ERR_UNSUPPORTED, "dense layer hidden=%d inter=%d: need hidden a multiple of 64 in [64, 2048] "
+                    "and inter a multiple of 256", H, I);
+    return MOE_OK;
+}
+
+int check_dense_weights(const moe_dense_weights* w) {
+    if (!w) return fail(MOE_ERR_INVALID, "dense weights are NULL");
+    if (!w->gate || !w->up || !w->down || !aligned16(w->gate) || !aligned16(w->up) || !aligned16(w->down))
+        return fail(MOE_ERR_INVALID, "dense gate/up/down NULL or not 16-byte aligned");
+    if (w->norm_w && !aligned16(w->norm_w)) return fail(MOE_ERR_INVALID, "dense norm_w not 16-byte aligned");
+    return MOE_OK;
+}
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+// The prefill workspace: the MoE layout first, then the dense layer's
+// scratch, its normalised output (the first MoE layer's input), its bf16
+// output (the residual stream) and its fp32 output.
+struct PrefillLayout {
+    size_t moe, dense, xnext, ybf, y32, bytes;
+};
+PrefillLayout prefill_layout(const moe_cfg* c, int I) {
+    PrefillLayout P{};
+    const size_t R = (size_t)c->max_rows, H = (size_t)c->hidden;
+    P.moe = 0;
+    P.dense = round256(layout(c, nullptr).bytes);
+    P.xnext = P.dense + round256(moe::dense_workspace_bytes(c->hidden, I, c->max_rows));
+    P.ybf = P.xnext + round256(R * H * 2);
+    P.y32 = P.ybf + round256(R * H * 2);
+    P.bytes = P.y32 + round256(R * H * 4);
+    return P;
+}
+
+}  // namespace
+
+size_t moe_dense_workspace_bytes(int32_t hidden, int32_t inter, int32_t max_rows) {
+    if (check_dense_shape(hidden, inter)) return 0;
+    if (max_rows < 1) {
+        fail(MOE_ERR_INVALID, "max_rows=%d < 1", max_rows);
+        return 0;
+    }
+    return moe::dense_workspace_bytes(hidden, inter, max_rows);
+}
+
+int moe_dense_mlp(const uint16_t* x, int32_t T, int32_t hidden, int32_t inter, const moe_dense_weights* w,
+                  const uint16_t* residual, float eps, uint16_t* y, float* y32, uint16_t* x_next, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+    int rc;
+    if ((rc = check_dense_shape(hidden, inter))) return rc;
+    if (T < 1) return fail(MOE_ERR_INVALID, "T=%d < 1", T);
+    if ((rc = check_dense_weights(w))) return rc;
+    if ((rc = check_io(x, y, y32, residual))) return rc;
+    if (!y32) return fail(MOE_ERR_INVALID, "y32 is NULL (the dense layer writes its fp32 output)");
+    if (x_next && !aligned16(x_next)) return fail(MOE_ERR_INVALID, "x_next not 16-byte aligned");
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(MOE_ERR_INVALID, "eps invalid");
+    const size_t need = moe::dense_workspace_bytes(hidden, inter, T);
+    if (!workspace || !aligned16(workspace)) return fail(MOE_ERR_INVALID, "workspace NULL or not 16-byte aligned");
+    if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    hipError_t e = moe::launch_dense_mlp(x, T, hidden, inter, w->gate, w->up, w->down, residual, w->norm_w, eps, y32, y,
+                                         x_next, workspace, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "dense layer launch");
+}
+
+size_t moe_prefill_workspace_bytes(const moe_cfg* cfg, int32_t dense_inter) {
+    if (check_cfg(cfg)) return 0;
+    if (check_dense_shape(cfg->hidden, dense_inter)) return 0;
+    return prefill_layout(cfg, dense_inter).bytes;
+}
+
+int moe_prefill_stack(const moe_cfg* cfg, const moe_dense_weights* dense, int32_t dense_inter,
+                      const moe_layer_weights* layers, int32_t n_layers, const uint16_t* x, const uint16_t* residual,
+                      int32_t T, uint16_t* y, float* y32, float* dense_y32, void* workspace, size_t workspace_bytes,
+                      void* stream, const moe_debug* dbg) {
+    int rc;
+    if ((rc = check_cfg(cfg))) return rc;
+    if ((rc = check_dense_shape(cfg->hidden, dense_inter))) return rc;
+    if ((rc = check_dense_weights(dense))) return rc;
+    if (T < 1 || T > cfg->max_rows) return fail(MOE_ERR_INVALID, "T=%d outside [1, max_rows=%d]", T, cfg->max_rows);
+    if ((rc = check_regime(cfg, T))) return rc;
+    if (!layers || n_layers < 1) return fail(MOE_ERR_INVALID, "need n_layers >= 1 and a layer array");
+    for (int l = 0; l < n_layers; ++l)
+        if ((rc = check_weights(cfg, &layers[l], l))) return rc;
+    if ((rc = check_io(x, y, y32, residual))) return rc;
+    if (dense_y32 && !aligned16(dense_y32)) return fail(MOE_ERR_INVALID, "dense_y32 not 16-byte aligned");
+    const PrefillLayout P = prefill_layout(cfg, dense_inter);
+    if (!workspace || !aligned16(workspace)) return fail(MOE_ERR_INVALID, "workspace NULL or not 16-byte aligned");
+    if (workspace_bytes < P.bytes)
+        return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, P.bytes);
+    char* ws = static_cast<char*>(workspace);
+    uint16_t* xnext = reinterpret_cast<uint16_t*>(ws + P.xnext);
+    uint16_t* ybf = reinterpret_cast<uint16_t*>(ws + P.ybf);
+    float* yd = dense_y32 ? dense_y32 : reinterpret_cast<float*>(ws + P.y32);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = moe::init_kernels();
+    if (e != hipSuccess) return hip_fail(e, "kernel attributes");
+    e = moe::launch_dense_mlp(x, T, cfg->hidden, dense_inter, dense->gate, dense->up, dense->down, residual,
+                              dense->norm_w, cfg->rms_eps, yd, ybf, xnext, ws + P.dense, st);
+    if (e != hipSuccess) return hip_fail(e, "dense layer launch");
+    return enqueue_stack(cfg, layers, n_layers, xnext, residual ? ybf : nullptr, T, y, y32, ws + P.moe, st, dbg);
 }
 
 int moe_verify_route(const moe_cfg* cfg, const float* logits, const float* bias, int32_t K,

@@ -206,6 +206,13 @@ constexpr int kRouteSpinLimit = 1 << 22;   // polls (with a short sleep each) be
 hipError_t launch_dequant(Fp4Mat m, int n_experts, int rows, int cols, float* out, hipStream_t st);
 hipError_t launch_stream_read(const void* src, size_t n16, uint32_t* sink, hipStream_t st);
 
+// Dense first layer (dense.hip).
+bool dense_shape_ok(int H, int I);
+size_t dense_workspace_bytes(int H, int I, int T);
+hipError_t launch_dense_mlp(const uint16_t* x, int T, int H, int I, const uint16_t* wg, const uint16_t* wu,
+                            const uint16_t* wd, const uint16_t* residual, const uint16_t* gamma, float eps, float* y32,
+                            uint16_t* y, uint16_t* x_next, void* workspace, hipStream_t st);
+
 // Grouped regime (moe_grouped.hip).
 hipError_t launch_router_mfma(const RouterArgs& a, hipStream_t st);  // many rows, plain bf16 x_in only
 hipError_t launch_select_rows(const SelectArgs& a, hipStream_t st);  // ids and w only

@@ -108,6 +108,63 @@ def run_stack_debug(cfg, layers_dev, x, n_layers, residual=None):
     return out
 
 
+def run_prefill_debug(cfg, dense_dev, layers_dev, x, residual=None):
+    """moe_prefill_stack with per-MoE-layer debug arrays and the dense
+    layer's fp32 output; returns numpy arrays (rows as given)."""
+    T, H = x.shape
+    E, k, L = cfg.n_experts, cfg.top_k, len(layers_dev)
+    dev = x.device
+    n = T * k
+    dbg_t = {
+        "logits": torch.empty(L, T, E, dtype=torch.float32, device=dev),
+        "ids": torch.empty(L, n, dtype=torch.int32, device=dev),
+        "w": torch.empty(L, n, dtype=torch.float32, device=dev),
+        "n_unique": torch.empty(L, dtype=torch.int32, device=dev),
+        "uniq": torch.empty(L, n, dtype=torch.int32, device=dev),
+        "off": torch.empty(L, n + 1, dtype=torch.int32, device=dev),
+        "asg": torch.empty(L, n, dtype=torch.int32, device=dev),
+        "inv": torch.empty(L, n, dtype=torch.int32, device=dev),
+        "x_in": torch.empty(L, T, H, dtype=torch.int16, device=dev),
+        "y32": torch.empty(L, T, H, dtype=torch.float32, device=dev),
+        "status": torch.full((L,), -1, dtype=torch.int32, device=dev),
+    }
+    if residual is not None:
+        dbg_t["res_in"] = torch.empty(L, T, H, dtype=torch.int16, device=dev)
+    y = torch.empty(T, H, dtype=torch.int16, device=dev)
+    y32 = torch.empty(T, H, dtype=torch.float32, device=dev)
+    yd = torch.full((T, H), float("nan"), dtype=torch.float32, device=dev)
+    I = dense_dev["gate"].shape[0]
+    ws = torch.empty(api.moe_prefill_workspace_bytes(cfg, I), dtype=torch.uint8, device=dev)
+    api.moe_prefill_stack(cfg, dense_dev, [api.make_weights(w, cfg) for w in layers_dev], x, y, ws, y32=y32,
+                          dense_y32=yd, residual=residual, debug=api.make_debug(**dbg_t))
+    torch.cuda.synchronize()
+    out = {kk: v.cpu().numpy() for kk, v in dbg_t.items()}
+    assert np.all(out["status"] == 0), "an in-kernel hand-off wait gave up: %s" % out["status"]
+    out["y"] = y.cpu().numpy().view(np.uint16)
+    out["y32_out"] = y32.cpu().numpy()
+    out["dense_y32"] = yd.cpu().numpy()
+    return out
+
+
+def oracle_dense_rows(w, x, residual=None, threads: int = 16) -> np.ndarray:
+    """orc.dense_mlp over the rows of x in chunks on parallel host threads
+    (each row's output depends on that row alone); float64 y."""
+    from concurrent.futures import ThreadPoolExecutor
+    wh = {kk: (None if v is None else np.ascontiguousarray(v.cpu().numpy() if hasattr(v, "cpu") else v))
+          for kk, v in w.items()}
+    xa = np.ascontiguousarray(np.asarray(x.cpu() if hasattr(x, "cpu") else x)).view(np.uint16)
+    ra = None if residual is None else np.ascontiguousarray(
+        np.asarray(residual.cpu() if hasattr(residual, "cpu") else residual)).view(np.uint16)
+    T = xa.shape[0]
+    bounds = np.linspace(0, T, min(threads, T) + 1).astype(int)
+    parts = [(a, b) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+    with ThreadPoolExecutor(len(parts)) as ex:
+        ys = list(ex.map(lambda ab: orc.dense_mlp(wh, np.ascontiguousarray(xa[ab[0]:ab[1]]),
+                                                  residual=None if ra is None else
+                                                  np.ascontiguousarray(ra[ab[0]:ab[1]]))["y"], parts))
+    return np.concatenate(ys)
+
+
 def oracle_layer_rows(w, x, k: int, score_fn: int = 0, rs: float = 1.0, residual=None, threads: int = 16):
     """orc.moe_layer over the rows of x in chunks on parallel host threads
     (the layer is defined row by row: each row's routing and FFN depend on
@@ -267,11 +324,16 @@ def check_glue(x_next_gpu: np.ndarray, y32_gpu: np.ndarray, eps: float, gamma, l
 
 
 def compare_stack(gpu, layers_host, x0: np.ndarray, k: int, n_experts: int, eps: float = 1e-6,
-                  score_fn: int = 0, rs: float = 1.0, label="", residual=None, max_flip_frac=0.02):
+                  score_fn: int = 0, rs: float = 1.0, label="", residual=None, max_flip_frac=0.02, pre=None):
     """Every layer of a stack against the oracle at the 2e-3 bar (rules
     above).  A row leaves the comparison only after a layer where it
     selected other experts at a certified near-tie of the oracle's keys.
-    residual: the stack's initial residual (bf16 bits) or None."""
+    residual: the stack's initial residual (bf16 bits) or None.
+    pre: a layer ahead of the MoE layers (the dense first layer of the
+    prefill stack), as {'y_oracle': its oracle output on x0, 'y32_gpu': the
+    GPU's, 'norm_w': its norm weight or None}; the first MoE layer's input
+    and residual are then checked like any later layer's, and x0 is the
+    pre-layer's input."""
     layers_host = list(layers_host)
     K, H = x0.shape
     alive = np.ones(K, bool)
@@ -279,6 +341,11 @@ def compare_stack(gpu, layers_host, x0: np.ndarray, k: int, n_experts: int, eps:
     ro = None if residual is None else np.ascontiguousarray(residual).view(np.uint16)
     reps = []
     prev = None
+    if pre is not None:
+        prev = (pre["y_oracle"], {"norm_w": pre["norm_w"]})
+        xo = orc.rmsnorm_bf16(pre["y_oracle"], eps, pre["norm_w"])
+        if ro is not None:
+            ro = orc.bf16_round(pre["y_oracle"])
     for l, w in enumerate(layers_host):
         g = {kk: gpu[kk][l] for kk in ("logits", "ids", "w", "n_unique", "uniq", "off", "asg", "inv",
                                        "x_in", "y32")}
@@ -290,7 +357,7 @@ def compare_stack(gpu, layers_host, x0: np.ndarray, k: int, n_experts: int, eps:
         glue_flips = 0
         if prev is not None:
             yo_prev, wprev = prev
-            y32g_prev = gpu["y32"][l - 1]
+            y32g_prev = gpu["y32"][l - 1] if l > 0 else pre["y32_gpu"]
             gam = wprev.get("norm_w")
             gam = None if gam is None else np.asarray(gam).view(np.uint16)
             # the glue on the GPU's own values (every row)
@@ -320,7 +387,7 @@ def compare_stack(gpu, layers_host, x0: np.ndarray, k: int, n_experts: int, eps:
                 flips_r = int(fr.sum())
                 ro = ro.copy()
                 ro[rows] = np.where(fr, rg[rows], ro[rows])
-        if ro is not None and l == 0:
+        if ro is not None and l == 0 and pre is None:
             np.testing.assert_array_equal(gpu["res_in"][0].view(np.uint16), ro, err_msg=label + " layer 0 residual")
         # the GPU consumed exactly the oracle chain's input on every compared row
         np.testing.assert_array_equal(xg[alive], xo[alive], err_msg="%s layer %d input" % (label, l))

@@ -32,7 +32,7 @@ def test_header_declares_the_expected_surface():
 def test_library_exports_every_declared_symbol(L):
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert api.moe_verify_version() == 200
+    assert api.moe_verify_version() == 210
 
 
 def test_struct_layouts_match_header_sizes():
@@ -42,6 +42,7 @@ def test_struct_layouts_match_header_sizes():
     assert ctypes.sizeof(api.moe_layer_weights) == 21 * P
     assert ctypes.sizeof(api.moe_route_out) == 7 * P
     assert ctypes.sizeof(api.moe_debug) == 12 * P
+    assert ctypes.sizeof(api.moe_dense_weights) == 4 * P
     assert ctypes.sizeof(api.moe_cfg) == 44
 
 
@@ -273,6 +274,50 @@ def test_noalloc_entry_rejects_a_cfg_beyond_its_scratch_before_device_work():
     rc = L.moe_verify_layer_noalloc(ctypes.byref(cfg), ctypes.byref(_weights()), FAKE, 2, None, FAKE, None, None,
                                     None)
     assert rc == api.MOE_ERR_UNSUPPORTED and "scratch" in api.moe_verify_last_error()
+
+
+def test_dense_and_prefill_argument_errors():
+    """Checked before any device work: shapes, NULL or misaligned pointers,
+    row counts, short workspaces."""
+    L = api.lib()
+    n = L.moe_dense_workspace_bytes(2048, 8192, 512)
+    assert n > 0 and n % 256 == 0
+    assert L.moe_dense_workspace_bytes(2048, 8192, 1024) > n
+    for H, I, R in ((2048, 100, 512), (2048, 8192 + 64, 8), (100, 8192, 8), (4096, 8192, 8), (2048, 8192, 0)):
+        assert L.moe_dense_workspace_bytes(H, I, R) == 0, (H, I, R)
+    dw = api.moe_dense_weights(FAKE, FAKE, FAKE, None)
+
+    def dense(x=FAKE, T=4, H=2048, I=8192, w=dw, res=None, eps=1e-6, y=FAKE, y32=FAKE, xn=None, ws=FAKE, nb=n):
+        return L.moe_dense_mlp(x, T, H, I, None if w is None else ctypes.byref(w), res, eps, y, y32, xn, ws, nb, None)
+
+    assert dense(T=0) == api.MOE_ERR_INVALID
+    assert dense(I=300) == api.MOE_ERR_UNSUPPORTED
+    assert dense(w=None) == api.MOE_ERR_INVALID
+    assert dense(w=api.moe_dense_weights(FAKE, None, FAKE, None)) == api.MOE_ERR_INVALID
+    assert dense(w=api.moe_dense_weights(FAKE, FAKE, FAKE, FAKE + 2)) == api.MOE_ERR_INVALID
+    assert dense(y32=None) == api.MOE_ERR_INVALID
+    assert dense(xn=FAKE + 8) == api.MOE_ERR_INVALID
+    assert dense(eps=-1.0) == api.MOE_ERR_INVALID
+    assert dense(ws=None) == api.MOE_ERR_INVALID
+    assert dense(nb=L.moe_dense_workspace_bytes(2048, 8192, 4) - 256) == api.MOE_ERR_WORKSPACE
+
+    cfg = _cfg(max_rows=512)
+    pn = L.moe_prefill_workspace_bytes(ctypes.byref(cfg), 8192)
+    assert pn > L.moe_verify_workspace_bytes(ctypes.byref(cfg)) + n
+    assert L.moe_prefill_workspace_bytes(ctypes.byref(cfg), 100) == 0
+    layers = (api.moe_layer_weights * 2)(_weights(), _weights())
+
+    def pre(T=512, w=dw, I=8192, nl=2, nb=pn, x=FAKE, y=FAKE):
+        return L.moe_prefill_stack(ctypes.byref(cfg), None if w is None else ctypes.byref(w), I, layers, nl, x, None,
+                                   T, y, None, None, FAKE, nb, None, None)
+
+    assert pre(T=0) == api.MOE_ERR_INVALID
+    assert pre(T=513) == api.MOE_ERR_INVALID
+    assert pre(I=100) == api.MOE_ERR_UNSUPPORTED
+    assert pre(w=None) == api.MOE_ERR_INVALID
+    assert pre(nl=0) == api.MOE_ERR_INVALID
+    assert pre(x=None) == api.MOE_ERR_INVALID
+    assert pre(nb=pn - 256) == api.MOE_ERR_WORKSPACE
 
 
 def test_lm_head_argument_errors():
