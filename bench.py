@@ -427,6 +427,131 @@ def lmhead(args):
     print(json.dumps(result), flush=True)
 
 
+def kv_ring(args):
+    """The verify step's sliding-window KV maintenance on the target's shape
+    (30 sliding layers, 8 KV heads of head_dim 128, window 512, K=2 rows):
+    per step, as a forward makes them, one in-place write of the block's rows
+    per layer and one device-side commit of 1 + n_accepted rows.  value =
+    microseconds per step; the roofline is the ring write's algorithmic bytes
+    (new rows read once, written once) over its time; the concatenating
+    cache that rebuilds every window per step is set beside it by its HBM
+    lower bound."""
+    import torch
+    from oracle import kv_oracle
+    from speculative_block_verify_amd import api
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L, NKV, D, W, K, POOL, SEED = 30, 8, 128, 512, args.rows, 8, 41
+    ring = api.KvRing(L, NKV, D, W, K, dev)
+    ring.reset(0)
+    g = torch.Generator(device=dev).manual_seed(SEED)
+    kn = [torch.randint(-32768, 32767, (L, K, NKV, D), generator=g, device=dev, dtype=torch.int16)
+          for _ in range(POOL)]
+    vn = [torch.randint(-32768, 32767, (L, K, NKV, D), generator=g, device=dev, dtype=torch.int16)
+          for _ in range(POOL)]
+    nacc = torch.randint(0, K, (POOL, 1), generator=g, device=dev, dtype=torch.int32)
+
+    def step(s):  # the forward's pattern: each layer written before its attention
+        for l in range(L):
+            ring.write_layer(l, kn[s % POOL][l], vn[s % POOL][l])
+        ring.commit(nacc[s % POOL], K)
+
+    def step_batched(s):  # all layers' rows in one launch
+        ring.write(kn[s % POOL], vn[s % POOL])
+        ring.commit(nacc[s % POOL], K)
+
+    # Steps are captured in HIP graphs (GSTEPS per graph) so the timed region
+    # holds the kernels, not the host's launch path: the eager rate is
+    # reported beside it.
+    GSTEPS = 32
+
+    def capture(fn):
+        g_ = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g_, stream=side):
+                for s in range(GSTEPS):
+                    fn(s)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        return g_
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for s in range(n):
+            fn(s)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / n * 1e3  # us per call
+
+    for s in range(args.warmup):
+        step(s)
+    us_eager = timed(step, max(1, args.steps // 8))
+    g_step = capture(step)
+    g_batched = capture(step_batched)
+    g_write = capture(lambda s: ring.write_layer(s % L, kn[s % POOL][s % L], vn[s % POOL][s % L]))
+    reps = max(1, args.steps // GSTEPS)
+    for _ in range(2):
+        g_step.replay()
+        g_batched.replay()
+        g_write.replay()
+    us_step = timed(lambda s: g_step.replay(), reps) / GSTEPS
+    us_batched = timed(lambda s: g_batched.replay(), reps) / GSTEPS
+    us_write = timed(lambda s: g_write.replay(), reps) / GSTEPS
+    nbytes = kv_oracle.copy_bytes_in_place(L, NKV, D, K)
+    layer_bytes = kv_oracle.copy_bytes_in_place(1, NKV, D, K)
+    concat = kv_oracle.copy_bytes_concat(L, NKV, D, W, K)
+    gbs = layer_bytes / (us_write * 1e-6) / 1e9
+    log("kv: %.2f us per step of %d layer writes + commit in graphs (%.2f us launched one by one from Python; "
+        "%.2f us with every layer in one write), %.3f us per layer write (%.1f GB/s); concatenation would move "
+        "%.3f GB (>= %.1f us at 8 TB/s)" % (us_step, L, us_eager, us_batched, us_write, gbs, concat / 1e9,
+                                           concat / HBM_PEAK_GBS / 1e3))
+    result = {
+        "metric": "verify-step sliding-window KV maintenance: microseconds per step",
+        "value": round(us_step, 3), "unit": "us/step", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us_step / 1e3, 6), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 rows (copied bit for bit)", "data": "synthetic",
+        "config": {"workload": "sliding-window KV ring, 30 layers x 8 KV heads x head_dim 128, window 512, "
+                               "K=%d rows per step: an in-place write per layer + device commit" % K,
+                   "rows": K, "layers": L, "kv_heads": NKV, "head_dim": D, "window": W,
+                   "capacity": ring.shape[2]},
+        "us_per_layer_write": round(us_write, 3),
+        "us_per_step_one_write_for_all_layers": round(us_batched, 3),
+        "us_per_step_eager_launches": round(us_eager, 3),
+        "graph_steps": GSTEPS,
+        "bytes_per_step": nbytes,
+        "concat_bytes_per_step": concat,
+        "concat_hbm_lower_bound_us": round(concat / HBM_PEAK_GBS / 1e3, 2),
+        "roofline": {"bound": "hbm", "kernel": "k_kv_write, one layer (graph of %d writes; time per write "
+                               "includes the gaps between them)" % GSTEPS, "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": layer_bytes},
+        "seed": SEED, "device": torch.cuda.get_device_name(dev), "rocm": torch.version.hip,
+    }
+    if not args.no_cpu_baseline:
+        import numpy as np
+        rng = np.random.default_rng(SEED)
+        hist = kv_oracle.KVHistory(L, NKV, D, W)
+        ko = rng.integers(0, 1 << 16, (L, K, NKV, D), dtype=np.uint16)
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 2.0:
+            hist.write(ko, ko)
+            for l in range(L):  # what the block's last row sees in every layer
+                hist.window(l, hist.length - 1)
+            hist.commit(n % K)
+            n += 1
+        sec = (time.perf_counter() - t0) / n
+        result["cpu_baseline"] = {"value": round(sec * 1e6, 1), "unit": "us/step", "cores": 1, "kind": "oracle",
+                                  "sample": "%d steps of the history model (write, every layer's window, commit), "
+                                            "about 2 s" % n}
+    print(json.dumps(result), flush=True)
+
+
 def layer_ksweep(args):
     """Dedup at real expert reuse: single verify layers (the 40 weight sets of
     the stack) on correlated rows -- rows 1..K/2 are row 0 plus noise that
@@ -599,12 +724,13 @@ def main():
     ap.add_argument("--timing-steps", type=int, default=16, help="steps of the per-kernel timing pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
-    ap.add_argument("--workload", choices=("stack", "prefill", "prefill-stack", "lmhead", "layer-ksweep"),
+    ap.add_argument("--workload", choices=("stack", "prefill", "prefill-stack", "lmhead", "layer-ksweep", "kv"),
                     default="stack",
                     help="stack: the 40-layer K=2 verify stack (default); prefill: one 512-row MoE layer; "
                          "prefill-stack: 512 rows through the dense first layer and 39 MoE layers; lmhead: the "
                          "verify rows' lm_head + greedy acceptance; layer-ksweep: one layer per launch on correlated "
-                         "rows, K = 1..16")
+                         "rows, K = 1..16; kv: the sliding-window KV ring's write + commit per "
+                         "verify step")
     ap.add_argument("--prefill-layers", type=int, default=8, help="distinct weight sets the prefill mode rotates")
     ap.add_argument("--layer-reps", type=int, default=5, help="launches of each layer graph in the layer K sweep")
     ap.add_argument("--one-launch", action="store_true",
@@ -636,6 +762,9 @@ def main():
         return
     if args.workload == "layer-ksweep":
         layer_ksweep(args)
+        return
+    if args.workload == "kv":
+        kv_ring(args)
         return
 
     import torch

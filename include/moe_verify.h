@@ -386,6 +386,67 @@ MOE_API int moe_prefill_stack(const moe_cfg* cfg, const moe_dense_weights* dense
                               const uint16_t* residual, int32_t T, uint16_t* y, float* y32, float* dense_y32,
                               void* workspace, size_t workspace_bytes, void* stream, const moe_debug* dbg);
 
+/* ------------------------------------------------------------------------
+ * The verify step's sliding-window KV cache (PR #844 section 8 items 1-2,
+ * section 10: at K >= 2 rows the sliding layers rebuilt their keys and
+ * values by concatenation every step, about 0.126 GB of copies per step
+ * (section 2), and a wrapped rotating cache could not drop rejected rows,
+ * so a rejecting round replayed the forward; mlxfast README, "Why this
+ * challenge exists": 512-token sliding windows, 8 KV heads of head_dim 128).
+ *
+ * A ring of `capacity` slots per layer and KV head holds position q in slot
+ * q % capacity.  A verify block of K rows writes its rows in place at the
+ * positions len .. len+K-1 (len: a device counter, read by the kernels);
+ * the commit keeps row 0 and the block's accepted drafts by advancing len
+ * by 1 + n_accepted (read on the device, e.g. moe_greedy_out.n_accepted),
+ * which drops the rejected rows without moving data.  capacity must be at
+ * least window + K - 1 (moe_kv_ring_capacity), so no position that a row of
+ * the block, or of the next block after any rollback, can see is ever
+ * overwritten.  No host round trip: a step is graph-capturable.
+ * ------------------------------------------------------------------------ */
+typedef struct moe_kv_ring {
+    uint16_t* k;       /* bf16 [n_layers][n_kv][capacity][head_dim], device */
+    uint16_t* v;       /* the same layout for values */
+    int32_t* len;      /* device int32 [1]: committed length */
+    int32_t n_layers, n_kv, head_dim, window, capacity;
+} moe_kv_ring;
+
+/* Slots per ring for blocks of up to max_rows rows: window + max_rows - 1
+ * (0 when window < 1 or max_rows < 1). */
+MOE_API int32_t moe_kv_ring_capacity(int32_t window, int32_t max_rows);
+
+/* Bytes of one of the ring's two arrays (keys or values). */
+MOE_API size_t moe_kv_ring_bytes(int32_t n_layers, int32_t n_kv, int32_t head_dim, int32_t capacity);
+
+/* Sets the committed length to len (>= 0) on `stream`. */
+MOE_API int moe_kv_ring_reset(const moe_kv_ring* ring, int32_t len, void* stream);
+
+/* Writes a block's rows: k_new, v_new bf16 [n_layers][K][n_kv][head_dim]
+ * device, row r at position len + r.  Errors: MOE_ERR_INVALID for NULL or
+ * misaligned pointers, head_dim not a positive multiple of 8, K < 1 or
+ * capacity < window + K - 1. */
+MOE_API int moe_kv_ring_write(const moe_kv_ring* ring, const uint16_t* k_new, const uint16_t* v_new, int32_t K,
+                              void* stream);
+
+/* Writes one layer's rows of a block: k_new, v_new bf16 [K][n_kv][head_dim]
+ * device, row r at position len + r of `layer` (a forward writes each sliding
+ * layer's new keys and values just before that layer's attention reads its
+ * window).  Errors as moe_kv_ring_write, and MOE_ERR_INVALID for a layer
+ * outside [0, n_layers). */
+MOE_API int moe_kv_ring_write_layer(const moe_kv_ring* ring, int32_t layer, const uint16_t* k_new,
+                                    const uint16_t* v_new, int32_t K, void* stream);
+
+/* Commits the last written block of K rows: len += 1 + n_accepted, the
+ * device count clamped to [0, K - 1]. */
+MOE_API int moe_kv_ring_commit(const moe_kv_ring* ring, const int32_t* n_accepted, int32_t K, void* stream);
+
+/* What the last written block's row r sees of `layer`, for r < K: k_out,
+ * v_out bf16 [K][n_kv][window][head_dim] device, positions
+ * len + r - window + 1 .. len + r oldest first, zeros before position 0.
+ * Call between the block's write and its commit. */
+MOE_API int moe_kv_ring_window(const moe_kv_ring* ring, int32_t layer, int32_t K, uint16_t* k_out, uint16_t* v_out,
+                               void* stream);
+
 MOE_API const char* moe_verify_last_error(void);
 
 /* ABI version (major * 100 + minor). */

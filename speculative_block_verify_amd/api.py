@@ -65,6 +65,11 @@ class moe_dense_weights(ctypes.Structure):
     _fields_ = [("gate", _c_void_p), ("up", _c_void_p), ("down", _c_void_p), ("norm_w", _c_void_p)]
 
 
+class moe_kv_ring(ctypes.Structure):
+    _fields_ = [("k", _c_void_p), ("v", _c_void_p), ("len", _c_void_p), ("n_layers", _i32), ("n_kv", _i32),
+                ("head_dim", _i32), ("window", _i32), ("capacity", _i32)]
+
+
 class moe_debug(ctypes.Structure):
     _fields_ = [("logits", _c_void_p), ("ids", _c_void_p), ("w", _c_void_p), ("n_unique", _c_void_p),
                 ("uniq", _c_void_p), ("off", _c_void_p), ("asg", _c_void_p), ("inv", _c_void_p),
@@ -77,7 +82,10 @@ EXPORTS = ["moe_verify_workspace_bytes", "moe_verify_layer", "moe_verify_layer_g
            "moe_verify_stack_timed", "moe_verify_route", "moe_verify_stream_read",
            "moe_verify_dequant_nvfp4", "moe_stack_graph_create", "moe_stack_graph_launch",
            "moe_stack_graph_destroy", "moe_verify_weight_bytes", "moe_dense_workspace_bytes", "moe_dense_mlp",
-           "moe_prefill_workspace_bytes", "moe_prefill_stack", "moe_verify_last_error", "moe_verify_version"]
+           "moe_prefill_workspace_bytes", "moe_prefill_stack", "moe_kv_ring_capacity", "moe_kv_ring_bytes",
+           "moe_kv_ring_reset", "moe_kv_ring_write", "moe_kv_ring_write_layer", "moe_kv_ring_commit",
+           "moe_kv_ring_window",
+           "moe_verify_last_error", "moe_verify_version"]
 
 _lib = None
 
@@ -136,6 +144,21 @@ def lib() -> ctypes.CDLL:
     L.moe_prefill_stack.restype = ctypes.c_int
     L.moe_prefill_stack.argtypes = [cfgp, dwp, _i32, wp, _i32, P, P, _i32, P, P, P, P, Z, P,
                                     ctypes.POINTER(moe_debug)]
+    rp = ctypes.POINTER(moe_kv_ring)
+    L.moe_kv_ring_capacity.restype = _i32
+    L.moe_kv_ring_capacity.argtypes = [_i32, _i32]
+    L.moe_kv_ring_bytes.restype = Z
+    L.moe_kv_ring_bytes.argtypes = [_i32, _i32, _i32, _i32]
+    L.moe_kv_ring_reset.restype = ctypes.c_int
+    L.moe_kv_ring_reset.argtypes = [rp, _i32, P]
+    L.moe_kv_ring_write.restype = ctypes.c_int
+    L.moe_kv_ring_write.argtypes = [rp, P, P, _i32, P]
+    L.moe_kv_ring_write_layer.restype = ctypes.c_int
+    L.moe_kv_ring_write_layer.argtypes = [rp, _i32, P, P, _i32, P]
+    L.moe_kv_ring_commit.restype = ctypes.c_int
+    L.moe_kv_ring_commit.argtypes = [rp, P, _i32, P]
+    L.moe_kv_ring_window.restype = ctypes.c_int
+    L.moe_kv_ring_window.argtypes = [rp, _i32, _i32, P, P, P]
     L.moe_verify_last_error.restype = ctypes.c_char_p
     L.moe_verify_last_error.argtypes = []
     L.moe_verify_version.restype = ctypes.c_int
@@ -552,6 +575,70 @@ def moe_prefill_stack(cfg: moe_cfg, dense: Dict[str, object], layers: Sequence[m
     _check(lib().moe_prefill_stack(ctypes.byref(cfg), ctypes.byref(dw), I, arr, len(layers), px, pr, T, py, py32,
                                    _ptr(dense_y32, torch.float32, "dense_y32", numel=T * cfg.hidden, device=dev),
                                    pw, nw, _stream(stream), ctypes.byref(debug) if debug is not None else None))
+
+
+# ---------------------------------------------------------------------------
+# the sliding-window KV ring of the verify step
+# ---------------------------------------------------------------------------
+
+
+class KvRing:
+    """Device tensors of one sequence's sliding-window KV ring (keys and
+    values bf16 [n_layers, n_kv, capacity, head_dim], the int32 committed
+    length) and the calls on it."""
+
+    def __init__(self, n_layers: int, n_kv: int, head_dim: int, window: int, max_rows: int, device):
+        cap = lib().moe_kv_ring_capacity(window, max_rows)
+        if cap == 0:
+            raise MoEError(MOE_ERR_INVALID, moe_verify_last_error())
+        self.shape = (n_layers, n_kv, cap, head_dim)
+        self.k = torch.zeros(self.shape, dtype=torch.int16, device=device)
+        self.v = torch.zeros(self.shape, dtype=torch.int16, device=device)
+        self.len = torch.zeros(1, dtype=torch.int32, device=device)
+        self.window, self.device = window, self.k.device
+        self.ring = moe_kv_ring(self.k.data_ptr(), self.v.data_ptr(), self.len.data_ptr(), n_layers, n_kv,
+                                head_dim, window, cap)
+
+    def reset(self, length: int = 0, stream=None) -> None:
+        _check(lib().moe_kv_ring_reset(ctypes.byref(self.ring), length, _stream(stream)))
+
+    def write(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
+        """k_new, v_new: bf16 [n_layers, K, n_kv, head_dim]."""
+        L, n_kv, _, D = self.shape
+        if k_new.dim() != 4 or tuple(k_new.shape) != (L, k_new.shape[1], n_kv, D) or v_new.shape != k_new.shape:
+            raise ValueError("k_new/v_new must be [%d, K, %d, %d] (got %s, %s)" % (L, n_kv, D, tuple(k_new.shape),
+                                                                                 tuple(v_new.shape)))
+        K = k_new.shape[1]
+        _check(lib().moe_kv_ring_write(ctypes.byref(self.ring), _ptr(k_new, _BITS16, "k_new", device=self.device),
+                                       _ptr(v_new, _BITS16, "v_new", device=self.device), K, _stream(stream)))
+
+    def write_layer(self, layer: int, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
+        """k_new, v_new: bf16 [K, n_kv, head_dim], the block's rows of one
+        layer."""
+        _, n_kv, _, D = self.shape
+        if k_new.dim() != 3 or tuple(k_new.shape[1:]) != (n_kv, D) or v_new.shape != k_new.shape:
+            raise ValueError("k_new/v_new must be [K, %d, %d] (got %s, %s)" % (n_kv, D, tuple(k_new.shape),
+                                                                             tuple(v_new.shape)))
+        K = k_new.shape[0]
+        _check(lib().moe_kv_ring_write_layer(ctypes.byref(self.ring), layer,
+                                             _ptr(k_new, _BITS16, "k_new", device=self.device),
+                                             _ptr(v_new, _BITS16, "v_new", device=self.device), K, _stream(stream)))
+
+    def commit(self, n_accepted: torch.Tensor, K: int, stream=None) -> None:
+        """n_accepted: device int32 [1] (e.g. the greedy step's count)."""
+        _check(lib().moe_kv_ring_commit(ctypes.byref(self.ring),
+                                        _ptr(n_accepted, torch.int32, "n_accepted", numel=1, device=self.device),
+                                        K, _stream(stream)))
+
+    def window_of(self, layer: int, K: int, stream=None):
+        """(keys, values) bf16 [K, n_kv, window, head_dim]: what each row of
+        the last written block sees of `layer`."""
+        _, n_kv, _, D = self.shape
+        ko = torch.empty(K, n_kv, self.window, D, dtype=torch.int16, device=self.device)
+        vo = torch.empty_like(ko)
+        _check(lib().moe_kv_ring_window(ctypes.byref(self.ring), layer, K, ko.data_ptr(), vo.data_ptr(),
+                                        _stream(stream)))
+        return ko, vo
 
 
 class StackGraph:

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoeverify.so")
-SOURCES = ["moe_kernels.hip", "moe_grouped.hip", "lm_head.hip", "dense.hip", "moe_abi.hip"]
+SOURCES = ["moe_kernels.hip", "moe_grouped.hip", "lm_head.hip", "dense.hip", "kv_ring.hip", "moe_abi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

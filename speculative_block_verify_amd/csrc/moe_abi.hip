@@ -681,6 +681,100 @@ PrefillLayout prefill_layout(const moe_cfg* c, int I) {
 
 }  // namespace
 
+int32_t moe_kv_ring_capacity(int32_t window, int32_t max_rows) {
+    if (window < 1 || max_rows < 1) {
+        fail(MOE_ERR_INVALID, "window=%d and max_rows=%d must be >= 1", window, max_rows);
+        return 0;
+    }
+    return window + max_rows - 1;
+}
+
+size_t moe_kv_ring_bytes(int32_t n_layers, int32_t n_kv, int32_t head_dim, int32_t capacity) {
+    if (n_layers < 1 || n_kv < 1 || head_dim < 1 || capacity < 1) return 0;
+    return (size_t)n_layers * n_kv * capacity * head_dim * 2;
+}
+
+static int check_ring(const moe_kv_ring* r, int K) {
+    if (!r) return fail(MOE_ERR_INVALID, "ring is NULL");
+    if (!r->k || !r->v || !r->len || !aligned16(r->k) || !aligned16(r->v))
+        return fail(MOE_ERR_INVALID, "ring k/v/len NULL or k/v not 16-byte aligned");
+    if (r->n_layers < 1 || r->n_kv < 1 || r->window < 1)
+        return fail(MOE_ERR_INVALID, "ring n_layers=%d n_kv=%d window=%d must be >= 1", r->n_layers, r->n_kv,
+                    r->window);
+    if (r->head_dim < 8 || r->head_dim % 8) return fail(MOE_ERR_INVALID, "head_dim=%d: need a multiple of 8", r->head_dim);
+    if (K < 1) return fail(MOE_ERR_INVALID, "K=%d < 1", K);
+    if (r->capacity < r->window + K - 1)
+        return fail(MOE_ERR_INVALID, "capacity=%d < window + K - 1 = %d: a rollback could lose visible rows",
+                    r->capacity, r->window + K - 1);
+    return MOE_OK;
+}
+
+static moe::KvArgs kv_args(const moe_kv_ring* r, int K) {
+    moe::KvArgs a{};
+    a.k = r->k; a.v = r->v; a.len = r->len;
+    a.L = r->n_layers; a.n_kv = r->n_kv; a.D = r->head_dim; a.W = r->window; a.C = r->capacity; a.K = K;
+    return a;
+}
+
+int moe_kv_ring_reset(const moe_kv_ring* ring, int32_t len, void* stream) {
+    int rc;
+    if ((rc = check_ring(ring, 1))) return rc;
+    if (len < 0) return fail(MOE_ERR_INVALID, "len=%d < 0", len);
+    moe::KvArgs a = kv_args(ring, 1);
+    a.len0 = len;
+    hipError_t e = moe::launch_kv_reset(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "ring reset launch");
+}
+
+static int kv_write(const moe_kv_ring* ring, int layer, int n_layers, const uint16_t* k_new, const uint16_t* v_new,
+                    int K, void* stream) {
+    if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new))
+        return fail(MOE_ERR_INVALID, "k_new/v_new NULL or not 16-byte aligned");
+    moe::KvArgs a = kv_args(ring, K);
+    a.k_new = k_new; a.v_new = v_new; a.layer = layer; a.L = n_layers;
+    hipError_t e = moe::launch_kv_write(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "ring write launch");
+}
+
+int moe_kv_ring_write(const moe_kv_ring* ring, const uint16_t* k_new, const uint16_t* v_new, int32_t K, void* stream) {
+    int rc;
+    if ((rc = check_ring(ring, K))) return rc;
+    return kv_write(ring, 0, ring->n_layers, k_new, v_new, K, stream);
+}
+
+int moe_kv_ring_write_layer(const moe_kv_ring* ring, int32_t layer, const uint16_t* k_new, const uint16_t* v_new,
+                            int32_t K, void* stream) {
+    int rc;
+    if ((rc = check_ring(ring, K))) return rc;
+    if (layer < 0 || layer >= ring->n_layers)
+        return fail(MOE_ERR_INVALID, "layer=%d outside [0, %d)", layer, ring->n_layers);
+    return kv_write(ring, layer, 1, k_new, v_new, K, stream);
+}
+
+int moe_kv_ring_commit(const moe_kv_ring* ring, const int32_t* n_accepted, int32_t K, void* stream) {
+    int rc;
+    if ((rc = check_ring(ring, K))) return rc;
+    if (!n_accepted) return fail(MOE_ERR_INVALID, "n_accepted is NULL");
+    moe::KvArgs a = kv_args(ring, K);
+    a.n_accepted = n_accepted;
+    hipError_t e = moe::launch_kv_commit(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "ring commit launch");
+}
+
+int moe_kv_ring_window(const moe_kv_ring* ring, int32_t layer, int32_t K, uint16_t* k_out, uint16_t* v_out,
+                       void* stream) {
+    int rc;
+    if ((rc = check_ring(ring, K))) return rc;
+    if (layer < 0 || layer >= ring->n_layers)
+        return fail(MOE_ERR_INVALID, "layer=%d outside [0, %d)", layer, ring->n_layers);
+    if (!k_out || !v_out || !aligned16(k_out) || !aligned16(v_out))
+        return fail(MOE_ERR_INVALID, "k_out/v_out NULL or not 16-byte aligned");
+    moe::KvArgs a = kv_args(ring, K);
+    a.layer = layer; a.k_out = k_out; a.v_out = v_out;
+    hipError_t e = moe::launch_kv_window(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "ring window launch");
+}
+
 size_t moe_dense_workspace_bytes(int32_t hidden, int32_t inter, int32_t max_rows) {
     if (check_dense_shape(hidden, inter)) return 0;
     if (max_rows < 1) {

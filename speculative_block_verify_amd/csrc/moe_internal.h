@@ -206,6 +206,23 @@ constexpr int kRouteSpinLimit = 1 << 22;   // polls (with a short sleep each) be
 hipError_t launch_dequant(Fp4Mat m, int n_experts, int rows, int cols, float* out, hipStream_t st);
 hipError_t launch_stream_read(const void* src, size_t n16, uint32_t* sink, hipStream_t st);
 
+// Sliding-window KV ring (kv_ring.hip).
+struct KvArgs {
+    uint16_t* k;                // bf16 [L][n_kv][C][D]
+    uint16_t* v;
+    int32_t* len;               // device [1]: committed length
+    const uint16_t* k_new;      // bf16 [L][K][n_kv][D] (write: layers layer .. layer + L - 1)
+    const uint16_t* v_new;
+    const int32_t* n_accepted;  // device [1] (commit)
+    uint16_t* k_out;            // bf16 [K][n_kv][W][D] (window)
+    uint16_t* v_out;
+    int L, n_kv, D, W, C, K, layer, len0;  // L: layers written by a write (the ring's count otherwise)
+};
+hipError_t launch_kv_write(const KvArgs& a, hipStream_t st);
+hipError_t launch_kv_commit(const KvArgs& a, hipStream_t st);
+hipError_t launch_kv_reset(const KvArgs& a, hipStream_t st);
+hipError_t launch_kv_window(const KvArgs& a, hipStream_t st);
+
 // Dense first layer (dense.hip).
 bool dense_shape_ok(int H, int I);
 size_t dense_workspace_bytes(int H, int I, int T);

@@ -342,3 +342,50 @@ def test_lm_head_argument_errors():
     assert call(logits=FAKE + 4) == api.MOE_ERR_INVALID
     assert call(nb=n - 16) == api.MOE_ERR_WORKSPACE
     assert call(o=api.moe_greedy_out(FAKE, FAKE, None, FAKE, FAKE)) == api.MOE_ERR_INVALID
+
+
+def test_kv_ring_argument_errors():
+    """The ring's sizes and the checks made before any device work."""
+    L = api.lib()
+    P = ctypes.sizeof(ctypes.c_void_p)
+    assert ctypes.sizeof(api.moe_kv_ring) == 3 * P + 5 * 4 + (4 if P == 8 else 0)
+    assert L.moe_kv_ring_capacity(512, 2) == 513
+    assert L.moe_kv_ring_capacity(512, 1) == 512
+    assert L.moe_kv_ring_capacity(0, 2) == 0 and L.moe_kv_ring_capacity(512, 0) == 0
+    # 30 sliding layers x 8 KV heads x 128 x 513 slots, bf16
+    assert L.moe_kv_ring_bytes(30, 8, 128, 513) == 30 * 8 * 128 * 513 * 2
+    assert L.moe_kv_ring_bytes(0, 8, 128, 513) == 0
+
+    def ring(k=FAKE, v=FAKE, ln=FAKE, nl=30, nkv=8, D=128, W=512, C=513):
+        return api.moe_kv_ring(k, v, ln, nl, nkv, D, W, C)
+
+    def write(r=None, K=2, kn=FAKE, vn=FAKE):
+        r = ring() if r is None else r
+        return L.moe_kv_ring_write(ctypes.byref(r), kn, vn, K, None)
+
+    assert L.moe_kv_ring_write(None, FAKE, FAKE, 2, None) == api.MOE_ERR_INVALID
+    assert write(K=0) == api.MOE_ERR_INVALID
+    assert write(K=3) == api.MOE_ERR_INVALID and "capacity" in api.moe_verify_last_error()
+    assert write(r=ring(D=100)) == api.MOE_ERR_INVALID and "head_dim" in api.moe_verify_last_error()
+    assert write(r=ring(D=0)) == api.MOE_ERR_INVALID
+    assert write(r=ring(k=None)) == api.MOE_ERR_INVALID
+    assert write(r=ring(v=FAKE + 8)) == api.MOE_ERR_INVALID
+    assert write(r=ring(ln=None)) == api.MOE_ERR_INVALID
+    assert write(r=ring(nl=0)) == api.MOE_ERR_INVALID
+    assert write(r=ring(W=0)) == api.MOE_ERR_INVALID
+    assert write(kn=None) == api.MOE_ERR_INVALID
+    assert write(vn=FAKE + 2) == api.MOE_ERR_INVALID
+    r = ring()
+    assert L.moe_kv_ring_write_layer(ctypes.byref(r), 30, FAKE, FAKE, 2, None) == api.MOE_ERR_INVALID
+    assert L.moe_kv_ring_write_layer(ctypes.byref(r), -1, FAKE, FAKE, 2, None) == api.MOE_ERR_INVALID
+    assert L.moe_kv_ring_write_layer(ctypes.byref(r), 0, FAKE, None, 2, None) == api.MOE_ERR_INVALID
+    assert L.moe_kv_ring_write_layer(ctypes.byref(r), 0, FAKE, FAKE, 3, None) == api.MOE_ERR_INVALID
+    assert L.moe_kv_ring_commit(ctypes.byref(r), None, 2, None) == api.MOE_ERR_INVALID
+    assert L.moe_kv_ring_commit(ctypes.byref(r), FAKE, 3, None) == api.MOE_ERR_INVALID
+    assert L.moe_kv_ring_reset(ctypes.byref(r), -1, None) == api.MOE_ERR_INVALID
+    assert L.moe_kv_ring_window(ctypes.byref(r), 30, 2, FAKE, FAKE, None) == api.MOE_ERR_INVALID
+    assert L.moe_kv_ring_window(ctypes.byref(r), -1, 2, FAKE, FAKE, None) == api.MOE_ERR_INVALID
+    assert L.moe_kv_ring_window(ctypes.byref(r), 0, 2, None, FAKE, None) == api.MOE_ERR_INVALID
+    assert L.moe_kv_ring_window(ctypes.byref(r), 0, 2, FAKE, FAKE + 4, None) == api.MOE_ERR_INVALID
+    with pytest.raises(api.MoEError):
+        api.KvRing(30, 8, 128, 0, 2, "cpu")
