@@ -485,18 +485,22 @@ __global__ __launch_bounds__(kBlock, 2) void k_gateup_grouped(GroupedGuArgs a, f
 // ---------------------------------------------------------------------------
 // grouped down
 //
-// Work item: (tile, group of G 64-row slabs of the output dimension).  The
-// tile's h rows are staged in LDS once per item as hi = fp16(h * 2^-sigma)
-// and lo = fp16(h * 2^-sigma - hi), sigma per token such that its max |h|
-// maps into [2^14, 2^15); staged rows span NSB whole superblocks, zero past
-// the row's length, stride NSB*256 + 8 halfs.  Then the item walks its
-// slabs: wave w computes output rows slab*64 + 16w .. +15 for the tile's
-// tokens; lane (i, kb) holds the codes of row n0 + i at columns
+// Work unit: (tile, 64-row slab of the output dimension), numbered tile by
+// tile.  The workgroups are persistent, one launch-wide round of them, and
+// each takes an equal contiguous run of units, so no workgroup waits on a
+// partial last round; a run is one or two segments of consecutive slabs of
+// one tile.  A segment stages the tile's h rows in LDS once, as
+// hi = fp16(h * 2^-sigma) and lo = fp16(h * 2^-sigma - hi), sigma per token
+// such that its max |h| maps into [2^14, 2^15); staged rows span NSB whole
+// superblocks, zero past the row's length, stride NSB*256 + 8 halfs.  Then
+// it walks its slabs: wave w computes output rows slab*64 + 16w .. +15 for
+// the tile's tokens; lane (i, kb) holds the codes of row n0 + i at columns
 // [sb*256 + kb*64, +64) of every superblock, and the next slab's codes are
 // in flight while the current slab is on the matrix cores.
 // ---------------------------------------------------------------------------
 
 constexpr int kGMaxSb = kGMaxCols / kSbCols;  // superblocks of the longest staged h row
+
 
 template <int NSB>
 struct DownCodes {
@@ -504,7 +508,7 @@ struct DownCodes {
     uint32_t sc[NSB];
 };
 
-template <int NSB, int G>
+template <int NSB>
 __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedDownArgs a, const float* hmax, const float* hmax_sh) {
     extern __shared__ __align__(16) _Float16 hb[];  // hi [32][S], then lo [32][S]
     __shared__ int s_sig[kGChunk];
@@ -516,13 +520,16 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedDownArgs a, cons
     const int H = a.H, I = a.I, Is = a.Is, T = a.T, kk = a.k;
     _Float16* hi = hb;
     _Float16* lo = hb + kGChunk * S;
-    const int nG = H / (kGRows * G), lgG = __builtin_ctz(nG);  // slab groups per tile (a power of two)
+    const int nS = H / kGRows;  // output slabs per tile
     const int n_tiles = *a.n_tiles;
     const int n_sh = dq_s ? (T + kGChunk - 1) / kGChunk : 0;
     const int n_rt = n_tiles - n_sh;
-    const int items = n_tiles * nG;
-    for (int it = blockIdx.x; it < items; it += gridDim.x) {
-        const int ti = it >> lgG, grp = it & (nG - 1);
+    const int units = n_tiles * nS;
+    const int u_end = (int)((long long)units * (blockIdx.x + 1) / gridDim.x);
+    for (int u = (int)((long long)units * blockIdx.x / gridDim.x); u < u_end;) {
+        const int ti = u / nS, s_lo = u - ti * nS;
+        const int n_seg = min(nS - s_lo, u_end - u);  // slabs s_lo .. s_lo + n_seg - 1 of tile ti
+        u += n_seg;
         const bool routed = ti < n_rt;
         const int4 tl = reinterpret_cast<const int4*>(a.tiles)[ti];
         const int e = routed ? tl.x : 0, p0 = tl.y, cnt = tl.z;
@@ -532,10 +539,10 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedDownArgs a, cons
         const uint8_t* ms = (routed ? ds_r : ds_s) + (size_t)e * H * (cols / 16);
         const float ts = (routed ? dts_r : dts_s)[e];
 
-        // codes of slab g of this item (loads at clamped columns past the
-        // row's length: their products meet the zero columns of the staged h)
+        // codes of slab s_lo + g (loads at clamped columns past the row's
+        // length: their products meet the zero columns of the staged h)
         auto load_codes = [&](int g, DownCodes<NSB>& c) {
-            const size_t row = (size_t)((grp * G + g) * kGRows + wave * 16 + i);
+            const size_t row = (size_t)((s_lo + g) * kGRows + wave * 16 + i);
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
                 const int col = min(sb * kSbCols + kb * 64, cols - 64);
@@ -545,7 +552,7 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedDownArgs a, cons
                 c.sc[sb] = *reinterpret_cast<const uint32_t*>(ms + row * (cols / 16) + col / 16);
             }
         };
-        // The item's loads in the order they are consumed (vector loads
+        // The segment's loads in the order they are consumed (vector loads
         // complete in issue order): max |h| entries, the tile's h rows, then
         // the codes of the first slab.  Entry (token m, slab sl) of max |h|
         // goes to thread 16m + sl of each half of the workgroup (clamped).
@@ -633,7 +640,7 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedDownArgs a, cons
                 }
             }
             // lane (j, q) holds output rows n0 + 4q .. +3 of token j
-            const int n0 = (grp * G + g) * kGRows + wave * 16;
+            const int n0 = (s_lo + g) * kGRows + wave * 16;
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const int m = tt * 16 + j;
@@ -652,13 +659,13 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedDownArgs a, cons
         // (the last slab's codes again at the end, an L2 hit) so the compiler
         // keeps an exact count of loads in flight
 #pragma unroll 1
-        for (int g = 0; g < G; g += 2) {
-            load_codes(g + 1 < G ? g + 1 : G - 1, cB);
+        for (int g = 0; g < n_seg; g += 2) {
+            load_codes(g + 1 < n_seg ? g + 1 : n_seg - 1, cB);
             compute(g, cA);
-            load_codes(g + 2 < G ? g + 2 : G - 1, cA);
-            if (g + 1 < G) compute(g + 1, cB);
+            load_codes(g + 2 < n_seg ? g + 2 : n_seg - 1, cA);
+            if (g + 1 < n_seg) compute(g + 1, cB);
         }
-        __syncthreads();  // staged rows and s_sig are replaced by the next item
+        __syncthreads();  // staged rows and s_sig are replaced by the next segment
     }
 }
 
@@ -781,7 +788,6 @@ size_t group_lds(int T, int E) { return (size_t)E * ((T + 31) / 32) * (group_pc_
 // superblocks of the longest staged h row, and the grouped down kernel's
 // output slabs per work item
 int down_nsb(int I, int Is) { return ((I > Is ? I : Is) + kSbCols - 1) / kSbCols; }
-int down_g(int H) { return H >= 8 * kGRows ? 8 : 4; }
 size_t down_lds(int I, int Is) {
     const int nsb = down_nsb(I, Is);
     return (size_t)2 * kGChunk * ((nsb == 3 ? 4 : nsb) * kSbCols + 8) * 2;
@@ -802,20 +808,30 @@ bool grouped_lds_fits(int T, int E, int I, int Is) {
            (size_t)kWaves * E * 4 <= (size_t)kMaxDynLds;
 }
 
+// persistent down workgroups per staged-row width (1, 2, 4 superblocks):
+// one round of resident workgroups, from the occupancy query at set-up
+static int g_down_grid[3] = {512, 512, 256};
+
 hipError_t init_grouped_kernels() {
     hipError_t e;
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_group),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, kGroupMaxLds)) != hipSuccess)
         return e;
-    const void* downs[] = {reinterpret_cast<const void*>(k_down_grouped<1, 4>),
-                           reinterpret_cast<const void*>(k_down_grouped<2, 4>),
-                           reinterpret_cast<const void*>(k_down_grouped<4, 4>),
-                           reinterpret_cast<const void*>(k_down_grouped<1, 8>),
-                           reinterpret_cast<const void*>(k_down_grouped<2, 8>),
-                           reinterpret_cast<const void*>(k_down_grouped<4, 8>)};
+    const void* downs[] = {reinterpret_cast<const void*>(k_down_grouped<1>),
+                           reinterpret_cast<const void*>(k_down_grouped<2>),
+                           reinterpret_cast<const void*>(k_down_grouped<4>)};
     for (const void* f : downs)
         if ((e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kGDownMaxLds)) != hipSuccess)
             return e;
+    int dev = 0, ncu = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    for (int v = 0; v < 3; ++v) {
+        int nb = 0;
+        const size_t lds = (size_t)2 * kGChunk * ((1 << v) * kSbCols + 8) * 2;
+        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, downs[v], kBlock, lds)) != hipSuccess) return e;
+        g_down_grid[v] = (nb > 0 ? nb : 1) * (ncu > 0 ? ncu : 1);
+    }
     return hipSuccess;
 }
 
@@ -860,20 +876,17 @@ hipError_t launch_gateup_grouped(const GroupedGuArgs& a, float* hmax, float* hma
 
 hipError_t launch_down_grouped(const GroupedDownArgs& a, const float* hmax, const float* hmax_sh, int max_tiles,
                                hipStream_t st) {
-    const int G = down_g(a.H), nsb = down_nsb(a.I, a.Is);
-    long long items = (long long)max_tiles * (a.H / (kGRows * G));
-    const int grid = (int)(items < kGMaxGrid ? items : kGMaxGrid);
+    const int nsb = down_nsb(a.I, a.Is);
+    // one round of persistent workgroups (two per compute unit fit the
+    // staged h and the registers), never more than there are units
+    const long long units = (long long)max_tiles * (a.H / kGRows);
+    const int resident = g_down_grid[nsb == 1 ? 0 : nsb == 2 ? 1 : 2];
+    const int grid = (int)(units < resident ? units : resident);
     const dim3 g(grid), b(kBlock);
     const size_t lds = down_lds(a.I, a.Is);
-    if (G == 8) {
-        if (nsb == 1) hipLaunchKernelGGL((k_down_grouped<1, 8>), g, b, lds, st, a, hmax, hmax_sh);
-        else if (nsb == 2) hipLaunchKernelGGL((k_down_grouped<2, 8>), g, b, lds, st, a, hmax, hmax_sh);
-        else hipLaunchKernelGGL((k_down_grouped<4, 8>), g, b, lds, st, a, hmax, hmax_sh);
-    } else {
-        if (nsb == 1) hipLaunchKernelGGL((k_down_grouped<1, 4>), g, b, lds, st, a, hmax, hmax_sh);
-        else if (nsb == 2) hipLaunchKernelGGL((k_down_grouped<2, 4>), g, b, lds, st, a, hmax, hmax_sh);
-        else hipLaunchKernelGGL((k_down_grouped<4, 4>), g, b, lds, st, a, hmax, hmax_sh);
-    }
+    if (nsb == 1) hipLaunchKernelGGL((k_down_grouped<1>), g, b, lds, st, a, hmax, hmax_sh);
+    else if (nsb == 2) hipLaunchKernelGGL((k_down_grouped<2>), g, b, lds, st, a, hmax, hmax_sh);
+    else hipLaunchKernelGGL((k_down_grouped<4>), g, b, lds, st, a, hmax, hmax_sh);
     return hipGetLastError();
 }
 
