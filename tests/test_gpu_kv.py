@@ -177,3 +177,22 @@ def test_a_step_replays_in_a_graph():
                                       ek.transpose(1, 0, 2)[:, 1:], err_msg="replay %d" % rep)
         np.testing.assert_array_equal(vo.cpu().numpy().view(np.uint16)[0][:, :-1],
                                       ev.transpose(1, 0, 2)[:, 1:], err_msg="replay %d" % rep)
+
+
+def test_commit_clamps_the_acceptance_count():
+    """A count outside [0, K - 1] read on the device is clamped: a negative
+    one keeps row 0 only, one of K or more keeps the whole block."""
+    say("case: kv ring commit clamp")
+    K = 3
+    ring = api.KvRing(1, 1, 8, 4, K, DEV)
+    ring.reset(5)
+    kn = torch.zeros(1, K, 1, 8, dtype=torch.int16, device=DEV)
+    nacc = torch.zeros(1, dtype=torch.int32, device=DEV)
+    expect = 5
+    for a, kept in ((-7, 1), (99, K), (K - 1, K), (0, 1), (K, K)):
+        ring.write(kn, kn)
+        nacc.fill_(a)
+        ring.commit(nacc, K)
+        expect += kept
+        torch.cuda.synchronize()
+        assert int(ring.len.item()) == expect, (a, kept)
