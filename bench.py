@@ -180,7 +180,7 @@ def prefill(args):
     from speculative_block_verify_amd import api, inputs
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    shape, T, NL, POOL, SEED = inputs.LAGUNA, 512, args.prefill_layers, 4, 4096
+    shape, T, NL, POOL, SEED = inputs.LAGUNA, 512, args.prefill_layers, 8, 4096
     layers = inputs.gen_stack(shape, NL, SEED, device=dev)
     xs = [inputs.gen_x(T, shape.hidden, SEED + 1 + i, device=dev) for i in range(POOL)]
     cfg = api.make_cfg(shape, T)

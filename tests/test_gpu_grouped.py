@@ -123,6 +123,18 @@ def test_grouped_layer_no_shared_expert():
     _layer(inputs.MoEShape(512, 32, 4, 256, 0), 50, 9, label="no shared")
 
 
+@pytest.mark.parametrize("shape,K", [
+    # hidden 1024 (four gate/up superblocks), intermediate and shared 1024:
+    # the down kernel stages 4-superblock rows, one workgroup per compute unit
+    (inputs.MoEShape(1024, 64, 4, 1024, 1024), 40),
+    # hidden 2048, intermediate 1024 with a shorter shared expert (512): rows
+    # of two lengths in the same staged tile width
+    (inputs.MoEShape(2048, 128, 8, 1024, 512), 24),
+])
+def test_grouped_layer_wide_intermediate(shape, K):
+    _layer(shape, K, 60 + K, label="wide I=%d Is=%d" % (shape.inter, shape.shared_inter))
+
+
 def test_grouped_layer_correlated_rows_span_several_tiles():
     # rows 1..K/2 are row 0 plus small noise: their experts get ~40+ tokens
     # each, so one expert spans two or three 32-token tiles with a ragged tail
