@@ -403,6 +403,12 @@ MOE_API int moe_prefill_stack(const moe_cfg* cfg, const moe_dense_weights* dense
  * least window + K - 1 (moe_kv_ring_capacity), so no position that a row of
  * the block, or of the next block after any rollback, can see is ever
  * overwritten.  No host round trip: a step is graph-capturable.
+ *
+ * Ownership: the caller allocates k, v and len (moe_kv_ring_bytes each for
+ * k and v) and keeps them alive while work on the ring is queued; the
+ * library holds no pointer after a call returns.  A ring's calls are
+ * ordered by the stream they are queued on: calls on different streams that
+ * overlap race on its length and slots.
  * ------------------------------------------------------------------------ */
 typedef struct moe_kv_ring {
     uint16_t* k;       /* bf16 [n_layers][n_kv][capacity][head_dim], device */
