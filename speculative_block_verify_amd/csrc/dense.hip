@@ -14,8 +14,8 @@
 //                   (+ residual), y32 and bf16 y, and the next layer's input
 //                   bf16(gamma * y / sqrt(mean(y^2) + eps)).
 //
-// Tiles.  A workgroup covers 64 rows (tokens) x 64 output columns; wave w
-// owns columns [16 w, 16 w + 16).  The weight rows are the MFMA A operand,
+// Tiles.  A workgroup covers 16 * NTT rows (tokens: 128 for prefill-sized
+// calls, 64 below) x 64 output columns; wave w owns columns [16 w, 16 w + 16).  The weight rows are the MFMA A operand,
 // read from global memory into registers one pipeline step ahead (lane
 // (i, kb) holds 16 consecutive k values of weight row i); the token rows are
 // the B operand, staged in LDS (double-buffered) and shared by the four
@@ -28,7 +28,6 @@ namespace moe {
 
 typedef __bf16 dense_bf16x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kDT = 64;                 // tokens per workgroup tile
 constexpr int kDN = 64;                 // output columns per workgroup tile (4 waves x 16)
 constexpr int kDK = 64;                 // k per pipeline step (2 MFMA k-blocks of 32)
 constexpr int kDXStride = kDK + 8;      // LDS row stride in bf16 elements (144 B)
@@ -53,23 +52,26 @@ struct DenseArgs {
 
 __device__ __forceinline__ dense_bf16x8_t as_bf8(uint4 v) { return __builtin_bit_cast(dense_bf16x8_t, v); }
 
-// Stage a 64-token x 64-k tile of a bf16 row-major [T][ld] matrix into LDS
-// rows of kDXStride (tokens past T read row T - 1; never stored later):
-// every thread moves two 16-byte pieces.
-__device__ __forceinline__ void dense_tile_load(const uint16_t* src, int ld, int t0, int T, int k0, uint4 (&v)[2]) {
+// Stage a (16 * NTT)-token x 64-k tile of a bf16 row-major [T][ld] matrix
+// into LDS rows of kDXStride (tokens past T read row T - 1; never stored
+// later): every thread moves NTT / 2 16-byte pieces.
+template <int NTT>
+__device__ __forceinline__ void dense_tile_load(const uint16_t* src, int ld, int t0, int T, int k0,
+                                                uint4 (&v)[NTT / 2]) {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int f = tid + p * kBlock;        // 512 pieces: 64 rows x 8 pieces of 8 bf16
+    for (int p = 0; p < NTT / 2; ++p) {
+        const int f = tid + p * kBlock;        // 16 * NTT rows x 8 pieces of 8 bf16
         const int r = f >> 3, c = (f & 7) * 8;
         const int t = min(t0 + r, T - 1);
         v[p] = *reinterpret_cast<const uint4*>(src + (size_t)t * ld + k0 + c);
     }
 }
-__device__ __forceinline__ void dense_tile_store(uint16_t* lds, const uint4 (&v)[2]) {
+template <int NTT>
+__device__ __forceinline__ void dense_tile_store(uint16_t* lds, const uint4 (&v)[NTT / 2]) {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int p = 0; p < NTT / 2; ++p) {
         const int f = tid + p * kBlock;
         const int r = f >> 3, c = (f & 7) * 8;
         *reinterpret_cast<uint4*>(lds + r * kDXStride + c) = v[p];
@@ -92,9 +94,11 @@ __device__ __forceinline__ dense_bf16x8_t dense_b(const uint16_t* lds, int tt, i
 }
 
 // ---------------------------------------------------------------------------
-// gate/up + SwiGLU.  Grid: (I / 64, ceil(T / 64)).
+// gate/up + SwiGLU.  Grid: (I / 64, ceil(T / (16 * NTT))).
 // ---------------------------------------------------------------------------
+template <int NTT>
 __global__ __launch_bounds__(kBlock) void k_dense_gateup(DenseArgs a) {
+    constexpr int kDT = 16 * NTT;
     __shared__ __align__(16) uint16_t xs[2][kDT * kDXStride];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int i = lane & 15, q = lane >> 4;
@@ -102,41 +106,41 @@ __global__ __launch_bounds__(kBlock) void k_dense_gateup(DenseArgs a) {
     const int t0 = blockIdx.y * kDT;
     const int u0 = blockIdx.x * kDN + wave * 16;  // this wave's 16 units
     const int nsteps = H / kDK;
-    f32x4_t accg[4], accu[4];
+    f32x4_t accg[NTT], accu[NTT];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) accg[tt] = accu[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < NTT; ++tt) accg[tt] = accu[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    uint4 gcur[2], ucur[2], gnext[2], unext[2], xv[2];
+    uint4 gcur[2], ucur[2], gnext[2], unext[2], xv[NTT / 2];
     dense_w_load(a.wg, H, u0 + i, 0, gcur);
     dense_w_load(a.wu, H, u0 + i, 0, ucur);
-    dense_tile_load(a.x, H, t0, T, 0, xv);
-    dense_tile_store(xs[0], xv);
+    dense_tile_load<NTT>(a.x, H, t0, T, 0, xv);
+    dense_tile_store<NTT>(xs[0], xv);
     __syncthreads();
     for (int step = 0; step < nsteps; ++step) {
         // the next step's operands in flight (the last step re-reads its own)
         const int kn = min(step + 1, nsteps - 1) * kDK;
         dense_w_load(a.wg, H, u0 + i, kn, gnext);
         dense_w_load(a.wu, H, u0 + i, kn, unext);
-        dense_tile_load(a.x, H, t0, T, kn, xv);
+        dense_tile_load<NTT>(a.x, H, t0, T, kn, xv);
         const uint16_t* xb = xs[step & 1];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const dense_bf16x8_t ag = as_bf8(gcur[s]), au = as_bf8(ucur[s]);
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
+            for (int tt = 0; tt < NTT; ++tt) {
                 const dense_bf16x8_t b = dense_b(xb, tt, s);
                 accg[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, b, accg[tt], 0, 0, 0);
                 accu[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, b, accu[tt], 0, 0, 0);
             }
         }
-        dense_tile_store(xs[(step + 1) & 1], xv);
+        dense_tile_store<NTT>(xs[(step + 1) & 1], xv);
         __syncthreads();
         gcur[0] = gnext[0]; gcur[1] = gnext[1];
         ucur[0] = unext[0]; ucur[1] = unext[1];
     }
     // lane (j = i, q) holds units u0 + 4q .. +3 of token t0 + 16 tt + j
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < NTT; ++tt) {
         const int t = t0 + tt * 16 + i;
         if (t >= T) continue;
         uint32_t hi2[2], lo2[2];
@@ -161,9 +165,11 @@ __global__ __launch_bounds__(kBlock) void k_dense_gateup(DenseArgs a) {
 
 // ---------------------------------------------------------------------------
 // down: partial y of one slice of the intermediate dimension.
-// Grid: (H / 64, ceil(T / 64), kDenseSplitK).
+// Grid: (H / 64, ceil(T / (16 * NTT)), kDenseSplitK).
 // ---------------------------------------------------------------------------
+template <int NTT>
 __global__ __launch_bounds__(kBlock) void k_dense_down(DenseArgs a) {
+    constexpr int kDT = 16 * NTT;
     __shared__ __align__(16) uint16_t hs[2][2][kDT * kDXStride];  // [buffer][hi, lo]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int i = lane & 15, q = lane >> 4;
@@ -172,41 +178,41 @@ __global__ __launch_bounds__(kBlock) void k_dense_down(DenseArgs a) {
     const int n0 = blockIdx.x * kDN + wave * 16;  // this wave's 16 output columns
     const int slice = I / kDenseSplitK, kbase = blockIdx.z * slice;
     const int nsteps = slice / kDK;
-    f32x4_t acc[4];
+    f32x4_t acc[NTT];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < NTT; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    uint4 wcur[2], wnext[2], hv[2], lv[2];
+    uint4 wcur[2], wnext[2], hv[NTT / 2], lv[NTT / 2];
     dense_w_load(a.wd, I, n0 + i, kbase, wcur);
-    dense_tile_load(a.h_hi, I, t0, T, kbase, hv);
-    dense_tile_load(a.h_lo, I, t0, T, kbase, lv);
-    dense_tile_store(hs[0][0], hv);
-    dense_tile_store(hs[0][1], lv);
+    dense_tile_load<NTT>(a.h_hi, I, t0, T, kbase, hv);
+    dense_tile_load<NTT>(a.h_lo, I, t0, T, kbase, lv);
+    dense_tile_store<NTT>(hs[0][0], hv);
+    dense_tile_store<NTT>(hs[0][1], lv);
     __syncthreads();
     for (int step = 0; step < nsteps; ++step) {
         const int kn = kbase + min(step + 1, nsteps - 1) * kDK;
         dense_w_load(a.wd, I, n0 + i, kn, wnext);
-        dense_tile_load(a.h_hi, I, t0, T, kn, hv);
-        dense_tile_load(a.h_lo, I, t0, T, kn, lv);
+        dense_tile_load<NTT>(a.h_hi, I, t0, T, kn, hv);
+        dense_tile_load<NTT>(a.h_lo, I, t0, T, kn, lv);
         const uint16_t* hb = hs[step & 1][0];
         const uint16_t* lb = hs[step & 1][1];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const dense_bf16x8_t aw = as_bf8(wcur[s]);
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
+            for (int tt = 0; tt < NTT; ++tt) {
                 acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, dense_b(hb, tt, s), acc[tt], 0, 0, 0);
                 acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, dense_b(lb, tt, s), acc[tt], 0, 0, 0);
             }
         }
-        dense_tile_store(hs[(step + 1) & 1][0], hv);
-        dense_tile_store(hs[(step + 1) & 1][1], lv);
+        dense_tile_store<NTT>(hs[(step + 1) & 1][0], hv);
+        dense_tile_store<NTT>(hs[(step + 1) & 1][1], lv);
         __syncthreads();
         wcur[0] = wnext[0]; wcur[1] = wnext[1];
     }
     float* part = a.part + (size_t)blockIdx.z * T * H;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < NTT; ++tt) {
         const int t = t0 + tt * 16 + i;
         if (t < T)
             *reinterpret_cast<float4*>(part + (size_t)t * H + n0 + 4 * q) =
@@ -283,12 +289,23 @@ hipError_t launch_dense_mlp(const uint16_t* x, int T, int H, int I, const uint16
     a.y32 = y32; a.y = y; a.x_next = x_next;
     a.eps = eps;
     a.T = T; a.H = H; a.I = I;
-    const int tt = (T + kDT - 1) / kDT;
-    hipLaunchKernelGGL(k_dense_gateup, dim3(I / kDN, tt), dim3(kBlock), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_dense_down, dim3(H / kDN, tt, kDenseSplitK), dim3(kBlock), 0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // 128-token tiles above 64 rows (each weight row loaded once per 128
+    // tokens), 64-token tiles below
+    if (T > 64) {
+        const int tt = (T + 127) / 128;
+        hipLaunchKernelGGL(k_dense_gateup<8>, dim3(I / kDN, tt), dim3(kBlock), 0, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_dense_down<8>, dim3(H / kDN, tt, kDenseSplitK), dim3(kBlock), 0, st, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+        hipLaunchKernelGGL(k_dense_gateup<4>, dim3(I / kDN, 1), dim3(kBlock), 0, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_dense_down<4>, dim3(H / kDN, 1, kDenseSplitK), dim3(kBlock), 0, st, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipError_t e;
     hipLaunchKernelGGL(k_dense_finish, dim3(T), dim3(kBlock), 0, st, a);
     return hipGetLastError();
 }
