@@ -221,6 +221,199 @@ __global__ __launch_bounds__(kBlock) void k_dense_down(DenseArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Prefill-sized calls (256 rows and more): 128-token x 128-column tiles on
+// eight waves, both operands staged through a three-stage LDS ring by
+// direct global-to-LDS loads (no registers hold a tile in flight).
+//
+// A stage is 48 KB: 48 blocks of 1 KB, each filled by one wave instruction
+// (lane l's 16 bytes at byte 16 l of the block); wave w fills blocks
+// 6w .. 6w + 5, so every wave has exactly kRingLoads loads per stage in
+// flight and a wait for "all but the newest stage" is vmcnt(kRingLoads).
+// Tiles are rows of 64 k values (8 pieces of 16 bytes); piece p of row r
+// sits at position p ^ (r & 7) of its row, so the 16 rows an MFMA operand
+// read touches spread over the banks.
+// gate/up stage: x [128 tokens] then gate [128 units] then up [128 units].
+// down stage:    h hi [128 tokens], h lo [128 tokens], then down [128 rows].
+// ---------------------------------------------------------------------------
+
+constexpr int kRingStages = 3;
+constexpr int kRingRows = 384;                    // rows of 64 k per stage
+constexpr int kRingStageBytes = kRingRows * 128;  // 48 KB
+constexpr int kRingLdsBytes = kRingStages * kRingStageBytes;
+constexpr int kRingThreads = 512;                 // 8 waves
+constexpr int kRingLoads = kRingStageBytes / 1024 / (kRingThreads / 64);  // per wave per stage: 6
+constexpr int kRingSplitK = 4;                    // down: slices of the intermediate dimension
+
+// s_waitcnt with only the vector-memory count limited (to n <= 63)
+#define DENSE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// Issue this wave's loads of one stage: block c of the stage holds rows
+// 8c .. 8c + 7; row_src(r) gives the global row (64 k values from k0).
+template <typename RowSrc>
+__device__ __forceinline__ void ring_issue(unsigned char* stage, int k0, RowSrc&& row_src) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int b = 0; b < kRingLoads; ++b) {
+        const int c = wave * kRingLoads + b;
+        const int r = c * 8 + (lane >> 3), pos = lane & 7;
+        const uint16_t* src = row_src(r) + k0 + ((pos ^ (r & 7)) << 3);
+        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)(stage + c * 1024), 16, 0, 0);
+    }
+}
+
+// MFMA operand: 8 k values (piece p) of stage row r
+__device__ __forceinline__ dense_bf16x8_t ring_piece(const unsigned char* stage, int r, int p) {
+    return *reinterpret_cast<const dense_bf16x8_t*>(stage + r * 128 + ((p ^ (r & 7)) << 4));
+}
+
+// gate/up + SwiGLU.  Grid: (I / 128, ceil(T / 128)).  Wave w: tokens
+// 64 (w >> 2) .. +63, units 32 (w & 3) .. +31 of the tile.
+__global__ __launch_bounds__(kRingThreads) void k_dense_gateup_ring(DenseArgs a) {
+    extern __shared__ __align__(16) unsigned char ring[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i = lane & 15, kb = lane >> 4;
+    const int H = a.H, I = a.I, T = a.T;
+    const int t0 = blockIdx.y * 128, u0 = blockIdx.x * 128;
+    const int tw = (wave >> 2) * 64, uw = (wave & 3) * 32;
+    const int nsteps = H / 64;
+    auto row_src = [&](int r) -> const uint16_t* {
+        const uint16_t* base = r < 128 ? a.x : (r < 256 ? a.wg : a.wu);
+        const int row = r < 128 ? min(t0 + r, T - 1) : u0 + (r & 127);
+        return base + (size_t)row * H;
+    };
+    f32x4_t accg[2][4], accu[2][4];
+#pragma unroll
+    for (int us = 0; us < 2; ++us)
+#pragma unroll
+        for (int ts = 0; ts < 4; ++ts) accg[us][ts] = accu[us][ts] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    ring_issue(ring, 0, row_src);
+    ring_issue(ring + kRingStageBytes, min(1, nsteps - 1) * 64, row_src);
+    for (int step = 0; step < nsteps; ++step) {
+        // this wave's part of this stage has landed (the next stage may still
+        // be in flight); the barrier (no memory fence: that would wait for
+        // every stage) makes every wave's part visible, and frees the slot
+        // refilled below (each wave's reads of it finished in the last step)
+        DENSE_WAIT_VM(kRingLoads);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);  // no load or LDS read moves above the barrier
+        ring_issue(ring + ((step + 2) % kRingStages) * kRingStageBytes, min(step + 2, nsteps - 1) * 64, row_src);
+        const unsigned char* st = ring + (step % kRingStages) * kRingStageBytes;
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk) {
+            const int p = kbk * 4 + kb;
+            dense_bf16x8_t ag[2], au[2], bx[4];
+#pragma unroll
+            for (int us = 0; us < 2; ++us) {
+                ag[us] = ring_piece(st, 128 + uw + us * 16 + i, p);
+                au[us] = ring_piece(st, 256 + uw + us * 16 + i, p);
+            }
+#pragma unroll
+            for (int ts = 0; ts < 4; ++ts) bx[ts] = ring_piece(st, tw + ts * 16 + i, p);
+#pragma unroll
+            for (int us = 0; us < 2; ++us)
+#pragma unroll
+                for (int ts = 0; ts < 4; ++ts) {
+                    accg[us][ts] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag[us], bx[ts], accg[us][ts], 0, 0, 0);
+                    accu[us][ts] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au[us], bx[ts], accu[us][ts], 0, 0, 0);
+                }
+        }
+    }
+    DENSE_WAIT_VM(0);  // the trailing (repeated) stages' loads are done before the workgroup ends
+    // lane (j = i, q = kb) holds units 4q .. 4q + 3 of its 16-unit block, token 16 ts + j
+#pragma unroll
+    for (int us = 0; us < 2; ++us)
+#pragma unroll
+        for (int ts = 0; ts < 4; ++ts) {
+            const int t = t0 + tw + ts * 16 + i;
+            if (t >= T) continue;
+            uint32_t hi2[2], lo2[2];
+#pragma unroll
+            for (int e = 0; e < 4; e += 2) {
+                uint16_t hb[2], lb[2];
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    const float g = accg[us][ts][e + d], u = accu[us][ts][e + d];
+                    const float h = g / (1.0f + expf(-g)) * u;
+                    hb[d] = f32_to_bf16_rne(h);
+                    lb[d] = f32_to_bf16_rne(h - bf16_to_f32(hb[d]));
+                }
+                hi2[e / 2] = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
+                lo2[e / 2] = (uint32_t)lb[0] | ((uint32_t)lb[1] << 16);
+            }
+            const size_t o = (size_t)t * I + u0 + uw + us * 16 + 4 * kb;
+            *reinterpret_cast<uint2*>(a.h_hi + o) = make_uint2(hi2[0], hi2[1]);
+            *reinterpret_cast<uint2*>(a.h_lo + o) = make_uint2(lo2[0], lo2[1]);
+        }
+}
+
+// down: partial y of one slice of the intermediate dimension.
+// Grid: (H / 128, ceil(T / 128), kRingSplitK).  Wave w: tokens 64 (w >> 2)
+// .. +63, output columns 32 (w & 3) .. +31 of the tile.
+__global__ __launch_bounds__(kRingThreads) void k_dense_down_ring(DenseArgs a) {
+    extern __shared__ __align__(16) unsigned char ring[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i = lane & 15, kb = lane >> 4;
+    const int H = a.H, I = a.I, T = a.T;
+    const int t0 = blockIdx.y * 128, n0 = blockIdx.x * 128;
+    const int tw = (wave >> 2) * 64, nw = (wave & 3) * 32;
+    const int slice = I / kRingSplitK, kbase = blockIdx.z * slice;
+    const int nsteps = slice / 64;
+    auto row_src = [&](int r) -> const uint16_t* {
+        const uint16_t* base = r < 128 ? a.h_hi : (r < 256 ? a.h_lo : a.wd);
+        const int row = r < 256 ? min(t0 + (r & 127), T - 1) : n0 + (r & 127);
+        return base + (size_t)row * I;
+    };
+    f32x4_t acc[2][4];
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+        for (int ts = 0; ts < 4; ++ts) acc[ns][ts] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    ring_issue(ring, kbase, row_src);
+    ring_issue(ring + kRingStageBytes, kbase + min(1, nsteps - 1) * 64, row_src);
+    for (int step = 0; step < nsteps; ++step) {
+        DENSE_WAIT_VM(kRingLoads);  // as in k_dense_gateup_ring
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        ring_issue(ring + ((step + 2) % kRingStages) * kRingStageBytes, kbase + min(step + 2, nsteps - 1) * 64,
+                   row_src);
+        const unsigned char* st = ring + (step % kRingStages) * kRingStageBytes;
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk) {
+            const int p = kbk * 4 + kb;
+            dense_bf16x8_t aw[2], bh[4], bl[4];
+#pragma unroll
+            for (int ns = 0; ns < 2; ++ns) aw[ns] = ring_piece(st, 256 + nw + ns * 16 + i, p);
+#pragma unroll
+            for (int ts = 0; ts < 4; ++ts) {
+                bh[ts] = ring_piece(st, tw + ts * 16 + i, p);
+                bl[ts] = ring_piece(st, 128 + tw + ts * 16 + i, p);
+            }
+#pragma unroll
+            for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+                for (int ts = 0; ts < 4; ++ts) {
+                    acc[ns][ts] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[ns], bh[ts], acc[ns][ts], 0, 0, 0);
+                    acc[ns][ts] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[ns], bl[ts], acc[ns][ts], 0, 0, 0);
+                }
+        }
+    }
+    DENSE_WAIT_VM(0);
+    float* part = a.part + (size_t)blockIdx.z * T * H;
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+        for (int ts = 0; ts < 4; ++ts) {
+            const int t = t0 + tw + ts * 16 + i;
+            if (t < T)
+                *reinterpret_cast<float4*>(part + (size_t)t * H + n0 + nw + ns * 16 + 4 * kb) =
+                    make_float4(acc[ns][ts][0], acc[ns][ts][1], acc[ns][ts][2], acc[ns][ts][3]);
+        }
+}
+
+// ---------------------------------------------------------------------------
 // finish: one workgroup per row.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kBlock) void k_dense_finish(DenseArgs a) {
@@ -265,6 +458,8 @@ __global__ __launch_bounds__(kBlock) void k_dense_finish(DenseArgs a) {
 // launcher and sizes
 // ---------------------------------------------------------------------------
 
+static_assert(kRingSplitK == kDenseSplitK, "the finish kernel sums kDenseSplitK partial slices");
+
 bool dense_shape_ok(int H, int I) {
     return H >= kDN && H % kDN == 0 && H <= 2048 && I >= kDenseSplitK * kDK && I % (kDenseSplitK * kDK) == 0 &&
            I % kDN == 0;
@@ -289,9 +484,27 @@ hipError_t launch_dense_mlp(const uint16_t* x, int T, int H, int I, const uint16
     a.y32 = y32; a.y = y; a.x_next = x_next;
     a.eps = eps;
     a.T = T; a.H = H; a.I = I;
-    // 128-token tiles above 64 rows (each weight row loaded once per 128
-    // tokens), 64-token tiles below
-    if (T > 64) {
+    // prefill-sized calls: the LDS-ring kernels (128 x 128 tiles, one
+    // workgroup per compute unit); 128-token tiles above 64 rows (each
+    // weight row loaded once per 128 tokens), 64-token tiles below
+    static const hipError_t ring_attr = [] {
+        hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(k_dense_gateup_ring),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kRingLdsBytes);
+        if (r == hipSuccess)
+            r = hipFuncSetAttribute(reinterpret_cast<const void*>(k_dense_down_ring),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, kRingLdsBytes);
+        return r;
+    }();
+    if (T >= 256 && H % 128 == 0 && I % 128 == 0) {
+        if (ring_attr != hipSuccess) return ring_attr;
+        const int tt = (T + 127) / 128;
+        hipLaunchKernelGGL(k_dense_gateup_ring, dim3(I / 128, tt), dim3(kRingThreads), kRingLdsBytes, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_dense_down_ring, dim3(H / 128, tt, kRingSplitK), dim3(kRingThreads), kRingLdsBytes, st,
+                           a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else if (T > 64) {
         const int tt = (T + 127) / 128;
         hipLaunchKernelGGL(k_dense_gateup<8>, dim3(I / kDN, tt), dim3(kBlock), 0, st, a);
         hipError_t e = hipGetLastError();

@@ -59,9 +59,10 @@ def _dense_case(T, H, I, seed, residual, gamma):
 
 
 @pytest.mark.parametrize("T,H,I", [(1, 256, 512), (5, 256, 512), (64, 512, 1024), (130, 256, 768),
-                                   (17, 2048, 256)])
+                                   (17, 2048, 256), (300, 256, 512), (257, 512, 1024)])
 def test_dense_layer_shapes(T, H, I):
-    # one row, a ragged token tile, several tiles, several column tiles
+    # one row, a ragged token tile, several tiles, several column tiles; from
+    # 256 rows the 128 x 128 LDS-ring kernels, with a ragged last tile
     _dense_case(T, H, I, 10 + T, residual=(T % 2 == 1), gamma=(T > 5))
 
 
