@@ -227,8 +227,8 @@ __global__ __launch_bounds__(kBlock) void k_dense_down(DenseArgs a) {
 //
 // A stage is 48 KB: 48 blocks of 1 KB, each filled by one wave instruction
 // (lane l's 16 bytes at byte 16 l of the block); wave w fills blocks
-// 6w .. 6w + 5, so every wave has exactly kRingLoads loads per stage in
-// flight and a wait for "all but the newest stage" is vmcnt(kRingLoads).
+// 6w .. 6w + 5, so every wave has exactly Ring::Loads loads per stage in
+// flight and a wait for "all but the newest stage" is vmcnt(Ring::Loads).
 // Tiles are rows of 64 k values (8 pieces of 16 bytes); piece p of row r
 // sits at position p ^ (r & 7) of its row, so the 16 rows an MFMA operand
 // read touches spread over the banks.
@@ -237,46 +237,59 @@ __global__ __launch_bounds__(kBlock) void k_dense_down(DenseArgs a) {
 // ---------------------------------------------------------------------------
 
 constexpr int kRingStages = 3;
-constexpr int kRingRows = 384;                    // rows of 64 k per stage
-constexpr int kRingStageBytes = kRingRows * 128;  // 48 KB
-constexpr int kRingLdsBytes = kRingStages * kRingStageBytes;
+constexpr int kRingRows = 384;                    // rows per stage
 constexpr int kRingThreads = 512;                 // 8 waves
-constexpr int kRingLoads = kRingStageBytes / 1024 / (kRingThreads / 64);  // per wave per stage: 6
 constexpr int kRingSplitK = 4;                    // down: slices of the intermediate dimension
+// Ring geometry for a k step of KS (64: 48 KB stages, one workgroup per
+// compute unit; 32 would give 24 KB stages and two, but more steps and
+// barriers: slower): RB bytes per row, PP 16-byte pieces per row, and each
+// wave's loads per stage.
+template <int KS>
+struct Ring {
+    static constexpr int RB = KS * 2, PP = KS / 8;
+    static constexpr int StageBytes = kRingRows * RB;
+    static constexpr int LdsBytes = kRingStages * StageBytes;
+    static constexpr int Loads = StageBytes / 1024 / (kRingThreads / 64);
+};
 
 // s_waitcnt with only the vector-memory count limited (to n <= 63)
 #define DENSE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 // Issue this wave's loads of one stage: block c of the stage holds rows
-// 8c .. 8c + 7; row_src(r) gives the global row (64 k values from k0).
-template <typename RowSrc>
+// c * (1024 / RB) ..; row_src(r) gives the global row (KS k values from k0).
+template <int KS, typename RowSrc>
 __device__ __forceinline__ void ring_issue(unsigned char* stage, int k0, RowSrc&& row_src) {
+    using G = Ring<KS>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int b = 0; b < kRingLoads; ++b) {
-        const int c = wave * kRingLoads + b;
-        const int r = c * 8 + (lane >> 3), pos = lane & 7;
-        const uint16_t* src = row_src(r) + k0 + ((pos ^ (r & 7)) << 3);
+    for (int b = 0; b < G::Loads; ++b) {
+        const int c = wave * G::Loads + b;
+        const int r = c * (1024 / G::RB) + lane / G::PP, pos = lane % G::PP;
+        const uint16_t* src = row_src(r) + k0 + ((pos ^ (r & (G::PP - 1))) << 3);
         __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
                                          (__attribute__((address_space(3))) void*)(stage + c * 1024), 16, 0, 0);
     }
 }
 
 // MFMA operand: 8 k values (piece p) of stage row r
+template <int KS>
 __device__ __forceinline__ dense_bf16x8_t ring_piece(const unsigned char* stage, int r, int p) {
-    return *reinterpret_cast<const dense_bf16x8_t*>(stage + r * 128 + ((p ^ (r & 7)) << 4));
+    using G = Ring<KS>;
+    return *reinterpret_cast<const dense_bf16x8_t*>(stage + r * G::RB + ((p ^ (r & (G::PP - 1))) << 4));
 }
 
 // gate/up + SwiGLU.  Grid: (I / 128, ceil(T / 128)).  Wave w: tokens
 // 64 (w >> 2) .. +63, units 32 (w & 3) .. +31 of the tile.
+template <int KS>
 __global__ __launch_bounds__(kRingThreads) void k_dense_gateup_ring(DenseArgs a) {
+    using G = Ring<KS>;
     extern __shared__ __align__(16) unsigned char ring[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int i = lane & 15, kb = lane >> 4;
     const int H = a.H, I = a.I, T = a.T;
     const int t0 = blockIdx.y * 128, u0 = blockIdx.x * 128;
     const int tw = (wave >> 2) * 64, uw = (wave & 3) * 32;
-    const int nsteps = H / 64;
+    const int nsteps = H / KS;
     auto row_src = [&](int r) -> const uint16_t* {
         const uint16_t* base = r < 128 ? a.x : (r < 256 ? a.wg : a.wu);
         const int row = r < 128 ? min(t0 + r, T - 1) : u0 + (r & 127);
@@ -288,29 +301,29 @@ __global__ __launch_bounds__(kRingThreads) void k_dense_gateup_ring(DenseArgs a)
 #pragma unroll
         for (int ts = 0; ts < 4; ++ts) accg[us][ts] = accu[us][ts] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    ring_issue(ring, 0, row_src);
-    ring_issue(ring + kRingStageBytes, min(1, nsteps - 1) * 64, row_src);
+    ring_issue<KS>(ring, 0, row_src);
+    ring_issue<KS>(ring + G::StageBytes, min(1, nsteps - 1) * KS, row_src);
     for (int step = 0; step < nsteps; ++step) {
         // this wave's part of this stage has landed (the next stage may still
         // be in flight); the barrier (no memory fence: that would wait for
         // every stage) makes every wave's part visible, and frees the slot
         // refilled below (each wave's reads of it finished in the last step)
-        DENSE_WAIT_VM(kRingLoads);
+        DENSE_WAIT_VM(G::Loads);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);  // no load or LDS read moves above the barrier
-        ring_issue(ring + ((step + 2) % kRingStages) * kRingStageBytes, min(step + 2, nsteps - 1) * 64, row_src);
-        const unsigned char* st = ring + (step % kRingStages) * kRingStageBytes;
+        ring_issue<KS>(ring + ((step + 2) % kRingStages) * G::StageBytes, min(step + 2, nsteps - 1) * KS, row_src);
+        const unsigned char* st = ring + (step % kRingStages) * G::StageBytes;
 #pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk) {
+        for (int kbk = 0; kbk < KS / 32; ++kbk) {
             const int p = kbk * 4 + kb;
             dense_bf16x8_t ag[2], au[2], bx[4];
 #pragma unroll
             for (int us = 0; us < 2; ++us) {
-                ag[us] = ring_piece(st, 128 + uw + us * 16 + i, p);
-                au[us] = ring_piece(st, 256 + uw + us * 16 + i, p);
+                ag[us] = ring_piece<KS>(st, 128 + uw + us * 16 + i, p);
+                au[us] = ring_piece<KS>(st, 256 + uw + us * 16 + i, p);
             }
 #pragma unroll
-            for (int ts = 0; ts < 4; ++ts) bx[ts] = ring_piece(st, tw + ts * 16 + i, p);
+            for (int ts = 0; ts < 4; ++ts) bx[ts] = ring_piece<KS>(st, tw + ts * 16 + i, p);
 #pragma unroll
             for (int us = 0; us < 2; ++us)
 #pragma unroll
@@ -351,7 +364,9 @@ __global__ __launch_bounds__(kRingThreads) void k_dense_gateup_ring(DenseArgs a)
 // down: partial y of one slice of the intermediate dimension.
 // Grid: (H / 128, ceil(T / 128), kRingSplitK).  Wave w: tokens 64 (w >> 2)
 // .. +63, output columns 32 (w & 3) .. +31 of the tile.
+template <int KS>
 __global__ __launch_bounds__(kRingThreads) void k_dense_down_ring(DenseArgs a) {
+    using G = Ring<KS>;
     extern __shared__ __align__(16) unsigned char ring[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int i = lane & 15, kb = lane >> 4;
@@ -359,7 +374,7 @@ __global__ __launch_bounds__(kRingThreads) void k_dense_down_ring(DenseArgs a) {
     const int t0 = blockIdx.y * 128, n0 = blockIdx.x * 128;
     const int tw = (wave >> 2) * 64, nw = (wave & 3) * 32;
     const int slice = I / kRingSplitK, kbase = blockIdx.z * slice;
-    const int nsteps = slice / 64;
+    const int nsteps = slice / KS;
     auto row_src = [&](int r) -> const uint16_t* {
         const uint16_t* base = r < 128 ? a.h_hi : (r < 256 ? a.h_lo : a.wd);
         const int row = r < 256 ? min(t0 + (r & 127), T - 1) : n0 + (r & 127);
@@ -371,25 +386,25 @@ __global__ __launch_bounds__(kRingThreads) void k_dense_down_ring(DenseArgs a) {
 #pragma unroll
         for (int ts = 0; ts < 4; ++ts) acc[ns][ts] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    ring_issue(ring, kbase, row_src);
-    ring_issue(ring + kRingStageBytes, kbase + min(1, nsteps - 1) * 64, row_src);
+    ring_issue<KS>(ring, kbase, row_src);
+    ring_issue<KS>(ring + G::StageBytes, kbase + min(1, nsteps - 1) * KS, row_src);
     for (int step = 0; step < nsteps; ++step) {
-        DENSE_WAIT_VM(kRingLoads);  // as in k_dense_gateup_ring
+        DENSE_WAIT_VM(G::Loads);  // as in k_dense_gateup_ring
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        ring_issue(ring + ((step + 2) % kRingStages) * kRingStageBytes, kbase + min(step + 2, nsteps - 1) * 64,
-                   row_src);
-        const unsigned char* st = ring + (step % kRingStages) * kRingStageBytes;
+        ring_issue<KS>(ring + ((step + 2) % kRingStages) * G::StageBytes, kbase + min(step + 2, nsteps - 1) * KS,
+                       row_src);
+        const unsigned char* st = ring + (step % kRingStages) * G::StageBytes;
 #pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk) {
+        for (int kbk = 0; kbk < KS / 32; ++kbk) {
             const int p = kbk * 4 + kb;
             dense_bf16x8_t aw[2], bh[4], bl[4];
 #pragma unroll
-            for (int ns = 0; ns < 2; ++ns) aw[ns] = ring_piece(st, 256 + nw + ns * 16 + i, p);
+            for (int ns = 0; ns < 2; ++ns) aw[ns] = ring_piece<KS>(st, 256 + nw + ns * 16 + i, p);
 #pragma unroll
             for (int ts = 0; ts < 4; ++ts) {
-                bh[ts] = ring_piece(st, tw + ts * 16 + i, p);
-                bl[ts] = ring_piece(st, 128 + tw + ts * 16 + i, p);
+                bh[ts] = ring_piece<KS>(st, tw + ts * 16 + i, p);
+                bl[ts] = ring_piece<KS>(st, 128 + tw + ts * 16 + i, p);
             }
 #pragma unroll
             for (int ns = 0; ns < 2; ++ns)
@@ -487,22 +502,24 @@ hipError_t launch_dense_mlp(const uint16_t* x, int T, int H, int I, const uint16
     // prefill-sized calls: the LDS-ring kernels (128 x 128 tiles, one
     // workgroup per compute unit); 128-token tiles above 64 rows (each
     // weight row loaded once per 128 tokens), 64-token tiles below
+    constexpr int KS = 64;
+    using G = Ring<KS>;
     static const hipError_t ring_attr = [] {
-        hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(k_dense_gateup_ring),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kRingLdsBytes);
+        hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(k_dense_gateup_ring<KS>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, G::LdsBytes);
         if (r == hipSuccess)
-            r = hipFuncSetAttribute(reinterpret_cast<const void*>(k_dense_down_ring),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, kRingLdsBytes);
+            r = hipFuncSetAttribute(reinterpret_cast<const void*>(k_dense_down_ring<KS>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, G::LdsBytes);
         return r;
     }();
     if (T >= 256 && H % 128 == 0 && I % 128 == 0) {
         if (ring_attr != hipSuccess) return ring_attr;
         const int tt = (T + 127) / 128;
-        hipLaunchKernelGGL(k_dense_gateup_ring, dim3(I / 128, tt), dim3(kRingThreads), kRingLdsBytes, st, a);
+        hipLaunchKernelGGL(k_dense_gateup_ring<KS>, dim3(I / 128, tt), dim3(kRingThreads), G::LdsBytes, st, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_dense_down_ring, dim3(H / 128, tt, kRingSplitK), dim3(kRingThreads), kRingLdsBytes, st,
-                           a);
+        hipLaunchKernelGGL(k_dense_down_ring<KS>, dim3(H / 128, tt, kRingSplitK), dim3(kRingThreads), G::LdsBytes,
+                           st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     } else if (T > 64) {
         const int tt = (T + 127) / 128;
