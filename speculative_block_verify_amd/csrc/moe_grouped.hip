@@ -181,13 +181,15 @@ __host__ __device__ inline bool group_pc_fits(int T, int E) {
 // k_group: CSR + tile list (one workgroup of kGGroupThreads)
 //
 // A row never selects an expert twice, so expert e's slots are one per row
-// that picked it, in row order.  rm[e][w] is the bitmap of those rows:
-//   count(e) = popcount(rm[e][*]),
-//   rank of slot (r, j) inside its expert = popcount of rm[e] below bit r.
+// that picked it, in row order.  rm[w][e] is the bitmap of those rows
+// (word w covers rows 32w .. 32w + 31; stored word-major, so the experts'
+// threads read consecutive words):
+//   count(e) = popcount(rm[*][e]),
+//   rank of slot (r, j) inside its expert = popcount of rm[.][e] below bit r.
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(kGGroupThreads) void k_group(GroupArgs a) {
-    // [E][W] row bitmaps, then (when group_pc_fits) [E][W] 16-bit prefix
+    // [W][E] row bitmaps, then (when group_pc_fits) [W][E] 16-bit prefix
     // popcounts: slots of expert e in rows below word w
     extern __shared__ uint32_t rm[];
     __shared__ int s_cstart[kMaxExperts];
@@ -217,7 +219,7 @@ __global__ __launch_bounds__(kGGroupThreads) void k_group(GroupArgs a) {
         const int s = tid + i * kGGroupThreads;
         if (s < n) {
             const int r = s / k;
-            atomicOr(&rm[expert_of(i, s) * W + (r >> 5)], 1u << (r & 31));
+            atomicOr(&rm[(r >> 5) * E + expert_of(i, s)], 1u << (r & 31));
         }
     }
     __syncthreads();
@@ -226,8 +228,8 @@ __global__ __launch_bounds__(kGGroupThreads) void k_group(GroupArgs a) {
     int c = 0;
     if (tid < E)
         for (int w = 0; w < W; ++w) {
-            if (use_pc) pc[tid * W + w] = (uint16_t)c;
-            c += __builtin_popcount(rm[tid * W + w]);
+            if (use_pc) pc[w * E + tid] = (uint16_t)c;
+            c += __builtin_popcount(rm[w * E + tid]);
         }
     const int f = c > 0, nt = (c + kGChunk - 1) / kGChunk;
     const int ci = wave_incl_scan(c), fi = wave_incl_scan(f), ti = wave_incl_scan(nt);
@@ -276,12 +278,12 @@ __global__ __launch_bounds__(kGGroupThreads) void k_group(GroupArgs a) {
         const int s = tid + i * kGGroupThreads;
         if (s < n) {
             const int e = expert_of(i, s), r = s / k;
-            const uint32_t* m = rm + e * W;
-            int rank = __builtin_popcount(m[r >> 5] & ((1u << (r & 31)) - 1u));
+            const uint32_t* m = rm + e;  // word w at m[w * E]
+            int rank = __builtin_popcount(m[(r >> 5) * E] & ((1u << (r & 31)) - 1u));
             if (use_pc) {
-                rank += pc[e * W + (r >> 5)];
+                rank += pc[(r >> 5) * E + e];
             } else {
-                for (int w = 0; w < (r >> 5); ++w) rank += __builtin_popcount(m[w]);
+                for (int w = 0; w < (r >> 5); ++w) rank += __builtin_popcount(m[w * E]);
             }
             const int pos = s_cstart[e] + rank;
             if (use_lds_asg) s_asg[pos] = s;
