@@ -14,8 +14,15 @@
 //                   (+ residual), y32 and bf16 y, and the next layer's input
 //                   bf16(gamma * y / sqrt(mean(y^2) + eps)).
 //
-// Tiles.  A workgroup covers 16 * NTT rows (tokens: 128 for prefill-sized
-// calls, 64 below) x 64 output columns; wave w owns columns [16 w, 16 w + 16).  The weight rows are the MFMA A operand,
+// Three tile regimes, one arithmetic (the same products summed in fp32 in
+// the same k order within a 64-wide step):
+//   256 rows and more: k_dense_gateup_ring / k_dense_down_ring, 128 x 128
+//     tiles on eight waves with both operands in a three-stage LDS ring
+//     (described at those kernels);
+//   65 .. 255 rows: 128-token x 64-column tiles (NTT = 8);
+//   up to 64 rows: 64-token x 64-column tiles (NTT = 4).
+// In the two register-staged regimes a workgroup covers 16 * NTT rows
+// (tokens) x 64 output columns; wave w owns columns [16 w, 16 w + 16).  The weight rows are the MFMA A operand,
 // read from global memory into registers one pipeline step ahead (lane
 // (i, kb) holds 16 consecutive k values of weight row i); the token rows are
 // the B operand, staged in LDS (double-buffered) and shared by the four
@@ -535,7 +542,6 @@ hipError_t launch_dense_mlp(const uint16_t* x, int T, int H, int I, const uint16
         hipLaunchKernelGGL(k_dense_down<4>, dim3(H / kDN, 1, kDenseSplitK), dim3(kBlock), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipError_t e;
     hipLaunchKernelGGL(k_dense_finish, dim3(T), dim3(kBlock), 0, st, a);
     return hipGetLastError();
 }

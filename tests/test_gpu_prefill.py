@@ -138,9 +138,10 @@ def _prefill_case(shape, dense_inter, T, n_moe, seed, residual, gamma, rows=None
         err, len(reps), int(alive.sum()), len(sel), max(r["max_abs_over_max_ref"] for r in reps)))
 
 
-@pytest.mark.parametrize("T", [17, 40])
+@pytest.mark.parametrize("T", [17, 40, 300])
 def test_prefill_stack_tiny_all_rows(T):
-    # grouped MoE kernels (more than 16 rows), norm weights, residual stream
+    # grouped MoE kernels (more than 16 rows), norm weights, residual stream;
+    # 300 rows: the dense layer's LDS-ring kernels with a ragged last tile
     _prefill_case(TINY_SH, 512, T, 3, 20 + T, residual=True, gamma=True, label="tiny")
 
 
