@@ -14,8 +14,9 @@
 //                   (+ residual), y32 and bf16 y, and the next layer's input
 //                   bf16(gamma * y / sqrt(mean(y^2) + eps)).
 //
-// Three tile regimes, one arithmetic (the same products summed in fp32 in
-// the same k order within a 64-wide step):
+// Three tile regimes (each deterministic; they group the k values of a
+// 64-wide step into MFMA blocks differently, so their fp32 sums may differ
+// in the last bits):
 //   256 rows and more: k_dense_gateup_ring / k_dense_down_ring, 128 x 128
 //     tiles on eight waves with both operands in a three-stage LDS ring
 //     (described at those kernels);
