@@ -352,13 +352,7 @@ int enqueue_layer_grouped(const moe_cfg* c, const moe_layer_weights* w, const ui
     sa.score_fn = c->score_fn; sa.norm_topk = c->norm_topk;
     if ((e = moe::launch_select_rows(sa, st)) != hipSuccess) return hip_fail(e, "row selection launch");
 
-    moe::GroupArgs ka{};
-    ka.ids = L.ids; ka.n_unique = n_unique; ka.uniq = L.uniq; ka.off = L.off; ka.asg = L.asg; ka.inv = L.inv;
-    ka.tiles = L.tiles; ka.n_tiles = n_tiles;
-    ka.status = L.meta + moe::kMetaStatus;
-    ka.T = K; ka.E = c->n_experts; ka.k = c->top_k; ka.has_shared = has_sh;
-    if ((e = moe::launch_group(ka, st)) != hipSuccess) return hip_fail(e, "grouping launch");
-
+    // the gate/up workgroups group the slots themselves (and publish the CSR)
     const int max_tiles = moe::grouped_max_tiles(K, c->n_experts, c->top_k, has_sh);
     moe::GroupedGuArgs ga{};
     ga.x = L.xh;
@@ -366,9 +360,12 @@ int enqueue_layer_grouped(const moe_cfg* c, const moe_layer_weights* w, const ui
     ga.gate = mat(w->gate); ga.up = mat(w->up);
     ga.sgate = has_sh ? mat(w->sh_gate) : none;
     ga.sup = has_sh ? mat(w->sh_up) : none;
-    ga.uniq = L.uniq; ga.off = L.off; ga.asg = L.asg; ga.tiles = L.tiles; ga.n_tiles = n_tiles;
+    ga.ids = L.ids;
+    ga.n_unique = n_unique; ga.uniq = L.uniq; ga.off = L.off; ga.asg = L.asg; ga.inv = L.inv;
+    ga.tiles = L.tiles; ga.n_tiles = n_tiles;
+    ga.status = L.meta + moe::kMetaStatus;
     ga.h = L.h; ga.h_sh = L.h_sh;
-    ga.T = K; ga.H = c->hidden; ga.I = c->inter; ga.Is = c->shared_inter; ga.k = c->top_k;
+    ga.T = K; ga.H = c->hidden; ga.I = c->inter; ga.Is = c->shared_inter; ga.k = c->top_k; ga.E = c->n_experts;
     if ((e = moe::launch_gateup_grouped(ga, L.hmax, L.hmax_sh, max_tiles, st)) != hipSuccess)
         return hip_fail(e, "grouped gate/up launch");
 

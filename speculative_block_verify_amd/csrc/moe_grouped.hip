@@ -6,12 +6,15 @@
 // Per layer, after the router GEMV on the matrix cores (k_router_mfma):
 //   k_select_rows   top-k and mixture weights, one wave per row (the same
 //                   selection code as the verify-width path);
-//   k_group         one workgroup: the canonical CSR of the T*k slots by
-//                   expert (unique experts ascending, slots ascending) from
-//                   per-expert row bitmaps, and a tile list of up to 32
+//   k_gateup_grouped  every workgroup first groups the T*k slots itself in
+//                   LDS: the canonical CSR by expert (unique experts
+//                   ascending, slots ascending), a tile list of up to 32
 //                   consecutive slots of one expert (plus the shared
-//                   expert's 32-token tiles);
-//   k_gateup_grouped  (tile, 64 intermediate rows) work items on the matrix
+//                   expert's 32-token tiles) and its own tiles' token rows,
+//                   from counts, prefix sums and row bitmaps of the slot
+//                   ids; workgroup 0 publishes the CSR and the tile list for
+//                   the down and combine kernels.  Then (tile, 64
+//                   intermediate rows) work items on the matrix
 //                   cores: FP4 codes decoded in registers to fp16 times their
 //                   E4M3 scale (exact), x columns staged in LDS as fp16 (the
 //                   router's copy, x * 2^-sig per row, undone in the epilogue),
@@ -178,7 +181,9 @@ __host__ __device__ inline bool group_pc_fits(int T, int E) {
 }
 
 // ---------------------------------------------------------------------------
-// k_group: CSR + tile list (one workgroup of kGGroupThreads)
+// k_group: CSR + tile list (one workgroup of kGGroupThreads), for the
+// routing-only entry point at grouped row counts (a layer groups inside its
+// gate/up kernel)
 //
 // A row never selects an expert twice, so expert e's slots are one per row
 // that picked it, in row order.  rm[w][e] is the bitmap of those rows
@@ -340,6 +345,30 @@ __device__ __forceinline__ void gg_mfma_sb(const GuSb& r, const _Float16* xb, in
     }
 }
 
+// The set-up's grouping tables, in the x double buffer before its first use:
+// per expert its slot count, first CSR position and first routed tile, and
+// the local index of the experts this workgroup's items need; then, for
+// those experts, the bitmap of the rows that selected each (word w covers
+// rows 32w .. 32w + 31) and the set bits in the words below each word.
+constexpr int kGuWords = kMaxGroupedRows / 32;
+constexpr int kGuIdRegs = 16;  // slot ids per thread kept in registers through the set-up
+constexpr size_t kGuGroupLds = (size_t)4 * kMaxExperts * 4 + 4 + (size_t)kGuMaxItems * kGuWords * 6;
+
+// Bit position of the r-th set bit of v (r < popcount(v)).
+__device__ __forceinline__ int nth_set_bit(uint32_t v, int r) {
+    int pos = 0;
+#pragma unroll
+    for (int b = 16; b > 0; b >>= 1) {
+        const int c = __builtin_popcount(v & ((1u << b) - 1u));
+        if (r >= c) {
+            r -= c;
+            v >>= b;
+            pos += b;
+        }
+    }
+    return pos;
+}
+
 template <int NSB>
 __global__ __launch_bounds__(kBlock, 2) void k_gateup_grouped(GroupedGuArgs a, float* hmax, float* hmax_sh) {
     constexpr int H = NSB * kSbCols;
@@ -349,49 +378,146 @@ __global__ __launch_bounds__(kBlock, 2) void k_gateup_grouped(GroupedGuArgs a, f
     constexpr int RING = NSB < 4 ? NSB : 4;
     constexpr int XL = NSB < 2 ? 1 : 2;
     __shared__ __align__(16) _Float16 xb[2][kGChunk * kGXStride];
+    static_assert(sizeof(xb) >= kGuGroupLds, "the grouping tables live in the x buffer during the set-up");
     __shared__ int s_tok[kGuMaxItems][kGChunk];
     __shared__ int s_tsig[kGuMaxItems][kGChunk];  // each token's x row exponent (the fp16 copy is x * 2^-sig)
     __shared__ int4 s_item[kGuMaxItems];   // {expert or -1 (shared), first asg position, tokens, slab}
     __shared__ float2 s_ts[kGuMaxItems];   // gate and up tensor scales
     __shared__ float s_max[kWaves][kGChunk];
+    __shared__ int s_wsum[kWaves][3];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int j = lane & 15, q = lane >> 4;
     const uint8_t *const gq_r = a.gate.q, *const gs_r = a.gate.s, *const uq_r = a.up.q, *const us_r = a.up.s;
     const uint8_t *const gq_s = a.sgate.q, *const gs_s = a.sgate.s, *const uq_s = a.sup.q, *const us_s = a.sup.s;
-    const int I = a.I, Is = a.Is, kk = a.k;
+    const int T = a.T, E = a.E, I = a.I, Is = a.Is, kk = a.k, n = T * kk, W = (T + 31) >> 5;
     const int nI = I / kGRows, nIs = max(Is / kGRows, 1);
-    const int n_tiles = *a.n_tiles;
-    const int n_sh = gq_s ? (a.T + kGChunk - 1) / kGChunk : 0;
-    const int n_rt = n_tiles - n_sh;
-    const int items = n_rt * nI + n_sh * nIs;
     const int G = gridDim.x;
+
+    // ---- set-up: the canonical CSR of the T*k slots by expert (experts
+    // ascending, an expert's slots in row order) and the tile list of up to
+    // kGChunk consecutive slots of one expert, as counts and prefix sums in
+    // LDS.  A row never selects an expert twice, so an expert's slots are
+    // one per row that picked it.
+    int* g_cnt = reinterpret_cast<int*>(&xb[0][0]);  // [E] slots per expert
+    int* g_cs = g_cnt + E;                            // [E] first CSR position
+    int* g_ts = g_cs + E;                             // [E] first routed tile
+    int* g_map = g_ts + E;                            // [E] local index (kGuMaxItems: none)
+    uint32_t* g_bm = reinterpret_cast<uint32_t*>(g_map + E);                 // [kGuMaxItems][W]
+    uint16_t* g_wp = reinterpret_cast<uint16_t*>(g_bm + kGuMaxItems * W);   // [kGuMaxItems][W]
+    int ev[kGuIdRegs];
+#pragma unroll
+    for (int i = 0; i < kGuIdRegs; ++i) {
+        const int s = tid + i * kBlock;
+        ev[i] = s < n ? a.ids[s] : 0;
+    }
+    // f(slot, expert) over this thread's slots tid, tid + kBlock, ...
+    auto for_slots = [&](auto&& f) {
+#pragma unroll
+        for (int i = 0; i < kGuIdRegs; ++i) {
+            const int s = tid + i * kBlock;
+            if (s < n) f(s, ev[i]);
+        }
+        for (int s = tid + kGuIdRegs * kBlock; s < n; s += kBlock) f(s, a.ids[s]);
+    };
+    for (int e = tid; e < E; e += kBlock) {
+        g_cnt[e] = 0;
+        g_map[e] = kGuMaxItems;
+    }
+    __syncthreads();
+    for_slots([&](int, int e) { atomicAdd(&g_cnt[e], 1); });
+    __syncthreads();
+    // exclusive prefix sums over experts of the slot count, of the used flag
+    // and of the tile count; each thread owns Q consecutive experts
+    const int Q = (E + kBlock - 1) / kBlock;
+    {
+        int c = 0, f = 0, nt = 0;
+        for (int u = 0; u < Q; ++u) {
+            const int e = tid * Q + u;
+            if (e < E) {
+                const int ce = g_cnt[e];
+                c += ce;
+                f += ce > 0;
+                nt += (ce + kGChunk - 1) / kGChunk;
+            }
+        }
+        const int ci = wave_incl_scan(c), fi = wave_incl_scan(f), ti = wave_incl_scan(nt);
+        if (lane == 63) {
+            s_wsum[wave][0] = ci;
+            s_wsum[wave][1] = fi;
+            s_wsum[wave][2] = ti;
+        }
+        __syncthreads();
+        int cs = ci - c, fs = fi - f, tsn = ti - nt;
+        for (int w = 0; w < wave; ++w) {
+            cs += s_wsum[w][0];
+            fs += s_wsum[w][1];
+            tsn += s_wsum[w][2];
+        }
+        int4* tiles = reinterpret_cast<int4*>(a.tiles);
+        const bool pub = blockIdx.x == 0;  // workgroup 0 publishes the per-expert outputs
+        for (int u = 0; u < Q; ++u) {
+            const int e = tid * Q + u;
+            if (e < E) {
+                const int ce = g_cnt[e], nte = (ce + kGChunk - 1) / kGChunk;
+                g_cs[e] = cs;
+                g_ts[e] = tsn;
+                if (pub && ce) {
+                    a.uniq[fs] = e;
+                    a.off[fs] = cs;
+                    for (int t = 0; t < nte; ++t)
+                        tiles[tsn + t] = make_int4(e, cs + t * kGChunk, min(kGChunk, ce - t * kGChunk), 0);
+                }
+                cs += ce;
+                fs += ce > 0;
+                tsn += nte;
+            }
+        }
+    }
+    int n_rt = 0, U = 0;
+    for (int w = 0; w < kWaves; ++w) {
+        U += s_wsum[w][1];
+        n_rt += s_wsum[w][2];
+    }
+    const int n_sh = gq_s ? (T + kGChunk - 1) / kGChunk : 0;
+    if (blockIdx.x == 0 && tid == 0) {
+        int4* tiles = reinterpret_cast<int4*>(a.tiles);
+        *a.n_unique = U;
+        a.off[U] = n;
+        for (int t = 0; t < n_sh; ++t) tiles[n_rt + t] = make_int4(-1, t * kGChunk, min(kGChunk, T - t * kGChunk), 0);
+        *a.n_tiles = n_rt + n_sh;
+        if (a.status) *a.status = 0;
+    }
+    const int items = n_rt * nI + n_sh * nIs;
     // this workgroup's items: blockIdx.x + k * G for k < n_my (<= kGuMaxItems by launch)
     const int n_my = items > (int)blockIdx.x ? min((items - 1 - (int)blockIdx.x) / G + 1, kGuMaxItems) : 0;
     if (n_my == 0) return;
 
-    // every item's descriptor, tensor scales and token rows into LDS up
-    // front: later lookups are LDS reads, never waits behind weight loads
+    // every item's descriptor into LDS (tensor scales into registers, stored
+    // once the first loads of the stream are out); a routed tile index ti
+    // belongs to the last expert whose first tile is at or below ti
+    float2 tsv = make_float2(0.f, 0.f);
     if (tid < n_my) {
         const int it = blockIdx.x + tid * G;
-        const bool routed = it < n_rt * nI;
-        const int ti = routed ? it / nI : n_rt + (it - n_rt * nI) / nIs;
-        const int slab = routed ? it % nI : (it - n_rt * nI) % nIs;
-        const int4 tl = reinterpret_cast<const int4*>(a.tiles)[ti];
-        const int e = routed ? tl.x : -1;
-        s_item[tid] = make_int4(e, tl.y, tl.z, slab);
-        s_ts[tid] = routed ? make_float2(a.gate.ts[e], a.up.ts[e]) : make_float2(a.sgate.ts[0], a.sup.ts[0]);
+        if (it < n_rt * nI) {
+            const int ti = it / nI;
+            int lo = 0, hi = E - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (g_ts[mid] <= ti) lo = mid;
+                else hi = mid - 1;
+            }
+            const int t = ti - g_ts[lo];
+            s_item[tid] = make_int4(lo, g_cs[lo] + t * kGChunk, min(kGChunk, g_cnt[lo] - t * kGChunk), it % nI);
+            atomicMin(&g_map[lo], tid);
+            tsv = make_float2(a.gate.ts[lo], a.up.ts[lo]);
+        } else {
+            const int r = it - n_rt * nI, t = r / nIs;
+            s_item[tid] = make_int4(-1, t * kGChunk, min(kGChunk, T - t * kGChunk), r % nIs);
+            tsv = make_float2(a.sgate.ts[0], a.sup.ts[0]);
+        }
     }
+    for (int i = tid; i < kGuMaxItems * W; i += kBlock) g_bm[i] = 0u;
     __syncthreads();
-    for (int t = tid; t < n_my * kGChunk; t += kBlock) {
-        const int k = t >> 5, m = t & 31;
-        const int4 d = s_item[k];
-        const int pos = d.y + min(m, d.z - 1);
-        const int tok = d.x >= 0 ? a.asg[pos] / kk : pos;
-        s_tok[k][m] = tok;
-        s_tsig[k][m] = a.x_sig[tok];
-    }
-    __syncthreads();
-
     // The workgroup's items form one stream of n_my * NSB superblock steps;
     // weights and x are loaded ahead along that stream, across item
     // boundaries (past the last item: the last item again, L2 hits).
@@ -404,6 +530,68 @@ __global__ __launch_bounds__(kBlock, 2) void k_gateup_grouped(GroupedGuArgs a, f
         return gu_load_sb((routed ? gq_r : gq_s) + eq, (routed ? gs_r : gs_s) + es, (routed ? uq_r : uq_s) + eq,
                           (routed ? us_r : us_s) + es, H, n0, sb, true);
     };
+    // the stream's first weights go out now, ahead of the rest of the set-up
+    GuSb w[RING];
+#pragma unroll
+    for (int p = 0; p < RING - 1; ++p) w[p] = load_w(p / NSB, p % NSB);
+    // row bitmaps of the experts this workgroup needs; row s / k as the
+    // high word of s * ceil(2^32 / k), exact for s < 2^32 / k (k = 1: s)
+    const uint32_t kmag = kk > 1 ? 0xFFFFFFFFu / (uint32_t)kk + 1u : 0u;
+    for_slots([&](int s, int e) {
+        const int li = g_map[e];
+        if (li < kGuMaxItems) {
+            const int r = kk > 1 ? (int)__umulhi((uint32_t)s, kmag) : s;
+            atomicOr(&g_bm[li * W + (r >> 5)], 1u << (r & 31));
+        }
+    });
+    __syncthreads();
+    // set bits below each word: lanes 0-31 scan local expert li's words,
+    // lanes 32-63 those of li + 1
+    for (int li = 2 * wave; li < n_my; li += 2 * kWaves) {
+        const int l2 = li + (lane >> 5), w = lane & 31;
+        const bool live = l2 < n_my && w < W;
+        const int pc = live ? __builtin_popcount(g_bm[l2 * W + w]) : 0;
+        int v = wave_incl_scan(pc);
+        const int low_total = __builtin_amdgcn_readlane(v, 31);
+        if (lane >= 32) v -= low_total;
+        if (live) g_wp[l2 * W + w] = (uint16_t)(v - pc);
+    }
+    __syncthreads();
+    // token rows of every item (tokens past a tile repeat its last one);
+    // a routed tile's m-th token is its expert's (first slot - CSR start +
+    // m)-th row in ascending order: the word whose count below is the last
+    // one not above that rank, then the bit inside it
+    constexpr int kTokPer = kGuMaxItems * kGChunk / kBlock;
+    int tsg[kTokPer];
+#pragma unroll
+    for (int u = 0; u < kTokPer; ++u) {
+        const int t = tid + u * kBlock;
+        tsg[u] = 0;
+        if (t < n_my * kGChunk) {
+            const int k = t >> 5, m = t & 31;
+            const int4 d = s_item[k];
+            int tok;
+            if (d.x >= 0) {
+                const int li = g_map[d.x];
+                const int idx = d.y - g_cs[d.x] + min(m, d.z - 1);
+                const uint32_t* bm = g_bm + li * W;
+                const uint16_t* wp = g_wp + li * W;
+                int lo = 0, hi = W - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if ((int)wp[mid] <= idx) lo = mid;
+                    else hi = mid - 1;
+                }
+                tok = 32 * lo + nth_set_bit(bm[lo], idx - (int)wp[lo]);
+            } else {
+                tok = d.y + min(m, d.z - 1);
+            }
+            s_tok[k][m] = tok;
+            tsg[u] = a.x_sig[tok];
+        }
+    }
+    __syncthreads();
+
     // fp16 x columns of superblock sb of item k: 32 tokens x 32 pieces of 16
     // bytes, four pieces per thread, at the tokens' rows (clamped)
     auto load_x = [&](int k, int sb, uint4 (&v)[4]) {
@@ -424,12 +612,16 @@ __global__ __launch_bounds__(kBlock, 2) void k_gateup_grouped(GroupedGuArgs a, f
         }
     };
 
-    GuSb w[RING];
     uint4 xv[XL][4];
 #pragma unroll
     for (int p = 0; p < XL; ++p) load_x(p / NSB, p % NSB, xv[p]);
+    // the set-up's row exponents and tensor scales
 #pragma unroll
-    for (int p = 0; p < RING - 1; ++p) w[p] = load_w(p / NSB, p % NSB);
+    for (int u = 0; u < kTokPer; ++u) {
+        const int t = tid + u * kBlock;
+        if (t < n_my * kGChunk) s_tsig[t >> 5][t & 31] = tsg[u];
+    }
+    if (tid < n_my) s_ts[tid] = tsv;
     store_x(0, 0, xv[0]);
     __syncthreads();
 
@@ -480,6 +672,22 @@ __global__ __launch_bounds__(kBlock, 2) void k_gateup_grouped(GroupedGuArgs a, f
             const float mx = fmaxf(fmaxf(s_max[0][tid], s_max[1][tid]), fmaxf(s_max[2][tid], s_max[3][tid]));
             if (routed) hmax[(size_t)(p0 + tid) * nI + slab] = mx;
             else hmax_sh[(size_t)(p0 + tid) * nIs + slab] = mx;
+        }
+    }
+    // the CSR entries of the routed tiles whose first slab this workgroup
+    // did: position p0 + m holds slot r*k + j, where row r = the m-th token
+    // and j its selection rank of the tile's expert
+    for (int t = tid; t < n_my * kGChunk; t += kBlock) {
+        const int k = t >> 5, m = t & 31;
+        const int4 d = s_item[k];
+        if (d.x >= 0 && d.w == 0 && m < d.z) {
+            const int r = s_tok[k][m];
+            int jr = 0;
+            for (int jj = 0; jj < kk; ++jj)
+                if (a.ids[(size_t)r * kk + jj] == d.x) jr = jj;
+            const int s = r * kk + jr;
+            a.asg[d.y + m] = s;
+            a.inv[s] = d.y + m;
         }
     }
 }

@@ -152,14 +152,22 @@ struct GroupedGuArgs {
     const int32_t* x_sig;   // [T] the row's power-of-two exponent
     Fp4Mat gate, up;        // [E][I][H/2]
     Fp4Mat sgate, sup;      // [1][Is][H/2] (q == nullptr: no shared expert)
-    const int32_t* uniq;
-    const int32_t* off;
-    const int32_t* asg;
-    const int32_t* tiles;
-    const int32_t* n_tiles;
+    const int32_t* ids;     // [T][k] the rows' selected experts
+    // The canonical CSR and tile list, which every workgroup rebuilds from
+    // ids in LDS and publishes for the down and combine kernels: workgroup 0
+    // the per-expert outputs, the workgroup of each routed tile's first slab
+    // that tile's asg / inv entries.
+    int32_t* n_unique;      // [1]
+    int32_t* uniq;          // [T*k]
+    int32_t* off;           // [T*k+1]
+    int32_t* asg;           // [T*k]
+    int32_t* inv;           // [T*k]
+    int32_t* tiles;         // int4 [max tiles]
+    int32_t* n_tiles;       // [1]
+    int32_t* status;        // the call's hand-off status word, set to 0 (no hand-off here), or nullptr
     float* h;               // [T*k][I] by asg position
     float* h_sh;            // [T][Is]
-    int T, H, I, Is, k;
+    int T, H, I, Is, k, E;
 };
 
 struct GroupedDownArgs {
