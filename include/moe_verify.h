@@ -262,10 +262,11 @@ MOE_API int moe_verify_stack_timed(const moe_cfg* cfg, const moe_layer_weights* 
 MOE_API int moe_verify_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 /* Selection only (steps 2-3) from given fp32 logits [K][E] (device), with
- * the same device code the layer uses.  bias as in moe_layer_weights.  For
- * K > 16 the grouped regime's selection and grouping kernels run, and the
- * workspace (sized by moe_verify_workspace_bytes) is required; for K <= 16
- * workspace may be NULL. */
+ * the same selection code the layer uses.  bias as in moe_layer_weights.
+ * For K > 16 the grouped regime's selection kernel runs, then a grouping
+ * kernel that builds the same CSR the layer's gate/up workgroups rebuild for
+ * themselves, and the workspace (sized by moe_verify_workspace_bytes) is
+ * required; for K <= 16 workspace may be NULL. */
 MOE_API int moe_verify_route(const moe_cfg* cfg, const float* logits, const float* bias, int32_t K,
                      const moe_route_out* out, void* workspace, size_t workspace_bytes, void* stream);
 
