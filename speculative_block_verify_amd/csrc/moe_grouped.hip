@@ -593,22 +593,23 @@ __global__ __launch_bounds__(kBlock, 2) void k_gateup_grouped(GroupedGuArgs a, f
     __syncthreads();
 
     // fp16 x columns of superblock sb of item k: 32 tokens x 32 pieces of 16
-    // bytes, four pieces per thread, at the tokens' rows (clamped)
+    // bytes, four pieces per thread, at the tokens' rows; zeros, not loaded,
+    // for tokens past the item's tile
     auto load_x = [&](int k, int sb, uint4 (&v)[4]) {
         const int kc = min(k, n_my - 1);
+        const int cnt = s_item[kc].z;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int f = t * kBlock + tid, m = f >> 5, c8 = f & 31;
-            v[t] = *reinterpret_cast<const uint4*>(a.x + (size_t)s_tok[kc][m] * H + sb * kSbCols + c8 * 8);
+            v[t] = m < cnt ? *reinterpret_cast<const uint4*>(a.x + (size_t)s_tok[kc][m] * H + sb * kSbCols + c8 * 8)
+                           : make_uint4(0, 0, 0, 0);
         }
     };
-    // zeros for tokens past the item's tile
-    auto store_x = [&](int buf, int k, const uint4 (&v)[4]) {
-        const int cnt = s_item[min(k, n_my - 1)].z;
+    auto store_x = [&](int buf, const uint4 (&v)[4]) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int f = t * kBlock + tid, m = f >> 5, c8 = f & 31;
-            *reinterpret_cast<uint4*>(&xb[buf][m * kGXStride + c8 * 8]) = m < cnt ? v[t] : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(&xb[buf][m * kGXStride + c8 * 8]) = v[t];
         }
     };
 
@@ -622,7 +623,7 @@ __global__ __launch_bounds__(kBlock, 2) void k_gateup_grouped(GroupedGuArgs a, f
         if (t < n_my * kGChunk) s_tsig[t >> 5][t & 31] = tsg[u];
     }
     if (tid < n_my) s_ts[tid] = tsv;
-    store_x(0, 0, xv[0]);
+    store_x(0, xv[0]);
     __syncthreads();
 
     for (int k = 0; k < n_my; ++k) {
@@ -638,7 +639,7 @@ __global__ __launch_bounds__(kBlock, 2) void k_gateup_grouped(GroupedGuArgs a, f
             if (RING > 1) w[(sb + RING - 1) % RING] = load_w(k + (sb + RING - 1) / NSB, (sb + RING - 1) % NSB);
             else w[0] = load_w(k, sb);
             gg_mfma_sb(w[sb % RING], xb[(k * NSB + sb) & 1], ntt, accg, accu);
-            store_x((k * NSB + sb + 1) & 1, k + (sb + 1) / NSB, xv[(sb + 1) % XL]);
+            store_x((k * NSB + sb + 1) & 1, xv[(sb + 1) % XL]);
             __syncthreads();
         }
 
@@ -781,7 +782,9 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedDownArgs a, cons
             for (int t = 0; t < 8; ++t) {
                 const int f = t * kBlock + tid, m = f >> 6, c4 = f & 63;
                 const int col = min(sb * kSbCols + c4 * 4, cols - 4);
-                v[sb][t] = *reinterpret_cast<const float4*>(hrow0 + (size_t)min(m, cnt - 1) * cols + col);
+                // rows past the tile's tokens are zero when staged: not loaded
+                v[sb][t] = m < cnt ? *reinterpret_cast<const float4*>(hrow0 + (size_t)m * cols + col)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
             }
         DownCodes<NSB> cA, cB;
         load_codes(0, cA);
