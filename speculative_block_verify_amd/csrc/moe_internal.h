@@ -128,10 +128,11 @@ struct RouteGateUpArgs {
 };
 
 // --- grouped (prefill) regime ----------------------------------------------
-// Tile list: int2 {u, p0}.  Routed tiles first (u = index into uniq, p0 = the
-// first asg position of up to kGChunk consecutive slots of that expert), then
-// the shared expert's tiles (u = -1, p0 = first token).  tiles[kMetaTiles]
-// of the workspace meta holds the total count.
+// Tile list: int4 {e, p0, cnt, 0}.  Routed tiles first, experts ascending
+// (e = the expert, p0 = the first asg position of up to kGChunk consecutive
+// slots of e, cnt = their number), then the shared expert's tiles (e = -1,
+// p0 = first token, cnt = tokens).  Word kMetaTiles of the workspace meta
+// holds the total count.
 
 struct GroupArgs {
     const int32_t* ids;     // [T][k]
@@ -140,7 +141,7 @@ struct GroupArgs {
     int32_t* off;           // [T*k+1]
     int32_t* asg;           // [T*k]
     int32_t* inv;           // [T*k]
-    int32_t* tiles;         // int2 [max tiles]
+    int32_t* tiles;         // int4 [max tiles]
     int32_t* n_tiles;       // [1]
     int32_t* status;        // the call's hand-off status word, set to 0 (no hand-off here), or nullptr
     int T, E, k;
