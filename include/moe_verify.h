@@ -254,11 +254,13 @@ MOE_API int moe_verify_stack_timed(const moe_cfg* cfg, const moe_layer_weights* 
                                    float* kernel_ms);
 
 /* Measurement aid: read `bytes` (a positive multiple of 16) of device memory
- * at src (16-byte aligned) once, as a plain streaming read with every
- * workgroup keeping several 16-byte loads per thread in flight; the XOR of
- * the data is XORed into the device word *sink (so the reads cannot be
- * dropped).  Timed by the caller: the read ceiling the layer's bandwidth
- * figures are compared with.  Asynchronous on `stream`. */
+ * at src (16-byte aligned) once, as a plain streaming read: each workgroup
+ * reads its own contiguous range with non-temporal 16-byte loads, several per
+ * thread in flight (the fastest of the read patterns measured on MI355X).
+ * A thread whose XOR of the data it read equals a fixed constant stores it
+ * to the device word *sink, so the reads cannot be dropped; *sink carries no
+ * other meaning.  Timed by the caller: the read ceiling the layer's
+ * bandwidth figures are compared with.  Asynchronous on `stream`. */
 MOE_API int moe_verify_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 /* Selection only (steps 2-3) from given fp32 logits [K][E] (device), with

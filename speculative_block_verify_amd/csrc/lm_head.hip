@@ -57,7 +57,7 @@ __device__ __forceinline__ void lm_load(const LmArgs& a, int v0, int sb, uint4 (
     const int row = min(v0 + i, a.V - 1);
     const uint4* p = reinterpret_cast<const uint4*>(a.w + (size_t)row * H + sb * kSbCols + kb * 64);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) r[s] = p[s];
+    for (int s = 0; s < 8; ++s) r[s] = ld16_nt(p + s);
 }
 
 template <int NSB>
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kBlock) void k_lm_head_rows(LmArgs a) {
         for (int rr = 0; rr < R; ++rr) {
             const uint4* p = reinterpret_cast<const uint4*>(a.w + (size_t)min(v0 + rr, V - 1) * H) + lane;
 #pragma unroll
-            for (int t = 0; t < NC; ++t) w[rr][t] = p[64 * t];
+            for (int t = 0; t < NC; ++t) w[rr][t] = ld16_nt(p + 64 * t);
         }
     };
     uint4 wa[R][NC], wb[R][NC];
