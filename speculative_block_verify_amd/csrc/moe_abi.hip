@@ -67,9 +67,9 @@ bool grouped_shape_ok(const moe_cfg* c, int T) {
 
 // Rows from which MOE_REGIME_AUTO runs the grouped kernels (when the shape
 // meets their limits): measured on the 40-layer stack at hidden 2048, 256
-// experts, top-8, the grouped kernels take 2319 / 3032 us per stack at 8 / 16
-// rows against 2796 / 6536 us for the verify-width launches, and lose at 4
-// rows (2005 against 1664 us).
+// experts, top-8, the grouped kernels take 2255 / 2929 us per stack at 8 / 16
+// rows against 2628 / 6262 us for the verify-width launches, and lose at 4
+// rows (1840 against 1280 us).
 constexpr int kAutoGroupedRows = 8;
 
 // Which kernels serve K rows under cfg: false = the verify-width launches
@@ -454,8 +454,8 @@ int enqueue_stack(const moe_cfg* c, const moe_layer_weights* layers, int n_layer
     const Layout L = layout(c, ws);
     hipError_t e = moe::init_kernels();
     if (e != hipSuccess) return hip_fail(e, "kernel attributes");
-    // the grouped kernels use no hand-off (their grouping kernel clears the
-    // status word)
+    // the grouped kernels use no hand-off (their gate/up workgroup 0 clears
+    // the status word)
     int rc0 = use_grouped(c, K) ? MOE_OK : start_call(L, st);
     if (rc0) return rc0;
     const bool stream_res = residual != nullptr;
