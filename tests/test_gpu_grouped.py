@@ -135,6 +135,18 @@ def test_grouped_layer_wide_intermediate(shape, K):
     _layer(shape, K, 60 + K, label="wide I=%d Is=%d" % (shape.inter, shape.shared_inter))
 
 
+@pytest.mark.parametrize("shape,K", [
+    # 1024 experts at top-32: 5120 slots (more than the 16 per thread a
+    # gate/up workgroup holds in registers while grouping) and the largest
+    # per-expert tables
+    (inputs.MoEShape(256, 1024, 32, 128, 128), 160),
+    # 1000 rows at top-8: 8000 slots and 32 row-bitmap words per expert
+    (inputs.MoEShape(256, 64, 8, 128, 128), 1000),
+])
+def test_grouped_layer_many_slots_and_experts(shape, K):
+    _layer(shape, K, 70 + K, label="E=%d k=%d" % (shape.n_experts, shape.top_k))
+
+
 def test_grouped_layer_correlated_rows_span_several_tiles():
     # rows 1..K/2 are row 0 plus small noise: their experts get ~40+ tokens
     # each, so one expert spans two or three 32-token tiles with a ragged tail
