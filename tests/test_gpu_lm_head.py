@@ -140,12 +140,13 @@ def test_lm_head_exact_tie_takes_lower_token_and_accepts_the_tied_draft():
         check(gpu, ol, fp32_bound(x, w), torch.as_tensor(d), tol, "tie tol=%g" % tol)
 
 
-@pytest.mark.parametrize("K", [1, 2, 4, 8])
+@pytest.mark.parametrize("K", [1, 2, 4, 8, 16])
 def test_lm_head_full_size(K):
     """The pages' lm_head: vocabulary 100352, hidden 2048 (0.41 GB bf16).
     Every logit of every row against the oracle; the call without a logits
     buffer (the hot path) gives the same greedy results.  Up to 4 rows run
-    the row-streaming vector kernel, 8 rows the matrix-core tiles."""
+    the row-streaming vector kernel, 8 and 16 rows (its widest tile) the
+    matrix-core tiles."""
     say("case: lm_head full size K=%d" % K)
     V, H = inputs.VOCAB, 2048
     x = inputs.gen_x(K, H, 100 + K, device=DEV)
