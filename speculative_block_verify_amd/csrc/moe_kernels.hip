@@ -988,10 +988,10 @@ __global__ __launch_bounds__(NT) void k_down(DownArgs a) {
             if (j * rpp < nr) {  // uniform: passes past the chunk are skipped
                 const int rr = c0 + min(j * rpp + r0, nr - 1);
                 const bool shared_row = rr >= n;
-                const int len4 = (shared_row ? Is : I) / 4;
-                const int cc = min(c4, len4 - 1);
-                hv4[j] = shared_row ? reinterpret_cast<const float4*>(a.h_sh + (size_t)(rr - n) * Is)[cc]
-                                    : reinterpret_cast<const float4*>(a.h + (size_t)rr * I)[cc];
+                const uint32_t len4 = (uint32_t)(shared_row ? Is : I) >> 2;
+                const uint32_t cc = min((uint32_t)c4, len4 - 1u);
+                const float4* hb = reinterpret_cast<const float4*>(shared_row ? a.h_sh : a.h);
+                hv4[j] = hb[(uint32_t)(shared_row ? rr - n : rr) * len4 + cc];
             }
         }
     };
@@ -1065,17 +1065,21 @@ __global__ __launch_bounds__(NT) void k_down(DownArgs a) {
                 const bool shared_task = !routed && t < nT;
                 const int lgC = shared_task ? lgS : lgI;
                 const int grp = routed ? (t & (gI - 1)) : (shared_task ? t - (u_hi - u_lo) * gI : 0);
-                const int e = ev[i];
+                // the expert is the same in every lane: the task's first row
+                // address is formed in scalar registers, and each lane adds
+                // a 32-bit offset
+                const int e = __builtin_amdgcn_readfirstlane(ev[i]);
                 const uint8_t* mq = shared_task ? sq : dq;
                 const uint8_t* ms = shared_task ? ss : ds;
                 const float* mts = shared_task ? sts : dts;
-                const int cols = shared_task ? Is : I;
+                const uint32_t cols = (uint32_t)(shared_task ? Is : I);
                 const int q = lane >> lgC, chunk = lane & ((1 << lgC) - 1);
                 const int nl = (grp << (6 - lgC)) + q;
-                const size_t row = (size_t)e * H + n_base + (nl < NH ? nl : 0);
+                const uint32_t lr = (uint32_t)(nl < NH ? nl : 0);
+                const size_t row0 = (size_t)e * H + n_base;
                 tsv[i] = mts[e];
-                code[i] = *reinterpret_cast<const uint4*>(mq + row * (cols / 2) + chunk * 16);
-                scl[i] = *reinterpret_cast<const uint16_t*>(ms + row * (cols / 16) + chunk * 2);
+                code[i] = *reinterpret_cast<const uint4*>(mq + row0 * (cols >> 1) + (lr * (cols >> 1) + (uint32_t)chunk * 16u));
+                scl[i] = *reinterpret_cast<const uint16_t*>(ms + row0 * (cols >> 4) + (lr * (cols >> 4) + (uint32_t)chunk * 2u));
             }
         };
         // A later chunk of h (more than CAP rows) is requested here, after
