@@ -321,27 +321,50 @@ constexpr int kGXStride = kSbCols + 8;  // halfs per staged token row
 constexpr int kGuMaxItems = 16;          // work items of one persistent gate/up workgroup
 constexpr int kGuGrid = 512;             // persistent gate/up workgroups (two per compute unit)
 
-__device__ __forceinline__ void gg_mfma_sb(const GuSb& r, const _Float16* xb, int ntt, f32x4_t* accg,
-                                           f32x4_t* accu) {
+// One superblock's eight MFMA steps, software pipelined: step s + 1's x
+// columns are read from LDS and its weights decoded before step s's MFMAs
+// issue, so neither the LDS round trip nor the decode waits behind the
+// matrix core.  Both 16-token column tiles are always multiplied: an item of
+// at most 16 tokens has zeros in the second tile's x rows and its results
+// are not stored.  The steps then hold no branch, which is what lets the
+// compiler interleave the decode with the MFMAs (a per-step branch on the
+// tile count kept every LDS read right before its MFMA); a scheduling
+// barrier closes each step, so the decoded operands of at most two steps
+// are in registers.
+__device__ __forceinline__ void gg_mfma_sb(const GuSb& r, const _Float16* xb, f32x4_t* accg, f32x4_t* accu) {
     const int lane = threadIdx.x & 63, j = lane & 15, kb = lane >> 4;
     const _Float16 g0 = e4m3_to_f16<0>(r.gs), g1 = e4m3_to_f16<1>(r.gs);
     const _Float16 g2 = e4m3_to_f16<2>(r.gs), g3 = e4m3_to_f16<3>(r.gs);
     const _Float16 u0 = e4m3_to_f16<0>(r.us), u1 = e4m3_to_f16<1>(r.us);
     const _Float16 u2 = e4m3_to_f16<2>(r.us), u3 = e4m3_to_f16<3>(r.us);
+    const _Float16* xr = xb + j * kGXStride + kb * 64;
+    auto dec_g = [&](int s) { return decode8_f16(pick_word(r.g0, r.g1, s), (s < 2) ? g0 : (s < 4) ? g1 : (s < 6) ? g2 : g3); };
+    auto dec_u = [&](int s) { return decode8_f16(pick_word(r.u0, r.u1, s), (s < 2) ? u0 : (s < 4) ? u1 : (s < 6) ? u2 : u3); };
+    f16x8_t b[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) b[t] = *reinterpret_cast<const f16x8_t*>(xr + 16 * t * kGXStride);
+    f16x8_t ag = dec_g(0), au = dec_u(0);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        const _Float16 gsc = (s < 2) ? g0 : (s < 4) ? g1 : (s < 6) ? g2 : g3;
-        const _Float16 usc = (s < 2) ? u0 : (s < 4) ? u1 : (s < 6) ? u2 : u3;
-        const f16x8_t ag = decode8_f16(pick_word(r.g0, r.g1, s), gsc);
-        const f16x8_t au = decode8_f16(pick_word(r.u0, r.u1, s), usc);
-        const f16x8_t b0 = *reinterpret_cast<const f16x8_t*>(xb + j * kGXStride + kb * 64 + 8 * s);
-        accg[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ag, b0, accg[0], 0, 0, 0);
-        accu[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(au, b0, accu[0], 0, 0, 0);
-        if (ntt > 1) {
-            const f16x8_t b1 = *reinterpret_cast<const f16x8_t*>(xb + (16 + j) * kGXStride + kb * 64 + 8 * s);
-            accg[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ag, b1, accg[1], 0, 0, 0);
-            accu[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(au, b1, accu[1], 0, 0, 0);
+        f16x8_t nb[2], nag = ag, nau = au;
+        if (s < 7) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) nb[t] = *reinterpret_cast<const f16x8_t*>(xr + 16 * t * kGXStride + 8 * (s + 1));
+            nag = dec_g(s + 1);
+            nau = dec_u(s + 1);
         }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            accg[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ag, b[t], accg[t], 0, 0, 0);
+            accu[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(au, b[t], accu[t], 0, 0, 0);
+        }
+        if (s < 7) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) b[t] = nb[t];
+            ag = nag;
+            au = nau;
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -638,7 +661,7 @@ __global__ __launch_bounds__(kBlock, 2) void k_gateup_grouped(GroupedGuArgs a, f
             load_x(k + (sb + XL) / NSB, (sb + XL) % NSB, xv[(sb + XL) % XL]);
             if (RING > 1) w[(sb + RING - 1) % RING] = load_w(k + (sb + RING - 1) / NSB, (sb + RING - 1) % NSB);
             else w[0] = load_w(k, sb);
-            gg_mfma_sb(w[sb % RING], xb[(k * NSB + sb) & 1], ntt, accg, accu);
+            gg_mfma_sb(w[sb % RING], xb[(k * NSB + sb) & 1], accg, accu);
             store_x((k * NSB + sb + 1) & 1, xv[(sb + 1) % XL]);
             __syncthreads();
         }
@@ -712,6 +735,11 @@ __global__ __launch_bounds__(kBlock, 2) void k_gateup_grouped(GroupedGuArgs a, f
 
 constexpr int kGMaxSb = kGMaxCols / kSbCols;  // superblocks of the longest staged h row
 
+
+template <int N>
+struct IntC {
+    static constexpr int value = N;
+};
 
 template <int NSB>
 struct DownCodes {
@@ -827,37 +855,56 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedDownArgs a, cons
 
         const int ntt = cnt > 16 ? 2 : 1;
         float* obase = a.o + (size_t)(routed ? p0 : T * kk + p0) * H;
-        auto compute = [&](int g, const DownCodes<NSB>& c) {
+        // NT: the tile's 16-token column tiles (1 or 2), a compile-time
+        // constant so that the MFMA steps hold no branch
+        auto compute = [&](auto ntc, int g, const DownCodes<NSB>& c) {
+            constexpr int NT = decltype(ntc)::value;
             f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-            // every superblock of the staged row, also past a shorter row's
-            // length (zero h there): no data-dependent branch around the chain
+            // Every superblock of the staged row, also past a shorter row's
+            // length (zero h there): no data-dependent branch in the chain.
+            // Software pipelined over the NSB * 8 MFMA steps: step q + 1's h
+            // columns are read from LDS before step q's MFMAs issue; a
+            // scheduling barrier closes each step, so at most two steps'
+            // operands are in registers.
+            const _Float16* hr = hi + j * S + kb * 64;
+            const _Float16* lr = lo + j * S + kb * 64;
+            auto ldb = [&](const _Float16* base, int q, int tt) {
+                return *reinterpret_cast<const f16x8_t*>(base + tt * 16 * S + (q >> 3) * kSbCols + 8 * (q & 7));
+            };
+            f16x8_t bh[NT], bl[NT];
 #pragma unroll
-            for (int sb = 0; sb < NSB; ++sb) {
-                const int colb = sb * kSbCols + kb * 64;
-                const _Float16 s0 = e4m3_to_f16<0>(c.sc[sb]), s1 = e4m3_to_f16<1>(c.sc[sb]);
-                const _Float16 s2 = e4m3_to_f16<2>(c.sc[sb]), s3 = e4m3_to_f16<3>(c.sc[sb]);
+            for (int tt = 0; tt < NT; ++tt) { bh[tt] = ldb(hr, 0, tt); bl[tt] = ldb(lr, 0, tt); }
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const _Float16 ssc = (s < 2) ? s0 : (s < 4) ? s1 : (s < 6) ? s2 : s3;
-                    const f16x8_t aw = decode8_f16(pick_word(c.c0[sb], c.c1[sb], s), ssc);
+            for (int q = 0; q < NSB * 8; ++q) {
+                const int sb = q >> 3, s = q & 7;
+                f16x8_t nh[NT], nl[NT];
+                if (q + 1 < NSB * 8) {
 #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) {
-                        if (tt < ntt) {
-                            const int m = tt * 16 + j;
-                            const f16x8_t bh = *reinterpret_cast<const f16x8_t*>(hi + m * S + colb + 8 * s);
-                            const f16x8_t bl = *reinterpret_cast<const f16x8_t*>(lo + m * S + colb + 8 * s);
-                            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, bh, acc[tt], 0, 0, 0);
-                            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, bl, acc[tt], 0, 0, 0);
-                        }
-                    }
+                    for (int tt = 0; tt < NT; ++tt) { nh[tt] = ldb(hr, q + 1, tt); nl[tt] = ldb(lr, q + 1, tt); }
                 }
+                const uint32_t scw = c.sc[sb];
+                const _Float16 ssc = (s < 2)   ? e4m3_to_f16<0>(scw)
+                                     : (s < 4) ? e4m3_to_f16<1>(scw)
+                                     : (s < 6) ? e4m3_to_f16<2>(scw)
+                                               : e4m3_to_f16<3>(scw);
+                const f16x8_t aw = decode8_f16(pick_word(c.c0[sb], c.c1[sb], s), ssc);
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) {
+                    acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, bh[tt], acc[tt], 0, 0, 0);
+                    acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, bl[tt], acc[tt], 0, 0, 0);
+                }
+                if (q + 1 < NSB * 8) {
+#pragma unroll
+                    for (int tt = 0; tt < NT; ++tt) { bh[tt] = nh[tt]; bl[tt] = nl[tt]; }
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
             // lane (j, q) holds output rows n0 + 4q .. +3 of token j
             const int n0 = (s_lo + g) * kGRows + wave * 16;
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
+            for (int tt = 0; tt < NT; ++tt) {
                 const int m = tt * 16 + j;
-                if (tt < ntt && m < cnt) {
+                if (m < cnt) {
                     const int sg = s_sig[m];
                     float4 ov;
                     ov.x = ldexpf(acc[tt][0], sg) * ts;
@@ -871,13 +918,17 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedDownArgs a, cons
         // slabs in pairs: the other register set's loads are always issued
         // (the last slab's codes again at the end, an L2 hit) so the compiler
         // keeps an exact count of loads in flight
+        auto run = [&](auto ntc) {
 #pragma unroll 1
-        for (int g = 0; g < n_seg; g += 2) {
-            load_codes(g + 1 < n_seg ? g + 1 : n_seg - 1, cB);
-            compute(g, cA);
-            load_codes(g + 2 < n_seg ? g + 2 : n_seg - 1, cA);
-            if (g + 1 < n_seg) compute(g + 1, cB);
-        }
+            for (int g = 0; g < n_seg; g += 2) {
+                load_codes(g + 1 < n_seg ? g + 1 : n_seg - 1, cB);
+                compute(ntc, g, cA);
+                load_codes(g + 2 < n_seg ? g + 2 : n_seg - 1, cA);
+                if (g + 1 < n_seg) compute(ntc, g + 1, cB);
+            }
+        };
+        if (ntt > 1) run(IntC<2>{});
+        else run(IntC<1>{});
         __syncthreads();  // staged rows and s_sig are replaced by the next segment
     }
 }
