@@ -736,6 +736,7 @@ __global__ __launch_bounds__(kBlock, 2) void k_gateup_grouped(GroupedGuArgs a, f
 constexpr int kGMaxSb = kGMaxCols / kSbCols;  // superblocks of the longest staged h row
 
 
+// a compile-time integer passed as a value (a tile's column-tile count)
 template <int N>
 struct IntC {
     static constexpr int value = N;
