@@ -343,14 +343,33 @@ int enqueue_layer_grouped(const moe_cfg* c, const moe_layer_weights* w, const ui
     ra.x_f16 = L.xh;
     ra.x_sig = L.xsig;
     ra.K = K; ra.H = c->hidden; ra.E = c->n_experts;
-    if ((e = moe::launch_router_mfma(ra, st)) != hipSuccess) return hip_fail(e, "router launch");
 
     moe::SelectArgs sa{};
     sa.logits = L.logits; sa.bias = w->router_bias;
     sa.ids = L.ids; sa.w = L.w;
     sa.K = K; sa.E = c->n_experts; sa.k = c->top_k;
     sa.score_fn = c->score_fn; sa.norm_topk = c->norm_topk;
-    if ((e = moe::launch_select_rows(sa, st)) != hipSuccess) return hip_fail(e, "row selection launch");
+
+    // Few rows: the router's column slices as workgroups of their own, their
+    // partial logits in the down output buffer (written only later in the
+    // layer), summed by the selection launch, which also makes the fp16 x.
+    const size_t parts_floats = (size_t)moe::kRouterWaves * K * c->n_experts;
+    const size_t o_floats = ((size_t)c->max_rows * c->top_k + c->max_rows) * c->hidden;
+    if (K <= moe::kRouterSplitMaxRows && c->n_experts <= moe::kRouterSplitMaxExperts && c->hidden <= 2048 &&
+        parts_floats <= o_floats) {
+        ra.logits = L.o;
+        ra.x_f16 = nullptr;
+        ra.x_sig = nullptr;
+        if ((e = moe::launch_router_split(ra, st)) != hipSuccess) return hip_fail(e, "router launch");
+        moe::SelectSplitArgs ss{};
+        ss.s = sa;
+        ss.parts = L.o; ss.logits = L.logits;
+        ss.x_in = x; ss.x_f16 = L.xh; ss.x_sig = L.xsig; ss.H = c->hidden;
+        if ((e = moe::launch_select_rows_split(ss, st)) != hipSuccess) return hip_fail(e, "row selection launch");
+    } else {
+        if ((e = moe::launch_router_mfma(ra, st)) != hipSuccess) return hip_fail(e, "router launch");
+        if ((e = moe::launch_select_rows(sa, st)) != hipSuccess) return hip_fail(e, "row selection launch");
+    }
 
     // the gate/up workgroups group the slots themselves (and publish the CSR)
     const int max_tiles = moe::grouped_max_tiles(K, c->n_experts, c->top_k, has_sh);

@@ -3,9 +3,12 @@
 // expert GEMMs are dense contractions for the matrix cores (the 512-row seed
 // prefill of the mlxfast README, "Why this challenge exists"; PR #844
 // section 8 notes the stock grouped GEMM needs several tokens per expert).
-// Per layer, after the router GEMV on the matrix cores (k_router_mfma):
+// Per layer, after the router GEMV on the matrix cores (k_router_mfma; up
+// to 16 rows k_router_split, its column slices as workgroups of their own):
 //   k_select_rows   top-k and mixture weights, one wave per row (the same
-//                   selection code as the verify-width path);
+//                   selection code as the verify-width path; up to 16 rows
+//                   k_select_rows_split, which first adds the router's
+//                   partial logits and makes the fp16 copy of x);
 //   k_gateup_grouped  every workgroup first groups the T*k slots itself in
 //                   LDS: the canonical CSR by expert (unique experts
 //                   ascending, slots ascending), a tile list of up to 32
@@ -51,7 +54,6 @@ namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kRouterWaves = 8;
 
 template <int H>
 __global__ __launch_bounds__(kRouterWaves * 64) void k_router_mfma(RouterArgs a) {
@@ -150,6 +152,45 @@ __global__ __launch_bounds__(kRouterWaves * 64) void k_router_mfma(RouterArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// k_router_split: the same logits for up to 16 rows, each column slice of
+// k_router_mfma's waves as a one-wave workgroup of its own: (E/16) x 8
+// workgroups instead of E/16, so the router rows stream from 8x the compute
+// units.  Slice z's MFMA chain is wave z's chain of k_router_mfma (rows
+// 0..15), and its 16x16 partial tile goes to a.logits[z][row][e];
+// k_select_rows_split adds the slices in order, which is the order the
+// many-row kernel adds its waves' tiles, so the logits are the same bits.
+// ---------------------------------------------------------------------------
+
+template <int H>
+__global__ __launch_bounds__(64) void k_router_split(RouterArgs a) {
+    constexpr int NS = H / kRouterWaves / 32;  // MFMA steps per slice
+    const int lane = threadIdx.x, i = lane & 15, kb = lane >> 4;
+    const int T = a.K, E = a.E;
+    const int e0 = blockIdx.x * 16, z = blockIdx.y;
+    const int c0 = z * (H / kRouterWaves) + 8 * kb;
+    const uint16_t* xr0 = a.x_in + (size_t)min(i, T - 1) * H + c0;
+    const uint16_t* wr0 = a.wr + (size_t)min(e0 + i, E - 1) * H + c0;
+    uint4 x0[NS], w0[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        x0[s] = *reinterpret_cast<const uint4*>(xr0 + 32 * s);
+        w0[s] = *reinterpret_cast<const uint4*>(wr0 + 32 * s);
+    }
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x0[s]),
+                                                      __builtin_bit_cast(bf16x8_t, w0[s]), acc, 0, 0, 0);
+    // lane (j, q) holds rows 4q .. 4q+3 of expert column j
+    const int j = lane & 15, q = lane >> 4, e = e0 + j;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = 4 * q + r;
+        if (row < T && e < E) a.logits[((size_t)z * T + row) * E + e] = acc[r];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // k_select_rows: kWaves rows per workgroup
 // ---------------------------------------------------------------------------
 
@@ -167,6 +208,71 @@ __global__ __launch_bounds__(kBlock) void k_select_rows(SelectArgs a) {
         if (lane < a.k) {
             a.ids[(size_t)(r0 + wave) * a.k + lane] = sm.sel[wave * a.k + lane];
             a.w[(size_t)(r0 + wave) * a.k + lane] = sm.w[wave * a.k + lane];
+        }
+    }
+}
+
+// k_select_rows with the router's slice partials added first (slice order)
+// and the summed logits stored; each row's wave also writes the row's fp16
+// copy of x and its exponent, as k_router_mfma does for many rows.
+__global__ __launch_bounds__(kBlock) void k_select_rows_split(SelectSplitArgs a) {
+    __shared__ SelectSmem sm;
+    extern __shared__ __align__(16) float lg[];  // [kWaves][E]
+    const SelectArgs& sa = a.s;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int K = sa.K, E = sa.E, H = a.H;
+    const int r0 = blockIdx.x * kWaves;
+    const int nr = min(kWaves, K - r0);
+    // this thread's logits (E <= kRouterSplitMaxExperts: at most four), every
+    // slice's partial requested before the first is added
+    static_assert(kWaves * kRouterSplitMaxExperts <= 4 * kBlock, "more than four logits per thread");
+    float pv[4][kRouterWaves];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int t = tid + u * kBlock;
+        const float* p = a.parts + (size_t)r0 * E + min(t, nr * E - 1);
+#pragma unroll
+        for (int z = 0; z < kRouterWaves; ++z) pv[u][z] = p[(size_t)z * K * E];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int t = tid + u * kBlock;
+        float v = pv[u][0];
+#pragma unroll
+        for (int z = 1; z < kRouterWaves; ++z) v += pv[u][z];
+        if (t < nr * E) {
+            lg[t] = v;
+            a.logits[(size_t)r0 * E + t] = v;
+        }
+    }
+    if (wave < nr) {
+        // the row's largest |x| -> its exponent, then the scaled fp16 copy
+        // (H <= 2048: at most four 8-column pieces per lane)
+        const int r = r0 + wave, n8 = H / 8;
+        const uint4* xr = reinterpret_cast<const uint4*>(a.x_in + (size_t)r * H);
+        uint4 v[4];
+        uint32_t m = 0u;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int c = lane + 64 * t;
+            v[t] = c < n8 ? xr[c] : make_uint4(0, 0, 0, 0);
+            m = max(m, bf16x8_maxabs(v[t]));
+        }
+        const int sg = row_sigma(wave_max_u32(m));
+        if (lane == 0) a.x_sig[r] = sg;
+        uint4* xo = reinterpret_cast<uint4*>(a.x_f16 + (size_t)r * H);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int c = lane + 64 * t;
+            if (c < n8) xo[c] = bf16x8_to_f16x8_scaled(v[t], -sg);
+        }
+    }
+    __syncthreads();
+    if (wave < nr) {
+        wave_topk_rt(sa, lg + wave * E, wave, sm);
+        if (lane < sa.k) {
+            sa.ids[(size_t)(r0 + wave) * sa.k + lane] = sm.sel[wave * sa.k + lane];
+            sa.w[(size_t)(r0 + wave) * sa.k + lane] = sm.w[wave * sa.k + lane];
         }
     }
 }
@@ -1109,6 +1215,24 @@ hipError_t launch_router_mfma(const RouterArgs& a, hipStream_t st) {
         case 2048: return launch_plain(k_router_mfma<2048>, g, b, 0, st, a);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_router_split(const RouterArgs& a, hipStream_t st) {
+    if (a.K > kRouterSplitMaxRows) return hipErrorInvalidValue;
+    const dim3 g((a.E + 15) / 16, kRouterWaves), b(64);
+    switch (a.H) {
+        case 256: return launch_plain(k_router_split<256>, g, b, 0, st, a);
+        case 512: return launch_plain(k_router_split<512>, g, b, 0, st, a);
+        case 1024: return launch_plain(k_router_split<1024>, g, b, 0, st, a);
+        case 2048: return launch_plain(k_router_split<2048>, g, b, 0, st, a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_select_rows_split(const SelectSplitArgs& a, hipStream_t st) {
+    if (a.H > 2048 || a.H % 8 || a.s.E > kRouterSplitMaxExperts) return hipErrorInvalidValue;
+    const int grid = (a.s.K + kWaves - 1) / kWaves;
+    return launch_plain(k_select_rows_split, dim3(grid), dim3(kBlock), (size_t)kWaves * a.s.E * 4, st, a);
 }
 
 hipError_t launch_select_rows(const SelectArgs& a, hipStream_t st) {

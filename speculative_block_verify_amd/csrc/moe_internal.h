@@ -50,6 +50,25 @@ struct SelectArgs {
 };
 
 // Router GEMV (and the RMS normalisation of the previous layer's output).
+// The many-row router's column slices: one wave each, its partial logits
+// added in slice order.  Up to kRouterSplitMaxRows rows each slice is a
+// workgroup of its own (more workgroups for few rows), for up to
+// kRouterSplitMaxExperts experts.
+constexpr int kRouterWaves = 8;
+constexpr int kRouterSplitMaxRows = 16;
+constexpr int kRouterSplitMaxExperts = 256;
+
+// Selection for the few-row grouped layer: the router's per-slice partial
+// logits are added here (slice order), and the fp16 copy of x is made here.
+struct SelectSplitArgs {
+    SelectArgs s;           // s.logits unused
+    const float* parts;     // [kRouterWaves][K][E] partial logits, one per column slice
+    float* logits;          // [K][E] their sums (written)
+    const uint16_t* x_in;   // bf16 [K][H]
+    uint16_t* x_f16;        // fp16 bit patterns [K][H] of x_in * 2^-x_sig[row]
+    int32_t* x_sig;         // [K]
+    int H;
+};
 struct RouterArgs {
     const uint16_t* x_in;   // bf16 [K][H], read when y_prev == nullptr
     const float* y_prev;    // fp32 [K][H] to RMS-normalise into x, or nullptr
@@ -242,6 +261,10 @@ hipError_t launch_dense_mlp(const uint16_t* x, int T, int H, int I, const uint16
 // Grouped regime (moe_grouped.hip).
 hipError_t launch_router_mfma(const RouterArgs& a, hipStream_t st);  // many rows, plain bf16 x_in only
 hipError_t launch_select_rows(const SelectArgs& a, hipStream_t st);  // ids and w only
+// few rows (K <= kRouterSplitMaxRows): partial logits per column slice into
+// a.logits ([kRouterWaves][K][E]), no fp16 copy of x
+hipError_t launch_router_split(const RouterArgs& a, hipStream_t st);
+hipError_t launch_select_rows_split(const SelectSplitArgs& a, hipStream_t st);
 hipError_t launch_group(const GroupArgs& a, hipStream_t st);
 // hmax [T*k][I/64] and hmax_sh [T][Is/64]: max |h| of each token per 64-row slab
 hipError_t launch_gateup_grouped(const GroupedGuArgs& a, float* hmax, float* hmax_sh, int max_tiles,

@@ -184,6 +184,28 @@ def test_grouped_and_verify_width_paths_agree_at_16_rows():
     assert np.abs(a["y32"] - b["y32"]).max() <= 2 * gh.Y_TOL * scale
 
 
+def test_few_row_router_matches_many_row_router():
+    """Up to 16 rows the grouped layer runs the router's eight column slices as
+    workgroups of their own and adds their partial logits in the selection
+    launch, in the order the many-row router adds its waves' tiles; it also
+    makes the fp16 copy of x there.  Rows 0..15 of a 17-row call (many-row
+    router) and of a 16-row call on the same rows must then have the same
+    logits, selections and weights bit for bit, and the same outputs."""
+    say("case: few-row vs many-row router, 16 / 17 rows")
+    shape = inputs.MoEShape(hidden=2048, n_experts=256, top_k=8, inter=512, shared_inter=512)
+    w = inputs.gen_layer(shape, 47, 0, device=DEV)
+    x = inputs.gen_x(17, shape.hidden, 47, device=DEV)
+    a = gh.run_layer(api.make_cfg(shape, 17), w, x, grouped=True)
+    b = gh.run_layer(api.make_cfg(shape, 16), w, x[:16].contiguous(), grouped=True)
+    E, k = shape.n_experts, shape.top_k
+    np.testing.assert_array_equal(a["logits"].reshape(17, E)[:16].view(np.uint32),
+                                  b["logits"].reshape(16, E).view(np.uint32))
+    np.testing.assert_array_equal(a["ids"].reshape(17, k)[:16], b["ids"].reshape(16, k))
+    np.testing.assert_array_equal(a["w"].reshape(17, k)[:16].view(np.uint32), b["w"].reshape(16, k).view(np.uint32))
+    ya, yb = a["y32"].reshape(17, -1)[:16], b["y32"].reshape(16, -1)
+    assert np.abs(ya - yb).max() <= 1e-6 * np.abs(ya).max()
+
+
 def test_grouped_layer_bitwise_invariants():
     say("case: grouped invariants")
     shape = inputs.LAGUNA
