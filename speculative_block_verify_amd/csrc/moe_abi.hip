@@ -67,9 +67,9 @@ bool grouped_shape_ok(const moe_cfg* c, int T) {
 
 // Rows from which MOE_REGIME_AUTO runs the grouped kernels (when the shape
 // meets their limits): measured on the 40-layer stack at hidden 2048, 256
-// experts, top-8, the grouped kernels take 2255 / 2929 us per stack at 8 / 16
-// rows against 2628 / 6262 us for the verify-width launches, and lose at 4
-// rows (1840 against 1280 us).
+// experts, top-8, the grouped kernels take 2118 / 2736 us per stack at 8 / 16
+// rows against 2592 / 6222 us for the verify-width launches, and lose at 4
+// rows (1702 against 1260 us).
 constexpr int kAutoGroupedRows = 8;
 
 // Which kernels serve K rows under cfg: false = the verify-width launches
