@@ -391,14 +391,14 @@ int enqueue_layer_grouped(const moe_cfg* c, const moe_layer_weights* w, const ui
     moe::GroupedDownArgs da{};
     da.down = mat(w->down);
     da.sdown = has_sh ? mat(w->sh_down) : none;
-    da.uniq = L.uniq; da.off = L.off; da.tiles = L.tiles; da.n_tiles = n_tiles;
+    da.uniq = L.uniq; da.off = L.off; da.tiles = L.tiles; da.n_tiles = n_tiles; da.asg = L.asg;
     da.h = L.h; da.h_sh = L.h_sh; da.o = L.o;
     da.T = K; da.H = c->hidden; da.I = c->inter; da.Is = c->shared_inter; da.k = c->top_k;
     if ((e = moe::launch_down_grouped(da, L.hmax, L.hmax_sh, max_tiles, st)) != hipSuccess)
         return hip_fail(e, "grouped down launch");
 
     moe::CombineArgs ca{};
-    ca.o = L.o; ca.w = L.w; ca.inv = L.inv;
+    ca.o = L.o; ca.w = L.w;
     ca.residual = residual; ca.y32 = y32; ca.y = y; ca.x_next = x_next;
     ca.gamma = x_next ? w->norm_w : nullptr;
     ca.eps = c->rms_eps; ca.rs = c->routed_scale;

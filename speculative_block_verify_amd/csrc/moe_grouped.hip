@@ -909,6 +909,15 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedDownArgs a, cons
             const int idx = u * kBlock + tid, m = idx >> 4, sl = idx & 15;
             hmv[u] = hmb[(size_t)(p0 + min(m, cnt - 1)) * nslab + min(sl, nslab - 1)];
         }
+        // output rows of this lane's tokens j and 16 + j: a routed token's
+        // slot (so the combine reads its rows without the CSR), a shared
+        // token's row after the routed ones
+        int orow[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int pm = p0 + min(tt * 16 + j, cnt - 1);
+            orow[tt] = routed ? a.asg[pm] : T * kk + pm;
+        }
         const float* hrow0 = routed ? a.h + (size_t)p0 * I : a.h_sh + (size_t)p0 * Is;
         float4 v[NSB][8];  // one superblock is 32 rows x 256 columns = 2048 float4
 #pragma unroll
@@ -961,7 +970,6 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedDownArgs a, cons
         __syncthreads();
 
         const int ntt = cnt > 16 ? 2 : 1;
-        float* obase = a.o + (size_t)(routed ? p0 : T * kk + p0) * H;
         // NT: the tile's 16-token column tiles (1 or 2), a compile-time
         // constant so that the MFMA steps hold no branch
         auto compute = [&](auto ntc, int g, const DownCodes<NSB>& c) {
@@ -1018,7 +1026,7 @@ __global__ __launch_bounds__(kBlock) void k_down_grouped(GroupedDownArgs a, cons
                     ov.y = ldexpf(acc[tt][1], sg) * ts;
                     ov.z = ldexpf(acc[tt][2], sg) * ts;
                     ov.w = ldexpf(acc[tt][3], sg) * ts;
-                    *reinterpret_cast<float4*>(obase + (size_t)m * H + n0 + 4 * q) = ov;
+                    *reinterpret_cast<float4*>(a.o + (size_t)orow[tt] * H + n0 + 4 * q) = ov;
                 }
             }
         };
@@ -1049,15 +1057,11 @@ constexpr int kCombineBatch = 8;                // slots whose rows are loaded t
 
 __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a) {
     __shared__ float s_w[kMaxTopK];
-    __shared__ int s_o[kMaxTopK];
     __shared__ float s_ss[kWaves];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = blockIdx.x, H = a.H, k = a.k;
     const int n4 = H / 4;  // float4 per row; thread tid owns float4 t * kBlock + tid
-    if (tid < k) {
-        s_w[tid] = a.w[(size_t)r * k + tid];
-        s_o[tid] = a.inv[(size_t)r * k + tid];
-    }
+    if (tid < k) s_w[tid] = a.w[(size_t)r * k + tid];
     // the shared expert's row is requested with the first batch of slots
     float4 sh[kCombineV4];
 #pragma unroll
@@ -1066,8 +1070,9 @@ __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a) {
         sh[t] = a.has_shared ? reinterpret_cast<const float4*>(a.o + ((size_t)a.T * k + r) * H)[i4]
                              : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    __syncthreads();
-    // y = rs * sum_j w_j o_j (j in rank order) + shared (+ residual), per element
+    // y = rs * sum_j w_j o_j (j in rank order) + shared (+ residual), per element;
+    // slot (r, j)'s row is o row r*k + j, so the first batch's loads leave
+    // with the weights
     float4 acc[kCombineV4];
 #pragma unroll
     for (int t = 0; t < kCombineV4; ++t) acc[t] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1075,10 +1080,11 @@ __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a) {
         float4 ov[kCombineBatch][kCombineV4];
 #pragma unroll
         for (int b = 0; b < kCombineBatch; ++b) {
-            const float4* orow = reinterpret_cast<const float4*>(a.o + (size_t)s_o[min(j0 + b, k - 1)] * H);
+            const float4* orow = reinterpret_cast<const float4*>(a.o + ((size_t)r * k + min(j0 + b, k - 1)) * H);
 #pragma unroll
             for (int t = 0; t < kCombineV4; ++t) ov[b][t] = orow[min(t * kBlock + tid, n4 - 1)];
         }
+        if (j0 == 0) __syncthreads();  // s_w visible (every thread takes the same batches)
 #pragma unroll
         for (int b = 0; b < kCombineBatch; ++b) {
             if (j0 + b < k) {

@@ -197,16 +197,16 @@ struct GroupedDownArgs {
     const int32_t* off;
     const int32_t* tiles;
     const int32_t* n_tiles;
+    const int32_t* asg;     // [T*k] slot of each CSR position
     const float* h;
     const float* h_sh;
-    float* o;               // [T*k + T][H]: rows by asg position, then the shared rows by token
+    float* o;               // [T*k + T][H]: the routed rows by slot (r*k + j), then the shared rows by token
     int T, H, I, Is, k;
 };
 
 struct CombineArgs {
     const float* o;         // as GroupedDownArgs::o
     const float* w;         // [T][k]
-    const int32_t* inv;     // [T*k]
     const uint16_t* residual;  // bf16 [T][H] or nullptr
     float* y32;             // [T][H]
     uint16_t* y;            // bf16 [T][H] or nullptr
